@@ -1,0 +1,62 @@
+"""Float64 CPU model of the chunkwise form of the OSDN recurrence.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  It exists so that the chunk algebra
+the GPU kernels implement is checked against the token recurrence in float64, apart from
+any kernel: the tests require it to equal ``oracle.chunk_fwd`` to ~1e-12 at every chunk
+size, including chunk = 1 and chunk = T.
+
+The pages state that OSDN keeps DeltaNet's chunkwise WY pipeline with the scaled key K~ in
+place of the stored key in the chunk Gram matrix and the intra-chunk scores (OSDN: Improving
+Delta Rule with Provable Online Preconditioning in Linear Attention, technical summary,
+sections 1, 2.1, 2.2); they give no chunk algebra.  The algebra below is derived here from
+the token step  M_t = a_t (I - b_t k~_t k_t^T) M_{t-1} + b_t k~_t v_t^T  (M = S^T).
+
+For one chunk of C rows starting from state M0, let g_r = sum_{s<=r} ln a_s, gam_r = e^{g_r},
+and the pseudo-values u_r = b_r (v_r - a_r M_{r-1}^T k_r).  Unrolling the step gives
+    M_r = gam_r M0 + sum_{s<=r} (gam_r / gam_s) k~_s u_s^T,
+and substituting M_{r-1} into u_r gives the unit lower-triangular system
+    (I + A) U = diag(b) (V - diag(gam) K M0),
+    A[r,s] = b_r e^{g_r - g_s} <k_r, k~_s>   for s < r, 0 otherwise.
+Then, with L the lower triangle including the diagonal,
+    O   = diag(gam) Q M0 + (L o (Q K~^T) o G) U,       G[r,s] = e^{g_r - g_s}
+    M_C = gam_C M0 + (diag(e^{g_C - g}) K~)^T U .
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import numpy as np
+from scipy.linalg import solve_triangular
+
+
+def chunk_fwd(q, k, v, beta, d, alpha=None, S0=None, chunk: int = 64
+              ) -> Tuple[np.ndarray, np.ndarray]:
+    """Same contract as ``oracle.chunk_fwd``; evaluates the chunk algebra above."""
+    q, k, v, beta, d = (np.asarray(x, dtype=np.float64) for x in (q, k, v, beta, d))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    o = np.zeros((B, H, T, dv))
+    S_T = np.zeros((B, H, dk, dv))
+    for b in range(B):
+        for h in range(H):
+            M = np.zeros((dk, dv)) if S0 is None else np.array(S0[b, h], dtype=np.float64)
+            for c0 in range(0, T, chunk):
+                c1 = min(c0 + chunk, T)
+                Q, K, V = q[b, h, c0:c1], k[b, h, c0:c1], v[b, h, c0:c1]
+                bet = beta[b, h, c0:c1]
+                Kt = d[b, h, c0:c1] * K
+                if alpha is None:
+                    g = np.zeros(c1 - c0)
+                else:
+                    g = np.cumsum(np.log(np.asarray(alpha[b, h, c0:c1], dtype=np.float64)))
+                gam = np.exp(g)
+                G = np.exp(g[:, None] - g[None, :])
+                n = c1 - c0
+                A = np.tril(bet[:, None] * G * (K @ Kt.T), -1)
+                rhs = bet[:, None] * (V - gam[:, None] * (K @ M))
+                U = solve_triangular(np.eye(n) + A, rhs, lower=True, unit_diagonal=True)
+                P = np.tril((Q @ Kt.T) * G)
+                o[b, h, c0:c1] = gam[:, None] * (Q @ M) + P @ U
+                M = gam[-1] * M + (np.exp(g[-1] - g)[:, None] * Kt).T @ U
+            S_T[b, h] = M
+    return o, S_T
