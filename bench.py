@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Benchmark of libosdn on one MI355X.
+
+One step = one osdn_chunk_fwd call over the 1.3B-shape workload (B=4, H=16, T=4096,
+dk=dv=128, chunk 64, bf16 q/k/v/o, fp32 beta/d/alpha, fp32 final state emitted), i.e. one
+pass of the whole chunkwise hot path over one batch of synthetic input already resident in
+HBM.  Prints ONE JSON line.  Besides the contract fields it carries:
+
+  roofline      the chunk kernel against HBM: algorithmic bytes per launch / average
+                launch time from HIP events on the launch stream (peak 8 TB/s);
+  mfma          algorithmic FLOPs per launch / launch time against the bf16 dense peak;
+  cpu_baseline  the float64 oracle on the host cores, same workload, with the parity error
+                of the GPU output against it;
+  decode        osdn_step over the decode workload (B=128, H=16, dk=dv=128), timed over
+                `--decode-steps` consecutive calls (state updated in place).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "tokens/s + TFLOP/s (fraction of bf16 MFMA peak), OSDN chunkwise fwd"
+PEAK_HBM = 8.0e12      # bytes/s, MI355X HBM3E
+PEAK_BF16 = 2.5e15     # FLOP/s, MI355X dense bf16 matrix peak
+CHUNK_KERNEL_SRC = ["delta_rule_sequence_chunkwise_amd/csrc/osdn_chunk_f32.hip"]
+STEP_KERNEL_SRC = ["delta_rule_sequence_chunkwise_amd/csrc/osdn_step.hip"]
+
+
+def flops_per_head_token(dk, dv, C):
+    """Chunkwise FLOPs per head-token counting only the useful triangular halves: the three
+    state products (W M or K M, Q M, K~^T U) 6 dk dv; the Gram, P and the dk-side of the WY
+    factors C (3 dk + 2 dv); the triangular inverse C^2 / 3."""
+    return 6 * dk * dv + C * (3 * dk + 2 * dv) + C * C / 3.0
+
+
+def bytes_per_head_token(dk, dv, eq, ed, alpha=True):
+    """Compulsory HBM bytes per head-token: q, k, v in; d in; beta (and alpha) in; o out."""
+    return (2 * dk + dv) * eq + dk * ed + 4 + (4 if alpha else 0) + dv * eq
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(name, paths):
+    """Counter-measured HBM bytes per launch from profiles/<name>.json, if the kernel source
+    has not changed since the counters were taken."""
+    fn = os.path.join(ROOT, "profiles", f"{name}.json")
+    if not os.path.exists(fn):
+        return None
+    with open(fn) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != source_hash(paths):
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="1.3b")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the (b,h) "
+              "sequences shard across GPUs with no communication; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from delta_rule_sequence_chunkwise_amd import osdn, synth
+
+    if not os.path.exists(osdn.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS[args.workload]
+    x = synth.make_inputs(w)
+    qdt = torch.bfloat16 if w.qkv == "bf16" else torch.float32
+    to = lambda a, dt: None if a is None else torch.from_numpy(a).to(dev).to(dt)
+    q, k, v = (to(x[n], qdt) for n in ("q", "k", "v"))
+    beta, d, alpha, S0 = (to(x[n], torch.float32) for n in ("beta", "d", "alpha", "S0"))
+    B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
+    o = torch.empty((B, H, T, dv), dtype=qdt, device=dev)
+    S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+
+    def step():
+        osdn.osdn_chunk_fwd(q, k, v, beta, d, alpha, S0, chunk=w.chunk, o=o, S_T=S_T)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall_s = (t1 - t0) / args.steps
+    launch_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
+
+    head_tokens = B * H * T
+    eq = 2 if w.qkv == "bf16" else 4
+    alg_bytes = head_tokens * bytes_per_head_token(dk, dv, eq, 4, alpha is not None) \
+        + B * H * dk * dv * 4 * (2 if S0 is not None else 1)
+    alg_flops = head_tokens * flops_per_head_token(dk, dv, w.chunk)
+    achieved = alg_bytes / launch_s
+    traffic = load_traffic("chunk_fwd_1.3b_traffic", CHUNK_KERNEL_SRC)
+
+    line = {
+        "metric": METRIC,
+        "value": round(B * T / wall_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.qkv,
+        "data": "synthetic (seeded generator; q,k unit-norm, v normal, beta sigmoid, "
+                "d log-normal, alpha in (0.86, 0.995))",
+        "config": {"workload": f"{w.name}-shape OSDN chunkwise forward: B={B} H={H} T={T} "
+                               f"dk={dk} dv={dv} chunk={w.chunk}, {w.qkv} q/k/v/o, fp32 "
+                               "beta/d/alpha, fp32 final state",
+                   "B": B, "H": H, "T": T, "dk": dk, "dv": dv, "chunk": w.chunk},
+        "head_tokens_per_s": round(head_tokens / wall_s, 1),
+        "tflops": round(alg_flops / launch_s / 1e12, 3),
+        "mfma": {"achieved": round(alg_flops / launch_s / 1e12, 3), "peak": PEAK_BF16 / 1e12,
+                 "unit": "TFLOP/s", "frac": round(alg_flops / launch_s / PEAK_BF16, 5),
+                 "flops_per_launch": alg_flops},
+        "roofline": {"bound": "hbm", "achieved": round(achieved / 1e9, 2),
+                     "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM, 5),
+                     "traffic": traffic, "alg_bytes_per_launch": alg_bytes,
+                     "launch_ms": round(launch_s * 1e3, 4)},
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle
+        nt = oracle.default_threads()
+        c0 = time.perf_counter()
+        o_ref, S_ref = oracle.chunk_fwd(x["q"], x["k"], x["v"], x["beta"], x["d"],
+                                        x["alpha"], x["S0"], nthreads=nt)
+        cpu_s = time.perf_counter() - c0
+        o_gpu = o.float().cpu().numpy()
+        S_gpu = S_T.cpu().numpy()
+        rel = lambda a, b: float(np.max(np.abs(a - b)) / np.max(np.abs(b)))
+        line["cpu_baseline"] = {"value": round(B * T / cpu_s, 1), "unit": "tokens/s",
+                                "cores": nt, "kind": "oracle",
+                                "sample": f"the whole {w.name} workload ({B * H} sequences x "
+                                          f"{T} tokens), float64 C recurrence, "
+                                          f"{cpu_s:.2f} s wall"}
+        line["parity"] = {"e_o": rel(o_gpu, o_ref), "e_S": rel(S_gpu, S_ref),
+                          "tol": 2e-2 if w.qkv == "bf16" else 1e-4}
+        del o_ref, S_ref
+
+    if args.decode_steps > 0:
+        line["decode"] = bench_decode(args.decode_steps, torch, dev, synth)
+
+    print(json.dumps(line), flush=True)
+
+
+def bench_decode(n_steps, torch, dev, synth, distinct=64):
+    """Times `n_steps` consecutive osdn_step calls on the decode workload.  The generator
+    draws `distinct` per-step input tuples, used round-robin (the values do not change the
+    kernel's cost); the state is carried in place from call to call."""
+    from delta_rule_sequence_chunkwise_amd import osdn
+
+    w = synth.WORKLOADS["decode"]
+    n_in = min(distinct, n_steps)
+    y = synth.make_decode_inputs(w, steps=n_in)
+    to = lambda a, dt: torch.from_numpy(a).to(dev).to(dt)
+    q, k, v = (to(y[n], torch.bfloat16) for n in ("q", "k", "v"))
+    beta, d, alpha = (to(y[n], torch.float32) for n in ("beta", "d", "alpha"))
+    S = to(y["S0"], torch.float32)
+    BH = w.B * w.H
+    o = torch.empty((n_in, w.B, w.H, w.dv), dtype=torch.bfloat16, device=dev)
+    Sw = S.clone()
+    for t in range(min(3, n_in)):  # warm-up on a scratch copy of the state
+        osdn.osdn_step(q[t], k[t], v[t], beta[t], d[t], alpha[t], Sw, o=o[t])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for t in range(n_steps):
+        i = t % n_in
+        osdn.osdn_step(q[i], k[i], v[i], beta[i], d[i], alpha[i], S, o=o[i])
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    per = ev0.elapsed_time(ev1) / 1e3 / n_steps
+    state_bytes = 2 * BH * w.dk * w.dv * 4
+    io_bytes = BH * ((2 * w.dk + 2 * w.dv) * 2 + w.dk * 4 + 8)
+    alg = state_bytes + io_bytes
+    return {"workload": f"osdn_step B={w.B} H={w.H} dk={w.dk} dv={w.dv}, bf16 q/k/v/o, fp32 "
+                        f"beta/d/alpha/state, {n_steps} consecutive steps over {n_in} "
+                        "distinct input tuples",
+            "us_per_step": round(per * 1e6, 3), "alg_bytes_per_step": alg,
+            "achieved_GBps": round(alg / per / 1e9, 1),
+            "frac_of_hbm_peak": round(alg / per / PEAK_HBM, 4),
+            "traffic": load_traffic("step_decode_traffic", STEP_KERNEL_SRC),
+            "note": "the 128 MiB state fits in the 256 MB Infinity Cache; achieved is "
+                    "algorithmic bytes / time, see profiles for DRAM counters"}
+
+
+if __name__ == "__main__":
+    main()

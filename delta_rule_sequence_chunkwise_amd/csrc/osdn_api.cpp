@@ -1,0 +1,151 @@
+// libosdn host layer: argument validation and kernel dispatch behind the C ABI of osdn.h.
+// Every check runs before anything is enqueued; a failed check returns its status and
+// touches no memory.
+#include <stdint.h>
+
+#include "osdn_internal.h"
+
+namespace {
+
+struct Range {
+    uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
+};
+
+Range range_of(const void *p, int64_t bytes) {
+    Range r;
+    if (p && bytes > 0) {
+        r.lo = reinterpret_cast<uintptr_t>(p);
+        r.hi = r.lo + static_cast<uintptr_t>(bytes);
+    }
+    return r;
+}
+
+bool overlap(const Range &a, const Range &b) {
+    return a.lo != a.hi && b.lo != b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void *p, uintptr_t n) {
+    return (reinterpret_cast<uintptr_t>(p) % n) == 0;
+}
+
+// a*b*... without signed overflow; false if the product exceeds `limit`
+bool mul_ok(int64_t &acc, int64_t x, int64_t limit) {
+    if (x < 0) return false;
+    if (x != 0 && acc > limit / x) return false;
+    acc *= x;
+    return true;
+}
+
+int64_t elem_size(osdn_dtype t) { return t == OSDN_BF16 ? 2 : 4; }
+bool dtype_ok(osdn_dtype t) { return t == OSDN_F32 || t == OSDN_BF16; }
+bool head_dim_ok(int32_t n) { return n == 64 || n == 128; }
+
+// Largest element count any tensor may hold: keeps every byte offset (and every index the
+// kernels form in 64-bit arithmetic) far from overflow.
+constexpr int64_t kMaxElems = int64_t(1) << 46;
+
+}  // namespace
+
+extern "C" {
+
+const char *osdn_status_string(osdn_status s) {
+    switch (s) {
+        case OSDN_OK: return "ok";
+        case OSDN_ERR_NULL: return "a required pointer is NULL";
+        case OSDN_ERR_SHAPE: return "invalid size or element-count overflow";
+        case OSDN_ERR_UNSUPPORTED: return "unsupported dk/dv/chunk/dtype combination";
+        case OSDN_ERR_ALIGN: return "misaligned pointer";
+        case OSDN_ERR_ALIAS: return "output overlaps memory it must not overlap";
+        case OSDN_ERR_LAUNCH: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+int32_t osdn_abi_version(void) { return OSDN_ABI_VERSION; }
+
+osdn_status osdn_chunk_fwd(const void *q, const void *k, const void *v, const float *beta,
+                           const void *d, const float *alpha, const float *S0, void *o,
+                           float *S_T, int64_t B, int64_t H, int64_t T, int32_t dk,
+                           int32_t dv, int32_t chunk, osdn_dtype qkv, osdn_dtype d_dtype,
+                           void *stream) {
+    if (B < 0 || H < 0 || T < 0) return OSDN_ERR_SHAPE;
+    if (!dtype_ok(qkv) || !dtype_ok(d_dtype)) return OSDN_ERR_UNSUPPORTED;
+    if (!head_dim_ok(dk) || !head_dim_ok(dv)) return OSDN_ERR_UNSUPPORTED;
+    if (qkv == OSDN_BF16 ? chunk != 64 : (chunk != 16 && chunk != 32 && chunk != 64))
+        return OSDN_ERR_UNSUPPORTED;
+
+    int64_t BH = 1, tok = 1, st = 1;
+    if (!mul_ok(BH, B, kMaxElems) || !mul_ok(BH, H, kMaxElems)) return OSDN_ERR_SHAPE;
+    tok = BH;
+    if (!mul_ok(tok, T, kMaxElems)) return OSDN_ERR_SHAPE;
+    int64_t nqk = tok, nv = tok;
+    if (!mul_ok(nqk, dk, kMaxElems) || !mul_ok(nv, dv, kMaxElems)) return OSDN_ERR_SHAPE;
+    st = BH;
+    if (!mul_ok(st, int64_t(dk) * dv, kMaxElems)) return OSDN_ERR_SHAPE;
+    if (BH > int64_t(0x7fffffff) / 4) return OSDN_ERR_SHAPE;  // grid: BH x (dv / 32) groups
+
+    if (BH == 0) return OSDN_OK;
+    if (T > 0 && (!q || !k || !v || !beta || !d || !o)) return OSDN_ERR_NULL;
+    if (T == 0 && !S_T) return OSDN_OK;
+
+    const int64_t eq = elem_size(qkv), ed = elem_size(d_dtype);
+    if (T > 0) {
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(d, 16) ||
+            !aligned(o, 16) || !aligned(beta, 4) || (alpha && !aligned(alpha, 4)))
+            return OSDN_ERR_ALIGN;
+    }
+    if ((S0 && !aligned(S0, 16)) || (S_T && !aligned(S_T, 16))) return OSDN_ERR_ALIGN;
+
+    const int64_t n_tok = T > 0 ? tok : 0;
+    const Range rq = range_of(q, n_tok ? nqk * eq : 0), rk = range_of(k, n_tok ? nqk * eq : 0);
+    const Range rv = range_of(v, n_tok ? nv * eq : 0), rd = range_of(d, n_tok ? nqk * ed : 0);
+    const Range rb = range_of(beta, n_tok * 4), ra = range_of(alpha, n_tok * 4);
+    const Range rs0 = range_of(S0, st * 4), rst = range_of(S_T, st * 4);
+    const Range ro = range_of(o, n_tok ? nv * eq : 0);
+    for (const Range *in : {&rq, &rk, &rv, &rd, &rb, &ra, &rs0, &rst})
+        if (overlap(ro, *in)) return OSDN_ERR_ALIAS;
+    for (const Range *in : {&rq, &rk, &rv, &rd, &rb, &ra})
+        if (overlap(rst, *in)) return OSDN_ERR_ALIAS;
+    if (overlap(rst, rs0) && (rst.lo != rs0.lo)) return OSDN_ERR_ALIAS;
+
+    osdn::ChunkArgs a{q, k, v, d, beta, alpha, S0, o, S_T, BH, T, dk, dv, chunk, qkv, d_dtype};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t err = osdn::launch_chunk_fwd_f32math(a, s);
+    return err == hipSuccess ? OSDN_OK : OSDN_ERR_LAUNCH;
+}
+
+osdn_status osdn_step(const void *q, const void *k, const void *v, const float *beta,
+                      const void *d, const float *alpha, float *S, void *o, int64_t B,
+                      int64_t H, int32_t dk, int32_t dv, osdn_dtype qkv, osdn_dtype d_dtype,
+                      void *stream) {
+    if (B < 0 || H < 0) return OSDN_ERR_SHAPE;
+    if (!dtype_ok(qkv) || !dtype_ok(d_dtype)) return OSDN_ERR_UNSUPPORTED;
+    if (!head_dim_ok(dk) || !head_dim_ok(dv)) return OSDN_ERR_UNSUPPORTED;
+    int64_t BH = 1;
+    if (!mul_ok(BH, B, kMaxElems) || !mul_ok(BH, H, kMaxElems)) return OSDN_ERR_SHAPE;
+    int64_t st = BH;
+    if (!mul_ok(st, int64_t(dk) * dv, kMaxElems)) return OSDN_ERR_SHAPE;
+    if (BH > int64_t(0x7fffffff)) return OSDN_ERR_SHAPE;
+    if (BH == 0) return OSDN_OK;
+    if (!q || !k || !v || !beta || !d || !S || !o) return OSDN_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(d, 16) ||
+        !aligned(o, 16) || !aligned(S, 16) || !aligned(beta, 4) ||
+        (alpha && !aligned(alpha, 4)))
+        return OSDN_ERR_ALIGN;
+
+    const int64_t eq = elem_size(qkv), ed = elem_size(d_dtype);
+    const Range rq = range_of(q, BH * dk * eq), rk = range_of(k, BH * dk * eq);
+    const Range rv = range_of(v, BH * dv * eq), rd = range_of(d, BH * dk * ed);
+    const Range rb = range_of(beta, BH * 4), ra = range_of(alpha, BH * 4);
+    const Range rS = range_of(S, st * 4), ro = range_of(o, BH * dv * eq);
+    for (const Range *in : {&rq, &rk, &rv, &rd, &rb, &ra, &rS})
+        if (overlap(ro, *in)) return OSDN_ERR_ALIAS;
+    for (const Range *in : {&rq, &rk, &rv, &rd, &rb, &ra})
+        if (overlap(rS, *in)) return OSDN_ERR_ALIAS;
+
+    osdn::StepArgs a{q, k, v, d, beta, alpha, S, o, BH, dk, dv, qkv, d_dtype};
+    const hipError_t err = osdn::launch_step(a, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? OSDN_OK : OSDN_ERR_LAUNCH;
+}
+
+}  // extern "C"

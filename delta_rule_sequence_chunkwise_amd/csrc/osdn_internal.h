@@ -1,0 +1,60 @@
+// Internal declarations shared by the libosdn host layer and its HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "osdn.h"
+
+namespace osdn {
+
+// ---- element access -------------------------------------------------------------------------
+// bf16 is carried as its 16 raw bits.  Widening is exact; narrowing rounds to nearest even.
+struct bf16_t {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) {
+    return __uint_as_float(static_cast<uint32_t>(x.bits) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu))  // NaN: keep it quiet
+        return static_cast<uint16_t>((u >> 16) | 0x0040u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
+    return bf16_t{f32_to_bf16_bits(x)};
+}
+
+// ---- launch arguments -----------------------------------------------------------------------
+struct ChunkArgs {
+    const void *q, *k, *v, *d;
+    const float *beta, *alpha, *S0;
+    void *o;
+    float *S_T;
+    int64_t BH, T;
+    int32_t dk, dv, chunk;
+    osdn_dtype qkv, d_dtype;
+};
+
+struct StepArgs {
+    const void *q, *k, *v, *d;
+    const float *beta, *alpha;
+    float *S;
+    void *o;
+    int64_t BH;
+    int32_t dk, dv;
+    osdn_dtype qkv, d_dtype;
+};
+
+// Each launcher enqueues its kernels on `stream` and returns the HIP error of the launch.
+// Arguments were validated by the host layer.
+hipError_t launch_chunk_fwd_f32math(const ChunkArgs &a, hipStream_t stream);
+hipError_t launch_step(const StepArgs &a, hipStream_t stream);
+
+}  // namespace osdn

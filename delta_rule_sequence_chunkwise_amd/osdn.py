@@ -1,0 +1,151 @@
+"""Python binding of libosdn: argument marshalling over the C ABI of include/osdn.h.
+
+Every step of the computation runs in the library's HIP kernels; this module only checks
+tensor types, allocates outputs with torch (device memory is torch's), and passes raw device
+pointers and the current HIP stream.  If libosdn.so has not been built, importing the
+library raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libosdn.so")
+
+OSDN_F32 = 0
+OSDN_BF16 = 1
+ABI_VERSION = 1
+
+STATUS = {0: "OSDN_OK", -1: "OSDN_ERR_NULL", -2: "OSDN_ERR_SHAPE", -3: "OSDN_ERR_UNSUPPORTED",
+          -4: "OSDN_ERR_ALIGN", -5: "OSDN_ERR_ALIAS", -6: "OSDN_ERR_LAUNCH"}
+EXPORTS = ("osdn_chunk_fwd", "osdn_step", "osdn_status_string", "osdn_abi_version")
+
+
+class OSDNError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({status_string(status)})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libosdn.so (raises if it is missing or has another ABI version)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libosdn.so is not built ({LIB_PATH}); run "
+                          "`python -c 'import __graft_entry__ as g; g.build()'`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    L.osdn_chunk_fwd.restype = ctypes.c_int
+    L.osdn_chunk_fwd.argtypes = [vp] * 9 + [i64, i64, i64, i32, i32, i32, ctypes.c_int,
+                                             ctypes.c_int, vp]
+    L.osdn_step.restype = ctypes.c_int
+    L.osdn_step.argtypes = [vp] * 8 + [i64, i64, i32, i32, ctypes.c_int, ctypes.c_int, vp]
+    L.osdn_status_string.restype = ctypes.c_char_p
+    L.osdn_status_string.argtypes = [ctypes.c_int]
+    L.osdn_abi_version.restype = ctypes.c_int32
+    L.osdn_abi_version.argtypes = []
+    if L.osdn_abi_version() != ABI_VERSION:
+        raise ImportError(f"libosdn ABI {L.osdn_abi_version()} != {ABI_VERSION}")
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    try:
+        return lib().osdn_status_string(status).decode()
+    except ImportError:
+        return "?"
+
+
+# ---- torch marshalling ------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return OSDN_F32
+    if t.dtype == torch.bfloat16:
+        return OSDN_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream, device) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return s.cuda_stream
+
+
+def osdn_chunk_fwd(q, k, v, beta, d, alpha=None, S0=None, *, chunk: int = 64, o=None,
+                   S_T=None, want_state: bool = True, stream=None):
+    """Chunkwise OSDN forward.  q, k, d [B,H,T,dk]; v [B,H,T,dv]; beta, alpha [B,H,T] fp32;
+    S0 [B,H,dk,dv] fp32 (M = S^T).  Returns (o, S_T) (S_T is None unless ``want_state`` or
+    an ``S_T`` buffer is given).  ``S_T`` may be ``S0`` for an in-place carry."""
+    torch = _torch()
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    if S_T is None and want_state:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    for name, t, shape in (("k", k, (B, H, T, dk)), ("v", v, (B, H, T, dv)),
+                           ("beta", beta, (B, H, T)), ("d", d, (B, H, T, dk)),
+                           ("o", o, (B, H, T, dv))):
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+    if alpha is not None and tuple(alpha.shape) != (B, H, T):
+        raise ValueError("alpha must be [B,H,T]")
+    for name, t in (("S0", S0), ("S_T", S_T)):
+        if t is not None and (tuple(t.shape) != (B, H, dk, dv) or t.dtype != torch.float32):
+            raise ValueError(f"{name} must be float32 [B,H,dk,dv]")
+    for name, t in (("beta", beta), ("alpha", alpha)):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    if k.dtype != q.dtype or v.dtype != q.dtype or o.dtype != q.dtype:
+        raise TypeError("q, k, v and o must share one dtype")
+    st = lib().osdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(d), _ptr(alpha),
+                              _ptr(S0), _ptr(o), _ptr(S_T), B, H, T, dk, dv, chunk,
+                              _dtype_code(q), _dtype_code(d), _stream(stream, q.device))
+    if st != 0:
+        raise OSDNError(st, "osdn_chunk_fwd")
+    return o, S_T
+
+
+def osdn_step(q, k, v, beta, d, alpha, S, *, o=None, stream=None):
+    """One decode step, S [B,H,dk,dv] fp32 updated in place.  q, k, d [B,H,dk]; v [B,H,dv];
+    beta, alpha [B,H] fp32 (alpha may be None).  Returns o [B,H,dv]."""
+    torch = _torch()
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
+    if tuple(S.shape) != (B, H, dk, dv) or S.dtype != torch.float32:
+        raise ValueError("S must be float32 [B,H,dk,dv]")
+    if k.dtype != q.dtype or v.dtype != q.dtype or o.dtype != q.dtype:
+        raise TypeError("q, k, v and o must share one dtype")
+    st = lib().osdn_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(d), _ptr(alpha), _ptr(S),
+                         _ptr(o), B, H, dk, dv, _dtype_code(q), _dtype_code(d),
+                         _stream(stream, q.device))
+    if st != 0:
+        raise OSDNError(st, "osdn_step")
+    return o

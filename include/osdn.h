@@ -1,0 +1,111 @@
+/*
+ * libosdn -- Online Scaled DeltaNet (OSDN) forward and decode step for AMD gfx950 (MI355X).
+ *
+ * The operation (OSDN: Improving Delta Rule with Provable Online Preconditioning in Linear
+ * Attention, technical summary, section 2.1, with the per-token loss of section 1): for every
+ * (batch b, head h) sequence, token by token,
+ *
+ *     S_t = alpha_t S_{t-1} + beta_t (v_t - alpha_t S_{t-1} k_t) (d_t (.) k_t)^T ,
+ *     o_t = S_t q_t ,
+ *
+ * i.e. one delta-rule write whose gradient step is right-preconditioned by diag(d_t), which
+ * the summary shows is the same as scaling the write-side key to k~_t = d_t (.) k_t while the
+ * residual keeps the plain key.  The optional per-head scalar decay alpha_t is the
+ * gated-delta form (Erase-then-Delta Attention, section 2.2, eq. 4); it multiplies the old
+ * state before the residual is formed.  The read-out is taken after the write.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The library allocates
+ *     nothing, keeps no per-call state, and never synchronises the stream.  Work is enqueued
+ *     on `stream` (a hipStream_t; NULL = the default stream) and is complete when that
+ *     stream reaches it.  Calls on different streams may run concurrently.
+ *   - Layouts are dense row-major, head-major:  q, k, d [B,H,T,dk];  v, o [B,H,T,dv];
+ *     beta, alpha [B,H,T];  states [B,H,dk,dv] holding M = S^T (row i = key feature,
+ *     column j = value feature), always float32.
+ *   - q, k, v and o share one element type (`qkv`: OSDN_F32 or OSDN_BF16); d has its own
+ *     (`d_dtype`); beta, alpha and states are float32.  bf16 outputs are rounded to nearest
+ *     even.
+ *   - q, k, v, d, o and the state pointers must be 16-byte aligned; beta and alpha 4-byte.
+ *   - Validation happens on the host before anything is enqueued.  On any error the call
+ *     returns the status and touches no memory.  NaN/Inf in the inputs are not checked;
+ *     they propagate to the outputs.
+ *   - The same inputs give bitwise-identical outputs on every run (no atomics, fixed
+ *     reduction orders).
+ */
+#ifndef OSDN_H
+#define OSDN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define OSDN_ABI_VERSION 1
+
+typedef enum osdn_status {
+    OSDN_OK = 0,
+    OSDN_ERR_NULL = -1,        /* a required pointer is NULL                                 */
+    OSDN_ERR_SHAPE = -2,       /* a size is negative, or an element count would overflow     */
+    OSDN_ERR_UNSUPPORTED = -3, /* dk / dv / chunk / dtype combination not implemented        */
+    OSDN_ERR_ALIGN = -4,       /* a pointer violates the alignment rule above                */
+    OSDN_ERR_ALIAS = -5,       /* an output overlaps memory it must not overlap              */
+    OSDN_ERR_LAUNCH = -6,      /* the HIP runtime rejected the launch (e.g. no gfx950 device) */
+} osdn_status;
+
+typedef enum osdn_dtype { OSDN_F32 = 0, OSDN_BF16 = 1 } osdn_dtype;
+
+/*
+ * Chunkwise-parallel forward over whole sequences (OSDN technical summary, section 2.1: the
+ * scaled key takes the place of the stored key in the chunk Gram matrix and in the
+ * intra-chunk scores; the chunk algebra itself is derived from the token step above).
+ *
+ *   q, k   [B,H,T,dk] qkv     queries and keys (the write-side key is d (.) k)
+ *   v      [B,H,T,dv] qkv     values
+ *   beta   [B,H,T]    f32     scalar write gate
+ *   d      [B,H,T,dk] d_dtype per-token, per-feature preconditioner diagonal
+ *   alpha  [B,H,T]    f32     per-token, per-head decay; NULL means alpha == 1 (no decay)
+ *   S0     [B,H,dk,dv] f32    initial state M0 = S0^T; NULL means zero
+ *   o      [B,H,T,dv] qkv     output, o_t = S_t q_t (written for every t < T)
+ *   S_T    [B,H,dk,dv] f32    final state, NULL means not written.  S_T may be the same
+ *                             pointer as S0 (in-place carry); any other overlap is an error.
+ *   B, H, T >= 0              T == 0 writes S_T = S0 (or zeros); B*H == 0 does nothing.
+ *   dk, dv in {64, 128}
+ *   chunk                     rows per chunk: 64 for OSDN_BF16; 16, 32 or 64 for OSDN_F32.
+ *                             The result does not depend on it beyond rounding.  T need
+ *                             not be a multiple of it (the last chunk is masked).
+ *   qkv                       OSDN_F32 (fp32 arithmetic throughout) or OSDN_BF16 (bf16
+ *                             matrix-core operands, fp32 accumulation and fp32 state)
+ *   d_dtype                   OSDN_F32 or OSDN_BF16
+ *   o must not overlap any input or S_T.
+ */
+osdn_status osdn_chunk_fwd(const void *q, const void *k, const void *v, const float *beta,
+                           const void *d, const float *alpha, const float *S0, void *o,
+                           float *S_T, int64_t B, int64_t H, int64_t T, int32_t dk,
+                           int32_t dv, int32_t chunk, osdn_dtype qkv, osdn_dtype d_dtype,
+                           void *stream);
+
+/*
+ * One recurrent decode step for every (b,h) (the token step above, applied once):
+ *   q, k   [B,H,dk] qkv;  v [B,H,dv] qkv;  beta [B,H] f32;  d [B,H,dk] d_dtype;
+ *   alpha  [B,H] f32 or NULL (no decay);
+ *   S      [B,H,dk,dv] f32, read as M_{t-1} and overwritten in place with M_t;
+ *   o      [B,H,dv] qkv, o = M_t^T q.
+ *   dk, dv in {64, 128}.  o must not overlap S or any input; S must not overlap an input.
+ */
+osdn_status osdn_step(const void *q, const void *k, const void *v, const float *beta,
+                      const void *d, const float *alpha, float *S, void *o, int64_t B,
+                      int64_t H, int32_t dk, int32_t dv, osdn_dtype qkv, osdn_dtype d_dtype,
+                      void *stream);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *osdn_status_string(osdn_status s);
+
+/* OSDN_ABI_VERSION of the built library. */
+int32_t osdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OSDN_H */

@@ -1,0 +1,131 @@
+"""libosdn's C ABI on the host: it loads, exports what include/osdn.h declares, and every
+validation path returns its status before anything is enqueued (no GPU needed: these calls
+never reach a launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from delta_rule_sequence_chunkwise_amd import osdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(osdn.LIB_PATH):
+        from delta_rule_sequence_chunkwise_amd import build
+        build.build()
+    return osdn.lib()
+
+
+def declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"\b(osdn_\w+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(osdn.EXPORTS) <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version(L):
+    assert L.osdn_abi_version() == osdn.ABI_VERSION
+    for code in osdn.STATUS:
+        s = L.osdn_status_string(code)
+        assert s and s.decode()
+    assert L.osdn_status_string(12345) == b"unknown status"
+
+
+# fake, 256-byte aligned device addresses: validation compares them, never dereferences
+BASE = 1 << 40
+SPAN = 1 << 32
+
+
+def addr(i):
+    return BASE + i * SPAN
+
+
+def chunk_args(**over):
+    a = dict(q=addr(1), k=addr(2), v=addr(3), beta=addr(4), d=addr(5), alpha=addr(6),
+             S0=addr(7), o=addr(8), S_T=addr(9), B=2, H=3, T=100, dk=128, dv=64, chunk=64,
+             qkv=osdn.OSDN_BF16, d_dtype=osdn.OSDN_F32, stream=None)
+    a.update(over)
+    return a
+
+
+def call_chunk(L, **over):
+    a = chunk_args(**over)
+    return L.osdn_chunk_fwd(a["q"], a["k"], a["v"], a["beta"], a["d"], a["alpha"], a["S0"],
+                            a["o"], a["S_T"], a["B"], a["H"], a["T"], a["dk"], a["dv"],
+                            a["chunk"], a["qkv"], a["d_dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(beta=None), -1),
+    (dict(d=None), -1), (dict(o=None), -1),
+    (dict(B=-1), -2), (dict(H=-2), -2), (dict(T=-5), -2),
+    (dict(B=1 << 40, H=1 << 20), -2), (dict(T=1 << 45), -2),
+    (dict(dk=96), -3), (dict(dv=32), -3), (dict(dk=256), -3),
+    (dict(chunk=32), -3), (dict(qkv=osdn.OSDN_F32, chunk=48), -3), (dict(qkv=7), -3),
+    (dict(d_dtype=3), -3),
+    (dict(q=addr(1) + 8), -4), (dict(o=addr(8) + 4), -4), (dict(S0=addr(7) + 4), -4),
+    (dict(beta=addr(4) + 2), -4), (dict(alpha=addr(6) + 1), -4),
+    (dict(o=addr(1)), -5), (dict(o=addr(3) + 256), -5), (dict(S_T=addr(8)), -5),
+    (dict(S_T=addr(2)), -5), (dict(S_T=addr(7) + 4096), -5), (dict(o=addr(9)), -5),
+])
+def test_chunk_fwd_rejects(L, over, status):
+    assert call_chunk(L, **over) == status
+
+
+def test_chunk_fwd_empty_work_is_ok_without_touching_memory(L):
+    assert call_chunk(L, B=0) == 0
+    assert call_chunk(L, H=0, q=None) == 0
+    # T == 0 with no final state requested: nothing to do, inputs may be NULL
+    assert call_chunk(L, T=0, q=None, k=None, v=None, beta=None, d=None, o=None,
+                      S_T=None) == 0
+
+
+def step_args(**over):
+    a = dict(q=addr(1), k=addr(2), v=addr(3), beta=addr(4), d=addr(5), alpha=addr(6),
+             S=addr(7), o=addr(8), B=4, H=2, dk=128, dv=128, qkv=osdn.OSDN_BF16,
+             d_dtype=osdn.OSDN_F32, stream=None)
+    a.update(over)
+    return a
+
+
+def call_step(L, **over):
+    a = step_args(**over)
+    return L.osdn_step(a["q"], a["k"], a["v"], a["beta"], a["d"], a["alpha"], a["S"], a["o"],
+                       a["B"], a["H"], a["dk"], a["dv"], a["qkv"], a["d_dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), -1), (dict(S=None), -1), (dict(o=None), -1), (dict(d=None), -1),
+    (dict(B=-1), -2), (dict(B=1 << 40, H=1 << 30), -2),
+    (dict(dk=32), -3), (dict(dv=100), -3), (dict(qkv=2), -3),
+    (dict(S=addr(7) + 4), -4), (dict(q=addr(1) + 2), -4),
+    (dict(o=addr(7)), -5), (dict(S=addr(1)), -5), (dict(o=addr(2) + 64), -5),
+])
+def test_step_rejects(L, over, status):
+    assert call_step(L, **over) == status
+
+
+def test_step_empty_is_ok(L):
+    assert call_step(L, B=0, q=None) == 0
+
+
+def test_python_binding_refuses_host_tensors(L):
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 1, 4, 64)
+    with pytest.raises(ValueError):
+        osdn.osdn_chunk_fwd(x, x, x, torch.zeros(1, 1, 4), x, want_state=False,
+                            o=torch.zeros(1, 1, 4, 64))

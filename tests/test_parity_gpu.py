@@ -1,0 +1,142 @@
+"""GPU parity: libosdn against the float64 oracle on the same seeded inputs.
+
+Error measure: max |x_gpu - x_ref| / max |x_ref| over the whole output, for o and for the
+final state; bounds 1e-4 for fp32 inputs and 2e-2 for bf16 inputs (fp32 accumulation)."""
+import numpy as np
+import pytest
+
+import oracle
+from delta_rule_sequence_chunkwise_amd import osdn, synth
+from tests.gpu_util import (TOL, gpu_chunk, oracle_inputs, rel_err, say, to_dev, to_np,
+                            torch_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def check(x, qkv, d_dtype="f32", chunk=64, label=""):
+    say("chunk_fwd", label, "qkv", qkv, "d", d_dtype, "chunk", chunk,
+        "shape", x["q"].shape, x["v"].shape[-1])
+    o, S = gpu_chunk(x, qkv=qkv, d_dtype=d_dtype, chunk=chunk)
+    o_ref, S_ref = oracle.chunk_fwd(*oracle_inputs(x, d_dtype))
+    eo, es = rel_err(o, o_ref), rel_err(S, S_ref)
+    say(f"  e_o={eo:.3e} e_S={es:.3e}")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(S))
+    assert eo <= TOL[qkv], f"e_o {eo:.3e}"
+    assert es <= TOL[qkv], f"e_S {es:.3e}"
+    return eo, es
+
+
+def test_tiny_workload():
+    x = synth.make_inputs(synth.WORKLOADS["tiny"])
+    check(x, "f32", label="tiny")
+
+
+F32_CASES = [
+    # B, H, T, dk, dv, chunk, alpha, s0, d dtype
+    (1, 2, 200, 64, 64, 16, True, True, "f32"),
+    (2, 1, 67, 128, 64, 32, True, False, "f32"),
+    (1, 3, 1, 64, 128, 64, False, True, "f32"),
+    (1, 1, 130, 128, 128, 64, True, True, "bf16"),
+    (3, 2, 64, 128, 128, 16, False, False, "f32"),
+    (1, 2, 321, 64, 64, 64, True, True, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", F32_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_f32_shapes(case):
+    B, H, T, dk, dv, chunk, alpha, s0, dd = case
+    x = synth.make_shape(B, H, T, dk, dv, qkv="f32", alpha=alpha, s0=s0, seed=T + dk)
+    check(x, "f32", d_dtype=dd, chunk=chunk, label=str(case))
+
+
+BF16_CASES = [
+    (2, 2, 300, 128, 128, True, True, "f32"),
+    (1, 2, 64, 64, 64, True, False, "f32"),
+    (1, 1, 65, 128, 64, False, True, "f32"),
+    (2, 3, 1, 128, 128, True, True, "f32"),
+    (1, 2, 200, 64, 128, True, True, "bf16"),
+    (4, 4, 512, 128, 128, True, False, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", BF16_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_bf16_shapes(case):
+    B, H, T, dk, dv, alpha, s0, dd = case
+    x = synth.make_shape(B, H, T, dk, dv, qkv="bf16", alpha=alpha, s0=s0, seed=T + dv)
+    check(x, "bf16", d_dtype=dd, label=str(case))
+
+
+@pytest.mark.parametrize("name", ["340m", "1.3b", "long"])
+def test_full_workload(name):
+    w = synth.WORKLOADS[name]
+    x = synth.make_inputs(w)
+    check(x, w.qkv, label=name)
+
+
+@pytest.mark.parametrize("qkv", ["f32", "bf16"])
+def test_zero_length_copies_initial_state(qkv):
+    torch, dev = torch_dev()
+    x = synth.make_shape(2, 2, 0, 128, 64, qkv=qkv, s0=True)
+    say("T=0", qkv)
+    o, S = gpu_chunk(x, qkv=qkv)
+    assert o.shape == (2, 2, 0, 64)
+    assert np.array_equal(S, x["S0"].astype(np.float64))
+    x["S0"] = None
+    o, S = gpu_chunk(x, qkv=qkv, S0=None)
+    assert not np.any(S)
+
+
+@pytest.mark.parametrize("qkv", ["f32", "bf16"])
+def test_split_continuation_and_in_place_carry(qkv):
+    """T1 then T2 from S_T(T1) equals T1 + T2; with T1 a multiple of the chunk the chunk
+    boundaries coincide and the results are bitwise equal.  S_T may be S0 (in place)."""
+    torch, dev = torch_dev()
+    x = synth.make_shape(2, 2, 64 * 3 + 17, 128, 128, qkv=qkv, s0=True, seed=5)
+    cut = 128
+    say("split", qkv)
+    dev_in = {n: to_dev(x[n], qkv) for n in ("q", "k", "v")}
+    beta, d, alpha = (to_dev(x[n], "f32") for n in ("beta", "d", "alpha"))
+    S0 = to_dev(x["S0"], "f32")
+    o_full, S_full = osdn.osdn_chunk_fwd(dev_in["q"], dev_in["k"], dev_in["v"], beta, d, alpha,
+                                         S0)
+    first = lambda t: t[:, :, :cut].contiguous()
+    last = lambda t: t[:, :, cut:].contiguous()
+    S = S0.clone()
+    o1, _ = osdn.osdn_chunk_fwd(*(first(dev_in[n]) for n in ("q", "k", "v")), first(beta),
+                                first(d), first(alpha), S, S_T=S)
+    o2, _ = osdn.osdn_chunk_fwd(*(last(dev_in[n]) for n in ("q", "k", "v")), last(beta),
+                                last(d), last(alpha), S, S_T=S)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([o1, o2], dim=2), o_full)
+    assert torch.equal(S, S_full)
+
+
+@pytest.mark.parametrize("qkv", ["f32", "bf16"])
+def test_bitwise_reproducible(qkv):
+    x = synth.make_shape(2, 4, 333, 128, 128, qkv=qkv, s0=True, seed=9)
+    say("repro", qkv)
+    o1, S1 = gpu_chunk(x, qkv=qkv)
+    o2, S2 = gpu_chunk(x, qkv=qkv)
+    assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
+
+
+def test_chunk_size_invariance_f32():
+    x = synth.make_shape(1, 2, 250, 128, 64, qkv="f32", s0=True, seed=3)
+    outs = []
+    for c in (16, 32, 64):
+        say("chunk size", c)
+        outs.append(gpu_chunk(x, qkv="f32", chunk=c))
+    for o, S in outs[1:]:
+        assert rel_err(o, outs[0][0]) <= 1e-5 and rel_err(S, outs[0][1]) <= 1e-5
+
+
+@pytest.mark.parametrize("qkv", ["f32", "bf16"])
+def test_nonfinite_inputs_propagate(qkv):
+    """A NaN is not checked for; it reaches every later output and the state, and leaves
+    the chunks before it untouched."""
+    x = synth.make_shape(1, 1, 140, 64, 64, qkv=qkv, seed=4)
+    x["v"][0, 0, 70, 3] = np.nan
+    say("nan propagation", qkv)
+    o, S = gpu_chunk(x, qkv=qkv)
+    assert np.isfinite(o[0, 0, :64]).all()
+    assert np.isnan(o[0, 0, 70:]).any() and np.isnan(S).any()
