@@ -30,7 +30,7 @@ if ROOT not in sys.path:
 METRIC = "tokens/s + TFLOP/s (fraction of bf16 MFMA peak), OSDN chunkwise fwd"
 PEAK_HBM = 8.0e12      # bytes/s, MI355X HBM3E
 PEAK_BF16 = 2.5e15     # FLOP/s, MI355X dense bf16 matrix peak
-CHUNK_KERNEL_SRC = ["delta_rule_sequence_chunkwise_amd/csrc/osdn_chunk_f32.hip"]
+CHUNK_KERNEL_SRC = ["delta_rule_sequence_chunkwise_amd/csrc/osdn_chunk_mfma.hip"]
 STEP_KERNEL_SRC = ["delta_rule_sequence_chunkwise_amd/csrc/osdn_step.hip"]
 
 

@@ -110,7 +110,8 @@ osdn_status osdn_chunk_fwd(const void *q, const void *k, const void *v, const fl
 
     osdn::ChunkArgs a{q, k, v, d, beta, alpha, S0, o, S_T, BH, T, dk, dv, chunk, qkv, d_dtype};
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const hipError_t err = osdn::launch_chunk_fwd_f32math(a, s);
+    const hipError_t err = qkv == OSDN_BF16 ? osdn::launch_chunk_fwd_mfma(a, s)
+                                            : osdn::launch_chunk_fwd_f32math(a, s);
     return err == hipSuccess ? OSDN_OK : OSDN_ERR_LAUNCH;
 }
 

@@ -55,6 +55,7 @@ struct StepArgs {
 // Each launcher enqueues its kernels on `stream` and returns the HIP error of the launch.
 // Arguments were validated by the host layer.
 hipError_t launch_chunk_fwd_f32math(const ChunkArgs &a, hipStream_t stream);
+hipError_t launch_chunk_fwd_mfma(const ChunkArgs &a, hipStream_t stream);
 hipError_t launch_step(const StepArgs &a, hipStream_t stream);
 
 }  // namespace osdn
