@@ -75,6 +75,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="1.3b")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (3 times): the "
+                         "reference for scaling HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the (b,h) "
@@ -84,6 +87,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n * 4, "copies": 3}), flush=True)
+        return
 
     from delta_rule_sequence_chunkwise_amd import osdn, synth
 
