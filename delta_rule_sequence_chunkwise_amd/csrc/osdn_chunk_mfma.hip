@@ -10,38 +10,38 @@
 //   a5  P = lower-inclusive( (Q K~^T) (.) e^{g_r - g_s} )                    intra-chunk scores
 //   a6  O = diag(gam) Q M + P U;   M <- gam_C M + K~^T diag(w) U            read-out, carry
 //
-// One workgroup of five waves owns one (b,h) sequence and a 32-wide slice of the value
+// One workgroup of seven waves owns one (b,h) sequence and a 32-wide slice of the value
 // columns (value columns are independent given the chunk's A and P) and walks the chunks in
-// order, with one barrier per chunk step.  The waves have three roles, each running its own
-// loop with the same barriers:
+// order, one barrier per step.  Each role runs its own loop over steps c = -2 .. nchunks-1:
 //
-// * State waves (0, 1), one per 16 value columns.  A state wave holds its dk x 16 slice of M
-//   in VGPRs (fp32, the C layout of 16x16 MFMA tiles) for the whole sequence and runs the
-//   state-dependent chain of chunk c without touching LDS for M or U: R, the block forward
-//   substitution U_i = D_i (R_i - sum_{k<i} A_ik U_k) (16x16x16 products; their output layout
-//   equals their B-operand layout), the read-out O^T = (M^T Q^T) diag(gam) + U^T P^T, the
-//   carry M <- gam_C M + K~^T (w U), and then K M and M^T Q^T of chunk c+1.
+// * State waves (0, 1), one per 16 value columns, process chunk c.  A state wave holds its
+//   dk x 16 slice of M in VGPRs (fp32, the C layout of 16x16 MFMA tiles) for the whole
+//   sequence and runs the state-dependent chain without touching LDS for M or U: R, the block
+//   forward substitution U_i = D_i (R_i - sum_{k<i} A_ik U_k) (16x16x16 products; their output
+//   layout equals their B-operand layout), the read-out O^T = (M^T Q^T) diag(gam) + U^T P^T,
+//   the carry M <- gam_C M + K~^T (w U), and then K M and M^T Q^T of chunk c+1.
 //   A pair of 16x16 C-layout tiles becomes one 16x16x32 operand fragment with two packs and
 //   four lane swaps (v_permlane32_swap, v_permlane16_swap): lane (quarter q, column n) then
 //   holds rows 8q..8q+7 of the 32-row pair, which is both the B layout of the pair and the
 //   A layout of its transpose.  So every K-slot runs in natural order and each q, k and P
 //   operand fragment is a single 16-byte LDS read.
-// * Prep waves (2, 3) work one chunk ahead: k~ of chunk c+1 (from the k tile and d prefetched
-//   into registers a chunk earlier), its Gram and score tiles, and the inverses
-//   D_i = (I + A_ii)^{-1} of the diagonal blocks, computed in registers as
-//   (I-N)(I+N^2)(I+N^4)(I+N^8) (N strictly lower, N^16 = 0).  The tiles are split by column
-//   block: wave 2 takes blocks {0,3}, wave 3 blocks {1,2}, ten tiles each, so each wave builds
-//   only its own k~ blocks and needs no other wave's k~.
-// * The loader wave (4) issues the q, k, v loads of chunk c+2 straight into LDS and runs the
-//   decay scan of chunk c+2.  Issuing loads stalls while HBM drains them; here that stall
-//   falls on a wave with little else to do.
+// * Prep waves (2, 3) build chunk c+1's Gram and score tiles and the inverses
+//   D_i = (I + A_ii)^{-1} of its diagonal blocks, computed in registers as
+//   (I-N)(I+N^2)(I+N^4)(I+N^8) (N strictly lower, N^16 = 0), two blocks in lockstep.  The
+//   tiles are split by column block: wave 2 takes blocks {0,3}, wave 3 blocks {1,2}.
+// * Stager waves (4, 5) bring the k rows of chunk c+2 into LDS (two row blocks each) and write
+//   k~ = d (.) k of those rows; d reaches their registers one step ahead.
+// * The loader wave (6) brings q and v of chunk c+2 into LDS and runs its decay scan.
+// Loads stall the issuing wave while HBM drains them, and too many in flight at once thrash
+// the CU's load queues; so they are issued in groups of at most 16 by waves whose other work
+// is light, and each state wave shares its SIMD with a stager.
 //
 // q, k and v reach LDS by global_load_lds (16 bytes per lane; the 16-byte units of each q/k
 // row are XOR-swizzled by the row index so fragment reads are bank-conflict free), double-
 // buffered by chunk parity; the state waves read the v tile of chunk c+1 into registers at
-// the end of step c.  k~, P and the block inverses are double-buffered by chunk parity, the
-// scan outputs by chunk mod 3.  Every wave drains its global memory operations before the
-// end-of-step barrier.
+// the end of step c.  P and the block inverses are double-buffered by chunk parity; k~ and
+// the scan outputs, written two steps before their last use, by chunk mod 3.  Waves whose
+// loads target LDS drain them before the end-of-step barrier.
 #include <type_traits>
 
 #include "osdn_internal.h"
@@ -63,7 +63,7 @@ constexpr int CH = 64;                       // rows per chunk
 constexpr int NBLK = CH / 16;                // 16-row blocks per chunk
 constexpr int NOFF = NBLK * (NBLK - 1) / 2;  // off-diagonal 16x16 blocks of the Gram matrix
 constexpr int BV = 32;                       // value columns per workgroup
-constexpr int NW = 5;                        // waves per workgroup: 2 state, 2 prep, 1 loader
+constexpr int NW = 7;  // waves per workgroup: 2 state, 2 prep, 2 stagers, 1 loader
 constexpr int VW = 16;                       // value columns per state wave
 
 __device__ __forceinline__ v4f mfma32(v8s a, v8s b, v4f c) {
@@ -135,16 +135,23 @@ __device__ __forceinline__ void wait_global() {
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     asm volatile("" ::: "memory");
 }
+// at most 8 vector memory operations of this wave still in flight: issuing loads in groups
+// of 8 with this wait between them keeps the CU's load queues from thrashing
+__device__ __forceinline__ void wait_global8() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0f78);  // vmcnt(8)
+    asm volatile("" ::: "memory");
+}
 
 template <int DK>
 struct alignas(16) Lds {
     static constexpr int KU = DK / 8;   // 16-byte units per q/k row
     static constexpr int KP = DK + 8;   // row pitch (bf16) of k~
     static constexpr int CP = CH + 8;   // row pitch (bf16) of P
-    static constexpr int DP = 16 + 4;   // row pitch (bf16) of 16x16 blocks
+    static constexpr int DP = 16;       // row pitch (bf16) of 16x16 blocks
     // element offset of logical 16-byte unit u of row r in a swizzled q/k tile
     __device__ static constexpr int qk_at(int r, int u) { return (r * KU + (u ^ (r & 7))) * 8; }
-    alignas(16) uint16_t kt[2][CH * KP];            // [chunk parity] k~, row-major
+    alignas(16) uint16_t kt[3][CH * KP];            // [chunk mod 3] k~, row-major
     alignas(16) uint16_t p[2][CH * CP];             // [chunk parity] P, row-major
     alignas(16) uint16_t dinv[2][NBLK * 16 * DP];   // D_i = (I + A_ii)^{-1}, row-major
     alignas(16) uint16_t aneg[2][NOFF * 16 * DP];   // -A_ik (i > k), row-major
@@ -164,31 +171,6 @@ struct alignas(16) Lds {
 // Prep wave pw owns the Gram/score column blocks kblk(pw, 0), kblk(pw, 1)
 __host__ __device__ constexpr int kblk(int pw, int j) { return pw == 0 ? (j == 0 ? 0 : 3) : (j == 0 ? 1 : 2); }
 
-// d of a prep wave's two blocks, one chunk ahead (fragment layout: lane (q, n) holds row
-// 16 kb + n, features 32 s + 8 q .. +7)
-template <int DK, typename TD>
-struct PrepRegs {
-    static constexpr int NS = DK / 32;
-    static constexpr int DU = sizeof(TD) * 8 / 16;  // uint4 per 8 values of d
-    uint4 d[2][NS][DU];
-};
-
-template <int DK, typename TD, int PW>
-__device__ __forceinline__ void load_d_frag(PrepRegs<DK, TD> &pr, const TD *d, int64_t row0,
-                                            int n, int lr, int lq) {
-    using PR = PrepRegs<DK, TD>;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int r = min(16 * kblk(PW, j) + lr, n - 1);
-#pragma unroll
-        for (int s = 0; s < PR::NS; ++s) {
-            const uint4 *src = reinterpret_cast<const uint4 *>(d + (row0 + r) * DK + 32 * s + 8 * lq);
-#pragma unroll
-            for (int e = 0; e < PR::DU; ++e) pr.d[j][s][e] = src[e];
-        }
-    }
-}
-
 __device__ __forceinline__ void d_values(const uint4 *src, float *out, float) {
     const float *f = reinterpret_cast<const float *>(src);
 #pragma unroll
@@ -203,20 +185,21 @@ __device__ __forceinline__ void d_values(const uint4 *src, float *out, bf16_t) {
     }
 }
 
-// q and k rows of one chunk into LDS (loader wave; rows past the end re-read the last row)
-template <int DK>
-__device__ __forceinline__ void load_qk(uint16_t *qb, uint16_t *kb, const uint16_t *q,
-                                        const uint16_t *k, int64_t row0, int n, int lane) {
+// rows [R0, R0 + NR) of one q or k chunk tile into LDS, 16-byte units XOR-swizzled by the
+// row (one wave; rows past the end of the sequence re-read its last row); at most 16 loads of
+// the wave in flight
+template <int DK, int R0, int NR>
+__device__ __forceinline__ void load_rows(uint16_t *dst, const uint16_t *src, int64_t row0, int n,
+                                          int lane) {
     using L = Lds<DK>;
-    constexpr int NLOAD = CH * L::KU / 64;
-    static_assert(CH * L::KU % 64 == 0, "whole wave-loads");
+    constexpr int NLOAD = NR * L::KU / 64;
+    static_assert(NR * L::KU % 64 == 0, "whole wave-loads");
 #pragma unroll
     for (int i = 0; i < NLOAD; ++i) {
-        const int base = i * 64;  // physical unit of lane 0
+        const int base = R0 * L::KU + i * 64;  // physical unit of lane 0
         const int pu = base + lane, r = pu / L::KU, lu = (pu % L::KU) ^ (r & 7);
-        const int64_t off = (row0 + min(r, n - 1)) * DK + 8 * lu;
-        load_to_lds16(q + off, qb + 8 * base);
-        load_to_lds16(k + off, kb + 8 * base);
+        load_to_lds16(src + (row0 + min(r, n - 1)) * DK + 8 * lu, dst + 8 * base);
+        if (i % 8 == 7 && i + 1 < NLOAD) wait_global8();
     }
 }
 
@@ -282,35 +265,70 @@ __device__ __forceinline__ void scan_chunk(Lds<DK> &sm, int slot, float beta, fl
     if (lane < 6) sm.cik[slot][lane] = __expf(gi - gk);
 }
 
-// D_kb = (I + N)^{-1} of diagonal block kb from N in the A layout (lane holds N[lr][4lq+e]);
-// the B layout (lane holds N[4lq+e][lr]) comes back through LDS with a transposing read
+// D_kb = (I + N)^{-1} for the two diagonal blocks kb0, kb1 of a prep wave, in lockstep so the
+// two dependent chains overlap.  Input: N in the A layout (lane holds N[lr][4lq+e]); the B
+// layout (lane holds N[4lq+e][lr]) comes back through LDS with a transposing read.
 template <int DK>
-__device__ __forceinline__ void diag_inverse(Lds<DK> &sm, int b, int kb, int lr, int lq,
-                                             v4f Na_f) {
+__device__ __forceinline__ void diag_inverse2(Lds<DK> &sm, int b, int kb0, int kb1, int lr,
+                                              int lq, const v4f (&na)[2]) {
     using L = Lds<DK>;
-    const uint2 na = pack4u(Na_f);
-    *reinterpret_cast<uint2 *>(&sm.ntile[kb][lr * 16 + 4 * lq]) = na;
-    const v4s Na = __builtin_bit_cast(v4s, na);
-    const v4s Nb = ld_tr(&sm.ntile[kb][(4 * lq + (lr >> 2)) * 16 + 4 * (lr & 3)]);
+    const int kb[2] = {kb0, kb1};
+    v4s Na[2], Nb[2], N2a[2], N2b[2], N4a[2], N4b[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const uint2 u = pack4u(na[j]);
+        *reinterpret_cast<uint2 *>(&sm.ntile[kb[j]][lr * 16 + 4 * lq]) = u;
+        Na[j] = __builtin_bit_cast(v4s, u);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+        Nb[j] = ld_tr(&sm.ntile[kb[j]][(4 * lq + (lr >> 2)) * 16 + 4 * (lr & 3)]);
     // squares in both layouts: X^2 (C = B layout) = X X;  (X^2)^T (C = A layout) = X^T X^T
-    const v4f N2 = mfma16(Na, Nb, zero4());
-    const v4f N2t = mfma16(Nb, Na, zero4());
-    const v4s N2a = pack4(N2t), N2b = pack4(N2);
-    const v4f N4 = mfma16(N2a, N2b, zero4());
-    const v4f N4t = mfma16(N2b, N2a, zero4());
-    const v4s N4a = pack4(N4t), N4b = pack4(N4);
+    v4f X[2], Xt[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        X[j] = mfma16(Na[j], Nb[j], zero4());
+        Xt[j] = mfma16(Nb[j], Na[j], zero4());
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        N2a[j] = pack4(Xt[j]);
+        N2b[j] = pack4(X[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        X[j] = mfma16(N2a[j], N2b[j], zero4());
+        Xt[j] = mfma16(N2b[j], N2a[j], zero4());
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        N4a[j] = pack4(Xt[j]);
+        N4b[j] = pack4(X[j]);
+    }
     // D^T = (I - N^T)(I + N^2T)(I + N^4T)(I + N^8T), built in C layout = A layout of D;
     // the A operand N^T (A layout) is N in the B layout
-    v4f Y = mfma16(N4b, N4a, zero4());  // (N^8)^T
+    v4f Y[2];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-        if (4 * lq + e == lr) Y[e] += 1.f;
-    Y = mfma16(N4b, pack4(Y), Y);
-    Y = mfma16(N2b, pack4(Y), Y);
-    const uint2 nb = __builtin_bit_cast(uint2, Nb);
-    const v4s mNb = __builtin_bit_cast(v4s, make_uint2(nb.x ^ 0x80008000u, nb.y ^ 0x80008000u));
-    Y = mfma16(mNb, pack4(Y), Y);
-    *reinterpret_cast<uint2 *>(&sm.dinv[b][kb * 16 * L::DP + lr * L::DP + 4 * lq]) = pack4u(Y);
+    for (int j = 0; j < 2; ++j) Y[j] = mfma16(N4b[j], N4a[j], zero4());  // (N^8)^T
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (4 * lq + e == lr) Y[j][e] += 1.f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) Y[j] = mfma16(N4b[j], pack4(Y[j]), Y[j]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) Y[j] = mfma16(N2b[j], pack4(Y[j]), Y[j]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const uint2 nb = __builtin_bit_cast(uint2, Nb[j]);
+        const v4s mNb = __builtin_bit_cast(v4s, make_uint2(nb.x ^ 0x80008000u, nb.y ^ 0x80008000u));
+        Y[j] = mfma16(mNb, pack4(Y[j]), Y[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+        *reinterpret_cast<uint2 *>(&sm.dinv[b][kb[j] * 16 * L::DP + lr * L::DP + 4 * lq]) =
+            pack4u(Y[j]);
 }
 
 template <int DK, typename TD>
@@ -325,18 +343,16 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
     constexpr int NFT = DK / 16;  // 16-row feature tiles of the state
 
     __shared__ L sm;
-    // q and k buffers: one __shared__ variable each (see the file comment)
-    __shared__ alignas(16) uint16_t q_buf0[CH * DK], q_buf1[CH * DK];
-    __shared__ alignas(16) uint16_t k_buf0[CH * DK], k_buf1[CH * DK];
-    __shared__ alignas(16) uint16_t v_buf0[BV * CH], v_buf1[BV * CH];
+    // q, k and v tiles by chunk parity: one __shared__ variable each, indexed by the parity,
+    // so the compiler can tell reads of them from the writes into sm
+    __shared__ alignas(16) uint16_t q_buf[2][CH * DK], k_buf[2][CH * DK];
+    __shared__ alignas(16) uint16_t v_buf[2][BV * CH];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int lr = lane & 15;  // row (A) / column (B, C) index inside a 16-tile
     const int lq = lane >> 4;  // quarter: k-offset (A, B) / row group (C)
-    const bool state_wave = wave < 2;
-    const int ct = wave & 1;   // value tile of a state wave
 
     // workgroup -> (sequence, value slice); slices of one sequence share an XCD (and its L2)
     const int nvt = dv / BV;
@@ -357,15 +373,21 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
     auto rows_of = [&](int64_t cc) __attribute__((always_inline)) {
         return static_cast<int>(T - cc * CH < CH ? T - cc * CH : CH);
     };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
 
     // score tiles above the diagonal are read as zeros by the read-out and never written
     for (int i = tid; i < 2 * CH * L::CP; i += NW * 64) (&sm.p[0][0])[i] = 0;
+    block_sync();
 
-    // The two roles run separate loops with the same barriers: two in the prologue (chunk 0
-    // loaded; chunk 0 scanned), then one per step c = -1 .. nchunks-1, where step -1 prepares
-    // chunk 0 and forms K M, M^T Q^T of chunk 0.
-    if (state_wave) {
-        // ---- state slice: C layout of 16x16 tiles, feature tile ft ----------------------------
+    // Every role runs steps c = -2 .. nchunks-1 with one barrier each.  In step c the state
+    // waves process chunk c and form K M, M^T Q^T of chunk c+1; the prep waves build the
+    // Gram/score tiles and block inverses of chunk c+1; the loader brings q, k, v of chunk
+    // c+2 into LDS and scans it; the stager writes k~ of chunk c+2.
+
+    if (wave < 2) {
+        // ---- state waves -----------------------------------------------------------------------
+        const int ct = wave;  // value tile
         v4f M[NFT], KM[NBLK], Z[NBLK];
         v4s VT[NBLK];  // v tile of the next chunk (C layout of this wave's 16 columns)
 #pragma unroll
@@ -375,7 +397,6 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                 const int row = 16 * ft + 4 * lq + i, col = j0 + VW * ct + lr;
                 M[ft][i] = S0 ? S0[(bh * DK + row) * dv + col] : 0.f;
             }
-        if (nchunks > 0) block_sync();
 
         // K M and M^T Q^T of the next chunk from the current state, and its v tile, from the
         // q/k/v buffers qn/kn/vn
@@ -406,79 +427,94 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
             }
         };
 
-        int sl = 2;  // c mod 3
-        for (int64_t c = -1; c < nchunks; ++c) {
+        int sl = 1;  // c mod 3
+        for (int64_t c = -2; c < nchunks; ++c) {
             if (c >= 0) {
                 // ---- chunk c: R, U, read-out, carry --------------------------------------------
                 const int b = static_cast<int>(c & 1);
                 const int n = rows_of(c);
                 const int64_t row0 = seq0 + c * CH;
-                // R = beta (V - gam (K M)), then U by block forward substitution
+                // operands that do not depend on the chain, read first
                 v4s dA[NBLK], aN[NOFF];
+                v4f bt4[NBLK], gm4[NBLK], w4[NBLK];
+                float gtok[NBLK];
 #pragma unroll
-                for (int rt = 0; rt < NBLK; ++rt)
+                for (int rt = 0; rt < NBLK; ++rt) {
                     dA[rt] = ld4s(&sm.dinv[b][rt * 16 * L::DP + lr * L::DP + 4 * lq]);
+                    bt4[rt] = ld4(&sm.beta[sl][16 * rt + 4 * lq]);
+                    gm4[rt] = ld4(&sm.gam[sl][16 * rt + 4 * lq]);
+                    w4[rt] = ld4(&sm.w[sl][16 * rt + 4 * lq]);
+                    gtok[rt] = sm.gam[sl][16 * rt + lr];
+                }
 #pragma unroll
                 for (int u = 0; u < NOFF; ++u)
                     aN[u] = ld4s(&sm.aneg[b][u * 16 * L::DP + lr * L::DP + 4 * lq]);
-                v4f U[NBLK];
+                const float gC = sm.gam[sl][CH - 1];
+                // P^T fragments (B operand of the read-out): rows 16rt+lr, chunk rows 32s+8lq..
+                v8s pf[NBLK][2];
 #pragma unroll
-                for (int i = 0; i < NBLK; ++i) {
-                    const v4f bt4 = ld4(&sm.beta[sl][16 * i + 4 * lq]);
-                    const v4f gm4 = ld4(&sm.gam[sl][16 * i + 4 * lq]);
+                for (int rt = 0; rt < NBLK; ++rt)
+#pragma unroll
+                    for (int s = 0; s <= rt / 2; ++s)
+                        pf[rt][s] = ld8(&sm.p[b][(16 * rt + lr) * L::CP + 32 * s + 8 * lq]);
+                // K~^T fragments of the carry by transposing reads of row-major K~
+                const uint16_t *ktc = sm.kt[sl];
+                auto kt_frag = [&](int ft, int s) __attribute__((always_inline)) {
+                    const uint16_t *base =
+                        &ktc[(32 * s + 8 * lq + (lr >> 2)) * L::KP + 16 * ft + 4 * (lr & 3)];
+                    return cat8(ld_tr(base), ld_tr(base + 4 * L::KP));
+                };
+                // R = beta (V - gam (K M)) and U by block forward substitution; after U_0, U_1 the
+                // first k-step of the carry and of the read-out can run beside U_2, U_3
+                v4f U[NBLK];
+                auto solve = [&](int i) __attribute__((always_inline)) {
                     v4f Y;
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        Y[e] = bt4[e] * (__uint_as_float(static_cast<uint32_t>(
-                                             static_cast<uint16_t>(VT[i][e])) << 16) -
-                                         gm4[e] * KM[i][e]);
+                        Y[e] = bt4[i][e] * (__uint_as_float(static_cast<uint32_t>(
+                                                static_cast<uint16_t>(VT[i][e])) << 16) -
+                                            gm4[i][e] * KM[i][e]);
 #pragma unroll
                     for (int kb = 0; kb < i; ++kb)
                         Y = mfma16(aN[(i * (i - 1)) / 2 + kb], pack4(U[kb]), Y);
                     U[i] = mfma16(dA[i], pack4(Y), zero4());
-                }
-                // U and w U as fragments over the chunk rows
-                v8s ub[2], uwb[2];
+                };
+                solve(0);
+                solve(1);
+                const v8s ub0 = c_to_frag(U[0], U[1]);
+                const v8s uwb0 = c_to_frag(w4[0] * U[0], w4[1] * U[1]);
+                v4f acc[NFT], oacc[NBLK];
 #pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const v4f w0 = ld4(&sm.w[sl][32 * s + 4 * lq]);
-                    const v4f w1 = ld4(&sm.w[sl][32 * s + 16 + 4 * lq]);
-                    ub[s] = c_to_frag(U[2 * s], U[2 * s + 1]);
-                    uwb[s] = c_to_frag(w0 * U[2 * s], w1 * U[2 * s + 1]);
-                }
-                // read-out O^T = (M^T Q^T) diag(gam) + U^T P^T: lane holds O[16rt+lr][4 columns]
+                for (int ft = 0; ft < NFT; ++ft) acc[ft] = mfma32(kt_frag(ft, 0), uwb0, gC * M[ft]);
+#pragma unroll
+                for (int rt = 0; rt < NBLK; ++rt) oacc[rt] = mfma32(ub0, pf[rt][0], gtok[rt] * Z[rt]);
+                solve(2);
+                solve(3);
+                const v8s ub1 = c_to_frag(U[2], U[3]);
+                const v8s uwb1 = c_to_frag(w4[2] * U[2], w4[3] * U[3]);
+#pragma unroll
+                for (int ft = 0; ft < NFT; ++ft) M[ft] = mfma32(kt_frag(ft, 1), uwb1, acc[ft]);
+                // read-out O^T = (M^T Q^T) diag(gam) + U^T P^T: lane holds O[16rt+lr][4 columns];
+                // rows past the chunk's last valid row fall outside the buffer range and are
+                // dropped by the store
+                const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+                    o + row0 * dv, 0, n * dv * 2, 0x00020000);
 #pragma unroll
                 for (int rt = 0; rt < NBLK; ++rt) {
-                    const int r = 16 * rt + lr;
-                    v4f acc = sm.gam[sl][r] * Z[rt];
-#pragma unroll
-                    for (int s = 0; s <= rt / 2; ++s)
-                        acc = mfma32(ub[s], ld8(&sm.p[b][r * L::CP + 32 * s + 8 * lq]), acc);
-                    if (r < n)
-                        *reinterpret_cast<uint2 *>(o + (row0 + r) * dv + j0 + VW * ct + 4 * lq) =
-                            pack4u(acc);
-                }
-                // carry: M <- gam_C M + K~^T (w U); A = K~^T by transposing reads of row-major K~
-                const float gC = sm.gam[sl][CH - 1];
-#pragma unroll
-                for (int ft = 0; ft < NFT; ++ft) {
-                    v4f acc = gC * M[ft];
-#pragma unroll
-                    for (int s = 0; s < 2; ++s) {
-                        const uint16_t *base =
-                            &sm.kt[b][(32 * s + 8 * lq + (lr >> 2)) * L::KP + 16 * ft + 4 * (lr & 3)];
-                        acc = mfma32(cat8(ld_tr(base), ld_tr(base + 4 * L::KP)), uwb[s], acc);
-                    }
-                    M[ft] = acc;
+                    v4f a = oacc[rt];
+                    if (rt >= 2) a = mfma32(ub1, pf[rt][1], a);
+                    const uint2 pk = pack4u(a);
+                    __builtin_amdgcn_raw_buffer_store_b64(
+                        u32x2{pk.x, pk.y}, orsrc, ((16 * rt + lr) * dv + j0 + VW * ct + 4 * lq) * 2,
+                        0, 0);
                 }
             }
-            // K M, M^T Q^T and v of chunk c+1 (a branch per buffer parity)
-            if (c + 1 < nchunks) {
-                if ((c + 1) & 1) products(q_buf1, k_buf1, v_buf1);
-                else products(q_buf0, k_buf0, v_buf0);
+            // K M, M^T Q^T and v of chunk c+1
+            if (c + 1 >= 0 && c + 1 < nchunks) {
+                const int p1 = static_cast<int>((c + 1) & 1);
+                products(q_buf[p1], k_buf[p1], v_buf[p1]);
             }
-            wait_global();
-            block_sync();
+            block_sync();  // the read-out stores need not complete before the barrier
             sl = sl == 2 ? 0 : sl + 1;
         }
 
@@ -494,95 +530,164 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
         return;
     }
 
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-
-    // ---- loader wave: q, k, v of chunk c+2 into LDS, and the decay scan of chunk c+2 --------
-    // Issuing the loads stalls while HBM drains them, so a wave with little other work issues
-    // them; the parity of the target buffers is a compile-time constant.
-    if (wave == 4) {
-        auto load_chunk = [&](auto par_c, int64_t cc, int slot) __attribute__((always_inline)) {
-            constexpr int PAR = decltype(par_c)::value;
-            if (cc >= nchunks) return;
-            const int64_t r0 = seq0 + cc * CH;
-            const int n = rows_of(cc);
-            load_qk<DK>(PAR ? q_buf1 : q_buf0, PAR ? k_buf1 : k_buf0, q, k, r0, n, lane);
-            load_v(PAR ? v_buf1 : v_buf0, v, r0, n, dv, j0, lane);
-            const int r = min(lane, n - 1);
-            const float bv = beta[r0 + r];
-            const float av = has_alpha ? alpha[r0 + r] : 1.f;
-            scan_chunk<DK>(sm, slot, bv, av, n, has_alpha, lane);  // slot = cc mod 3
+    if (wave == 6) {
+        // ---- loader wave: q and v of chunk c+2 into LDS, and the decay scan of chunk c+2 ------
+        // Issuing the loads stalls while HBM drains them, so a wave with little other work
+        // issues them; the parity of the target buffers is a compile-time constant.
+        // beta and alpha of the next chunk to scan, one step ahead in registers
+        float nbeta = 0.f, nalpha = 1.f;
+        auto load_ba = [&](int64_t cc) __attribute__((always_inline)) {
+            const int64_t cl = cc < nchunks ? cc : nchunks - 1;
+            const int r = min(lane, rows_of(cl) - 1);
+            nbeta = beta[seq0 + cl * CH + r];
+            nalpha = has_alpha ? alpha[seq0 + cl * CH + r] : 1.f;
         };
-        if (nchunks > 0) {
-            load_chunk(I0{}, 0, 0);
+        if (nchunks > 0) load_ba(0);
+        auto load_step = [&](auto par_c, int64_t cc, int slot) __attribute__((always_inline)) {
+            constexpr int PAR = decltype(par_c)::value;  // cc mod 2
+            if (cc >= 0 && cc < nchunks) {
+                const int64_t r0 = seq0 + cc * CH;
+                const int n = rows_of(cc);
+                load_rows<DK, 0, CH>(q_buf[PAR], q, r0, n, lane);
+                load_v(v_buf[PAR], v, r0, n, dv, j0, lane);
+                scan_chunk<DK>(sm, slot, nbeta, nalpha, n, has_alpha, lane);  // slot = cc mod 3
+                load_ba(cc + 1);
+            }
             wait_global();
             block_sync();
-        }
-        load_chunk(I1{}, 1, 1);  // step -1
-        wait_global();
-        block_sync();
-        int sl = 2;  // (c+2) mod 3
-        for (int64_t c = 0; c < nchunks; c += 2) {
-            load_chunk(I0{}, c + 2, sl);
-            wait_global();
-            block_sync();
-            sl = sl == 2 ? 0 : sl + 1;
+        };
+        int sl2 = 0;  // (c+2) mod 3
+        for (int64_t c = -2; c < nchunks; c += 2) {
+            load_step(I0{}, c + 2, sl2);
+            sl2 = sl2 == 2 ? 0 : sl2 + 1;
             if (c + 1 < nchunks) {
-                load_chunk(I1{}, c + 3, sl);
-                wait_global();
-                block_sync();
-                sl = sl == 2 ? 0 : sl + 1;
+                load_step(I1{}, c + 3, sl2);
+                sl2 = sl2 == 2 ? 0 : sl2 + 1;
             }
         }
         return;
     }
 
-    // ---- prep waves ----------------------------------------------------------------------------
-    const int pw = wave - 2;
-    PrepRegs<DK, TD> pr;  // d of chunk c+1 at the start of step c
+    if (wave == 4 || wave == 5) {
+        // ---- stager waves: k rows of chunk c+2 into LDS, then k~ = d (.) k of chunk c+2 -------
+        // Stager h owns row blocks 2h, 2h+1.  d is loaded into registers one step before it is
+        // used, block by block as soon as the block's registers are free (lane (q, n) holds
+        // row 16 kb + n, features 32 s + 8 q .. +7).
+        constexpr int DU = sizeof(TD) * 8 / 16;  // uint4 per 8 values of d
+        uint4 dreg[2][NS][DU];
+        auto stager = [&](auto h_c) __attribute__((always_inline)) {
+            constexpr int H = decltype(h_c)::value;
+            auto load_dblock = [&](int64_t cc, int j) __attribute__((always_inline)) {
+                const int64_t row = seq0 + cc * CH + min(16 * (2 * H + j) + lr, rows_of(cc) - 1);
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    const uint4 *src = reinterpret_cast<const uint4 *>(d + row * DK + 32 * s + 8 * lq);
+#pragma unroll
+                    for (int e = 0; e < DU; ++e) dreg[j][s][e] = src[e];
+                }
+            };
+            if (nchunks > 0) {
+                load_dblock(0, 0);
+                load_dblock(0, 1);
+            }
+            auto stage_step = [&](auto par_c, int64_t cc, int slot) __attribute__((always_inline)) {
+                constexpr int PAR = decltype(par_c)::value;  // cc mod 2
+                if (cc < nchunks) {
+                    load_rows<DK, 32 * H, 32>(k_buf[PAR], k, seq0 + cc * CH, rows_of(cc), lane);
+                    wait_global();  // this chunk's k rows and d registers
+                    const int64_t cn = cc + 1 < nchunks ? cc + 1 : nchunks - 1;
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const int kb = 2 * H + j;
+                        v8s kr[NS];
+#pragma unroll
+                        for (int s = 0; s < NS; ++s)
+                            kr[s] = ld8(&k_buf[PAR][L::qk_at(16 * kb + lr, 4 * s + lq)]);
+#pragma unroll
+                        for (int s = 0; s < NS; ++s) {
+                            float dd[8];
+                            d_values(dreg[j][s], dd, TD{});
+                            const uint4 xu = __builtin_bit_cast(uint4, kr[s]);
+                            const uint32_t xw[4] = {xu.x, xu.y, xu.z, xu.w};
+                            uint32_t pk[4];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                pk[e] = pack2(dd[2 * e] * bf_lo(xw[e]), dd[2 * e + 1] * bf_hi(xw[e]));
+                            *reinterpret_cast<uint4 *>(&sm.kt[slot][(16 * kb + lr) * L::KP + 32 * s + 8 * lq]) =
+                                make_uint4(pk[0], pk[1], pk[2], pk[3]);
+                        }
+                        load_dblock(cn, j);  // d of chunk c+3 (clamped to the last chunk)
+                    }
+                }
+                block_sync();  // the d loads stay in flight across the barrier
+            };
+            int sl2 = 0;  // (c+2) mod 3
+            for (int64_t c = -2; c < nchunks; c += 2) {
+                stage_step(I0{}, c + 2, sl2);
+                sl2 = sl2 == 2 ? 0 : sl2 + 1;
+                if (c + 1 < nchunks) {
+                    stage_step(I1{}, c + 3, sl2);
+                    sl2 = sl2 == 2 ? 0 : sl2 + 1;
+                }
+            }
+        };
+        if (wave == 4) stager(I0{});
+        else stager(I1{});
+        return;
+    }
 
-    // Prep wave PW in step c: k~, Gram/score tiles and block inverses of chunk c+1; d of chunk
-    // c+2 into registers (clamped to the last chunk); s1 = (c+1) mod 3
+    // ---- prep waves: Gram/score tiles and block inverses of chunk c+1 ----------------------------
+    // Prep wave PW owns the column blocks kblk(PW, 0), kblk(PW, 1); s1 = (c+1) mod 3
     auto prep_step = [&](auto pw_c, int64_t c, int s1) __attribute__((always_inline)) {
         constexpr int PW = decltype(pw_c)::value;
-        const int64_t c1 = c + 1, c2 = c + 2;
-        if (c1 >= nchunks) return;
+        const int64_t c1 = c + 1;
+        if (c1 < 0 || c1 >= nchunks) return;
         const int b1 = static_cast<int>(c1 & 1);
-        const uint16_t *qx = b1 ? q_buf1 : q_buf0;
-        const uint16_t *kx = b1 ? k_buf1 : k_buf0;
-        // k~ of the own blocks: fragments in registers, rows into LDS for the carry (all reads
-        // first: the compiler cannot reorder the k reads across the k~ writes)
-        v8s kt[2][NS];
+        const uint16_t *qx = q_buf[b1];
+        const uint16_t *kx = k_buf[b1];
+        const uint16_t *ktx = sm.kt[s1];
+        // k~, k and q rows of the own blocks (all reads first: the compiler cannot move them
+        // across the LDS writes below)
+        v8s kt[2][NS], kr[2][NS], qd[2][NS];
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int s = 0; s < NS; ++s) kt[j][s] = ld8(&kx[L::qk_at(16 * kblk(PW, j) + lr, 4 * s + lq)]);
+            for (int s = 0; s < NS; ++s) {
+                const int row = 16 * kblk(PW, j) + lr;
+                kt[j][s] = ld8(&ktx[row * L::KP + 32 * s + 8 * lq]);
+                kr[j][s] = ld8(&kx[L::qk_at(row, 4 * s + lq)]);
+                qd[j][s] = ld8(&qx[L::qk_at(row, 4 * s + lq)]);
+            }
+        // diagonal blocks: tile (kb, kb) = K~_kb X_kb^T, the lane holds row r = 16kb+lr,
+        // columns s = 16kb+4lq..+3; exact e^{g_r - g_s} shared by the score tile (s <= r)
+        // and N (s < r); then both block inverses in lockstep
+        v4f na[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int kb = kblk(PW, j);
+            const int r = 16 * kb + lr;
+            v4f sc = zero4(), Gdt = zero4();
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-                const uint4 xu = __builtin_bit_cast(uint4, kt[j][s]);
-                float dd[8];
-                d_values(pr.d[j][s], dd, TD{});
-                const uint32_t xw[4] = {xu.x, xu.y, xu.z, xu.w};
-                uint32_t pk[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    pk[e] = pack2(dd[2 * e] * bf_lo(xw[e]), dd[2 * e + 1] * bf_hi(xw[e]));
-                const uint4 ku = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-                kt[j][s] = __builtin_bit_cast(v8s, ku);
-                *reinterpret_cast<uint4 *>(&sm.kt[b1][(16 * kb + lr) * L::KP + 32 * s + 8 * lq]) = ku;
+                sc = mfma32(kt[j][s], qd[j][s], sc);
+                Gdt = mfma32(kt[j][s], kr[j][s], Gdt);  // G in the A layout: lane holds G[r][s]
             }
+            const float gr = sm.g[s1][r], bt = sm.beta[s1][r];
+            const v4f gs = ld4(&sm.g[s1][16 * kb + 4 * lq]);
+            v4f pv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float ex = __expf(gr - gs[e]);
+                pv[e] = (4 * lq + e <= lr) ? ex * sc[e] : 0.f;
+                na[j][e] = (4 * lq + e < lr) ? (bt * ex) * Gdt[e] : 0.f;
+            }
+            *reinterpret_cast<uint2 *>(&sm.p[b1][r * L::CP + 16 * kb + 4 * lq]) = pack4u(pv);
         }
-        {
-            const int64_t cd = c2 < nchunks ? c2 : c1;
-            load_d_frag<DK, TD, PW>(pr, d, seq0 + cd * CH, rows_of(cd), lr, lq);
-        }
-        // tiles (i, kb) = K~_kb X_i^T (X = Q: scores, X = K: Gram), row block by row block;
-        // the lane holds row 16i+lr, columns 16kb+4lq..+3
-        constexpr int IMIN = kblk(PW, 0) < kblk(PW, 1) ? kblk(PW, 0) : kblk(PW, 1);
-        // the fragments of row block i+1 are read before block i is processed
+        diag_inverse2<DK>(sm, b1, kblk(PW, 0), kblk(PW, 1), lr, lq, na);
+        // off-diagonal tiles (i, kb), i > kb, row block by row block; the fragments of the
+        // next row block are read before the current one is processed.  The lane holds row
+        // 16i+lr, columns 16kb+4lq..+3; e^{g_r - g_s} = ea[r] cik eb[s], each factor <= 1.
+        constexpr int IMIN = (kblk(PW, 0) < kblk(PW, 1) ? kblk(PW, 0) : kblk(PW, 1)) + 1;
         v8s kf[NS], qf[NS], kf_n[NS], qf_n[NS];
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
@@ -604,72 +709,43 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                 }
             }
             const int r = 16 * i + lr;
+            const float ear = sm.ea[s1][r], nbr = -sm.beta[s1][r];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int kb = kblk(PW, j);
-                if (kb > i) continue;
-                v4f sc = zero4();
+                if (kb >= i) continue;
+                v4f sc = zero4(), gm = zero4();
 #pragma unroll
-                for (int s = 0; s < NS; ++s) sc = mfma32(kt[j][s], qf[s], sc);
-                if (i > kb) {
-                    // off-diagonal: e^{g_r - g_s} = ea[r] cik eb[s], each factor <= 1
-                    const int t = (i * (i - 1)) / 2 + kb;
-                    const float rowf = sm.ea[s1][r] * sm.cik[s1][t];
-                    const v4f eb4 = ld4(&sm.eb[s1][16 * kb + 4 * lq]);
-                    v4f gm = zero4();
-#pragma unroll
-                    for (int s = 0; s < NS; ++s) gm = mfma32(kt[j][s], kf[s], gm);
-                    const float growf = -sm.beta[s1][r] * rowf;
-                    v4f pv, av;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        pv[e] = (sc[e] * rowf) * eb4[e];
-                        av[e] = (gm[e] * growf) * eb4[e];
-                    }
-                    *reinterpret_cast<uint2 *>(&sm.p[b1][r * L::CP + 16 * kb + 4 * lq]) = pack4u(pv);
-                    *reinterpret_cast<uint2 *>(&sm.aneg[b1][t * 16 * L::DP + lr * L::DP + 4 * lq]) =
-                        pack4u(av);
-                } else {
-                    // diagonal block: exact e^{g_r - g_s} (r = 16kb+lr, s = 16kb+4lq+e), shared
-                    // by the score tile (s <= r) and N (s < r)
-                    const float gr = sm.g[s1][r], bt = sm.beta[s1][r];
-                    const v4f gs = ld4(&sm.g[s1][16 * kb + 4 * lq]);
-                    v4f Gdt = zero4();  // G in the A layout: lane holds G[r][s]
-#pragma unroll
-                    for (int s = 0; s < NS; ++s) Gdt = mfma32(kt[j][s], kf[s], Gdt);
-                    v4f pv, na;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float ex = __expf(gr - gs[e]);
-                        pv[e] = (4 * lq + e <= lr) ? ex * sc[e] : 0.f;
-                        na[e] = (4 * lq + e < lr) ? (bt * ex) * Gdt[e] : 0.f;
-                    }
-                    *reinterpret_cast<uint2 *>(&sm.p[b1][r * L::CP + 16 * kb + 4 * lq]) = pack4u(pv);
-                    diag_inverse<DK>(sm, b1, kb, lr, lq, na);
+                for (int s = 0; s < NS; ++s) {
+                    sc = mfma32(kt[j][s], qf[s], sc);
+                    gm = mfma32(kt[j][s], kf[s], gm);
                 }
+                const int t = (i * (i - 1)) / 2 + kb;
+                const float rowf = ear * sm.cik[s1][t];
+                const float growf = nbr * rowf;
+                const v4f eb4 = ld4(&sm.eb[s1][16 * kb + 4 * lq]);
+                v4f pv, av;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    pv[e] = (sc[e] * rowf) * eb4[e];
+                    av[e] = (gm[e] * growf) * eb4[e];
+                }
+                *reinterpret_cast<uint2 *>(&sm.p[b1][r * L::CP + 16 * kb + 4 * lq]) = pack4u(pv);
+                *reinterpret_cast<uint2 *>(&sm.aneg[b1][t * 16 * L::DP + lr * L::DP + 4 * lq]) =
+                    pack4u(av);
             }
         }
     };
-
-    if (nchunks > 0) {
-        // prologue: d of chunk 0
-        if (pw == 0) load_d_frag<DK, TD, 0>(pr, d, seq0, rows_of(0), lr, lq);
-        else load_d_frag<DK, TD, 1>(pr, d, seq0, rows_of(0), lr, lq);
-        wait_global();
-        block_sync();
-    }
     // one loop per prep wave, so its registers need no merging between the two variants
     auto prep_loop = [&](auto pw_c) __attribute__((always_inline)) {
-        int sl1 = 0;  // (c+1) mod 3
-        for (int64_t c = -1; c < nchunks; ++c) {
-            const int sl2 = sl1 == 2 ? 0 : sl1 + 1;
+        int sl1 = 2;  // (c+1) mod 3
+        for (int64_t c = -2; c < nchunks; ++c) {
             prep_step(pw_c, c, sl1);
-            wait_global();
             block_sync();
-            sl1 = sl2;
+            sl1 = sl1 == 2 ? 0 : sl1 + 1;
         }
     };
-    if (pw == 0) prep_loop(I0{});
+    if (wave == 2) prep_loop(I0{});
     else prep_loop(I1{});
 }
 

@@ -140,3 +140,25 @@ def test_nonfinite_inputs_propagate(qkv):
     o, S = gpu_chunk(x, qkv=qkv)
     assert np.isfinite(o[0, 0, :64]).all()
     assert np.isnan(o[0, 0, 70:]).any() and np.isnan(S).any()
+
+
+@pytest.mark.parametrize("qkv", ["bf16", "f32"])
+def test_outputs_stay_in_bounds(qkv):
+    """Rows past a ragged tail are never written: o is the head of a larger buffer whose
+    remainder holds a sentinel, and the last sequence ends mid-chunk."""
+    torch, dev = torch_dev()
+    B, H, T, dk, dv = 2, 3, 70, 128, 128
+    x = synth.make_shape(B, H, T, dk, dv, qkv=qkv, alpha=True, s0=True, seed=5)
+    say("chunk_fwd bounds", qkv, B, H, T, dk, dv)
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16}[qkv]
+    n = B * H * T * dv
+    guard = 64 * dv * 4
+    buf = torch.full((n + guard,), 7.0, dtype=dt, device=dev)
+    o = buf[:n].view(B, H, T, dv)
+    osdn.osdn_chunk_fwd(to_dev(x["q"], qkv), to_dev(x["k"], qkv), to_dev(x["v"], qkv),
+                        to_dev(x["beta"], "f32"), to_dev(x["d"], "f32"),
+                        to_dev(x["alpha"], "f32"), to_dev(x["S0"], "f32"), o=o)
+    torch.cuda.synchronize()
+    assert bool(torch.all(buf[n:] == 7.0)), "write past the end of o"
+    o_ref, _ = oracle.chunk_fwd(*oracle_inputs(x))
+    assert rel_err(to_np(o), o_ref) <= TOL[qkv]
