@@ -145,16 +145,31 @@ __device__ __forceinline__ void wait_global8() {
 
 template <int DK>
 struct alignas(16) Lds {
-    static constexpr int KU = DK / 8;   // 16-byte units per q/k row
-    static constexpr int KP = DK + 8;   // row pitch (bf16) of k~
+    static constexpr int KU = DK / 8;   // 16-byte units per q/k/k~ row
+    static constexpr int KP = DK;       // row pitch (bf16) of k~
     static constexpr int CP = CH + 8;   // row pitch (bf16) of P
     static constexpr int DP = 16;       // row pitch (bf16) of 16x16 blocks
-    // element offset of logical 16-byte unit u of row r in a swizzled q/k tile
-    __device__ static constexpr int qk_at(int r, int u) { return (r * KU + (u ^ (r & 7))) * 8; }
-    alignas(16) uint16_t kt[3][CH * KP];            // [chunk mod 3] k~, row-major
+    // Swizzles, so that the access patterns below touch each of the 64 four-byte LDS banks at
+    // most once per cycle (16 lanes of a 16-byte access, 32 lanes of an 8-byte access):
+    // * q/k tiles: 16-byte unit u of row r sits at unit u ^ fqk(r); fragment reads take one
+    //   unit from each of 16 consecutive rows.
+    __device__ static constexpr int fqk(int r) { return DK == 128 ? (r & 15) : ((r >> 1) & 7); }
+    __device__ static constexpr int qk_at(int r, int u) { return (r * KU + (u ^ fqk(r))) * 8; }
+    // * k~: 8-byte granule g of row r sits at granule g ^ 2 pk(r), pk a bit permutation of the
+    //   row index, so that both 16-byte reads of 16 consecutive rows and the transposing reads
+    //   (four granules of rows k0..k0+3 and k0+8..k0+11) are spread over all banks.
+    __device__ static constexpr int pk(int r) {
+        return DK == 128 ? (((r & 3) << 2) | (((r >> 3) & 1) << 1) | ((r >> 2) & 1))
+                         : ((((r >> 1) & 1) << 2) | (((r >> 3) & 1) << 1) | ((r >> 2) & 1));
+    }
+    __device__ static constexpr int kt_gr(int r, int g) { return r * KP + 4 * (g ^ (2 * pk(r))); }
+    __device__ static constexpr int kt_at(int r, int u) { return kt_gr(r, 2 * u); }
+    // * 16x16 blocks (pitch 16): granule g of row r at g ^ 2 ((r >> 3) & 1)
+    __device__ static constexpr int blk(int r, int g) { return r * DP + 4 * (g ^ (((r >> 3) & 1) << 1)); }
+    alignas(16) uint16_t kt[3][CH * KP];            // [chunk mod 3] k~, rows swizzled by kt_gr
     alignas(16) uint16_t p[2][CH * CP];             // [chunk parity] P, row-major
-    alignas(16) uint16_t dinv[2][NBLK * 16 * DP];   // D_i = (I + A_ii)^{-1}, row-major
-    alignas(16) uint16_t aneg[2][NOFF * 16 * DP];   // -A_ik (i > k), row-major
+    alignas(16) uint16_t dinv[2][NBLK * 16 * DP];   // D_i = (I + A_ii)^{-1}, rows by blk
+    alignas(16) uint16_t aneg[2][NOFF * 16 * DP];   // -A_ik (i > k), rows by blk
     alignas(16) float beta[3][CH];                  // [chunk mod 3] scan outputs
     alignas(16) float g[3][CH];
     alignas(16) float gam[3][CH];
@@ -165,7 +180,7 @@ struct alignas(16) Lds {
     alignas(16) float ea[3][CH];
     alignas(16) float eb[3][CH];
     alignas(16) float cik[3][8];
-    alignas(16) uint16_t ntile[NBLK][16 * 16];  // N of diagonal block kb, row-major (prep)
+    alignas(16) uint16_t ntile[NBLK][16 * 16];  // N of diagonal block kb, rows by blk (prep)
 };
 
 // Prep wave pw owns the Gram/score column blocks kblk(pw, 0), kblk(pw, 1)
@@ -197,7 +212,7 @@ __device__ __forceinline__ void load_rows(uint16_t *dst, const uint16_t *src, in
 #pragma unroll
     for (int i = 0; i < NLOAD; ++i) {
         const int base = R0 * L::KU + i * 64;  // physical unit of lane 0
-        const int pu = base + lane, r = pu / L::KU, lu = (pu % L::KU) ^ (r & 7);
+        const int pu = base + lane, r = pu / L::KU, lu = (pu % L::KU) ^ L::fqk(r);
         load_to_lds16(src + (row0 + min(r, n - 1)) * DK + 8 * lu, dst + 8 * base);
         if (i % 8 == 7 && i + 1 < NLOAD) wait_global8();
     }
@@ -277,12 +292,12 @@ __device__ __forceinline__ void diag_inverse2(Lds<DK> &sm, int b, int kb0, int k
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const uint2 u = pack4u(na[j]);
-        *reinterpret_cast<uint2 *>(&sm.ntile[kb[j]][lr * 16 + 4 * lq]) = u;
+        *reinterpret_cast<uint2 *>(&sm.ntile[kb[j]][L::blk(lr, lq)]) = u;
         Na[j] = __builtin_bit_cast(v4s, u);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-        Nb[j] = ld_tr(&sm.ntile[kb[j]][(4 * lq + (lr >> 2)) * 16 + 4 * (lr & 3)]);
+        Nb[j] = ld_tr(&sm.ntile[kb[j]][L::blk(4 * lq + (lr >> 2), lr & 3)]);
     // squares in both layouts: X^2 (C = B layout) = X X;  (X^2)^T (C = A layout) = X^T X^T
     v4f X[2], Xt[2];
 #pragma unroll
@@ -327,7 +342,7 @@ __device__ __forceinline__ void diag_inverse2(Lds<DK> &sm, int b, int kb0, int k
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-        *reinterpret_cast<uint2 *>(&sm.dinv[b][kb[j] * 16 * L::DP + lr * L::DP + 4 * lq]) =
+        *reinterpret_cast<uint2 *>(&sm.dinv[b][kb[j] * 16 * L::DP + L::blk(lr, lq)]) =
             pack4u(Y[j]);
 }
 
@@ -440,7 +455,7 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                 float gtok[NBLK];
 #pragma unroll
                 for (int rt = 0; rt < NBLK; ++rt) {
-                    dA[rt] = ld4s(&sm.dinv[b][rt * 16 * L::DP + lr * L::DP + 4 * lq]);
+                    dA[rt] = ld4s(&sm.dinv[b][rt * 16 * L::DP + L::blk(lr, lq)]);
                     bt4[rt] = ld4(&sm.beta[sl][16 * rt + 4 * lq]);
                     gm4[rt] = ld4(&sm.gam[sl][16 * rt + 4 * lq]);
                     w4[rt] = ld4(&sm.w[sl][16 * rt + 4 * lq]);
@@ -448,7 +463,7 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                 }
 #pragma unroll
                 for (int u = 0; u < NOFF; ++u)
-                    aN[u] = ld4s(&sm.aneg[b][u * 16 * L::DP + lr * L::DP + 4 * lq]);
+                    aN[u] = ld4s(&sm.aneg[b][u * 16 * L::DP + L::blk(lr, lq)]);
                 const float gC = sm.gam[sl][CH - 1];
                 // P^T fragments (B operand of the read-out): rows 16rt+lr, chunk rows 32s+8lq..
                 v8s pf[NBLK][2];
@@ -460,9 +475,8 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                 // K~^T fragments of the carry by transposing reads of row-major K~
                 const uint16_t *ktc = sm.kt[sl];
                 auto kt_frag = [&](int ft, int s) __attribute__((always_inline)) {
-                    const uint16_t *base =
-                        &ktc[(32 * s + 8 * lq + (lr >> 2)) * L::KP + 16 * ft + 4 * (lr & 3)];
-                    return cat8(ld_tr(base), ld_tr(base + 4 * L::KP));
+                    const int r = 32 * s + 8 * lq + (lr >> 2), g = 4 * ft + (lr & 3);
+                    return cat8(ld_tr(&ktc[L::kt_gr(r, g)]), ld_tr(&ktc[L::kt_gr(r + 4, g)]));
                 };
                 // R = beta (V - gam (K M)) and U by block forward substitution; after U_0, U_1 the
                 // first k-step of the carry and of the read-out can run beside U_2, U_3
@@ -613,7 +627,7 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
 #pragma unroll
                             for (int e = 0; e < 4; ++e)
                                 pk[e] = pack2(dd[2 * e] * bf_lo(xw[e]), dd[2 * e + 1] * bf_hi(xw[e]));
-                            *reinterpret_cast<uint4 *>(&sm.kt[slot][(16 * kb + lr) * L::KP + 32 * s + 8 * lq]) =
+                            *reinterpret_cast<uint4 *>(&sm.kt[slot][L::kt_at(16 * kb + lr, 4 * s + lq)]) =
                                 make_uint4(pk[0], pk[1], pk[2], pk[3]);
                         }
                         load_dblock(cn, j);  // d of chunk c+3 (clamped to the last chunk)
@@ -654,7 +668,7 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
                 const int row = 16 * kblk(PW, j) + lr;
-                kt[j][s] = ld8(&ktx[row * L::KP + 32 * s + 8 * lq]);
+                kt[j][s] = ld8(&ktx[L::kt_at(row, 4 * s + lq)]);
                 kr[j][s] = ld8(&kx[L::qk_at(row, 4 * s + lq)]);
                 qd[j][s] = ld8(&qx[L::qk_at(row, 4 * s + lq)]);
             }
@@ -731,7 +745,7 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                     av[e] = (gm[e] * growf) * eb4[e];
                 }
                 *reinterpret_cast<uint2 *>(&sm.p[b1][r * L::CP + 16 * kb + 4 * lq]) = pack4u(pv);
-                *reinterpret_cast<uint2 *>(&sm.aneg[b1][t * 16 * L::DP + lr * L::DP + 4 * lq]) =
+                *reinterpret_cast<uint2 *>(&sm.aneg[b1][t * 16 * L::DP + L::blk(lr, lq)]) =
                     pack4u(av);
             }
         }
