@@ -9,6 +9,10 @@ does, and shares no code with it.
 technical summary, sections 1 and 2.1; gated form from Erase-then-Delta Attention,
 section 2.2, eq. 4).  ``step`` is the same loop body for one token.  State is stored as
 M = S^T, [B, H, dk, dv].
+
+``precond`` (numpy, float64) is the Phase-1 preconditioner scan that produces the d_t sequence
+(same summary, sections 2.2 and 2.3); ``chunkwise`` holds float64 models of the chunk forms
+of both recurrences, checked against the token loops.
 """
 from __future__ import annotations
 

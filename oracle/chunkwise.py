@@ -60,3 +60,51 @@ def chunk_fwd(q, k, v, beta, d, alpha=None, S0=None, chunk: int = 64
                 M = gam[-1] * M + (np.exp(g[-1] - g)[:, None] * Kt).T @ U
             S_T[b, h] = M
     return o, S_T
+
+
+def precond_scan(k, beta, eta: float, r=None, d1=None, chunk: int = 64
+                 ) -> Tuple[np.ndarray, np.ndarray]:
+    """Same contract as ``oracle.precond.precond_scan``; evaluates the chunk form of the
+    Phase-1 preconditioner recurrence (OSDN summary, sections 2.2 and 2.3), derived here.
+
+    The token step  d_{t+1} = r_t d_t + c_t e_t x_t,  x_t = k_t^2,  c_t = eta b_t / ||k_t||^2
+    (0 for a zero key),  e_t = 1 - b_t <d_t, x_t>,  is affine in d.  Over one chunk of rows
+    j = 0..C-1 starting from d0, with rho_j = prod_{i<j} r_i and R[j,i] = rho_j / rho_{i+1}:
+        d_j = rho_j d0 + sum_{i<j} R[j,i] c_i e_i x_i,
+    and substituting d_j into e_j gives the unit lower-triangular system
+        (I + L) e = 1 - b . rho . (X d0),   L[j,i] = b_j R[j,i] c_i <x_j, x_i>   (i < j),
+    after which  D = rho d0^T + W X  with  W[j,i] = R[j,i] c_i e_i  (i < j), and the state
+    carried to the next chunk is  rho_C d0 + sum_i R[C,i] c_i e_i x_i .
+    """
+    k = np.asarray(k, dtype=np.float64)
+    beta = np.asarray(beta, dtype=np.float64)
+    B, H, T, dk = k.shape
+    out = np.zeros((B, H, T, dk))
+    d_next = np.zeros((B, H, dk))
+    for b in range(B):
+        for h in range(H):
+            d0 = np.ones(dk) if d1 is None else np.array(d1[b, h], dtype=np.float64)
+            for c0 in range(0, T, chunk):
+                c1 = min(c0 + chunk, T)
+                n = c1 - c0
+                X = k[b, h, c0:c1] ** 2
+                nrm = X.sum(axis=1)
+                bet = beta[b, h, c0:c1]
+                c = np.divide(eta * bet, nrm, out=np.zeros(n), where=nrm > 0)
+                rr = np.ones(n) if r is None else np.asarray(r[b, h, c0:c1], dtype=np.float64)
+                # R[j, i] = prod_{i < m < j} r_m for rows j = 0..n (row n is the chunk end)
+                R = np.zeros((n + 1, n))
+                for j in range(n + 1):
+                    for i in range(min(j, n)):
+                        R[j, i] = np.prod(rr[i + 1:j])
+                rho = np.array([np.prod(rr[:j]) for j in range(n + 1)])
+                L = np.tril(bet[:, None] * R[:n] * c[None, :] * (X @ X.T), -1)
+                rhs = 1.0 - bet * rho[:n] * (X @ d0)
+                e = solve_triangular(np.eye(n) + L, rhs, lower=True, unit_diagonal=True)
+                W = R * (c * e)[None, :]
+                W[:n] = np.tril(W[:n], -1)
+                Dall = rho[:, None] * d0[None, :] + W @ X
+                out[b, h, c0:c1] = Dall[:n]
+                d0 = Dall[n]
+            d_next[b, h] = d0
+    return out, d_next
