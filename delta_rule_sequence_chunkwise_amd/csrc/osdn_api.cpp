@@ -149,4 +149,80 @@ osdn_status osdn_step(const void *q, const void *k, const void *v, const float *
     return err == hipSuccess ? OSDN_OK : OSDN_ERR_LAUNCH;
 }
 
+osdn_status osdn_precond_scan(const void *k, const float *beta, const float *r,
+                              const float *d1, float eta, void *d, float *d_next, int64_t B,
+                              int64_t H, int64_t T, int32_t dk, int32_t chunk,
+                              osdn_dtype k_dtype, osdn_dtype d_dtype, void *stream) {
+    if (B < 0 || H < 0 || T < 0) return OSDN_ERR_SHAPE;
+    if (!dtype_ok(k_dtype) || !dtype_ok(d_dtype)) return OSDN_ERR_UNSUPPORTED;
+    if (!head_dim_ok(dk)) return OSDN_ERR_UNSUPPORTED;
+    if (chunk != 1 && !(chunk == 64 && k_dtype == OSDN_BF16)) return OSDN_ERR_UNSUPPORTED;
+
+    int64_t BH = 1, tok = 1, nk = 1, st = 1;
+    if (!mul_ok(BH, B, kMaxElems) || !mul_ok(BH, H, kMaxElems)) return OSDN_ERR_SHAPE;
+    tok = BH;
+    if (!mul_ok(tok, T, kMaxElems)) return OSDN_ERR_SHAPE;
+    nk = tok;
+    if (!mul_ok(nk, dk, kMaxElems)) return OSDN_ERR_SHAPE;
+    st = BH;
+    if (!mul_ok(st, dk, kMaxElems)) return OSDN_ERR_SHAPE;
+    if (BH > int64_t(0x7fffffff)) return OSDN_ERR_SHAPE;  // one workgroup per sequence
+
+    if (BH == 0) return OSDN_OK;
+    if (T > 0 && (!k || !beta || !d)) return OSDN_ERR_NULL;
+    if (T == 0 && !d_next) return OSDN_OK;
+
+    const int64_t ek = elem_size(k_dtype), ed = elem_size(d_dtype);
+    if (T > 0) {
+        if (!aligned(k, 16) || !aligned(d, 16) || !aligned(beta, 4) || (r && !aligned(r, 4)))
+            return OSDN_ERR_ALIGN;
+    }
+    if ((d1 && !aligned(d1, 16)) || (d_next && !aligned(d_next, 16))) return OSDN_ERR_ALIGN;
+
+    const int64_t n_tok = T > 0 ? tok : 0;
+    const Range rk = range_of(k, n_tok ? nk * ek : 0), rd = range_of(d, n_tok ? nk * ed : 0);
+    const Range rb = range_of(beta, n_tok * 4), rr = range_of(r, n_tok * 4);
+    const Range r1 = range_of(d1, st * 4), rn = range_of(d_next, st * 4);
+    for (const Range *in : {&rk, &rb, &rr, &r1, &rn})
+        if (overlap(rd, *in)) return OSDN_ERR_ALIAS;
+    for (const Range *in : {&rk, &rb, &rr})
+        if (overlap(rn, *in)) return OSDN_ERR_ALIAS;
+    if (overlap(rn, r1) && rn.lo != r1.lo) return OSDN_ERR_ALIAS;
+
+    osdn::PrecondArgs a{k, beta, r, d1, eta, d, d_next, BH, T, dk, chunk, k_dtype, d_dtype};
+    const hipError_t err = osdn::launch_precond(a, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? OSDN_OK : OSDN_ERR_LAUNCH;
+}
+
+osdn_status osdn_precond_step(const void *k, const float *beta, const float *r, float *dstate,
+                              void *d_out, float eta, int64_t B, int64_t H, int32_t dk,
+                              osdn_dtype k_dtype, osdn_dtype d_dtype, void *stream) {
+    if (B < 0 || H < 0) return OSDN_ERR_SHAPE;
+    if (!dtype_ok(k_dtype) || !dtype_ok(d_dtype)) return OSDN_ERR_UNSUPPORTED;
+    if (!head_dim_ok(dk)) return OSDN_ERR_UNSUPPORTED;
+    int64_t BH = 1;
+    if (!mul_ok(BH, B, kMaxElems) || !mul_ok(BH, H, kMaxElems)) return OSDN_ERR_SHAPE;
+    int64_t st = BH;
+    if (!mul_ok(st, dk, kMaxElems)) return OSDN_ERR_SHAPE;
+    if (BH > int64_t(0x7fffffff)) return OSDN_ERR_SHAPE;
+    if (BH == 0) return OSDN_OK;
+    if (!k || !beta || !dstate) return OSDN_ERR_NULL;
+    if (!aligned(k, 16) || !aligned(dstate, 16) || (d_out && !aligned(d_out, 16)) ||
+        !aligned(beta, 4) || (r && !aligned(r, 4)))
+        return OSDN_ERR_ALIGN;
+
+    const int64_t ek = elem_size(k_dtype), ed = elem_size(d_dtype);
+    const Range rk = range_of(k, st * ek), rb = range_of(beta, BH * 4), rr = range_of(r, BH * 4);
+    const Range rs = range_of(dstate, st * 4), ro = range_of(d_out, st * ed);
+    for (const Range *in : {&rk, &rb, &rr, &rs})
+        if (overlap(ro, *in)) return OSDN_ERR_ALIAS;
+    for (const Range *in : {&rk, &rb, &rr})
+        if (overlap(rs, *in)) return OSDN_ERR_ALIAS;
+
+    // one token of the serial scan, reading and writing the state in place
+    osdn::PrecondArgs a{k, beta, r, dstate, eta, d_out, dstate, BH, 1, dk, 1, k_dtype, d_dtype};
+    const hipError_t err = osdn::launch_precond(a, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? OSDN_OK : OSDN_ERR_LAUNCH;
+}
+
 }  // extern "C"

@@ -52,10 +52,22 @@ struct StepArgs {
     osdn_dtype qkv, d_dtype;
 };
 
+struct PrecondArgs {
+    const void *k;
+    const float *beta, *r, *d1;
+    float eta;
+    void *d;          // [BH, T, dk] output, may be NULL for the serial kernel only
+    float *d_next;
+    int64_t BH, T;
+    int32_t dk, chunk;  // chunk 1: token-serial kernel; 64: chunked kernel (bf16 keys)
+    osdn_dtype k_dtype, d_dtype;
+};
+
 // Each launcher enqueues its kernels on `stream` and returns the HIP error of the launch.
 // Arguments were validated by the host layer.
 hipError_t launch_chunk_fwd_f32math(const ChunkArgs &a, hipStream_t stream);
 hipError_t launch_chunk_fwd_mfma(const ChunkArgs &a, hipStream_t stream);
 hipError_t launch_step(const StepArgs &a, hipStream_t stream);
+hipError_t launch_precond(const PrecondArgs &a, hipStream_t stream);
 
 }  // namespace osdn

@@ -1,0 +1,136 @@
+// Device helpers shared by the gfx950 matrix-core kernels of libosdn: bf16 MFMA operands and
+// products, LDS access forms (including the transposing read), global-to-LDS copies, wait and
+// barrier forms, and cross-lane sums.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "osdn_internal.h"
+
+namespace osdn {
+
+typedef short v8s __attribute__((__vector_size__(8 * sizeof(short))));
+typedef short v4s __attribute__((__vector_size__(4 * sizeof(short))));
+typedef float v4f __attribute__((__vector_size__(4 * sizeof(float))));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
+
+__device__ __forceinline__ v4f mfma32(v8s a, v8s b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ v4f mfma16(v4s a, v4s b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ uint32_t pack2(float a, float b) {  // one v_cvt_pk_bf16_f32
+    bf16x2_t r = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ uint2 pack4u(v4f x) {
+    return make_uint2(pack2(x[0], x[1]), pack2(x[2], x[3]));
+}
+__device__ __forceinline__ v4s pack4(v4f x) { return __builtin_bit_cast(v4s, pack4u(x)); }
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ v4f zero4() { return v4f{0.f, 0.f, 0.f, 0.f}; }
+__device__ __forceinline__ v4f ld4(const float *p) {  // 16-byte aligned LDS read
+    return *reinterpret_cast<const v4f *>(p);
+}
+__device__ __forceinline__ v8s ld8(const uint16_t *p) {  // 16-byte aligned LDS read
+    return *reinterpret_cast<const v8s *>(p);
+}
+__device__ __forceinline__ v4s ld4s(const uint16_t *p) {  // 8-byte aligned LDS read
+    return *reinterpret_cast<const v4s *>(p);
+}
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each 16-lane group, lane j addresses 8
+// bytes (four bf16); lane i receives element i%4 of the four addressed by lane 4e + i/4, for
+// e = 0..3.  With a row-major matrix X and lane j addressing X[k0 + j/4][n0 + 4(j%4)], lane i
+// receives X[k0 + e][n0 + i], e = 0..3.
+__device__ __forceinline__ v4s ld_tr(const uint16_t *p) {
+    return __builtin_bit_cast(
+        v4s, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)(p)));
+}
+__device__ __forceinline__ v8s cat8(v4s lo, v4s hi) {
+    return v8s{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+// Two 16x16 fp32 tiles in C layout (lane (q, n) holds rows 4q..4q+3 of column n; x0 is rows
+// 0..15 of a 32-row pair, x1 rows 16..31) -> one bf16 fragment in which lane (q, n) holds
+// rows 8q..8q+7 of column n.  permlane32_swap(a, b) returns (a.r0 a.r1 b.r0 b.r1) and
+// (a.r2 a.r3 b.r2 b.r3), permlane16_swap(a, b) returns (a.r0 b.r0 a.r2 b.r2) and
+// (a.r1 b.r1 a.r3 b.r3), with r0..r3 the four 16-lane rows.
+__device__ __forceinline__ v8s c_to_frag(v4f x0, v4f x1) {
+    const uint32_t a0 = pack2(x0[0], x0[1]), a1 = pack2(x0[2], x0[3]);
+    const uint32_t b0 = pack2(x1[0], x1[1]), b1 = pack2(x1[2], x1[3]);
+    const u32x2 s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+    const u32x2 s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+    const u32x2 t0 = __builtin_amdgcn_permlane16_swap(s0[0], s0[1], false, false);
+    const u32x2 t1 = __builtin_amdgcn_permlane16_swap(s1[0], s1[1], false, false);
+    return __builtin_bit_cast(v8s, make_uint4(t0[0], t1[0], t0[1], t1[1]));
+}
+// 16 bytes from global memory straight into LDS: lane l's bytes land at lds_base + 16 l
+__device__ __forceinline__ void load_to_lds16(const void *g, void *lds_base) {
+    __builtin_amdgcn_global_load_lds((glb_void_t *)(g), (lds_void_t *)(lds_base), 16, 0, 0);
+}
+// Workgroup barrier for LDS hand-offs: wait for this wave's LDS operations, then s_barrier.
+// The waits are the s_waitcnt builtin (not inline asm) so the compiler's own wait insertion
+// knows the counters they drain; the empty asm statements keep memory accesses on their side.
+__device__ __forceinline__ void block_sync() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void wait_global() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    asm volatile("" ::: "memory");
+}
+// at most 8 vector memory operations of this wave still in flight: issuing loads in groups
+// of 8 with this wait between them keeps the CU's load queues from thrashing
+__device__ __forceinline__ void wait_global8() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0f78);  // vmcnt(8)
+    asm volatile("" ::: "memory");
+}
+// at most N vector memory operations of this wave still in flight
+template <int N>
+__device__ __forceinline__ void wait_global_n() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
+    asm volatile("" ::: "memory");
+}
+
+// x + (x of the lane selected by the DPP control), 0 where the control selects no lane
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float x) {
+    const int y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, false);
+    return x + __int_as_float(y);
+}
+__device__ __forceinline__ float lane_value(float x, int l) {  // x of lane l (wave-uniform)
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+// x summed with the lanes 16 and 32 away: each 16-lane row receives the sum of the four rows
+// at its own position (the two row swaps v_permlane32_swap and v_permlane16_swap)
+__device__ __forceinline__ float sum_rows(float x) {
+    const uint32_t b = __float_as_uint(x);
+    const u32x2 s = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+    const float y = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+    const uint32_t c = __float_as_uint(y);
+    const u32x2 t = __builtin_amdgcn_permlane16_swap(c, c, false, false);
+    return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+
+// four consecutive outputs from fp32 accumulators: 16 bytes (fp32) or 8 bytes (bf16)
+__device__ __forceinline__ void store4(float *p, v4f x) {
+    *reinterpret_cast<v4f *>(p) = x;
+}
+__device__ __forceinline__ void store4(bf16_t *p, v4f x) {
+    *reinterpret_cast<uint2 *>(p) = pack4u(x);
+}
+
+}  // namespace osdn

@@ -20,7 +20,8 @@ ABI_VERSION = 1
 
 STATUS = {0: "OSDN_OK", -1: "OSDN_ERR_NULL", -2: "OSDN_ERR_SHAPE", -3: "OSDN_ERR_UNSUPPORTED",
           -4: "OSDN_ERR_ALIGN", -5: "OSDN_ERR_ALIAS", -6: "OSDN_ERR_LAUNCH"}
-EXPORTS = ("osdn_chunk_fwd", "osdn_step", "osdn_status_string", "osdn_abi_version")
+EXPORTS = ("osdn_chunk_fwd", "osdn_step", "osdn_precond_scan", "osdn_precond_step",
+           "osdn_status_string", "osdn_abi_version")
 
 
 class OSDNError(RuntimeError):
@@ -47,6 +48,12 @@ def lib() -> ctypes.CDLL:
                                              ctypes.c_int, vp]
     L.osdn_step.restype = ctypes.c_int
     L.osdn_step.argtypes = [vp] * 8 + [i64, i64, i32, i32, ctypes.c_int, ctypes.c_int, vp]
+    L.osdn_precond_scan.restype = ctypes.c_int
+    L.osdn_precond_scan.argtypes = [vp] * 4 + [ctypes.c_float, vp, vp, i64, i64, i64, i32, i32,
+                                               ctypes.c_int, ctypes.c_int, vp]
+    L.osdn_precond_step.restype = ctypes.c_int
+    L.osdn_precond_step.argtypes = [vp] * 5 + [ctypes.c_float, i64, i64, i32, ctypes.c_int,
+                                               ctypes.c_int, vp]
     L.osdn_status_string.restype = ctypes.c_char_p
     L.osdn_status_string.argtypes = [ctypes.c_int]
     L.osdn_abi_version.restype = ctypes.c_int32
@@ -149,3 +156,52 @@ def osdn_step(q, k, v, beta, d, alpha, S, *, o=None, stream=None):
     if st != 0:
         raise OSDNError(st, "osdn_step")
     return o
+
+
+def osdn_precond_scan(k, beta, r=None, d1=None, *, eta: float, chunk: Optional[int] = None,
+                      d_dtype=None, d=None, d_next=None, want_state: bool = True, stream=None):
+    """Phase-1 preconditioner scan.  k [B,H,T,dk]; beta, r [B,H,T] fp32 (r may be None);
+    d1 [B,H,dk] fp32 (None: ones).  Returns (d [B,H,T,dk] in ``d_dtype`` (default float32),
+    d_next [B,H,dk] fp32 or None).  ``chunk`` defaults to 64 for bf16 keys and 1 otherwise;
+    ``d_next`` may be ``d1`` for an in-place carry."""
+    torch = _torch()
+    B, H, T, dk = k.shape
+    if chunk is None:
+        chunk = 64 if k.dtype == torch.bfloat16 else 1
+    if d is None:
+        d = torch.empty((B, H, T, dk), dtype=d_dtype or torch.float32, device=k.device)
+    if d_next is None and want_state:
+        d_next = torch.empty((B, H, dk), dtype=torch.float32, device=k.device)
+    if tuple(d.shape) != (B, H, T, dk):
+        raise ValueError(f"d has shape {tuple(d.shape)}, expected {(B, H, T, dk)}")
+    for name, t, shape in (("beta", beta, (B, H, T)), ("r", r, (B, H, T)),
+                           ("d1", d1, (B, H, dk)), ("d_next", d_next, (B, H, dk))):
+        if t is not None and (tuple(t.shape) != shape or t.dtype != torch.float32):
+            raise ValueError(f"{name} must be float32 {shape}")
+    st = lib().osdn_precond_scan(_ptr(k), _ptr(beta), _ptr(r), _ptr(d1), float(eta), _ptr(d),
+                                 _ptr(d_next), B, H, T, dk, chunk, _dtype_code(k),
+                                 _dtype_code(d), _stream(stream, k.device))
+    if st != 0:
+        raise OSDNError(st, "osdn_precond_scan")
+    return d, d_next
+
+
+def osdn_precond_step(k, beta, r, dstate, *, eta: float, d_out=None, d_dtype=None,
+                      stream=None):
+    """One decode token of the scan: k [B,H,dk]; beta, r [B,H] fp32 (r may be None); dstate
+    [B,H,dk] fp32 updated in place.  Returns d_out [B,H,dk] (the d this token writes with)."""
+    torch = _torch()
+    B, H, dk = k.shape
+    if d_out is None:
+        d_out = torch.empty((B, H, dk), dtype=d_dtype or torch.float32, device=k.device)
+    if tuple(dstate.shape) != (B, H, dk) or dstate.dtype != torch.float32:
+        raise ValueError("dstate must be float32 [B,H,dk]")
+    for name, t in (("beta", beta), ("r", r)):
+        if t is not None and (tuple(t.shape) != (B, H) or t.dtype != torch.float32):
+            raise ValueError(f"{name} must be float32 [B,H]")
+    st = lib().osdn_precond_step(_ptr(k), _ptr(beta), _ptr(r), _ptr(dstate), _ptr(d_out),
+                                 float(eta), B, H, dk, _dtype_code(k), _dtype_code(d_out),
+                                 _stream(stream, k.device))
+    if st != 0:
+        raise OSDNError(st, "osdn_precond_step")
+    return d_out

@@ -17,6 +17,11 @@ weights and datasets, so these synthetic tensors stand in for them):
   bfloat16 (RNE) and kept as float32 arrays holding exactly bf16-representable values, so
   that the GPU copy (bf16) and the oracle copy (float64) hold the same numbers.
 
+The Phase-1 preconditioner scan takes the workload's k and beta and, from a stream of its
+own (seed + 7919, so the draws above are unchanged), its retention gate and start value:
+r = exp(-0.01 * softplus(N(0, 1))) per token and head (in (0.97, 1)), d_1 = exp(0.25 N(0, 1))
+per head and feature, both rounded to float32.  The meta step eta = 2 is a workload constant.
+
 The decode workload draws its initial state first (S0 ~ N(0, 0.02^2), float32, stored as
 M = S^T, i.e. ``[B, H, dk, dv]``), then the per-step tuples in the order above.
 """
@@ -167,3 +172,14 @@ def make_shape(B: int, H: int, T: int, dk: int, dv: int, *, qkv: str = "f32",
     w = Workload("custom", B=B, H=H, T=T, dk=dk, dv=dv, qkv=qkv, alpha=alpha, s0=s0,
                  sigma_d=sigma_d, seed_index=0)
     return make_inputs(w, seed=BASE_SEED + 1000 + seed)
+
+
+PRECOND_ETA = 2.0
+
+
+def make_precond_gates(B: int, H: int, T: int, dk: int, seed: int) -> Dict[str, np.ndarray]:
+    """Retention gate r [B,H,T] and start value d1 [B,H,dk] of the Phase-1 scan."""
+    rng = np.random.Generator(np.random.PCG64(seed + 7919))
+    r = np.exp(-0.01 * np.logaddexp(0.0, rng.standard_normal((B, H, T))))
+    d1 = np.exp(0.25 * rng.standard_normal((B, H, dk)))
+    return {"r": round_f32(r), "d1": round_f32(d1)}

@@ -98,6 +98,52 @@ osdn_status osdn_step(const void *q, const void *k, const void *v, const float *
                       int64_t H, int32_t dk, int32_t dv, osdn_dtype qkv, osdn_dtype d_dtype,
                       void *stream);
 
+/*
+ * Phase-1 preconditioner scan: the per-token diagonal d_t that osdn_chunk_fwd takes, produced
+ * from the key stream (OSDN technical summary, section 2.2: d is moved by online gradient
+ * descent on the hypergradient surrogate h_t, whose closed form depends only on k_t and
+ * beta_t; section 2.3: the APF retention gate r multiplies the preconditioner state).  For
+ * every (b,h), token by token, with x_t = k_t^2 (elementwise):
+ *
+ *     token t writes with d_t;
+ *     d_{t+1} = r_t d_t + eta beta_t (1 - beta_t <d_t, x_t>) x_t / ||k_t||^2
+ *             = r_t d_t - eta grad_d h_t(d_t);
+ *
+ * a zero key takes no gradient step (d_{t+1} = r_t d_t).
+ *
+ *   k      [B,H,T,dk] k_dtype  keys (the same k that osdn_chunk_fwd takes)
+ *   beta   [B,H,T]    f32      scalar write gate
+ *   r      [B,H,T]    f32      retention gate, expected in (0, 1]; NULL means r == 1
+ *   d1     [B,H,dk]   f32      preconditioner of each sequence's first token; NULL means 1
+ *   eta                        meta step size
+ *   d      [B,H,T,dk] d_dtype  output: d_t for every t < T
+ *   d_next [B,H,dk]   f32      output: the preconditioner after the last token, NULL means not
+ *                              written; it may be the same pointer as d1 (in-place carry)
+ *   B, H, T >= 0;  dk in {64, 128}
+ *   chunk                      1: token-serial scan (any k_dtype; one wave per sequence).
+ *                              64: chunkwise form (k_dtype must be OSDN_BF16): the step is affine
+ *                              in d, so each 64-token chunk is one small triangular solve plus
+ *                              bf16 matrix-core products with fp32 accumulation.  The two agree
+ *                              to rounding; for ln r below -80 the chunkwise form uses -80.
+ *   d must not overlap any input or d_next; d_next may overlap d1 only exactly.
+ */
+osdn_status osdn_precond_scan(const void *k, const float *beta, const float *r,
+                              const float *d1, float eta, void *d, float *d_next, int64_t B,
+                              int64_t H, int64_t T, int32_t dk, int32_t chunk,
+                              osdn_dtype k_dtype, osdn_dtype d_dtype, void *stream);
+
+/*
+ * One decode token of the scan above, for every (b,h):
+ *   k [B,H,dk] k_dtype;  beta [B,H] f32;  r [B,H] f32 or NULL;
+ *   dstate [B,H,dk] f32, read as d_t and overwritten in place with d_{t+1};
+ *   d_out  [B,H,dk] d_dtype, receives d_t (the diagonal this token writes with: osdn_step's d);
+ *          NULL means not written.
+ *   d_out must not overlap dstate or an input; dstate must not overlap an input.
+ */
+osdn_status osdn_precond_step(const void *k, const float *beta, const float *r, float *dstate,
+                              void *d_out, float eta, int64_t B, int64_t H, int32_t dk,
+                              osdn_dtype k_dtype, osdn_dtype d_dtype, void *stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char *osdn_status_string(osdn_status s);
 

@@ -129,3 +129,61 @@ def test_python_binding_refuses_host_tensors(L):
     with pytest.raises(ValueError):
         osdn.osdn_chunk_fwd(x, x, x, torch.zeros(1, 1, 4), x, want_state=False,
                             o=torch.zeros(1, 1, 4, 64))
+
+
+def precond_args(**over):
+    a = dict(k=addr(1), beta=addr(2), r=addr(3), d1=addr(4), eta=0.5, d=addr(5),
+             d_next=addr(6), B=2, H=3, T=100, dk=128, chunk=64, k_dtype=osdn.OSDN_BF16,
+             d_dtype=osdn.OSDN_F32, stream=None)
+    a.update(over)
+    return a
+
+
+def call_precond(L, **over):
+    a = precond_args(**over)
+    return L.osdn_precond_scan(a["k"], a["beta"], a["r"], a["d1"], a["eta"], a["d"],
+                               a["d_next"], a["B"], a["H"], a["T"], a["dk"], a["chunk"],
+                               a["k_dtype"], a["d_dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(k=None), -1), (dict(beta=None), -1), (dict(d=None), -1),
+    (dict(B=-1), -2), (dict(T=-1), -2), (dict(B=1 << 40, H=1 << 20), -2),
+    (dict(dk=96), -3), (dict(chunk=32), -3), (dict(chunk=0), -3),
+    (dict(chunk=64, k_dtype=osdn.OSDN_F32), -3), (dict(k_dtype=5), -3), (dict(d_dtype=2), -3),
+    (dict(k=addr(1) + 8), -4), (dict(d=addr(5) + 4), -4), (dict(beta=addr(2) + 2), -4),
+    (dict(d1=addr(4) + 4), -4), (dict(d_next=addr(6) + 8), -4), (dict(r=addr(3) + 1), -4),
+    (dict(d=addr(1)), -5), (dict(d=addr(2) - 256), -5), (dict(d_next=addr(5) + 1024), -5),
+    (dict(d_next=addr(1)), -5), (dict(d_next=addr(4) + 16), -5), (dict(d=addr(6)), -5),
+])
+def test_precond_scan_rejects(L, over, status):
+    assert call_precond(L, **over) == status
+
+
+def test_precond_scan_empty_work_is_ok(L):
+    assert call_precond(L, B=0) == 0
+    assert call_precond(L, T=0, k=None, beta=None, d=None, d_next=None) == 0
+    # the serial form takes either key type
+    assert call_precond(L, B=0, chunk=1, k_dtype=osdn.OSDN_F32) == 0
+
+
+def call_precond_step(L, **over):
+    a = dict(k=addr(1), beta=addr(2), r=addr(3), dstate=addr(4), d_out=addr(5), eta=0.5, B=4,
+             H=2, dk=64, k_dtype=osdn.OSDN_BF16, d_dtype=osdn.OSDN_BF16, stream=None)
+    a.update(over)
+    return L.osdn_precond_step(a["k"], a["beta"], a["r"], a["dstate"], a["d_out"], a["eta"],
+                               a["B"], a["H"], a["dk"], a["k_dtype"], a["d_dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(k=None), -1), (dict(dstate=None), -1), (dict(beta=None), -1),
+    (dict(B=-3), -2), (dict(dk=100), -3), (dict(k_dtype=9), -3),
+    (dict(dstate=addr(4) + 4), -4), (dict(d_out=addr(5) + 8), -4),
+    (dict(d_out=addr(4)), -5), (dict(dstate=addr(1)), -5), (dict(d_out=addr(2)), -5),
+])
+def test_precond_step_rejects(L, over, status):
+    assert call_precond_step(L, **over) == status
+
+
+def test_precond_step_empty_is_ok(L):
+    assert call_precond_step(L, H=0, k=None) == 0

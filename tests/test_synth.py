@@ -55,3 +55,12 @@ def test_decode_inputs():
     assert x["S0"].shape == (2, 3, 128, 128)
     assert x["q"].shape == (3, 2, 3, 128) and x["beta"].shape == (3, 2, 3)
     assert abs(x["S0"].std() - 0.02) < 0.002
+
+
+def test_precond_gates():
+    a = synth.make_precond_gates(2, 3, 50, 64, seed=5)
+    b = synth.make_precond_gates(2, 3, 50, 64, seed=5)
+    assert a["r"].shape == (2, 3, 50) and a["d1"].shape == (2, 3, 64)
+    assert np.array_equal(a["r"], b["r"]) and np.array_equal(a["d1"], b["d1"])
+    assert a["r"].dtype == np.float32 and np.all((a["r"] > 0.9) & (a["r"] <= 1.0))
+    assert np.all(a["d1"] > 0)
