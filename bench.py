@@ -12,7 +12,10 @@ HBM.  Prints ONE JSON line.  Besides the contract fields it carries:
   cpu_baseline  the float64 oracle on the host cores, same workload, with the parity error
                 of the GPU output against it;
   decode        osdn_step over the decode workload (B=128, H=16, dk=dv=128), timed over
-                `--decode-steps` consecutive calls (state updated in place).
+                `--decode-steps` consecutive calls (state updated in place);
+  precond_scan  the Phase-1 preconditioner scan (osdn_precond_scan, chunkwise form) over the
+                same workload's keys and gates, with its own HBM roofline, its oracle timed on
+                the host, and the forward with the scan in front (scan + chunkwise forward).
 """
 from __future__ import annotations
 
@@ -32,6 +35,7 @@ PEAK_HBM = 8.0e12      # bytes/s, MI355X HBM3E
 PEAK_BF16 = 2.5e15     # FLOP/s, MI355X dense bf16 matrix peak
 CHUNK_KERNEL_SRC = ["delta_rule_sequence_chunkwise_amd/csrc/osdn_chunk_mfma.hip"]
 STEP_KERNEL_SRC = ["delta_rule_sequence_chunkwise_amd/csrc/osdn_step.hip"]
+PRECOND_KERNEL_SRC = ["delta_rule_sequence_chunkwise_amd/csrc/osdn_precond.hip"]
 
 
 def flops_per_head_token(dk, dv, C):
@@ -73,6 +77,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--precond-steps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="1.3b")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -193,6 +198,11 @@ def main():
     if args.decode_steps > 0:
         line["decode"] = bench_decode(args.decode_steps, torch, dev, synth)
 
+    if args.precond_steps > 0:
+        line["precond_scan"] = bench_precond(args.precond_steps, torch, dev, synth, w, x,
+                                             (q, k, v, beta, alpha, S0, o, S_T),
+                                             not args.no_cpu_baseline)
+
     print(json.dumps(line), flush=True)
 
 
@@ -236,6 +246,73 @@ def bench_decode(n_steps, torch, dev, synth, distinct=64):
             "traffic": load_traffic("step_decode_traffic", STEP_KERNEL_SRC),
             "note": "the 128 MiB state fits in the 256 MB Infinity Cache; achieved is "
                     "algorithmic bytes / time, see profiles for DRAM counters"}
+
+
+def bench_precond(n_steps, torch, dev, synth, w, x, fwd, cpu):
+    """Times `n_steps` launches of the chunkwise Phase-1 scan over the workload's keys and
+    gates (fp32 d out, final state out), then `n_steps` forwards with the scan in front."""
+    import numpy as np
+    from delta_rule_sequence_chunkwise_amd import osdn
+
+    B, H, T, dk = w.B, w.H, w.T, w.dk
+    g = synth.make_precond_gates(B, H, T, dk, seed=w.seed)
+    eta = synth.PRECOND_ETA
+    q, k, v, beta, alpha, S0, o, S_T = fwd
+    r = torch.from_numpy(g["r"]).to(dev)
+    d1 = torch.from_numpy(g["d1"]).to(dev)
+    d = torch.empty((B, H, T, dk), dtype=torch.float32, device=dev)
+    dn = torch.empty((B, H, dk), dtype=torch.float32, device=dev)
+
+    def scan():
+        osdn.osdn_precond_scan(k, beta, r, d1, eta=eta, chunk=w.chunk, d=d, d_next=dn)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n_steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / n_steps
+
+    per = timed(scan)
+    head_tokens = B * H * T
+    alg = head_tokens * (2 * dk + 8 + 4 * dk) + 2 * B * H * dk * 4
+    d_gpu = d.cpu().numpy()
+
+    def fwd_with_scan():
+        scan()
+        osdn.osdn_chunk_fwd(q, k, v, beta, d, alpha, S0, chunk=w.chunk, o=o, S_T=S_T)
+
+    per_fwd = timed(fwd_with_scan)
+    rec = {"workload": f"{w.name}-shape keys and gates: B={B} H={H} T={T} dk={dk}, chunk "
+                       f"{w.chunk}, bf16 k, fp32 beta/r/d1, eta={eta}, fp32 d and final d out",
+           "launch_ms": round(per * 1e3, 4),
+           "head_tokens_per_s": round(head_tokens / per, 1),
+           "roofline": {"bound": "hbm", "achieved": round(alg / per / 1e9, 2),
+                        "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                        "frac": round(alg / per / PEAK_HBM, 5),
+                        "traffic": load_traffic("precond_scan_1.3b_traffic",
+                                                PRECOND_KERNEL_SRC),
+                        "alg_bytes_per_launch": alg},
+           "fwd_with_scan": {"ms_per_step": round(per_fwd * 1e3, 4),
+                             "tokens_per_s": round(B * T / per_fwd, 1)}}
+    if cpu:
+        from oracle import precond
+        c0 = time.perf_counter()
+        d_ref, _ = precond.precond_scan(x["k"], x["beta"], eta, g["r"], g["d1"])
+        cpu_s = time.perf_counter() - c0
+        rec["cpu_baseline"] = {"value": round(head_tokens / cpu_s, 1), "unit": "head-tokens/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"the whole workload ({B * H} sequences x {T} tokens),"
+                                         f" float64 numpy token loop, {cpu_s:.2f} s wall"}
+        rec["parity"] = {"e_d": float(np.max(np.abs(d_gpu - d_ref)) / np.max(np.abs(d_ref))),
+                         "tol": 3e-3}
+    return rec
 
 
 if __name__ == "__main__":

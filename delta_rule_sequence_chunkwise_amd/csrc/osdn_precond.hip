@@ -20,24 +20,32 @@
 //     (I + L) e = 1 - b . rho . (X d0),      L[j,i] = b_j R[j,i] c_i <x_j, x_i>  (i < j),
 //   after which the chunk's outputs are  D = rho d0^T + W X,  W[j,i] = R[j,i] c_i e_i (i < j),
 //   and the next chunk starts from  rho_C d0 + X^T (R[C,.] . c . e).
-//   The Gram matrix X X^T and the output product W X are bf16 matrix-core products (x = k^2 is
-//   exact in fp32 for a bf16 key and rounded to bf16 only as an operand); everything the
-//   carried state depends on besides L -- X d0, the solve and the carry -- runs in fp32 on
-//   exact x.  R is formed from the running sum lr of ln r (clamped at -80 per token), as
-//   e^{lr_j - lr_{i+1}}, which is at most 1 for a retention gate r <= 1.
+//   Every product runs on 16x16x32 bf16 matrix cores with fp32 accumulation.  x = k^2 of a
+//   bf16 key is exact in fp32 and splits exactly into xh = bf16(x) plus xl = bf16(x - xh).
+//   The products the carried state depends on -- X d0 and X^T w -- use both halves of x and
+//   of the other operand (hi/lo bf16 pairs), so they are accurate to fp32; the Gram matrix
+//   X X^T (which only enters through L) and the output product W X use xh alone, and the
+//   forward substitution is fp32.  R is formed from the running sum lr of ln r (clamped at
+//   -80 per token), as e^{lr_j - lr_{i+1}}, at most 1 for a retention gate r <= 1.
 //
-//   One workgroup of eight waves owns one sequence and walks its chunks; step s handles the
-//   chain of chunk s, the preparation of chunk s+1 and the output of chunk s-1, in three
-//   phases separated by barriers:
-//     A  all waves: partial sums of X d0 for chunk s (each wave one slice of the features),
-//        and x = k^2 for chunk s+1: bf16 copy for the matrix cores, fp32 row norms -> c.
-//     B  wave 0: the forward substitution for chunk s (row j of L in lane j's registers,
-//        63 broadcast-and-update steps);  waves 1-4: output of chunk s-1 as D^T = X^T W^T on
-//        16x16x32 products (W built in registers), stored as 16-byte rows of d;  waves 5-6:
-//        keys of chunk s+3 into LDS (global_load_lds);  wave 7: the ln r scan of chunk s+2
-//        and the gate loads of chunk s+3.
-//     C  all waves: the carry d0 <- rho_C d0 + X^T (R[C,.] c e) for chunk s (each wave a slice
-//        of the features), and the Gram tiles of chunk s+1 -> L.
+//   One workgroup of eight waves owns one sequence and walks its chunks with one barrier per
+//   step; each role runs its own loop, so registers one role keeps do not add to another's:
+//     wave 0      the chain of chunk s: X d0 (A = xh, xl rows; B = hi/lo of d0 in columns 0
+//                 and 1), the forward substitution (row j of L in lane j's registers, 63
+//                 broadcast-and-update steps), the carry d0 <- rho_C d0 + X^T w
+//                 (A = hi/lo of w in rows 0 and 1; B = xh, xl by transposing LDS reads);
+//     waves 1-3, 7  the output of chunk s-1 as D^T = X^T W^T (W built in registers from one
+//                 exponential per fragment and per-token factors), stored as 16-byte rows
+//                 of d, and two Gram tiles of chunk s+1 each;
+//     waves 5-6   keys of chunk s+2 squared from registers into xh, xl and the row norms,
+//                 then the keys of chunk s+3 loaded into registers (a step of latency hidden);
+//     wave 4      the gate scan of chunk s+2, the gate loads of chunk s+3 and two Gram tiles
+//                 (it shares a SIMD with wave 0, so its load is kept light).
+//   Keys go through registers rather than global_load_lds: an LDS read that may alias an
+//   in-flight LDS DMA makes the compiler wait for every outstanding vector memory operation
+//   of the wave, stores included.
+#include <type_traits>
+
 #include "osdn_internal.h"
 #include "osdn_mfma.h"
 
@@ -121,24 +129,35 @@ constexpr int NW = 8;        // waves per workgroup
 constexpr int NT = NW * 64;  // threads per workgroup
 constexpr float kMinLogR = -80.f;
 
+// f(integral_constant<I>) for I = B .. E-1, unrolled at compile time
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 template <int DK>
 struct alignas(16) PrecondLds {
-    static constexpr int KU = DK / 8;   // 16-byte units per key row
+    static constexpr int KU = DK / 8;   // 16-byte units per row of x
     static constexpr int LP = CH + 4;   // fp32 row pitch of L (rows start 4 banks apart)
-    // 16-byte unit u of key row j sits at unit u ^ sw(j): reads that take one unit from each
-    // of 16 consecutive rows, and rows of 16 consecutive units, are bank-conflict free
+    // 16-byte unit u of row j sits at unit u ^ sw(j): reads that take one unit from each of 16
+    // consecutive rows, and rows of consecutive units, are bank-conflict free
     __device__ static constexpr int sw(int j) { return DK == 128 ? (j & 15) : ((j >> 1) & 7); }
     __device__ static constexpr int at(int j, int u) { return (j * KU + (u ^ sw(j))) * 8; }
-    alignas(16) uint16_t kb[4][CH * DK];  // [chunk mod 4] keys (bf16), swizzled rows
-    alignas(16) uint16_t xb[3][CH * DK];  // [chunk mod 3] bf16(k^2), same layout
+    alignas(16) uint16_t xh[4][CH * DK];  // [chunk mod 4] bf16(x), x = k^2 (fp32-exact)
+    alignas(16) uint16_t xl[3][CH * DK];  // [chunk mod 3] bf16(x - xh): xh + xl = x exactly
     alignas(16) float L[2][CH * LP];      // [chunk parity] L, row-major (upper part zero)
-    alignas(16) float beta[4][CH];        // [chunk mod 4] gate (0 past the end)
+    alignas(16) float nrm[4][CH];         // [chunk mod 4] ||k_j||^2
+    alignas(16) float beta[4][CH];        // gate (0 past the end)
     alignas(16) float cc[4][CH];          // eta b / ||k||^2
     alignas(16) float lr[4][CH + 4];      // lr[0] = 0, lr[j+1] = sum_{i<=j} max(ln r_i, -80)
-    alignas(16) float d0[2][DK];          // [chunk parity] start state of the chunk
-    alignas(16) float ee[2][CH];          // [chunk parity] e of the chunk
-    alignas(16) float wc[CH];             // R[C,j] c_j e_j of the chunk in its chain
-    alignas(16) float up[NW][CH];         // per-wave partial sums of X d0
+    alignas(16) float rho[4][CH];         // e^{lr_j}
+    alignas(16) float d0[3][DK];          // [chunk mod 3] start state of the chunk
+    alignas(16) float ew[2][CH];          // [chunk parity] e^{lr_{32(i/32)} - lr_{i+1}} c_i e_i
+    alignas(16) float wc[CH];             // the chain wave's R[C,j] c_j e_j
+    alignas(16) float uu[CH];             // the chain wave's X d0
 };
 
 // inclusive prefix sum over the 64 lanes (shifts by 1, 2, 4, 8 inside each 16-lane row, then
@@ -153,41 +172,96 @@ __device__ __forceinline__ float wave_prefix(float x) {
     return x;
 }
 
+// eight fp32 values -> hi = bf16(v) and lo = bf16(v - hi), as operand fragments for the lanes
+// of column (or row) 0 and 1 of a 16x16x32 product; other lanes get zero
+__device__ __forceinline__ v8s split_frag(v4f a, v4f b, int n) {
+    const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t h = pack2(v[2 * i], v[2 * i + 1]);
+        const uint32_t l = pack2(v[2 * i] - bf_lo(h), v[2 * i + 1] - bf_hi(h));
+        w[i] = n == 0 ? h : (n == 1 ? l : 0u);
+    }
+    return __builtin_bit_cast(v8s, make_uint4(w[0], w[1], w[2], w[3]));
+}
+
 template <int DK, typename TD>
 __global__ void __launch_bounds__(NT)
 precond_chunk_kernel(const uint16_t *__restrict__ k, const float *__restrict__ beta,
                      const float *__restrict__ r, const float *d1, float eta,
                      TD *__restrict__ d_out, float *d_next, int64_t T) {
     using L = PrecondLds<DK>;
+    constexpr int NLD = 32 * L::KU / 64;  // 16-byte key loads per lane for half a key tile
+    constexpr int KS = DK / 32;           // 32-feature slices of a row
+    constexpr int NF = DK / 16;           // 16-feature tiles of a row
     __shared__ L sm;
     const int64_t bh = blockIdx.x;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int q = lane >> 4, n = lane & 15;
     const int nc = static_cast<int>((T + CH - 1) / CH);
     const uint16_t *kq = k + bh * T * DK;
     const float *bq = beta + bh * T;
     const float *rq = r ? r + bh * T : nullptr;
     TD *oq = d_out + bh * T * DK;
 
-    // keys of chunk cd into kb[cd & 3] (one wave: rows [R0, R0 + 32)); rows past the end
-    // re-read the last row (their gate is zero)
-    auto dma = [&](int cd, int R0) __attribute__((always_inline)) {
-        constexpr int NLD = 32 * L::KU / 64;
-        uint16_t *dst = sm.kb[cd & 3];
-        const int64_t row0 = int64_t(cd) * CH;
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-            const int base = R0 * L::KU + i * 64;
-            const int pu = base + lane, j = pu / L::KU, u = (pu % L::KU) ^ L::sw(j);
-            const int64_t row = row0 + j < T ? row0 + j : T - 1;
-            load_to_lds16(kq + row * DK + 8 * u, dst + 8 * base);
-        }
+    // ---- key loading (waves 5 and 6, rows [R0, R0 + 32) of a chunk each): keys go to eight
+    // named registers (a register array carried across the step loop would live in scratch)
+    // and are squared there; rows past the end re-read the last row (their gate is zero)
+    const int R0 = 32 * (wave - 5);
+    uint4 kr0, kr1, kr2, kr3, kr4, kr5, kr6, kr7;
+    auto kreg = [&](auto I) __attribute__((always_inline)) -> uint4 & {
+        if constexpr (I == 0) return kr0;
+        else if constexpr (I == 1) return kr1;
+        else if constexpr (I == 2) return kr2;
+        else if constexpr (I == 3) return kr3;
+        else if constexpr (I == 4) return kr4;
+        else if constexpr (I == 5) return kr5;
+        else if constexpr (I == 6) return kr6;
+        else return kr7;
     };
-    // gate scan of chunk cs from this lane's b and r (one wave, row = lane)
+    auto load_keys = [&](int cl) __attribute__((always_inline)) {
+        const int64_t row0 = int64_t(cl) * CH;
+        static_for<0, NLD>([&](auto I) __attribute__((always_inline)) {
+            const int pu = R0 * L::KU + I * 64 + lane, j = pu / L::KU, u = pu % L::KU;
+            const int64_t row = row0 + j < T ? row0 + j : T - 1;
+            kreg(I) = *reinterpret_cast<const uint4 *>(kq + row * DK + 8 * u);
+        });
+    };
+    // x = k^2 of the keys in registers -> xh, xl (xh + xl = x exactly for bf16 keys) and the
+    // row norms (the KU units of a row sit in KU consecutive lanes)
+    auto square_keys = [&](int cl) __attribute__((always_inline)) {
+        uint16_t *xh = sm.xh[cl & 3], *xl = sm.xl[cl % 3];
+        static_for<0, NLD>([&](auto I) __attribute__((always_inline)) {
+            const int pu = R0 * L::KU + I * 64 + lane, j = pu / L::KU, u = pu % L::KU;
+            const uint4 w = kreg(I);
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+            uint32_t hi[4], lo[4];
+            float sn = 0.f;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const float a = bf_lo(ws[h]), b = bf_hi(ws[h]);
+                const float xa = a * a, xb = b * b;
+                sn += xa + xb;
+                hi[h] = pack2(xa, xb);
+                lo[h] = pack2(xa - bf_lo(hi[h]), xb - bf_hi(hi[h]));
+            }
+            *reinterpret_cast<uint4 *>(xh + L::at(j, u)) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+            *reinterpret_cast<uint4 *>(xl + L::at(j, u)) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+            sn = dpp_add<0xb1, 0xf>(sn);
+            sn = dpp_add<0x4e, 0xf>(sn);
+            sn = dpp_add<0x141, 0xf>(sn);
+            if (L::KU == 16) sn = dpp_add<0x140, 0xf>(sn);
+            if (u == 0) sm.nrm[cl & 3][j] = sn;
+        });
+    };
+    // gate scan of chunk cs from this lane's b and r (wave 4, row = lane)
     auto scan = [&](int cs, float bv, float rv) __attribute__((always_inline)) {
         const bool ok = int64_t(cs) * CH + lane < T;
         const float x = (ok && rq) ? fmaxf(__logf(rv), kMinLogR) : 0.f;
         const float incl = wave_prefix(x);
         sm.lr[cs & 3][lane + 1] = incl;
+        sm.rho[cs & 3][lane] = __expf(incl - x);
         if (lane == 0) sm.lr[cs & 3][0] = 0.f;
         sm.beta[cs & 3][lane] = ok ? bv : 0.f;
     };
@@ -196,85 +270,98 @@ precond_chunk_kernel(const uint16_t *__restrict__ k, const float *__restrict__ b
         bv = t < T ? bq[t] : 0.f;
         rv = (t < T && rq) ? rq[t] : 1.f;
     };
+    // Gram tiles t0 and t1 of chunk cg (tiles of the lower triangle in row order) -> L, and
+    // c = eta b / ||k||^2 of the tile's columns (written by the diagonal tile)
+    auto gram2 = [&](int cg, int t0, int t1) __attribute__((always_inline)) {
+        const int sl = cg & 3;
+        const uint16_t *xh = sm.xh[sl];
+        int J[2], I[2];
+        v4f acc[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int t = h == 0 ? t0 : t1;
+            J[h] = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+            I[h] = t - J[h] * (J[h] + 1) / 2;
+            acc[h] = zero4();
+        }
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int u = 4 * st + q;
+                acc[h] = mfma32(ld8(xh + L::at(16 * J[h] + n, u)), ld8(xh + L::at(16 * I[h] + n, u)),
+                                acc[h]);
+            }
+        }
+        float *Lt = sm.L[cg & 1];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int i = 16 * I[h] + n;
+            const float ni = sm.nrm[sl][i];
+            const float ci = ni > 0.f ? eta * sm.beta[sl][i] / ni : 0.f;
+            if (J[h] == I[h] && q == 0) sm.cc[sl][i] = ci;
+            const float lri = sm.lr[sl][i + 1];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int j = 16 * J[h] + 4 * q + m;
+                Lt[j * L::LP + i] =
+                    i < j ? sm.beta[sl][j] * __expf(sm.lr[sl][j] - lri) * ci * acc[h][m] : 0.f;
+            }
+        }
+    };
 
-    // ---- prologue: zero L (its upper part is never written), d0 of chunk 0, keys of
-    // chunks 0 and 1, gates of chunk 0 scanned and of chunk 1 in registers
+    // ---- prologue: zero L (its upper part is never written), d0 of chunk 0, x of chunk 0,
+    // gates of chunk 0 scanned
     for (int i = threadIdx.x; i < 2 * CH * L::LP; i += NT) (&sm.L[0][0])[i] = 0.f;
     if (threadIdx.x < DK) sm.d0[0][threadIdx.x] = d1 ? d1[bh * DK + threadIdx.x] : 1.f;
-    float bnext = 0.f, rnext = 1.f;
     if (nc > 0) {
         if (wave == 5 || wave == 6) {
-            dma(0, 32 * (wave - 5));
-            if (nc > 1) dma(1, 32 * (wave - 5));
-            wait_global();
-        } else if (wave == 7) {
+            load_keys(0);
+            square_keys(0);
+        } else if (wave == 4) {
             float b0, r0;
             gates(0, b0, r0);
             scan(0, b0, r0);
-            if (nc > 1) gates(1, bnext, rnext);
         }
     }
     block_sync();
 
-    const int q = lane >> 4, n = lane & 15;
-    for (int s = -1; s <= nc; ++s) {
-        const bool chain = s >= 0 && s < nc, prep = s + 1 < nc;
-        // ---- phase A ----------------------------------------------------------------------
-        if (chain) {  // partial X d0 over this wave's features; lane = row
-            constexpr int UPW = L::KU / NW;
-            const uint16_t *kt = sm.kb[s & 3];
-            const float *d0 = sm.d0[s & 1];
-            float acc = 0.f;
+    // Each role runs its own loop over steps s = -1 .. nc, one barrier per step: in step s
+    // wave 0 chains chunk s, waves 1-3 and 7 write out chunk s-1, waves 1-4 and 7 build the
+    // Gram tiles of chunk s+1, waves 5-6 square the keys of chunk s+2 and wave 4 scans its
+    // gates.
+    if (wave == 0) {
+        for (int s = -1; s <= nc; ++s) {
+            if (s >= 0 && s < nc) {
+                const int sl = s & 3;
+                const uint16_t *xh = sm.xh[sl], *xl = sm.xl[s % 3];
+                const float *d0 = sm.d0[s % 3];
+                // u = X d0: A = xh then xl (rows 16J..), B = [hi(d0) | lo(d0) | 0 ...], so the
+                // sum of output columns 0 and 1 is x . d0 to fp32 accuracy.  The fragments of
+                // a feature slice are read together, one slice ahead of the products.
+                v4f ua[4];
 #pragma unroll
-            for (int qq = 0; qq < UPW; ++qq) {
-                const int u = wave * UPW + qq;
-                const uint4 w = *reinterpret_cast<const uint4 *>(kt + L::at(lane, u));
-                const v4f da = ld4(d0 + 8 * u), db = ld4(d0 + 8 * u + 4);
-                const float k0 = bf_lo(w.x), k1 = bf_hi(w.x), k2 = bf_lo(w.y), k3 = bf_hi(w.y);
-                const float k4 = bf_lo(w.z), k5 = bf_hi(w.z), k6 = bf_lo(w.w), k7 = bf_hi(w.w);
-                acc += k0 * k0 * da[0] + k1 * k1 * da[1] + k2 * k2 * da[2] + k3 * k3 * da[3];
-                acc += k4 * k4 * db[0] + k5 * k5 * db[1] + k6 * k6 * db[2] + k7 * k7 * db[3];
-            }
-            sm.up[wave][lane] = acc;
-        }
-        if (prep) {  // x = k^2 of chunk s+1: bf16 copy and fp32 row norms
-            constexpr int LPR = L::KU;             // lanes per row
-            constexpr int RPW = 64 / LPR;          // rows per wave and pass
-            constexpr int NPASS = CH / (RPW * NW);
-            const int cn = s + 1;
-            const uint16_t *kt = sm.kb[cn & 3];
-            uint16_t *xt = sm.xb[cn % 3];
+                for (int J = 0; J < 4; ++J) ua[J] = zero4();
+                v8s fa[2][8];
+                auto read_u = [&](int st, v8s *f) __attribute__((always_inline)) {
+                    const int u = 4 * st + q;
 #pragma unroll
-            for (int p = 0; p < NPASS; ++p) {
-                const int row = (p * NW + wave) * RPW + lane / LPR;
-                const int e = (row * L::KU + lane % LPR) * 8;
-                const uint4 w = *reinterpret_cast<const uint4 *>(kt + e);
-                const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-                uint32_t o[4];
-                float sn = 0.f;
+                    for (int J = 0; J < 4; ++J) {
+                        f[2 * J] = ld8(xh + L::at(16 * J + n, u));
+                        f[2 * J + 1] = ld8(xl + L::at(16 * J + n, u));
+                    }
+                };
+                read_u(0, fa[0]);
 #pragma unroll
-                for (int h = 0; h < 4; ++h) {
-                    const float a = bf_lo(ws[h]), b = bf_hi(ws[h]);
-                    const float xa = a * a, xb = b * b;
-                    sn += xa + xb;
-                    o[h] = pack2(xa, xb);
+                for (int st = 0; st < KS; ++st) {
+                    if (st + 1 < KS) read_u(st + 1, fa[(st + 1) & 1]);
+                    const v8s b = split_frag(ld4(d0 + 32 * st + 8 * q), ld4(d0 + 32 * st + 8 * q + 4), n);
+#pragma unroll
+                    for (int J = 0; J < 4; ++J) {
+                        ua[J] = mfma32(fa[st & 1][2 * J], b, ua[J]);
+                        ua[J] = mfma32(fa[st & 1][2 * J + 1], b, ua[J]);
+                    }
                 }
-                *reinterpret_cast<uint4 *>(xt + e) = make_uint4(o[0], o[1], o[2], o[3]);
-                sn = dpp_add<0xb1, 0xf>(sn);
-                sn = dpp_add<0x4e, 0xf>(sn);
-                sn = dpp_add<0x141, 0xf>(sn);
-                if (LPR == 16) sn = dpp_add<0x140, 0xf>(sn);
-                if (lane % LPR == 0) {
-                    const float bv = sm.beta[cn & 3][row];
-                    sm.cc[cn & 3][row] = sn > 0.f ? eta * bv / sn : 0.f;
-                }
-            }
-        }
-        block_sync();
-
-        // ---- phase B ----------------------------------------------------------------------
-        if (wave == 0) {
-            if (chain) {  // forward substitution (I + L) e = 1 - b rho (X d0); lane = row
                 float Lrow[CH];
                 const float *Lr = sm.L[s & 1] + lane * L::LP;
 #pragma unroll
@@ -285,46 +372,94 @@ precond_chunk_kernel(const uint16_t *__restrict__ k, const float *__restrict__ b
                     Lrow[4 * m + 2] = t4[2];
                     Lrow[4 * m + 3] = t4[3];
                 }
-                float u = 0.f;
 #pragma unroll
-                for (int w = 0; w < NW; ++w) u += sm.up[w][lane];
-                const float lrj = sm.lr[s & 3][lane];
-                float e = 1.f - sm.beta[s & 3][lane] * __expf(lrj) * u;
+                for (int J = 0; J < 4; ++J) {
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const float v = dpp_add<0xb1, 0xf>(ua[J][m]);  // column 0 + column 1
+                        if (n == 0) sm.uu[16 * J + 4 * q + m] = v;
+                    }
+                }
+                // (I + L) e = 1 - b rho u by forward substitution; lane = row
+                float e = 1.f - sm.beta[sl][lane] * sm.rho[sl][lane] * sm.uu[lane];
 #pragma unroll
                 for (int i = 0; i < CH - 1; ++i) e = fmaf(-Lrow[i], lane_value(e, i), e);
-                sm.ee[s & 1][lane] = e;
-                sm.wc[lane] = __expf(sm.lr[s & 3][CH] - sm.lr[s & 3][lane + 1]) *
-                              sm.cc[s & 3][lane] * e;
+                const float lr1 = sm.lr[sl][lane + 1], ce = sm.cc[sl][lane] * e;
+                sm.wc[lane] = __expf(sm.lr[sl][CH] - lr1) * ce;
+                sm.ew[s & 1][lane] = __expf(sm.lr[sl][lane & 32] - lr1) * ce;
+                // carry d0 <- rho_C d0 + X^T w: A = [hi(w) ; lo(w) ; 0 ...], B = xh then xl
+                v8s aw[2];
+#pragma unroll
+                for (int st = 0; st < 2; ++st)
+                    aw[st] = split_frag(ld4(sm.wc + 32 * st + 8 * q), ld4(sm.wc + 32 * st + 8 * q + 4), n);
+                v4f ca[NF];
+                v8s fb[2][4];
+                auto read_c = [&](int F, v8s *f) __attribute__((always_inline)) {
+#pragma unroll
+                    for (int st = 0; st < 2; ++st) {
+                        const int col = 16 * F + 4 * (n & 3), r0 = 32 * st + 8 * q + (n >> 2);
+                        const int o0 = L::at(r0, col >> 3) + (col & 7);
+                        const int o1 = L::at(r0 + 4, col >> 3) + (col & 7);
+                        f[2 * st] = cat8(ld_tr(xh + o0), ld_tr(xh + o1));
+                        f[2 * st + 1] = cat8(ld_tr(xl + o0), ld_tr(xl + o1));
+                    }
+                };
+                read_c(0, fb[0]);
+#pragma unroll
+                for (int F = 0; F < NF; ++F) {
+                    if (F + 1 < NF) read_c(F + 1, fb[(F + 1) & 1]);
+                    ca[F] = zero4();
+#pragma unroll
+                    for (int st = 0; st < 2; ++st) {
+                        ca[F] = mfma32(aw[st], fb[F & 1][2 * st], ca[F]);
+                        ca[F] = mfma32(aw[st], fb[F & 1][2 * st + 1], ca[F]);
+                    }
+                }
+                if (q == 0) {  // rows 0 (hi(w) . x) and 1 (lo(w) . x) of column n
+                    const float rc = __expf(sm.lr[sl][CH]);
+                    float *dn = sm.d0[(s + 1) % 3];
+#pragma unroll
+                    for (int F = 0; F < NF; ++F)
+                        dn[16 * F + n] = rc * d0[16 * F + n] + ca[F][0] + ca[F][1];
+                }
             }
-        } else if (wave <= 4) {
-            if (s >= 1) {  // output of chunk s-1: D^T = rho-scaled d0 + X^T W^T
+            block_sync();
+        }
+    } else if (wave != 4 && wave != 5 && wave != 6) {
+        // output waves 1, 2, 3, 7
+        constexpr int FPW = NF / 4;  // 16-feature tiles per output wave
+        const int ow = wave == 7 ? 3 : wave - 1;
+        for (int s = -1; s <= nc; ++s) {
+            if (s + 1 < nc) gram2(s + 1, ow, ow + 4);
+            if (s >= 1) {  // output of chunk s-1: D^T = d0 rho^T + X^T W^T, W[j,i] = R c_i e_i
                 const int co = s - 1, sl = co & 3;
-                const uint16_t *xt = sm.xb[co % 3];
-                const float *ee = sm.ee[co & 1];
-                const float *lr = sm.lr[sl], *cc = sm.cc[sl];
-                constexpr int FPW = DK / 16 / 4;  // 16-feature tiles per output wave
+                const uint16_t *xt = sm.xh[sl];
+                const float *ew = sm.ew[co & 1], *lr = sm.lr[sl];
+                // W^T fragments for (row block J, token slice st): lane (q, n) holds
+                // W[16J + n][32 st + 8q + m] = e^{lr_j - lr_{32 st}} ew[i]  (i < j)
                 v8s wb[6];
 #pragma unroll
                 for (int J = 0, idx = 0; J < 4; ++J) {
 #pragma unroll
                     for (int st = 0; st <= (J >> 1); ++st, ++idx) {
-                        const int j = 16 * J + n;
-                        const float lrj = lr[j];
+                        const int j = 16 * J + n, i0 = 32 * st + 8 * q;
+                        const float ej = __expf(lr[j] - lr[32 * st]);
+                        const v4f w0 = ld4(ew + i0), w1 = ld4(ew + i0 + 4);
                         float wv[8];
 #pragma unroll
-                        for (int m = 0; m < 8; ++m) {
-                            const int i = 32 * st + 8 * q + m;
-                            wv[m] = i < j ? __expf(lrj - lr[i + 1]) * cc[i] * ee[i] : 0.f;
+                        for (int m = 0; m < 4; ++m) {
+                            wv[m] = i0 + m < j ? ej * w0[m] : 0.f;
+                            wv[m + 4] = i0 + 4 + m < j ? ej * w1[m] : 0.f;
                         }
                         wb[idx] = __builtin_bit_cast(
                             v8s, make_uint4(pack2(wv[0], wv[1]), pack2(wv[2], wv[3]),
                                             pack2(wv[4], wv[5]), pack2(wv[6], wv[7])));
                     }
                 }
-                const float *d0 = sm.d0[co & 1];
+                const float *d0 = sm.d0[co % 3];
 #pragma unroll
                 for (int ft = 0; ft < FPW; ++ft) {
-                    const int F = (wave - 1) * FPW + ft;
+                    const int F = ow * FPW + ft;
                     v8s xa[2];
 #pragma unroll
                     for (int st = 0; st < 2; ++st) {
@@ -337,71 +472,40 @@ precond_chunk_kernel(const uint16_t *__restrict__ k, const float *__restrict__ b
                     const v4f dv = ld4(d0 + 16 * F + 4 * q);
 #pragma unroll
                     for (int J = 0, idx = 0; J < 4; ++J) {
-                        const float rho = __expf(lr[16 * J + n]);
+                        const float rho = sm.rho[sl][16 * J + n];
                         v4f acc = v4f{rho * dv[0], rho * dv[1], rho * dv[2], rho * dv[3]};
 #pragma unroll
-                        for (int st = 0; st <= (J >> 1); ++st, ++idx) acc = mfma32(xa[st], wb[idx], acc);
+                        for (int st = 0; st <= (J >> 1); ++st, ++idx)
+                            acc = mfma32(xa[st], wb[idx], acc);
                         const int64_t tok = int64_t(co) * CH + 16 * J + n;
                         if (tok < T) store4(oq + tok * DK + 16 * F + 4 * q, acc);
                     }
                 }
             }
-        } else if (wave <= 6) {
-            if (s + 3 < nc) dma(s + 3, 32 * (wave - 5));
-        } else {
-            if (s + 2 < nc) scan(s + 2, bnext, rnext);
-            if (s + 3 < nc) gates(s + 3, bnext, rnext);
+            block_sync();
         }
-        block_sync();
-
-        // ---- phase C ----------------------------------------------------------------------
-        if (chain) {  // carry: d0 <- rho_C d0 + X^T (R[C,.] c e) over this wave's features
-            constexpr int FW = DK / NW;  // features per wave
-            constexpr int G = 64 / FW;   // row groups
-            const int f = wave * FW + lane % FW, g = lane / FW;
-            const uint16_t *kt = sm.kb[s & 3];
-            float acc = 0.f;
-#pragma unroll
-            for (int m = 0; m < CH / G; ++m) {
-                const int j = g + G * m;
-                const float kv = __uint_as_float(uint32_t(kt[L::at(j, f >> 3) + (f & 7)]) << 16);
-                acc += sm.wc[j] * (kv * kv);
-            }
-            if (G == 8) acc = dpp_add<0x128, 0xf>(acc);  // row_ror:8
-            acc = sum_rows(acc);                          // + lanes 16 and 32 away
-            if (g == 0)
-                sm.d0[(s + 1) & 1][f] = __expf(sm.lr[s & 3][CH]) * sm.d0[s & 1][f] + acc;
+    } else if (wave != 4) {
+        // keys of chunk c (waves 5 and 6): loaded into registers in step c-3, squared into LDS
+        // in step c-2
+        if (nc > 1) load_keys(1);
+        for (int s = -1; s <= nc; ++s) {
+            if (s + 2 < nc) square_keys(s + 2);
+            if (s + 3 < nc) load_keys(s + 3);
+            block_sync();
         }
-        if (prep) {  // Gram tiles of chunk s+1 -> L
-            const int cg = s + 1, sl = cg & 3;
-            const uint16_t *xt = sm.xb[cg % 3];
-            for (int tIdx = wave; tIdx < 10; tIdx += NW) {
-                const int J = tIdx < 1 ? 0 : tIdx < 3 ? 1 : tIdx < 6 ? 2 : 3;
-                const int I = tIdx - J * (J + 1) / 2;
-                v4f acc = zero4();
-#pragma unroll
-                for (int st = 0; st < DK / 32; ++st) {
-                    const int u = 4 * st + q;
-                    acc = mfma32(ld8(xt + L::at(16 * J + n, u)), ld8(xt + L::at(16 * I + n, u)), acc);
-                }
-                const int i = 16 * I + n;
-                const float ci = sm.cc[sl][i], lri = sm.lr[sl][i + 1];
-                float *Lt = sm.L[cg & 1];
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const int j = 16 * J + 4 * q + m;
-                    Lt[j * L::LP + i] =
-                        i < j ? sm.beta[sl][j] * __expf(sm.lr[sl][j] - lri) * ci * acc[m] : 0.f;
-                }
-            }
+    } else {
+        // gates of chunk c (wave 4, which shares a SIMD with the chain wave, so its load is
+        // light): loaded in step c-3, scanned in step c-2
+        float bv = 0.f, rv = 1.f;
+        if (nc > 1) gates(1, bv, rv);
+        for (int s = -1; s <= nc; ++s) {
+            if (s + 2 < nc) scan(s + 2, bv, rv);
+            if (s + 3 < nc) gates(s + 3, bv, rv);
+            if (s + 1 < nc) gram2(s + 1, 8, 9);
+            block_sync();
         }
-        if (wave == 5 || wave == 6) {  // keys of chunk s+2 have landed
-            if (s + 3 < nc) wait_global_n<32 * L::KU / 64>();
-            else wait_global();
-        }
-        block_sync();
     }
-    if (d_next && threadIdx.x < DK) d_next[bh * DK + threadIdx.x] = sm.d0[nc & 1][threadIdx.x];
+    if (d_next && threadIdx.x < DK) d_next[bh * DK + threadIdx.x] = sm.d0[nc % 3][threadIdx.x];
 }
 
 template <int DK>
