@@ -33,10 +33,12 @@
 //     wave 0      the chain of chunk s: X d0 (A = xh, xl rows; B = hi/lo of d0 in columns 0
 //                 and 1), the forward substitution (row j of L in lane j's registers, 63
 //                 broadcast-and-update steps), the carry d0 <- rho_C d0 + X^T w
-//                 (A = hi/lo of w in rows 0 and 1; B = xh, xl by transposing LDS reads);
+//                 (A = hi/lo of w in rows 0 and 1; B = xh, xl by transposing LDS reads); d0
+//                 and w are kept as bf16 hi/lo pairs too, ready as operands;
 //     waves 1-3, 7  the output of chunk s-1 as D^T = X^T W^T (W built in registers from one
-//                 exponential per fragment and per-token factors), stored as 16-byte rows
-//                 of d, and two Gram tiles of chunk s+1 each;
+//                 exponential per fragment and per-token factors; each wave takes two token
+//                 row blocks and half of the features), stored as 16-byte rows of d, and two
+//                 Gram tiles of chunk s+1 each;
 //     waves 5-6   keys of chunk s+2 squared from registers into xh, xl and the row norms,
 //                 then the keys of chunk s+3 loaded into registers (a step of latency hidden);
 //     wave 4      the gate scan of chunk s+2, the gate loads of chunk s+3 and two Gram tiles
@@ -156,7 +158,8 @@ struct alignas(16) PrecondLds {
     alignas(16) float rho[4][CH];         // e^{lr_j}
     alignas(16) float d0[3][DK];          // [chunk mod 3] start state of the chunk
     alignas(16) float ew[2][CH];          // [chunk parity] e^{lr_{32(i/32)} - lr_{i+1}} c_i e_i
-    alignas(16) float wc[CH];             // the chain wave's R[C,j] c_j e_j
+    alignas(16) uint16_t dsp[2][2][DK];   // [chunk parity][hi, lo] bf16 split of d0
+    alignas(16) uint16_t wsp[2][CH];      // [hi, lo] bf16 split of w = R[C,.] c e
     alignas(16) float uu[CH];             // the chain wave's X d0
 };
 
@@ -172,18 +175,18 @@ __device__ __forceinline__ float wave_prefix(float x) {
     return x;
 }
 
-// eight fp32 values -> hi = bf16(v) and lo = bf16(v - hi), as operand fragments for the lanes
-// of column (or row) 0 and 1 of a 16x16x32 product; other lanes get zero
-__device__ __forceinline__ v8s split_frag(v4f a, v4f b, int n) {
-    const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t h = pack2(v[2 * i], v[2 * i + 1]);
-        const uint32_t l = pack2(v[2 * i] - bf_lo(h), v[2 * i + 1] - bf_hi(h));
-        w[i] = n == 0 ? h : (n == 1 ? l : 0u);
-    }
-    return __builtin_bit_cast(v8s, make_uint4(w[0], w[1], w[2], w[3]));
+// an fp32 value -> (bf16(v), bf16(v - bf16(v))) as raw bits
+__device__ __forceinline__ void split1(float v, uint16_t &hi, uint16_t &lo) {
+    const uint32_t p = pack2(v, 0.f);
+    hi = static_cast<uint16_t>(p);
+    lo = static_cast<uint16_t>(pack2(v - bf_lo(p), 0.f));
+}
+// operand fragment whose lanes of column (or row) 0 hold eight hi values and of column 1 the
+// matching lo values (from a [hi, lo] pair of bf16 arrays); other lanes hold zero
+__device__ __forceinline__ v8s split_frag(const uint16_t *hi, const uint16_t *lo, int off, int n) {
+    const v8s x = ld8((n == 1 ? lo : hi) + off);
+    const v8s z = {0, 0, 0, 0, 0, 0, 0, 0};
+    return n < 2 ? x : z;
 }
 
 template <int DK, typename TD>
@@ -313,7 +316,11 @@ precond_chunk_kernel(const uint16_t *__restrict__ k, const float *__restrict__ b
     // ---- prologue: zero L (its upper part is never written), d0 of chunk 0, x of chunk 0,
     // gates of chunk 0 scanned
     for (int i = threadIdx.x; i < 2 * CH * L::LP; i += NT) (&sm.L[0][0])[i] = 0.f;
-    if (threadIdx.x < DK) sm.d0[0][threadIdx.x] = d1 ? d1[bh * DK + threadIdx.x] : 1.f;
+    if (threadIdx.x < DK) {
+        const float v = d1 ? d1[bh * DK + threadIdx.x] : 1.f;
+        sm.d0[0][threadIdx.x] = v;
+        split1(v, sm.dsp[0][0][threadIdx.x], sm.dsp[0][1][threadIdx.x]);
+    }
     if (nc > 0) {
         if (wave == 5 || wave == 6) {
             load_keys(0);
@@ -355,7 +362,8 @@ precond_chunk_kernel(const uint16_t *__restrict__ k, const float *__restrict__ b
 #pragma unroll
                 for (int st = 0; st < KS; ++st) {
                     if (st + 1 < KS) read_u(st + 1, fa[(st + 1) & 1]);
-                    const v8s b = split_frag(ld4(d0 + 32 * st + 8 * q), ld4(d0 + 32 * st + 8 * q + 4), n);
+                    const v8s b = split_frag(sm.dsp[s & 1][0], sm.dsp[s & 1][1], 32 * st + 8 * q, n);
+                    __builtin_amdgcn_sched_barrier(0);  // the next slice's reads stay ahead
 #pragma unroll
                     for (int J = 0; J < 4; ++J) {
                         ua[J] = mfma32(fa[st & 1][2 * J], b, ua[J]);
@@ -385,13 +393,12 @@ precond_chunk_kernel(const uint16_t *__restrict__ k, const float *__restrict__ b
 #pragma unroll
                 for (int i = 0; i < CH - 1; ++i) e = fmaf(-Lrow[i], lane_value(e, i), e);
                 const float lr1 = sm.lr[sl][lane + 1], ce = sm.cc[sl][lane] * e;
-                sm.wc[lane] = __expf(sm.lr[sl][CH] - lr1) * ce;
+                split1(__expf(sm.lr[sl][CH] - lr1) * ce, sm.wsp[0][lane], sm.wsp[1][lane]);
                 sm.ew[s & 1][lane] = __expf(sm.lr[sl][lane & 32] - lr1) * ce;
                 // carry d0 <- rho_C d0 + X^T w: A = [hi(w) ; lo(w) ; 0 ...], B = xh then xl
                 v8s aw[2];
 #pragma unroll
-                for (int st = 0; st < 2; ++st)
-                    aw[st] = split_frag(ld4(sm.wc + 32 * st + 8 * q), ld4(sm.wc + 32 * st + 8 * q + 4), n);
+                for (int st = 0; st < 2; ++st) aw[st] = split_frag(sm.wsp[0], sm.wsp[1], 32 * st + 8 * q, n);
                 v4f ca[NF];
                 v8s fb[2][4];
                 auto read_c = [&](int F, v8s *f) __attribute__((always_inline)) {
@@ -408,6 +415,7 @@ precond_chunk_kernel(const uint16_t *__restrict__ k, const float *__restrict__ b
 #pragma unroll
                 for (int F = 0; F < NF; ++F) {
                     if (F + 1 < NF) read_c(F + 1, fb[(F + 1) & 1]);
+                    __builtin_amdgcn_sched_barrier(0);  // the next tile's reads stay ahead
                     ca[F] = zero4();
 #pragma unroll
                     for (int st = 0; st < 2; ++st) {
@@ -419,47 +427,50 @@ precond_chunk_kernel(const uint16_t *__restrict__ k, const float *__restrict__ b
                     const float rc = __expf(sm.lr[sl][CH]);
                     float *dn = sm.d0[(s + 1) % 3];
 #pragma unroll
-                    for (int F = 0; F < NF; ++F)
-                        dn[16 * F + n] = rc * d0[16 * F + n] + ca[F][0] + ca[F][1];
+                    for (int F = 0; F < NF; ++F) {
+                        const int f = 16 * F + n;
+                        const float v = rc * d0[f] + ca[F][0] + ca[F][1];
+                        dn[f] = v;
+                        split1(v, sm.dsp[(s + 1) & 1][0][f], sm.dsp[(s + 1) & 1][1][f]);
+                    }
                 }
             }
             block_sync();
         }
     } else if (wave != 4 && wave != 5 && wave != 6) {
-        // output waves 1, 2, 3, 7
-        constexpr int FPW = NF / 4;  // 16-feature tiles per output wave
+        // output waves 1, 2, 3, 7: wave ow takes the token row blocks {0, 3} or {1, 2} (the
+        // same number of products) and one half of the feature tiles
         const int ow = wave == 7 ? 3 : wave - 1;
+        const int Ja = (ow & 1) ? 1 : 0, Jb = 3 - Ja;  // Ja < 2 needs one token slice, Jb two
         for (int s = -1; s <= nc; ++s) {
             if (s + 1 < nc) gram2(s + 1, ow, ow + 4);
             if (s >= 1) {  // output of chunk s-1: D^T = d0 rho^T + X^T W^T, W[j,i] = R c_i e_i
                 const int co = s - 1, sl = co & 3;
                 const uint16_t *xt = sm.xh[sl];
                 const float *ew = sm.ew[co & 1], *lr = sm.lr[sl];
-                // W^T fragments for (row block J, token slice st): lane (q, n) holds
+                // W^T fragment for (row block J, token slice st): lane (q, n) holds
                 // W[16J + n][32 st + 8q + m] = e^{lr_j - lr_{32 st}} ew[i]  (i < j)
-                v8s wb[6];
+                auto wfrag = [&](int J, int st) __attribute__((always_inline)) {
+                    const int j = 16 * J + n, i0 = 32 * st + 8 * q;
+                    const float ej = __expf(lr[j] - lr[32 * st]);
+                    const v4f w0 = ld4(ew + i0), w1 = ld4(ew + i0 + 4);
+                    float wv[8];
 #pragma unroll
-                for (int J = 0, idx = 0; J < 4; ++J) {
-#pragma unroll
-                    for (int st = 0; st <= (J >> 1); ++st, ++idx) {
-                        const int j = 16 * J + n, i0 = 32 * st + 8 * q;
-                        const float ej = __expf(lr[j] - lr[32 * st]);
-                        const v4f w0 = ld4(ew + i0), w1 = ld4(ew + i0 + 4);
-                        float wv[8];
-#pragma unroll
-                        for (int m = 0; m < 4; ++m) {
-                            wv[m] = i0 + m < j ? ej * w0[m] : 0.f;
-                            wv[m + 4] = i0 + 4 + m < j ? ej * w1[m] : 0.f;
-                        }
-                        wb[idx] = __builtin_bit_cast(
-                            v8s, make_uint4(pack2(wv[0], wv[1]), pack2(wv[2], wv[3]),
-                                            pack2(wv[4], wv[5]), pack2(wv[6], wv[7])));
+                    for (int m = 0; m < 4; ++m) {
+                        wv[m] = i0 + m < j ? ej * w0[m] : 0.f;
+                        wv[m + 4] = i0 + 4 + m < j ? ej * w1[m] : 0.f;
                     }
-                }
+                    return __builtin_bit_cast(
+                        v8s, make_uint4(pack2(wv[0], wv[1]), pack2(wv[2], wv[3]),
+                                        pack2(wv[4], wv[5]), pack2(wv[6], wv[7])));
+                };
+                const v8s wa = wfrag(Ja, 0), wb0 = wfrag(Jb, 0), wb1 = wfrag(Jb, 1);
                 const float *d0 = sm.d0[co % 3];
+                const float rA = sm.rho[sl][16 * Ja + n], rB = sm.rho[sl][16 * Jb + n];
+                const int64_t tA = int64_t(co) * CH + 16 * Ja + n, tB = int64_t(co) * CH + 16 * Jb + n;
 #pragma unroll
-                for (int ft = 0; ft < FPW; ++ft) {
-                    const int F = ow * FPW + ft;
+                for (int ft = 0; ft < NF / 2; ++ft) {
+                    const int F = (ow >> 1) * (NF / 2) + ft;
                     v8s xa[2];
 #pragma unroll
                     for (int st = 0; st < 2; ++st) {
@@ -470,16 +481,13 @@ precond_chunk_kernel(const uint16_t *__restrict__ k, const float *__restrict__ b
                         xa[st] = cat8(lo, hi);
                     }
                     const v4f dv = ld4(d0 + 16 * F + 4 * q);
-#pragma unroll
-                    for (int J = 0, idx = 0; J < 4; ++J) {
-                        const float rho = sm.rho[sl][16 * J + n];
-                        v4f acc = v4f{rho * dv[0], rho * dv[1], rho * dv[2], rho * dv[3]};
-#pragma unroll
-                        for (int st = 0; st <= (J >> 1); ++st, ++idx)
-                            acc = mfma32(xa[st], wb[idx], acc);
-                        const int64_t tok = int64_t(co) * CH + 16 * J + n;
-                        if (tok < T) store4(oq + tok * DK + 16 * F + 4 * q, acc);
-                    }
+                    v4f accA = v4f{rA * dv[0], rA * dv[1], rA * dv[2], rA * dv[3]};
+                    v4f accB = v4f{rB * dv[0], rB * dv[1], rB * dv[2], rB * dv[3]};
+                    accA = mfma32(xa[0], wa, accA);
+                    accB = mfma32(xa[0], wb0, accB);
+                    accB = mfma32(xa[1], wb1, accB);
+                    if (tA < T) store4(oq + tA * DK + 16 * F + 4 * q, accA);
+                    if (tB < T) store4(oq + tB * DK + 16 * F + 4 * q, accB);
                 }
             }
             block_sync();
