@@ -33,9 +33,11 @@ if ROOT not in sys.path:
 METRIC = "tokens/s + TFLOP/s (fraction of bf16 MFMA peak), OSDN chunkwise fwd"
 PEAK_HBM = 8.0e12      # bytes/s, MI355X HBM3E
 PEAK_BF16 = 2.5e15     # FLOP/s, MI355X dense bf16 matrix peak
-CHUNK_KERNEL_SRC = ["delta_rule_sequence_chunkwise_amd/csrc/osdn_chunk_mfma.hip"]
+CHUNK_KERNEL_SRC = ["delta_rule_sequence_chunkwise_amd/csrc/osdn_chunk_mfma.hip",
+                    "delta_rule_sequence_chunkwise_amd/csrc/osdn_mfma.h"]
 STEP_KERNEL_SRC = ["delta_rule_sequence_chunkwise_amd/csrc/osdn_step.hip"]
-PRECOND_KERNEL_SRC = ["delta_rule_sequence_chunkwise_amd/csrc/osdn_precond.hip"]
+PRECOND_KERNEL_SRC = ["delta_rule_sequence_chunkwise_amd/csrc/osdn_precond.hip",
+                      "delta_rule_sequence_chunkwise_amd/csrc/osdn_mfma.h"]
 
 
 def flops_per_head_token(dk, dv, C):

@@ -11,7 +11,7 @@ Attention, technical summary):
   hypergradient surrogate h_t(d) = (f_t(S_t) - f_t(S_{t-1})) / ||grad f_t(S_{t-1})||_F^2, whose
   closed form ((1 - b_t <d, k_t^2>)^2 - 1) / (2 ||k_t||^2) depends on k_t and b_t only.  Its
   gradient is  grad_d h_t(d) = -b_t (1 - b_t <d, k_t^2>) k_t^2 / ||k_t||^2 ;
-  Phase 1 is the sequential O(dk) scan over the key stream that produces every d_t;
+  Phase 1 walks the keys in order, carrying only the dk-vector d, and emits every d_t;
 * section 2.3 (APF) -- a per-token, per-head retention gate r_t multiplies the preconditioner
   state (and nothing else) before the gradient step.
 
