@@ -108,3 +108,42 @@ def precond_scan(k, beta, eta: float, r=None, d1=None, chunk: int = 64
                 d0 = Dall[n]
             d_next[b, h] = d0
     return out, d_next
+
+
+def chunk_fwd_channel(q, k, v, beta, d, alpha_ch, S0=None, chunk: int = 64
+                      ) -> Tuple[np.ndarray, np.ndarray]:
+    """Chunk form of the recurrence with a channel-wise gate a_t in R^dk (Erase-then-Delta
+    Attention, section 2.2, eq. 5) and the OSDN write key k~ = d (.) k; derived here.
+
+    Inside a chunk let G_r = prod_{s<=r} a_s (per feature, inclusive).  Unrolling
+    M_r = Diag(a_r) M_{r-1} + k~_r u_r^T gives M_r = Diag(G_r) M0 + sum_{s<=r} Diag(G_r / G_s) k~_s u_s^T,
+    so with the operands scaled per feature,  q' = q G,  k' = k G,  k~' = k~ / G,
+    every decay factor folds into them:
+        (I + A) U = diag(b) (V - K' M0),  A[r,s] = b_r <k'_r, k~'_s>  (s < r),
+        O = Q' M0 + lower_incl(Q' K~'^T) U,
+        M_C = Diag(G_C) (M0 + K~'^T U).
+    """
+    q, k, v, beta, d, alpha_ch = (np.asarray(x, dtype=np.float64)
+                                  for x in (q, k, v, beta, d, alpha_ch))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    o = np.zeros((B, H, T, dv))
+    S_T = np.zeros((B, H, dk, dv))
+    for b in range(B):
+        for h in range(H):
+            M = np.zeros((dk, dv)) if S0 is None else np.array(S0[b, h], dtype=np.float64)
+            for c0 in range(0, T, chunk):
+                c1 = min(c0 + chunk, T)
+                G = np.cumprod(alpha_ch[b, h, c0:c1], axis=0)
+                Qp = q[b, h, c0:c1] * G
+                Kp = k[b, h, c0:c1] * G
+                Ktp = d[b, h, c0:c1] * k[b, h, c0:c1] / G
+                bet = beta[b, h, c0:c1]
+                n = c1 - c0
+                A = np.tril(bet[:, None] * (Kp @ Ktp.T), -1)
+                rhs = bet[:, None] * (v[b, h, c0:c1] - Kp @ M)
+                U = solve_triangular(np.eye(n) + A, rhs, lower=True, unit_diagonal=True)
+                o[b, h, c0:c1] = Qp @ M + np.tril(Qp @ Ktp.T) @ U
+                M = G[-1][:, None] * (M + Ktp.T @ U)
+            S_T[b, h] = M
+    return o, S_T

@@ -15,11 +15,16 @@
  *        S_t = S_{t-1} + beta_t (v_t - S_{t-1} k_t) k~_t^T .
  *   Gated form (Erase-then-Delta Attention, section 2.2, eq. 4): a per-head scalar
  *   alpha_t in (0,1] decays the old state before the delta step.
+ *   Channel-wise form (Erase-then-Delta Attention, section 2.2, eq. 5, the Kimi Delta
+ *   Attention gate; section 3.2, eq. 7): a per-token diagonal Diag(a_t), one retention
+ *   factor per key feature, decays the old state (its key-indexed rows) before the delta
+ *   step, in place of (or on top of) the scalar gate.
  *   Read-out (Erase-then-Delta Attention, section 2.1, eq. 1): o_t = S_t^T q_t in that
  *   page's dk x dv convention, i.e. after the write.
  *
  * Storage convention: M = S^T in R^{dk x dv}, row-major [dk][dv] per (b,h).  One token is
- *        M <- alpha_t M
+ *        M <- alpha_t M                     (scalar gate), then
+ *        M[i][:] <- a_t[i] M[i][:]          (channel-wise gate), then
  *        r <- v_t - M^T k_t
  *        M <- M + beta_t (d_t (.) k_t) r^T
  *        o_t <- M^T q_t
@@ -32,7 +37,7 @@
 #include <string.h>
 
 typedef struct {
-    const double *q, *k, *v, *beta, *d, *alpha, *S0;
+    const double *q, *k, *v, *beta, *d, *alpha, *alpha_ch, *S0;
     double *o, *S_T;
     int64_t BH, T, dk, dv;
     int64_t first, stride;
@@ -48,6 +53,7 @@ static int run_sequence(const oracle_job *J, int64_t bh) {
     const double *beta = J->beta + bh * T;
     const double *d = J->d + bh * T * dk;
     const double *alpha = J->alpha ? J->alpha + bh * T : NULL;
+    const double *alpha_ch = J->alpha_ch ? J->alpha_ch + bh * T * dk : NULL;
     double *o = J->o ? J->o + bh * T * dv : NULL;
 
     double *M = (double *)malloc((size_t)(dk * dv) * sizeof(double));
@@ -67,8 +73,11 @@ static int run_sequence(const oracle_job *J, int64_t bh) {
         const double a = alpha ? alpha[t] : 1.0;
         const double b = beta[t];
 
-        /* decay of the old state */
+        /* decay of the old state: scalar gate, then one factor per key feature (row) */
         for (int64_t i = 0; i < dk * dv; ++i) M[i] *= a;
+        if (alpha_ch)
+            for (int64_t i = 0; i < dk; ++i)
+                for (int64_t j = 0; j < dv; ++j) M[i * dv + j] *= alpha_ch[t * dk + i];
 
         /* residual against the plain key: r = v - M^T k */
         for (int64_t j = 0; j < dv; ++j) r[j] = vt[j];
@@ -104,15 +113,16 @@ static void *worker(void *arg) {
 }
 
 /*
- * q, k, d: [B,H,T,dk]; v: [B,H,T,dv]; beta: [B,H,T]; alpha: [B,H,T] or NULL (no decay);
- * S0: [B,H,dk,dv] or NULL (zero state); o: [B,H,T,dv] or NULL; S_T: [B,H,dk,dv] or NULL.
+ * q, k, d: [B,H,T,dk]; v: [B,H,T,dv]; beta: [B,H,T]; alpha: [B,H,T] or NULL (no scalar
+ * decay); alpha_ch: [B,H,T,dk] or NULL (no channel-wise decay); S0: [B,H,dk,dv] or NULL
+ * (zero state); o: [B,H,T,dv] or NULL; S_T: [B,H,dk,dv] or NULL.
  * S_T may equal S0 (each sequence copies its S0 slice before writing S_T).
  * Returns 0 on success, -1 on bad arguments or allocation failure.
  */
-int osdn_oracle_fwd(const double *q, const double *k, const double *v, const double *beta,
-                    const double *d, const double *alpha, const double *S0, double *o,
-                    double *S_T, int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
-                    int nthreads) {
+int osdn_oracle_fwd2(const double *q, const double *k, const double *v, const double *beta,
+                     const double *d, const double *alpha, const double *alpha_ch,
+                     const double *S0, double *o, double *S_T, int64_t B, int64_t H, int64_t T,
+                     int64_t dk, int64_t dv, int nthreads) {
     if (!q || !k || !v || !beta || !d) return -1;
     if (B < 0 || H < 0 || T < 0 || dk <= 0 || dv <= 0) return -1;
     const int64_t BH = B * H;
@@ -127,7 +137,8 @@ int osdn_oracle_fwd(const double *q, const double *k, const double *v, const dou
         return -1;
     }
     for (int w = 0; w < nthreads; ++w) {
-        oracle_job J = {q, k, v, beta, d, alpha, S0, o, S_T, BH, T, dk, dv, w, nthreads, 0};
+        oracle_job J = {q, k, v, beta, d, alpha, alpha_ch, S0, o, S_T, BH, T, dk, dv,
+                        w, nthreads, 0};
         jobs[w] = J;
     }
     int status = 0;
@@ -148,4 +159,13 @@ int osdn_oracle_fwd(const double *q, const double *k, const double *v, const dou
     free(jobs);
     free(tid);
     return status;
+}
+
+/* The same without the channel-wise gate. */
+int osdn_oracle_fwd(const double *q, const double *k, const double *v, const double *beta,
+                    const double *d, const double *alpha, const double *S0, double *o,
+                    double *S_T, int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv,
+                    int nthreads) {
+    return osdn_oracle_fwd2(q, k, v, beta, d, alpha, NULL, S0, o, S_T, B, H, T, dk, dv,
+                            nthreads);
 }
