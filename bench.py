@@ -15,7 +15,10 @@ HBM.  Prints ONE JSON line.  Besides the contract fields it carries:
                 `--decode-steps` consecutive calls (state updated in place);
   precond_scan  the Phase-1 preconditioner scan (osdn_precond_scan, chunkwise form) over the
                 same workload's keys and gates, with its own HBM roofline, its oracle timed on
-                the host, and the forward with the scan in front (scan + chunkwise forward).
+                the host, and the forward with the scan in front (scan + chunkwise forward);
+  kda           the forward with the channel-wise gate (osdn_chunk_fwd_kda: the gate-scaling
+                kernel, then the chunkwise forward) on the same workload with a per-feature
+                gate, with its HBM roofline and the parity of its output.
 """
 from __future__ import annotations
 
@@ -36,6 +39,8 @@ PEAK_BF16 = 2.5e15     # FLOP/s, MI355X dense bf16 matrix peak
 CHUNK_KERNEL_SRC = ["delta_rule_sequence_chunkwise_amd/csrc/osdn_chunk_mfma.hip",
                     "delta_rule_sequence_chunkwise_amd/csrc/osdn_mfma.h"]
 STEP_KERNEL_SRC = ["delta_rule_sequence_chunkwise_amd/csrc/osdn_step.hip"]
+KDA_PREP_SRC = ["delta_rule_sequence_chunkwise_amd/csrc/osdn_kda.hip",
+                "delta_rule_sequence_chunkwise_amd/csrc/osdn_mfma.h"]
 PRECOND_KERNEL_SRC = ["delta_rule_sequence_chunkwise_amd/csrc/osdn_precond.hip",
                       "delta_rule_sequence_chunkwise_amd/csrc/osdn_mfma.h"]
 
@@ -80,6 +85,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--precond-steps", type=int, default=20)
+    ap.add_argument("--kda-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="1.3b")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -205,7 +211,65 @@ def main():
                                              (q, k, v, beta, alpha, S0, o, S_T),
                                              not args.no_cpu_baseline)
 
+    if args.kda_steps > 0:
+        line["kda"] = bench_kda(args.kda_steps, torch, dev, synth, w, x, (q, k, v, beta, d, S0),
+                                not args.no_cpu_baseline)
+
     print(json.dumps(line), flush=True)
+
+
+def bench_kda(n_steps, torch, dev, synth, w, x, fwd, cpu):
+    """Times `n_steps` osdn_chunk_fwd_kda calls (gate scaling + forward) on the workload with a
+    channel-wise gate in place of the scalar one."""
+    import numpy as np
+    from delta_rule_sequence_chunkwise_amd import osdn
+
+    B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
+    q, k, v, beta, d, S0 = fwd
+    a_np = synth.make_channel_gate(B, H, T, dk, seed=w.seed)
+    a = torch.from_numpy(a_np).to(dev)
+    o = torch.empty((B, H, T, dv), dtype=q.dtype, device=dev)
+    S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(osdn.kda_workspace_bytes(B, H, T, dk, w.chunk, osdn.OSDN_BF16),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        osdn.osdn_chunk_fwd_kda(q, k, v, beta, d, a, S0, chunk=w.chunk, o=o, S_T=S_T,
+                                workspace=ws)
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n_steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    per = e0.elapsed_time(e1) / 1e3 / n_steps
+    head_tokens = B * H * T
+    # q, k, v, o in bf16; d and the channel gate in fp32; beta; the final state
+    alg = head_tokens * ((2 * dk + 2 * dv) * 2 + dk * 4 + dk * 4 + 4) \
+        + B * H * dk * dv * 4 * (2 if S0 is not None else 1)
+    rec = {"workload": f"{w.name}-shape forward with a channel-wise gate a[B,H,T,dk] in place "
+                       f"of the scalar one: B={B} H={H} T={T} dk={dk} dv={dv}, bf16 q/k/v/o, fp32 "
+                       "beta/d/gate, fp32 final state",
+           "ms_per_step": round(per * 1e3, 4),
+           "tokens_per_s": round(B * T / per, 1),
+           "roofline": {"bound": "hbm", "achieved": round(alg / per / 1e9, 2),
+                        "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                        "frac": round(alg / per / PEAK_HBM, 5), "alg_bytes_per_step": alg,
+                        "note": "two launches: the gate-scaling kernel writes and the forward "
+                                "reads gate-scaled q, k, d (workspace traffic beyond alg)"}}
+    if cpu:
+        import oracle
+        o_ref, S_ref = oracle.chunk_fwd(x["q"], x["k"], x["v"], x["beta"], x["d"], None,
+                                        x["S0"], alpha_ch=a_np)
+        rel = lambda p, r: float(np.max(np.abs(p - r)) / np.max(np.abs(r)))
+        rec["parity"] = {"e_o": rel(o.float().cpu().numpy(), o_ref),
+                         "e_S": rel(S_T.cpu().numpy(), S_ref), "tol": 2e-2}
+    return rec
 
 
 def bench_decode(n_steps, torch, dev, synth, distinct=64):

@@ -225,4 +225,147 @@ osdn_status osdn_precond_step(const void *k, const float *beta, const float *r, 
     return err == hipSuccess ? OSDN_OK : OSDN_ERR_LAUNCH;
 }
 
+namespace {
+
+int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
+
+// byte offsets of the channel-wise gate's workspace: q', k', d', G_C
+struct KdaLayout {
+    int64_t q, k, d, g, total;
+};
+
+bool kda_layout(int64_t B, int64_t H, int64_t T, int32_t dk, int32_t chunk, osdn_dtype qkv,
+                KdaLayout &L) {
+    if (B < 0 || H < 0 || T < 0 || !dtype_ok(qkv) || !head_dim_ok(dk)) return false;
+    if (qkv == OSDN_BF16 ? chunk != 64 : (chunk != 16 && chunk != 32 && chunk != 64))
+        return false;
+    int64_t n = 1;
+    if (!mul_ok(n, B, kMaxElems) || !mul_ok(n, H, kMaxElems) || !mul_ok(n, T, kMaxElems) ||
+        !mul_ok(n, dk, kMaxElems))
+        return false;
+    int64_t ng = 1;
+    if (!mul_ok(ng, B, kMaxElems) || !mul_ok(ng, H, kMaxElems) ||
+        !mul_ok(ng, (T + chunk - 1) / chunk, kMaxElems) || !mul_ok(ng, dk, kMaxElems))
+        return false;
+    const int64_t eq = elem_size(qkv), ed = qkv == OSDN_BF16 ? 2 : 4;
+    L.q = 0;
+    L.k = round256(n * eq);
+    L.d = L.k + round256(n * eq);
+    L.g = L.d + round256(n * ed);
+    L.total = L.g + round256(ng * 4);
+    return true;
+}
+
+}  // namespace
+
+int64_t osdn_chunk_fwd_kda_workspace(int64_t B, int64_t H, int64_t T, int32_t dk,
+                                     int32_t chunk, osdn_dtype qkv) {
+    KdaLayout L;
+    return kda_layout(B, H, T, dk, chunk, qkv, L) ? L.total : -1;
+}
+
+osdn_status osdn_chunk_fwd_kda(const void *q, const void *k, const void *v, const float *beta,
+                               const void *d, const float *alpha_ch, const float *S0, void *o,
+                               float *S_T, void *workspace, int64_t workspace_bytes,
+                               int64_t B, int64_t H, int64_t T, int32_t dk, int32_t dv,
+                               int32_t chunk, osdn_dtype qkv, osdn_dtype d_dtype,
+                               void *stream) {
+    if (B < 0 || H < 0 || T < 0) return OSDN_ERR_SHAPE;
+    if (!dtype_ok(qkv) || !dtype_ok(d_dtype)) return OSDN_ERR_UNSUPPORTED;
+    if (!head_dim_ok(dk) || !head_dim_ok(dv)) return OSDN_ERR_UNSUPPORTED;
+    if (qkv == OSDN_BF16 ? chunk != 64 : (chunk != 16 && chunk != 32 && chunk != 64))
+        return OSDN_ERR_UNSUPPORTED;
+    KdaLayout W;
+    if (!kda_layout(B, H, T, dk, chunk, qkv, W)) return OSDN_ERR_SHAPE;
+    int64_t BH = 1, tok = 1, st = 1;
+    if (!mul_ok(BH, B, kMaxElems) || !mul_ok(BH, H, kMaxElems)) return OSDN_ERR_SHAPE;
+    tok = BH;
+    if (!mul_ok(tok, T, kMaxElems)) return OSDN_ERR_SHAPE;
+    int64_t nqk = tok, nv = tok;
+    if (!mul_ok(nqk, dk, kMaxElems) || !mul_ok(nv, dv, kMaxElems)) return OSDN_ERR_SHAPE;
+    st = BH;
+    if (!mul_ok(st, int64_t(dk) * dv, kMaxElems)) return OSDN_ERR_SHAPE;
+    if (BH > int64_t(0x7fffffff) / 4) return OSDN_ERR_SHAPE;
+    const int64_t nchunks = (T + chunk - 1) / chunk;
+    if (BH * nchunks > int64_t(0x7fffffff)) return OSDN_ERR_SHAPE;  // prep grid
+
+    if (BH == 0) return OSDN_OK;
+    if (T > 0 && (!q || !k || !v || !beta || !d || !alpha_ch || !o || !workspace))
+        return OSDN_ERR_NULL;
+    if (T == 0 && !S_T) return OSDN_OK;
+    if (T > 0 && workspace_bytes < W.total) return OSDN_ERR_SHAPE;
+
+    const int64_t eq = elem_size(qkv), ed = elem_size(d_dtype);
+    if (T > 0) {
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(d, 16) ||
+            !aligned(o, 16) || !aligned(beta, 4) || !aligned(alpha_ch, 4) ||
+            !aligned(workspace, 256))
+            return OSDN_ERR_ALIGN;
+    }
+    if ((S0 && !aligned(S0, 16)) || (S_T && !aligned(S_T, 16))) return OSDN_ERR_ALIGN;
+
+    const int64_t n_tok = T > 0 ? tok : 0;
+    const Range rq = range_of(q, n_tok ? nqk * eq : 0), rk = range_of(k, n_tok ? nqk * eq : 0);
+    const Range rv = range_of(v, n_tok ? nv * eq : 0), rd = range_of(d, n_tok ? nqk * ed : 0);
+    const Range rb = range_of(beta, n_tok * 4), ra = range_of(alpha_ch, n_tok ? nqk * 4 : 0);
+    const Range rs0 = range_of(S0, st * 4), rst = range_of(S_T, st * 4);
+    const Range ro = range_of(o, n_tok ? nv * eq : 0);
+    const Range rw = range_of(workspace, T > 0 ? W.total : 0);
+    for (const Range *in : {&rq, &rk, &rv, &rd, &rb, &ra, &rs0, &rst})
+        if (overlap(ro, *in)) return OSDN_ERR_ALIAS;
+    for (const Range *in : {&rq, &rk, &rv, &rd, &rb, &ra})
+        if (overlap(rst, *in)) return OSDN_ERR_ALIAS;
+    if (overlap(rst, rs0) && (rst.lo != rs0.lo)) return OSDN_ERR_ALIAS;
+    for (const Range *in : {&rq, &rk, &rv, &rd, &rb, &ra, &rs0, &rst, &ro})
+        if (overlap(rw, *in)) return OSDN_ERR_ALIAS;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    float *gcs = T > 0 ? reinterpret_cast<float *>(ws + W.g) : nullptr;
+    const osdn_dtype dp_dtype = qkv == OSDN_BF16 ? OSDN_BF16 : OSDN_F32;
+    if (T > 0) {
+        osdn::KdaPrepArgs p{q, k, d, alpha_ch, ws + W.q, ws + W.k, ws + W.d, gcs, BH, T,
+                            nchunks, dk, chunk, qkv, d_dtype};
+        if (osdn::launch_kda_prep(p, s) != hipSuccess) return OSDN_ERR_LAUNCH;
+    }
+    osdn::ChunkArgs a{T > 0 ? ws + W.q : q, T > 0 ? ws + W.k : k, v, T > 0 ? ws + W.d : d,
+                      beta, nullptr, S0, o, S_T, BH, T, dk, dv, chunk, qkv, dp_dtype, gcs};
+    const hipError_t err = qkv == OSDN_BF16 ? osdn::launch_chunk_fwd_mfma(a, s)
+                                            : osdn::launch_chunk_fwd_f32math(a, s);
+    return err == hipSuccess ? OSDN_OK : OSDN_ERR_LAUNCH;
+}
+
+osdn_status osdn_step_kda(const void *q, const void *k, const void *v, const float *beta,
+                          const void *d, const float *alpha_ch, float *S, void *o, int64_t B,
+                          int64_t H, int32_t dk, int32_t dv, osdn_dtype qkv,
+                          osdn_dtype d_dtype, void *stream) {
+    if (B < 0 || H < 0) return OSDN_ERR_SHAPE;
+    if (!dtype_ok(qkv) || !dtype_ok(d_dtype)) return OSDN_ERR_UNSUPPORTED;
+    if (!head_dim_ok(dk) || !head_dim_ok(dv)) return OSDN_ERR_UNSUPPORTED;
+    int64_t BH = 1;
+    if (!mul_ok(BH, B, kMaxElems) || !mul_ok(BH, H, kMaxElems)) return OSDN_ERR_SHAPE;
+    int64_t st = BH;
+    if (!mul_ok(st, int64_t(dk) * dv, kMaxElems)) return OSDN_ERR_SHAPE;
+    if (BH > int64_t(0x7fffffff)) return OSDN_ERR_SHAPE;
+    if (BH == 0) return OSDN_OK;
+    if (!q || !k || !v || !beta || !d || !alpha_ch || !S || !o) return OSDN_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(d, 16) ||
+        !aligned(o, 16) || !aligned(S, 16) || !aligned(beta, 4) || !aligned(alpha_ch, 4))
+        return OSDN_ERR_ALIGN;
+
+    const int64_t eq = elem_size(qkv), ed = elem_size(d_dtype);
+    const Range rq = range_of(q, BH * dk * eq), rk = range_of(k, BH * dk * eq);
+    const Range rv = range_of(v, BH * dv * eq), rd = range_of(d, BH * dk * ed);
+    const Range rb = range_of(beta, BH * 4), ra = range_of(alpha_ch, BH * dk * 4);
+    const Range rS = range_of(S, st * 4), ro = range_of(o, BH * dv * eq);
+    for (const Range *in : {&rq, &rk, &rv, &rd, &rb, &ra, &rS})
+        if (overlap(ro, *in)) return OSDN_ERR_ALIAS;
+    for (const Range *in : {&rq, &rk, &rv, &rd, &rb, &ra})
+        if (overlap(rS, *in)) return OSDN_ERR_ALIAS;
+
+    osdn::StepArgs a{q, k, v, d, beta, alpha_ch, S, o, BH, dk, dv, qkv, d_dtype};
+    const hipError_t err = osdn::launch_step_kda(a, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? OSDN_OK : OSDN_ERR_LAUNCH;
+}
+
 }  // extern "C"

@@ -15,6 +15,8 @@
 //   a6  O = diag(e^g) Q M + P U;  M <- e^{g_C} M + (diag(e^{g_C - g}) K~)^T U
 //
 // Rows past the end of the sequence are zero (beta = 0, alpha = 1), so they add nothing.
+// With the channel-wise gate the caller passes pre-scaled q, k, d and per-chunk factors G_C,
+// and the state's rows are multiplied by G_C after each carry.
 #include "osdn_internal.h"
 
 namespace osdn {
@@ -27,7 +29,8 @@ __global__ void __launch_bounds__(kThreads)
 chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
                      const TQ *__restrict__ v, const TD *__restrict__ d,
                      const float *__restrict__ beta, const float *__restrict__ alpha,
-                     const float *S0, TQ *__restrict__ o, float *S_T, int64_t T, int dv) {
+                     const float *S0, TQ *__restrict__ o, float *S_T, int64_t T, int dv,
+                     const float *__restrict__ gcs) {
     constexpr int PX = DK + 1;  // padded row pitches (bank-conflict relief)
     constexpr int PC = CH + 1;
     constexpr int PV = BV + 1;
@@ -180,7 +183,9 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
             float acc = 0.f;
             for (int s = 0; s < CH; ++s)
                 acc += sdec[s] * sKt[s * PX + i] * sU[s * PV + j];
-            sM[i * PV + j] = gam_last * sM[i * PV + j] + acc;
+            const float mv = gam_last * sM[i * PV + j] + acc;
+            // channel-wise gate: the state's rows times the chunk's G_C
+            sM[i * PV + j] = gcs ? gcs[(bh * ((T + CH - 1) / CH) + c0 / CH) * DK + i] * mv : mv;
         }
     }
     __syncthreads();
@@ -200,7 +205,7 @@ hipError_t launch_typed(const ChunkArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL((chunk_f32math_kernel<DK, BV, CH, TQ, TD>), grid, dim3(kThreads), 0,
                        stream, static_cast<const TQ *>(a.q), static_cast<const TQ *>(a.k),
                        static_cast<const TQ *>(a.v), static_cast<const TD *>(a.d), a.beta,
-                       a.alpha, a.S0, static_cast<TQ *>(a.o), a.S_T, a.T, a.dv);
+                       a.alpha, a.S0, static_cast<TQ *>(a.o), a.S_T, a.T, a.dv, a.gcs);
     return hipGetLastError();
 }
 

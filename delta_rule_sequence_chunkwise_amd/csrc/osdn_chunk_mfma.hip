@@ -32,6 +32,9 @@
 // * Stager waves (4, 5) bring the k rows of chunk c+2 into LDS (two row blocks each) and write
 //   k~ = d (.) k of those rows; d reaches their registers one step ahead.
 // * The loader wave (6) brings q and v of chunk c+2 into LDS and runs its decay scan.
+// With the channel-wise gate (the caller passes pre-scaled q, k, d and per-chunk factors G_C)
+// the state waves also multiply the state's rows by G_C after each carry; the loader brings
+// G_C into LDS with the other loads of its chunk.
 // Loads stall the issuing wave while HBM drains them, and too many in flight at once thrash
 // the CU's load queues; so they are issued in groups of at most 16 by waves whose other work
 // is light, and each state wave shares its SIMD with a stager.
@@ -93,6 +96,7 @@ struct alignas(16) Lds {
     // cik = e^{g_{16i} - g_{16k+15}}, eb[s] = e^{g_{16k+15} - g_s}
     alignas(16) float ea[3][CH];
     alignas(16) float eb[3][CH];
+    alignas(16) float gc[3][DK];                    // channel-wise gate: G_C of the chunk
     alignas(16) float cik[3][8];
     alignas(16) uint16_t ntile[NBLK][16 * 16];  // N of diagonal block kb, rows by blk (prep)
 };
@@ -257,7 +261,7 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                   const uint16_t *__restrict__ v, const TD *__restrict__ d,
                   const float *__restrict__ beta, const float *__restrict__ alpha,
                   const float *S0, uint16_t *__restrict__ o, float *S_T, int64_t BH,
-                  int64_t T, int dv) {
+                  int64_t T, int dv, const float *__restrict__ gcs) {
     using L = Lds<DK>;
     constexpr int NS = DK / 32;   // 32-wide k-steps over the key features
     constexpr int NFT = DK / 16;  // 16-row feature tiles of the state
@@ -413,6 +417,10 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                 const v8s uwb1 = c_to_frag(w4[2] * U[2], w4[3] * U[3]);
 #pragma unroll
                 for (int ft = 0; ft < NFT; ++ft) M[ft] = mfma32(kt_frag(ft, 1), uwb1, acc[ft]);
+                if (gcs) {  // channel-wise gate: the state's rows times the chunk's G_C
+#pragma unroll
+                    for (int ft = 0; ft < NFT; ++ft) M[ft] *= ld4(&sm.gc[sl][16 * ft + 4 * lq]);
+                }
                 // read-out O^T = (M^T Q^T) diag(gam) + U^T P^T: lane holds O[16rt+lr][4 columns];
                 // rows past the chunk's last valid row fall outside the buffer range and are
                 // dropped by the store
@@ -464,6 +472,10 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
         if (nchunks > 0) load_ba(0);
         auto load_step = [&](auto par_c, int64_t cc, int slot) __attribute__((always_inline)) {
             constexpr int PAR = decltype(par_c)::value;  // cc mod 2
+            // channel-wise gate: the chunk's G_C, through registers into LDS
+            const bool has_gc = gcs != nullptr && cc >= 0 && cc < nchunks && lane < DK / 4;
+            float4 gcv = make_float4(1.f, 1.f, 1.f, 1.f);
+            if (has_gc) gcv = *reinterpret_cast<const float4 *>(gcs + (bh * nchunks + cc) * DK + 4 * lane);
             if (cc >= 0 && cc < nchunks) {
                 const int64_t r0 = seq0 + cc * CH;
                 const int n = rows_of(cc);
@@ -473,6 +485,7 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                 load_ba(cc + 1);
             }
             wait_global();
+            if (has_gc) *reinterpret_cast<float4 *>(&sm.gc[slot][4 * lane]) = gcv;
             block_sync();
         };
         int sl2 = 0;  // (c+2) mod 3
@@ -676,7 +689,7 @@ hipError_t launch_typed(const ChunkArgs &a, hipStream_t stream) {
                        static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
                        static_cast<const uint16_t *>(a.v), static_cast<const TD *>(a.d),
                        a.beta, a.alpha, a.S0, static_cast<uint16_t *>(a.o), a.S_T, a.BH, a.T,
-                       a.dv);
+                       a.dv, a.gcs);
     return hipGetLastError();
 }
 

@@ -40,6 +40,18 @@ struct ChunkArgs {
     int64_t BH, T;
     int32_t dk, dv, chunk;
     osdn_dtype qkv, d_dtype;
+    const float *gcs = nullptr;  // [BH, nchunks, dk]: per-feature factor applied to the
+                                 // state's rows after each chunk's carry (channel-wise gate)
+};
+
+struct KdaPrepArgs {
+    const void *q, *k, *d;
+    const float *alpha_ch;
+    void *qp, *kp, *dp;  // workspace: q', k' (qkv dtype), d' (bf16 for OSDN_BF16, else fp32)
+    float *gcs;          // workspace: [BH, nchunks, dk]
+    int64_t BH, T, nchunks;
+    int32_t dk, chunk;
+    osdn_dtype qkv, d_dtype;
 };
 
 struct StepArgs {
@@ -69,5 +81,7 @@ hipError_t launch_chunk_fwd_f32math(const ChunkArgs &a, hipStream_t stream);
 hipError_t launch_chunk_fwd_mfma(const ChunkArgs &a, hipStream_t stream);
 hipError_t launch_step(const StepArgs &a, hipStream_t stream);
 hipError_t launch_precond(const PrecondArgs &a, hipStream_t stream);
+hipError_t launch_kda_prep(const KdaPrepArgs &a, hipStream_t stream);
+hipError_t launch_step_kda(const StepArgs &a, hipStream_t stream);  // alpha: [BH, dk]
 
 }  // namespace osdn

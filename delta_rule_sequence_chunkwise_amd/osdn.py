@@ -21,6 +21,7 @@ ABI_VERSION = 1
 STATUS = {0: "OSDN_OK", -1: "OSDN_ERR_NULL", -2: "OSDN_ERR_SHAPE", -3: "OSDN_ERR_UNSUPPORTED",
           -4: "OSDN_ERR_ALIGN", -5: "OSDN_ERR_ALIAS", -6: "OSDN_ERR_LAUNCH"}
 EXPORTS = ("osdn_chunk_fwd", "osdn_step", "osdn_precond_scan", "osdn_precond_step",
+           "osdn_chunk_fwd_kda", "osdn_chunk_fwd_kda_workspace", "osdn_step_kda",
            "osdn_status_string", "osdn_abi_version")
 
 
@@ -54,6 +55,13 @@ def lib() -> ctypes.CDLL:
     L.osdn_precond_step.restype = ctypes.c_int
     L.osdn_precond_step.argtypes = [vp] * 5 + [ctypes.c_float, i64, i64, i32, ctypes.c_int,
                                                ctypes.c_int, vp]
+    L.osdn_chunk_fwd_kda_workspace.restype = i64
+    L.osdn_chunk_fwd_kda_workspace.argtypes = [i64, i64, i64, i32, i32, ctypes.c_int]
+    L.osdn_chunk_fwd_kda.restype = ctypes.c_int
+    L.osdn_chunk_fwd_kda.argtypes = [vp] * 10 + [i64, i64, i64, i64, i32, i32, i32, ctypes.c_int,
+                                                 ctypes.c_int, vp]
+    L.osdn_step_kda.restype = ctypes.c_int
+    L.osdn_step_kda.argtypes = [vp] * 8 + [i64, i64, i32, i32, ctypes.c_int, ctypes.c_int, vp]
     L.osdn_status_string.restype = ctypes.c_char_p
     L.osdn_status_string.argtypes = [ctypes.c_int]
     L.osdn_abi_version.restype = ctypes.c_int32
@@ -205,3 +213,70 @@ def osdn_precond_step(k, beta, r, dstate, *, eta: float, d_out=None, d_dtype=Non
     if st != 0:
         raise OSDNError(st, "osdn_precond_step")
     return d_out
+
+
+def kda_workspace_bytes(B: int, H: int, T: int, dk: int, chunk: int, dtype_code: int) -> int:
+    n = lib().osdn_chunk_fwd_kda_workspace(B, H, T, dk, chunk, dtype_code)
+    if n < 0:
+        raise ValueError("invalid shape for the channel-wise gate's workspace")
+    return n
+
+
+def osdn_chunk_fwd_kda(q, k, v, beta, d, alpha_ch, S0=None, *, chunk: int = 64, o=None,
+                       S_T=None, want_state: bool = True, workspace=None, stream=None):
+    """Chunkwise forward with the channel-wise gate alpha_ch [B,H,T,dk] fp32 (no scalar alpha).
+    Other arguments as osdn_chunk_fwd.  ``workspace`` (a uint8 device tensor of at least
+    kda_workspace_bytes(...) bytes) is allocated with torch when not given."""
+    torch = _torch()
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    if S_T is None and want_state:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    for name, t, shape in (("k", k, (B, H, T, dk)), ("v", v, (B, H, T, dv)),
+                           ("beta", beta, (B, H, T)), ("d", d, (B, H, T, dk)),
+                           ("alpha_ch", alpha_ch, (B, H, T, dk)), ("o", o, (B, H, T, dv))):
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+    for name, t in (("S0", S0), ("S_T", S_T)):
+        if t is not None and (tuple(t.shape) != (B, H, dk, dv) or t.dtype != torch.float32):
+            raise ValueError(f"{name} must be float32 [B,H,dk,dv]")
+    for name, t in (("beta", beta), ("alpha_ch", alpha_ch)):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    if k.dtype != q.dtype or v.dtype != q.dtype or o.dtype != q.dtype:
+        raise TypeError("q, k, v and o must share one dtype")
+    need = kda_workspace_bytes(B, H, T, dk, chunk, _dtype_code(q))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib().osdn_chunk_fwd_kda(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(d),
+                                  _ptr(alpha_ch), _ptr(S0), _ptr(o), _ptr(S_T),
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  B, H, T, dk, dv, chunk, _dtype_code(q), _dtype_code(d),
+                                  _stream(stream, q.device))
+    if st != 0:
+        raise OSDNError(st, "osdn_chunk_fwd_kda")
+    return o, S_T
+
+
+def osdn_step_kda(q, k, v, beta, d, alpha_ch, S, *, o=None, stream=None):
+    """One decode step with the channel-wise gate alpha_ch [B,H,dk] fp32; S [B,H,dk,dv] fp32
+    updated in place.  Returns o [B,H,dv]."""
+    torch = _torch()
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
+    if tuple(S.shape) != (B, H, dk, dv) or S.dtype != torch.float32:
+        raise ValueError("S must be float32 [B,H,dk,dv]")
+    if tuple(alpha_ch.shape) != (B, H, dk) or alpha_ch.dtype != torch.float32:
+        raise ValueError("alpha_ch must be float32 [B,H,dk]")
+    if k.dtype != q.dtype or v.dtype != q.dtype or o.dtype != q.dtype:
+        raise TypeError("q, k, v and o must share one dtype")
+    st = lib().osdn_step_kda(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(d), _ptr(alpha_ch),
+                             _ptr(S), _ptr(o), B, H, dk, dv, _dtype_code(q), _dtype_code(d),
+                             _stream(stream, q.device))
+    if st != 0:
+        raise OSDNError(st, "osdn_step_kda")
+    return o

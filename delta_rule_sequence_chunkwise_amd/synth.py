@@ -22,6 +22,10 @@ own (seed + 7919, so the draws above are unchanged), its retention gate and star
 r = exp(-0.01 * softplus(N(0, 1))) per token and head (in (0.97, 1)), d_1 = exp(0.25 N(0, 1))
 per head and feature, both rounded to float32.  The meta step eta = 2 is a workload constant.
 
+The channel-wise (KDA) gate a_t [B,H,T,dk] of the KDA variant comes from a stream of its own
+(seed + 104729): a = exp(-0.05 * softplus(N(0, 1))) per token, head and key feature, i.e. the
+scalar gate's recipe drawn per feature, rounded to float32.
+
 The decode workload draws its initial state first (S0 ~ N(0, 0.02^2), float32, stored as
 M = S^T, i.e. ``[B, H, dk, dv]``), then the per-step tuples in the order above.
 """
@@ -183,3 +187,9 @@ def make_precond_gates(B: int, H: int, T: int, dk: int, seed: int) -> Dict[str, 
     r = np.exp(-0.01 * np.logaddexp(0.0, rng.standard_normal((B, H, T))))
     d1 = np.exp(0.25 * rng.standard_normal((B, H, dk)))
     return {"r": round_f32(r), "d1": round_f32(d1)}
+
+
+def make_channel_gate(B: int, H: int, T: int, dk: int, seed: int) -> np.ndarray:
+    """Channel-wise gate a [B,H,T,dk] (the scalar gate's recipe, one draw per key feature)."""
+    rng = np.random.Generator(np.random.PCG64(seed + 104729))
+    return round_f32(np.exp(-0.05 * np.logaddexp(0.0, rng.standard_normal((B, H, T, dk)))))

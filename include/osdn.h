@@ -144,6 +144,48 @@ osdn_status osdn_precond_step(const void *k, const float *beta, const float *r, 
                               void *d_out, float eta, int64_t B, int64_t H, int32_t dk,
                               osdn_dtype k_dtype, osdn_dtype d_dtype, void *stream);
 
+/*
+ * Chunkwise forward with the channel-wise (Kimi Delta Attention) gate in place of the scalar
+ * one (Erase-then-Delta Attention, section 2.2, eq. 5, and section 3.2, eq. 7, with the OSDN
+ * write key of section 2.1 of the OSDN technical summary).  For every (b,h), token by token,
+ * in the storage convention M = S^T:
+ *
+ *     M_t = Diag(a_t) M_{t-1} + beta_t k~_t (v_t - (Diag(a_t) M_{t-1})^T k_t)^T ,
+ *     o_t = M_t^T q_t ,      k~_t = d_t (.) k_t ,
+ *
+ * i.e. each key feature (row of M) has its own retention factor a_t[i].
+ *
+ *   alpha_ch  [B,H,T,dk] f32   per-token, per-key-feature retention, in (0, 1]; within one
+ *                              chunk the running product of a feature's factors must stay
+ *                              above 2^-60 (below that it is taken as 2^-60)
+ *   workspace                  caller-owned device memory of at least
+ *                              osdn_chunk_fwd_kda_workspace(B, H, T, dk, chunk, qkv) bytes,
+ *                              256-byte aligned; its contents on entry are ignored and on
+ *                              return unspecified; it must not overlap any other argument
+ *   workspace_bytes            its size
+ *   every other argument       as for osdn_chunk_fwd (there is no scalar alpha here)
+ * Two kernels run on `stream`: one writes the gate-scaled q, k, d and the per-chunk decay
+ * into the workspace, the chunkwise forward then reads them.
+ */
+int64_t osdn_chunk_fwd_kda_workspace(int64_t B, int64_t H, int64_t T, int32_t dk,
+                                     int32_t chunk, osdn_dtype qkv); /* -1 if invalid */
+
+osdn_status osdn_chunk_fwd_kda(const void *q, const void *k, const void *v, const float *beta,
+                               const void *d, const float *alpha_ch, const float *S0, void *o,
+                               float *S_T, void *workspace, int64_t workspace_bytes,
+                               int64_t B, int64_t H, int64_t T, int32_t dk, int32_t dv,
+                               int32_t chunk, osdn_dtype qkv, osdn_dtype d_dtype,
+                               void *stream);
+
+/*
+ * One decode step with the channel-wise gate (the token step above, applied once):
+ *   alpha_ch [B,H,dk] f32; every other argument as for osdn_step (no scalar alpha).
+ */
+osdn_status osdn_step_kda(const void *q, const void *k, const void *v, const float *beta,
+                          const void *d, const float *alpha_ch, float *S, void *o, int64_t B,
+                          int64_t H, int32_t dk, int32_t dv, osdn_dtype qkv,
+                          osdn_dtype d_dtype, void *stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char *osdn_status_string(osdn_status s);
 

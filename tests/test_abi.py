@@ -187,3 +187,48 @@ def test_precond_step_rejects(L, over, status):
 
 def test_precond_step_empty_is_ok(L):
     assert call_precond_step(L, H=0, k=None) == 0
+
+
+def call_kda(L, **over):
+    a = dict(q=addr(1), k=addr(2), v=addr(3), beta=addr(4), d=addr(5), alpha_ch=addr(6),
+             S0=addr(7), o=addr(8), S_T=addr(9), ws=addr(10), wsb=1 << 31, B=2, H=3, T=100,
+             dk=128, dv=64, chunk=64, qkv=osdn.OSDN_BF16, d_dtype=osdn.OSDN_F32, stream=None)
+    a.update(over)
+    return L.osdn_chunk_fwd_kda(a["q"], a["k"], a["v"], a["beta"], a["d"], a["alpha_ch"],
+                                a["S0"], a["o"], a["S_T"], a["ws"], a["wsb"], a["B"], a["H"],
+                                a["T"], a["dk"], a["dv"], a["chunk"], a["qkv"], a["d_dtype"],
+                                a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(alpha_ch=None), -1), (dict(ws=None), -1), (dict(q=None), -1),
+    (dict(T=-1), -2), (dict(wsb=1000), -2), (dict(dk=32), -3), (dict(chunk=16), -3),
+    (dict(ws=addr(10) + 128), -4), (dict(alpha_ch=addr(6) + 2), -4),
+    (dict(ws=addr(1)), -5), (dict(o=addr(10)), -5), (dict(S_T=addr(10) + 512), -5),
+])
+def test_chunk_fwd_kda_rejects(L, over, status):
+    assert call_kda(L, **over) == status
+
+
+def test_kda_workspace_size(L):
+    n = L.osdn_chunk_fwd_kda_workspace(2, 3, 100, 128, 64, osdn.OSDN_BF16)
+    # q', k' (bf16), d' (bf16), G_C (fp32, two chunks), each rounded up to 256 bytes
+    assert n == 3 * (2 * 3 * 100 * 128 * 2) + 2 * 3 * 2 * 128 * 4
+    assert L.osdn_chunk_fwd_kda_workspace(2, 3, 100, 96, 64, osdn.OSDN_BF16) == -1
+    assert L.osdn_chunk_fwd_kda_workspace(1, 1, 10, 64, 16, osdn.OSDN_F32) == 3 * 2560 + 256
+    assert call_kda(L, B=0) == 0 and call_kda(L, T=0, q=None, S_T=None, ws=None) == 0
+
+
+def test_step_kda_rejects(L):
+    args = [addr(1), addr(2), addr(3), addr(4), addr(5), addr(6), addr(7), addr(8), 4, 2, 128,
+            128, osdn.OSDN_BF16, osdn.OSDN_F32, None]
+    assert L.osdn_step_kda(*args[:5], None, *args[6:]) == -1
+    bad = list(args)
+    bad[5] = addr(6) + 2
+    assert L.osdn_step_kda(*bad) == -4
+    bad = list(args)
+    bad[7] = addr(6)
+    assert L.osdn_step_kda(*bad) == -5
+    bad = list(args)
+    bad[8] = 0
+    assert L.osdn_step_kda(*bad) == 0
