@@ -287,7 +287,7 @@ osdn_status osdn_chunk_fwd_kda(const void *q, const void *k, const void *v, cons
     if (!mul_ok(st, int64_t(dk) * dv, kMaxElems)) return OSDN_ERR_SHAPE;
     if (BH > int64_t(0x7fffffff) / 4) return OSDN_ERR_SHAPE;
     const int64_t nchunks = (T + chunk - 1) / chunk;
-    if (BH * nchunks > int64_t(0x7fffffff)) return OSDN_ERR_SHAPE;  // prep grid
+    if (BH * nchunks * (dk / 4) > int64_t(0x7fffffff) * 64) return OSDN_ERR_SHAPE;  // prep grid
 
     if (BH == 0) return OSDN_OK;
     if (T > 0 && (!q || !k || !v || !beta || !d || !alpha_ch || !o || !workspace))
@@ -298,7 +298,7 @@ osdn_status osdn_chunk_fwd_kda(const void *q, const void *k, const void *v, cons
     const int64_t eq = elem_size(qkv), ed = elem_size(d_dtype);
     if (T > 0) {
         if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(d, 16) ||
-            !aligned(o, 16) || !aligned(beta, 4) || !aligned(alpha_ch, 4) ||
+            !aligned(o, 16) || !aligned(beta, 4) || !aligned(alpha_ch, 16) ||
             !aligned(workspace, 256))
             return OSDN_ERR_ALIGN;
     }

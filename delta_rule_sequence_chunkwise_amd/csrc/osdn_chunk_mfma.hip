@@ -60,7 +60,7 @@ constexpr int BV = 32;                       // value columns per workgroup
 constexpr int NW = 7;  // waves per workgroup: 2 state, 2 prep, 2 stagers, 1 loader
 constexpr int VW = 16;                       // value columns per state wave
 
-template <int DK>
+template <int DK, bool GATE = false>
 struct alignas(16) Lds {
     static constexpr int KU = DK / 8;   // 16-byte units per q/k/k~ row
     static constexpr int KP = DK;       // row pitch (bf16) of k~
@@ -96,7 +96,7 @@ struct alignas(16) Lds {
     // cik = e^{g_{16i} - g_{16k+15}}, eb[s] = e^{g_{16k+15} - g_s}
     alignas(16) float ea[3][CH];
     alignas(16) float eb[3][CH];
-    alignas(16) float gc[3][DK];                    // channel-wise gate: G_C of the chunk
+    alignas(16) float gc[GATE ? 3 : 1][GATE ? DK : 4];  // channel-wise gate: G_C of the chunk
     alignas(16) float cik[3][8];
     alignas(16) uint16_t ntile[NBLK][16 * 16];  // N of diagonal block kb, rows by blk (prep)
 };
@@ -158,8 +158,8 @@ __device__ __forceinline__ float per_block(float v0, float v1, float v2, float v
 // alpha = 1, so they leave U, M and every kept output unchanged.  The inclusive prefix sum of
 // ln(alpha) runs on DPP: shifts by 1, 2, 4, 8 inside each 16-lane row, then the last lane of
 // rows 0 and 2 into rows 1 and 3, then lane 31 into rows 2 and 3.
-template <int DK>
-__device__ __forceinline__ void scan_chunk(Lds<DK> &sm, int slot, float beta, float alpha, int n,
+template <int DK, bool G>
+__device__ __forceinline__ void scan_chunk(Lds<DK, G> &sm, int slot, float beta, float alpha, int n,
                                            bool has_alpha, int lane) {
     const bool ok = lane < n;
     float x = (ok && has_alpha) ? __logf(alpha) : 0.f;
@@ -192,8 +192,8 @@ __device__ __forceinline__ void scan_chunk(Lds<DK> &sm, int slot, float beta, fl
 // D_kb = (I + N)^{-1} for the two diagonal blocks kb0, kb1 of a prep wave, in lockstep so the
 // two dependent chains overlap.  Input: N in the A layout (lane holds N[lr][4lq+e]); the B
 // layout (lane holds N[4lq+e][lr]) comes back through LDS with a transposing read.
-template <int DK>
-__device__ __forceinline__ void diag_inverse2(Lds<DK> &sm, int b, int kb0, int kb1, int lr,
+template <int DK, bool G>
+__device__ __forceinline__ void diag_inverse2(Lds<DK, G> &sm, int b, int kb0, int kb1, int lr,
                                               int lq, const v4f (&na)[2]) {
     using L = Lds<DK>;
     const int kb[2] = {kb0, kb1};
@@ -255,14 +255,14 @@ __device__ __forceinline__ void diag_inverse2(Lds<DK> &sm, int b, int kb0, int k
             pack4u(Y[j]);
 }
 
-template <int DK, typename TD>
+template <int DK, typename TD, bool GATE>
 __global__ void __launch_bounds__(NW * 64)
 chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                   const uint16_t *__restrict__ v, const TD *__restrict__ d,
                   const float *__restrict__ beta, const float *__restrict__ alpha,
                   const float *S0, uint16_t *__restrict__ o, float *S_T, int64_t BH,
                   int64_t T, int dv, const float *__restrict__ gcs) {
-    using L = Lds<DK>;
+    using L = Lds<DK, GATE>;
     constexpr int NS = DK / 32;   // 32-wide k-steps over the key features
     constexpr int NFT = DK / 16;  // 16-row feature tiles of the state
 
@@ -417,7 +417,7 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                 const v8s uwb1 = c_to_frag(w4[2] * U[2], w4[3] * U[3]);
 #pragma unroll
                 for (int ft = 0; ft < NFT; ++ft) M[ft] = mfma32(kt_frag(ft, 1), uwb1, acc[ft]);
-                if (gcs) {  // channel-wise gate: the state's rows times the chunk's G_C
+                if constexpr (GATE) {  // channel-wise gate: the state's rows times the chunk's G_C
 #pragma unroll
                     for (int ft = 0; ft < NFT; ++ft) M[ft] *= ld4(&sm.gc[sl][16 * ft + 4 * lq]);
                 }
@@ -473,9 +473,11 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
         auto load_step = [&](auto par_c, int64_t cc, int slot) __attribute__((always_inline)) {
             constexpr int PAR = decltype(par_c)::value;  // cc mod 2
             // channel-wise gate: the chunk's G_C, through registers into LDS
-            const bool has_gc = gcs != nullptr && cc >= 0 && cc < nchunks && lane < DK / 4;
+            const bool has_gc = GATE && cc >= 0 && cc < nchunks && lane < DK / 4;
             float4 gcv = make_float4(1.f, 1.f, 1.f, 1.f);
-            if (has_gc) gcv = *reinterpret_cast<const float4 *>(gcs + (bh * nchunks + cc) * DK + 4 * lane);
+            if constexpr (GATE) {
+                if (has_gc) gcv = *reinterpret_cast<const float4 *>(gcs + (bh * nchunks + cc) * DK + 4 * lane);
+            }
             if (cc >= 0 && cc < nchunks) {
                 const int64_t r0 = seq0 + cc * CH;
                 const int n = rows_of(cc);
@@ -485,7 +487,9 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                 load_ba(cc + 1);
             }
             wait_global();
-            if (has_gc) *reinterpret_cast<float4 *>(&sm.gc[slot][4 * lane]) = gcv;
+            if constexpr (GATE) {
+                if (has_gc) *reinterpret_cast<float4 *>(&sm.gc[slot][4 * lane]) = gcv;
+            }
             block_sync();
         };
         int sl2 = 0;  // (c+2) mod 3
@@ -685,11 +689,15 @@ template <int DK, typename TD>
 hipError_t launch_typed(const ChunkArgs &a, hipStream_t stream) {
     const int nvt = a.dv / BV;
     const dim3 grid(static_cast<unsigned>(a.BH * nvt));
-    hipLaunchKernelGGL((chunk_mfma_kernel<DK, TD>), grid, dim3(NW * 64), 0, stream,
-                       static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
-                       static_cast<const uint16_t *>(a.v), static_cast<const TD *>(a.d),
-                       a.beta, a.alpha, a.S0, static_cast<uint16_t *>(a.o), a.S_T, a.BH, a.T,
-                       a.dv, a.gcs);
+#define OSDN_CHUNK_LAUNCH(GATE)                                                               \
+    hipLaunchKernelGGL((chunk_mfma_kernel<DK, TD, GATE>), grid, dim3(NW * 64), 0, stream,     \
+                       static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k), \
+                       static_cast<const uint16_t *>(a.v), static_cast<const TD *>(a.d),       \
+                       a.beta, a.alpha, a.S0, static_cast<uint16_t *>(a.o), a.S_T, a.BH, a.T,  \
+                       a.dv, a.gcs)
+    if (a.gcs) OSDN_CHUNK_LAUNCH(true);
+    else OSDN_CHUNK_LAUNCH(false);
+#undef OSDN_CHUNK_LAUNCH
     return hipGetLastError();
 }
 

@@ -10,7 +10,8 @@
 // k~' = d' k' = k~ / G) the chunk is the undecayed chunk algebra on (q', k', d'), except that
 // the carried state becomes  Diag(G_C) (M0 + K~'^T U)  -- the forward kernels take G_C per
 // chunk and scale the state's rows after each carry.  kda_prep_kernel writes q', k', d' and
-// G_C into a workspace; it is bound by HBM bandwidth.  G is clamped at 2^-60 inside 1/G^2,
+// G_C into a workspace (one thread per four consecutive features of a chunk, 8- and 16-byte
+// accesses); it is bound by HBM bandwidth.  G is clamped at 2^-60 inside 1/G^2,
 // so a chunk whose product of gates on a feature falls below that is computed as if it were
 // 2^-60 there.
 //
@@ -23,29 +24,52 @@ namespace {
 
 constexpr float kMinGate = 0x1p-60f;
 
-// one workgroup per (sequence, chunk); thread f walks the chunk's rows of feature f
+// four consecutive elements as fp32 (16 bytes of fp32, 8 bytes of bf16)
+__device__ __forceinline__ float4 load4f(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+__device__ __forceinline__ float4 load4f(const bf16_t *p) {
+    const uint2 u = *reinterpret_cast<const uint2 *>(p);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+}
+__device__ __forceinline__ void store4f(float *p, float4 x) { *reinterpret_cast<float4 *>(p) = x; }
+__device__ __forceinline__ void store4f(bf16_t *p, float4 x) {
+    *reinterpret_cast<uint2 *>(p) = make_uint2(
+        uint32_t(f32_to_bf16_bits(x.x)) | (uint32_t(f32_to_bf16_bits(x.y)) << 16),
+        uint32_t(f32_to_bf16_bits(x.z)) | (uint32_t(f32_to_bf16_bits(x.w)) << 16));
+}
+
+constexpr int kPrepThreads = 256;
+
+// thread -> (sequence, chunk, four consecutive features); it walks the chunk's rows
 template <int DK, typename TQ, typename TDI, typename TDO>
-__global__ void __launch_bounds__(DK)
+__global__ void __launch_bounds__(kPrepThreads)
 kda_prep_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k, const TDI *__restrict__ d,
                 const float *__restrict__ a, TQ *__restrict__ qp, TQ *__restrict__ kp,
                 TDO *__restrict__ dp, float *__restrict__ gcs, int64_t T, int chunk,
-                int64_t nchunks) {
-    const int64_t bh = blockIdx.x / nchunks, c = blockIdx.x % nchunks;
-    const int f = threadIdx.x;
+                int64_t nchunks, int64_t total) {
+    constexpr int QPR = DK / 4;  // feature quads per row
+    const int64_t g = int64_t(blockIdx.x) * kPrepThreads + threadIdx.x;
+    if (g >= total) return;
+    const int64_t seg = g / QPR;  // (sequence, chunk)
+    const int f = static_cast<int>(g % QPR) * 4;
+    const int64_t bh = seg / nchunks, c = seg % nchunks;
     const int64_t t0 = c * chunk;
     const int n = static_cast<int>(T - t0 < chunk ? T - t0 : chunk);
     const int64_t base = (bh * T + t0) * DK + f;
-    float G = 1.f;
+    float4 G = make_float4(1.f, 1.f, 1.f, 1.f);
 #pragma unroll 4
     for (int r = 0; r < n; ++r) {
         const int64_t i = base + int64_t(r) * DK;
-        G *= a[i];
-        qp[i] = from_f32<TQ>(to_f32(q[i]) * G);
-        kp[i] = from_f32<TQ>(to_f32(k[i]) * G);
-        const float g = fmaxf(G, kMinGate);
-        dp[i] = from_f32<TDO>(to_f32(d[i]) / (g * g));
+        const float4 av = load4f(a + i), qv = load4f(q + i), kv = load4f(k + i), dv = load4f(d + i);
+        G.x *= av.x; G.y *= av.y; G.z *= av.z; G.w *= av.w;
+        store4f(qp + i, make_float4(qv.x * G.x, qv.y * G.y, qv.z * G.z, qv.w * G.w));
+        store4f(kp + i, make_float4(kv.x * G.x, kv.y * G.y, kv.z * G.z, kv.w * G.w));
+        const float gx = fmaxf(G.x, kMinGate), gy = fmaxf(G.y, kMinGate);
+        const float gz = fmaxf(G.z, kMinGate), gw = fmaxf(G.w, kMinGate);
+        store4f(dp + i, make_float4(dv.x / (gx * gx), dv.y / (gy * gy), dv.z / (gz * gz),
+                                    dv.w / (gw * gw)));
     }
-    gcs[(bh * nchunks + c) * DK + f] = G;
+    store4f(gcs + seg * DK + f, G);
 }
 
 // one decode token with the channel-wise gate (same layout as step_kernel)
@@ -138,12 +162,13 @@ step_kda_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k, const TQ *__
 
 template <int DK, typename TQ, typename TDI, typename TDO>
 hipError_t prep_typed(const KdaPrepArgs &a, hipStream_t stream) {
-    const dim3 grid(static_cast<unsigned>(a.BH * a.nchunks));
-    hipLaunchKernelGGL((kda_prep_kernel<DK, TQ, TDI, TDO>), grid, dim3(DK), 0, stream,
+    const int64_t total = a.BH * a.nchunks * (DK / 4);
+    const dim3 grid(static_cast<unsigned>((total + kPrepThreads - 1) / kPrepThreads));
+    hipLaunchKernelGGL((kda_prep_kernel<DK, TQ, TDI, TDO>), grid, dim3(kPrepThreads), 0, stream,
                        static_cast<const TQ *>(a.q), static_cast<const TQ *>(a.k),
                        static_cast<const TDI *>(a.d), a.alpha_ch, static_cast<TQ *>(a.qp),
                        static_cast<TQ *>(a.kp), static_cast<TDO *>(a.dp), a.gcs, a.T, a.chunk,
-                       a.nchunks);
+                       a.nchunks, total);
     return hipGetLastError();
 }
 

@@ -157,7 +157,8 @@ osdn_status osdn_precond_step(const void *k, const float *beta, const float *r, 
  *
  *   alpha_ch  [B,H,T,dk] f32   per-token, per-key-feature retention, in (0, 1]; within one
  *                              chunk the running product of a feature's factors must stay
- *                              above 2^-60 (below that it is taken as 2^-60)
+ *                              above 2^-60 (below that it is taken as 2^-60); 16-byte
+ *                              aligned (OSDN_ERR_ALIGN otherwise)
  *   workspace                  caller-owned device memory of at least
  *                              osdn_chunk_fwd_kda_workspace(B, H, T, dk, chunk, qkv) bytes,
  *                              256-byte aligned; its contents on entry are ignored and on

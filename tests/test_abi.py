@@ -204,6 +204,7 @@ def call_kda(L, **over):
     (dict(alpha_ch=None), -1), (dict(ws=None), -1), (dict(q=None), -1),
     (dict(T=-1), -2), (dict(wsb=1000), -2), (dict(dk=32), -3), (dict(chunk=16), -3),
     (dict(ws=addr(10) + 128), -4), (dict(alpha_ch=addr(6) + 2), -4),
+    (dict(alpha_ch=addr(6) + 4), -4),
     (dict(ws=addr(1)), -5), (dict(o=addr(10)), -5), (dict(S_T=addr(10) + 512), -5),
 ])
 def test_chunk_fwd_kda_rejects(L, over, status):
