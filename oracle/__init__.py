@@ -12,7 +12,8 @@ M = S^T, [B, H, dk, dv].
 
 ``precond`` (numpy, float64) is the Phase-1 preconditioner scan that produces the d_t sequence
 (same summary, sections 2.2 and 2.3); ``chunkwise`` holds float64 models of the chunk forms
-of both recurrences, checked against the token loops.
+of both recurrences, checked against the token loops; ``backward`` (numpy, float64) is
+reverse-mode differentiation of the token recurrence (the gradients of every input).
 """
 from __future__ import annotations
 

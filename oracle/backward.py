@@ -1,0 +1,128 @@
+"""Float64 CPU oracle for the gradients of the OSDN forward (reverse mode through the token
+recurrence).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU-baseline leg may
+import this module; the product path (the HIP library and its Python binding) never does.
+
+The forward is the token step of the OSDN technical summary, section 2.1 (the delta write with
+the write-side key scaled, k~_t = d_t (.) k_t), with the gated-delta decay of Erase-then-Delta
+Attention, section 2.2, eq. 4, in the storage convention M = S^T (dk x dv):
+
+    Mh_t = alpha_t M_{t-1}                   decayed old state
+    y_t  = Mh_t^T k_t                        what the old state recalls for k_t
+    u_t  = beta_t (v_t - y_t)                the write's residual
+    M_t  = Mh_t + k~_t u_t^T                 the write
+    o_t  = M_t^T q_t                         read-out after the write
+
+The pages give no backward pass; this module is reverse-mode differentiation of those five
+lines, taken in reverse order for t = T..1, for a scalar loss L whose gradients with respect to
+the outputs are given: do_t = dL/do_t and dS_T = dL/dM_T (zero when absent).  Every line below
+is the chain rule applied to one of the lines above:
+
+    dM_t  += q_t do_t^T ;           dq_t  = M_t do_t                       (read-out)
+    dk~_t  = dM_t u_t ;             du_t  = dM_t^T k~_t ;  dMh = dM_t      (write)
+    dbeta_t = <du_t, v_t - y_t> ;   dv_t  = beta_t du_t ;  dy = -beta_t du_t   (residual)
+    dMh   += k_t dy^T ;             dk_t  = Mh_t dy                        (recall)
+    dd_t   = dk~_t (.) k_t ;        dk_t += dk~_t (.) d_t                  (write key)
+    dalpha_t = <dMh, M_{t-1}>_F ;   dM_{t-1} = alpha_t dMh                 (decay)
+
+and dS0 = dM_0.  Everything is float64 and vectorised over (batch, head) only.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional
+
+import numpy as np
+
+
+def _f64(x):
+    return None if x is None else np.asarray(x, dtype=np.float64)
+
+
+def forward_states(q, k, v, beta, d, alpha=None, S0=None):
+    """The token recurrence above, keeping what the reverse pass needs.
+
+    Returns dict with o [B,H,T,dv], S_T [B,H,dk,dv], and per token the state before the step
+    (Mprev [B,H,T,dk,dv]), the decayed state (Mh), y and u [B,H,T,dv]."""
+    q, k, v, beta, d, alpha, S0 = map(_f64, (q, k, v, beta, d, alpha, S0))
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    M = np.zeros((B, H, dk, dv)) if S0 is None else S0.copy()
+    o = np.empty((B, H, T, dv))
+    Mprev = np.empty((B, H, T, dk, dv))
+    Mh_all = np.empty((B, H, T, dk, dv))
+    ys = np.empty((B, H, T, dv))
+    us = np.empty((B, H, T, dv))
+    for t in range(T):
+        Mprev[:, :, t] = M
+        a = 1.0 if alpha is None else alpha[:, :, t, None, None]
+        Mh = a * M
+        kt = k[:, :, t]
+        y = np.einsum("bhkv,bhk->bhv", Mh, kt)
+        u = beta[:, :, t, None] * (v[:, :, t] - y)
+        kw = d[:, :, t] * kt
+        M = Mh + kw[..., :, None] * u[..., None, :]
+        o[:, :, t] = np.einsum("bhkv,bhk->bhv", M, q[:, :, t])
+        Mh_all[:, :, t] = Mh
+        ys[:, :, t] = y
+        us[:, :, t] = u
+    return dict(o=o, S_T=M, Mprev=Mprev, Mh=Mh_all, y=ys, u=us)
+
+
+def chunk_bwd(q, k, v, beta, d, alpha=None, S0=None, do=None, dS_T=None) -> Dict[str, np.ndarray]:
+    """Gradients of L with respect to every input of the forward.
+
+    q, k, d [B,H,T,dk]; v [B,H,T,dv]; beta [B,H,T]; alpha [B,H,T] or None (no decay); S0
+    [B,H,dk,dv] or None (zero state); do [B,H,T,dv] (dL/do; zero if None); dS_T [B,H,dk,dv]
+    (dL/dS_T; zero if None).  Returns dq, dk, dv, dbeta, dd, dalpha (None without decay) and
+    dS0 (the gradient with respect to the initial state, whether or not S0 was given)."""
+    q, k, v, beta, d, alpha, S0, do, dS_T = map(_f64, (q, k, v, beta, d, alpha, S0, do, dS_T))
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    f = forward_states(q, k, v, beta, d, alpha, S0)
+    if do is None:
+        do = np.zeros((B, H, T, dv))
+    dM = np.zeros((B, H, dk, dv)) if dS_T is None else dS_T.copy()
+    g = {name: np.zeros_like(x) for name, x in (("dq", q), ("dk", k), ("dv", v),
+                                                 ("dbeta", beta), ("dd", d))}
+    g["dalpha"] = None if alpha is None else np.zeros_like(alpha)
+    for t in range(T - 1, -1, -1):
+        kt, qt, dot = k[:, :, t], q[:, :, t], do[:, :, t]
+        kw = d[:, :, t] * kt
+        u, y, Mh = f["u"][:, :, t], f["y"][:, :, t], f["Mh"][:, :, t]
+        Mt = Mh + kw[..., :, None] * u[..., None, :]
+        # read-out o_t = M_t^T q_t
+        dM = dM + qt[..., :, None] * dot[..., None, :]
+        g["dq"][:, :, t] = np.einsum("bhkv,bhv->bhk", Mt, dot)
+        # write M_t = Mh_t + k~_t u_t^T
+        dkw = np.einsum("bhkv,bhv->bhk", dM, u)
+        du = np.einsum("bhkv,bhk->bhv", dM, kw)
+        dMh = dM
+        # residual u_t = beta_t (v_t - y_t)
+        g["dbeta"][:, :, t] = np.sum(du * (v[:, :, t] - y), axis=-1)
+        g["dv"][:, :, t] = beta[:, :, t, None] * du
+        dy = -beta[:, :, t, None] * du
+        # recall y_t = Mh_t^T k_t
+        dMh = dMh + kt[..., :, None] * dy[..., None, :]
+        dkt = np.einsum("bhkv,bhv->bhk", Mh, dy)
+        # write key k~_t = d_t (.) k_t
+        g["dd"][:, :, t] = dkw * kt
+        g["dk"][:, :, t] = dkt + dkw * d[:, :, t]
+        # decay Mh_t = alpha_t M_{t-1}
+        if alpha is None:
+            dM = dMh
+        else:
+            g["dalpha"][:, :, t] = np.einsum("bhkv,bhkv->bh", dMh, f["Mprev"][:, :, t])
+            dM = alpha[:, :, t, None, None] * dMh
+    g["dS0"] = dM
+    g["o"] = f["o"]
+    g["S_T"] = f["S_T"]
+    return g
+
+
+def loss(o, S_T, do, dS_T) -> float:
+    """The linear loss whose output gradients are (do, dS_T): sum(o * do) + sum(S_T * dS_T)."""
+    val = float(np.sum(np.asarray(o, np.float64) * np.asarray(do, np.float64)))
+    if dS_T is not None:
+        val += float(np.sum(np.asarray(S_T, np.float64) * np.asarray(dS_T, np.float64)))
+    return val

@@ -1,0 +1,131 @@
+"""Pins for a CPU implementation of the gradients of the OSDN forward.
+
+Each pin takes ``impl(q, k, v, beta, d, alpha, S0, do, dS_T) -> dict`` returning float64 arrays
+dq, dk, dv, dbeta, dd, dalpha (None without decay), dS0 and the forward's o, S_T, and returns the
+worst relative error it sees.  None of them restates the reverse pass:
+
+* finite_diff   -- central differences of the loss L = <o, do> + <S_T, dS_T>, with the forward
+                   evaluated by the C oracle (a separate implementation of the token step), for
+                   every element of every input on a tiny problem;
+* autograd      -- torch float64 autograd through an independent forward written as dense
+                   matrices, S_t = alpha_t (I - b_t k~_t k_t^T) S_{t-1} + b_t k~_t v_t^T in the
+                   dk x dv convention of Erase-then-Delta Attention, section 2.2, eq. 4, with the
+                   write key scaled as in the OSDN summary, section 2.1;
+* homog_q       -- o is linear in q, so sum <dq, q> = <do, o>;
+* homog_vs      -- o and S_T are linear in (V, S0) jointly, so sum <dv, v> + <dS0, S0> = L;
+* scale_inv     -- the forward depends on beta_t and d_t only through beta_t d_t (OSDN summary,
+                   section 2.1), so for every token beta_t dbeta_t = <d_t, dd_t>.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from oracle import backward
+from tests.pins import _rand_inputs
+
+
+def rand_bwd(rng, B, H, T, dk, dv, alpha=True, s0=True):
+    q, k, v, beta, d, a, S0 = _rand_inputs(rng, B, H, T, dk, dv, alpha=alpha, s0=s0)
+    do = rng.standard_normal((B, H, T, dv))
+    dS_T = rng.standard_normal((B, H, dk, dv))
+    return q, k, v, beta, d, a, S0, do, dS_T
+
+
+def _rel(x, ref):
+    x, ref = np.asarray(x, np.float64), np.asarray(ref, np.float64)
+    return float(np.max(np.abs(x - ref)) / max(float(np.max(np.abs(ref))), 1e-300))
+
+
+def _c_loss(q, k, v, beta, d, a, S0, do, dS_T):
+    o, S_T = oracle.chunk_fwd(q, k, v, beta, d, a, S0, nthreads=1)
+    return backward.loss(o, S_T, do, dS_T)
+
+
+def finite_diff(impl, seed=51, h=1e-6) -> float:
+    rng = np.random.default_rng(seed)
+    q, k, v, beta, d, a, S0, do, dS_T = rand_bwd(rng, 1, 2, 6, 3, 2)
+    g = impl(q, k, v, beta, d, a, S0, do, dS_T)
+    args = dict(q=q, k=k, v=v, beta=beta, d=d, a=a, S0=S0)
+    names = dict(q="dq", k="dk", v="dv", beta="dbeta", d="dd", a="dalpha", S0="dS0")
+    worst = 0.0
+    for name, x in args.items():
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            old = x[idx]
+            x[idx] = old + h
+            lp = _c_loss(**args, do=do, dS_T=dS_T)
+            x[idx] = old - h
+            lm = _c_loss(**args, do=do, dS_T=dS_T)
+            x[idx] = old
+            fd[idx] = (lp - lm) / (2 * h)
+        worst = max(worst, _rel(g[names[name]], fd))
+    return worst
+
+
+def _torch_forward(torch, q, k, v, beta, d, a, S0):
+    """Dense-matrix forward in the dk x dv convention: S <- a (I - b k~ k^T) S + b k~ v^T."""
+    B, H, T, dk = k.shape
+    outs = []
+    S = S0
+    eye = torch.eye(dk, dtype=torch.float64)
+    for t in range(T):
+        kt, kw = k[:, :, t], d[:, :, t] * k[:, :, t]
+        bt = beta[:, :, t, None, None]
+        trans = eye - bt * kw[..., :, None] * kt[..., None, :]
+        S = a[:, :, t, None, None] * (trans @ S) + bt * kw[..., :, None] * v[:, :, t, None, :]
+        outs.append((S.transpose(-1, -2) @ q[:, :, t, :, None])[..., 0])
+    return torch.stack(outs, dim=2), S
+
+
+def autograd(impl, seed=52) -> float:
+    import torch
+    rng = np.random.default_rng(seed)
+    q, k, v, beta, d, a, S0, do, dS_T = rand_bwd(rng, 2, 2, 30, 8, 5)
+    g = impl(q, k, v, beta, d, a, S0, do, dS_T)
+    ts = [torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v, beta, d, a, S0)]
+    o, S_T = _torch_forward(torch, *ts)
+    L = (o * torch.tensor(do)).sum() + (S_T * torch.tensor(dS_T)).sum()
+    grads = torch.autograd.grad(L, ts)
+    worst = 0.0
+    for name, tg in zip(("dq", "dk", "dv", "dbeta", "dd", "dalpha", "dS0"), grads):
+        worst = max(worst, _rel(g[name], tg.numpy()))
+    return worst
+
+
+def homog_q(impl, seed=53) -> float:
+    rng = np.random.default_rng(seed)
+    q, k, v, beta, d, a, S0, do, dS_T = rand_bwd(rng, 2, 3, 40, 6, 4)
+    g = impl(q, k, v, beta, d, a, S0, do, dS_T)
+    lhs = np.sum(g["dq"] * q)
+    rhs = np.sum(g["o"] * do)
+    return abs(lhs - rhs) / max(abs(rhs), 1e-300)
+
+
+def homog_vs(impl, seed=54) -> float:
+    rng = np.random.default_rng(seed)
+    q, k, v, beta, d, a, S0, do, dS_T = rand_bwd(rng, 2, 3, 40, 6, 4)
+    g = impl(q, k, v, beta, d, a, S0, do, dS_T)
+    lhs = np.sum(g["dv"] * v) + np.sum(g["dS0"] * S0)
+    rhs = backward.loss(g["o"], g["S_T"], do, dS_T)
+    return abs(lhs - rhs) / max(abs(rhs), 1e-300)
+
+
+def scale_inv(impl, seed=55) -> float:
+    rng = np.random.default_rng(seed)
+    q, k, v, beta, d, a, S0, do, dS_T = rand_bwd(rng, 2, 2, 40, 6, 4)
+    g = impl(q, k, v, beta, d, a, S0, do, dS_T)
+    lhs = beta * g["dbeta"]
+    rhs = np.sum(d * g["dd"], axis=-1)
+    return float(np.max(np.abs(lhs - rhs)) / max(float(np.max(np.abs(rhs))), 1e-300))
+
+
+# name -> (pin, tolerance); the tolerances sit far above float64 rounding and far below what
+# a wrong term gives
+BWD_PINS = {
+    "finite_diff": (finite_diff, 1e-6),
+    "autograd": (autograd, 1e-10),
+    "homog_q": (homog_q, 1e-10),
+    "homog_vs": (homog_vs, 1e-10),
+    "scale_inv": (scale_inv, 1e-10),
+}

@@ -1,0 +1,88 @@
+"""The backward oracle against what the mathematics fixes (CPU): finite differences of the C
+oracle's forward, torch autograd through an independent dense forward, and exact identities."""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import backward
+from tests import bwd_pins as pins
+
+
+def oracle_impl(q, k, v, beta, d, a, S0, do, dS_T):
+    return backward.chunk_bwd(q, k, v, beta, d, a, S0, do, dS_T)
+
+
+@pytest.mark.parametrize("name", sorted(pins.BWD_PINS))
+def test_oracle_meets_pin(name):
+    fn, tol = pins.BWD_PINS[name]
+    err = fn(oracle_impl)
+    assert err <= tol, f"{name}: {err:.3e} > {tol:.1e}"
+
+
+def test_forward_states_match_c_oracle():
+    rng = np.random.default_rng(56)
+    q, k, v, beta, d, a, S0, do, dS_T = pins.rand_bwd(rng, 2, 2, 33, 7, 5)
+    g = backward.chunk_bwd(q, k, v, beta, d, a, S0, do, dS_T)
+    o, S_T = oracle.chunk_fwd(q, k, v, beta, d, a, S0, nthreads=2)
+    assert pins._rel(g["o"], o) < 1e-13 and pins._rel(g["S_T"], S_T) < 1e-13
+
+
+def test_no_decay_equals_unit_decay():
+    rng = np.random.default_rng(57)
+    q, k, v, beta, d, a, S0, do, dS_T = pins.rand_bwd(rng, 1, 2, 20, 5, 4)
+    g0 = backward.chunk_bwd(q, k, v, beta, d, None, S0, do, dS_T)
+    g1 = backward.chunk_bwd(q, k, v, beta, d, np.ones_like(a), S0, do, dS_T)
+    assert g0["dalpha"] is None
+    for n in ("dq", "dk", "dv", "dbeta", "dd", "dS0"):
+        assert np.array_equal(g0[n], g1[n]), n
+
+
+def _mutant(kind):
+    """The reverse pass with one planted mistake (kind == "none": faithful)."""
+    def impl(q, k, v, beta, d, a, S0, do, dS_T):
+        f = backward.forward_states(q, k, v, beta, d, a, S0)
+        B, H, T, dk = k.shape
+        dM = np.array(dS_T, dtype=np.float64)
+        g = {n: np.zeros_like(x) for n, x in (("dq", q), ("dk", k), ("dv", v), ("dbeta", beta),
+                                              ("dd", d), ("dalpha", a))}
+        for t in range(T - 1, -1, -1):
+            kt, qt, dot = k[:, :, t], q[:, :, t], do[:, :, t]
+            kw = d[:, :, t] * kt
+            u, y, Mh = f["u"][:, :, t], f["y"][:, :, t], f["Mh"][:, :, t]
+            Mt = Mh + kw[..., :, None] * u[..., None, :]
+            dM = dM + qt[..., :, None] * dot[..., None, :]
+            Mread = f["Mprev"][:, :, t] if kind == "readout_before_write" else Mt
+            g["dq"][:, :, t] = np.einsum("bhkv,bhv->bhk", Mread, dot)
+            dkw = np.einsum("bhkv,bhv->bhk", dM, u)
+            du = np.einsum("bhkv,bhk->bhv", dM, kt if kind == "du_plain_key" else kw)
+            res = v[:, :, t] if kind == "dbeta_no_recall" else v[:, :, t] - y
+            g["dbeta"][:, :, t] = np.sum(du * res, axis=-1)
+            g["dv"][:, :, t] = beta[:, :, t, None] * du
+            dy = (1.0 if kind == "dy_sign" else -1.0) * beta[:, :, t, None] * du
+            dMh = dM + kt[..., :, None] * dy[..., None, :]
+            dkt = np.einsum("bhkv,bhv->bhk", Mh, dy)
+            g["dd"][:, :, t] = dkw * kt
+            g["dk"][:, :, t] = dkt if kind == "dk_no_write_key" else dkt + dkw * d[:, :, t]
+            g["dalpha"][:, :, t] = np.einsum("bhkv,bhkv->bh", dMh, f["Mprev"][:, :, t])
+            dM = dMh if kind == "carry_undecayed" else a[:, :, t, None, None] * dMh
+        g["dS0"] = dM
+        g["o"], g["S_T"] = f["o"], f["S_T"]
+        return g
+    return impl
+
+
+MUTANTS = ["readout_before_write", "du_plain_key", "dbeta_no_recall", "dy_sign",
+           "dk_no_write_key", "carry_undecayed"]
+
+
+def test_mutant_harness_is_faithful():
+    impl = _mutant("none")
+    for name, (fn, tol) in pins.BWD_PINS.items():
+        assert fn(impl) <= tol, name
+
+
+@pytest.mark.parametrize("kind", MUTANTS)
+def test_pins_reject_mutant(kind):
+    impl = _mutant(kind)
+    failed = [n for n, (fn, tol) in pins.BWD_PINS.items() if not fn(impl) <= tol]
+    assert len(failed) >= 2, f"mutant {kind} fails only {failed}"
