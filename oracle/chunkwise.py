@@ -147,3 +147,86 @@ def chunk_fwd_channel(q, k, v, beta, d, alpha_ch, S0=None, chunk: int = 64
                 M = G[-1][:, None] * (M + Ktp.T @ U)
             S_T[b, h] = M
     return o, S_T
+
+
+def chunk_bwd(q, k, v, beta, d, alpha=None, S0=None, do=None, dS_T=None, chunk: int = 64):
+    """Chunk form of the reverse pass of ``oracle.backward.chunk_bwd`` (same contract and
+    outputs), derived here by differentiating the chunk algebra above.  Per chunk, with M0 the
+    state at its start, dMC the gradient with respect to the state at its end, w_s =
+    e^{g_C - g_s}, L the last row of the chunk, P = lower-inclusive((Q K~^T) o G) and A as above:
+
+        dU  = P^T dO + diag(w) K~ dMC          dR = (I + A)^{-T} dU
+        dM0 = gam_L dMC + Q^T diag(gam) dO - K^T diag(gam b) dR
+        dP  = lower-inclusive(dO U^T)          dA = -strictly-lower(dR U^T)
+        dQ  = diag(gam) dO M0^T + (dP o G) K~
+        Gb  = dA o G scaled by b_r (row r)
+        dK  = -diag(gam b) dR M0^T + Gb K~
+        dK~ = diag(w) U dMC^T + (dP o G)^T Q + Gb^T K
+        dV  = diag(b) dR
+        db_r = <dR_r, v_r - gam_r (K M0)_r> + sum_{s<r} dA[r,s] (K K~^T)[r,s] G[r,s]
+        dg_r = gam_r <dO_r, (Q M0)_r> - b_r gam_r <dR_r, (K M0)_r>
+               + sum_s (dP o P)[r,s] - sum_s (dP o P)[s,r]
+               + sum_s (dA o A)[r,s] - sum_s (dA o A)[s,r]  - w_r <k~_r, dMC u_r>
+               + [r = L] (gam_L <dMC, M0> + sum_s w_s <k~_s, dMC u_s>)
+        d ln a_t = sum_{t <= r <= L} dg_r ;  da = d ln a / a
+        dd  = dK~ o K ;  dK += dK~ o D
+    """
+    q, k, v, beta, d = (np.asarray(x, dtype=np.float64) for x in (q, k, v, beta, d))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    out = dict(dq=np.zeros_like(q), dk=np.zeros_like(k), dv=np.zeros_like(v),
+               dbeta=np.zeros_like(beta), dd=np.zeros_like(d),
+               dalpha=None if alpha is None else np.zeros((B, H, T)),
+               dS0=np.zeros((B, H, dk, dv)))
+    for b in range(B):
+        for h in range(H):
+            M = np.zeros((dk, dv)) if S0 is None else np.array(S0[b, h], dtype=np.float64)
+            starts, parts = [], []
+            for c0 in range(0, T, chunk):  # forward: the state at every chunk start
+                c1 = min(c0 + chunk, T)
+                Q, K, V, bt = q[b, h, c0:c1], k[b, h, c0:c1], v[b, h, c0:c1], beta[b, h, c0:c1]
+                Kt = d[b, h, c0:c1] * K
+                la = np.zeros(c1 - c0) if alpha is None else np.log(np.asarray(alpha[b, h, c0:c1], np.float64))
+                g = np.cumsum(la)
+                gam = np.exp(g)
+                G = np.exp(g[:, None] - g[None, :])
+                A = np.tril(bt[:, None] * (K @ Kt.T) * G, -1)
+                R = bt[:, None] * (V - gam[:, None] * (K @ M))
+                U = solve_triangular(np.eye(c1 - c0) + A, R, lower=True, unit_diagonal=True)
+                P = np.tril((Q @ Kt.T) * G)
+                w = np.exp(g[-1] - g)
+                starts.append(M)
+                parts.append((c0, c1, Q, K, V, bt, Kt, g, gam, G, A, U, P, w))
+                M = gam[-1] * M + (w[:, None] * Kt).T @ U
+            dM = np.zeros((dk, dv)) if dS_T is None else np.array(dS_T[b, h], dtype=np.float64)
+            for (c0, c1, Q, K, V, bt, Kt, g, gam, G, A, U, P, w), M0 in zip(parts[::-1], starts[::-1]):
+                n = c1 - c0
+                dO = np.zeros((n, dv)) if do is None else np.asarray(do[b, h, c0:c1], np.float64)
+                KdM = Kt @ dM
+                dU = P.T @ dO + w[:, None] * KdM
+                dR = solve_triangular(np.eye(n) + A, dU, lower=True, unit_diagonal=True, trans=1)
+                dP = np.tril(dO @ U.T)
+                dA = -np.tril(dR @ U.T, -1)
+                KM0, QM0 = K @ M0, Q @ M0
+                dPG = dP * G
+                Gb = dA * G * bt[:, None]
+                dQ = gam[:, None] * (dO @ M0.T) + dPG @ Kt
+                dK = -(gam * bt)[:, None] * (dR @ M0.T) + Gb @ Kt
+                dKt = w[:, None] * (U @ dM.T) + dPG.T @ Q + Gb.T @ K
+                out["dv"][b, h, c0:c1] = bt[:, None] * dR
+                out["dbeta"][b, h, c0:c1] = (np.sum(dR * (V - gam[:, None] * KM0), axis=1)
+                                             + np.sum(np.tril(dA * (K @ Kt.T) * G, -1), axis=1))
+                EP, EA = dP * P, dA * A
+                ew = w * np.sum(KdM * U, axis=1)
+                dg = (gam * np.sum(dO * QM0, axis=1) - bt * gam * np.sum(dR * KM0, axis=1)
+                      + EP.sum(1) - EP.sum(0) + EA.sum(1) - EA.sum(0) - ew)
+                dg[-1] += gam[-1] * np.sum(dM * M0) + ew.sum()
+                if alpha is not None:
+                    dla = np.cumsum(dg[::-1])[::-1]
+                    out["dalpha"][b, h, c0:c1] = dla / np.asarray(alpha[b, h, c0:c1], np.float64)
+                out["dq"][b, h, c0:c1] = dQ
+                out["dd"][b, h, c0:c1] = dKt * K
+                out["dk"][b, h, c0:c1] = dK + dKt * d[b, h, c0:c1]
+                dM = gam[-1] * dM + Q.T @ (gam[:, None] * dO) - K.T @ ((gam * bt)[:, None] * dR)
+            out["dS0"][b, h] = dM
+    return out

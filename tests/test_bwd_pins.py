@@ -86,3 +86,17 @@ def test_pins_reject_mutant(kind):
     impl = _mutant(kind)
     failed = [n for n, (fn, tol) in pins.BWD_PINS.items() if not fn(impl) <= tol]
     assert len(failed) >= 2, f"mutant {kind} fails only {failed}"
+
+
+@pytest.mark.parametrize("chunk", [1, 3, 16, 64, 150])
+def test_chunk_model_equals_reverse_pass(chunk):
+    """The chunk form of the backward (what the GPU kernels compute) against the token
+    reverse pass, with and without decay and initial state."""
+    from oracle import chunkwise
+    rng = np.random.default_rng(58 + chunk)
+    q, k, v, beta, d, a, S0, do, dS_T = pins.rand_bwd(rng, 2, 2, 130, 8, 5)
+    for aa, ss, dst in ((a, S0, dS_T), (None, None, None)):
+        ref = backward.chunk_bwd(q, k, v, beta, d, aa, ss, do, dst)
+        got = chunkwise.chunk_bwd(q, k, v, beta, d, aa, ss, do, dst, chunk=chunk)
+        for n in ("dq", "dk", "dv", "dbeta", "dd", "dS0") + (("dalpha",) if aa is not None else ()):
+            assert pins._rel(got[n], ref[n]) < 1e-12, (n, chunk)
