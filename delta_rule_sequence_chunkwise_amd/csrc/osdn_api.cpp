@@ -369,3 +369,104 @@ osdn_status osdn_step_kda(const void *q, const void *k, const void *v, const flo
 }
 
 }  // extern "C"
+
+namespace {
+
+// bytes of each of the two state checkpoints of the backward, [BH, nchunks, dk, dv] fp32;
+// -1 if the sizes are invalid
+int64_t bwd_ckpt_bytes(int64_t B, int64_t H, int64_t T, int32_t dk, int32_t dv, osdn_dtype qkv) {
+    if (B < 0 || H < 0 || T < 0 || !dtype_ok(qkv) || !head_dim_ok(dk) || !head_dim_ok(dv))
+        return -1;
+    const int64_t C = osdn::bwd_chunk_size(qkv);
+    int64_t n = 1;
+    if (!mul_ok(n, B, kMaxElems) || !mul_ok(n, H, kMaxElems) ||
+        !mul_ok(n, (T + C - 1) / C, kMaxElems) || !mul_ok(n, int64_t(dk) * dv, kMaxElems))
+        return -1;
+    return round256(n * 4);
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t osdn_chunk_bwd_workspace(int64_t B, int64_t H, int64_t T, int32_t dk, int32_t dv,
+                                 osdn_dtype qkv) {
+    const int64_t b = bwd_ckpt_bytes(B, H, T, dk, dv, qkv);
+    return b < 0 ? -1 : 2 * b;
+}
+
+osdn_status osdn_chunk_bwd(const void *q, const void *k, const void *v, const float *beta,
+                           const void *d, const float *alpha, const float *S0,
+                           const void *grad_o, const float *grad_S_T, void *grad_q,
+                           void *grad_k, void *grad_v, float *grad_beta, void *grad_d,
+                           float *grad_alpha, float *grad_S0, void *workspace,
+                           int64_t workspace_bytes, int64_t B, int64_t H, int64_t T, int32_t dk,
+                           int32_t dv, osdn_dtype qkv, osdn_dtype d_dtype, void *stream) {
+    if (B < 0 || H < 0 || T < 0) return OSDN_ERR_SHAPE;
+    if (!dtype_ok(qkv) || !dtype_ok(d_dtype)) return OSDN_ERR_UNSUPPORTED;
+    if (!head_dim_ok(dk) || !head_dim_ok(dv)) return OSDN_ERR_UNSUPPORTED;
+    const int64_t ck = bwd_ckpt_bytes(B, H, T, dk, dv, qkv);
+    if (ck < 0) return OSDN_ERR_SHAPE;
+    int64_t BH = 1;
+    if (!mul_ok(BH, B, kMaxElems) || !mul_ok(BH, H, kMaxElems)) return OSDN_ERR_SHAPE;
+    int64_t tok = BH, st = BH;
+    if (!mul_ok(tok, T, kMaxElems) || !mul_ok(st, int64_t(dk) * dv, kMaxElems))
+        return OSDN_ERR_SHAPE;
+    int64_t nqk = tok, nv = tok;
+    if (!mul_ok(nqk, dk, kMaxElems) || !mul_ok(nv, dv, kMaxElems)) return OSDN_ERR_SHAPE;
+    const int64_t C = osdn::bwd_chunk_size(qkv), nch = (T + C - 1) / C;
+    if (BH * nch > int64_t(0x7fffffff) || BH * (dv / 32) > int64_t(0x7fffffff))
+        return OSDN_ERR_SHAPE;  // grid sizes
+
+    if (BH == 0) return OSDN_OK;
+    if (T > 0 && (!q || !k || !v || !beta || !d || !grad_o || !grad_q || !grad_k || !grad_v ||
+                  !grad_beta || !grad_d || !workspace))
+        return OSDN_ERR_NULL;
+    if (T == 0 && !grad_S0) return OSDN_OK;
+    if (T > 0 && workspace_bytes < 2 * ck) return OSDN_ERR_SHAPE;
+    if (!alpha) grad_alpha = nullptr;
+
+    const int64_t eq = elem_size(qkv), ed = elem_size(d_dtype);
+    if (T > 0) {
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(d, 16) ||
+            !aligned(grad_o, 16) || !aligned(grad_q, 16) || !aligned(grad_k, 16) ||
+            !aligned(grad_v, 16) || !aligned(grad_d, 16) || !aligned(beta, 4) ||
+            !aligned(grad_beta, 4) || (alpha && !aligned(alpha, 4)) ||
+            (grad_alpha && !aligned(grad_alpha, 4)) || !aligned(workspace, 256))
+            return OSDN_ERR_ALIGN;
+    }
+    if ((S0 && !aligned(S0, 16)) || (grad_S_T && !aligned(grad_S_T, 16)) ||
+        (grad_S0 && !aligned(grad_S0, 16)))
+        return OSDN_ERR_ALIGN;
+
+    const int64_t nt = T > 0 ? tok : 0;
+    const Range rq = range_of(q, nt ? nqk * eq : 0), rk = range_of(k, nt ? nqk * eq : 0);
+    const Range rv = range_of(v, nt ? nv * eq : 0), rd = range_of(d, nt ? nqk * ed : 0);
+    const Range rb = range_of(beta, nt * 4), ra = range_of(alpha, alpha ? nt * 4 : 0);
+    const Range rs0 = range_of(S0, st * 4), rgo = range_of(grad_o, nt ? nv * eq : 0);
+    const Range rgst = range_of(grad_S_T, st * 4);
+    const Range gq = range_of(grad_q, nt ? nqk * eq : 0), gk = range_of(grad_k, nt ? nqk * eq : 0);
+    const Range gv = range_of(grad_v, nt ? nv * eq : 0), gd = range_of(grad_d, nt ? nqk * ed : 0);
+    const Range gb = range_of(grad_beta, nt * 4), ga = range_of(grad_alpha, grad_alpha ? nt * 4 : 0);
+    const Range gs0 = range_of(grad_S0, st * 4);
+    const Range rw = range_of(workspace, T > 0 ? 2 * ck : 0);
+    const Range *outs[] = {&gq, &gk, &gv, &gd, &gb, &ga, &gs0, &rw};
+    const Range *ins[] = {&rq, &rk, &rv, &rd, &rb, &ra, &rs0, &rgo, &rgst};
+    for (int i = 0; i < 8; ++i) {
+        for (const Range *in : ins)
+            if (overlap(*outs[i], *in)) return OSDN_ERR_ALIAS;
+        for (int j = i + 1; j < 8; ++j)
+            if (overlap(*outs[i], *outs[j])) return OSDN_ERR_ALIAS;
+    }
+
+    char *ws = static_cast<char *>(workspace);
+    osdn::BwdArgs a{q, k, v, d, beta, alpha, S0, grad_o, grad_S_T, grad_q, grad_k, grad_v,
+                    grad_beta, grad_alpha, grad_d, grad_S0,
+                    T > 0 ? reinterpret_cast<float *>(ws) : nullptr,
+                    T > 0 ? reinterpret_cast<float *>(ws + ck) : nullptr, BH, T, dk, dv, qkv,
+                    d_dtype};
+    const hipError_t err = osdn::launch_chunk_bwd(a, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? OSDN_OK : OSDN_ERR_LAUNCH;
+}
+
+}  // extern "C"

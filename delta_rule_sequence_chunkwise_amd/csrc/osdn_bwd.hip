@@ -1,0 +1,580 @@
+// Backward of the chunkwise OSDN forward, gfx950: the gradients of q, k, v, beta, d, alpha and
+// the initial state for given gradients of o and of the final state.
+//
+// The pages give no backward pass.  The chunk form used here is derived by differentiating the
+// chunk algebra of the forward (itself derived from the token step of the OSDN technical
+// summary, section 2.1, with the gated-delta decay of Erase-then-Delta Attention, section 2.2,
+// eq. 4).  Per chunk of C rows, with M0 the state at its start, dMC the gradient with respect
+// to the state at its end, L its last row, and A, P, U, g, gam = e^g, w = e^{g_L - g} and
+// G[r,s] = e^{g_r - g_s} as in the forward (A = b_r AS with AS the strictly lower, decayed
+// K K~^T):
+//
+//   dU  = P^T dO + diag(w) K~ dMC               dR = (I + A)^{-T} dU
+//   dM0 = gam_L dMC + Q^T diag(gam) dO - K^T diag(gam b) dR
+//   dP  = lower-inclusive(dO U^T)               dA = -strictly-lower(dR U^T)
+//   dQ  = diag(gam) dO M0^T + (dP o G) K~
+//   dK  = -diag(gam b) dR M0^T + Gb K~          Gb = dA o G, row r scaled by b_r
+//   dK~ = diag(w) U dMC^T + (dP o G)^T Q + Gb^T K
+//   dV  = diag(b) dR
+//   db_r = <dR_r, v_r - gam_r (K M0)_r> + sum_s dA[r,s] AS[r,s]
+//   dg_r = gam_r <dO_r, (Q M0)_r> - b_r gam_r <dR_r, (K M0)_r> - w_r <(K~ dMC)_r, U_r>
+//          + (row sum - column sum)_r of (dP o P + dA o A)
+//          + [r = L] (gam_L <dMC, M0> + sum_s w_s <(K~ dMC)_s, U_s>)
+//   d ln a_t = sum_{t <= r <= L} dg_r,   da = d ln a / a
+//   dd  = dK~ o K,   dK += dK~ o D
+//
+// Three launches on the caller's stream: (1) the fp32 forward records M0 of every chunk into
+// the workspace; (2) bwd_state_kernel walks the chunks backwards per (sequence, value slice)
+// carrying dM, records dMC of every chunk and writes the initial-state gradient; (3)
+// bwd_chunk_kernel, one workgroup per (sequence, chunk), computes every gradient of the
+// chunk's rows from M0 and dMC.  Arithmetic is fp32 on the vector ALUs for both input types:
+// tile products are register-blocked (each of the 256 threads owns one (M/16) x (N/16) block
+// of every M x N product), the triangular solves run column-parallel with the partial sums of
+// one column reduced across adjacent lanes.  Rows past the end of the sequence are zero
+// (beta = 0, alpha = 1, dO = 0), so they add nothing.
+#include "osdn_internal.h"
+
+namespace osdn {
+namespace {
+
+constexpr int NT = 256;  // threads per workgroup
+
+// acc[m][n] += sum_{kk < K} a(i0 + m, kk) * b(kk, j0 + n)
+template <int TM, int TN, int K, typename FA, typename FB>
+__device__ __forceinline__ void mm(float (&acc)[TM][TN], int i0, int j0, FA &&a, FB &&b) {
+#pragma unroll 2
+    for (int kk = 0; kk < K; ++kk) {
+        float av[TM], bv[TN];
+#pragma unroll
+        for (int m = 0; m < TM; ++m) av[m] = a(i0 + m, kk);
+#pragma unroll
+        for (int n = 0; n < TN; ++n) bv[n] = b(kk, j0 + n);
+#pragma unroll
+        for (int m = 0; m < TM; ++m)
+#pragma unroll
+            for (int n = 0; n < TN; ++n) acc[m][n] += av[m] * bv[n];
+    }
+}
+
+template <int TM, int TN>
+__device__ __forceinline__ void zero(float (&acc)[TM][TN]) {
+#pragma unroll
+    for (int m = 0; m < TM; ++m)
+#pragma unroll
+        for (int n = 0; n < TN; ++n) acc[m][n] = 0.f;
+}
+
+// X[r][j] -= b_r sum_{s<r} AS[r][s] X[s][j] for every row r in order, columns j < NC, in place
+// (X = (I + A)^{-1} X with A = diag(b) AS).  Column j is owned by TPC adjacent lanes; lane sub
+// keeps rows s = i TPC + sub of it in registers.
+template <int C, int NC, int PX, int PA>
+__device__ __forceinline__ void solve_lower(float *X, const float *AS, const float *b, int tid) {
+    constexpr int TPC = NT / NC, RPT = C / TPC;
+    static_assert(TPC * NC == NT && RPT * TPC == C && 64 % TPC == 0, "solve layout");
+    const int j = tid / TPC, sub = tid % TPC;
+    float mine[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) mine[i] = 0.f;
+#pragma unroll
+    for (int r = 0; r < C; ++r) {
+        float part = 0.f;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            if (i * TPC < r) {
+                const int s = i * TPC + sub;
+                if (s < r) part += AS[r * PA + s] * mine[i];
+            }
+        }
+#pragma unroll
+        for (int m = 1; m < TPC; m <<= 1) part += __shfl_xor(part, m);
+        const float val = X[r * PX + j] - b[r] * part;
+        if (r % TPC == sub) mine[r / TPC] = val;
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) X[(i * TPC + sub) * PX + j] = mine[i];
+}
+
+// X[r][j] -= sum_{s>r} b_s AS[s][r] X[s][j] for rows r = C-1 .. 0, in place
+// (X = (I + A)^{-T} X)
+template <int C, int NC, int PX, int PA>
+__device__ __forceinline__ void solve_upper(float *X, const float *AS, const float *b, int tid) {
+    constexpr int TPC = NT / NC, RPT = C / TPC;
+    static_assert(TPC * NC == NT && RPT * TPC == C && 64 % TPC == 0, "solve layout");
+    const int j = tid / TPC, sub = tid % TPC;
+    float mine[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) mine[i] = 0.f;
+#pragma unroll
+    for (int r = C - 1; r >= 0; --r) {
+        float part = 0.f;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            if (i * TPC + TPC - 1 > r) {
+                const int s = i * TPC + sub;
+                if (s > r) part += b[s] * AS[s * PA + r] * mine[i];
+            }
+        }
+#pragma unroll
+        for (int m = 1; m < TPC; m <<= 1) part += __shfl_xor(part, m);
+        const float val = X[r * PX + j] - part;
+        if (r % TPC == sub) mine[r / TPC] = val;
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) X[(i * TPC + sub) * PX + j] = mine[i];
+}
+
+// g = running sum of ln(alpha) over the chunk's rows (0 past the end), gam = e^g,
+// w = e^{g_last - g}; beta (0 past the end).  Wave 0 only.
+template <int C>
+__device__ __forceinline__ void decay_scan(const float *beta, const float *alpha, int64_t row0,
+                                           int n, float *sb, float *sg, float *sgam, float *sw,
+                                           int lane) {
+    float x = (lane < n && alpha) ? logf(alpha[row0 + lane]) : 0.f;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    const float gl = __shfl(x, C - 1);
+    if (lane < C) {
+        sb[lane] = lane < n ? beta[row0 + lane] : 0.f;
+        sg[lane] = x;
+        sgam[lane] = __expf(x);
+        sw[lane] = __expf(gl - x);
+    }
+}
+
+// Q and K of the chunk in their input type, K~ = d (.) k in fp32 (zero rows past the end)
+template <int C, int DK, int PQ, int PX, typename TQ, typename TD>
+__device__ __forceinline__ void load_qk(const TQ *q, const TQ *k, const TD *d, int64_t row0, int n,
+                                        TQ *sQ, TQ *sK, float *sKt, int tid) {
+    for (int idx = tid; idx < C * DK; idx += NT) {
+        const int r = idx / DK, f = idx % DK;
+        TQ qv = from_f32<TQ>(0.f), kv = from_f32<TQ>(0.f);
+        float dv = 0.f;
+        if (r < n) {
+            qv = q[(row0 + r) * DK + f];
+            kv = k[(row0 + r) * DK + f];
+            dv = to_f32(d[(row0 + r) * DK + f]);
+        }
+        sQ[r * PQ + f] = qv;
+        sK[r * PQ + f] = kv;
+        sKt[r * PX + f] = dv * to_f32(kv);
+    }
+}
+
+// AS = strictly lower (K K~^T) o G and P = lower-inclusive (Q K~^T) o G
+template <int C, int DK, int PQ, int PX, int PC, typename TQ>
+__device__ __forceinline__ void scores(const TQ *sQ, const TQ *sK, const float *sKt,
+                                       const float *sg, float *sAS, float *sP, int tid) {
+    constexpr int TM = C / 16;
+    const int i0 = (tid / 16) * TM, j0 = (tid % 16) * TM;
+    float ak[TM][TM], aq[TM][TM];
+    zero(ak);
+    zero(aq);
+    auto bkt = [&](int kk, int j) { return sKt[j * PX + kk]; };
+    mm<TM, TM, DK>(ak, i0, j0, [&](int i, int kk) { return to_f32(sK[i * PQ + kk]); }, bkt);
+    mm<TM, TM, DK>(aq, i0, j0, [&](int i, int kk) { return to_f32(sQ[i * PQ + kk]); }, bkt);
+#pragma unroll
+    for (int m = 0; m < TM; ++m)
+#pragma unroll
+        for (int nn = 0; nn < TM; ++nn) {
+            const int i = i0 + m, j = j0 + nn;
+            const float G = j <= i ? __expf(sg[i] - sg[j]) : 0.f;
+            sAS[i * PC + j] = j < i ? ak[m][nn] * G : 0.f;
+            sP[i * PC + j] = aq[m][nn] * G;
+        }
+}
+
+// Fixed-order sum over the workgroup (every thread passes its part; every thread gets the sum)
+__device__ __forceinline__ float block_sum(float x, float *scratch4, int tid) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+    __syncthreads();
+    if ((tid & 63) == 0) scratch4[tid >> 6] = x;
+    __syncthreads();
+    return scratch4[0] + scratch4[1] + scratch4[2] + scratch4[3];
+}
+
+// ---- reverse pass over chunks: the state gradient ------------------------------------------
+// One workgroup per (sequence, BV-wide value slice); dM[:, slice] stays in LDS.  dMck[c] gets
+// the gradient with respect to the state at the end of chunk c; dS0 the one at the start.
+template <int C, int DK, int BV, typename TQ, typename TD>
+__global__ void __launch_bounds__(NT)
+bwd_state_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k, const TD *__restrict__ d,
+                 const float *__restrict__ beta, const float *__restrict__ alpha,
+                 const TQ *__restrict__ dO, const float *__restrict__ dS_T,
+                 float *__restrict__ dMck, float *__restrict__ dS0, int64_t T, int dv) {
+    constexpr int PQ = DK + (sizeof(TQ) == 2 ? 2 : 1);
+    constexpr int PX = DK + 1, PC = C + 1, PS = BV + 1;
+    __shared__ TQ sQ[C * PQ], sK[C * PQ];
+    __shared__ float sKt[C * PX], sAS[C * PC], sP[C * PC];
+    __shared__ float sdO[C * PS], sX[C * PS], sdM[DK * PS];
+    __shared__ float sb[C], sg[C], sgam[C], sw[C];
+
+    const int nvt = dv / BV;
+    const int64_t bh = blockIdx.x / nvt;
+    const int j0 = static_cast<int>(blockIdx.x % nvt) * BV;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int64_t nch = (T + C - 1) / C;
+
+    for (int idx = tid; idx < DK * BV; idx += NT) {
+        const int f = idx / BV, j = idx % BV;
+        sdM[f * PS + j] = dS_T ? dS_T[(bh * DK + f) * dv + j0 + j] : 0.f;
+    }
+    for (int64_t c = nch - 1; c >= 0; --c) {
+        const int64_t c0 = c * C, row0 = bh * T + c0;
+        const int n = static_cast<int>(T - c0 < C ? T - c0 : C);
+        __syncthreads();  // the previous chunk is done with every buffer
+        load_qk<C, DK, PQ, PX>(q, k, d, row0, n, sQ, sK, sKt, tid);
+        for (int idx = tid; idx < C * BV; idx += NT) {
+            const int r = idx / BV, j = idx % BV;
+            sdO[r * PS + j] = r < n ? to_f32(dO[(row0 + r) * dv + j0 + j]) : 0.f;
+        }
+        if (tid < 64) decay_scan<C>(beta, alpha, row0, n, sb, sg, sgam, sw, lane);
+        // the gradient with respect to the state at the end of this chunk
+        for (int idx = tid; idx < DK * BV; idx += NT) {
+            const int f = idx / BV, j = idx % BV;
+            dMck[((bh * nch + c) * DK + f) * dv + j0 + j] = sdM[f * PS + j];
+        }
+        __syncthreads();
+        scores<C, DK, PQ, PX, PC>(sQ, sK, sKt, sg, sAS, sP, tid);
+        __syncthreads();
+        {  // dU = P^T dO + diag(w) K~ dM
+            constexpr int TM = C / 16, TN = BV / 16;
+            const int i0 = (tid / 16) * TM, j0l = (tid % 16) * TN;
+            float acc[TM][TN], acc2[TM][TN];
+            zero(acc);
+            zero(acc2);
+            mm<TM, TN, DK>(acc, i0, j0l, [&](int i, int kk) { return sKt[i * PX + kk]; },
+                           [&](int kk, int j) { return sdM[kk * PS + j]; });
+            mm<TM, TN, C>(acc2, i0, j0l, [&](int i, int kk) { return sP[kk * PC + i]; },
+                          [&](int kk, int j) { return sdO[kk * PS + j]; });
+#pragma unroll
+            for (int m = 0; m < TM; ++m)
+#pragma unroll
+                for (int nn = 0; nn < TN; ++nn)
+                    sX[(i0 + m) * PS + j0l + nn] = acc2[m][nn] + sw[i0 + m] * acc[m][nn];
+        }
+        __syncthreads();
+        solve_upper<C, BV, PS, PC>(sX, sAS, sb, tid);  // dR
+        __syncthreads();
+        {  // dM <- gam_L dM + Q^T diag(gam) dO - K^T diag(gam b) dR
+            constexpr int TM = DK / 16, TN = BV / 16;
+            const int i0 = (tid / 16) * TM, j0l = (tid % 16) * TN;
+            float acc[TM][TN];
+            zero(acc);
+            mm<TM, TN, C>(acc, i0, j0l, [&](int f, int r) { return to_f32(sQ[r * PQ + f]); },
+                          [&](int r, int j) { return sgam[r] * sdO[r * PS + j]; });
+            mm<TM, TN, C>(acc, i0, j0l, [&](int f, int r) { return to_f32(sK[r * PQ + f]); },
+                          [&](int r, int j) { return -sgam[r] * sb[r] * sX[r * PS + j]; });
+            const float gl = sgam[C - 1];
+#pragma unroll
+            for (int m = 0; m < TM; ++m)
+#pragma unroll
+                for (int nn = 0; nn < TN; ++nn) {
+                    float &x = sdM[(i0 + m) * PS + j0l + nn];
+                    x = gl * x + acc[m][nn];
+                }
+        }
+    }
+    __syncthreads();
+    if (dS0) {
+        for (int idx = tid; idx < DK * BV; idx += NT) {
+            const int f = idx / BV, j = idx % BV;
+            dS0[(bh * DK + f) * dv + j0 + j] = sdM[f * PS + j];
+        }
+    }
+}
+
+// ---- per-chunk gradients ----------------------------------------------------------------------
+// One workgroup per (sequence, chunk).  The value columns are taken BV at a time; dP, dA, dQ,
+// dK and dK~ accumulate over them in registers.
+template <int C, int DK, int DV, int BV, typename TQ, typename TD>
+__global__ void __launch_bounds__(NT)
+bwd_chunk_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k, const TQ *__restrict__ v,
+                 const TD *__restrict__ d, const float *__restrict__ beta,
+                 const float *__restrict__ alpha, const TQ *__restrict__ dO,
+                 const float *__restrict__ Mck, const float *__restrict__ dMck,
+                 TQ *__restrict__ gq, TQ *__restrict__ gk, TQ *__restrict__ gv,
+                 float *__restrict__ gbeta, TD *__restrict__ gd, float *__restrict__ galpha,
+                 int64_t T, int64_t nch) {
+    constexpr int PQ = DK + (sizeof(TQ) == 2 ? 2 : 1);
+    constexpr int PX = DK + 1, PC = C + 1, PS = BV + 1;
+    constexpr int TC = C / 16, TK = DK / 16, TV = BV / 16;  // register blocks
+    __shared__ TQ sQ[C * PQ], sK[C * PQ];
+    __shared__ float sKt[C * PX], sAS[C * PC], sP[C * PC];
+    // slice buffers; after the slices, sM0/sdM hold column partial sums
+    __shared__ float sM0[DK * PS], sdM[DK * PS];
+    __shared__ float sY[C * PS], sdO[C * PS], sU[C * PS], sdR[C * PS];
+    __shared__ float sKM[C * PS], sQM[C * PS], sKdM[C * PS];
+    __shared__ float sb[C], sg[C], sgam[C], sw[C], sdb[C], sdg[C], sew[C], sred[4];
+
+    const int64_t bh = blockIdx.x / nch, c = blockIdx.x % nch;
+    const int64_t c0 = c * C, row0 = bh * T + c0;
+    const int n = static_cast<int>(T - c0 < C ? T - c0 : C);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int ti = tid / 16, tj = tid % 16;
+    const float *M0 = Mck + (bh * nch + c) * DK * DV;
+    const float *dMC = dMck + (bh * nch + c) * DK * DV;
+
+    load_qk<C, DK, PQ, PX>(q, k, d, row0, n, sQ, sK, sKt, tid);
+    if (tid < 64) decay_scan<C>(beta, alpha, row0, n, sb, sg, sgam, sw, lane);
+    if (tid < C) sdb[tid] = sdg[tid] = sew[tid] = 0.f;
+    __syncthreads();
+    scores<C, DK, PQ, PX, PC>(sQ, sK, sKt, sg, sAS, sP, tid);
+
+    float aQ[TC][TK], aK[TC][TK], aKt[TC][TK], adP[TC][TC], adA[TC][TC];
+    zero(aQ);
+    zero(aK);
+    zero(aKt);
+    zero(adP);
+    zero(adA);
+    float frob = 0.f;  // this thread's part of <dMC, M0>
+    const int ic = ti * TC, jc = tj * TC;  // C x C block
+    const int ik = ti * TC, jk = tj * TK;  // C x DK block
+    const int is = ti * TC, js = tj * TV;  // C x BV block
+
+    for (int s0 = 0; s0 < DV; s0 += BV) {
+        __syncthreads();  // the previous slice (and the scores) are done
+        for (int idx = tid; idx < DK * BV; idx += NT) {
+            const int f = idx / BV, j = idx % BV;
+            const float m0 = M0[f * DV + s0 + j], dm = dMC[f * DV + s0 + j];
+            sM0[f * PS + j] = m0;
+            sdM[f * PS + j] = dm;
+            frob += m0 * dm;
+        }
+        for (int idx = tid; idx < C * BV; idx += NT) {
+            const int r = idx / BV, j = idx % BV;
+            sY[r * PS + j] = r < n ? to_f32(v[(row0 + r) * DV + s0 + j]) : 0.f;
+            sdO[r * PS + j] = r < n ? to_f32(dO[(row0 + r) * DV + s0 + j]) : 0.f;
+        }
+        __syncthreads();
+        {  // K M0, Q M0, K~ dMC on this slice; then Y = V - gam K M0 and R = b Y into U
+            float a1[TC][TV], a2[TC][TV], a3[TC][TV];
+            zero(a1);
+            zero(a2);
+            zero(a3);
+            auto bm = [&](int kk, int j) { return sM0[kk * PS + j]; };
+            mm<TC, TV, DK>(a1, is, js, [&](int i, int kk) { return to_f32(sK[i * PQ + kk]); }, bm);
+            mm<TC, TV, DK>(a2, is, js, [&](int i, int kk) { return to_f32(sQ[i * PQ + kk]); }, bm);
+            mm<TC, TV, DK>(a3, is, js, [&](int i, int kk) { return sKt[i * PX + kk]; },
+                           [&](int kk, int j) { return sdM[kk * PS + j]; });
+#pragma unroll
+            for (int m = 0; m < TC; ++m)
+#pragma unroll
+                for (int nn = 0; nn < TV; ++nn) {
+                    const int r = is + m, j = js + nn;
+                    sKM[r * PS + j] = a1[m][nn];
+                    sQM[r * PS + j] = a2[m][nn];
+                    sKdM[r * PS + j] = a3[m][nn];
+                    const float y = sY[r * PS + j] - sgam[r] * a1[m][nn];
+                    sY[r * PS + j] = y;
+                    sU[r * PS + j] = sb[r] * y;
+                }
+        }
+        __syncthreads();
+        solve_lower<C, BV, PS, PC>(sU, sAS, sb, tid);  // U = (I + A)^{-1} R
+        __syncthreads();
+        {  // dU = P^T dO + diag(w) K~ dMC
+            float acc[TC][TV];
+            zero(acc);
+            mm<TC, TV, C>(acc, is, js, [&](int i, int kk) { return sP[kk * PC + i]; },
+                          [&](int kk, int j) { return sdO[kk * PS + j]; });
+#pragma unroll
+            for (int m = 0; m < TC; ++m)
+#pragma unroll
+                for (int nn = 0; nn < TV; ++nn) {
+                    const int r = is + m, j = js + nn;
+                    sdR[r * PS + j] = acc[m][nn] + sw[r] * sKdM[r * PS + j];
+                }
+        }
+        __syncthreads();
+        solve_upper<C, BV, PS, PC>(sdR, sAS, sb, tid);  // dR = (I + A)^{-T} dU
+        __syncthreads();
+        for (int idx = tid; idx < C * BV; idx += NT) {
+            const int r = idx / BV, j = idx % BV;
+            if (r < n) gv[(row0 + r) * DV + s0 + j] = from_f32<TQ>(sb[r] * sdR[r * PS + j]);
+        }
+        if (tid < C) {  // row sums of this slice (each row owned by one thread)
+            const int r = tid;
+            float db = 0.f, go = 0.f, gr = 0.f, ew = 0.f;
+            for (int j = 0; j < BV; ++j) {
+                db += sdR[r * PS + j] * sY[r * PS + j];
+                go += sdO[r * PS + j] * sQM[r * PS + j];
+                gr += sdR[r * PS + j] * sKM[r * PS + j];
+                ew += sKdM[r * PS + j] * sU[r * PS + j];
+            }
+            sdb[r] += db;
+            sdg[r] += sgam[r] * go - sb[r] * sgam[r] * gr;
+            sew[r] += sw[r] * ew;
+        }
+        // dP += dO U^T, dA += dR U^T (negated later), and the slice's part of dQ, dK, dK~
+        auto bu = [&](int kk, int j) { return sU[j * PS + kk]; };
+        mm<TC, TC, BV>(adP, ic, jc, [&](int i, int kk) { return sdO[i * PS + kk]; }, bu);
+        mm<TC, TC, BV>(adA, ic, jc, [&](int i, int kk) { return sdR[i * PS + kk]; }, bu);
+        auto bm0t = [&](int kk, int f) { return sM0[f * PS + kk]; };
+        mm<TC, TK, BV>(aQ, ik, jk, [&](int i, int kk) { return sgam[i] * sdO[i * PS + kk]; }, bm0t);
+        mm<TC, TK, BV>(aK, ik, jk,
+                       [&](int i, int kk) { return -sgam[i] * sb[i] * sdR[i * PS + kk]; }, bm0t);
+        mm<TC, TK, BV>(aKt, ik, jk, [&](int i, int kk) { return sw[i] * sU[i * PS + kk]; },
+                       [&](int kk, int f) { return sdM[f * PS + kk]; });
+    }
+    frob = block_sum(frob, sred, tid);  // ends with a barrier: the slices are done
+
+    // dP (lower-inclusive) and dA (strictly lower, negated); their products with P and A give
+    // the decay terms: row sums here, column sums through LDS (sM0 as [16][C] partials)
+    float *colpart = sM0;
+    {
+        float rowp[TC], colp[TC];
+#pragma unroll
+        for (int m = 0; m < TC; ++m) rowp[m] = colp[m] = 0.f;
+        float rowb[TC];
+#pragma unroll
+        for (int m = 0; m < TC; ++m) rowb[m] = 0.f;
+#pragma unroll
+        for (int m = 0; m < TC; ++m)
+#pragma unroll
+            for (int nn = 0; nn < TC; ++nn) {
+                const int i = ic + m, j = jc + nn;
+                const float dp = j <= i ? adP[m][nn] : 0.f;
+                const float da = j < i ? -adA[m][nn] : 0.f;
+                adP[m][nn] = dp;
+                adA[m][nn] = da;
+                const float e = dp * sP[i * PC + j] + da * sb[i] * sAS[i * PC + j];
+                rowp[m] += e;
+                colp[nn] += e;
+                rowb[m] += da * sAS[i * PC + j];
+            }
+#pragma unroll
+        for (int m = 0; m < TC; ++m) {
+#pragma unroll
+            for (int w = 1; w < 16; w <<= 1) {
+                rowp[m] += __shfl_xor(rowp[m], w);
+                rowb[m] += __shfl_xor(rowb[m], w);
+            }
+        }
+        if (tj == 0) {
+#pragma unroll
+            for (int m = 0; m < TC; ++m) {
+                sdg[ic + m] += rowp[m];
+                sdb[ic + m] += rowb[m];
+            }
+        }
+#pragma unroll
+        for (int nn = 0; nn < TC; ++nn) colpart[ti * C + jc + nn] = colp[nn];
+    }
+    __syncthreads();
+    if (tid < C) {
+        float s = 0.f;
+        for (int t = 0; t < 16; ++t) s += colpart[t * C + tid];
+        sdg[tid] -= s;
+    }
+    // dP o G and Gb = dA o G (row scaled by b) replace P and AS
+#pragma unroll
+    for (int m = 0; m < TC; ++m)
+#pragma unroll
+        for (int nn = 0; nn < TC; ++nn) {
+            const int i = ic + m, j = jc + nn;
+            const float G = j <= i ? __expf(sg[i] - sg[j]) : 0.f;
+            sP[i * PC + j] = adP[m][nn] * G;
+            sAS[i * PC + j] = adA[m][nn] * G * sb[i];
+        }
+    __syncthreads();
+    {
+        auto bkt = [&](int kk, int f) { return sKt[kk * PX + f]; };
+        mm<TC, TK, C>(aQ, ik, jk, [&](int i, int kk) { return sP[i * PC + kk]; }, bkt);
+        mm<TC, TK, C>(aK, ik, jk, [&](int i, int kk) { return sAS[i * PC + kk]; }, bkt);
+        mm<TC, TK, C>(aKt, ik, jk, [&](int i, int kk) { return sP[kk * PC + i]; },
+                      [&](int kk, int f) { return to_f32(sQ[kk * PQ + f]); });
+        mm<TC, TK, C>(aKt, ik, jk, [&](int i, int kk) { return sAS[kk * PC + i]; },
+                      [&](int kk, int f) { return to_f32(sK[kk * PQ + f]); });
+    }
+#pragma unroll
+    for (int m = 0; m < TC; ++m) {
+        const int r = ik + m;
+        if (r < n) {
+#pragma unroll
+            for (int nn = 0; nn < TK; ++nn) {
+                const int f = jk + nn;
+                const int64_t e = (row0 + r) * DK + f;
+                const float kv = to_f32(sK[r * PQ + f]);
+                gq[e] = from_f32<TQ>(aQ[m][nn]);
+                gk[e] = from_f32<TQ>(aK[m][nn] + aKt[m][nn] * to_f32(d[e]));
+                gd[e] = from_f32<TD>(aKt[m][nn] * kv);
+            }
+        }
+    }
+    __syncthreads();
+    if (tid == 0) {  // the last row's terms, then the reverse running sum of dg
+        float ews = 0.f;
+        for (int r = 0; r < n; ++r) ews += sew[r];
+        float acc = 0.f;
+        for (int r = n - 1; r >= 0; --r) {
+            float g = sdg[r] - sew[r];
+            if (r == n - 1) g += sgam[C - 1] * frob + ews;
+            acc += g;
+            sdg[r] = acc;  // d ln(alpha_r)
+        }
+    }
+    __syncthreads();
+    if (tid < n) {
+        gbeta[row0 + tid] = sdb[tid];
+        if (alpha && galpha) galpha[row0 + tid] = sdg[tid] / alpha[row0 + tid];
+    }
+}
+
+template <int C, int DK, int DV, typename TQ, typename TD>
+hipError_t bwd_typed(const BwdArgs &a, hipStream_t stream) {
+    const int64_t nch = (a.T + C - 1) / C;
+    // forward states at every chunk start (fp32 arithmetic)
+    if (nch > 0) {
+        ChunkArgs f{a.q, a.k, a.v, a.d, a.beta, a.alpha, a.S0, nullptr, nullptr, a.BH, a.T, DK,
+                    DV, C, a.qkv, a.d_dtype};
+        f.ckpt = a.Mck;
+        const hipError_t e = launch_chunk_fwd_f32math(f, stream);
+        if (e != hipSuccess) return e;
+    }
+    constexpr int BVA = 32;  // value slice of the reverse pass
+    hipLaunchKernelGGL((bwd_state_kernel<C, DK, BVA, TQ, TD>),
+                       dim3(static_cast<unsigned>(a.BH * (DV / BVA))), dim3(NT), 0, stream,
+                       static_cast<const TQ *>(a.q), static_cast<const TQ *>(a.k),
+                       static_cast<const TD *>(a.d), a.beta, a.alpha,
+                       static_cast<const TQ *>(a.dO), a.dS_T, a.dMck, a.dS0, a.T, DV);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || nch == 0) return e;
+    constexpr int BVB = C == 64 ? 16 : 32;  // value slice of the per-chunk pass
+    hipLaunchKernelGGL((bwd_chunk_kernel<C, DK, DV, BVB, TQ, TD>),
+                       dim3(static_cast<unsigned>(a.BH * nch)), dim3(NT), 0, stream,
+                       static_cast<const TQ *>(a.q), static_cast<const TQ *>(a.k),
+                       static_cast<const TQ *>(a.v), static_cast<const TD *>(a.d), a.beta,
+                       a.alpha, static_cast<const TQ *>(a.dO), a.Mck, a.dMck,
+                       static_cast<TQ *>(a.gq), static_cast<TQ *>(a.gk), static_cast<TQ *>(a.gv),
+                       a.gbeta, static_cast<TD *>(a.gd), a.galpha, a.T, nch);
+    return hipGetLastError();
+}
+
+// bf16 inputs use 64-row chunks, fp32 inputs 32-row chunks (their fp32 tiles take twice
+// the LDS)
+template <typename TQ, int DK, int DV>
+hipError_t bwd_dtypes(const BwdArgs &a, hipStream_t stream) {
+    constexpr int C = sizeof(TQ) == 2 ? 64 : 32;
+    return a.d_dtype == OSDN_F32 ? bwd_typed<C, DK, DV, TQ, float>(a, stream)
+                                 : bwd_typed<C, DK, DV, TQ, bf16_t>(a, stream);
+}
+
+template <typename TQ>
+hipError_t bwd_dims(const BwdArgs &a, hipStream_t stream) {
+    if (a.dk == 64) return a.dv == 64 ? bwd_dtypes<TQ, 64, 64>(a, stream) : bwd_dtypes<TQ, 64, 128>(a, stream);
+    return a.dv == 64 ? bwd_dtypes<TQ, 128, 64>(a, stream) : bwd_dtypes<TQ, 128, 128>(a, stream);
+}
+
+}  // namespace
+
+int32_t bwd_chunk_size(osdn_dtype qkv) { return qkv == OSDN_BF16 ? 64 : 32; }
+
+hipError_t launch_chunk_bwd(const BwdArgs &a, hipStream_t stream) {
+    return a.qkv == OSDN_BF16 ? bwd_dims<bf16_t>(a, stream) : bwd_dims<float>(a, stream);
+}
+
+}  // namespace osdn

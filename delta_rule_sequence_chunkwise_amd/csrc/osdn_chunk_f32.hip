@@ -15,6 +15,7 @@
 //   a6  O = diag(e^g) Q M + P U;  M <- e^{g_C} M + (diag(e^{g_C - g}) K~)^T U
 //
 // Rows past the end of the sequence are zero (beta = 0, alpha = 1), so they add nothing.
+// For the backward the kernel can also record the state at every chunk start (and skip o).
 // With the channel-wise gate the caller passes pre-scaled q, k, d and per-chunk factors G_C,
 // and the state's rows are multiplied by G_C after each carry.
 #include "osdn_internal.h"
@@ -30,7 +31,7 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
                      const TQ *__restrict__ v, const TD *__restrict__ d,
                      const float *__restrict__ beta, const float *__restrict__ alpha,
                      const float *S0, TQ *__restrict__ o, float *S_T, int64_t T, int dv,
-                     const float *__restrict__ gcs) {
+                     const float *__restrict__ gcs, float *__restrict__ ckpt) {
     constexpr int PX = DK + 1;  // padded row pitches (bank-conflict relief)
     constexpr int PC = CH + 1;
     constexpr int PV = BV + 1;
@@ -61,6 +62,13 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
         const int n = static_cast<int>(T - c0 < CH ? T - c0 : CH);
         const int64_t row0 = bh * T + c0;
         __syncthreads();  // the previous chunk is done with every buffer
+        if (ckpt) {  // the state at this chunk's start, for the backward
+            const int64_t cc = bh * ((T + CH - 1) / CH) + c0 / CH;
+            for (int idx = tid; idx < DK * BV; idx += kThreads) {
+                const int i = idx / BV, j = idx % BV;
+                ckpt[(cc * DK + i) * dv + j0 + j] = sM[i * PV + j];
+            }
+        }
 
         // a1: keys, scaled keys, values, gates
         for (int idx = tid; idx < CH * DK; idx += kThreads) {
@@ -171,7 +179,7 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
         // a6: outputs of this chunk and the state carried to the next one
         for (int idx = tid; idx < CH * BV; idx += kThreads) {
             const int r = idx / BV, j = idx % BV;
-            if (r < n) {
+            if (o && r < n) {
                 float acc = sgam[r] * sQM[r * PV + j];
                 for (int s = 0; s <= r; ++s) acc += sA[r * PC + s] * sU[s * PV + j];
                 o[(row0 + r) * dv + j0 + j] = from_f32<TQ>(acc);
@@ -205,7 +213,7 @@ hipError_t launch_typed(const ChunkArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL((chunk_f32math_kernel<DK, BV, CH, TQ, TD>), grid, dim3(kThreads), 0,
                        stream, static_cast<const TQ *>(a.q), static_cast<const TQ *>(a.k),
                        static_cast<const TQ *>(a.v), static_cast<const TD *>(a.d), a.beta,
-                       a.alpha, a.S0, static_cast<TQ *>(a.o), a.S_T, a.T, a.dv, a.gcs);
+                       a.alpha, a.S0, static_cast<TQ *>(a.o), a.S_T, a.T, a.dv, a.gcs, a.ckpt);
     return hipGetLastError();
 }
 

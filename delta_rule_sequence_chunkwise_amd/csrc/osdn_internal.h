@@ -42,6 +42,23 @@ struct ChunkArgs {
     osdn_dtype qkv, d_dtype;
     const float *gcs = nullptr;  // [BH, nchunks, dk]: per-feature factor applied to the
                                  // state's rows after each chunk's carry (channel-wise gate)
+    float *ckpt = nullptr;       // [BH, nchunks, dk, dv]: the state at every chunk start
+                                 // (fp32 path only; o may then be NULL)
+};
+
+struct BwdArgs {
+    const void *q, *k, *v, *d;
+    const float *beta, *alpha, *S0;
+    const void *dO;
+    const float *dS_T;
+    void *gq, *gk, *gv;   // qkv dtype
+    float *gbeta, *galpha;
+    void *gd;             // d dtype
+    float *dS0;
+    float *Mck, *dMck;    // workspace: [BH, nchunks, dk, dv] each
+    int64_t BH, T;
+    int32_t dk, dv;
+    osdn_dtype qkv, d_dtype;
 };
 
 struct KdaPrepArgs {
@@ -83,5 +100,7 @@ hipError_t launch_step(const StepArgs &a, hipStream_t stream);
 hipError_t launch_precond(const PrecondArgs &a, hipStream_t stream);
 hipError_t launch_kda_prep(const KdaPrepArgs &a, hipStream_t stream);
 hipError_t launch_step_kda(const StepArgs &a, hipStream_t stream);  // alpha: [BH, dk]
+hipError_t launch_chunk_bwd(const BwdArgs &a, hipStream_t stream);
+int32_t bwd_chunk_size(osdn_dtype qkv);  // rows per chunk of the backward
 
 }  // namespace osdn

@@ -26,6 +26,9 @@ The channel-wise (KDA) gate a_t [B,H,T,dk] of the KDA variant comes from a strea
 (seed + 104729): a = exp(-0.05 * softplus(N(0, 1))) per token, head and key feature, i.e. the
 scalar gate's recipe drawn per feature, rounded to float32.
 
+The backward's output gradients come from a stream of their own (seed + 15485863): do ~ N(0, 1)
+[B,H,T,dv] (rounded to the qkv type) and dS_T ~ N(0, 1) [B,H,dk,dv] (float32).
+
 The decode workload draws its initial state first (S0 ~ N(0, 0.02^2), float32, stored as
 M = S^T, i.e. ``[B, H, dk, dv]``), then the per-step tuples in the order above.
 """
@@ -193,3 +196,15 @@ def make_channel_gate(B: int, H: int, T: int, dk: int, seed: int) -> np.ndarray:
     """Channel-wise gate a [B,H,T,dk] (the scalar gate's recipe, one draw per key feature)."""
     rng = np.random.Generator(np.random.PCG64(seed + 104729))
     return round_f32(np.exp(-0.05 * np.logaddexp(0.0, rng.standard_normal((B, H, T, dk)))))
+
+
+def make_output_grads(B: int, H: int, T: int, dk: int, dv: int, *, qkv: str, seed: int,
+                      state: bool = True) -> Dict[str, Optional[np.ndarray]]:
+    """Output gradients for the backward: do [B,H,T,dv] ~ N(0,1) (rounded to the qkv type) and,
+    when ``state``, dS_T [B,H,dk,dv] ~ N(0,1) (fp32), from a stream of their own (seed + 15485863)."""
+    rng = np.random.Generator(np.random.PCG64(seed + 15485863))
+    do = round_f32(rng.standard_normal((B, H, T, dv)))
+    if qkv == "bf16":
+        do = round_bf16(do)
+    dS_T = round_f32(rng.standard_normal((B, H, dk, dv))) if state else None
+    return {"do": do, "dS_T": dS_T}

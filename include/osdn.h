@@ -187,6 +187,37 @@ osdn_status osdn_step_kda(const void *q, const void *k, const void *v, const flo
                           int64_t H, int32_t dk, int32_t dv, osdn_dtype qkv,
                           osdn_dtype d_dtype, void *stream);
 
+/*
+ * Gradients of the chunkwise forward (osdn_chunk_fwd with the same inputs) for a scalar loss
+ * whose gradients with respect to the outputs are grad_o [B,H,T,dv] (qkv dtype) and grad_S_T
+ * [B,H,dk,dv] fp32 (NULL: zero).  The pages give no backward pass; the gradients are those of
+ * the token step (OSDN technical summary, section 2.1; decay as in Erase-then-Delta Attention,
+ * section 2.2, eq. 4), computed in a chunk form derived from the forward's.
+ *
+ *   grad_q, grad_k [B,H,T,dk], grad_v [B,H,T,dv]   out, qkv dtype
+ *   grad_beta [B,H,T] fp32, grad_d [B,H,T,dk] d dtype   out
+ *   grad_alpha [B,H,T] fp32   out; ignored when alpha is NULL, may be NULL (not written)
+ *   grad_S0 [B,H,dk,dv] fp32  out, the gradient with respect to the initial state (whether or
+ *                             not S0 is given); NULL: not written
+ *   workspace                 caller-owned device memory of at least
+ *                             osdn_chunk_bwd_workspace(B, H, T, dk, dv, qkv) bytes, 256-byte
+ *                             aligned; contents on entry ignored, on return unspecified
+ * Every other argument as for osdn_chunk_fwd; the chunk size is the library's (64 rows for
+ * bf16 inputs, 32 for fp32).  Outputs must not overlap each other, an input or the workspace.
+ * Arithmetic is fp32.  Three kernels run on `stream`: the forward recording the state at every
+ * chunk start, a reverse pass over chunks for the state gradient, and the per-chunk gradients.
+ */
+int64_t osdn_chunk_bwd_workspace(int64_t B, int64_t H, int64_t T, int32_t dk, int32_t dv,
+                                 osdn_dtype qkv); /* -1 if invalid */
+
+osdn_status osdn_chunk_bwd(const void *q, const void *k, const void *v, const float *beta,
+                           const void *d, const float *alpha, const float *S0,
+                           const void *grad_o, const float *grad_S_T, void *grad_q,
+                           void *grad_k, void *grad_v, float *grad_beta, void *grad_d,
+                           float *grad_alpha, float *grad_S0, void *workspace,
+                           int64_t workspace_bytes, int64_t B, int64_t H, int64_t T, int32_t dk,
+                           int32_t dv, osdn_dtype qkv, osdn_dtype d_dtype, void *stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char *osdn_status_string(osdn_status s);
 

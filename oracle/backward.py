@@ -43,14 +43,13 @@ def forward_states(q, k, v, beta, d, alpha=None, S0=None):
     """The token recurrence above, keeping what the reverse pass needs.
 
     Returns dict with o [B,H,T,dv], S_T [B,H,dk,dv], and per token the state before the step
-    (Mprev [B,H,T,dk,dv]), the decayed state (Mh), y and u [B,H,T,dv]."""
+    (Mprev [B,H,T,dk,dv]), y and u [B,H,T,dv]; the decayed state is alpha_t Mprev_t."""
     q, k, v, beta, d, alpha, S0 = map(_f64, (q, k, v, beta, d, alpha, S0))
     B, H, T, dk = k.shape
     dv = v.shape[-1]
     M = np.zeros((B, H, dk, dv)) if S0 is None else S0.copy()
     o = np.empty((B, H, T, dv))
     Mprev = np.empty((B, H, T, dk, dv))
-    Mh_all = np.empty((B, H, T, dk, dv))
     ys = np.empty((B, H, T, dv))
     us = np.empty((B, H, T, dv))
     for t in range(T):
@@ -63,10 +62,9 @@ def forward_states(q, k, v, beta, d, alpha=None, S0=None):
         kw = d[:, :, t] * kt
         M = Mh + kw[..., :, None] * u[..., None, :]
         o[:, :, t] = np.einsum("bhkv,bhk->bhv", M, q[:, :, t])
-        Mh_all[:, :, t] = Mh
         ys[:, :, t] = y
         us[:, :, t] = u
-    return dict(o=o, S_T=M, Mprev=Mprev, Mh=Mh_all, y=ys, u=us)
+    return dict(o=o, S_T=M, Mprev=Mprev, y=ys, u=us)
 
 
 def chunk_bwd(q, k, v, beta, d, alpha=None, S0=None, do=None, dS_T=None) -> Dict[str, np.ndarray]:
@@ -89,7 +87,8 @@ def chunk_bwd(q, k, v, beta, d, alpha=None, S0=None, do=None, dS_T=None) -> Dict
     for t in range(T - 1, -1, -1):
         kt, qt, dot = k[:, :, t], q[:, :, t], do[:, :, t]
         kw = d[:, :, t] * kt
-        u, y, Mh = f["u"][:, :, t], f["y"][:, :, t], f["Mh"][:, :, t]
+        u, y = f["u"][:, :, t], f["y"][:, :, t]
+        Mh = f["Mprev"][:, :, t] * (1.0 if alpha is None else alpha[:, :, t, None, None])
         Mt = Mh + kw[..., :, None] * u[..., None, :]
         # read-out o_t = M_t^T q_t
         dM = dM + qt[..., :, None] * dot[..., None, :]

@@ -48,7 +48,8 @@ def _mutant(kind):
         for t in range(T - 1, -1, -1):
             kt, qt, dot = k[:, :, t], q[:, :, t], do[:, :, t]
             kw = d[:, :, t] * kt
-            u, y, Mh = f["u"][:, :, t], f["y"][:, :, t], f["Mh"][:, :, t]
+            u, y = f["u"][:, :, t], f["y"][:, :, t]
+            Mh = a[:, :, t, None, None] * f["Mprev"][:, :, t]
             Mt = Mh + kw[..., :, None] * u[..., None, :]
             dM = dM + qt[..., :, None] * dot[..., None, :]
             Mread = f["Mprev"][:, :, t] if kind == "readout_before_write" else Mt
