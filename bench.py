@@ -18,7 +18,11 @@ HBM.  Prints ONE JSON line.  Besides the contract fields it carries:
                 the host, and the forward with the scan in front (scan + chunkwise forward);
   kda           the forward with the channel-wise gate (osdn_chunk_fwd_kda: the gate-scaling
                 kernel, then the chunkwise forward) on the same workload with a per-feature
-                gate, with its HBM roofline and the parity of its output.
+                gate, with its HBM roofline and the parity of its output;
+  bwd           the backward (osdn_chunk_bwd: forward state checkpoints, the reverse pass over
+                chunks, the per-chunk gradients) on the same workload with seeded output
+                gradients, with its HBM roofline, its fp32 vector-ALU FLOP count, and the float64
+                reverse pass on one sampled sequence (parity and CPU baseline).
 """
 from __future__ import annotations
 
@@ -86,6 +90,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--precond-steps", type=int, default=20)
     ap.add_argument("--kda-steps", type=int, default=10)
+    ap.add_argument("--bwd-steps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="1.3b")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -215,7 +220,87 @@ def main():
         line["kda"] = bench_kda(args.kda_steps, torch, dev, synth, w, x, (q, k, v, beta, d, S0),
                                 not args.no_cpu_baseline)
 
+    if args.bwd_steps > 0:
+        line["bwd"] = bench_bwd(args.bwd_steps, torch, dev, synth, w, x,
+                                (q, k, v, beta, d, alpha, S0), not args.no_cpu_baseline)
+
     print(json.dumps(line), flush=True)
+
+
+def bwd_flops_per_head_token(dk, dv, C):
+    """fp32 FLOPs per head-token of the three backward launches, counting useful triangular
+    halves: the forward recompute (the forward's count), the reverse pass (K~ dM, Q^T dO,
+    K^T dR: 3 dk dv MACs; P^T dO and the solve: C dv; the Gram and P: C dk) and the per-chunk
+    pass (K M0, Q M0, K~ dMC and the three dk x dv gradient products: 6 dk dv; two solves,
+    P^T dO, dP and dA: 2.5 C dv; the Gram, P and the four C-contractions: 3 C dk)."""
+    fwd = flops_per_head_token(dk, dv, C)
+    rev = 2 * (3 * dk * dv + C * dv + C * dk)
+    per_chunk = 2 * (6 * dk * dv + 2.5 * C * dv + 3 * C * dk)
+    return fwd + rev + per_chunk
+
+
+def bench_bwd(n_steps, torch, dev, synth, w, x, fwd, cpu):
+    """Times `n_steps` osdn_chunk_bwd calls on the workload (output gradients seeded)."""
+    import numpy as np
+    from delta_rule_sequence_chunkwise_amd import osdn
+
+    B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
+    q, k, v, beta, d, alpha, S0 = fwd
+    gr = synth.make_output_grads(B, H, T, dk, dv, qkv=w.qkv, seed=w.seed, state=True)
+    do = torch.from_numpy(gr["do"]).to(dev).to(q.dtype)
+    dS_T = torch.from_numpy(gr["dS_T"]).to(dev)
+    ws = torch.empty(osdn.bwd_workspace_bytes(B, H, T, dk, dv, osdn.OSDN_BF16),
+                     dtype=torch.uint8, device=dev)
+    grads = osdn.osdn_chunk_bwd(q, k, v, beta, d, alpha, S0, do, dS_T, workspace=ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n_steps):
+        osdn.osdn_chunk_bwd(q, k, v, beta, d, alpha, S0, do, dS_T, grads=grads, workspace=ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    per = e0.elapsed_time(e1) / 1e3 / n_steps
+    head_tokens = B * H * T
+    eq = 2 if w.qkv == "bf16" else 4
+    # in: q, k, v, do (qkv type), d (fp32), beta, alpha; out: grad q, k, v (qkv type), grad d
+    # (fp32), grad beta, alpha; per sequence: S0 and dS_T in, grad S0 out (fp32)
+    alg = head_tokens * ((2 * dk + 2 * dv) * eq + dk * 4 + 8 + (2 * dk + dv) * eq + dk * 4 + 8) \
+        + B * H * dk * dv * 4 * 3
+    flops = head_tokens * bwd_flops_per_head_token(dk, dv, 64)
+    rec = {"workload": f"{w.name}-shape backward: B={B} H={H} T={T} dk={dk} dv={dv}, bf16 "
+                       "q/k/v/do and gradients of q/k/v, fp32 beta/d/alpha and their gradients, "
+                       "fp32 S0, dS_T and grad S0",
+           "ms_per_step": round(per * 1e3, 4),
+           "tokens_per_s": round(B * T / per, 1),
+           "roofline": {"bound": "hbm", "achieved": round(alg / per / 1e9, 2),
+                        "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                        "frac": round(alg / per / PEAK_HBM, 5), "alg_bytes_per_step": alg,
+                        "note": "three launches; the state checkpoints (2 x 268 MB written and "
+                                "read) are beyond alg"},
+           "alu": {"achieved": round(flops / per / 1e12, 3), "peak": 157.3, "unit": "TFLOP/s",
+                   "frac": round(flops / per / 157.3e12, 5), "flops_per_step": flops,
+                   "note": "fp32 vector arithmetic in this version"}}
+    if cpu:
+        from oracle import backward
+        b, h = 0, 0
+        sl = lambda a: None if a is None else np.ascontiguousarray(a[b:b + 1, h:h + 1])
+        c0 = time.perf_counter()
+        ref = backward.chunk_bwd(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["beta"]), sl(x["d"]),
+                                 sl(x["alpha"]), sl(x["S0"]), sl(gr["do"]), sl(gr["dS_T"]))
+        cpu_s = time.perf_counter() - c0
+        rel = lambda p, r: float(np.max(np.abs(p - r)) / np.max(np.abs(r)))
+        par = {}
+        for n, gn in (("dq", "grad_q"), ("dk", "grad_k"), ("dv", "grad_v"), ("dbeta", "grad_beta"),
+                      ("dd", "grad_d"), ("dalpha", "grad_alpha"), ("dS0", "grad_S0")):
+            par[n] = rel(grads[gn][b:b + 1, h:h + 1].float().cpu().numpy(), ref[n])
+        par["tol"] = 2e-2
+        rec["parity"] = par
+        rec["cpu_baseline"] = {"value": round(T / cpu_s, 1), "unit": "head-tokens/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"one (b,h) sequence of the workload ({T} tokens), "
+                                         f"float64 numpy reverse pass, {cpu_s:.2f} s wall"}
+    return rec
 
 
 def bench_kda(n_steps, torch, dev, synth, w, x, fwd, cpu):

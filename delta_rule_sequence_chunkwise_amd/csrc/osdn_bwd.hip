@@ -23,11 +23,11 @@
 //   d ln a_t = sum_{t <= r <= L} dg_r,   da = d ln a / a
 //   dd  = dK~ o K,   dK += dK~ o D
 //
-// Three launches on the caller's stream: (1) the fp32 forward records M0 of every chunk into
-// the workspace; (2) bwd_state_kernel walks the chunks backwards per (sequence, value slice)
+// Three launches on the caller's stream: (1) the forward (the bf16 matrix-core kernel for bf16
+// inputs, the fp32 one for fp32 inputs) records M0 of every chunk into the workspace; (2) bwd_state_kernel walks the chunks backwards per (sequence, value slice)
 // carrying dM, records dMC of every chunk and writes the initial-state gradient; (3)
 // bwd_chunk_kernel, one workgroup per (sequence, chunk), computes every gradient of the
-// chunk's rows from M0 and dMC.  Arithmetic is fp32 on the vector ALUs for both input types:
+// chunk's rows from M0 and dMC.  Arithmetic of (2) and (3) is fp32 on the vector ALUs:
 // tile products are register-blocked (each of the 256 threads owns one (M/16) x (N/16) block
 // of every M x N product), the triangular solves run column-parallel with the partial sums of
 // one column reduced across adjacent lanes.  Rows past the end of the sequence are zero
@@ -527,12 +527,14 @@ bwd_chunk_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k, const TQ *_
 template <int C, int DK, int DV, typename TQ, typename TD>
 hipError_t bwd_typed(const BwdArgs &a, hipStream_t stream) {
     const int64_t nch = (a.T + C - 1) / C;
-    // forward states at every chunk start (fp32 arithmetic)
+    // forward states at every chunk start (the matrix-core forward for bf16 inputs, the fp32
+    // one for fp32 inputs)
     if (nch > 0) {
         ChunkArgs f{a.q, a.k, a.v, a.d, a.beta, a.alpha, a.S0, nullptr, nullptr, a.BH, a.T, DK,
                     DV, C, a.qkv, a.d_dtype};
         f.ckpt = a.Mck;
-        const hipError_t e = launch_chunk_fwd_f32math(f, stream);
+        const hipError_t e = sizeof(TQ) == 2 ? launch_chunk_fwd_mfma(f, stream)
+                                             : launch_chunk_fwd_f32math(f, stream);
         if (e != hipSuccess) return e;
     }
     constexpr int BVA = 32;  // value slice of the reverse pass

@@ -34,7 +34,8 @@
 // * The loader wave (6) brings q and v of chunk c+2 into LDS and runs its decay scan.
 // With the channel-wise gate (the caller passes pre-scaled q, k, d and per-chunk factors G_C)
 // the state waves also multiply the state's rows by G_C after each carry; the loader brings
-// G_C into LDS with the other loads of its chunk.
+// G_C into LDS with the other loads of its chunk.  For the backward a variant records the state
+// at every chunk start instead of writing o.
 // Loads stall the issuing wave while HBM drains them, and too many in flight at once thrash
 // the CU's load queues; so they are issued in groups of at most 16 by waves whose other work
 // is light, and each state wave shares its SIMD with a stager.
@@ -255,13 +256,13 @@ __device__ __forceinline__ void diag_inverse2(Lds<DK, G> &sm, int b, int kb0, in
             pack4u(Y[j]);
 }
 
-template <int DK, typename TD, bool GATE>
+template <int DK, typename TD, bool GATE, bool CKPT>
 __global__ void __launch_bounds__(NW * 64)
 chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                   const uint16_t *__restrict__ v, const TD *__restrict__ d,
                   const float *__restrict__ beta, const float *__restrict__ alpha,
                   const float *S0, uint16_t *__restrict__ o, float *S_T, int64_t BH,
-                  int64_t T, int dv, const float *__restrict__ gcs) {
+                  int64_t T, int dv, const float *__restrict__ gcs, float *__restrict__ ckpt) {
     using L = Lds<DK, GATE>;
     constexpr int NS = DK / 32;   // 32-wide k-steps over the key features
     constexpr int NFT = DK / 16;  // 16-row feature tiles of the state
@@ -355,6 +356,13 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
         for (int64_t c = -2; c < nchunks; ++c) {
             if (c >= 0) {
                 // ---- chunk c: R, U, read-out, carry --------------------------------------------
+                if constexpr (CKPT) {  // the state at this chunk's start, for the backward
+                    float *dst = ckpt + (bh * nchunks + c) * DK * dv + j0 + VW * ct + lr;
+#pragma unroll
+                    for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) dst[(16 * ft + 4 * lq + i) * dv] = M[ft][i];
+                }
                 const int b = static_cast<int>(c & 1);
                 const int n = rows_of(c);
                 const int64_t row0 = seq0 + c * CH;
@@ -427,7 +435,7 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                 const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
                     o + row0 * dv, 0, n * dv * 2, 0x00020000);
 #pragma unroll
-                for (int rt = 0; rt < NBLK; ++rt) {
+                for (int rt = 0; rt < NBLK && !CKPT; ++rt) {
                     v4f a = oacc[rt];
                     if (rt >= 2) a = mfma32(ub1, pf[rt][1], a);
                     const uint2 pk = pack4u(a);
@@ -689,14 +697,15 @@ template <int DK, typename TD>
 hipError_t launch_typed(const ChunkArgs &a, hipStream_t stream) {
     const int nvt = a.dv / BV;
     const dim3 grid(static_cast<unsigned>(a.BH * nvt));
-#define OSDN_CHUNK_LAUNCH(GATE)                                                               \
-    hipLaunchKernelGGL((chunk_mfma_kernel<DK, TD, GATE>), grid, dim3(NW * 64), 0, stream,     \
-                       static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k), \
-                       static_cast<const uint16_t *>(a.v), static_cast<const TD *>(a.d),       \
-                       a.beta, a.alpha, a.S0, static_cast<uint16_t *>(a.o), a.S_T, a.BH, a.T,  \
-                       a.dv, a.gcs)
-    if (a.gcs) OSDN_CHUNK_LAUNCH(true);
-    else OSDN_CHUNK_LAUNCH(false);
+#define OSDN_CHUNK_LAUNCH(GATE, CKPT)                                                         \
+    hipLaunchKernelGGL((chunk_mfma_kernel<DK, TD, GATE, CKPT>), grid, dim3(NW * 64), 0,       \
+                       stream, static_cast<const uint16_t *>(a.q),                             \
+                       static_cast<const uint16_t *>(a.k), static_cast<const uint16_t *>(a.v), \
+                       static_cast<const TD *>(a.d), a.beta, a.alpha, a.S0,                    \
+                       static_cast<uint16_t *>(a.o), a.S_T, a.BH, a.T, a.dv, a.gcs, a.ckpt)
+    if (a.gcs) OSDN_CHUNK_LAUNCH(true, false);
+    else if (a.ckpt) OSDN_CHUNK_LAUNCH(false, true);
+    else OSDN_CHUNK_LAUNCH(false, false);
 #undef OSDN_CHUNK_LAUNCH
     return hipGetLastError();
 }

@@ -43,7 +43,7 @@ struct ChunkArgs {
     const float *gcs = nullptr;  // [BH, nchunks, dk]: per-feature factor applied to the
                                  // state's rows after each chunk's carry (channel-wise gate)
     float *ckpt = nullptr;       // [BH, nchunks, dk, dv]: the state at every chunk start
-                                 // (fp32 path only; o may then be NULL)
+                                 // (then o is not written and may be NULL; no channel gate)
 };
 
 struct BwdArgs {

@@ -204,8 +204,9 @@ osdn_status osdn_step_kda(const void *q, const void *k, const void *v, const flo
  *                             aligned; contents on entry ignored, on return unspecified
  * Every other argument as for osdn_chunk_fwd; the chunk size is the library's (64 rows for
  * bf16 inputs, 32 for fp32).  Outputs must not overlap each other, an input or the workspace.
- * Arithmetic is fp32.  Three kernels run on `stream`: the forward recording the state at every
- * chunk start, a reverse pass over chunks for the state gradient, and the per-chunk gradients.
+ * Three kernels run on `stream`: the forward recording the state at every chunk start (the same
+ * forward osdn_chunk_fwd runs for this input type), a reverse pass over chunks for the state
+ * gradient, and the per-chunk gradients.
  */
 int64_t osdn_chunk_bwd_workspace(int64_t B, int64_t H, int64_t T, int32_t dk, int32_t dv,
                                  osdn_dtype qkv); /* -1 if invalid */
