@@ -33,6 +33,7 @@
 // one column reduced across adjacent lanes.  Rows past the end of the sequence are zero
 // (beta = 0, alpha = 1, dO = 0), so they add nothing.
 #include "osdn_internal.h"
+#include "osdn_mfma.h"
 
 namespace osdn {
 namespace {
@@ -524,6 +525,348 @@ bwd_chunk_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k, const TQ *_
     }
 }
 
+// ---- per-chunk gradients on bf16 matrix cores (bf16 inputs, C = 64) ---------------------------
+// Same data flow as bwd_chunk_kernel.  Wave w owns rows 16w..16w+15 of every product, as 16x16
+// fp32 tiles in the MFMA C layout (lane (q, n) holds rows 4q..4q+3 of column n); operand
+// fragments are gathered from the fp32/bf16 LDS tiles through the same accessors and rounded
+// to bf16 (K steps of 32, or 16 for the value-slice contractions).  The triangular solves and
+// every row or column sum stay fp32.
+
+// tile += sum_{kk < K} a(i0 + row, kk) b(kk, j0 + col) on one 16x16 output tile
+template <int K, typename FA, typename FB>
+__device__ __forceinline__ v4f mtile(v4f acc, int i0, int j0, int lr, int lq, FA &&a, FB &&b) {
+    static_assert(K % 32 == 0 || K == 16, "K steps of 32 or one of 16");
+    if constexpr (K == 16) {
+        const int kb = 4 * lq;
+        const v4s af = __builtin_bit_cast(
+            v4s, make_uint2(pack2(a(i0 + lr, kb), a(i0 + lr, kb + 1)),
+                            pack2(a(i0 + lr, kb + 2), a(i0 + lr, kb + 3))));
+        const v4s bf = __builtin_bit_cast(
+            v4s, make_uint2(pack2(b(kb, j0 + lr), b(kb + 1, j0 + lr)),
+                            pack2(b(kb + 2, j0 + lr), b(kb + 3, j0 + lr))));
+        return mfma16(af, bf, acc);
+    } else {
+#pragma unroll
+        for (int k0 = 0; k0 < K; k0 += 32) {
+            const int kb = k0 + 8 * lq;
+            uint32_t au[4], bu[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                au[e] = pack2(a(i0 + lr, kb + 2 * e), a(i0 + lr, kb + 2 * e + 1));
+                bu[e] = pack2(b(kb + 2 * e, j0 + lr), b(kb + 2 * e + 1, j0 + lr));
+            }
+            acc = mfma32(__builtin_bit_cast(v8s, make_uint4(au[0], au[1], au[2], au[3])),
+                         __builtin_bit_cast(v8s, make_uint4(bu[0], bu[1], bu[2], bu[3])), acc);
+        }
+        return acc;
+    }
+}
+
+template <int DK, int DV, int BV, typename TD>
+__global__ void __launch_bounds__(NT)
+bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
+                      const bf16_t *__restrict__ v, const TD *__restrict__ d,
+                      const float *__restrict__ beta, const float *__restrict__ alpha,
+                      const bf16_t *__restrict__ dO, const float *__restrict__ Mck,
+                      const float *__restrict__ dMck, bf16_t *__restrict__ gq,
+                      bf16_t *__restrict__ gk, bf16_t *__restrict__ gv,
+                      float *__restrict__ gbeta, TD *__restrict__ gd,
+                      float *__restrict__ galpha, int64_t T, int64_t nch) {
+    constexpr int C = 64;
+    constexpr int PQ = DK + 2, PX = DK + 1, PC = C + 1, PS = BV + 1;
+    constexpr int NF = DK / 16, NV = BV / 16;  // column tiles of C x DK and C x BV products
+    constexpr int TC = C / 16, TV = BV / 16;  // register blocks of the fp32 C x BV products
+    __shared__ bf16_t sQ[C * PQ], sK[C * PQ];
+    __shared__ float sKt[C * PX], sAS[C * PC], sP[C * PC], sT[C * PC];
+    __shared__ float sM0[DK * PS], sdM[DK * PS];
+    __shared__ float sY[C * PS], sdO[C * PS], sU[C * PS], sR[C * PS], sdU[C * PS];
+    __shared__ float sb[C], sg[C], sgam[C], sw[C], sdb[C], sdg[C], sew[C], sred[4];
+
+    const int64_t bh = blockIdx.x / nch, c = blockIdx.x % nch;
+    const int64_t c0 = c * C, row0 = bh * T + c0;
+    const int n = static_cast<int>(T - c0 < C ? T - c0 : C);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 15, lq = lane >> 4;
+    const int R0 = 16 * wave;  // this wave's rows
+    const float *M0 = Mck + (bh * nch + c) * DK * DV;
+    const float *dMC = dMck + (bh * nch + c) * DK * DV;
+
+    load_qk<C, DK, PQ, PX>(q, k, d, row0, n, sQ, sK, sKt, tid);
+    if (tid < 64) decay_scan<C>(beta, alpha, row0, n, sb, sg, sgam, sw, lane);
+    if (tid < C) sdb[tid] = sdg[tid] = sew[tid] = 0.f;
+    __syncthreads();
+    // AS = strictly lower (K K~^T) o G, P = lower-inclusive (Q K~^T) o G
+    {
+        auto bkt = [&](int kk, int j) { return sKt[j * PX + kk]; };
+#pragma unroll
+        for (int t = 0; t < C / 16; ++t) {
+            v4f ak = zero4(), aq = zero4();
+            if (t <= wave) {
+                ak = mtile<DK>(ak, R0, 16 * t, lr, lq,
+                               [&](int i, int kk) { return to_f32(sK[i * PQ + kk]); }, bkt);
+                aq = mtile<DK>(aq, R0, 16 * t, lr, lq,
+                               [&](int i, int kk) { return to_f32(sQ[i * PQ + kk]); }, bkt);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = R0 + 4 * lq + e, j = 16 * t + lr;
+                const float G = j <= i ? __expf(sg[i] - sg[j]) : 0.f;
+                sAS[i * PC + j] = j < i ? ak[e] * G : 0.f;
+                sP[i * PC + j] = aq[e] * G;
+            }
+        }
+    }
+
+    // T = (I + A)^{-1} once per chunk (fp32): the slices then need two products, not solves
+    for (int idx = tid; idx < C * C; idx += NT) sT[(idx / C) * PC + idx % C] = idx / C == idx % C;
+    __syncthreads();
+    solve_lower<C, C, PC, PC>(sT, sAS, sb, tid);
+
+    v4f aQ[NF], aK[NF], aKt[NF], adP[C / 16], adA[C / 16];
+#pragma unroll
+    for (int t = 0; t < NF; ++t) aQ[t] = aK[t] = aKt[t] = zero4();
+#pragma unroll
+    for (int t = 0; t < C / 16; ++t) adP[t] = adA[t] = zero4();
+    float frob = 0.f;
+
+    for (int s0 = 0; s0 < DV; s0 += BV) {
+        __syncthreads();  // the previous slice (and the scores) are done
+        for (int idx = tid; idx < DK * BV; idx += NT) {
+            const int f = idx / BV, j = idx % BV;
+            const float m0 = M0[f * DV + s0 + j], dm = dMC[f * DV + s0 + j];
+            sM0[f * PS + j] = m0;
+            sdM[f * PS + j] = dm;
+            frob += m0 * dm;
+        }
+        for (int idx = tid; idx < C * BV; idx += NT) {
+            const int r = idx / BV, j = idx % BV;
+            sY[r * PS + j] = r < n ? to_f32(v[(row0 + r) * DV + s0 + j]) : 0.f;
+            sdO[r * PS + j] = r < n ? to_f32(dO[(row0 + r) * DV + s0 + j]) : 0.f;
+        }
+        __syncthreads();
+        // K M0, Q M0, K~ dMC on this slice, kept in registers (this wave's rows); Y = V - gam
+        // K M0 and R = b Y into LDS; the read-out row sums <dO_r, (Q M0)_r>
+        v4f km[NV], kdm[NV];
+        float go[4] = {0.f, 0.f, 0.f, 0.f};
+        {
+            auto bm = [&](int kk, int j) { return sM0[kk * PS + j]; };
+#pragma unroll
+            for (int t = 0; t < NV; ++t) {
+                km[t] = mtile<DK>(zero4(), R0, 16 * t, lr, lq,
+                                  [&](int i, int kk) { return to_f32(sK[i * PQ + kk]); }, bm);
+                const v4f qm = mtile<DK>(zero4(), R0, 16 * t, lr, lq,
+                                         [&](int i, int kk) { return to_f32(sQ[i * PQ + kk]); }, bm);
+                kdm[t] = mtile<DK>(zero4(), R0, 16 * t, lr, lq,
+                                   [&](int i, int kk) { return sKt[i * PX + kk]; },
+                                   [&](int kk, int j) { return sdM[kk * PS + j]; });
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = R0 + 4 * lq + e, j = 16 * t + lr;
+                    go[e] += sdO[r * PS + j] * qm[e];
+                    const float y = sY[r * PS + j] - sgam[r] * km[t][e];
+                    sY[r * PS + j] = y;
+                    sR[r * PS + j] = sb[r] * y;
+                }
+            }
+        }
+        __syncthreads();
+        {  // U = T R (fp32); dU = P^T dO + diag(w) K~ dMC
+            float acc[TC][TV];
+            zero(acc);
+            const int i0 = (tid / 16) * TC, j0 = (tid % 16) * TV;
+            mm<TC, TV, C>(acc, i0, j0, [&](int i, int kk) { return sT[i * PC + kk]; },
+                          [&](int kk, int j) { return sR[kk * PS + j]; });
+#pragma unroll
+            for (int m = 0; m < TC; ++m)
+#pragma unroll
+                for (int nn = 0; nn < TV; ++nn) sU[(i0 + m) * PS + j0 + nn] = acc[m][nn];
+#pragma unroll
+            for (int t = 0; t < NV; ++t) {
+                const v4f du = mtile<C>(zero4(), R0, 16 * t, lr, lq,
+                                        [&](int i, int kk) { return sP[kk * PC + i]; },
+                                        [&](int kk, int j) { return sdO[kk * PS + j]; });
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = R0 + 4 * lq + e, j = 16 * t + lr;
+                    sdU[r * PS + j] = du[e] + sw[r] * kdm[t][e];
+                }
+            }
+        }
+        __syncthreads();
+        {  // dR = T^T dU (fp32), into sR
+            float acc[TC][TV];
+            zero(acc);
+            const int i0 = (tid / 16) * TC, j0 = (tid % 16) * TV;
+            mm<TC, TV, C>(acc, i0, j0, [&](int i, int kk) { return sT[kk * PC + i]; },
+                          [&](int kk, int j) { return sdU[kk * PS + j]; });
+#pragma unroll
+            for (int m = 0; m < TC; ++m)
+#pragma unroll
+                for (int nn = 0; nn < TV; ++nn) sR[(i0 + m) * PS + j0 + nn] = acc[m][nn];
+        }
+        __syncthreads();
+        float *const sdR = sR;
+        for (int idx = tid; idx < C * BV; idx += NT) {
+            const int r = idx / BV, j = idx % BV;
+            if (r < n) gv[(row0 + r) * DV + s0 + j] = from_f32<bf16_t>(sb[r] * sdR[r * PS + j]);
+        }
+        {  // row sums of this slice: <dR_r, Y_r>, <dR_r, (K M0)_r>, <(K~ dMC)_r, U_r>
+            float gr[4] = {0.f, 0.f, 0.f, 0.f}, ew[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < NV; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = R0 + 4 * lq + e, j = 16 * t + lr;
+                    gr[e] += sdR[r * PS + j] * km[t][e];
+                    ew[e] += kdm[t][e] * sU[r * PS + j];
+                }
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int m = 1; m < 16; m <<= 1) {
+                    go[e] += __shfl_xor(go[e], m);
+                    gr[e] += __shfl_xor(gr[e], m);
+                    ew[e] += __shfl_xor(ew[e], m);
+                }
+            if (lr == 0) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = R0 + 4 * lq + e;
+                    sdg[r] += sgam[r] * go[e] - sb[r] * sgam[r] * gr[e];
+                    sew[r] += sw[r] * ew[e];
+                }
+            }
+            if (tid < C) {
+                const int r = tid;
+                float db = 0.f;
+                for (int j = 0; j < BV; ++j) db += sdR[r * PS + j] * sY[r * PS + j];
+                sdb[r] += db;
+            }
+        }
+        // dP += dO U^T, dA += dR U^T (negated later), and the slice's part of dQ, dK, dK~
+        auto bu = [&](int kk, int j) { return sU[j * PS + kk]; };
+#pragma unroll
+        for (int t = 0; t < C / 16; ++t) {
+            if (t <= wave) {
+                adP[t] = mtile<BV>(adP[t], R0, 16 * t, lr, lq,
+                                   [&](int i, int kk) { return sdO[i * PS + kk]; }, bu);
+                adA[t] = mtile<BV>(adA[t], R0, 16 * t, lr, lq,
+                                   [&](int i, int kk) { return sdR[i * PS + kk]; }, bu);
+            }
+        }
+        auto bm0t = [&](int kk, int f) { return sM0[f * PS + kk]; };
+#pragma unroll
+        for (int t = 0; t < NF; ++t) {
+            aQ[t] = mtile<BV>(aQ[t], R0, 16 * t, lr, lq,
+                              [&](int i, int kk) { return sgam[i] * sdO[i * PS + kk]; }, bm0t);
+            aK[t] = mtile<BV>(aK[t], R0, 16 * t, lr, lq,
+                              [&](int i, int kk) { return -sgam[i] * sb[i] * sdR[i * PS + kk]; },
+                              bm0t);
+            aKt[t] = mtile<BV>(aKt[t], R0, 16 * t, lr, lq,
+                               [&](int i, int kk) { return sw[i] * sU[i * PS + kk]; },
+                               [&](int kk, int f) { return sdM[f * PS + kk]; });
+        }
+    }
+    frob = block_sum(frob, sred, tid);  // ends with a barrier: the slices are done
+
+    // masks, the decay terms (row sums inside the wave, column sums through LDS) and the
+    // dbeta term of A
+    float *colpart = sM0;  // [4][C]
+    {
+        float rowp[4], rowb[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rowp[e] = rowb[e] = 0.f;
+#pragma unroll
+        for (int t = 0; t < C / 16; ++t) {
+            float colp = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = R0 + 4 * lq + e, j = 16 * t + lr;
+                const float dp = j <= i ? adP[t][e] : 0.f;
+                const float da = j < i ? -adA[t][e] : 0.f;
+                adP[t][e] = dp;
+                adA[t][e] = da;
+                const float ex = dp * sP[i * PC + j] + da * sb[i] * sAS[i * PC + j];
+                rowp[e] += ex;
+                colp += ex;
+                rowb[e] += da * sAS[i * PC + j];
+            }
+            colp += __shfl_xor(colp, 16);
+            colp += __shfl_xor(colp, 32);
+            if (lq == 0) colpart[wave * C + 16 * t + lr] = colp;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+#pragma unroll
+            for (int m = 1; m < 16; m <<= 1) {
+                rowp[e] += __shfl_xor(rowp[e], m);
+                rowb[e] += __shfl_xor(rowb[e], m);
+            }
+        }
+        if (lr == 0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sdg[R0 + 4 * lq + e] += rowp[e];
+                sdb[R0 + 4 * lq + e] += rowb[e];
+            }
+        }
+    }
+    __syncthreads();
+    if (tid < C) sdg[tid] -= colpart[tid] + colpart[C + tid] + colpart[2 * C + tid] + colpart[3 * C + tid];
+    // dP o G and Gb = dA o G (row scaled by b) replace P and AS
+#pragma unroll
+    for (int t = 0; t < C / 16; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = R0 + 4 * lq + e, j = 16 * t + lr;
+            const float G = j <= i ? __expf(sg[i] - sg[j]) : 0.f;
+            sP[i * PC + j] = adP[t][e] * G;
+            sAS[i * PC + j] = adA[t][e] * G * sb[i];
+        }
+    __syncthreads();
+    {
+        auto bkt = [&](int kk, int f) { return sKt[kk * PX + f]; };
+#pragma unroll
+        for (int t = 0; t < NF; ++t) {
+            aQ[t] = mtile<C>(aQ[t], R0, 16 * t, lr, lq, [&](int i, int kk) { return sP[i * PC + kk]; }, bkt);
+            aK[t] = mtile<C>(aK[t], R0, 16 * t, lr, lq, [&](int i, int kk) { return sAS[i * PC + kk]; }, bkt);
+            aKt[t] = mtile<C>(aKt[t], R0, 16 * t, lr, lq, [&](int i, int kk) { return sP[kk * PC + i]; },
+                              [&](int kk, int f) { return to_f32(sQ[kk * PQ + f]); });
+            aKt[t] = mtile<C>(aKt[t], R0, 16 * t, lr, lq, [&](int i, int kk) { return sAS[kk * PC + i]; },
+                              [&](int kk, int f) { return to_f32(sK[kk * PQ + f]); });
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NF; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = R0 + 4 * lq + e, f = 16 * t + lr;
+            if (r < n) {
+                const int64_t ix = (row0 + r) * DK + f;
+                gq[ix] = from_f32<bf16_t>(aQ[t][e]);
+                gk[ix] = from_f32<bf16_t>(aK[t][e] + aKt[t][e] * to_f32(d[ix]));
+                gd[ix] = from_f32<TD>(aKt[t][e] * to_f32(sK[r * PQ + f]));
+            }
+        }
+    __syncthreads();
+    if (tid == 0) {  // the last row's terms, then the reverse running sum of dg
+        float ews = 0.f;
+        for (int r = 0; r < n; ++r) ews += sew[r];
+        float acc = 0.f;
+        for (int r = n - 1; r >= 0; --r) {
+            float g = sdg[r] - sew[r];
+            if (r == n - 1) g += sgam[C - 1] * frob + ews;
+            acc += g;
+            sdg[r] = acc;  // d ln(alpha_r)
+        }
+    }
+    __syncthreads();
+    if (tid < n) {
+        gbeta[row0 + tid] = sdb[tid];
+        if (alpha && galpha) galpha[row0 + tid] = sdg[tid] / alpha[row0 + tid];
+    }
+}
+
 template <int C, int DK, int DV, typename TQ, typename TD>
 hipError_t bwd_typed(const BwdArgs &a, hipStream_t stream) {
     const int64_t nch = (a.T + C - 1) / C;
@@ -546,6 +889,17 @@ hipError_t bwd_typed(const BwdArgs &a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || nch == 0) return e;
     constexpr int BVB = C == 64 ? 16 : 32;  // value slice of the per-chunk pass
+    if constexpr (sizeof(TQ) == 2) {
+        hipLaunchKernelGGL((bwd_chunk_mfma_kernel<DK, DV, BVB, TD>),
+                           dim3(static_cast<unsigned>(a.BH * nch)), dim3(NT), 0, stream,
+                           static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.k),
+                           static_cast<const bf16_t *>(a.v), static_cast<const TD *>(a.d),
+                           a.beta, a.alpha, static_cast<const bf16_t *>(a.dO), a.Mck, a.dMck,
+                           static_cast<bf16_t *>(a.gq), static_cast<bf16_t *>(a.gk),
+                           static_cast<bf16_t *>(a.gv), a.gbeta, static_cast<TD *>(a.gd),
+                           a.galpha, a.T, nch);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL((bwd_chunk_kernel<C, DK, DV, BVB, TQ, TD>),
                        dim3(static_cast<unsigned>(a.BH * nch)), dim3(NT), 0, stream,
                        static_cast<const TQ *>(a.q), static_cast<const TQ *>(a.k),
