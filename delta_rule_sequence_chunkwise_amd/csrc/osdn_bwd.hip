@@ -867,6 +867,168 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
     }
 }
 
+// ---- reverse pass over chunks on bf16 matrix cores (bf16 inputs, C = 64) --------------------
+// Same data flow as bwd_state_kernel.  The score tiles, K~ dM, P^T dO and the dM update run on
+// 16x16 MFMA tiles (wave w owns rows 16w..16w+15 of the C-row products and rows 32w..32w+31
+// of dM); dR = (I + A)^{-T} dU is solved by 16-row blocks from the blocks' own inverses
+// D_i = (I + A_ii)^{-1} (fp32), four short steps instead of a 64-row chain.  dM stays fp32.
+template <int DK, int BV, typename TD>
+__global__ void __launch_bounds__(NT)
+bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
+                      const TD *__restrict__ d, const float *__restrict__ beta,
+                      const float *__restrict__ alpha, const bf16_t *__restrict__ dO,
+                      const float *__restrict__ dS_T, float *__restrict__ dMck,
+                      float *__restrict__ dS0, int64_t T, int dv) {
+    constexpr int C = 64;
+    constexpr int PQ = DK + 2, PX = DK + 1, PC = C + 1, PS = BV + 1, PD = 17;
+    constexpr int NV = BV / 16;           // column tiles of the C x BV products
+    constexpr int MR = DK / 64;           // 16-row tiles of dM per wave
+    __shared__ bf16_t sQ[C * PQ], sK[C * PQ];
+    __shared__ float sKt[C * PX], sAS[C * PC], sP[C * PC];
+    __shared__ float sdO[C * PS], sX[C * PS], sY16[16 * PS], sdM[DK * PS];
+    __shared__ float sD[4 * 16 * PD];     // D_i, block i at rows 16 i
+    __shared__ float sb[C], sg[C], sgam[C], sw[C];
+
+    const int nvt = dv / BV;
+    const int64_t bh = blockIdx.x / nvt;
+    const int j0 = static_cast<int>(blockIdx.x % nvt) * BV;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 15, lq = lane >> 4;
+    const int R0 = 16 * wave;
+    const int64_t nch = (T + C - 1) / C;
+
+    for (int idx = tid; idx < DK * BV; idx += NT) {
+        const int f = idx / BV, j = idx % BV;
+        sdM[f * PS + j] = dS_T ? dS_T[(bh * DK + f) * dv + j0 + j] : 0.f;
+    }
+    for (int64_t c = nch - 1; c >= 0; --c) {
+        const int64_t c0 = c * C, row0 = bh * T + c0;
+        const int n = static_cast<int>(T - c0 < C ? T - c0 : C);
+        __syncthreads();  // the previous chunk is done with every buffer
+        load_qk<C, DK, PQ, PX>(q, k, d, row0, n, sQ, sK, sKt, tid);
+        for (int idx = tid; idx < C * BV; idx += NT) {
+            const int r = idx / BV, j = idx % BV;
+            sdO[r * PS + j] = r < n ? to_f32(dO[(row0 + r) * dv + j0 + j]) : 0.f;
+        }
+        if (tid < 64) decay_scan<C>(beta, alpha, row0, n, sb, sg, sgam, sw, lane);
+        for (int idx = tid; idx < DK * BV; idx += NT) {  // gradient at this chunk's end
+            const int f = idx / BV, j = idx % BV;
+            dMck[((bh * nch + c) * DK + f) * dv + j0 + j] = sdM[f * PS + j];
+        }
+        __syncthreads();
+        // scores of this wave's rows; K~ dM of this wave's rows (registers)
+        v4f kdm[NV];
+        {
+            auto bkt = [&](int kk, int j) { return sKt[j * PX + kk]; };
+#pragma unroll
+            for (int t = 0; t < C / 16; ++t) {
+                v4f ak = zero4(), aq = zero4();
+                if (t <= wave) {
+                    ak = mtile<DK>(ak, R0, 16 * t, lr, lq,
+                                   [&](int i, int kk) { return to_f32(sK[i * PQ + kk]); }, bkt);
+                    aq = mtile<DK>(aq, R0, 16 * t, lr, lq,
+                                   [&](int i, int kk) { return to_f32(sQ[i * PQ + kk]); }, bkt);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = R0 + 4 * lq + e, j = 16 * t + lr;
+                    const float G = j <= i ? __expf(sg[i] - sg[j]) : 0.f;
+                    sAS[i * PC + j] = j < i ? ak[e] * G : 0.f;
+                    sP[i * PC + j] = aq[e] * G;
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < NV; ++t)
+                kdm[t] = mtile<DK>(zero4(), R0, 16 * t, lr, lq,
+                                   [&](int i, int kk) { return sKt[i * PX + kk]; },
+                                   [&](int kk, int j) { return sdM[kk * PS + j]; });
+        }
+        __syncthreads();
+        // dU = P^T dO + diag(w) K~ dM into sX; the diagonal blocks' inverses D_i into sD
+#pragma unroll
+        for (int t = 0; t < NV; ++t) {
+            const v4f du = mtile<C>(zero4(), R0, 16 * t, lr, lq,
+                                    [&](int i, int kk) { return sP[kk * PC + i]; },
+                                    [&](int kk, int j) { return sdO[kk * PS + j]; });
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = R0 + 4 * lq + e, j = 16 * t + lr;
+                sX[r * PS + j] = du[e] + sw[r] * kdm[t][e];
+            }
+        }
+        {  // column jj of D_blk by forward substitution, four adjacent lanes per column
+            const int blk = tid >> 6, jj = (tid >> 2) & 15, sub = tid & 3, rb = 16 * blk;
+            float mine[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float part = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (4 * i < r) {
+                        const int s2 = 4 * i + sub;
+                        if (s2 < r) part += sAS[(rb + r) * PC + rb + s2] * mine[i];
+                    }
+                }
+                part += __shfl_xor(part, 1);
+                part += __shfl_xor(part, 2);
+                const float val = (r == jj ? 1.f : 0.f) - sb[rb + r] * part;
+                if (r % 4 == sub) mine[r / 4] = val;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sD[(rb + 4 * i + sub) * PD + jj] = mine[i];
+        }
+        __syncthreads();
+        // dR = (I + A)^{-T} dU by blocks i = 3..0: y = dU_i - sum_{k>i} A_ki^T dR_k, then
+        // dR_i = D_i^T y (in place in sX)
+        for (int ib = 3; ib >= 0; --ib) {
+            for (int idx = tid; idx < 16 * BV; idx += NT) {
+                const int r = idx / BV, j = idx % BV, ri = 16 * ib + r;
+                float y = sX[ri * PS + j];
+                for (int s2 = 16 * (ib + 1); s2 < C; ++s2)
+                    y -= sb[s2] * sAS[s2 * PC + ri] * sX[s2 * PS + j];
+                sY16[r * PS + j] = y;
+            }
+            __syncthreads();
+            for (int idx = tid; idx < 16 * BV; idx += NT) {
+                const int r = idx / BV, j = idx % BV;
+                float acc = 0.f;
+                for (int r2 = r; r2 < 16; ++r2) acc += sD[(16 * ib + r2) * PD + r] * sY16[r2 * PS + j];
+                sX[(16 * ib + r) * PS + j] = acc;
+            }
+            __syncthreads();
+        }
+        // dM <- gam_L dM + Q^T diag(gam) dO - K^T diag(gam b) dR (this wave's 32 rows of dM)
+        {
+            const float gl = sgam[C - 1];
+#pragma unroll
+            for (int mt = 0; mt < MR; ++mt) {
+                const int f0 = 16 * (MR * wave + mt);
+#pragma unroll
+                for (int t = 0; t < NV; ++t) {
+                    v4f acc = mtile<C>(zero4(), f0, 16 * t, lr, lq,
+                                       [&](int f, int r) { return to_f32(sQ[r * PQ + f]); },
+                                       [&](int r, int j) { return sgam[r] * sdO[r * PS + j]; });
+                    acc = mtile<C>(acc, f0, 16 * t, lr, lq,
+                                   [&](int f, int r) { return to_f32(sK[r * PQ + f]); },
+                                   [&](int r, int j) { return -sgam[r] * sb[r] * sX[r * PS + j]; });
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float &x = sdM[(f0 + 4 * lq + e) * PS + 16 * t + lr];
+                        x = gl * x + acc[e];
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+    if (dS0) {
+        for (int idx = tid; idx < DK * BV; idx += NT) {
+            const int f = idx / BV, j = idx % BV;
+            dS0[(bh * DK + f) * dv + j0 + j] = sdM[f * PS + j];
+        }
+    }
+}
+
 template <int C, int DK, int DV, typename TQ, typename TD>
 hipError_t bwd_typed(const BwdArgs &a, hipStream_t stream) {
     const int64_t nch = (a.T + C - 1) / C;
@@ -881,6 +1043,13 @@ hipError_t bwd_typed(const BwdArgs &a, hipStream_t stream) {
         if (e != hipSuccess) return e;
     }
     constexpr int BVA = 32;  // value slice of the reverse pass
+    if constexpr (sizeof(TQ) == 2)
+        hipLaunchKernelGGL((bwd_state_mfma_kernel<DK, BVA, TD>),
+                           dim3(static_cast<unsigned>(a.BH * (DV / BVA))), dim3(NT), 0, stream,
+                           static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.k),
+                           static_cast<const TD *>(a.d), a.beta, a.alpha,
+                           static_cast<const bf16_t *>(a.dO), a.dS_T, a.dMck, a.dS0, a.T, DV);
+    else
     hipLaunchKernelGGL((bwd_state_kernel<C, DK, BVA, TQ, TD>),
                        dim3(static_cast<unsigned>(a.BH * (DV / BVA))), dim3(NT), 0, stream,
                        static_cast<const TQ *>(a.q), static_cast<const TQ *>(a.k),
