@@ -562,6 +562,36 @@ __device__ __forceinline__ v4f mtile(v4f acc, int i0, int j0, int lr, int lq, FA
     }
 }
 
+// the same product with fp32-accurate operands: each factor x is split into bf16 hi = bf16(x)
+// and lo = bf16(x - hi), and hi.hi + hi.lo + lo.hi is accumulated (the dropped lo.lo term is
+// below 2^-16 of the product)
+template <int K, typename FA, typename FB>
+__device__ __forceinline__ v4f mtile_split(v4f acc, int i0, int j0, int lr, int lq, FA &&a, FB &&b) {
+    static_assert(K % 32 == 0, "K steps of 32");
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 32) {
+        const int kb = k0 + 8 * lq;
+        uint32_t ah[4], al[4], bh[4], bl[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float a0 = a(i0 + lr, kb + 2 * e), a1 = a(i0 + lr, kb + 2 * e + 1);
+            const float b0 = b(kb + 2 * e, j0 + lr), b1 = b(kb + 2 * e + 1, j0 + lr);
+            ah[e] = pack2(a0, a1);
+            bh[e] = pack2(b0, b1);
+            al[e] = pack2(a0 - bf_lo(ah[e]), a1 - bf_hi(ah[e]));
+            bl[e] = pack2(b0 - bf_lo(bh[e]), b1 - bf_hi(bh[e]));
+        }
+        const v8s Ah = __builtin_bit_cast(v8s, make_uint4(ah[0], ah[1], ah[2], ah[3]));
+        const v8s Al = __builtin_bit_cast(v8s, make_uint4(al[0], al[1], al[2], al[3]));
+        const v8s Bh = __builtin_bit_cast(v8s, make_uint4(bh[0], bh[1], bh[2], bh[3]));
+        const v8s Bl = __builtin_bit_cast(v8s, make_uint4(bl[0], bl[1], bl[2], bl[3]));
+        acc = mfma32(Ah, Bh, acc);
+        acc = mfma32(Ah, Bl, acc);
+        acc = mfma32(Al, Bh, acc);
+    }
+    return acc;
+}
+
 template <int DK, int DV, int BV, typename TD>
 __global__ void __launch_bounds__(NT)
 bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
@@ -575,7 +605,6 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
     constexpr int C = 64;
     constexpr int PQ = DK + 2, PX = DK + 1, PC = C + 1, PS = BV + 1;
     constexpr int NF = DK / 16, NV = BV / 16;  // column tiles of C x DK and C x BV products
-    constexpr int TC = C / 16, TV = BV / 16;  // register blocks of the fp32 C x BV products
     __shared__ bf16_t sQ[C * PQ], sK[C * PQ];
     __shared__ float sKt[C * PX], sAS[C * PC], sP[C * PC], sT[C * PC];
     __shared__ float sM0[DK * PS], sdM[DK * PS];
@@ -670,16 +699,15 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             }
         }
         __syncthreads();
-        {  // U = T R (fp32); dU = P^T dO + diag(w) K~ dMC
-            float acc[TC][TV];
-            zero(acc);
-            const int i0 = (tid / 16) * TC, j0 = (tid % 16) * TV;
-            mm<TC, TV, C>(acc, i0, j0, [&](int i, int kk) { return sT[i * PC + kk]; },
-                          [&](int kk, int j) { return sR[kk * PS + j]; });
+        {  // U = T R (split precision); dU = P^T dO + diag(w) K~ dMC
 #pragma unroll
-            for (int m = 0; m < TC; ++m)
+            for (int t = 0; t < NV; ++t) {
+                const v4f u = mtile_split<C>(zero4(), R0, 16 * t, lr, lq,
+                                             [&](int i, int kk) { return sT[i * PC + kk]; },
+                                             [&](int kk, int j) { return sR[kk * PS + j]; });
 #pragma unroll
-                for (int nn = 0; nn < TV; ++nn) sU[(i0 + m) * PS + j0 + nn] = acc[m][nn];
+                for (int e = 0; e < 4; ++e) sU[(R0 + 4 * lq + e) * PS + 16 * t + lr] = u[e];
+            }
 #pragma unroll
             for (int t = 0; t < NV; ++t) {
                 const v4f du = mtile<C>(zero4(), R0, 16 * t, lr, lq,
@@ -693,16 +721,13 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             }
         }
         __syncthreads();
-        {  // dR = T^T dU (fp32), into sR
-            float acc[TC][TV];
-            zero(acc);
-            const int i0 = (tid / 16) * TC, j0 = (tid % 16) * TV;
-            mm<TC, TV, C>(acc, i0, j0, [&](int i, int kk) { return sT[kk * PC + i]; },
-                          [&](int kk, int j) { return sdU[kk * PS + j]; });
 #pragma unroll
-            for (int m = 0; m < TC; ++m)
+        for (int t = 0; t < NV; ++t) {  // dR = T^T dU (split precision), into sR
+            const v4f dr = mtile_split<C>(zero4(), R0, 16 * t, lr, lq,
+                                          [&](int i, int kk) { return sT[kk * PC + i]; },
+                                          [&](int kk, int j) { return sdU[kk * PS + j]; });
 #pragma unroll
-                for (int nn = 0; nn < TV; ++nn) sR[(i0 + m) * PS + j0 + nn] = acc[m][nn];
+            for (int e = 0; e < 4; ++e) sR[(R0 + 4 * lq + e) * PS + 16 * t + lr] = dr[e];
         }
         __syncthreads();
         float *const sdR = sR;
@@ -889,9 +914,21 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
     __shared__ float sD[4 * 16 * PD];     // D_i, block i at rows 16 i
     __shared__ float sb[C], sg[C], sgam[C], sw[C];
 
+    // workgroup -> (sequence, value slice); the slices of one sequence share an XCD (and its
+    // L2) when the sequence count allows it, so their re-reads of q, k, d hit L2
     const int nvt = dv / BV;
-    const int64_t bh = blockIdx.x / nvt;
-    const int j0 = static_cast<int>(blockIdx.x % nvt) * BV;
+    const int64_t nseq = gridDim.x / nvt;
+    int64_t bh;
+    int vt;
+    if ((nseq & 7) == 0) {
+        const int64_t xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+        vt = static_cast<int>(slot % nvt);
+        bh = (slot / nvt) * 8 + xcd;
+    } else {
+        vt = static_cast<int>(blockIdx.x % nvt);
+        bh = blockIdx.x / nvt;
+    }
+    const int j0 = vt * BV;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lq = lane >> 4;
     const int R0 = 16 * wave;
@@ -981,19 +1018,30 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
         // dR = (I + A)^{-T} dU by blocks i = 3..0: y = dU_i - sum_{k>i} A_ki^T dR_k, then
         // dR_i = D_i^T y (in place in sX)
         for (int ib = 3; ib >= 0; --ib) {
-            for (int idx = tid; idx < 16 * BV; idx += NT) {
-                const int r = idx / BV, j = idx % BV, ri = 16 * ib + r;
-                float y = sX[ri * PS + j];
-                for (int s2 = 16 * (ib + 1); s2 < C; ++s2)
-                    y -= sb[s2] * sAS[s2 * PC + ri] * sX[s2 * PS + j];
-                sY16[r * PS + j] = y;
+            const int rb = 16 * ib;
+            if (wave < NV) {  // wave t: columns 16t..16t+15 of the block
+                v4f y = zero4();
+                if (ib < 3) {
+                    // sum over the later rows s >= 16(ib+1); rows past C - 1 read as zero
+                    y = mtile_split<64>(zero4(), 0, 16 * wave, lr, lq,
+                                        [&](int r, int s2) {
+                                            return s2 >= rb + 16 ? sb[s2] * sAS[s2 * PC + rb + r] : 0.f;
+                                        },
+                                        [&](int s2, int j) { return s2 >= rb + 16 ? sX[s2 * PS + j] : 0.f; });
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * lq + e, j = 16 * wave + lr;
+                    sY16[r * PS + j] = sX[(rb + r) * PS + j] - y[e];
+                }
             }
             __syncthreads();
-            for (int idx = tid; idx < 16 * BV; idx += NT) {
-                const int r = idx / BV, j = idx % BV;
-                float acc = 0.f;
-                for (int r2 = r; r2 < 16; ++r2) acc += sD[(16 * ib + r2) * PD + r] * sY16[r2 * PS + j];
-                sX[(16 * ib + r) * PS + j] = acc;
+            if (wave < NV) {  // dR_i = D_i^T y: 16 x 16 times 16 x 16, padded to K = 32
+                const v4f dr = mtile_split<32>(zero4(), 0, 16 * wave, lr, lq,
+                                               [&](int r, int r2) { return r2 < 16 ? sD[(rb + r2) * PD + r] : 0.f; },
+                                               [&](int r2, int j) { return r2 < 16 ? sY16[r2 * PS + j] : 0.f; });
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sX[(rb + 4 * lq + e) * PS + 16 * wave + lr] = dr[e];
             }
             __syncthreads();
         }
