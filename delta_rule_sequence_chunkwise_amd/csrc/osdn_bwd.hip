@@ -145,6 +145,22 @@ __device__ __forceinline__ void decay_scan(const float *beta, const float *alpha
     }
 }
 
+// eight consecutive values of d as fp32 (32 bytes of fp32 or 16 bytes of bf16)
+__device__ __forceinline__ void load8(const float *p, float (&out)[8]) {
+    const float4 a = *reinterpret_cast<const float4 *>(p), b = *reinterpret_cast<const float4 *>(p + 4);
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+}
+__device__ __forceinline__ void load8(const bf16_t *p, float (&out)[8]) {
+    const uint4 u = *reinterpret_cast<const uint4 *>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        out[2 * e] = __uint_as_float(w[e] << 16);
+        out[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
+}
+
 // Q and K of the chunk in their input type, K~ = d (.) k in fp32 (zero rows past the end)
 template <int C, int DK, int PQ, int PX, typename TQ, typename TD>
 __device__ __forceinline__ void load_qk(const TQ *q, const TQ *k, const TD *d, int64_t row0, int n,
@@ -592,6 +608,35 @@ __device__ __forceinline__ v4f mtile_split(v4f acc, int i0, int j0, int lr, int 
     return acc;
 }
 
+// bf16 MFMA fragments from bf16 row-major LDS tiles (pitch a multiple of 8 elements):
+// rows: lane (q, n) gets X[r0 + n][k0 + 8q .. +7] (one 16-byte read);
+// cols: lane (q, n) gets X[k0 + 8q .. +7][c0 + n] (two transposing reads)
+__device__ __forceinline__ v8s frag_rows(const uint16_t *X, int pitch, int r0, int k0, int lr, int lq) {
+    return ld8(&X[(r0 + lr) * pitch + k0 + 8 * lq]);
+}
+__device__ __forceinline__ v8s frag_cols(const uint16_t *X, int pitch, int k0, int c0, int lr, int lq) {
+    const int kb = k0 + 8 * lq, c = c0 + 4 * (lr & 3), r = lr >> 2;
+    return cat8(ld_tr(&X[(kb + r) * pitch + c]), ld_tr(&X[(kb + 4 + r) * pitch + c]));
+}
+// the 16-deep row form: lane (q, n) gets X[r0 + n][k0 + 4q .. +3]
+__device__ __forceinline__ v4s frag4_rows(const uint16_t *X, int pitch, int r0, int k0, int lr, int lq) {
+    return ld4s(&X[(r0 + lr) * pitch + k0 + 4 * lq]);
+}
+// tile += A B over K (a multiple of 16), fragments from callables fa(k0) / fb(k0) that return
+// the 32-deep (v8s) or, for K == 16, the 16-deep (v4s) fragment at k0
+template <int K, typename FA, typename FB, typename FA4, typename FB4>
+__device__ __forceinline__ v4f ftile(v4f acc, FA &&fa, FB &&fb, FA4 &&fa4, FB4 &&fb4) {
+    if constexpr (K == 16) {
+        return mfma16(fa4(0), fb4(0), acc);
+    } else {
+        static_assert(K % 32 == 0, "K steps of 32");
+#pragma unroll
+        for (int k0 = 0; k0 < K; k0 += 32) acc = mfma32(fa(k0), fb(k0), acc);
+        return acc;
+    }
+}
+__device__ __forceinline__ uint16_t bf16_bits(float x) { return f32_to_bf16_bits(x); }
+
 template <int DK, int DV, int BV, typename TD>
 __global__ void __launch_bounds__(NT)
 bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
@@ -603,13 +648,19 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
                       float *__restrict__ gbeta, TD *__restrict__ gd,
                       float *__restrict__ galpha, int64_t T, int64_t nch) {
     constexpr int C = 64;
-    constexpr int PQ = DK + 2, PX = DK + 1, PC = C + 1, PS = BV + 1;
-    constexpr int NF = DK / 16, NV = BV / 16;  // column tiles of C x DK and C x BV products
-    __shared__ bf16_t sQ[C * PQ], sK[C * PQ];
-    __shared__ float sKt[C * PX], sAS[C * PC], sP[C * PC], sT[C * PC];
-    __shared__ float sM0[DK * PS], sdM[DK * PS];
-    __shared__ float sY[C * PS], sdO[C * PS], sU[C * PS], sR[C * PS], sdU[C * PS];
+    constexpr int PH = DK + 8, PCH = C + 8, PVH = BV + 8;  // bf16 pitches
+    constexpr int PC = C + 1, PS = BV + 1;                 // fp32 pitches
+    constexpr int NF = DK / 16, NV = BV / 16;
+    constexpr int MB = 2 * DK * PVH > C * PCH ? 2 * DK * PVH : C * PCH;
+    __shared__ alignas(16) uint16_t sQ[C * PH], sK[C * PH], sKt[C * PH];
+    __shared__ float sAS[C * PC], sP[C * PC], sT[C * PC];
+    __shared__ alignas(16) uint16_t sPb[C * PCH];  // P, later dP o G (bf16)
+    __shared__ alignas(16) uint16_t sMb[MB];       // M0 and dMC slices, later Gb (bf16)
+    __shared__ alignas(16) uint16_t sDOb[C * PVH], sGDOb[C * PVH], sUb[C * PVH], sWUb[C * PVH];
+    __shared__ alignas(16) uint16_t sDRb[C * PVH], sGDRb[C * PVH];
+    __shared__ float sY[C * PS], sR[C * PS], sU[C * PS], sdU[C * PS];
     __shared__ float sb[C], sg[C], sgam[C], sw[C], sdb[C], sdg[C], sew[C], sred[4];
+    uint16_t *const sM0b = sMb, *const sdMb = sMb + DK * PVH;
 
     const int64_t bh = blockIdx.x / nch, c = blockIdx.x % nch;
     const int64_t c0 = c * C, row0 = bh * T + c0;
@@ -620,32 +671,58 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
     const float *M0 = Mck + (bh * nch + c) * DK * DV;
     const float *dMC = dMck + (bh * nch + c) * DK * DV;
 
-    load_qk<C, DK, PQ, PX>(q, k, d, row0, n, sQ, sK, sKt, tid);
+    {  // Q, K, K~ = d (.) k as bf16: 8 features per 16-byte unit, all loads issued first
+        constexpr int G = DK / 8, NU = C * G / NT;  // units per row, units per thread
+        static_assert(NU * NT == C * G, "whole units");
+        uint4 qu[NU], ku[NU];
+        float dd[NU][8];
+#pragma unroll
+        for (int i = 0; i < NU; ++i) {
+            const int u = tid + i * NT, r = u / G, g = u % G;
+            const int64_t e = (row0 + (r < n ? r : n - 1)) * DK + 8 * g;
+            qu[i] = *reinterpret_cast<const uint4 *>(q + e);
+            ku[i] = *reinterpret_cast<const uint4 *>(k + e);
+            load8(d + e, dd[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < NU; ++i) {
+            const int u = tid + i * NT, r = u / G, g = u % G;
+            const bool ok = r < n;
+            const uint32_t kw[4] = {ku[i].x, ku[i].y, ku[i].z, ku[i].w};
+            uint32_t kt[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) kt[e] = pack2(dd[i][2 * e] * bf_lo(kw[e]), dd[i][2 * e + 1] * bf_hi(kw[e]));
+            const uint32_t m = ok ? 0xffffffffu : 0u;  // rows past the end are zero
+            *reinterpret_cast<uint4 *>(&sQ[r * PH + 8 * g]) =
+                make_uint4(qu[i].x & m, qu[i].y & m, qu[i].z & m, qu[i].w & m);
+            *reinterpret_cast<uint4 *>(&sK[r * PH + 8 * g]) = make_uint4(kw[0] & m, kw[1] & m, kw[2] & m, kw[3] & m);
+            *reinterpret_cast<uint4 *>(&sKt[r * PH + 8 * g]) = make_uint4(kt[0] & m, kt[1] & m, kt[2] & m, kt[3] & m);
+        }
+    }
     if (tid < 64) decay_scan<C>(beta, alpha, row0, n, sb, sg, sgam, sw, lane);
     if (tid < C) sdb[tid] = sdg[tid] = sew[tid] = 0.f;
     __syncthreads();
-    // AS = strictly lower (K K~^T) o G, P = lower-inclusive (Q K~^T) o G
-    {
-        auto bkt = [&](int kk, int j) { return sKt[j * PX + kk]; };
+    // AS = strictly lower (K K~^T) o G, P = lower-inclusive (Q K~^T) o G (fp32, and P in bf16)
 #pragma unroll
-        for (int t = 0; t < C / 16; ++t) {
-            v4f ak = zero4(), aq = zero4();
-            if (t <= wave) {
-                ak = mtile<DK>(ak, R0, 16 * t, lr, lq,
-                               [&](int i, int kk) { return to_f32(sK[i * PQ + kk]); }, bkt);
-                aq = mtile<DK>(aq, R0, 16 * t, lr, lq,
-                               [&](int i, int kk) { return to_f32(sQ[i * PQ + kk]); }, bkt);
-            }
+    for (int t = 0; t < C / 16; ++t) {
+        v4f ak = zero4(), aq = zero4();
+        if (t <= wave) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = R0 + 4 * lq + e, j = 16 * t + lr;
-                const float G = j <= i ? __expf(sg[i] - sg[j]) : 0.f;
-                sAS[i * PC + j] = j < i ? ak[e] * G : 0.f;
-                sP[i * PC + j] = aq[e] * G;
+            for (int k0 = 0; k0 < DK; k0 += 32) {
+                const v8s kt = frag_rows(sKt, PH, 16 * t, k0, lr, lq);
+                ak = mfma32(frag_rows(sK, PH, R0, k0, lr, lq), kt, ak);
+                aq = mfma32(frag_rows(sQ, PH, R0, k0, lr, lq), kt, aq);
             }
         }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = R0 + 4 * lq + e, j = 16 * t + lr;
+            const float G = j <= i ? __expf(sg[i] - sg[j]) : 0.f;
+            sAS[i * PC + j] = j < i ? ak[e] * G : 0.f;
+            sP[i * PC + j] = aq[e] * G;
+            sPb[i * PCH + j] = bf16_bits(aq[e] * G);
+        }
     }
-
     // T = (I + A)^{-1} once per chunk (fp32): the slices then need two products, not solves
     for (int idx = tid; idx < C * C; idx += NT) sT[(idx / C) * PC + idx % C] = idx / C == idx % C;
     __syncthreads();
@@ -658,76 +735,129 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
     for (int t = 0; t < C / 16; ++t) adP[t] = adA[t] = zero4();
     float frob = 0.f;
 
+    // the value slice's M0, dMC (fp32, four per 16-byte unit) and v, dO (bf16, eight per unit)
+    // pass through registers one slice ahead: units u = tid + i NT
+    constexpr int MU = DK * BV / 4 / NT, VU = C * BV / 8;  // per thread / per workgroup
+    static_assert(MU * NT * 4 == DK * BV && VU <= NT, "slice units");
+    static_assert(MU == 1 || MU == 2, "one or two M units per thread");
+    // named registers (an array carried across the loop would live in scratch)
+    float4 m0a = make_float4(0.f, 0.f, 0.f, 0.f), m0b = m0a, dma = m0a, dmb = m0a;
+    uint4 vu = make_uint4(0, 0, 0, 0), ou = make_uint4(0, 0, 0, 0);
+#define OSDN_BWD_LOAD_SLICE(S0)                                                               \
+    do {                                                                                      \
+        {                                                                                     \
+            const int f = tid / (BV / 4), j = 4 * (tid % (BV / 4));                          \
+            m0a = *reinterpret_cast<const float4 *>(M0 + f * DV + (S0) + j);                  \
+            dma = *reinterpret_cast<const float4 *>(dMC + f * DV + (S0) + j);                 \
+        }                                                                                     \
+        if constexpr (MU == 2) {                                                              \
+            const int u = tid + NT, f = u / (BV / 4), j = 4 * (u % (BV / 4));                \
+            m0b = *reinterpret_cast<const float4 *>(M0 + f * DV + (S0) + j);                  \
+            dmb = *reinterpret_cast<const float4 *>(dMC + f * DV + (S0) + j);                 \
+        }                                                                                     \
+        if (tid < VU) {                                                                       \
+            const int r = tid / (BV / 8), j = 8 * (tid % (BV / 8));                          \
+            const int64_t e = (row0 + (r < n ? r : n - 1)) * DV + (S0) + j;                   \
+            vu = *reinterpret_cast<const uint4 *>(v + e);                                     \
+            ou = *reinterpret_cast<const uint4 *>(dO + e);                                    \
+        }                                                                                     \
+    } while (0)
+    OSDN_BWD_LOAD_SLICE(0);
+
     for (int s0 = 0; s0 < DV; s0 += BV) {
-        __syncthreads();  // the previous slice (and the scores) are done
-        for (int idx = tid; idx < DK * BV; idx += NT) {
-            const int f = idx / BV, j = idx % BV;
-            const float m0 = M0[f * DV + s0 + j], dm = dMC[f * DV + s0 + j];
-            sM0[f * PS + j] = m0;
-            sdM[f * PS + j] = dm;
-            frob += m0 * dm;
+        __syncthreads();  // the previous slice (and T) are done
+#pragma unroll
+        for (int i = 0; i < MU; ++i) {
+            const int u = tid + i * NT, f = u / (BV / 4), j = 4 * (u % (BV / 4));
+            const float4 mm4 = i == 0 ? m0a : m0b, dd4 = i == 0 ? dma : dmb;
+            *reinterpret_cast<uint2 *>(&sM0b[f * PVH + j]) =
+                make_uint2(pack2(mm4.x, mm4.y), pack2(mm4.z, mm4.w));
+            *reinterpret_cast<uint2 *>(&sdMb[f * PVH + j]) =
+                make_uint2(pack2(dd4.x, dd4.y), pack2(dd4.z, dd4.w));
+            frob += mm4.x * dd4.x + mm4.y * dd4.y + mm4.z * dd4.z + mm4.w * dd4.w;
         }
-        for (int idx = tid; idx < C * BV; idx += NT) {
-            const int r = idx / BV, j = idx % BV;
-            sY[r * PS + j] = r < n ? to_f32(v[(row0 + r) * DV + s0 + j]) : 0.f;
-            sdO[r * PS + j] = r < n ? to_f32(dO[(row0 + r) * DV + s0 + j]) : 0.f;
+        if (tid < VU) {
+            const int r = tid / (BV / 8), j = 8 * (tid % (BV / 8));
+            const bool ok = r < n;
+            const uint32_t vw[4] = {vu.x, vu.y, vu.z, vu.w}, ow[4] = {ou.x, ou.y, ou.z, ou.w};
+            uint32_t gw[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sY[r * PS + j + 2 * e] = ok ? bf_lo(vw[e]) : 0.f;
+                sY[r * PS + j + 2 * e + 1] = ok ? bf_hi(vw[e]) : 0.f;
+                gw[e] = pack2(sgam[r] * bf_lo(ow[e]), sgam[r] * bf_hi(ow[e]));
+            }
+            const uint32_t m = ok ? 0xffffffffu : 0u;  // rows past the end are zero
+            *reinterpret_cast<uint4 *>(&sDOb[r * PVH + j]) = make_uint4(ow[0] & m, ow[1] & m, ow[2] & m, ow[3] & m);
+            *reinterpret_cast<uint4 *>(&sGDOb[r * PVH + j]) = make_uint4(gw[0] & m, gw[1] & m, gw[2] & m, gw[3] & m);
         }
+        if (s0 + BV < DV) OSDN_BWD_LOAD_SLICE(s0 + BV);  // in flight through this slice's work
         __syncthreads();
         // K M0, Q M0, K~ dMC on this slice, kept in registers (this wave's rows); Y = V - gam
         // K M0 and R = b Y into LDS; the read-out row sums <dO_r, (Q M0)_r>
         v4f km[NV], kdm[NV];
         float go[4] = {0.f, 0.f, 0.f, 0.f};
-        {
-            auto bm = [&](int kk, int j) { return sM0[kk * PS + j]; };
 #pragma unroll
-            for (int t = 0; t < NV; ++t) {
-                km[t] = mtile<DK>(zero4(), R0, 16 * t, lr, lq,
-                                  [&](int i, int kk) { return to_f32(sK[i * PQ + kk]); }, bm);
-                const v4f qm = mtile<DK>(zero4(), R0, 16 * t, lr, lq,
-                                         [&](int i, int kk) { return to_f32(sQ[i * PQ + kk]); }, bm);
-                kdm[t] = mtile<DK>(zero4(), R0, 16 * t, lr, lq,
-                                   [&](int i, int kk) { return sKt[i * PX + kk]; },
-                                   [&](int kk, int j) { return sdM[kk * PS + j]; });
+        for (int t = 0; t < NV; ++t) {
+            v4f qm = zero4();
+            km[t] = kdm[t] = zero4();
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = R0 + 4 * lq + e, j = 16 * t + lr;
-                    go[e] += sdO[r * PS + j] * qm[e];
-                    const float y = sY[r * PS + j] - sgam[r] * km[t][e];
-                    sY[r * PS + j] = y;
-                    sR[r * PS + j] = sb[r] * y;
-                }
-            }
-        }
-        __syncthreads();
-        {  // U = T R (split precision); dU = P^T dO + diag(w) K~ dMC
-#pragma unroll
-            for (int t = 0; t < NV; ++t) {
-                const v4f u = mtile_split<C>(zero4(), R0, 16 * t, lr, lq,
-                                             [&](int i, int kk) { return sT[i * PC + kk]; },
-                                             [&](int kk, int j) { return sR[kk * PS + j]; });
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sU[(R0 + 4 * lq + e) * PS + 16 * t + lr] = u[e];
+            for (int k0 = 0; k0 < DK; k0 += 32) {
+                const v8s m0f = frag_cols(sM0b, PVH, k0, 16 * t, lr, lq);
+                km[t] = mfma32(frag_rows(sK, PH, R0, k0, lr, lq), m0f, km[t]);
+                qm = mfma32(frag_rows(sQ, PH, R0, k0, lr, lq), m0f, qm);
+                kdm[t] = mfma32(frag_rows(sKt, PH, R0, k0, lr, lq),
+                                frag_cols(sdMb, PVH, k0, 16 * t, lr, lq), kdm[t]);
             }
 #pragma unroll
-            for (int t = 0; t < NV; ++t) {
-                const v4f du = mtile<C>(zero4(), R0, 16 * t, lr, lq,
-                                        [&](int i, int kk) { return sP[kk * PC + i]; },
-                                        [&](int kk, int j) { return sdO[kk * PS + j]; });
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = R0 + 4 * lq + e, j = 16 * t + lr;
-                    sdU[r * PS + j] = du[e] + sw[r] * kdm[t][e];
-                }
+            for (int e = 0; e < 4; ++e) {
+                const int r = R0 + 4 * lq + e, j = 16 * t + lr;
+                go[e] += __uint_as_float(uint32_t(sDOb[r * PVH + j]) << 16) * qm[e];
+                const float y = sY[r * PS + j] - sgam[r] * km[t][e];
+                sY[r * PS + j] = y;
+                sR[r * PS + j] = sb[r] * y;
             }
         }
         __syncthreads();
 #pragma unroll
-        for (int t = 0; t < NV; ++t) {  // dR = T^T dU (split precision), into sR
+        for (int t = 0; t < NV; ++t) {  // U = T R (split precision), with its bf16 copies
+            const v4f u = mtile_split<C>(zero4(), R0, 16 * t, lr, lq,
+                                         [&](int i, int kk) { return sT[i * PC + kk]; },
+                                         [&](int kk, int j) { return sR[kk * PS + j]; });
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = R0 + 4 * lq + e, j = 16 * t + lr;
+                sU[r * PS + j] = u[e];
+                sUb[r * PVH + j] = bf16_bits(u[e]);
+                sWUb[r * PVH + j] = bf16_bits(sw[r] * u[e]);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < NV; ++t) {  // dU = P^T dO + diag(w) K~ dMC
+            v4f du = zero4();
+#pragma unroll
+            for (int k0 = 0; k0 < C; k0 += 32)
+                du = mfma32(frag_cols(sPb, PCH, k0, R0, lr, lq),
+                            frag_cols(sDOb, PVH, k0, 16 * t, lr, lq), du);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = R0 + 4 * lq + e, j = 16 * t + lr;
+                sdU[r * PS + j] = du[e] + sw[r] * kdm[t][e];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < NV; ++t) {  // dR = T^T dU (split precision), into sR, with copies
             const v4f dr = mtile_split<C>(zero4(), R0, 16 * t, lr, lq,
                                           [&](int i, int kk) { return sT[kk * PC + i]; },
                                           [&](int kk, int j) { return sdU[kk * PS + j]; });
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sR[(R0 + 4 * lq + e) * PS + 16 * t + lr] = dr[e];
+            for (int e = 0; e < 4; ++e) {
+                const int r = R0 + 4 * lq + e, j = 16 * t + lr;
+                sR[r * PS + j] = dr[e];
+                sDRb[r * PVH + j] = bf16_bits(dr[e]);
+                sGDRb[r * PVH + j] = bf16_bits(-sgam[r] * sb[r] * dr[e]);
+            }
         }
         __syncthreads();
         float *const sdR = sR;
@@ -769,34 +899,36 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             }
         }
         // dP += dO U^T, dA += dR U^T (negated later), and the slice's part of dQ, dK, dK~
-        auto bu = [&](int kk, int j) { return sU[j * PS + kk]; };
 #pragma unroll
         for (int t = 0; t < C / 16; ++t) {
             if (t <= wave) {
-                adP[t] = mtile<BV>(adP[t], R0, 16 * t, lr, lq,
-                                   [&](int i, int kk) { return sdO[i * PS + kk]; }, bu);
-                adA[t] = mtile<BV>(adA[t], R0, 16 * t, lr, lq,
-                                   [&](int i, int kk) { return sdR[i * PS + kk]; }, bu);
+                auto ub = [&](int k0) { return frag_rows(sUb, PVH, 16 * t, k0, lr, lq); };
+                auto ub4 = [&](int k0) { return frag4_rows(sUb, PVH, 16 * t, k0, lr, lq); };
+                adP[t] = ftile<BV>(adP[t], [&](int k0) { return frag_rows(sDOb, PVH, R0, k0, lr, lq); }, ub,
+                                   [&](int k0) { return frag4_rows(sDOb, PVH, R0, k0, lr, lq); }, ub4);
+                adA[t] = ftile<BV>(adA[t], [&](int k0) { return frag_rows(sDRb, PVH, R0, k0, lr, lq); }, ub,
+                                   [&](int k0) { return frag4_rows(sDRb, PVH, R0, k0, lr, lq); }, ub4);
             }
         }
-        auto bm0t = [&](int kk, int f) { return sM0[f * PS + kk]; };
 #pragma unroll
         for (int t = 0; t < NF; ++t) {
-            aQ[t] = mtile<BV>(aQ[t], R0, 16 * t, lr, lq,
-                              [&](int i, int kk) { return sgam[i] * sdO[i * PS + kk]; }, bm0t);
-            aK[t] = mtile<BV>(aK[t], R0, 16 * t, lr, lq,
-                              [&](int i, int kk) { return -sgam[i] * sb[i] * sdR[i * PS + kk]; },
-                              bm0t);
-            aKt[t] = mtile<BV>(aKt[t], R0, 16 * t, lr, lq,
-                               [&](int i, int kk) { return sw[i] * sU[i * PS + kk]; },
-                               [&](int kk, int f) { return sdM[f * PS + kk]; });
+            auto m0r = [&](int k0) { return frag_rows(sM0b, PVH, 16 * t, k0, lr, lq); };
+            auto m0r4 = [&](int k0) { return frag4_rows(sM0b, PVH, 16 * t, k0, lr, lq); };
+            aQ[t] = ftile<BV>(aQ[t], [&](int k0) { return frag_rows(sGDOb, PVH, R0, k0, lr, lq); }, m0r,
+                              [&](int k0) { return frag4_rows(sGDOb, PVH, R0, k0, lr, lq); }, m0r4);
+            aK[t] = ftile<BV>(aK[t], [&](int k0) { return frag_rows(sGDRb, PVH, R0, k0, lr, lq); }, m0r,
+                              [&](int k0) { return frag4_rows(sGDRb, PVH, R0, k0, lr, lq); }, m0r4);
+            aKt[t] = ftile<BV>(aKt[t], [&](int k0) { return frag_rows(sWUb, PVH, R0, k0, lr, lq); },
+                               [&](int k0) { return frag_rows(sdMb, PVH, 16 * t, k0, lr, lq); },
+                               [&](int k0) { return frag4_rows(sWUb, PVH, R0, k0, lr, lq); },
+                               [&](int k0) { return frag4_rows(sdMb, PVH, 16 * t, k0, lr, lq); });
         }
     }
     frob = block_sum(frob, sred, tid);  // ends with a barrier: the slices are done
 
     // masks, the decay terms (row sums inside the wave, column sums through LDS) and the
     // dbeta term of A
-    float *colpart = sM0;  // [4][C]
+    float *colpart = sY;  // [4][C]
     {
         float rowp[4], rowb[4];
 #pragma unroll
@@ -838,27 +970,37 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
     }
     __syncthreads();
     if (tid < C) sdg[tid] -= colpart[tid] + colpart[C + tid] + colpart[2 * C + tid] + colpart[3 * C + tid];
-    // dP o G and Gb = dA o G (row scaled by b) replace P and AS
+    // dP o G into sPb and Gb = dA o G (row scaled by b) into sMb, as bf16
+    uint16_t *const sGb = sMb;
 #pragma unroll
     for (int t = 0; t < C / 16; ++t)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = R0 + 4 * lq + e, j = 16 * t + lr;
             const float G = j <= i ? __expf(sg[i] - sg[j]) : 0.f;
-            sP[i * PC + j] = adP[t][e] * G;
-            sAS[i * PC + j] = adA[t][e] * G * sb[i];
+            sPb[i * PCH + j] = bf16_bits(adP[t][e] * G);
+            sGb[i * PCH + j] = bf16_bits(adA[t][e] * G * sb[i]);
         }
     __syncthreads();
-    {
-        auto bkt = [&](int kk, int f) { return sKt[kk * PX + f]; };
+    float dfin[NF][4];  // d at this lane's output positions, loaded ahead of the products
 #pragma unroll
-        for (int t = 0; t < NF; ++t) {
-            aQ[t] = mtile<C>(aQ[t], R0, 16 * t, lr, lq, [&](int i, int kk) { return sP[i * PC + kk]; }, bkt);
-            aK[t] = mtile<C>(aK[t], R0, 16 * t, lr, lq, [&](int i, int kk) { return sAS[i * PC + kk]; }, bkt);
-            aKt[t] = mtile<C>(aKt[t], R0, 16 * t, lr, lq, [&](int i, int kk) { return sP[kk * PC + i]; },
-                              [&](int kk, int f) { return to_f32(sQ[kk * PQ + f]); });
-            aKt[t] = mtile<C>(aKt[t], R0, 16 * t, lr, lq, [&](int i, int kk) { return sAS[kk * PC + i]; },
-                              [&](int kk, int f) { return to_f32(sK[kk * PQ + f]); });
+    for (int t = 0; t < NF; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = R0 + 4 * lq + e;
+            dfin[t][e] = to_f32(d[(row0 + (r < n ? r : n - 1)) * DK + 16 * t + lr]);
+        }
+#pragma unroll
+    for (int t = 0; t < NF; ++t) {
+#pragma unroll
+        for (int k0 = 0; k0 < C; k0 += 32) {
+            const v8s ktc = frag_cols(sKt, PH, k0, 16 * t, lr, lq);
+            aQ[t] = mfma32(frag_rows(sPb, PCH, R0, k0, lr, lq), ktc, aQ[t]);
+            aK[t] = mfma32(frag_rows(sGb, PCH, R0, k0, lr, lq), ktc, aK[t]);
+            aKt[t] = mfma32(frag_cols(sPb, PCH, k0, R0, lr, lq),
+                            frag_cols(sQ, PH, k0, 16 * t, lr, lq), aKt[t]);
+            aKt[t] = mfma32(frag_cols(sGb, PCH, k0, R0, lr, lq),
+                            frag_cols(sK, PH, k0, 16 * t, lr, lq), aKt[t]);
         }
     }
 #pragma unroll
@@ -869,8 +1011,8 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             if (r < n) {
                 const int64_t ix = (row0 + r) * DK + f;
                 gq[ix] = from_f32<bf16_t>(aQ[t][e]);
-                gk[ix] = from_f32<bf16_t>(aK[t][e] + aKt[t][e] * to_f32(d[ix]));
-                gd[ix] = from_f32<TD>(aKt[t][e] * to_f32(sK[r * PQ + f]));
+                gk[ix] = from_f32<bf16_t>(aK[t][e] + aKt[t][e] * dfin[t][e]);
+                gd[ix] = from_f32<TD>(aKt[t][e] * __uint_as_float(uint32_t(sK[r * PH + f]) << 16));
             }
         }
     __syncthreads();
@@ -890,6 +1032,7 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
         gbeta[row0 + tid] = sdb[tid];
         if (alpha && galpha) galpha[row0 + tid] = sdg[tid] / alpha[row0 + tid];
     }
+#undef OSDN_BWD_LOAD_SLICE
 }
 
 // ---- reverse pass over chunks on bf16 matrix cores (bf16 inputs, C = 64) --------------------
