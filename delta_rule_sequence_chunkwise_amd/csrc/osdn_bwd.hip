@@ -32,6 +32,8 @@
 // of every M x N product), the triangular solves run column-parallel with the partial sums of
 // one column reduced across adjacent lanes.  Rows past the end of the sequence are zero
 // (beta = 0, alpha = 1, dO = 0), so they add nothing.
+#include <type_traits>
+
 #include "osdn_internal.h"
 #include "osdn_mfma.h"
 
@@ -39,6 +41,14 @@ namespace osdn {
 namespace {
 
 constexpr int NT = 256;  // threads per workgroup
+
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
 
 // acc[m][n] += sum_{kk < K} a(i0 + m, kk) * b(kk, j0 + n)
 template <int TM, int TN, int K, typename FA, typename FB>
@@ -1048,13 +1058,20 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
                       const float *__restrict__ dS_T, float *__restrict__ dMck,
                       float *__restrict__ dS0, int64_t T, int dv) {
     constexpr int C = 64;
-    constexpr int PQ = DK + 2, PX = DK + 1, PC = C + 1, PS = BV + 1, PD = 17;
-    constexpr int NV = BV / 16;           // column tiles of the C x BV products
-    constexpr int MR = DK / 64;           // 16-row tiles of dM per wave
-    __shared__ bf16_t sQ[C * PQ], sK[C * PQ];
-    __shared__ float sKt[C * PX], sAS[C * PC], sP[C * PC];
-    __shared__ float sdO[C * PS], sX[C * PS], sY16[16 * PS], sdM[DK * PS];
-    __shared__ float sD[4 * 16 * PD];     // D_i, block i at rows 16 i
+    constexpr int PH = DK + 8, PCH = C + 8, PVH = BV + 8;  // bf16 pitches
+    constexpr int PC = C + 1, PS = BV + 1, PD = 17;        // fp32 pitches
+    constexpr int NV = BV / 16;   // column tiles of the C x BV products
+    constexpr int MR = DK / 64;   // 16-row tiles of dM per wave
+    constexpr int G = DK / 8, NU = C * G / NT;  // 16-byte units of a Q/K row; units per thread
+    constexpr int DU = sizeof(TD) == 4 ? 2 : 1;  // 16-byte units of d per unit of k
+    static_assert(NU * NT == C * G && NU <= 4 && C * BV / 8 == NT, "unit layout");
+    __shared__ alignas(16) uint16_t sQ[C * PH], sK[C * PH], sKt[C * PH];
+    __shared__ float sAS[C * PC], sP[C * PC];
+    __shared__ alignas(16) uint16_t sPb[C * PCH];
+    __shared__ alignas(16) uint16_t sDOb[C * PVH], sGDOb[C * PVH], sGDRb[C * PVH];
+    __shared__ alignas(16) uint16_t sdMb[DK * PVH];  // bf16 copy of dM (operand of K~ dM)
+    __shared__ float sX[C * PS], sY16[16 * PS], sdM[DK * PS];
+    __shared__ float sD[4 * 16 * PD];  // D_i, block i at rows 16 i
     __shared__ float sb[C], sg[C], sgam[C], sw[C];
 
     // workgroup -> (sequence, value slice); the slices of one sequence share an XCD (and its
@@ -1077,59 +1094,164 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
     const int R0 = 16 * wave;
     const int64_t nch = (T + C - 1) / C;
 
+    // the next chunk's q, k, d, dO, beta, alpha, loaded into named registers one chunk ahead
+    // (an array carried across the loop would live in scratch); unit i of this thread is
+    // u = tid + i NT: row u / G, features 8 (u % G) .. +7
+    uint4 q0, q1, q2, q3, k0r, k1r, k2r, k3r, dl0, dl1, dl2, dl3, dh0, dh1, dh2, dh3, ou;
+    float bv = 0.f, av = 1.f;
+    auto qreg = [&](auto I) -> uint4 & {
+        constexpr int i = decltype(I)::value;
+        if constexpr (i == 0) return q0; else if constexpr (i == 1) return q1;
+        else if constexpr (i == 2) return q2; else return q3;
+    };
+    auto kreg = [&](auto I) -> uint4 & {
+        constexpr int i = decltype(I)::value;
+        if constexpr (i == 0) return k0r; else if constexpr (i == 1) return k1r;
+        else if constexpr (i == 2) return k2r; else return k3r;
+    };
+    auto dlreg = [&](auto I) -> uint4 & {
+        constexpr int i = decltype(I)::value;
+        if constexpr (i == 0) return dl0; else if constexpr (i == 1) return dl1;
+        else if constexpr (i == 2) return dl2; else return dl3;
+    };
+    auto dhreg = [&](auto I) -> uint4 & {
+        constexpr int i = decltype(I)::value;
+        if constexpr (i == 0) return dh0; else if constexpr (i == 1) return dh1;
+        else if constexpr (i == 2) return dh2; else return dh3;
+    };
+    auto load_chunk = [&](int64_t cc) __attribute__((always_inline)) {
+        const int64_t r0 = bh * T + cc * C;
+        const int nn = static_cast<int>(T - cc * C < C ? T - cc * C : C);
+        static_for<0, NU>([&](auto I) __attribute__((always_inline)) {
+            const int u = tid + I * NT, r = u / G, g = u % G;
+            const int64_t e = (r0 + (r < nn ? r : nn - 1)) * DK + 8 * g;
+            qreg(I) = *reinterpret_cast<const uint4 *>(q + e);
+            kreg(I) = *reinterpret_cast<const uint4 *>(k + e);
+            const uint4 *dp = reinterpret_cast<const uint4 *>(d + e);
+            dlreg(I) = dp[0];
+            if constexpr (DU == 2) dhreg(I) = dp[1];
+        });
+        {
+            const int r = tid / (BV / 8), j = 8 * (tid % (BV / 8));
+            ou = *reinterpret_cast<const uint4 *>(dO + (r0 + (r < nn ? r : nn - 1)) * dv + j0 + j);
+        }
+        if (tid < 64 && tid < nn) {
+            bv = beta[r0 + tid];
+            av = alpha ? alpha[r0 + tid] : 1.f;
+        }
+    };
+    if (nch > 0) load_chunk(nch - 1);
+
     for (int idx = tid; idx < DK * BV; idx += NT) {
         const int f = idx / BV, j = idx % BV;
-        sdM[f * PS + j] = dS_T ? dS_T[(bh * DK + f) * dv + j0 + j] : 0.f;
+        const float x = dS_T ? dS_T[(bh * DK + f) * dv + j0 + j] : 0.f;
+        sdM[f * PS + j] = x;
+        sdMb[f * PVH + j] = bf16_bits(x);
     }
     for (int64_t c = nch - 1; c >= 0; --c) {
-        const int64_t c0 = c * C, row0 = bh * T + c0;
+        const int64_t c0 = c * C;
         const int n = static_cast<int>(T - c0 < C ? T - c0 : C);
         __syncthreads();  // the previous chunk is done with every buffer
-        load_qk<C, DK, PQ, PX>(q, k, d, row0, n, sQ, sK, sKt, tid);
-        for (int idx = tid; idx < C * BV; idx += NT) {
-            const int r = idx / BV, j = idx % BV;
-            sdO[r * PS + j] = r < n ? to_f32(dO[(row0 + r) * dv + j0 + j]) : 0.f;
+        // this chunk's registers into LDS: Q, K, K~ = d (.) k (bf16), dO; the decay scan
+        static_for<0, NU>([&](auto I) __attribute__((always_inline)) {
+            const int u = tid + I * NT, r = u / G, g = u % G;
+            const uint32_t m = r < n ? 0xffffffffu : 0u;  // rows past the end are zero
+            const uint4 kq = kreg(I), qq = qreg(I);
+            const uint32_t kw[4] = {kq.x, kq.y, kq.z, kq.w};
+            float dd[8];
+            if constexpr (DU == 2) {
+                const uint4 lo = dlreg(I), hi = dhreg(I);
+                const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dd[e] = __uint_as_float(w[e]);
+            } else {
+                const uint4 lo = dlreg(I);
+                const uint32_t w[4] = {lo.x, lo.y, lo.z, lo.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    dd[2 * e] = bf_lo(w[e]);
+                    dd[2 * e + 1] = bf_hi(w[e]);
+                }
+            }
+            uint32_t kt[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) kt[e] = pack2(dd[2 * e] * bf_lo(kw[e]), dd[2 * e + 1] * bf_hi(kw[e]));
+            *reinterpret_cast<uint4 *>(&sQ[r * PH + 8 * g]) = make_uint4(qq.x & m, qq.y & m, qq.z & m, qq.w & m);
+            *reinterpret_cast<uint4 *>(&sK[r * PH + 8 * g]) = make_uint4(kw[0] & m, kw[1] & m, kw[2] & m, kw[3] & m);
+            *reinterpret_cast<uint4 *>(&sKt[r * PH + 8 * g]) = make_uint4(kt[0] & m, kt[1] & m, kt[2] & m, kt[3] & m);
+        });
+        {
+            const int r = tid / (BV / 8), j = 8 * (tid % (BV / 8));
+            const uint32_t m = r < n ? 0xffffffffu : 0u;
+            *reinterpret_cast<uint4 *>(&sDOb[r * PVH + j]) = make_uint4(ou.x & m, ou.y & m, ou.z & m, ou.w & m);
         }
-        if (tid < 64) decay_scan<C>(beta, alpha, row0, n, sb, sg, sgam, sw, lane);
+        if (tid < 64) {
+            float x = (lane < n && alpha) ? logf(av) : 0.f;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(x, off);
+                if (lane >= off) x += y;
+            }
+            const float gl = __shfl(x, C - 1);
+            sb[lane] = lane < n ? bv : 0.f;
+            sg[lane] = x;
+            sgam[lane] = __expf(x);
+            sw[lane] = __expf(gl - x);
+        }
         for (int idx = tid; idx < DK * BV; idx += NT) {  // gradient at this chunk's end
             const int f = idx / BV, j = idx % BV;
             dMck[((bh * nch + c) * DK + f) * dv + j0 + j] = sdM[f * PS + j];
         }
+        if (c > 0) load_chunk(c - 1);  // in flight through this chunk's work
         __syncthreads();
-        // scores of this wave's rows; K~ dM of this wave's rows (registers)
+        {  // gam-scaled dO for the dM update
+            const int r = tid / (BV / 8), j = 8 * (tid % (BV / 8));
+            const uint4 o = *reinterpret_cast<const uint4 *>(&sDOb[r * PVH + j]);
+            const uint32_t w[4] = {o.x, o.y, o.z, o.w};
+            uint32_t gw[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gw[e] = pack2(sgam[r] * bf_lo(w[e]), sgam[r] * bf_hi(w[e]));
+            *reinterpret_cast<uint4 *>(&sGDOb[r * PVH + j]) = make_uint4(gw[0], gw[1], gw[2], gw[3]);
+        }
+        // scores of this wave's rows (AS, P in fp32, P in bf16); K~ dM of this wave's rows
         v4f kdm[NV];
-        {
-            auto bkt = [&](int kk, int j) { return sKt[j * PX + kk]; };
 #pragma unroll
-            for (int t = 0; t < C / 16; ++t) {
-                v4f ak = zero4(), aq = zero4();
-                if (t <= wave) {
-                    ak = mtile<DK>(ak, R0, 16 * t, lr, lq,
-                                   [&](int i, int kk) { return to_f32(sK[i * PQ + kk]); }, bkt);
-                    aq = mtile<DK>(aq, R0, 16 * t, lr, lq,
-                                   [&](int i, int kk) { return to_f32(sQ[i * PQ + kk]); }, bkt);
-                }
+        for (int t = 0; t < C / 16; ++t) {
+            v4f ak = zero4(), aq = zero4();
+            if (t <= wave) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = R0 + 4 * lq + e, j = 16 * t + lr;
-                    const float G = j <= i ? __expf(sg[i] - sg[j]) : 0.f;
-                    sAS[i * PC + j] = j < i ? ak[e] * G : 0.f;
-                    sP[i * PC + j] = aq[e] * G;
+                for (int k0 = 0; k0 < DK; k0 += 32) {
+                    const v8s kt = frag_rows(sKt, PH, 16 * t, k0, lr, lq);
+                    ak = mfma32(frag_rows(sK, PH, R0, k0, lr, lq), kt, ak);
+                    aq = mfma32(frag_rows(sQ, PH, R0, k0, lr, lq), kt, aq);
                 }
             }
 #pragma unroll
-            for (int t = 0; t < NV; ++t)
-                kdm[t] = mtile<DK>(zero4(), R0, 16 * t, lr, lq,
-                                   [&](int i, int kk) { return sKt[i * PX + kk]; },
-                                   [&](int kk, int j) { return sdM[kk * PS + j]; });
+            for (int e = 0; e < 4; ++e) {
+                const int i = R0 + 4 * lq + e, j = 16 * t + lr;
+                const float Gd = j <= i ? __expf(sg[i] - sg[j]) : 0.f;
+                sAS[i * PC + j] = j < i ? ak[e] * Gd : 0.f;
+                sP[i * PC + j] = aq[e] * Gd;
+                sPb[i * PCH + j] = bf16_bits(aq[e] * Gd);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < NV; ++t) {
+            kdm[t] = zero4();
+#pragma unroll
+            for (int k0 = 0; k0 < DK; k0 += 32)
+                kdm[t] = mfma32(frag_rows(sKt, PH, R0, k0, lr, lq),
+                                frag_cols(sdMb, PVH, k0, 16 * t, lr, lq), kdm[t]);
         }
         __syncthreads();
         // dU = P^T dO + diag(w) K~ dM into sX; the diagonal blocks' inverses D_i into sD
 #pragma unroll
         for (int t = 0; t < NV; ++t) {
-            const v4f du = mtile<C>(zero4(), R0, 16 * t, lr, lq,
-                                    [&](int i, int kk) { return sP[kk * PC + i]; },
-                                    [&](int kk, int j) { return sdO[kk * PS + j]; });
+            v4f du = zero4();
+#pragma unroll
+            for (int k0 = 0; k0 < C; k0 += 32)
+                du = mfma32(frag_cols(sPb, PCH, k0, R0, lr, lq),
+                            frag_cols(sDOb, PVH, k0, 16 * t, lr, lq), du);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = R0 + 4 * lq + e, j = 16 * t + lr;
@@ -1165,7 +1287,6 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             if (wave < NV) {  // wave t: columns 16t..16t+15 of the block
                 v4f y = zero4();
                 if (ib < 3) {
-                    // sum over the later rows s >= 16(ib+1); rows past C - 1 read as zero
                     y = mtile_split<64>(zero4(), 0, 16 * wave, lr, lq,
                                         [&](int r, int s2) {
                                             return s2 >= rb + 16 ? sb[s2] * sAS[s2 * PC + rb + r] : 0.f;
@@ -1184,11 +1305,15 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
                                                [&](int r, int r2) { return r2 < 16 ? sD[(rb + r2) * PD + r] : 0.f; },
                                                [&](int r2, int j) { return r2 < 16 ? sY16[r2 * PS + j] : 0.f; });
 #pragma unroll
-                for (int e = 0; e < 4; ++e) sX[(rb + 4 * lq + e) * PS + 16 * wave + lr] = dr[e];
+                for (int e = 0; e < 4; ++e) {
+                    const int r = rb + 4 * lq + e, j = 16 * wave + lr;
+                    sX[r * PS + j] = dr[e];
+                    sGDRb[r * PVH + j] = bf16_bits(-sgam[r] * sb[r] * dr[e]);
+                }
             }
             __syncthreads();
         }
-        // dM <- gam_L dM + Q^T diag(gam) dO - K^T diag(gam b) dR (this wave's 32 rows of dM)
+        // dM <- gam_L dM + Q^T diag(gam) dO - K^T diag(gam b) dR (this wave's rows of dM)
         {
             const float gl = sgam[C - 1];
 #pragma unroll
@@ -1196,16 +1321,20 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
                 const int f0 = 16 * (MR * wave + mt);
 #pragma unroll
                 for (int t = 0; t < NV; ++t) {
-                    v4f acc = mtile<C>(zero4(), f0, 16 * t, lr, lq,
-                                       [&](int f, int r) { return to_f32(sQ[r * PQ + f]); },
-                                       [&](int r, int j) { return sgam[r] * sdO[r * PS + j]; });
-                    acc = mtile<C>(acc, f0, 16 * t, lr, lq,
-                                   [&](int f, int r) { return to_f32(sK[r * PQ + f]); },
-                                   [&](int r, int j) { return -sgam[r] * sb[r] * sX[r * PS + j]; });
+                    v4f acc = zero4();
+#pragma unroll
+                    for (int k0 = 0; k0 < C; k0 += 32) {
+                        acc = mfma32(frag_cols(sQ, PH, k0, f0, lr, lq),
+                                     frag_cols(sGDOb, PVH, k0, 16 * t, lr, lq), acc);
+                        acc = mfma32(frag_cols(sK, PH, k0, f0, lr, lq),
+                                     frag_cols(sGDRb, PVH, k0, 16 * t, lr, lq), acc);
+                    }
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        float &x = sdM[(f0 + 4 * lq + e) * PS + 16 * t + lr];
-                        x = gl * x + acc[e];
+                        const int f = f0 + 4 * lq + e, j = 16 * t + lr;
+                        const float x = gl * sdM[f * PS + j] + acc[e];
+                        sdM[f * PS + j] = x;
+                        sdMb[f * PVH + j] = bf16_bits(x);
                     }
                 }
             }
