@@ -213,6 +213,72 @@ __device__ __forceinline__ void scores(const TQ *sQ, const TQ *sK, const float *
         }
 }
 
+// T = (I + A)^{-1} for C = 64, A = diag(b) AS strictly lower, by 16-row blocks: the diagonal
+// blocks D_i = (I + A_ii)^{-1} by forward substitution (four adjacent lanes per column), then
+// the blocks below the diagonal level by level, T_ij = -D_i sum_{j<=k<i} A_ik T_kj, in fp32.
+// tmp holds 3 x 16 x 17 floats.  Ends with a barrier.
+template <int PC>
+__device__ __forceinline__ void block_inverse64(float *sT, const float *sAS, const float *sb,
+                                                float *tmp, int tid) {
+    constexpr int C = 64;
+    for (int idx = tid; idx < C * C; idx += NT) sT[(idx / C) * PC + idx % C] = 0.f;
+    __syncthreads();
+    {
+        const int blk = tid >> 6, jj = (tid >> 2) & 15, sub = tid & 3, rb = 16 * blk;
+        float mine[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float part = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (4 * i < r) {
+                    const int s2 = 4 * i + sub;
+                    if (s2 < r) part += sAS[(rb + r) * PC + rb + s2] * mine[i];
+                }
+            }
+            part += __shfl_xor(part, 1);
+            part += __shfl_xor(part, 2);
+            const float val = (r == jj ? 1.f : 0.f) - sb[rb + r] * part;
+            if (r % 4 == sub) mine[r / 4] = val;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sT[(rb + 4 * i + sub) * PC + rb + jj] = mine[i];
+    }
+    __syncthreads();
+    static_for<1, 4>([&](auto LV) __attribute__((always_inline)) {  // blocks (i, j = i - lv)
+        constexpr int lv = decltype(LV)::value, np = 4 - lv;
+        for (int idx = tid; idx < np * 256; idx += NT) {  // W = sum_k A_ik T_kj
+            const int pr = idx >> 8, r = (idx >> 4) & 15, cc = idx & 15;
+            const int i = pr + lv, j = pr;
+            const float *arow = sAS + (16 * i + r) * PC + 16 * j;
+            const float *tcol = sT + 16 * j * PC + 16 * j + cc;
+            float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 0.f;
+#pragma unroll
+            for (int s2 = 0; s2 < 16 * lv; s2 += 4) {
+                w0 += arow[s2] * tcol[s2 * PC];
+                w1 += arow[s2 + 1] * tcol[(s2 + 1) * PC];
+                w2 += arow[s2 + 2] * tcol[(s2 + 2) * PC];
+                w3 += arow[s2 + 3] * tcol[(s2 + 3) * PC];
+            }
+            tmp[(pr * 16 + r) * 17 + cc] = sb[16 * i + r] * ((w0 + w1) + (w2 + w3));
+        }
+        __syncthreads();
+        for (int idx = tid; idx < np * 256; idx += NT) {  // T_ij = -D_i W (D_i lower)
+            const int pr = idx >> 8, r = (idx >> 4) & 15, cc = idx & 15;
+            const int i = pr + lv, j = pr;
+            const float *drow = sT + (16 * i + r) * PC + 16 * i;
+            float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+            for (int r2 = 0; r2 < 16; r2 += 2) {
+                a0 += (r2 <= r ? drow[r2] : 0.f) * tmp[(pr * 16 + r2) * 17 + cc];
+                a1 += (r2 + 1 <= r ? drow[r2 + 1] : 0.f) * tmp[(pr * 16 + r2 + 1) * 17 + cc];
+            }
+            sT[(16 * i + r) * PC + 16 * j + cc] = -(a0 + a1);
+        }
+        __syncthreads();
+    });
+}
+
 // Fixed-order sum over the workgroup (every thread passes its part; every thread gets the sum)
 __device__ __forceinline__ float block_sum(float x, float *scratch4, int tid) {
 #pragma unroll
@@ -734,9 +800,8 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
         }
     }
     // T = (I + A)^{-1} once per chunk (fp32): the slices then need two products, not solves
-    for (int idx = tid; idx < C * C; idx += NT) sT[(idx / C) * PC + idx % C] = idx / C == idx % C;
     __syncthreads();
-    solve_lower<C, C, PC, PC>(sT, sAS, sb, tid);
+    block_inverse64<PC>(sT, sAS, sb, sY, tid);
 
     v4f aQ[NF], aK[NF], aKt[NF], adP[C / 16], adA[C / 16];
 #pragma unroll
@@ -1026,16 +1091,20 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             }
         }
     __syncthreads();
-    if (tid == 0) {  // the last row's terms, then the reverse running sum of dg
-        float ews = 0.f;
-        for (int r = 0; r < n; ++r) ews += sew[r];
-        float acc = 0.f;
-        for (int r = n - 1; r >= 0; --r) {
-            float g = sdg[r] - sew[r];
-            if (r == n - 1) g += sgam[C - 1] * frob + ews;
-            acc += g;
-            sdg[r] = acc;  // d ln(alpha_r)
+    if (tid < 64) {  // the last row's terms, then the reverse running sum of dg (wave 0)
+        const float ew = lane < n ? sew[lane] : 0.f;
+        float ews = ew;
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) ews += __shfl_xor(ews, m);
+        float g = lane < n ? sdg[lane] - ew : 0.f;
+        if (lane == n - 1) g += sgam[C - 1] * frob + ews;
+        // suffix sum: x_r = sum_{r' >= r} g_r'
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_down(g, off);
+            if (lane + off < 64) g += y;
         }
+        sdg[lane] = g;  // d ln(alpha_r)
     }
     __syncthreads();
     if (tid < n) {
