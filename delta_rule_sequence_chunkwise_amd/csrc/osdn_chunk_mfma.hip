@@ -31,7 +31,8 @@
 //   tiles are split by column block: wave 2 takes blocks {0,3}, wave 3 blocks {1,2}.
 // * Stager waves (4, 5) bring the k rows of chunk c+2 into LDS (two row blocks each) and write
 //   k~ = d (.) k of those rows; d reaches their registers one step ahead.
-// * The loader wave (6) brings q and v of chunk c+2 into LDS and runs its decay scan.
+// * The loader wave (6) brings q and v of chunk c+2 into LDS.  Prep wave 2 runs chunk c+2's
+//   decay scan after its tiles: its LDS writes then never queue behind an LDS DMA of its own.
 // With the channel-wise gate (the caller passes pre-scaled q, k, d and per-chunk factors G_C)
 // the state waves also multiply the state's rows by G_C after each carry; the loader brings
 // G_C into LDS with the other loads of its chunk.  For the backward a variant records the state
@@ -469,15 +470,6 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
         // ---- loader wave: q and v of chunk c+2 into LDS, and the decay scan of chunk c+2 ------
         // Issuing the loads stalls while HBM drains them, so a wave with little other work
         // issues them; the parity of the target buffers is a compile-time constant.
-        // beta and alpha of the next chunk to scan, one step ahead in registers
-        float nbeta = 0.f, nalpha = 1.f;
-        auto load_ba = [&](int64_t cc) __attribute__((always_inline)) {
-            const int64_t cl = cc < nchunks ? cc : nchunks - 1;
-            const int r = min(lane, rows_of(cl) - 1);
-            nbeta = beta[seq0 + cl * CH + r];
-            nalpha = has_alpha ? alpha[seq0 + cl * CH + r] : 1.f;
-        };
-        if (nchunks > 0) load_ba(0);
         auto load_step = [&](auto par_c, int64_t cc, int slot) __attribute__((always_inline)) {
             constexpr int PAR = decltype(par_c)::value;  // cc mod 2
             // channel-wise gate: the chunk's G_C, through registers into LDS
@@ -491,8 +483,6 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                 const int n = rows_of(cc);
                 load_rows<DK, 0, CH>(q_buf[PAR], q, r0, n, lane);
                 load_v(v_buf[PAR], v, r0, n, dv, j0, lane);
-                scan_chunk<DK>(sm, slot, nbeta, nalpha, n, has_alpha, lane);  // slot = cc mod 3
-                load_ba(cc + 1);
             }
             wait_global();
             if constexpr (GATE) {
@@ -680,11 +670,30 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
             }
         }
     };
-    // one loop per prep wave, so its registers need no merging between the two variants
+    // one loop per prep wave, so its registers need no merging between the two variants.
+    // Prep wave 0 also runs the decay scan of chunk c+2 after its tiles (it issues no LDS DMA,
+    // so its LDS writes never wait for loads); beta and alpha come one step ahead in registers.
     auto prep_loop = [&](auto pw_c) __attribute__((always_inline)) {
-        int sl1 = 2;  // (c+1) mod 3
+        constexpr int PW = decltype(pw_c)::value;
+        float nbeta = 0.f, nalpha = 1.f;
+        auto load_ba = [&](int64_t cc) __attribute__((always_inline)) {
+            const int64_t cl = cc < nchunks ? cc : nchunks - 1;
+            const int r = min(lane, rows_of(cl) - 1);
+            nbeta = beta[seq0 + cl * CH + r];
+            nalpha = has_alpha ? alpha[seq0 + cl * CH + r] : 1.f;
+        };
+        if (PW == 0 && nchunks > 0) load_ba(0);
+        int sl1 = 2;  // (c+1) mod 3; (c+2) mod 3 is the slot after it
         for (int64_t c = -2; c < nchunks; ++c) {
             prep_step(pw_c, c, sl1);
+            if constexpr (PW == 0) {
+                const int64_t cc = c + 2;
+                if (cc < nchunks) {
+                    const int sl2 = sl1 == 2 ? 0 : sl1 + 1;
+                    scan_chunk<DK>(sm, sl2, nbeta, nalpha, rows_of(cc), has_alpha, lane);
+                    load_ba(cc + 1);
+                }
+            }
             block_sync();
             sl1 = sl1 == 2 ? 0 : sl1 + 1;
         }
