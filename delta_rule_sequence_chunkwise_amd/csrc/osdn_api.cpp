@@ -385,6 +385,18 @@ int64_t bwd_ckpt_bytes(int64_t B, int64_t H, int64_t T, int32_t dk, int32_t dv, 
     return round256(n * 4);
 }
 
+// bytes of the chunk inverses of the backward (bf16 inputs: two bf16 64 x 64 planes per chunk;
+// fp32 inputs: none); called after bwd_ckpt_bytes has accepted the sizes
+int64_t bwd_tinv_bytes(int64_t B, int64_t H, int64_t T, osdn_dtype qkv) {
+    if (qkv != OSDN_BF16) return 0;
+    const int64_t C = osdn::bwd_chunk_size(qkv);
+    int64_t n = 1;
+    if (!mul_ok(n, B, kMaxElems) || !mul_ok(n, H, kMaxElems) ||
+        !mul_ok(n, (T + C - 1) / C, kMaxElems) || !mul_ok(n, 2 * C * C, kMaxElems))
+        return -1;
+    return round256(n * 2);
+}
+
 }  // namespace
 
 extern "C" {
@@ -392,7 +404,9 @@ extern "C" {
 int64_t osdn_chunk_bwd_workspace(int64_t B, int64_t H, int64_t T, int32_t dk, int32_t dv,
                                  osdn_dtype qkv) {
     const int64_t b = bwd_ckpt_bytes(B, H, T, dk, dv, qkv);
-    return b < 0 ? -1 : 2 * b;
+    if (b < 0) return -1;
+    const int64_t t = bwd_tinv_bytes(B, H, T, qkv);
+    return t < 0 ? -1 : 2 * b + t;
 }
 
 osdn_status osdn_chunk_bwd(const void *q, const void *k, const void *v, const float *beta,
@@ -407,6 +421,9 @@ osdn_status osdn_chunk_bwd(const void *q, const void *k, const void *v, const fl
     if (!head_dim_ok(dk) || !head_dim_ok(dv)) return OSDN_ERR_UNSUPPORTED;
     const int64_t ck = bwd_ckpt_bytes(B, H, T, dk, dv, qkv);
     if (ck < 0) return OSDN_ERR_SHAPE;
+    const int64_t tk = bwd_tinv_bytes(B, H, T, qkv);
+    if (tk < 0) return OSDN_ERR_SHAPE;
+    const int64_t wsb = 2 * ck + tk;
     int64_t BH = 1;
     if (!mul_ok(BH, B, kMaxElems) || !mul_ok(BH, H, kMaxElems)) return OSDN_ERR_SHAPE;
     int64_t tok = BH, st = BH;
@@ -423,7 +440,7 @@ osdn_status osdn_chunk_bwd(const void *q, const void *k, const void *v, const fl
                   !grad_beta || !grad_d || !workspace))
         return OSDN_ERR_NULL;
     if (T == 0 && !grad_S0) return OSDN_OK;
-    if (T > 0 && workspace_bytes < 2 * ck) return OSDN_ERR_SHAPE;
+    if (T > 0 && workspace_bytes < wsb) return OSDN_ERR_SHAPE;
     if (!alpha) grad_alpha = nullptr;
 
     const int64_t eq = elem_size(qkv), ed = elem_size(d_dtype);
@@ -449,7 +466,7 @@ osdn_status osdn_chunk_bwd(const void *q, const void *k, const void *v, const fl
     const Range gv = range_of(grad_v, nt ? nv * eq : 0), gd = range_of(grad_d, nt ? nqk * ed : 0);
     const Range gb = range_of(grad_beta, nt * 4), ga = range_of(grad_alpha, grad_alpha ? nt * 4 : 0);
     const Range gs0 = range_of(grad_S0, st * 4);
-    const Range rw = range_of(workspace, T > 0 ? 2 * ck : 0);
+    const Range rw = range_of(workspace, T > 0 ? wsb : 0);
     const Range *outs[] = {&gq, &gk, &gv, &gd, &gb, &ga, &gs0, &rw};
     const Range *ins[] = {&rq, &rk, &rv, &rd, &rb, &ra, &rs0, &rgo, &rgst};
     for (int i = 0; i < 8; ++i) {
@@ -463,8 +480,9 @@ osdn_status osdn_chunk_bwd(const void *q, const void *k, const void *v, const fl
     osdn::BwdArgs a{q, k, v, d, beta, alpha, S0, grad_o, grad_S_T, grad_q, grad_k, grad_v,
                     grad_beta, grad_alpha, grad_d, grad_S0,
                     T > 0 ? reinterpret_cast<float *>(ws) : nullptr,
-                    T > 0 ? reinterpret_cast<float *>(ws + ck) : nullptr, BH, T, dk, dv, qkv,
-                    d_dtype};
+                    T > 0 ? reinterpret_cast<float *>(ws + ck) : nullptr,
+                    T > 0 && tk > 0 ? reinterpret_cast<uint16_t *>(ws + 2 * ck) : nullptr, BH, T,
+                    dk, dv, qkv, d_dtype};
     const hipError_t err = osdn::launch_chunk_bwd(a, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? OSDN_OK : OSDN_ERR_LAUNCH;
 }

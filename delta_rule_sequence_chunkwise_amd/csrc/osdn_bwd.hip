@@ -23,14 +23,18 @@
 //   d ln a_t = sum_{t <= r <= L} dg_r,   da = d ln a / a
 //   dd  = dK~ o K,   dK += dK~ o D
 //
-// Three launches on the caller's stream: (1) the forward (the bf16 matrix-core kernel for bf16
-// inputs, the fp32 one for fp32 inputs) records M0 of every chunk into the workspace; (2) bwd_state_kernel walks the chunks backwards per (sequence, value slice)
-// carrying dM, records dMC of every chunk and writes the initial-state gradient; (3)
-// bwd_chunk_kernel, one workgroup per (sequence, chunk), computes every gradient of the
-// chunk's rows from M0 and dMC.  Arithmetic of (2) and (3) is fp32 on the vector ALUs:
-// tile products are register-blocked (each of the 256 threads owns one (M/16) x (N/16) block
-// of every M x N product), the triangular solves run column-parallel with the partial sums of
-// one column reduced across adjacent lanes.  Rows past the end of the sequence are zero
+// Launches on the caller's stream: (1) the forward (the bf16 matrix-core kernel for bf16
+// inputs, the fp32 one for fp32 inputs) records M0 of every chunk into the workspace; (2) for
+// bf16 inputs, bwd_tinv_kernel inverts every chunk's I + A in parallel into the workspace (T
+// does not depend on the state); (3) the reverse pass walks the chunks backwards per
+// (sequence, value slice) carrying dM, records dMC of every chunk and writes the initial-state
+// gradient; (4) the per-chunk pass, one workgroup per (sequence, chunk), computes every
+// gradient of the chunk's rows from M0, dMC (and T).  For fp32 inputs (2) is skipped and
+// (3), (4) are fp32 on the vector ALUs (bwd_state_kernel, bwd_chunk_kernel): tile products
+// are register-blocked (each of the 256 threads owns one (M/16) x (N/16) block of every M x N
+// product), the triangular solves run column-parallel with the partial sums of one column
+// reduced across adjacent lanes.  For bf16 inputs they run on matrix cores
+// (bwd_state_mfma_kernel, bwd_chunk_mfma_kernel).  Rows past the end of the sequence are zero
 // (beta = 0, alpha = 1, dO = 0), so they add nothing.
 #include <type_traits>
 
@@ -620,69 +624,10 @@ bwd_chunk_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k, const TQ *_
 // ---- per-chunk gradients on bf16 matrix cores (bf16 inputs, C = 64) ---------------------------
 // Same data flow as bwd_chunk_kernel.  Wave w owns rows 16w..16w+15 of every product, as 16x16
 // fp32 tiles in the MFMA C layout (lane (q, n) holds rows 4q..4q+3 of column n); operand
-// fragments are gathered from the fp32/bf16 LDS tiles through the same accessors and rounded
-// to bf16 (K steps of 32, or 16 for the value-slice contractions).  The triangular solves and
-// every row or column sum stay fp32.
-
-// tile += sum_{kk < K} a(i0 + row, kk) b(kk, j0 + col) on one 16x16 output tile
-template <int K, typename FA, typename FB>
-__device__ __forceinline__ v4f mtile(v4f acc, int i0, int j0, int lr, int lq, FA &&a, FB &&b) {
-    static_assert(K % 32 == 0 || K == 16, "K steps of 32 or one of 16");
-    if constexpr (K == 16) {
-        const int kb = 4 * lq;
-        const v4s af = __builtin_bit_cast(
-            v4s, make_uint2(pack2(a(i0 + lr, kb), a(i0 + lr, kb + 1)),
-                            pack2(a(i0 + lr, kb + 2), a(i0 + lr, kb + 3))));
-        const v4s bf = __builtin_bit_cast(
-            v4s, make_uint2(pack2(b(kb, j0 + lr), b(kb + 1, j0 + lr)),
-                            pack2(b(kb + 2, j0 + lr), b(kb + 3, j0 + lr))));
-        return mfma16(af, bf, acc);
-    } else {
-#pragma unroll
-        for (int k0 = 0; k0 < K; k0 += 32) {
-            const int kb = k0 + 8 * lq;
-            uint32_t au[4], bu[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                au[e] = pack2(a(i0 + lr, kb + 2 * e), a(i0 + lr, kb + 2 * e + 1));
-                bu[e] = pack2(b(kb + 2 * e, j0 + lr), b(kb + 2 * e + 1, j0 + lr));
-            }
-            acc = mfma32(__builtin_bit_cast(v8s, make_uint4(au[0], au[1], au[2], au[3])),
-                         __builtin_bit_cast(v8s, make_uint4(bu[0], bu[1], bu[2], bu[3])), acc);
-        }
-        return acc;
-    }
-}
-
-// the same product with fp32-accurate operands: each factor x is split into bf16 hi = bf16(x)
-// and lo = bf16(x - hi), and hi.hi + hi.lo + lo.hi is accumulated (the dropped lo.lo term is
-// below 2^-16 of the product)
-template <int K, typename FA, typename FB>
-__device__ __forceinline__ v4f mtile_split(v4f acc, int i0, int j0, int lr, int lq, FA &&a, FB &&b) {
-    static_assert(K % 32 == 0, "K steps of 32");
-#pragma unroll
-    for (int k0 = 0; k0 < K; k0 += 32) {
-        const int kb = k0 + 8 * lq;
-        uint32_t ah[4], al[4], bh[4], bl[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float a0 = a(i0 + lr, kb + 2 * e), a1 = a(i0 + lr, kb + 2 * e + 1);
-            const float b0 = b(kb + 2 * e, j0 + lr), b1 = b(kb + 2 * e + 1, j0 + lr);
-            ah[e] = pack2(a0, a1);
-            bh[e] = pack2(b0, b1);
-            al[e] = pack2(a0 - bf_lo(ah[e]), a1 - bf_hi(ah[e]));
-            bl[e] = pack2(b0 - bf_lo(bh[e]), b1 - bf_hi(bh[e]));
-        }
-        const v8s Ah = __builtin_bit_cast(v8s, make_uint4(ah[0], ah[1], ah[2], ah[3]));
-        const v8s Al = __builtin_bit_cast(v8s, make_uint4(al[0], al[1], al[2], al[3]));
-        const v8s Bh = __builtin_bit_cast(v8s, make_uint4(bh[0], bh[1], bh[2], bh[3]));
-        const v8s Bl = __builtin_bit_cast(v8s, make_uint4(bl[0], bl[1], bl[2], bl[3]));
-        acc = mfma32(Ah, Bh, acc);
-        acc = mfma32(Ah, Bl, acc);
-        acc = mfma32(Al, Bh, acc);
-    }
-    return acc;
-}
+// fragments are 16-byte or transposing reads of bf16 LDS tiles (K steps of 32, or 16 for the
+// value-slice contractions).  U = T R and dR = T^T dU take T from its hi/lo planes and R, dU
+// split the same way (hi.hi + hi.lo + lo.hi: fp32 accuracy; the dropped lo.lo term is below
+// 2^-16 of the product).  Every row or column sum stays fp32.
 
 // bf16 MFMA fragments from bf16 row-major LDS tiles (pitch a multiple of 8 elements):
 // rows: lane (q, n) gets X[r0 + n][k0 + 8q .. +7] (one 16-byte read);
@@ -719,22 +664,24 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
                       const bf16_t *__restrict__ v, const TD *__restrict__ d,
                       const float *__restrict__ beta, const float *__restrict__ alpha,
                       const bf16_t *__restrict__ dO, const float *__restrict__ Mck,
-                      const float *__restrict__ dMck, bf16_t *__restrict__ gq,
+                      const float *__restrict__ dMck, const uint16_t *__restrict__ Tck,
+                      bf16_t *__restrict__ gq,
                       bf16_t *__restrict__ gk, bf16_t *__restrict__ gv,
                       float *__restrict__ gbeta, TD *__restrict__ gd,
                       float *__restrict__ galpha, int64_t T, int64_t nch) {
     constexpr int C = 64;
     constexpr int PH = DK + 8, PCH = C + 8, PVH = BV + 8;  // bf16 pitches
-    constexpr int PC = C + 1, PS = BV + 1;                 // fp32 pitches
+    constexpr int PS = BV + 1;                             // fp32 pitch
     constexpr int NF = DK / 16, NV = BV / 16;
     constexpr int MB = 2 * DK * PVH > C * PCH ? 2 * DK * PVH : C * PCH;
     __shared__ alignas(16) uint16_t sQ[C * PH], sK[C * PH], sKt[C * PH];
-    __shared__ float sAS[C * PC], sP[C * PC], sT[C * PC];
     __shared__ alignas(16) uint16_t sPb[C * PCH];  // P, later dP o G (bf16)
+    __shared__ alignas(16) uint16_t sTh[C * PCH], sTl[C * PCH];  // T = (I + A)^{-1}: hi, lo
     __shared__ alignas(16) uint16_t sMb[MB];       // M0 and dMC slices, later Gb (bf16)
     __shared__ alignas(16) uint16_t sDOb[C * PVH], sGDOb[C * PVH], sUb[C * PVH], sWUb[C * PVH];
     __shared__ alignas(16) uint16_t sDRb[C * PVH], sGDRb[C * PVH];
-    __shared__ float sY[C * PS], sR[C * PS], sU[C * PS], sdU[C * PS];
+    __shared__ alignas(16) uint16_t sRh[C * PVH], sRl[C * PVH], sdUh[C * PVH], sdUl[C * PVH];
+    __shared__ float sY[C * PS], sU[C * PS], sdR[C * PS];
     __shared__ float sb[C], sg[C], sgam[C], sw[C], sdb[C], sdg[C], sew[C], sred[4];
     uint16_t *const sM0b = sMb, *const sdMb = sMb + DK * PVH;
 
@@ -747,10 +694,12 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
     const float *M0 = Mck + (bh * nch + c) * DK * DV;
     const float *dMC = dMck + (bh * nch + c) * DK * DV;
 
-    {  // Q, K, K~ = d (.) k as bf16: 8 features per 16-byte unit, all loads issued first
+    {  // Q, K, K~ = d (.) k as bf16 (8 features per 16-byte unit) and the T planes, all loads
+       // issued first
         constexpr int G = DK / 8, NU = C * G / NT;  // units per row, units per thread
-        static_assert(NU * NT == C * G, "whole units");
-        uint4 qu[NU], ku[NU];
+        constexpr int TU = 2 * C * C / 8 / NT;      // 16-byte units of the T planes per thread
+        static_assert(NU * NT == C * G && TU * NT * 8 == 2 * C * C, "whole units");
+        uint4 qu[NU], ku[NU], tu[TU];
         float dd[NU][8];
 #pragma unroll
         for (int i = 0; i < NU; ++i) {
@@ -759,6 +708,14 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             qu[i] = *reinterpret_cast<const uint4 *>(q + e);
             ku[i] = *reinterpret_cast<const uint4 *>(k + e);
             load8(d + e, dd[i]);
+        }
+        const uint4 *tp = reinterpret_cast<const uint4 *>(Tck + (bh * nch + c) * (2 * C * C));
+#pragma unroll
+        for (int i = 0; i < TU; ++i) tu[i] = tp[tid + i * NT];
+#pragma unroll
+        for (int i = 0; i < TU; ++i) {  // unit u: plane u / 512, row (u / 8) % 64, columns 8 (u % 8) ..
+            const int u = tid + i * NT, r = (u >> 3) & 63, g = u & 7;
+            *reinterpret_cast<uint4 *>(&(i < TU / 2 ? sTh : sTl)[r * PCH + 8 * g]) = tu[i];
         }
 #pragma unroll
         for (int i = 0; i < NU; ++i) {
@@ -778,10 +735,12 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
     if (tid < 64) decay_scan<C>(beta, alpha, row0, n, sb, sg, sgam, sw, lane);
     if (tid < C) sdb[tid] = sdg[tid] = sew[tid] = 0.f;
     __syncthreads();
-    // AS = strictly lower (K K~^T) o G, P = lower-inclusive (Q K~^T) o G (fp32, and P in bf16)
-#pragma unroll
-    for (int t = 0; t < C / 16; ++t) {
-        v4f ak = zero4(), aq = zero4();
+    // the score tiles of this wave's rows: AS = strictly lower (K K~^T) o G and P =
+    // lower-inclusive (Q K~^T) o G, in the C layout of tile t (columns 16t..16t+15); P also
+    // into LDS as bf16 for the slices
+    auto score_tiles = [&](int t, v4f &ak, v4f &aq) __attribute__((always_inline)) {
+        ak = zero4();
+        aq = zero4();
         if (t <= wave) {
 #pragma unroll
             for (int k0 = 0; k0 < DK; k0 += 32) {
@@ -794,14 +753,25 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
         for (int e = 0; e < 4; ++e) {
             const int i = R0 + 4 * lq + e, j = 16 * t + lr;
             const float G = j <= i ? __expf(sg[i] - sg[j]) : 0.f;
-            sAS[i * PC + j] = j < i ? ak[e] * G : 0.f;
-            sP[i * PC + j] = aq[e] * G;
-            sPb[i * PCH + j] = bf16_bits(aq[e] * G);
+            ak[e] = j < i ? ak[e] * G : 0.f;
+            aq[e] = aq[e] * G;
+        }
+    };
+#pragma unroll
+    for (int t = 0; t < C / 16; ++t) {  // P only (AS is formed again where it is used)
+        v4f aq = zero4();
+        if (t <= wave) {
+#pragma unroll
+            for (int k0 = 0; k0 < DK; k0 += 32)
+                aq = mfma32(frag_rows(sQ, PH, R0, k0, lr, lq), frag_rows(sKt, PH, 16 * t, k0, lr, lq), aq);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = R0 + 4 * lq + e, j = 16 * t + lr;
+            sPb[i * PCH + j] = bf16_bits(j <= i ? aq[e] * __expf(sg[i] - sg[j]) : 0.f);
         }
     }
-    // T = (I + A)^{-1} once per chunk (fp32): the slices then need two products, not solves
     __syncthreads();
-    block_inverse64<PC>(sT, sAS, sb, sY, tid);
 
     v4f aQ[NF], aK[NF], aKt[NF], adP[C / 16], adA[C / 16];
 #pragma unroll
@@ -890,15 +860,25 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
                 go[e] += __uint_as_float(uint32_t(sDOb[r * PVH + j]) << 16) * qm[e];
                 const float y = sY[r * PS + j] - sgam[r] * km[t][e];
                 sY[r * PS + j] = y;
-                sR[r * PS + j] = sb[r] * y;
+                const float x = sb[r] * y;  // R, as hi/lo bf16
+                const uint16_t h = bf16_bits(x);
+                sRh[r * PVH + j] = h;
+                sRl[r * PVH + j] = bf16_bits(x - __uint_as_float(uint32_t(h) << 16));
             }
         }
         __syncthreads();
 #pragma unroll
-        for (int t = 0; t < NV; ++t) {  // U = T R (split precision), with its bf16 copies
-            const v4f u = mtile_split<C>(zero4(), R0, 16 * t, lr, lq,
-                                         [&](int i, int kk) { return sT[i * PC + kk]; },
-                                         [&](int kk, int j) { return sR[kk * PS + j]; });
+        for (int t = 0; t < NV; ++t) {  // U = T R (hi.hi + hi.lo + lo.hi), with its bf16 copies
+            v4f u = zero4();
+#pragma unroll
+            for (int k0 = 0; k0 < C; k0 += 32) {
+                if (k0 > R0 + 15) continue;  // T lower triangular
+                const v8s th = frag_rows(sTh, PCH, R0, k0, lr, lq), tl = frag_rows(sTl, PCH, R0, k0, lr, lq);
+                const v8s rh = frag_cols(sRh, PVH, k0, 16 * t, lr, lq), rl = frag_cols(sRl, PVH, k0, 16 * t, lr, lq);
+                u = mfma32(th, rh, u);
+                u = mfma32(th, rl, u);
+                u = mfma32(tl, rh, u);
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = R0 + 4 * lq + e, j = 16 * t + lr;
@@ -917,25 +897,34 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = R0 + 4 * lq + e, j = 16 * t + lr;
-                sdU[r * PS + j] = du[e] + sw[r] * kdm[t][e];
+                const float x = du[e] + sw[r] * kdm[t][e];  // as hi/lo bf16
+                const uint16_t h = bf16_bits(x);
+                sdUh[r * PVH + j] = h;
+                sdUl[r * PVH + j] = bf16_bits(x - __uint_as_float(uint32_t(h) << 16));
             }
         }
         __syncthreads();
 #pragma unroll
-        for (int t = 0; t < NV; ++t) {  // dR = T^T dU (split precision), into sR, with copies
-            const v4f dr = mtile_split<C>(zero4(), R0, 16 * t, lr, lq,
-                                          [&](int i, int kk) { return sT[kk * PC + i]; },
-                                          [&](int kk, int j) { return sdU[kk * PS + j]; });
+        for (int t = 0; t < NV; ++t) {  // dR = T^T dU (hi.hi + hi.lo + lo.hi), with copies
+            v4f dr = zero4();
+#pragma unroll
+            for (int k0 = 0; k0 < C; k0 += 32) {
+                if (k0 + 32 <= R0) continue;  // T^T upper triangular
+                const v8s th = frag_cols(sTh, PCH, k0, R0, lr, lq), tl = frag_cols(sTl, PCH, k0, R0, lr, lq);
+                const v8s uh = frag_cols(sdUh, PVH, k0, 16 * t, lr, lq), ul = frag_cols(sdUl, PVH, k0, 16 * t, lr, lq);
+                dr = mfma32(th, uh, dr);
+                dr = mfma32(th, ul, dr);
+                dr = mfma32(tl, uh, dr);
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = R0 + 4 * lq + e, j = 16 * t + lr;
-                sR[r * PS + j] = dr[e];
+                sdR[r * PS + j] = dr[e];
                 sDRb[r * PVH + j] = bf16_bits(dr[e]);
                 sGDRb[r * PVH + j] = bf16_bits(-sgam[r] * sb[r] * dr[e]);
             }
         }
         __syncthreads();
-        float *const sdR = sR;
         for (int idx = tid; idx < C * BV; idx += NT) {
             const int r = idx / BV, j = idx % BV;
             if (r < n) gv[(row0 + r) * DV + s0 + j] = from_f32<bf16_t>(sb[r] * sdR[r * PS + j]);
@@ -1010,6 +999,8 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
         for (int e = 0; e < 4; ++e) rowp[e] = rowb[e] = 0.f;
 #pragma unroll
         for (int t = 0; t < C / 16; ++t) {
+            v4f as, ps;  // AS and P of the tile, formed again
+            score_tiles(t, as, ps);
             float colp = 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -1018,10 +1009,10 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
                 const float da = j < i ? -adA[t][e] : 0.f;
                 adP[t][e] = dp;
                 adA[t][e] = da;
-                const float ex = dp * sP[i * PC + j] + da * sb[i] * sAS[i * PC + j];
+                const float ex = dp * ps[e] + da * sb[i] * as[e];
                 rowp[e] += ex;
                 colp += ex;
-                rowb[e] += da * sAS[i * PC + j];
+                rowb[e] += da * as[e];
             }
             colp += __shfl_xor(colp, 16);
             colp += __shfl_xor(colp, 32);
@@ -1114,37 +1105,126 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
 #undef OSDN_BWD_LOAD_SLICE
 }
 
+// ---- (I + A)^{-1} of every chunk (bf16 inputs, C = 64) ---------------------------------------
+// One workgroup per (sequence, chunk).  AS = strictly lower (K K~^T) o G on matrix cores (the
+// same tiles the per-chunk pass forms), then T = (I + diag(b) AS)^{-1} in fp32 by blocks, stored
+// as two bf16 planes, hi = bf16(T) and lo = bf16(T - hi), row-major 64 x 64 each.  The reverse
+// pass and the per-chunk pass take their products with T and T^T from the planes at fp32
+// accuracy (hi.hi + hi.lo + lo.hi).  T of a chunk does not depend on the state, so all chunks
+// are inverted in parallel instead of inside the sequential reverse pass.
+template <int DK, typename TD>
+__global__ void __launch_bounds__(NT)
+bwd_tinv_kernel(const bf16_t *__restrict__ k, const TD *__restrict__ d,
+                const float *__restrict__ beta, const float *__restrict__ alpha,
+                uint16_t *__restrict__ Tck, int64_t T, int64_t nch) {
+    constexpr int C = 64, PH = DK + 8, PC = C + 1;
+    // K, K~ (bf16) until AS is in registers; then AS, T and the block products' scratch (fp32)
+    // in the same bytes, so four workgroups fit a CU
+    constexpr int KB = 2 * C * PH * 2, FB = (2 * C * PC + 3 * 16 * 17) * 4;
+    __shared__ alignas(16) unsigned char smem[KB > FB ? KB : FB];
+    __shared__ float sb[C], sg[C], sgam[C], sw[C];
+    uint16_t *const sK = reinterpret_cast<uint16_t *>(smem), *const sKt = sK + C * PH;
+    float *const sAS = reinterpret_cast<float *>(smem), *const sT = sAS + C * PC;
+    float *const sTmp = sT + C * PC;
+
+    const int64_t bh = blockIdx.x / nch, c = blockIdx.x % nch;
+    const int64_t c0 = c * C, row0 = bh * T + c0;
+    const int n = static_cast<int>(T - c0 < C ? T - c0 : C);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 15, lq = lane >> 4;
+    const int R0 = 16 * wave;
+    {  // K and K~ = d (.) k as bf16, rows past the end zero
+        constexpr int G = DK / 8, NU = C * G / NT;
+        static_assert(NU * NT == C * G, "whole units");
+        uint4 ku[NU];
+        float dd[NU][8];
+#pragma unroll
+        for (int i = 0; i < NU; ++i) {
+            const int u = tid + i * NT, r = u / G, g = u % G;
+            const int64_t e = (row0 + (r < n ? r : n - 1)) * DK + 8 * g;
+            ku[i] = *reinterpret_cast<const uint4 *>(k + e);
+            load8(d + e, dd[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < NU; ++i) {
+            const int u = tid + i * NT, r = u / G, g = u % G;
+            const uint32_t kw[4] = {ku[i].x, ku[i].y, ku[i].z, ku[i].w};
+            uint32_t kt[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) kt[e] = pack2(dd[i][2 * e] * bf_lo(kw[e]), dd[i][2 * e + 1] * bf_hi(kw[e]));
+            const uint32_t m = r < n ? 0xffffffffu : 0u;
+            *reinterpret_cast<uint4 *>(&sK[r * PH + 8 * g]) = make_uint4(kw[0] & m, kw[1] & m, kw[2] & m, kw[3] & m);
+            *reinterpret_cast<uint4 *>(&sKt[r * PH + 8 * g]) = make_uint4(kt[0] & m, kt[1] & m, kt[2] & m, kt[3] & m);
+        }
+    }
+    if (tid < 64) decay_scan<C>(beta, alpha, row0, n, sb, sg, sgam, sw, lane);
+    __syncthreads();
+    v4f ak[C / 16];  // this wave's rows of AS
+#pragma unroll
+    for (int t = 0; t < C / 16; ++t) {
+        ak[t] = zero4();
+        if (t <= wave) {
+#pragma unroll
+            for (int k0 = 0; k0 < DK; k0 += 32)
+                ak[t] = mfma32(frag_rows(sK, PH, R0, k0, lr, lq), frag_rows(sKt, PH, 16 * t, k0, lr, lq), ak[t]);
+        }
+    }
+    __syncthreads();  // K and K~ are dead: AS takes their bytes
+#pragma unroll
+    for (int t = 0; t < C / 16; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = R0 + 4 * lq + e, j = 16 * t + lr;
+            sAS[i * PC + j] = j < i ? ak[t][e] * __expf(sg[i] - sg[j]) : 0.f;
+        }
+    block_inverse64<PC>(sT, sAS, sb, sTmp, tid);  // its first barrier orders the AS writes
+    uint16_t *dst = Tck + (bh * nch + c) * (2 * C * C);
+    for (int u = tid; u < C * C / 4; u += NT) {  // four elements per thread and pass
+        const int r = u / (C / 4), j = 4 * (u % (C / 4));
+        uint32_t hw[2], lw[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const float x0 = sT[r * PC + j + 2 * e], x1 = sT[r * PC + j + 2 * e + 1];
+            hw[e] = pack2(x0, x1);
+            lw[e] = pack2(x0 - bf_lo(hw[e]), x1 - bf_hi(hw[e]));
+        }
+        *reinterpret_cast<uint2 *>(dst + r * C + j) = make_uint2(hw[0], hw[1]);
+        *reinterpret_cast<uint2 *>(dst + C * C + r * C + j) = make_uint2(lw[0], lw[1]);
+    }
+}
+
 // ---- reverse pass over chunks on bf16 matrix cores (bf16 inputs, C = 64) --------------------
-// Same data flow as bwd_state_kernel.  The score tiles, K~ dM, P^T dO and the dM update run on
-// 16x16 MFMA tiles (wave w owns rows 16w..16w+15 of the C-row products and rows 32w..32w+31
-// of dM); dR = (I + A)^{-T} dU is solved by 16-row blocks from the blocks' own inverses
-// D_i = (I + A_ii)^{-1} (fp32), four short steps instead of a 64-row chain.  dM stays fp32.
+// Same data flow as bwd_state_kernel.  The scores P, K~ dM, P^T dO and the dM update run on
+// 16x16 MFMA tiles (wave w owns rows 16w..16w+15 of the C-row products and rows 32w..32w+31 of
+// dM); dR = T^T dU takes the chunk's inverse T = (I + A)^{-1} from its hi/lo bf16 planes
+// (written by bwd_tinv_kernel) with dU split the same way, three products per k-step.  dM stays
+// fp32.  Five barriers per chunk.
 template <int DK, int BV, typename TD>
 __global__ void __launch_bounds__(NT)
 bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                       const TD *__restrict__ d, const float *__restrict__ beta,
                       const float *__restrict__ alpha, const bf16_t *__restrict__ dO,
-                      const float *__restrict__ dS_T, float *__restrict__ dMck,
-                      float *__restrict__ dS0, int64_t T, int dv) {
+                      const float *__restrict__ dS_T, const uint16_t *__restrict__ Tck,
+                      float *__restrict__ dMck, float *__restrict__ dS0, int64_t T, int dv) {
     constexpr int C = 64;
     constexpr int PH = DK + 8, PCH = C + 8, PVH = BV + 8;  // bf16 pitches
-    constexpr int PC = C + 1, PS = BV + 1, PD = 17;        // fp32 pitches
+    constexpr int PS = BV + 1;                             // fp32 pitch
     constexpr int NV = BV / 16;   // column tiles of the C x BV products
     constexpr int MR = DK / 64;   // 16-row tiles of dM per wave
     constexpr int G = DK / 8, NU = C * G / NT;  // 16-byte units of a Q/K row; units per thread
     constexpr int DU = sizeof(TD) == 4 ? 2 : 1;  // 16-byte units of d per unit of k
-    static_assert(NU * NT == C * G && NU <= 4 && C * BV / 8 == NT, "unit layout");
+    constexpr int TU = 2 * C * C / 8 / NT;       // 16-byte units of the T planes per thread
+    static_assert(NU * NT == C * G && NU <= 4 && C * BV / 8 == NT && TU == 4, "unit layout");
     __shared__ alignas(16) uint16_t sQ[C * PH], sK[C * PH], sKt[C * PH];
-    __shared__ float sAS[C * PC], sP[C * PC];
-    __shared__ alignas(16) uint16_t sPb[C * PCH];
+    __shared__ alignas(16) uint16_t sPb[C * PCH], sTh[C * PCH], sTl[C * PCH];
     __shared__ alignas(16) uint16_t sDOb[C * PVH], sGDOb[C * PVH], sGDRb[C * PVH];
+    __shared__ alignas(16) uint16_t sdUh[C * PVH], sdUl[C * PVH];
     __shared__ alignas(16) uint16_t sdMb[DK * PVH];  // bf16 copy of dM (operand of K~ dM)
-    __shared__ float sX[C * PS], sY16[16 * PS], sdM[DK * PS];
-    __shared__ float sD[4 * 16 * PD];  // D_i, block i at rows 16 i
+    __shared__ float sdM[DK * PS];
     __shared__ float sb[C], sg[C], sgam[C], sw[C];
 
     // workgroup -> (sequence, value slice); the slices of one sequence share an XCD (and its
-    // L2) when the sequence count allows it, so their re-reads of q, k, d hit L2
+    // L2) when the sequence count allows it, so their re-reads of q, k, d and T hit L2
     const int nvt = dv / BV;
     const int64_t nseq = gridDim.x / nvt;
     int64_t bh;
@@ -1163,10 +1243,12 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
     const int R0 = 16 * wave;
     const int64_t nch = (T + C - 1) / C;
 
-    // the next chunk's q, k, d, dO, beta, alpha, loaded into named registers one chunk ahead
-    // (an array carried across the loop would live in scratch); unit i of this thread is
-    // u = tid + i NT: row u / G, features 8 (u % G) .. +7
+    // the next chunk's q, k, d, dO, T planes, beta, alpha, loaded into named registers one
+    // chunk ahead (an array carried across the loop would live in scratch); unit i of this
+    // thread is u = tid + i NT: row u / G, features 8 (u % G) .. +7; T unit u holds elements
+    // 8u .. 8u + 7 of the two planes (plane u / 512, row (u / 8) % 64, columns 8 (u % 8) ..)
     uint4 q0, q1, q2, q3, k0r, k1r, k2r, k3r, dl0, dl1, dl2, dl3, dh0, dh1, dh2, dh3, ou;
+    uint4 t0, t1, t2, t3;
     float bv = 0.f, av = 1.f;
     auto qreg = [&](auto I) -> uint4 & {
         constexpr int i = decltype(I)::value;
@@ -1188,6 +1270,11 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
         if constexpr (i == 0) return dh0; else if constexpr (i == 1) return dh1;
         else if constexpr (i == 2) return dh2; else return dh3;
     };
+    auto treg = [&](auto I) -> uint4 & {
+        constexpr int i = decltype(I)::value;
+        if constexpr (i == 0) return t0; else if constexpr (i == 1) return t1;
+        else if constexpr (i == 2) return t2; else return t3;
+    };
     auto load_chunk = [&](int64_t cc) __attribute__((always_inline)) {
         const int64_t r0 = bh * T + cc * C;
         const int nn = static_cast<int>(T - cc * C < C ? T - cc * C : C);
@@ -1200,6 +1287,8 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             dlreg(I) = dp[0];
             if constexpr (DU == 2) dhreg(I) = dp[1];
         });
+        const uint4 *tp = reinterpret_cast<const uint4 *>(Tck + (bh * nch + cc) * (2 * C * C));
+        static_for<0, TU>([&](auto I) __attribute__((always_inline)) { treg(I) = tp[tid + I * NT]; });
         {
             const int r = tid / (BV / 8), j = 8 * (tid % (BV / 8));
             ou = *reinterpret_cast<const uint4 *>(dO + (r0 + (r < nn ? r : nn - 1)) * dv + j0 + j);
@@ -1221,7 +1310,8 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
         const int64_t c0 = c * C;
         const int n = static_cast<int>(T - c0 < C ? T - c0 : C);
         __syncthreads();  // the previous chunk is done with every buffer
-        // this chunk's registers into LDS: Q, K, K~ = d (.) k (bf16), dO; the decay scan
+        // this chunk's registers into LDS: Q, K, K~ = d (.) k (bf16), dO, the T planes; the
+        // decay scan
         static_for<0, NU>([&](auto I) __attribute__((always_inline)) {
             const int u = tid + I * NT, r = u / G, g = u % G;
             const uint32_t m = r < n ? 0xffffffffu : 0u;  // rows past the end are zero
@@ -1249,6 +1339,12 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             *reinterpret_cast<uint4 *>(&sK[r * PH + 8 * g]) = make_uint4(kw[0] & m, kw[1] & m, kw[2] & m, kw[3] & m);
             *reinterpret_cast<uint4 *>(&sKt[r * PH + 8 * g]) = make_uint4(kt[0] & m, kt[1] & m, kt[2] & m, kt[3] & m);
         });
+        static_for<0, TU>([&](auto I) __attribute__((always_inline)) {
+            constexpr int i = decltype(I)::value;
+            const int u = tid + i * NT, r = (u >> 3) & 63, g = u & 7;
+            uint16_t *dst = i < TU / 2 ? sTh : sTl;
+            *reinterpret_cast<uint4 *>(&dst[r * PCH + 8 * g]) = treg(I);
+        });
         {
             const int r = tid / (BV / 8), j = 8 * (tid % (BV / 8));
             const uint32_t m = r < n ? 0xffffffffu : 0u;
@@ -1267,9 +1363,11 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             sgam[lane] = __expf(x);
             sw[lane] = __expf(gl - x);
         }
-        for (int idx = tid; idx < DK * BV; idx += NT) {  // gradient at this chunk's end
-            const int f = idx / BV, j = idx % BV;
-            dMck[((bh * nch + c) * DK + f) * dv + j0 + j] = sdM[f * PS + j];
+        for (int u = tid; u < DK * BV / 4; u += NT) {  // gradient at this chunk's end
+            const int f = u / (BV / 4), j = 4 * (u % (BV / 4));
+            const float *src = &sdM[f * PS + j];
+            *reinterpret_cast<float4 *>(&dMck[((bh * nch + c) * DK + f) * dv + j0 + j]) =
+                make_float4(src[0], src[1], src[2], src[3]);
         }
         if (c > 0) load_chunk(c - 1);  // in flight through this chunk's work
         __syncthreads();
@@ -1282,28 +1380,22 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             for (int e = 0; e < 4; ++e) gw[e] = pack2(sgam[r] * bf_lo(w[e]), sgam[r] * bf_hi(w[e]));
             *reinterpret_cast<uint4 *>(&sGDOb[r * PVH + j]) = make_uint4(gw[0], gw[1], gw[2], gw[3]);
         }
-        // scores of this wave's rows (AS, P in fp32, P in bf16); K~ dM of this wave's rows
-        v4f kdm[NV];
+        // this wave's rows of P (bf16, zero above the diagonal) and of K~ dM
 #pragma unroll
         for (int t = 0; t < C / 16; ++t) {
-            v4f ak = zero4(), aq = zero4();
+            v4f aq = zero4();
             if (t <= wave) {
 #pragma unroll
-                for (int k0 = 0; k0 < DK; k0 += 32) {
-                    const v8s kt = frag_rows(sKt, PH, 16 * t, k0, lr, lq);
-                    ak = mfma32(frag_rows(sK, PH, R0, k0, lr, lq), kt, ak);
-                    aq = mfma32(frag_rows(sQ, PH, R0, k0, lr, lq), kt, aq);
-                }
+                for (int k0 = 0; k0 < DK; k0 += 32)
+                    aq = mfma32(frag_rows(sQ, PH, R0, k0, lr, lq), frag_rows(sKt, PH, 16 * t, k0, lr, lq), aq);
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = R0 + 4 * lq + e, j = 16 * t + lr;
-                const float Gd = j <= i ? __expf(sg[i] - sg[j]) : 0.f;
-                sAS[i * PC + j] = j < i ? ak[e] * Gd : 0.f;
-                sP[i * PC + j] = aq[e] * Gd;
-                sPb[i * PCH + j] = bf16_bits(aq[e] * Gd);
+                sPb[i * PCH + j] = bf16_bits(j <= i ? aq[e] * __expf(sg[i] - sg[j]) : 0.f);
             }
         }
+        v4f kdm[NV];
 #pragma unroll
         for (int t = 0; t < NV; ++t) {
             kdm[t] = zero4();
@@ -1313,7 +1405,7 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
                                 frag_cols(sdMb, PVH, k0, 16 * t, lr, lq), kdm[t]);
         }
         __syncthreads();
-        // dU = P^T dO + diag(w) K~ dM into sX; the diagonal blocks' inverses D_i into sD
+        // dU = P^T dO + diag(w) K~ dM, as hi/lo bf16 planes
 #pragma unroll
         for (int t = 0; t < NV; ++t) {
             v4f du = zero4();
@@ -1324,64 +1416,34 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = R0 + 4 * lq + e, j = 16 * t + lr;
-                sX[r * PS + j] = du[e] + sw[r] * kdm[t][e];
+                const float x = du[e] + sw[r] * kdm[t][e];
+                const uint16_t h = bf16_bits(x);
+                sdUh[r * PVH + j] = h;
+                sdUl[r * PVH + j] = bf16_bits(x - __uint_as_float(uint32_t(h) << 16));
             }
-        }
-        {  // column jj of D_blk by forward substitution, four adjacent lanes per column
-            const int blk = tid >> 6, jj = (tid >> 2) & 15, sub = tid & 3, rb = 16 * blk;
-            float mine[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float part = 0.f;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if (4 * i < r) {
-                        const int s2 = 4 * i + sub;
-                        if (s2 < r) part += sAS[(rb + r) * PC + rb + s2] * mine[i];
-                    }
-                }
-                part += __shfl_xor(part, 1);
-                part += __shfl_xor(part, 2);
-                const float val = (r == jj ? 1.f : 0.f) - sb[rb + r] * part;
-                if (r % 4 == sub) mine[r / 4] = val;
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sD[(rb + 4 * i + sub) * PD + jj] = mine[i];
         }
         __syncthreads();
-        // dR = (I + A)^{-T} dU by blocks i = 3..0: y = dU_i - sum_{k>i} A_ki^T dR_k, then
-        // dR_i = D_i^T y (in place in sX)
-        for (int ib = 3; ib >= 0; --ib) {
-            const int rb = 16 * ib;
-            if (wave < NV) {  // wave t: columns 16t..16t+15 of the block
-                v4f y = zero4();
-                if (ib < 3) {
-                    y = mtile_split<64>(zero4(), 0, 16 * wave, lr, lq,
-                                        [&](int r, int s2) {
-                                            return s2 >= rb + 16 ? sb[s2] * sAS[s2 * PC + rb + r] : 0.f;
-                                        },
-                                        [&](int s2, int j) { return s2 >= rb + 16 ? sX[s2 * PS + j] : 0.f; });
-                }
+        // dR = T^T dU (T^T upper triangular: k-steps from this wave's first row on), and
+        // -diag(gam b) dR in bf16 for the dM update
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * lq + e, j = 16 * wave + lr;
-                    sY16[r * PS + j] = sX[(rb + r) * PS + j] - y[e];
-                }
-            }
-            __syncthreads();
-            if (wave < NV) {  // dR_i = D_i^T y: 16 x 16 times 16 x 16, padded to K = 32
-                const v4f dr = mtile_split<32>(zero4(), 0, 16 * wave, lr, lq,
-                                               [&](int r, int r2) { return r2 < 16 ? sD[(rb + r2) * PD + r] : 0.f; },
-                                               [&](int r2, int j) { return r2 < 16 ? sY16[r2 * PS + j] : 0.f; });
+        for (int t = 0; t < NV; ++t) {
+            v4f dr = zero4();
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = rb + 4 * lq + e, j = 16 * wave + lr;
-                    sX[r * PS + j] = dr[e];
-                    sGDRb[r * PVH + j] = bf16_bits(-sgam[r] * sb[r] * dr[e]);
-                }
+            for (int k0 = 0; k0 < C; k0 += 32) {
+                if (k0 + 32 <= R0) continue;
+                const v8s th = frag_cols(sTh, PCH, k0, R0, lr, lq), tl = frag_cols(sTl, PCH, k0, R0, lr, lq);
+                const v8s uh = frag_cols(sdUh, PVH, k0, 16 * t, lr, lq), ul = frag_cols(sdUl, PVH, k0, 16 * t, lr, lq);
+                dr = mfma32(th, uh, dr);
+                dr = mfma32(th, ul, dr);
+                dr = mfma32(tl, uh, dr);
             }
-            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = R0 + 4 * lq + e, j = 16 * t + lr;
+                sGDRb[r * PVH + j] = bf16_bits(-sgam[r] * sb[r] * dr[e]);
+            }
         }
+        __syncthreads();
         // dM <- gam_L dM + Q^T diag(gam) dO - K^T diag(gam b) dR (this wave's rows of dM)
         {
             const float gl = sgam[C - 1];
@@ -1432,13 +1494,21 @@ hipError_t bwd_typed(const BwdArgs &a, hipStream_t stream) {
         if (e != hipSuccess) return e;
     }
     constexpr int BVA = 32;  // value slice of the reverse pass
-    if constexpr (sizeof(TQ) == 2)
+    if constexpr (sizeof(TQ) == 2) {
+        if (nch > 0) {
+            hipLaunchKernelGGL((bwd_tinv_kernel<DK, TD>), dim3(static_cast<unsigned>(a.BH * nch)),
+                               dim3(NT), 0, stream, static_cast<const bf16_t *>(a.k),
+                               static_cast<const TD *>(a.d), a.beta, a.alpha, a.Tck, a.T, nch);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
         hipLaunchKernelGGL((bwd_state_mfma_kernel<DK, BVA, TD>),
                            dim3(static_cast<unsigned>(a.BH * (DV / BVA))), dim3(NT), 0, stream,
                            static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.k),
                            static_cast<const TD *>(a.d), a.beta, a.alpha,
-                           static_cast<const bf16_t *>(a.dO), a.dS_T, a.dMck, a.dS0, a.T, DV);
-    else
+                           static_cast<const bf16_t *>(a.dO), a.dS_T, a.Tck, a.dMck, a.dS0,
+                           a.T, DV);
+    } else
     hipLaunchKernelGGL((bwd_state_kernel<C, DK, BVA, TQ, TD>),
                        dim3(static_cast<unsigned>(a.BH * (DV / BVA))), dim3(NT), 0, stream,
                        static_cast<const TQ *>(a.q), static_cast<const TQ *>(a.k),
@@ -1453,7 +1523,7 @@ hipError_t bwd_typed(const BwdArgs &a, hipStream_t stream) {
                            static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.k),
                            static_cast<const bf16_t *>(a.v), static_cast<const TD *>(a.d),
                            a.beta, a.alpha, static_cast<const bf16_t *>(a.dO), a.Mck, a.dMck,
-                           static_cast<bf16_t *>(a.gq), static_cast<bf16_t *>(a.gk),
+                           a.Tck, static_cast<bf16_t *>(a.gq), static_cast<bf16_t *>(a.gk),
                            static_cast<bf16_t *>(a.gv), a.gbeta, static_cast<TD *>(a.gd),
                            a.galpha, a.T, nch);
         return hipGetLastError();

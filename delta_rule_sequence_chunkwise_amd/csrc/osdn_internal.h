@@ -56,6 +56,8 @@ struct BwdArgs {
     void *gd;             // d dtype
     float *dS0;
     float *Mck, *dMck;    // workspace: [BH, nchunks, dk, dv] each
+    uint16_t *Tck;        // workspace (bf16 inputs): (I + A)^{-1} of every chunk, [BH, nchunks,
+                          // 2, 64, 64] bf16, planes hi = bf16(T) and lo = bf16(T - hi)
     int64_t BH, T;
     int32_t dk, dv;
     osdn_dtype qkv, d_dtype;

@@ -204,9 +204,11 @@ osdn_status osdn_step_kda(const void *q, const void *k, const void *v, const flo
  *                             aligned; contents on entry ignored, on return unspecified
  * Every other argument as for osdn_chunk_fwd; the chunk size is the library's (64 rows for
  * bf16 inputs, 32 for fp32).  Outputs must not overlap each other, an input or the workspace.
- * Three kernels run on `stream`: the forward recording the state at every chunk start (the same
- * forward osdn_chunk_fwd runs for this input type), a reverse pass over chunks for the state
- * gradient, and the per-chunk gradients.
+ * Kernels run on `stream`: the forward recording the state at every chunk start (the same
+ * forward osdn_chunk_fwd runs for this input type), for bf16 inputs the inverse (I + A)^{-1} of
+ * every chunk, a reverse pass over chunks for the state gradient, and the per-chunk gradients.
+ * The workspace holds the state and state-gradient checkpoints (fp32, [B,H,nchunks,dk,dv]
+ * each) and, for bf16 inputs, the chunk inverses (two bf16 planes of 64 x 64 per chunk).
  */
 int64_t osdn_chunk_bwd_workspace(int64_t B, int64_t H, int64_t T, int32_t dk, int32_t dv,
                                  osdn_dtype qkv); /* -1 if invalid */
