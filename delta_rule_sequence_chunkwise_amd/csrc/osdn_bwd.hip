@@ -621,14 +621,6 @@ bwd_chunk_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k, const TQ *_
     }
 }
 
-// ---- per-chunk gradients on bf16 matrix cores (bf16 inputs, C = 64) ---------------------------
-// Same data flow as bwd_chunk_kernel.  Wave w owns rows 16w..16w+15 of every product, as 16x16
-// fp32 tiles in the MFMA C layout (lane (q, n) holds rows 4q..4q+3 of column n); operand
-// fragments are 16-byte or transposing reads of bf16 LDS tiles (K steps of 32, or 16 for the
-// value-slice contractions).  U = T R and dR = T^T dU take T from its hi/lo planes and R, dU
-// split the same way (hi.hi + hi.lo + lo.hi: fp32 accuracy; the dropped lo.lo term is below
-// 2^-16 of the product).  Every row or column sum stays fp32.
-
 // bf16 MFMA fragments from bf16 row-major LDS tiles (pitch a multiple of 8 elements):
 // rows: lane (q, n) gets X[r0 + n][k0 + 8q .. +7] (one 16-byte read);
 // cols: lane (q, n) gets X[k0 + 8q .. +7][c0 + n] (two transposing reads)
@@ -639,71 +631,76 @@ __device__ __forceinline__ v8s frag_cols(const uint16_t *X, int pitch, int k0, i
     const int kb = k0 + 8 * lq, c = c0 + 4 * (lr & 3), r = lr >> 2;
     return cat8(ld_tr(&X[(kb + r) * pitch + c]), ld_tr(&X[(kb + 4 + r) * pitch + c]));
 }
-// the 16-deep row form: lane (q, n) gets X[r0 + n][k0 + 4q .. +3]
-__device__ __forceinline__ v4s frag4_rows(const uint16_t *X, int pitch, int r0, int k0, int lr, int lq) {
-    return ld4s(&X[(r0 + lr) * pitch + k0 + 4 * lq]);
-}
-// tile += A B over K (a multiple of 16), fragments from callables fa(k0) / fb(k0) that return
-// the 32-deep (v8s) or, for K == 16, the 16-deep (v4s) fragment at k0
-template <int K, typename FA, typename FB, typename FA4, typename FB4>
-__device__ __forceinline__ v4f ftile(v4f acc, FA &&fa, FB &&fb, FA4 &&fa4, FB4 &&fb4) {
-    if constexpr (K == 16) {
-        return mfma16(fa4(0), fb4(0), acc);
-    } else {
-        static_assert(K % 32 == 0, "K steps of 32");
-#pragma unroll
-        for (int k0 = 0; k0 < K; k0 += 32) acc = mfma32(fa(k0), fb(k0), acc);
-        return acc;
-    }
-}
 __device__ __forceinline__ uint16_t bf16_bits(float x) { return f32_to_bf16_bits(x); }
 
-template <int DK, int DV, int BV, typename TD>
-__global__ void __launch_bounds__(NT)
+// ---- per-chunk gradients on bf16 matrix cores (bf16 inputs, C = 64) ---------------------------
+// Same data flow as bwd_chunk_kernel, on eight waves (two per SIMD, so one wave's LDS and
+// memory waits overlap the other's matrix work).  Wave (rw, hw) = (wave % 4, wave / 4) owns
+// rows 16rw..16rw+15 of every product; of the 32-column value slice it takes columns
+// 16hw..16hw+15, of the dk x C and C x C gradient tiles the feature tiles of half hw and the
+// score tiles t = hw, hw + 2.  Products are 16x16 fp32 tiles in the MFMA C layout (lane (q, n)
+// holds rows 4q..4q+3 of column n); operand fragments are 16-byte or transposing reads of bf16
+// LDS tiles.  U = T R and dR = T^T dU take T from its hi/lo planes and R, dU split the same
+// way (hi.hi + hi.lo + lo.hi: fp32 accuracy; the dropped lo.lo term is below 2^-16 of the
+// product).  The row sums of the decay and beta gradients stay in registers as per-lane fp32
+// partials across the slices and are reduced once at the end.
+template <int DK, int DV, typename TD>
+__global__ void __launch_bounds__(2 * NT)
 bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                       const bf16_t *__restrict__ v, const TD *__restrict__ d,
                       const float *__restrict__ beta, const float *__restrict__ alpha,
                       const bf16_t *__restrict__ dO, const float *__restrict__ Mck,
                       const float *__restrict__ dMck, const uint16_t *__restrict__ Tck,
-                      bf16_t *__restrict__ gq,
-                      bf16_t *__restrict__ gk, bf16_t *__restrict__ gv,
+                      bf16_t *__restrict__ gq, bf16_t *__restrict__ gk, bf16_t *__restrict__ gv,
                       float *__restrict__ gbeta, TD *__restrict__ gd,
                       float *__restrict__ galpha, int64_t T, int64_t nch) {
-    constexpr int C = 64;
+    constexpr int C = 64, BV = 32, NW = 8, NTH = NW * 64;
     constexpr int PH = DK + 8, PCH = C + 8, PVH = BV + 8;  // bf16 pitches
-    constexpr int PS = BV + 1;                             // fp32 pitch
-    constexpr int NF = DK / 16, NV = BV / 16;
+    constexpr int NF = DK / 16, NFH = NF / 2;  // feature tiles; per half
     constexpr int MB = 2 * DK * PVH > C * PCH ? 2 * DK * PVH : C * PCH;
+    constexpr int MU = DK * BV / 4 / NTH;      // float4 units of an M0 (dMC) slice per thread
+    static_assert(MU == 1 || MU == 2, "one or two M units per thread");
+    static_assert(C * BV / 4 == NTH, "one 4-value unit of v and dO per thread");
     __shared__ alignas(16) uint16_t sQ[C * PH], sK[C * PH], sKt[C * PH];
     __shared__ alignas(16) uint16_t sPb[C * PCH];  // P, later dP o G (bf16)
     __shared__ alignas(16) uint16_t sTh[C * PCH], sTl[C * PCH];  // T = (I + A)^{-1}: hi, lo
     __shared__ alignas(16) uint16_t sMb[MB];       // M0 and dMC slices, later Gb (bf16)
     __shared__ alignas(16) uint16_t sDOb[C * PVH], sGDOb[C * PVH], sUb[C * PVH], sWUb[C * PVH];
     __shared__ alignas(16) uint16_t sDRb[C * PVH], sGDRb[C * PVH];
-    __shared__ alignas(16) uint16_t sRh[C * PVH], sRl[C * PVH], sdUh[C * PVH], sdUl[C * PVH];
-    __shared__ float sY[C * PS], sU[C * PS], sdR[C * PS];
-    __shared__ float sb[C], sg[C], sgam[C], sw[C], sdb[C], sdg[C], sew[C], sred[4];
+    __shared__ alignas(16) uint16_t sRh[C * PVH], sRl[C * PVH];  // V, then R (hi, lo)
+    __shared__ alignas(16) uint16_t sdUh[C * PVH], sdUl[C * PVH];
+    __shared__ float sb[C], sg[C], sgam[C], sw[C];
+    __shared__ float srow[2][6][C];  // per-half row sums: go, gr, ew, db, rowp, rowb
+    __shared__ float scol[4][C];     // column sums of the decay term, by row block
+    __shared__ float sred[NW];
     uint16_t *const sM0b = sMb, *const sdMb = sMb + DK * PVH;
 
     const int64_t bh = blockIdx.x / nch, c = blockIdx.x % nch;
     const int64_t c0 = c * C, row0 = bh * T + c0;
     const int n = static_cast<int>(T - c0 < C ? T - c0 : C);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int rw = wave & 3, hw = wave >> 2;
     const int lr = lane & 15, lq = lane >> 4;
-    const int R0 = 16 * wave;  // this wave's rows
+    const int R0 = 16 * rw;  // this wave's rows
+    const int jt = 16 * hw;  // this wave's columns of the value slice
     const float *M0 = Mck + (bh * nch + c) * DK * DV;
     const float *dMC = dMck + (bh * nch + c) * DK * DV;
+    // the chunk's rows of every per-token array: uniform bases, 32-bit offsets
+    const bf16_t *vc = v + row0 * DV, *oc = dO + row0 * DV;
+    bf16_t *gvc = gv + row0 * DV, *gqc = gq + row0 * DK, *gkc = gk + row0 * DK;
+    TD *gdc = gd + row0 * DK;
+    const TD *dc = d + row0 * DK;
 
     {  // Q, K, K~ = d (.) k as bf16 (8 features per 16-byte unit) and the T planes, all loads
        // issued first
-        constexpr int G = DK / 8, NU = C * G / NT;  // units per row, units per thread
-        constexpr int TU = 2 * C * C / 8 / NT;      // 16-byte units of the T planes per thread
-        static_assert(NU * NT == C * G && TU * NT * 8 == 2 * C * C, "whole units");
+        constexpr int G = DK / 8, NU = C * G / NTH;  // units per row, units per thread
+        constexpr int TU = 2 * C * C / 8 / NTH;      // 16-byte units of the T planes per thread
+        static_assert(NU * NTH == C * G && TU == 2, "whole units");
         uint4 qu[NU], ku[NU], tu[TU];
         float dd[NU][8];
 #pragma unroll
         for (int i = 0; i < NU; ++i) {
-            const int u = tid + i * NT, r = u / G, g = u % G;
+            const int u = tid + i * NTH, r = u / G, g = u % G;
             const int64_t e = (row0 + (r < n ? r : n - 1)) * DK + 8 * g;
             qu[i] = *reinterpret_cast<const uint4 *>(q + e);
             ku[i] = *reinterpret_cast<const uint4 *>(k + e);
@@ -711,21 +708,20 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
         }
         const uint4 *tp = reinterpret_cast<const uint4 *>(Tck + (bh * nch + c) * (2 * C * C));
 #pragma unroll
-        for (int i = 0; i < TU; ++i) tu[i] = tp[tid + i * NT];
+        for (int i = 0; i < TU; ++i) tu[i] = tp[tid + i * NTH];
 #pragma unroll
         for (int i = 0; i < TU; ++i) {  // unit u: plane u / 512, row (u / 8) % 64, columns 8 (u % 8) ..
-            const int u = tid + i * NT, r = (u >> 3) & 63, g = u & 7;
-            *reinterpret_cast<uint4 *>(&(i < TU / 2 ? sTh : sTl)[r * PCH + 8 * g]) = tu[i];
+            const int u = tid + i * NTH, r = (u >> 3) & 63, g = u & 7;
+            *reinterpret_cast<uint4 *>(&(i == 0 ? sTh : sTl)[r * PCH + 8 * g]) = tu[i];
         }
 #pragma unroll
         for (int i = 0; i < NU; ++i) {
-            const int u = tid + i * NT, r = u / G, g = u % G;
-            const bool ok = r < n;
+            const int u = tid + i * NTH, r = u / G, g = u % G;
             const uint32_t kw[4] = {ku[i].x, ku[i].y, ku[i].z, ku[i].w};
             uint32_t kt[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) kt[e] = pack2(dd[i][2 * e] * bf_lo(kw[e]), dd[i][2 * e + 1] * bf_hi(kw[e]));
-            const uint32_t m = ok ? 0xffffffffu : 0u;  // rows past the end are zero
+            const uint32_t m = r < n ? 0xffffffffu : 0u;  // rows past the end are zero
             *reinterpret_cast<uint4 *>(&sQ[r * PH + 8 * g]) =
                 make_uint4(qu[i].x & m, qu[i].y & m, qu[i].z & m, qu[i].w & m);
             *reinterpret_cast<uint4 *>(&sK[r * PH + 8 * g]) = make_uint4(kw[0] & m, kw[1] & m, kw[2] & m, kw[3] & m);
@@ -733,15 +729,13 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
         }
     }
     if (tid < 64) decay_scan<C>(beta, alpha, row0, n, sb, sg, sgam, sw, lane);
-    if (tid < C) sdb[tid] = sdg[tid] = sew[tid] = 0.f;
     __syncthreads();
-    // the score tiles of this wave's rows: AS = strictly lower (K K~^T) o G and P =
-    // lower-inclusive (Q K~^T) o G, in the C layout of tile t (columns 16t..16t+15); P also
-    // into LDS as bf16 for the slices
+    // score tile t of this wave's rows: AS = strictly lower (K K~^T) o G and P =
+    // lower-inclusive (Q K~^T) o G in the C layout (zero for tiles above the diagonal)
     auto score_tiles = [&](int t, v4f &ak, v4f &aq) __attribute__((always_inline)) {
         ak = zero4();
         aq = zero4();
-        if (t <= wave) {
+        if (t <= rw) {
 #pragma unroll
             for (int k0 = 0; k0 < DK; k0 += 32) {
                 const v8s kt = frag_rows(sKt, PH, 16 * t, k0, lr, lq);
@@ -757,10 +751,11 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             aq[e] = aq[e] * G;
         }
     };
-#pragma unroll
-    for (int t = 0; t < C / 16; ++t) {  // P only (AS is formed again where it is used)
+    // P of this wave's score tiles into LDS (bf16) for the slices; AS is formed again at the end
+    static_for<0, 2>([&](auto I) __attribute__((always_inline)) {
+        const int t = 2 * I + hw;
         v4f aq = zero4();
-        if (t <= wave) {
+        if (t <= rw) {
 #pragma unroll
             for (int k0 = 0; k0 < DK; k0 += 32)
                 aq = mfma32(frag_rows(sQ, PH, R0, k0, lr, lq), frag_rows(sKt, PH, 16 * t, k0, lr, lq), aq);
@@ -770,24 +765,23 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             const int i = R0 + 4 * lq + e, j = 16 * t + lr;
             sPb[i * PCH + j] = bf16_bits(j <= i ? aq[e] * __expf(sg[i] - sg[j]) : 0.f);
         }
-    }
-    __syncthreads();
+    });
 
-    v4f aQ[NF], aK[NF], aKt[NF], adP[C / 16], adA[C / 16];
+    v4f aQ[NFH], aK[NFH], aKt[NFH], adP[2], adA[2];
 #pragma unroll
-    for (int t = 0; t < NF; ++t) aQ[t] = aK[t] = aKt[t] = zero4();
-#pragma unroll
-    for (int t = 0; t < C / 16; ++t) adP[t] = adA[t] = zero4();
+    for (int t = 0; t < NFH; ++t) aQ[t] = aK[t] = aKt[t] = zero4();
+    adP[0] = adP[1] = adA[0] = adA[1] = zero4();
+    // per-lane partial row sums over the value columns: <dO_r, (Q M0)_r>, <dR_r, (K M0)_r>,
+    // <(K~ dMC)_r, U_r>, <dR_r, Y_r> for rows R0 + 4 lq + e
+    float pgo[4] = {0.f, 0.f, 0.f, 0.f}, pgr[4] = {0.f, 0.f, 0.f, 0.f};
+    float pew[4] = {0.f, 0.f, 0.f, 0.f}, pdb[4] = {0.f, 0.f, 0.f, 0.f};
     float frob = 0.f;
 
-    // the value slice's M0, dMC (fp32, four per 16-byte unit) and v, dO (bf16, eight per unit)
-    // pass through registers one slice ahead: units u = tid + i NT
-    constexpr int MU = DK * BV / 4 / NT, VU = C * BV / 8;  // per thread / per workgroup
-    static_assert(MU * NT * 4 == DK * BV && VU <= NT, "slice units");
-    static_assert(MU == 1 || MU == 2, "one or two M units per thread");
-    // named registers (an array carried across the loop would live in scratch)
+    // the value slice's M0, dMC (fp32, four per 16-byte unit) and v, dO (bf16, four per 8-byte
+    // unit) pass through named registers one slice ahead (an array carried across the loop
+    // would live in scratch)
     float4 m0a = make_float4(0.f, 0.f, 0.f, 0.f), m0b = m0a, dma = m0a, dmb = m0a;
-    uint4 vu = make_uint4(0, 0, 0, 0), ou = make_uint4(0, 0, 0, 0);
+    uint2 vu = make_uint2(0, 0), ou = make_uint2(0, 0);
 #define OSDN_BWD_LOAD_SLICE(S0)                                                               \
     do {                                                                                      \
         {                                                                                     \
@@ -796,24 +790,25 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             dma = *reinterpret_cast<const float4 *>(dMC + f * DV + (S0) + j);                 \
         }                                                                                     \
         if constexpr (MU == 2) {                                                              \
-            const int u = tid + NT, f = u / (BV / 4), j = 4 * (u % (BV / 4));                \
+            const int u = tid + NTH, f = u / (BV / 4), j = 4 * (u % (BV / 4));               \
             m0b = *reinterpret_cast<const float4 *>(M0 + f * DV + (S0) + j);                  \
             dmb = *reinterpret_cast<const float4 *>(dMC + f * DV + (S0) + j);                 \
         }                                                                                     \
-        if (tid < VU) {                                                                       \
-            const int r = tid / (BV / 8), j = 8 * (tid % (BV / 8));                          \
-            const int64_t e = (row0 + (r < n ? r : n - 1)) * DV + (S0) + j;                   \
-            vu = *reinterpret_cast<const uint4 *>(v + e);                                     \
-            ou = *reinterpret_cast<const uint4 *>(dO + e);                                    \
+        {                                                                                     \
+            const int r = tid / (BV / 4), j = 4 * (tid % (BV / 4));                          \
+            const int e = (r < n ? r : n - 1) * DV + (S0) + j;                                \
+            vu = *reinterpret_cast<const uint2 *>(vc + e);                                    \
+            ou = *reinterpret_cast<const uint2 *>(oc + e);                                    \
         }                                                                                     \
     } while (0)
     OSDN_BWD_LOAD_SLICE(0);
 
+#pragma unroll 1
     for (int s0 = 0; s0 < DV; s0 += BV) {
-        __syncthreads();  // the previous slice (and T) are done
+        __syncthreads();  // the previous slice (and the scores) are done
 #pragma unroll
         for (int i = 0; i < MU; ++i) {
-            const int u = tid + i * NT, f = u / (BV / 4), j = 4 * (u % (BV / 4));
+            const int u = tid + i * NTH, f = u / (BV / 4), j = 4 * (u % (BV / 4));
             const float4 mm4 = i == 0 ? m0a : m0b, dd4 = i == 0 ? dma : dmb;
             *reinterpret_cast<uint2 *>(&sM0b[f * PVH + j]) =
                 make_uint2(pack2(mm4.x, mm4.y), pack2(mm4.z, mm4.w));
@@ -821,288 +816,237 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
                 make_uint2(pack2(dd4.x, dd4.y), pack2(dd4.z, dd4.w));
             frob += mm4.x * dd4.x + mm4.y * dd4.y + mm4.z * dd4.z + mm4.w * dd4.w;
         }
-        if (tid < VU) {
-            const int r = tid / (BV / 8), j = 8 * (tid % (BV / 8));
-            const bool ok = r < n;
-            const uint32_t vw[4] = {vu.x, vu.y, vu.z, vu.w}, ow[4] = {ou.x, ou.y, ou.z, ou.w};
-            uint32_t gw[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sY[r * PS + j + 2 * e] = ok ? bf_lo(vw[e]) : 0.f;
-                sY[r * PS + j + 2 * e + 1] = ok ? bf_hi(vw[e]) : 0.f;
-                gw[e] = pack2(sgam[r] * bf_lo(ow[e]), sgam[r] * bf_hi(ow[e]));
-            }
-            const uint32_t m = ok ? 0xffffffffu : 0u;  // rows past the end are zero
-            *reinterpret_cast<uint4 *>(&sDOb[r * PVH + j]) = make_uint4(ow[0] & m, ow[1] & m, ow[2] & m, ow[3] & m);
-            *reinterpret_cast<uint4 *>(&sGDOb[r * PVH + j]) = make_uint4(gw[0] & m, gw[1] & m, gw[2] & m, gw[3] & m);
+        {  // v into sRh (R replaces it in place), dO and gam dO; rows past the end are zero
+            const int r = tid / (BV / 4), j = 4 * (tid % (BV / 4));
+            const uint32_t m = r < n ? 0xffffffffu : 0u;
+            *reinterpret_cast<uint2 *>(&sRh[r * PVH + j]) = make_uint2(vu.x & m, vu.y & m);
+            *reinterpret_cast<uint2 *>(&sDOb[r * PVH + j]) = make_uint2(ou.x & m, ou.y & m);
+            const float gm = sgam[r];
+            *reinterpret_cast<uint2 *>(&sGDOb[r * PVH + j]) =
+                make_uint2(pack2(gm * bf_lo(ou.x), gm * bf_hi(ou.x)) & m,
+                           pack2(gm * bf_lo(ou.y), gm * bf_hi(ou.y)) & m);
         }
         if (s0 + BV < DV) OSDN_BWD_LOAD_SLICE(s0 + BV);  // in flight through this slice's work
         __syncthreads();
-        // K M0, Q M0, K~ dMC on this slice, kept in registers (this wave's rows); Y = V - gam
-        // K M0 and R = b Y into LDS; the read-out row sums <dO_r, (Q M0)_r>
-        v4f km[NV], kdm[NV];
-        float go[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int t = 0; t < NV; ++t) {
-            v4f qm = zero4();
-            km[t] = kdm[t] = zero4();
-#pragma unroll
-            for (int k0 = 0; k0 < DK; k0 += 32) {
-                const v8s m0f = frag_cols(sM0b, PVH, k0, 16 * t, lr, lq);
-                km[t] = mfma32(frag_rows(sK, PH, R0, k0, lr, lq), m0f, km[t]);
-                qm = mfma32(frag_rows(sQ, PH, R0, k0, lr, lq), m0f, qm);
-                kdm[t] = mfma32(frag_rows(sKt, PH, R0, k0, lr, lq),
-                                frag_cols(sdMb, PVH, k0, 16 * t, lr, lq), kdm[t]);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = R0 + 4 * lq + e, j = 16 * t + lr;
-                go[e] += __uint_as_float(uint32_t(sDOb[r * PVH + j]) << 16) * qm[e];
-                const float y = sY[r * PS + j] - sgam[r] * km[t][e];
-                sY[r * PS + j] = y;
-                const float x = sb[r] * y;  // R, as hi/lo bf16
-                const uint16_t h = bf16_bits(x);
-                sRh[r * PVH + j] = h;
-                sRl[r * PVH + j] = bf16_bits(x - __uint_as_float(uint32_t(h) << 16));
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int t = 0; t < NV; ++t) {  // U = T R (hi.hi + hi.lo + lo.hi), with its bf16 copies
-            v4f u = zero4();
-#pragma unroll
-            for (int k0 = 0; k0 < C; k0 += 32) {
-                if (k0 > R0 + 15) continue;  // T lower triangular
-                const v8s th = frag_rows(sTh, PCH, R0, k0, lr, lq), tl = frag_rows(sTl, PCH, R0, k0, lr, lq);
-                const v8s rh = frag_cols(sRh, PVH, k0, 16 * t, lr, lq), rl = frag_cols(sRl, PVH, k0, 16 * t, lr, lq);
-                u = mfma32(th, rh, u);
-                u = mfma32(th, rl, u);
-                u = mfma32(tl, rh, u);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = R0 + 4 * lq + e, j = 16 * t + lr;
-                sU[r * PS + j] = u[e];
-                sUb[r * PVH + j] = bf16_bits(u[e]);
-                sWUb[r * PVH + j] = bf16_bits(sw[r] * u[e]);
-            }
-        }
-#pragma unroll
-        for (int t = 0; t < NV; ++t) {  // dU = P^T dO + diag(w) K~ dMC
-            v4f du = zero4();
-#pragma unroll
-            for (int k0 = 0; k0 < C; k0 += 32)
-                du = mfma32(frag_cols(sPb, PCH, k0, R0, lr, lq),
-                            frag_cols(sDOb, PVH, k0, 16 * t, lr, lq), du);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = R0 + 4 * lq + e, j = 16 * t + lr;
-                const float x = du[e] + sw[r] * kdm[t][e];  // as hi/lo bf16
-                const uint16_t h = bf16_bits(x);
-                sdUh[r * PVH + j] = h;
-                sdUl[r * PVH + j] = bf16_bits(x - __uint_as_float(uint32_t(h) << 16));
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int t = 0; t < NV; ++t) {  // dR = T^T dU (hi.hi + hi.lo + lo.hi), with copies
-            v4f dr = zero4();
-#pragma unroll
-            for (int k0 = 0; k0 < C; k0 += 32) {
-                if (k0 + 32 <= R0) continue;  // T^T upper triangular
-                const v8s th = frag_cols(sTh, PCH, k0, R0, lr, lq), tl = frag_cols(sTl, PCH, k0, R0, lr, lq);
-                const v8s uh = frag_cols(sdUh, PVH, k0, 16 * t, lr, lq), ul = frag_cols(sdUl, PVH, k0, 16 * t, lr, lq);
-                dr = mfma32(th, uh, dr);
-                dr = mfma32(th, ul, dr);
-                dr = mfma32(tl, uh, dr);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = R0 + 4 * lq + e, j = 16 * t + lr;
-                sdR[r * PS + j] = dr[e];
-                sDRb[r * PVH + j] = bf16_bits(dr[e]);
-                sGDRb[r * PVH + j] = bf16_bits(-sgam[r] * sb[r] * dr[e]);
-            }
-        }
-        __syncthreads();
-        for (int idx = tid; idx < C * BV; idx += NT) {
-            const int r = idx / BV, j = idx % BV;
-            if (r < n) gv[(row0 + r) * DV + s0 + j] = from_f32<bf16_t>(sb[r] * sdR[r * PS + j]);
-        }
-        {  // row sums of this slice: <dR_r, Y_r>, <dR_r, (K M0)_r>, <(K~ dMC)_r, U_r>
-            float gr[4] = {0.f, 0.f, 0.f, 0.f}, ew[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int t = 0; t < NV; ++t)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = R0 + 4 * lq + e, j = 16 * t + lr;
-                    gr[e] += sdR[r * PS + j] * km[t][e];
-                    ew[e] += kdm[t][e] * sU[r * PS + j];
-                }
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-#pragma unroll
-                for (int m = 1; m < 16; m <<= 1) {
-                    go[e] += __shfl_xor(go[e], m);
-                    gr[e] += __shfl_xor(gr[e], m);
-                    ew[e] += __shfl_xor(ew[e], m);
-                }
-            if (lr == 0) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = R0 + 4 * lq + e;
-                    sdg[r] += sgam[r] * go[e] - sb[r] * sgam[r] * gr[e];
-                    sew[r] += sw[r] * ew[e];
-                }
-            }
-            if (tid < C) {
-                const int r = tid;
-                float db = 0.f;
-                for (int j = 0; j < BV; ++j) db += sdR[r * PS + j] * sY[r * PS + j];
-                sdb[r] += db;
-            }
-        }
-        // dP += dO U^T, dA += dR U^T (negated later), and the slice's part of dQ, dK, dK~
-#pragma unroll
-        for (int t = 0; t < C / 16; ++t) {
-            if (t <= wave) {
-                auto ub = [&](int k0) { return frag_rows(sUb, PVH, 16 * t, k0, lr, lq); };
-                auto ub4 = [&](int k0) { return frag4_rows(sUb, PVH, 16 * t, k0, lr, lq); };
-                adP[t] = ftile<BV>(adP[t], [&](int k0) { return frag_rows(sDOb, PVH, R0, k0, lr, lq); }, ub,
-                                   [&](int k0) { return frag4_rows(sDOb, PVH, R0, k0, lr, lq); }, ub4);
-                adA[t] = ftile<BV>(adA[t], [&](int k0) { return frag_rows(sDRb, PVH, R0, k0, lr, lq); }, ub,
-                                   [&](int k0) { return frag4_rows(sDRb, PVH, R0, k0, lr, lq); }, ub4);
-            }
-        }
-#pragma unroll
-        for (int t = 0; t < NF; ++t) {
-            auto m0r = [&](int k0) { return frag_rows(sM0b, PVH, 16 * t, k0, lr, lq); };
-            auto m0r4 = [&](int k0) { return frag4_rows(sM0b, PVH, 16 * t, k0, lr, lq); };
-            aQ[t] = ftile<BV>(aQ[t], [&](int k0) { return frag_rows(sGDOb, PVH, R0, k0, lr, lq); }, m0r,
-                              [&](int k0) { return frag4_rows(sGDOb, PVH, R0, k0, lr, lq); }, m0r4);
-            aK[t] = ftile<BV>(aK[t], [&](int k0) { return frag_rows(sGDRb, PVH, R0, k0, lr, lq); }, m0r,
-                              [&](int k0) { return frag4_rows(sGDRb, PVH, R0, k0, lr, lq); }, m0r4);
-            aKt[t] = ftile<BV>(aKt[t], [&](int k0) { return frag_rows(sWUb, PVH, R0, k0, lr, lq); },
-                               [&](int k0) { return frag_rows(sdMb, PVH, 16 * t, k0, lr, lq); },
-                               [&](int k0) { return frag4_rows(sWUb, PVH, R0, k0, lr, lq); },
-                               [&](int k0) { return frag4_rows(sdMb, PVH, 16 * t, k0, lr, lq); });
-        }
-    }
-    frob = block_sum(frob, sred, tid);  // ends with a barrier: the slices are done
-
-    // masks, the decay terms (row sums inside the wave, column sums through LDS) and the
-    // dbeta term of A
-    float *colpart = sY;  // [4][C]
-    {
-        float rowp[4], rowb[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) rowp[e] = rowb[e] = 0.f;
-#pragma unroll
-        for (int t = 0; t < C / 16; ++t) {
-            v4f as, ps;  // AS and P of the tile, formed again
-            score_tiles(t, as, ps);
-            float colp = 0.f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = R0 + 4 * lq + e, j = 16 * t + lr;
-                const float dp = j <= i ? adP[t][e] : 0.f;
-                const float da = j < i ? -adA[t][e] : 0.f;
-                adP[t][e] = dp;
-                adA[t][e] = da;
-                const float ex = dp * ps[e] + da * sb[i] * as[e];
-                rowp[e] += ex;
-                colp += ex;
-                rowb[e] += da * as[e];
-            }
-            colp += __shfl_xor(colp, 16);
-            colp += __shfl_xor(colp, 32);
-            if (lq == 0) colpart[wave * C + 16 * t + lr] = colp;
+        // K M0, Q M0, K~ dMC on this wave's tile; Y = V - gam K M0 (registers), R = b Y into
+        // LDS as hi/lo bf16 over V
+        v4f km = zero4(), qm = zero4(), kdm = zero4(), y;
+#pragma unroll 2
+        for (int k0 = 0; k0 < DK; k0 += 32) {
+            const v8s m0f = frag_cols(sM0b, PVH, k0, jt, lr, lq);
+            km = mfma32(frag_rows(sK, PH, R0, k0, lr, lq), m0f, km);
+            qm = mfma32(frag_rows(sQ, PH, R0, k0, lr, lq), m0f, qm);
+            kdm = mfma32(frag_rows(sKt, PH, R0, k0, lr, lq), frag_cols(sdMb, PVH, k0, jt, lr, lq), kdm);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-#pragma unroll
-            for (int m = 1; m < 16; m <<= 1) {
-                rowp[e] += __shfl_xor(rowp[e], m);
-                rowb[e] += __shfl_xor(rowb[e], m);
-            }
+            const int r = R0 + 4 * lq + e, j = jt + lr;
+            pgo[e] += __uint_as_float(uint32_t(sDOb[r * PVH + j]) << 16) * qm[e];
+            y[e] = __uint_as_float(uint32_t(sRh[r * PVH + j]) << 16) - sgam[r] * km[e];
+            const float x = sb[r] * y[e];
+            const uint16_t h = bf16_bits(x);
+            sRh[r * PVH + j] = h;
+            sRl[r * PVH + j] = bf16_bits(x - __uint_as_float(uint32_t(h) << 16));
         }
-        if (lr == 0) {
+        __syncthreads();
+        // U = T R (T lower triangular) and dU = P^T dO + diag(w) K~ dMC
+        v4f u = zero4(), du = zero4();
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sdg[R0 + 4 * lq + e] += rowp[e];
-                sdb[R0 + 4 * lq + e] += rowb[e];
+        for (int k0 = 0; k0 < C; k0 += 32) {
+            if (k0 > R0 + 15) continue;
+            const v8s th = frag_rows(sTh, PCH, R0, k0, lr, lq), tl = frag_rows(sTl, PCH, R0, k0, lr, lq);
+            const v8s rh = frag_cols(sRh, PVH, k0, jt, lr, lq), rl = frag_cols(sRl, PVH, k0, jt, lr, lq);
+            u = mfma32(th, rh, u);
+            u = mfma32(th, rl, u);
+            u = mfma32(tl, rh, u);
+        }
+#pragma unroll
+        for (int k0 = 0; k0 < C; k0 += 32)
+            du = mfma32(frag_cols(sPb, PCH, k0, R0, lr, lq), frag_cols(sDOb, PVH, k0, jt, lr, lq), du);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = R0 + 4 * lq + e, j = jt + lr;
+            sUb[r * PVH + j] = bf16_bits(u[e]);
+            sWUb[r * PVH + j] = bf16_bits(sw[r] * u[e]);
+            pew[e] += kdm[e] * u[e];
+            const float x = du[e] + sw[r] * kdm[e];
+            const uint16_t h = bf16_bits(x);
+            sdUh[r * PVH + j] = h;
+            sdUl[r * PVH + j] = bf16_bits(x - __uint_as_float(uint32_t(h) << 16));
+        }
+        __syncthreads();
+        // dR = T^T dU (T^T upper triangular); dV = diag(b) dR
+        v4f dr = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < C; k0 += 32) {
+            if (k0 + 32 <= R0) continue;
+            const v8s th = frag_cols(sTh, PCH, k0, R0, lr, lq), tl = frag_cols(sTl, PCH, k0, R0, lr, lq);
+            const v8s uh = frag_cols(sdUh, PVH, k0, jt, lr, lq), ul = frag_cols(sdUl, PVH, k0, jt, lr, lq);
+            dr = mfma32(th, uh, dr);
+            dr = mfma32(th, ul, dr);
+            dr = mfma32(tl, uh, dr);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = R0 + 4 * lq + e, j = jt + lr;
+            sDRb[r * PVH + j] = bf16_bits(dr[e]);
+            sGDRb[r * PVH + j] = bf16_bits(-sgam[r] * sb[r] * dr[e]);
+            pgr[e] += dr[e] * km[e];
+            pdb[e] += dr[e] * y[e];
+            if (r < n) gvc[r * DV + s0 + j] = from_f32<bf16_t>(sb[r] * dr[e]);
+        }
+        __syncthreads();
+        // dP += dO U^T, dA += dR U^T (negated later) on this wave's score tiles, and the
+        // slice's part of dQ, dK, dK~ on this wave's feature tiles (K = the slice's 32 columns)
+        static_for<0, 2>([&](auto I) __attribute__((always_inline)) {
+            const int t = 2 * I + hw;
+            if (t <= rw) {
+                const v8s ub = frag_rows(sUb, PVH, 16 * t, 0, lr, lq);
+                adP[I] = mfma32(frag_rows(sDOb, PVH, R0, 0, lr, lq), ub, adP[I]);
+                adA[I] = mfma32(frag_rows(sDRb, PVH, R0, 0, lr, lq), ub, adA[I]);
             }
+        });
+        const v8s gdo = frag_rows(sGDOb, PVH, R0, 0, lr, lq), gdr = frag_rows(sGDRb, PVH, R0, 0, lr, lq);
+        const v8s wub = frag_rows(sWUb, PVH, R0, 0, lr, lq);
+#pragma unroll 2
+        for (int t = 0; t < NFH; ++t) {
+            const int f0 = 16 * (NFH * hw + t);
+            const v8s m0r = frag_rows(sM0b, PVH, f0, 0, lr, lq);
+            aQ[t] = mfma32(gdo, m0r, aQ[t]);
+            aK[t] = mfma32(gdr, m0r, aK[t]);
+            aKt[t] = mfma32(wub, frag_rows(sdMb, PVH, f0, 0, lr, lq), aKt[t]);
         }
     }
-    __syncthreads();
-    if (tid < C) sdg[tid] -= colpart[tid] + colpart[C + tid] + colpart[2 * C + tid] + colpart[3 * C + tid];
-    // dP o G into sPb and Gb = dA o G (row scaled by b) into sMb, as bf16
-    uint16_t *const sGb = sMb;
+#undef OSDN_BWD_LOAD_SLICE
+    {  // <dMC, M0> over the workgroup (fixed order); ends with a barrier: the slices are done
 #pragma unroll
-    for (int t = 0; t < C / 16; ++t)
+        for (int m = 32; m >= 1; m >>= 1) frob += __shfl_xor(frob, m);
+        __syncthreads();
+        if (lane == 0) sred[wave] = frob;
+        __syncthreads();
+        frob = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) frob += sred[w];
+    }
+
+    // masks of dP, dA; the decay terms dP o P + dA o A (row sums, and column sums by row
+    // block) and the dbeta term of A, on this wave's score tiles
+    float rowp[4] = {0.f, 0.f, 0.f, 0.f}, rowb[4] = {0.f, 0.f, 0.f, 0.f};
+    static_for<0, 2>([&](auto I) __attribute__((always_inline)) {
+        const int t = 2 * I + hw;
+        v4f as, ps;  // AS and P of the tile, formed again
+        score_tiles(t, as, ps);
+        float colp = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = R0 + 4 * lq + e, j = 16 * t + lr;
+            const float dp = j <= i ? adP[I][e] : 0.f;
+            const float da = j < i ? -adA[I][e] : 0.f;
+            adP[I][e] = dp;
+            adA[I][e] = da;
+            const float ex = dp * ps[e] + da * sb[i] * as[e];
+            rowp[e] += ex;
+            colp += ex;
+            rowb[e] += da * as[e];
+        }
+        colp += __shfl_xor(colp, 16);
+        colp += __shfl_xor(colp, 32);
+        if (lq == 0) scol[rw][16 * t + lr] = colp;
+    });
+    // row sums: across the 16 lanes of a row, then (below) across the two halves
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) {
+            pgo[e] += __shfl_xor(pgo[e], m);
+            pgr[e] += __shfl_xor(pgr[e], m);
+            pew[e] += __shfl_xor(pew[e], m);
+            pdb[e] += __shfl_xor(pdb[e], m);
+            rowp[e] += __shfl_xor(rowp[e], m);
+            rowb[e] += __shfl_xor(rowb[e], m);
+        }
+    }
+    if (lr == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = R0 + 4 * lq + e;
+            srow[hw][0][r] = pgo[e];
+            srow[hw][1][r] = pgr[e];
+            srow[hw][2][r] = pew[e];
+            srow[hw][3][r] = pdb[e];
+            srow[hw][4][r] = rowp[e];
+            srow[hw][5][r] = rowb[e];
+        }
+    }
+    // dP o G into sPb and Gb = dA o G (row scaled by b) into sMb, as bf16 (this wave's tiles)
+    uint16_t *const sGb = sMb;
+    static_for<0, 2>([&](auto I) __attribute__((always_inline)) {
+        const int t = 2 * I + hw;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = R0 + 4 * lq + e, j = 16 * t + lr;
             const float G = j <= i ? __expf(sg[i] - sg[j]) : 0.f;
-            sPb[i * PCH + j] = bf16_bits(adP[t][e] * G);
-            sGb[i * PCH + j] = bf16_bits(adA[t][e] * G * sb[i]);
+            sPb[i * PCH + j] = bf16_bits(adP[I][e] * G);
+            sGb[i * PCH + j] = bf16_bits(adA[I][e] * G * sb[i]);
         }
-    __syncthreads();
-    float dfin[NF][4];  // d at this lane's output positions, loaded ahead of the products
+    });
+    float dfin[NFH][4];  // d at this lane's output positions, loaded ahead of the products
 #pragma unroll
-    for (int t = 0; t < NF; ++t)
+    for (int t = 0; t < NFH; ++t)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = R0 + 4 * lq + e;
-            dfin[t][e] = to_f32(d[(row0 + (r < n ? r : n - 1)) * DK + 16 * t + lr]);
-        }
-#pragma unroll
-    for (int t = 0; t < NF; ++t) {
-#pragma unroll
-        for (int k0 = 0; k0 < C; k0 += 32) {
-            const v8s ktc = frag_cols(sKt, PH, k0, 16 * t, lr, lq);
-            aQ[t] = mfma32(frag_rows(sPb, PCH, R0, k0, lr, lq), ktc, aQ[t]);
-            aK[t] = mfma32(frag_rows(sGb, PCH, R0, k0, lr, lq), ktc, aK[t]);
-            aKt[t] = mfma32(frag_cols(sPb, PCH, k0, R0, lr, lq),
-                            frag_cols(sQ, PH, k0, 16 * t, lr, lq), aKt[t]);
-            aKt[t] = mfma32(frag_cols(sGb, PCH, k0, R0, lr, lq),
-                            frag_cols(sK, PH, k0, 16 * t, lr, lq), aKt[t]);
-        }
-    }
-#pragma unroll
-    for (int t = 0; t < NF; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = R0 + 4 * lq + e, f = 16 * t + lr;
-            if (r < n) {
-                const int64_t ix = (row0 + r) * DK + f;
-                gq[ix] = from_f32<bf16_t>(aQ[t][e]);
-                gk[ix] = from_f32<bf16_t>(aK[t][e] + aKt[t][e] * dfin[t][e]);
-                gd[ix] = from_f32<TD>(aKt[t][e] * __uint_as_float(uint32_t(sK[r * PH + f]) << 16));
-            }
+            dfin[t][e] = to_f32(dc[(r < n ? r : n - 1) * DK + 16 * (NFH * hw + t) + lr]);
         }
     __syncthreads();
-    if (tid < 64) {  // the last row's terms, then the reverse running sum of dg (wave 0)
-        const float ew = lane < n ? sew[lane] : 0.f;
-        float ews = ew;
+    if (tid < 64) {  // dbeta; dg of every row, then its reverse running sum d ln(alpha) (wave 0)
+        const int r = lane;
+        const float go = srow[0][0][r] + srow[1][0][r], gr = srow[0][1][r] + srow[1][1][r];
+        const float ew = sw[r] * (srow[0][2][r] + srow[1][2][r]);
+        const float db = srow[0][3][r] + srow[1][3][r] + srow[0][5][r] + srow[1][5][r];
+        float g = sgam[r] * go - sb[r] * sgam[r] * gr + srow[0][4][r] + srow[1][4][r] -
+                  (scol[0][r] + scol[1][r] + scol[2][r] + scol[3][r]);
+        // the last row's terms: gam_L <dMC, M0> + sum_s w_s <(K~ dMC)_s, U_s>
+        float ews = r < n ? ew : 0.f;
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) ews += __shfl_xor(ews, m);
-        float g = lane < n ? sdg[lane] - ew : 0.f;
-        if (lane == n - 1) g += sgam[C - 1] * frob + ews;
-        // suffix sum: x_r = sum_{r' >= r} g_r'
+        g = r < n ? g - ew : 0.f;
+        if (r == n - 1) g += sgam[C - 1] * frob + ews;
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_down(g, off);
-            if (lane + off < 64) g += y;
+        for (int off = 1; off < 64; off <<= 1) {  // suffix sum: x_r = sum_{r' >= r} g_r'
+            const float yv = __shfl_down(g, off);
+            if (lane + off < 64) g += yv;
         }
-        sdg[lane] = g;  // d ln(alpha_r)
+        if (r < n) {
+            gbeta[row0 + r] = db;
+            if (alpha && galpha) galpha[row0 + r] = g / alpha[row0 + r];
+        }
     }
-    __syncthreads();
-    if (tid < n) {
-        gbeta[row0 + tid] = sdb[tid];
-        if (alpha && galpha) galpha[row0 + tid] = sdg[tid] / alpha[row0 + tid];
+    // dQ += (dP o G) K~, dK += Gb K~, dK~ += (dP o G)^T Q + Gb^T K on this wave's feature tiles
+#pragma unroll
+    for (int t = 0; t < NFH; ++t) {
+        const int f0 = 16 * (NFH * hw + t);
+#pragma unroll
+        for (int k0 = 0; k0 < C; k0 += 32) {
+            const v8s ktc = frag_cols(sKt, PH, k0, f0, lr, lq);
+            aQ[t] = mfma32(frag_rows(sPb, PCH, R0, k0, lr, lq), ktc, aQ[t]);
+            aK[t] = mfma32(frag_rows(sGb, PCH, R0, k0, lr, lq), ktc, aK[t]);
+            aKt[t] = mfma32(frag_cols(sPb, PCH, k0, R0, lr, lq), frag_cols(sQ, PH, k0, f0, lr, lq), aKt[t]);
+            aKt[t] = mfma32(frag_cols(sGb, PCH, k0, R0, lr, lq), frag_cols(sK, PH, k0, f0, lr, lq), aKt[t]);
+        }
     }
-#undef OSDN_BWD_LOAD_SLICE
+#pragma unroll
+    for (int t = 0; t < NFH; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = R0 + 4 * lq + e, f = 16 * (NFH * hw + t) + lr;
+            if (r < n) {
+                const int ix = r * DK + f;
+                gqc[ix] = from_f32<bf16_t>(aQ[t][e]);
+                gkc[ix] = from_f32<bf16_t>(aK[t][e] + aKt[t][e] * dfin[t][e]);
+                gdc[ix] = from_f32<TD>(aKt[t][e] * __uint_as_float(uint32_t(sK[r * PH + f]) << 16));
+            }
+        }
 }
 
 // ---- (I + A)^{-1} of every chunk (bf16 inputs, C = 64) ---------------------------------------
@@ -1516,25 +1460,26 @@ hipError_t bwd_typed(const BwdArgs &a, hipStream_t stream) {
                        static_cast<const TQ *>(a.dO), a.dS_T, a.dMck, a.dS0, a.T, DV);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || nch == 0) return e;
-    constexpr int BVB = C == 64 ? 16 : 32;  // value slice of the per-chunk pass
     if constexpr (sizeof(TQ) == 2) {
-        hipLaunchKernelGGL((bwd_chunk_mfma_kernel<DK, DV, BVB, TD>),
-                           dim3(static_cast<unsigned>(a.BH * nch)), dim3(NT), 0, stream,
+        hipLaunchKernelGGL((bwd_chunk_mfma_kernel<DK, DV, TD>),
+                           dim3(static_cast<unsigned>(a.BH * nch)), dim3(2 * NT), 0, stream,
                            static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.k),
                            static_cast<const bf16_t *>(a.v), static_cast<const TD *>(a.d),
                            a.beta, a.alpha, static_cast<const bf16_t *>(a.dO), a.Mck, a.dMck,
                            a.Tck, static_cast<bf16_t *>(a.gq), static_cast<bf16_t *>(a.gk),
                            static_cast<bf16_t *>(a.gv), a.gbeta, static_cast<TD *>(a.gd),
                            a.galpha, a.T, nch);
-        return hipGetLastError();
+    } else {
+        constexpr int BVB = 32;  // value slice of the fp32 per-chunk pass
+        hipLaunchKernelGGL((bwd_chunk_kernel<C, DK, DV, BVB, TQ, TD>),
+                           dim3(static_cast<unsigned>(a.BH * nch)), dim3(NT), 0, stream,
+                           static_cast<const TQ *>(a.q), static_cast<const TQ *>(a.k),
+                           static_cast<const TQ *>(a.v), static_cast<const TD *>(a.d), a.beta,
+                           a.alpha, static_cast<const TQ *>(a.dO), a.Mck, a.dMck,
+                           static_cast<TQ *>(a.gq), static_cast<TQ *>(a.gk),
+                           static_cast<TQ *>(a.gv), a.gbeta, static_cast<TD *>(a.gd), a.galpha,
+                           a.T, nch);
     }
-    hipLaunchKernelGGL((bwd_chunk_kernel<C, DK, DV, BVB, TQ, TD>),
-                       dim3(static_cast<unsigned>(a.BH * nch)), dim3(NT), 0, stream,
-                       static_cast<const TQ *>(a.q), static_cast<const TQ *>(a.k),
-                       static_cast<const TQ *>(a.v), static_cast<const TD *>(a.d), a.beta,
-                       a.alpha, static_cast<const TQ *>(a.dO), a.Mck, a.dMck,
-                       static_cast<TQ *>(a.gq), static_cast<TQ *>(a.gk), static_cast<TQ *>(a.gv),
-                       a.gbeta, static_cast<TD *>(a.gd), a.galpha, a.T, nch);
     return hipGetLastError();
 }
 
