@@ -1138,34 +1138,39 @@ bwd_tinv_kernel(const bf16_t *__restrict__ k, const TD *__restrict__ d,
 }
 
 // ---- reverse pass over chunks on bf16 matrix cores (bf16 inputs, C = 64) --------------------
-// Same data flow as bwd_state_kernel.  The scores P, K~ dM, P^T dO and the dM update run on
-// 16x16 MFMA tiles (wave w owns rows 16w..16w+15 of the C-row products and rows 32w..32w+31 of
-// dM); dR = T^T dU takes the chunk's inverse T = (I + A)^{-1} from its hi/lo bf16 planes
-// (written by bwd_tinv_kernel) with dU split the same way, three products per k-step.  dM stays
-// fp32.  Five barriers per chunk.
+// Same data flow as bwd_state_kernel, on eight waves (two per SIMD).  One workgroup per
+// (sequence, 32-column value slice) walks the chunks backwards.  dM (fp32, dk x 32) lives in
+// registers: wave w owns its 16x16 tiles in the MFMA C layout and stores them straight to the
+// checkpoint; LDS holds its bf16 copy, the operand of K~ dM.  Per chunk, with a barrier after
+// each phase:
+//   stores   the chunk's q, k, K~ = d (.) k, T planes and dO (prefetched into registers one
+//            chunk ahead) into LDS, and the next chunk's loads issued;
+//   scores   gam dO; the ten lower tiles of P spread over the waves; one 16x16 tile of K~ dM
+//            per wave; one wave runs the decay scan of the next chunk (double-buffered);
+//   dU       dU = P^T dO + diag(w) K~ dM, one tile per wave, as hi/lo bf16;
+//   dR       dR = T^T dU from the T planes (hi.hi + hi.lo + lo.hi), one tile per wave;
+//   update   dM <- gam_L dM + Q^T diag(gam) dO - K^T diag(gam b) dR on the wave's own tiles.
 template <int DK, int BV, typename TD>
-__global__ void __launch_bounds__(NT)
+__global__ void __launch_bounds__(2 * NT)
 bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                       const TD *__restrict__ d, const float *__restrict__ beta,
                       const float *__restrict__ alpha, const bf16_t *__restrict__ dO,
                       const float *__restrict__ dS_T, const uint16_t *__restrict__ Tck,
                       float *__restrict__ dMck, float *__restrict__ dS0, int64_t T, int dv) {
-    constexpr int C = 64;
+    constexpr int C = 64, NW = 8, NTH = NW * 64;
     constexpr int PH = DK + 8, PCH = C + 8, PVH = BV + 8;  // bf16 pitches
-    constexpr int PS = BV + 1;                             // fp32 pitch
-    constexpr int NV = BV / 16;   // column tiles of the C x BV products
-    constexpr int MR = DK / 64;   // 16-row tiles of dM per wave
-    constexpr int G = DK / 8, NU = C * G / NT;  // 16-byte units of a Q/K row; units per thread
+    constexpr int G = DK / 8, NU = C * G / NTH;  // 16-byte units of a Q/K row; units per thread
     constexpr int DU = sizeof(TD) == 4 ? 2 : 1;  // 16-byte units of d per unit of k
-    constexpr int TU = 2 * C * C / 8 / NT;       // 16-byte units of the T planes per thread
-    static_assert(NU * NT == C * G && NU <= 4 && C * BV / 8 == NT && TU == 4, "unit layout");
+    constexpr int TU = 2 * C * C / 8 / NTH;      // 16-byte units of the T planes per thread
+    constexpr int MT = DK / 64;                  // 16x16 tiles of dM per wave
+    static_assert(BV == 32 && NU * NTH == C * G && NU <= 2 && TU == 2 && C * BV / 4 == NTH,
+                  "unit layout");
     __shared__ alignas(16) uint16_t sQ[C * PH], sK[C * PH], sKt[C * PH];
     __shared__ alignas(16) uint16_t sPb[C * PCH], sTh[C * PCH], sTl[C * PCH];
     __shared__ alignas(16) uint16_t sDOb[C * PVH], sGDOb[C * PVH], sGDRb[C * PVH];
     __shared__ alignas(16) uint16_t sdUh[C * PVH], sdUl[C * PVH];
     __shared__ alignas(16) uint16_t sdMb[DK * PVH];  // bf16 copy of dM (operand of K~ dM)
-    __shared__ float sdM[DK * PS];
-    __shared__ float sb[C], sg[C], sgam[C], sw[C];
+    __shared__ float sb[2][C], sg[2][C], sgam[2][C], sw[2][C];  // decay scan, by chunk parity
 
     // workgroup -> (sequence, value slice); the slices of one sequence share an XCD (and its
     // L2) when the sequence count allows it, so their re-reads of q, k, d and T hit L2
@@ -1182,82 +1187,99 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
         bh = blockIdx.x / nvt;
     }
     const int j0 = vt * BV;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lq = lane >> 4;
-    const int R0 = 16 * wave;
+    const int rb = wave & 3, ct = wave >> 2;  // this wave's tile of the C x 32 products
+    const int R0 = 16 * rb, jt = 16 * ct;
     const int64_t nch = (T + C - 1) / C;
+    const int64_t seq0 = bh * T;
+    auto rows_of = [&](int64_t cc) { return static_cast<int>(T - cc * C < C ? T - cc * C : C); };
 
-    // the next chunk's q, k, d, dO, T planes, beta, alpha, loaded into named registers one
-    // chunk ahead (an array carried across the loop would live in scratch); unit i of this
-    // thread is u = tid + i NT: row u / G, features 8 (u % G) .. +7; T unit u holds elements
-    // 8u .. 8u + 7 of the two planes (plane u / 512, row (u / 8) % 64, columns 8 (u % 8) ..)
-    uint4 q0, q1, q2, q3, k0r, k1r, k2r, k3r, dl0, dl1, dl2, dl3, dh0, dh1, dh2, dh3, ou;
-    uint4 t0, t1, t2, t3;
-    float bv = 0.f, av = 1.f;
-    auto qreg = [&](auto I) -> uint4 & {
-        constexpr int i = decltype(I)::value;
-        if constexpr (i == 0) return q0; else if constexpr (i == 1) return q1;
-        else if constexpr (i == 2) return q2; else return q3;
-    };
-    auto kreg = [&](auto I) -> uint4 & {
-        constexpr int i = decltype(I)::value;
-        if constexpr (i == 0) return k0r; else if constexpr (i == 1) return k1r;
-        else if constexpr (i == 2) return k2r; else return k3r;
-    };
-    auto dlreg = [&](auto I) -> uint4 & {
-        constexpr int i = decltype(I)::value;
-        if constexpr (i == 0) return dl0; else if constexpr (i == 1) return dl1;
-        else if constexpr (i == 2) return dl2; else return dl3;
-    };
-    auto dhreg = [&](auto I) -> uint4 & {
-        constexpr int i = decltype(I)::value;
-        if constexpr (i == 0) return dh0; else if constexpr (i == 1) return dh1;
-        else if constexpr (i == 2) return dh2; else return dh3;
-    };
-    auto treg = [&](auto I) -> uint4 & {
-        constexpr int i = decltype(I)::value;
-        if constexpr (i == 0) return t0; else if constexpr (i == 1) return t1;
-        else if constexpr (i == 2) return t2; else return t3;
-    };
+    // the next chunk's q, k, d, T planes and dO in named registers, loaded one chunk ahead (an
+    // array carried across the loop would live in scratch); unit i of this thread is
+    // u = tid + i NTH: row u / G, features 8 (u % G) .. +7; T unit u holds elements 8u .. 8u+7
+    // of the two planes (plane u / 512, row (u / 8) % 64, columns 8 (u % 8) ..)
+    uint4 q0, q1, k0r, k1r, dl0, dl1, dh0, dh1, t0, t1;
+    uint2 ou;
+    auto qreg = [&](auto I) -> uint4 & { if constexpr (decltype(I)::value == 0) return q0; else return q1; };
+    auto kreg = [&](auto I) -> uint4 & { if constexpr (decltype(I)::value == 0) return k0r; else return k1r; };
+    auto dlreg = [&](auto I) -> uint4 & { if constexpr (decltype(I)::value == 0) return dl0; else return dl1; };
+    auto dhreg = [&](auto I) -> uint4 & { if constexpr (decltype(I)::value == 0) return dh0; else return dh1; };
     auto load_chunk = [&](int64_t cc) __attribute__((always_inline)) {
-        const int64_t r0 = bh * T + cc * C;
-        const int nn = static_cast<int>(T - cc * C < C ? T - cc * C : C);
+        const bf16_t *qc = q + (seq0 + cc * C) * DK, *kc = k + (seq0 + cc * C) * DK;
+        const TD *dc = d + (seq0 + cc * C) * DK;
+        const int nn = rows_of(cc);
         static_for<0, NU>([&](auto I) __attribute__((always_inline)) {
-            const int u = tid + I * NT, r = u / G, g = u % G;
-            const int64_t e = (r0 + (r < nn ? r : nn - 1)) * DK + 8 * g;
-            qreg(I) = *reinterpret_cast<const uint4 *>(q + e);
-            kreg(I) = *reinterpret_cast<const uint4 *>(k + e);
-            const uint4 *dp = reinterpret_cast<const uint4 *>(d + e);
+            const int u = tid + I * NTH, r = u / G, g = u % G;
+            const int e = (r < nn ? r : nn - 1) * DK + 8 * g;
+            qreg(I) = *reinterpret_cast<const uint4 *>(qc + e);
+            kreg(I) = *reinterpret_cast<const uint4 *>(kc + e);
+            const uint4 *dp = reinterpret_cast<const uint4 *>(dc + e);
             dlreg(I) = dp[0];
             if constexpr (DU == 2) dhreg(I) = dp[1];
         });
         const uint4 *tp = reinterpret_cast<const uint4 *>(Tck + (bh * nch + cc) * (2 * C * C));
-        static_for<0, TU>([&](auto I) __attribute__((always_inline)) { treg(I) = tp[tid + I * NT]; });
-        {
-            const int r = tid / (BV / 8), j = 8 * (tid % (BV / 8));
-            ou = *reinterpret_cast<const uint4 *>(dO + (r0 + (r < nn ? r : nn - 1)) * dv + j0 + j);
-        }
-        if (tid < 64 && tid < nn) {
-            bv = beta[r0 + tid];
-            av = alpha ? alpha[r0 + tid] : 1.f;
-        }
+        t0 = tp[tid];
+        t1 = tp[tid + NTH];
+        const int r = tid / (BV / 4), j = 4 * (tid % (BV / 4));
+        ou = *reinterpret_cast<const uint2 *>(dO + (seq0 + cc * C + (r < nn ? r : nn - 1)) * dv + j0 + j);
     };
-    if (nch > 0) load_chunk(nch - 1);
+    // decay scan of chunk cc into buffer cc & 1 (one wave; beta, alpha of the chunk in bv, av)
+    float bv = 0.f, av = 1.f;
+    auto load_ba = [&](int64_t cc) __attribute__((always_inline)) {
+        const int r = min(lane, rows_of(cc) - 1);
+        bv = beta[seq0 + cc * C + r];
+        av = alpha ? alpha[seq0 + cc * C + r] : 1.f;
+    };
+    auto scan = [&](int64_t cc) __attribute__((always_inline)) {
+        const int nn = rows_of(cc), pb = static_cast<int>(cc & 1);
+        float x = (lane < nn && alpha) ? logf(av) : 0.f;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_up(x, off);
+            if (lane >= off) x += y;
+        }
+        const float gl = __shfl(x, C - 1);
+        sb[pb][lane] = lane < nn ? bv : 0.f;
+        sg[pb][lane] = x;
+        sgam[pb][lane] = __expf(x);
+        sw[pb][lane] = __expf(gl - x);
+    };
 
-    for (int idx = tid; idx < DK * BV; idx += NT) {
-        const int f = idx / BV, j = idx % BV;
-        const float x = dS_T ? dS_T[(bh * DK + f) * dv + j0 + j] : 0.f;
-        sdM[f * PS + j] = x;
-        sdMb[f * PVH + j] = bf16_bits(x);
+    // dM tiles of this wave: tile index ti = MT wave + m, rows 16 (ti / 2) .., columns 16 (ti % 2) ..
+    v4f dM[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const int ti = MT * wave + m, f0 = 16 * (ti >> 1), c0 = 16 * (ti & 1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int f = f0 + 4 * lq + e, j = c0 + lr;
+            dM[m][e] = dS_T ? dS_T[(bh * DK + f) * dv + j0 + j] : 0.f;
+            sdMb[f * PVH + j] = bf16_bits(dM[m][e]);
+            if (nch > 0) dMck[((bh * nch + nch - 1) * DK + f) * dv + j0 + j] = dM[m][e];
+        }
     }
+    for (int i = tid; i < C * PCH; i += NTH) sPb[i] = 0;  // tiles above the diagonal stay zero
+    if (nch > 0) {
+        load_chunk(nch - 1);
+        if (wave == NW - 1) {
+            load_ba(nch - 1);
+            scan(nch - 1);
+            if (nch > 1) load_ba(nch - 2);
+        }
+    }
+    // this wave's lower tiles of P: (row block, column tile) codes 4 rb + t, -1 for none
+    const int pt0 = wave == 0 ? 15 : wave == 1 ? 14 : wave == 2 ? 13 : wave == 3 ? 12
+                  : wave == 4 ? 10 : wave == 5 ? 9 : wave == 6 ? 8 : -1;
+    const int pt1 = wave == 0 ? 0 : wave == 1 ? 5 : wave == 6 ? 4 : -1;
+
     for (int64_t c = nch - 1; c >= 0; --c) {
-        const int64_t c0 = c * C;
-        const int n = static_cast<int>(T - c0 < C ? T - c0 : C);
+        const int n = rows_of(c), pb = static_cast<int>(c & 1);
         __syncthreads();  // the previous chunk is done with every buffer
-        // this chunk's registers into LDS: Q, K, K~ = d (.) k (bf16), dO, the T planes; the
-        // decay scan
+        // this chunk's registers into LDS: Q, K, K~ = d (.) k (bf16), the T planes, dO
         static_for<0, NU>([&](auto I) __attribute__((always_inline)) {
-            const int u = tid + I * NT, r = u / G, g = u % G;
+            const int u = tid + I * NTH, r = u / G, g = u % G;
             const uint32_t m = r < n ? 0xffffffffu : 0u;  // rows past the end are zero
             const uint4 kq = kreg(I), qq = qreg(I);
             const uint32_t kw[4] = {kq.x, kq.y, kq.z, kq.w};
@@ -1283,143 +1305,113 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             *reinterpret_cast<uint4 *>(&sK[r * PH + 8 * g]) = make_uint4(kw[0] & m, kw[1] & m, kw[2] & m, kw[3] & m);
             *reinterpret_cast<uint4 *>(&sKt[r * PH + 8 * g]) = make_uint4(kt[0] & m, kt[1] & m, kt[2] & m, kt[3] & m);
         });
-        static_for<0, TU>([&](auto I) __attribute__((always_inline)) {
-            constexpr int i = decltype(I)::value;
-            const int u = tid + i * NT, r = (u >> 3) & 63, g = u & 7;
-            uint16_t *dst = i < TU / 2 ? sTh : sTl;
-            *reinterpret_cast<uint4 *>(&dst[r * PCH + 8 * g]) = treg(I);
-        });
         {
-            const int r = tid / (BV / 8), j = 8 * (tid % (BV / 8));
+            const int r = (tid >> 3) & 63, g = tid & 7;  // unit tid of each plane
+            *reinterpret_cast<uint4 *>(&sTh[r * PCH + 8 * g]) = t0;
+            *reinterpret_cast<uint4 *>(&sTl[r * PCH + 8 * g]) = t1;
+        }
+        {
+            const int r = tid / (BV / 4), j = 4 * (tid % (BV / 4));
             const uint32_t m = r < n ? 0xffffffffu : 0u;
-            *reinterpret_cast<uint4 *>(&sDOb[r * PVH + j]) = make_uint4(ou.x & m, ou.y & m, ou.z & m, ou.w & m);
-        }
-        if (tid < 64) {
-            float x = (lane < n && alpha) ? logf(av) : 0.f;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(x, off);
-                if (lane >= off) x += y;
-            }
-            const float gl = __shfl(x, C - 1);
-            sb[lane] = lane < n ? bv : 0.f;
-            sg[lane] = x;
-            sgam[lane] = __expf(x);
-            sw[lane] = __expf(gl - x);
-        }
-        for (int u = tid; u < DK * BV / 4; u += NT) {  // gradient at this chunk's end
-            const int f = u / (BV / 4), j = 4 * (u % (BV / 4));
-            const float *src = &sdM[f * PS + j];
-            *reinterpret_cast<float4 *>(&dMck[((bh * nch + c) * DK + f) * dv + j0 + j]) =
-                make_float4(src[0], src[1], src[2], src[3]);
+            *reinterpret_cast<uint2 *>(&sDOb[r * PVH + j]) = make_uint2(ou.x & m, ou.y & m);
         }
         if (c > 0) load_chunk(c - 1);  // in flight through this chunk's work
         __syncthreads();
         {  // gam-scaled dO for the dM update
-            const int r = tid / (BV / 8), j = 8 * (tid % (BV / 8));
-            const uint4 o = *reinterpret_cast<const uint4 *>(&sDOb[r * PVH + j]);
-            const uint32_t w[4] = {o.x, o.y, o.z, o.w};
-            uint32_t gw[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) gw[e] = pack2(sgam[r] * bf_lo(w[e]), sgam[r] * bf_hi(w[e]));
-            *reinterpret_cast<uint4 *>(&sGDOb[r * PVH + j]) = make_uint4(gw[0], gw[1], gw[2], gw[3]);
+            const int r = tid / (BV / 4), j = 4 * (tid % (BV / 4));
+            const uint2 o = *reinterpret_cast<const uint2 *>(&sDOb[r * PVH + j]);
+            const float gm = sgam[pb][r];
+            *reinterpret_cast<uint2 *>(&sGDOb[r * PVH + j]) =
+                make_uint2(pack2(gm * bf_lo(o.x), gm * bf_hi(o.x)), pack2(gm * bf_lo(o.y), gm * bf_hi(o.y)));
         }
-        // this wave's rows of P (bf16, zero above the diagonal) and of K~ dM
-#pragma unroll
-        for (int t = 0; t < C / 16; ++t) {
+        // this wave's lower tiles of P (bf16; zero above the diagonal inside a diagonal tile)
+        auto p_tile = [&](int code) __attribute__((always_inline)) {
+            const int pr = 16 * (code >> 2), t = code & 3;
             v4f aq = zero4();
-            if (t <= wave) {
-#pragma unroll
-                for (int k0 = 0; k0 < DK; k0 += 32)
-                    aq = mfma32(frag_rows(sQ, PH, R0, k0, lr, lq), frag_rows(sKt, PH, 16 * t, k0, lr, lq), aq);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = R0 + 4 * lq + e, j = 16 * t + lr;
-                sPb[i * PCH + j] = bf16_bits(j <= i ? aq[e] * __expf(sg[i] - sg[j]) : 0.f);
-            }
-        }
-        v4f kdm[NV];
-#pragma unroll
-        for (int t = 0; t < NV; ++t) {
-            kdm[t] = zero4();
 #pragma unroll
             for (int k0 = 0; k0 < DK; k0 += 32)
-                kdm[t] = mfma32(frag_rows(sKt, PH, R0, k0, lr, lq),
-                                frag_cols(sdMb, PVH, k0, 16 * t, lr, lq), kdm[t]);
+                aq = mfma32(frag_rows(sQ, PH, pr, k0, lr, lq), frag_rows(sKt, PH, 16 * t, k0, lr, lq), aq);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = pr + 4 * lq + e, j = 16 * t + lr;
+                sPb[i * PCH + j] = bf16_bits(j <= i ? aq[e] * __expf(sg[pb][i] - sg[pb][j]) : 0.f);
+            }
+        };
+        if (pt0 >= 0) p_tile(pt0);
+        if (pt1 >= 0) p_tile(pt1);
+        // this wave's tile of K~ dM
+        v4f kdm = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < DK; k0 += 32)
+            kdm = mfma32(frag_rows(sKt, PH, R0, k0, lr, lq), frag_cols(sdMb, PVH, k0, jt, lr, lq), kdm);
+        if (wave == NW - 1 && c > 0) {  // the next chunk's decay scan, into the other buffer
+            scan(c - 1);
+            if (c > 1) load_ba(c - 2);
         }
         __syncthreads();
-        // dU = P^T dO + diag(w) K~ dM, as hi/lo bf16 planes
-#pragma unroll
-        for (int t = 0; t < NV; ++t) {
+        {  // dU = P^T dO + diag(w) K~ dM on this wave's tile, as hi/lo bf16
             v4f du = zero4();
 #pragma unroll
             for (int k0 = 0; k0 < C; k0 += 32)
-                du = mfma32(frag_cols(sPb, PCH, k0, R0, lr, lq),
-                            frag_cols(sDOb, PVH, k0, 16 * t, lr, lq), du);
+                du = mfma32(frag_cols(sPb, PCH, k0, R0, lr, lq), frag_cols(sDOb, PVH, k0, jt, lr, lq), du);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int r = R0 + 4 * lq + e, j = 16 * t + lr;
-                const float x = du[e] + sw[r] * kdm[t][e];
+                const int r = R0 + 4 * lq + e, j = jt + lr;
+                const float x = du[e] + sw[pb][r] * kdm[e];
                 const uint16_t h = bf16_bits(x);
                 sdUh[r * PVH + j] = h;
                 sdUl[r * PVH + j] = bf16_bits(x - __uint_as_float(uint32_t(h) << 16));
             }
         }
         __syncthreads();
-        // dR = T^T dU (T^T upper triangular: k-steps from this wave's first row on), and
-        // -diag(gam b) dR in bf16 for the dM update
-#pragma unroll
-        for (int t = 0; t < NV; ++t) {
+        {  // dR = T^T dU (T^T upper triangular: k-steps from the tile's first row on); -gam b dR
             v4f dr = zero4();
 #pragma unroll
             for (int k0 = 0; k0 < C; k0 += 32) {
                 if (k0 + 32 <= R0) continue;
                 const v8s th = frag_cols(sTh, PCH, k0, R0, lr, lq), tl = frag_cols(sTl, PCH, k0, R0, lr, lq);
-                const v8s uh = frag_cols(sdUh, PVH, k0, 16 * t, lr, lq), ul = frag_cols(sdUl, PVH, k0, 16 * t, lr, lq);
+                const v8s uh = frag_cols(sdUh, PVH, k0, jt, lr, lq), ul = frag_cols(sdUl, PVH, k0, jt, lr, lq);
                 dr = mfma32(th, uh, dr);
                 dr = mfma32(th, ul, dr);
                 dr = mfma32(tl, uh, dr);
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int r = R0 + 4 * lq + e, j = 16 * t + lr;
-                sGDRb[r * PVH + j] = bf16_bits(-sgam[r] * sb[r] * dr[e]);
+                const int r = R0 + 4 * lq + e, j = jt + lr;
+                sGDRb[r * PVH + j] = bf16_bits(-sgam[pb][r] * sb[pb][r] * dr[e]);
             }
         }
         __syncthreads();
-        // dM <- gam_L dM + Q^T diag(gam) dO - K^T diag(gam b) dR (this wave's rows of dM)
-        {
-            const float gl = sgam[C - 1];
+        {  // dM <- gam_L dM + Q^T diag(gam) dO - K^T diag(gam b) dR on this wave's tiles; the
+           // result is the gradient at the previous chunk's end
+            const float gl = sgam[pb][C - 1];
 #pragma unroll
-            for (int mt = 0; mt < MR; ++mt) {
-                const int f0 = 16 * (MR * wave + mt);
+            for (int m = 0; m < MT; ++m) {
+                const int ti = MT * wave + m, f0 = 16 * (ti >> 1), c0 = 16 * (ti & 1);
+                v4f acc = zero4();
 #pragma unroll
-                for (int t = 0; t < NV; ++t) {
-                    v4f acc = zero4();
+                for (int k0 = 0; k0 < C; k0 += 32) {
+                    acc = mfma32(frag_cols(sQ, PH, k0, f0, lr, lq), frag_cols(sGDOb, PVH, k0, c0, lr, lq), acc);
+                    acc = mfma32(frag_cols(sK, PH, k0, f0, lr, lq), frag_cols(sGDRb, PVH, k0, c0, lr, lq), acc);
+                }
+                float *ck = dMck + ((bh * nch + (c > 0 ? c - 1 : 0)) * DK + f0) * dv + j0 + c0;
 #pragma unroll
-                    for (int k0 = 0; k0 < C; k0 += 32) {
-                        acc = mfma32(frag_cols(sQ, PH, k0, f0, lr, lq),
-                                     frag_cols(sGDOb, PVH, k0, 16 * t, lr, lq), acc);
-                        acc = mfma32(frag_cols(sK, PH, k0, f0, lr, lq),
-                                     frag_cols(sGDRb, PVH, k0, 16 * t, lr, lq), acc);
-                    }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int f = f0 + 4 * lq + e, j = 16 * t + lr;
-                        const float x = gl * sdM[f * PS + j] + acc[e];
-                        sdM[f * PS + j] = x;
-                        sdMb[f * PVH + j] = bf16_bits(x);
-                    }
+                for (int e = 0; e < 4; ++e) {
+                    const int f = f0 + 4 * lq + e, j = c0 + lr;
+                    dM[m][e] = gl * dM[m][e] + acc[e];
+                    sdMb[f * PVH + j] = bf16_bits(dM[m][e]);
+                    if (c > 0) ck[(4 * lq + e) * dv + lr] = dM[m][e];
                 }
             }
         }
     }
-    __syncthreads();
     if (dS0) {
-        for (int idx = tid; idx < DK * BV; idx += NT) {
-            const int f = idx / BV, j = idx % BV;
-            dS0[(bh * DK + f) * dv + j0 + j] = sdM[f * PS + j];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const int ti = MT * wave + m, f0 = 16 * (ti >> 1), c0 = 16 * (ti & 1);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                dS0[(bh * DK + f0 + 4 * lq + e) * dv + j0 + c0 + lr] = dM[m][e];
         }
     }
 }
@@ -1447,7 +1439,7 @@ hipError_t bwd_typed(const BwdArgs &a, hipStream_t stream) {
             if (e != hipSuccess) return e;
         }
         hipLaunchKernelGGL((bwd_state_mfma_kernel<DK, BVA, TD>),
-                           dim3(static_cast<unsigned>(a.BH * (DV / BVA))), dim3(NT), 0, stream,
+                           dim3(static_cast<unsigned>(a.BH * (DV / BVA))), dim3(2 * NT), 0, stream,
                            static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.k),
                            static_cast<const TD *>(a.d), a.beta, a.alpha,
                            static_cast<const bf16_t *>(a.dO), a.dS_T, a.Tck, a.dMck, a.dS0,
