@@ -1206,24 +1206,34 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
     auto kreg = [&](auto I) -> uint4 & { if constexpr (decltype(I)::value == 0) return k0r; else return k1r; };
     auto dlreg = [&](auto I) -> uint4 & { if constexpr (decltype(I)::value == 0) return dl0; else return dl1; };
     auto dhreg = [&](auto I) -> uint4 & { if constexpr (decltype(I)::value == 0) return dh0; else return dh1; };
-    auto load_chunk = [&](int64_t cc) __attribute__((always_inline)) {
+    // issued in three parts spread over the phases of the chunk before (a wave stalls while
+    // the CU's load queue is full, so one burst would hold up the barrier that follows it)
+    auto load_qk = [&](int64_t cc) __attribute__((always_inline)) {
         const bf16_t *qc = q + (seq0 + cc * C) * DK, *kc = k + (seq0 + cc * C) * DK;
-        const TD *dc = d + (seq0 + cc * C) * DK;
         const int nn = rows_of(cc);
         static_for<0, NU>([&](auto I) __attribute__((always_inline)) {
             const int u = tid + I * NTH, r = u / G, g = u % G;
             const int e = (r < nn ? r : nn - 1) * DK + 8 * g;
             qreg(I) = *reinterpret_cast<const uint4 *>(qc + e);
             kreg(I) = *reinterpret_cast<const uint4 *>(kc + e);
-            const uint4 *dp = reinterpret_cast<const uint4 *>(dc + e);
+        });
+        const int r = tid / (BV / 4), j = 4 * (tid % (BV / 4));
+        ou = *reinterpret_cast<const uint2 *>(dO + (seq0 + cc * C + (r < nn ? r : nn - 1)) * dv + j0 + j);
+    };
+    auto load_d = [&](int64_t cc) __attribute__((always_inline)) {
+        const TD *dc = d + (seq0 + cc * C) * DK;
+        const int nn = rows_of(cc);
+        static_for<0, NU>([&](auto I) __attribute__((always_inline)) {
+            const int u = tid + I * NTH, r = u / G, g = u % G;
+            const uint4 *dp = reinterpret_cast<const uint4 *>(dc + (r < nn ? r : nn - 1) * DK + 8 * g);
             dlreg(I) = dp[0];
             if constexpr (DU == 2) dhreg(I) = dp[1];
         });
+    };
+    auto load_t = [&](int64_t cc) __attribute__((always_inline)) {
         const uint4 *tp = reinterpret_cast<const uint4 *>(Tck + (bh * nch + cc) * (2 * C * C));
         t0 = tp[tid];
         t1 = tp[tid + NTH];
-        const int r = tid / (BV / 4), j = 4 * (tid % (BV / 4));
-        ou = *reinterpret_cast<const uint2 *>(dO + (seq0 + cc * C + (r < nn ? r : nn - 1)) * dv + j0 + j);
     };
     // decay scan of chunk cc into buffer cc & 1 (one wave; beta, alpha of the chunk in bv, av)
     float bv = 0.f, av = 1.f;
@@ -1262,7 +1272,9 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
     }
     for (int i = tid; i < C * PCH; i += NTH) sPb[i] = 0;  // tiles above the diagonal stay zero
     if (nch > 0) {
-        load_chunk(nch - 1);
+        load_qk(nch - 1);
+        load_d(nch - 1);
+        load_t(nch - 1);
         if (wave == NW - 1) {
             load_ba(nch - 1);
             scan(nch - 1);
@@ -1315,7 +1327,7 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             const uint32_t m = r < n ? 0xffffffffu : 0u;
             *reinterpret_cast<uint2 *>(&sDOb[r * PVH + j]) = make_uint2(ou.x & m, ou.y & m);
         }
-        if (c > 0) load_chunk(c - 1);  // in flight through this chunk's work
+        if (c > 0) load_qk(c - 1);  // in flight through this chunk's work
         __syncthreads();
         {  // gam-scaled dO for the dM update
             const int r = tid / (BV / 4), j = 4 * (tid % (BV / 4));
@@ -1348,6 +1360,7 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             scan(c - 1);
             if (c > 1) load_ba(c - 2);
         }
+        if (c > 0) load_d(c - 1);
         __syncthreads();
         {  // dU = P^T dO + diag(w) K~ dM on this wave's tile, as hi/lo bf16
             v4f du = zero4();
@@ -1363,6 +1376,7 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
                 sdUl[r * PVH + j] = bf16_bits(x - __uint_as_float(uint32_t(h) << 16));
             }
         }
+        if (c > 0) load_t(c - 1);
         __syncthreads();
         {  // dR = T^T dU (T^T upper triangular: k-steps from the tile's first row on); -gam b dR
             v4f dr = zero4();
