@@ -886,6 +886,7 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             dr = mfma32(th, ul, dr);
             dr = mfma32(tl, uh, dr);
         }
+        v4f gvt;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = R0 + 4 * lq + e, j = jt + lr;
@@ -893,7 +894,12 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             sGDRb[r * PVH + j] = bf16_bits(-sgam[r] * sb[r] * dr[e]);
             pgr[e] += dr[e] * km[e];
             pdb[e] += dr[e] * y[e];
-            if (r < n) gvc[r * DV + s0 + j] = from_f32<bf16_t>(sb[r] * dr[e]);
+            gvt[e] = sb[r] * dr[e];
+        }
+        gvt = quad_transpose(gvt, lane);  // row R0 + 4 lq + lr % 4, columns jt + 4 (lr / 4) ..
+        {
+            const int r = R0 + 4 * lq + (lr & 3);
+            if (r < n) store4(gvc + r * DV + s0 + jt + 4 * (lr >> 2), gvt);
         }
         __syncthreads();
         // dP += dO U^T, dA += dR U^T (negated later) on this wave's score tiles, and the
@@ -949,24 +955,21 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             colp += ex;
             rowb[e] += da * as[e];
         }
-        colp += __shfl_xor(colp, 16);
-        colp += __shfl_xor(colp, 32);
+        colp = sum_rows(colp);
         if (lq == 0) scol[rw][16 * t + lr] = colp;
     });
-    // row sums: across the 16 lanes of a row, then (below) across the two halves
+    // row sums: across the 16 lanes of a row (total in its last lane), then (below) across the
+    // two halves
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-#pragma unroll
-        for (int m = 1; m < 16; m <<= 1) {
-            pgo[e] += __shfl_xor(pgo[e], m);
-            pgr[e] += __shfl_xor(pgr[e], m);
-            pew[e] += __shfl_xor(pew[e], m);
-            pdb[e] += __shfl_xor(pdb[e], m);
-            rowp[e] += __shfl_xor(rowp[e], m);
-            rowb[e] += __shfl_xor(rowb[e], m);
-        }
+        pgo[e] = row16_total(pgo[e]);
+        pgr[e] = row16_total(pgr[e]);
+        pew[e] = row16_total(pew[e]);
+        pdb[e] = row16_total(pdb[e]);
+        rowp[e] = row16_total(rowp[e]);
+        rowb[e] = row16_total(rowb[e]);
     }
-    if (lr == 0) {
+    if (lr == 15) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = R0 + 4 * lq + e;
@@ -990,14 +993,25 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             sGb[i * PCH + j] = bf16_bits(adA[I][e] * G * sb[i]);
         }
     });
-    float dfin[NFH][4];  // d at this lane's output positions, loaded ahead of the products
+    // the outputs leave as 4-vectors: after a quad transpose lane (lq, lr) holds row
+    // R0 + 4 lq + lr % 4, features 16 tile + 4 (lr / 4) .. +3; d there, loaded ahead of the
+    // products
+    const int ro = R0 + 4 * lq + (lr & 3), fo = 4 * (lr >> 2);
+    float dfin[NFH][4];
 #pragma unroll
-    for (int t = 0; t < NFH; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = R0 + 4 * lq + e;
-            dfin[t][e] = to_f32(dc[(r < n ? r : n - 1) * DK + 16 * (NFH * hw + t) + lr]);
+    for (int t = 0; t < NFH; ++t) {
+        float d8[8];
+        const int off = (ro < n ? ro : n - 1) * DK + 16 * (NFH * hw + t) + fo;
+        if constexpr (sizeof(TD) == 4) {
+            const float4 x = *reinterpret_cast<const float4 *>(dc + off);
+            d8[0] = x.x; d8[1] = x.y; d8[2] = x.z; d8[3] = x.w;
+        } else {
+            const uint2 x = *reinterpret_cast<const uint2 *>(dc + off);
+            d8[0] = bf_lo(x.x); d8[1] = bf_hi(x.x); d8[2] = bf_lo(x.y); d8[3] = bf_hi(x.y);
         }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dfin[t][e] = d8[e];
+    }
     __syncthreads();
     if (tid < 64) {  // dbeta; dg of every row, then its reverse running sum d ln(alpha) (wave 0)
         const int r = lane;
@@ -1036,17 +1050,24 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
         }
     }
 #pragma unroll
-    for (int t = 0; t < NFH; ++t)
+    for (int t = 0; t < NFH; ++t) {
+        const v4f gqt = quad_transpose(aQ[t], lane), gkt = quad_transpose(aK[t], lane);
+        const v4f gkw = quad_transpose(aKt[t], lane);  // dK~
+        const int f = 16 * (NFH * hw + t) + fo;
+        const uint2 kr = *reinterpret_cast<const uint2 *>(&sK[ro * PH + f]);
+        const float kv[4] = {bf_lo(kr.x), bf_hi(kr.x), bf_lo(kr.y), bf_hi(kr.y)};
+        v4f gk4, gd4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int r = R0 + 4 * lq + e, f = 16 * (NFH * hw + t) + lr;
-            if (r < n) {
-                const int ix = r * DK + f;
-                gqc[ix] = from_f32<bf16_t>(aQ[t][e]);
-                gkc[ix] = from_f32<bf16_t>(aK[t][e] + aKt[t][e] * dfin[t][e]);
-                gdc[ix] = from_f32<TD>(aKt[t][e] * __uint_as_float(uint32_t(sK[r * PH + f]) << 16));
-            }
+            gk4[e] = gkt[e] + gkw[e] * dfin[t][e];
+            gd4[e] = gkw[e] * kv[e];
         }
+        if (ro < n) {
+            store4(gqc + ro * DK + f, gqt);
+            store4(gkc + ro * DK + f, gk4);
+            store4(gdc + ro * DK + f, gd4);
+        }
+    }
 }
 
 // ---- (I + A)^{-1} of every chunk (bf16 inputs, C = 64) ---------------------------------------
@@ -1408,13 +1429,15 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
                     acc = mfma32(frag_cols(sQ, PH, k0, f0, lr, lq), frag_cols(sGDOb, PVH, k0, c0, lr, lq), acc);
                     acc = mfma32(frag_cols(sK, PH, k0, f0, lr, lq), frag_cols(sGDRb, PVH, k0, c0, lr, lq), acc);
                 }
-                float *ck = dMck + ((bh * nch + (c > 0 ? c - 1 : 0)) * DK + f0) * dv + j0 + c0;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int f = f0 + 4 * lq + e, j = c0 + lr;
                     dM[m][e] = gl * dM[m][e] + acc[e];
                     sdMb[f * PVH + j] = bf16_bits(dM[m][e]);
-                    if (c > 0) ck[(4 * lq + e) * dv + lr] = dM[m][e];
+                }
+                if (c > 0) {  // row f0 + 4 lq + lr % 4, columns c0 + 4 (lr / 4) .. +3
+                    const v4f x = quad_transpose(dM[m], lane);
+                    store4(dMck + ((bh * nch + c - 1) * DK + f0 + 4 * lq + (lr & 3)) * dv + j0 + c0 + 4 * (lr >> 2), x);
                 }
             }
         }
@@ -1423,9 +1446,8 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             const int ti = MT * wave + m, f0 = 16 * (ti >> 1), c0 = 16 * (ti & 1);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                dS0[(bh * DK + f0 + 4 * lq + e) * dv + j0 + c0 + lr] = dM[m][e];
+            const v4f x = quad_transpose(dM[m], lane);
+            store4(dS0 + (bh * DK + f0 + 4 * lq + (lr & 3)) * dv + j0 + c0 + 4 * (lr >> 2), x);
         }
     }
 }

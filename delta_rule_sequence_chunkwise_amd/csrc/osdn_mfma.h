@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "osdn_internal.h"
 
 namespace osdn {
@@ -123,6 +125,40 @@ __device__ __forceinline__ float sum_rows(float x) {
     const uint32_t c = __float_as_uint(y);
     const u32x2 t = __builtin_amdgcn_permlane16_swap(c, c, false, false);
     return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+
+// sum of x over the 16 lanes of each row (inclusive prefix sums by DPP row shifts), valid in
+// the row's last lane
+__device__ __forceinline__ float row16_total(float x) {
+    x = dpp_add<0x111, 0xf>(x);  // row_shr:1
+    x = dpp_add<0x112, 0xf>(x);  // row_shr:2
+    x = dpp_add<0x114, 0xf>(x);  // row_shr:4
+    return dpp_add<0x118, 0xf>(x);  // row_shr:8
+}
+// 4 x 4 transpose inside each quad of lanes by two DPP exchange stages: lane 4a + l holds
+// x[e] = X[l][e] on entry and X[e][l] on return.  On a 16x16 tile in the MFMA C layout (lane
+// (q, n) holds rows 4q..4q+3 of column n) lane (q, n) then holds row 4q + (n & 3), columns
+// 4 (n >> 2) .. +3, ready for one vector store.
+__device__ __forceinline__ v4f quad_transpose(v4f x, int lane) {
+    const bool o1 = lane & 1, o2 = lane & 2;
+    auto xch = [](float v, auto ctrl) {
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), decltype(ctrl)::value, 0xf, 0xf, false));
+    };
+    using X1 = std::integral_constant<int, 0xB1>;  // quad_perm [1, 0, 3, 2]
+    using X2 = std::integral_constant<int, 0x4E>;  // quad_perm [2, 3, 0, 1]
+    const float r01 = xch(o1 ? x[0] : x[1], X1{}), r23 = xch(o1 ? x[2] : x[3], X1{});
+    v4f z;
+    z[0] = o1 ? r01 : x[0];
+    z[1] = o1 ? x[1] : r01;
+    z[2] = o1 ? r23 : x[2];
+    z[3] = o1 ? x[3] : r23;
+    const float r02 = xch(o2 ? z[0] : z[2], X2{}), r13 = xch(o2 ? z[1] : z[3], X2{});
+    v4f y;
+    y[0] = o2 ? r02 : z[0];
+    y[2] = o2 ? z[2] : r02;
+    y[1] = o2 ? r13 : z[1];
+    y[3] = o2 ? z[3] : r13;
+    return y;
 }
 
 // four consecutive outputs from fp32 accumulators: 16 bytes (fp32) or 8 bytes (bf16)
