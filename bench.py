@@ -19,10 +19,10 @@ HBM.  Prints ONE JSON line.  Besides the contract fields it carries:
   kda           the forward with the channel-wise gate (osdn_chunk_fwd_kda: the gate-scaling
                 kernel, then the chunkwise forward) on the same workload with a per-feature
                 gate, with its HBM roofline and the parity of its output;
-  bwd           the backward (osdn_chunk_bwd: forward state checkpoints, the reverse pass over
-                chunks, the per-chunk gradients) on the same workload with seeded output
-                gradients, with its HBM roofline, its fp32 vector-ALU FLOP count, and the float64
-                reverse pass on one sampled sequence (parity and CPU baseline).
+  bwd           the backward (osdn_chunk_bwd: forward state checkpoints, the chunk inverses, the
+                reverse pass over chunks, the per-chunk gradients) on the same workload with
+                seeded output gradients, with its HBM roofline, its matrix-core FLOP count, and
+                the float64 reverse pass on one sampled sequence (parity and CPU baseline).
 """
 from __future__ import annotations
 
@@ -228,11 +228,12 @@ def main():
 
 
 def bwd_flops_per_head_token(dk, dv, C):
-    """fp32 FLOPs per head-token of the three backward launches, counting useful triangular
-    halves: the forward recompute (the forward's count), the reverse pass (K~ dM, Q^T dO,
-    K^T dR: 3 dk dv MACs; P^T dO and the solve: C dv; the Gram and P: C dk) and the per-chunk
-    pass (K M0, Q M0, K~ dMC and the three dk x dv gradient products: 6 dk dv; two solves,
-    P^T dO, dP and dA: 2.5 C dv; the Gram, P and the four C-contractions: 3 C dk)."""
+    """FLOPs per head-token of the backward launches, counting useful triangular halves: the
+    forward recompute (the forward's count), the reverse pass with the chunk inverses (K~ dM,
+    Q^T dO, K^T dR: 3 dk dv MACs; P^T dO and T^T dU: C dv; the Gram and P: C dk) and the
+    per-chunk pass (K M0, Q M0, K~ dMC and the three dk x dv gradient products: 6 dk dv; T R,
+    T^T dU, P^T dO, dP and dA: 2.5 C dv; the Gram, P and the four C-contractions: 3 C dk).
+    Split-precision products count once."""
     fwd = flops_per_head_token(dk, dv, C)
     rev = 2 * (3 * dk * dv + C * dv + C * dk)
     per_chunk = 2 * (6 * dk * dv + 2.5 * C * dv + 3 * C * dk)
@@ -276,11 +277,12 @@ def bench_bwd(n_steps, torch, dev, synth, w, x, fwd, cpu):
            "roofline": {"bound": "hbm", "achieved": round(alg / per / 1e9, 2),
                         "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                         "frac": round(alg / per / PEAK_HBM, 5), "alg_bytes_per_step": alg,
-                        "note": "three launches; the state checkpoints (2 x 268 MB written and "
-                                "read) are beyond alg"},
-           "alu": {"achieved": round(flops / per / 1e12, 3), "peak": 157.3, "unit": "TFLOP/s",
-                   "frac": round(flops / per / 157.3e12, 5), "flops_per_step": flops,
-                   "note": "fp32 vector arithmetic in this version"}}
+                        "note": "four launches; the state checkpoints (bf16, 2 x 134 MB written "
+                                "and read) and the chunk inverses (67 MB) are beyond alg"},
+           "mfma": {"achieved": round(flops / per / 1e12, 3), "peak": PEAK_BF16 / 1e12,
+                    "unit": "TFLOP/s", "frac": round(flops / per / PEAK_BF16, 5),
+                    "flops_per_step": flops,
+                    "note": "useful FLOPs; the products run on bf16 matrix cores"}}
     if cpu:
         from oracle import backward
         b, h = 0, 0

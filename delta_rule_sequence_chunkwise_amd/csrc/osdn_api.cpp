@@ -372,8 +372,8 @@ osdn_status osdn_step_kda(const void *q, const void *k, const void *v, const flo
 
 namespace {
 
-// bytes of each of the two state checkpoints of the backward, [BH, nchunks, dk, dv] fp32;
-// -1 if the sizes are invalid
+// bytes of each of the two state checkpoints of the backward, [BH, nchunks, dk, dv] (bf16 for
+// bf16 inputs, fp32 for fp32 inputs); -1 if the sizes are invalid
 int64_t bwd_ckpt_bytes(int64_t B, int64_t H, int64_t T, int32_t dk, int32_t dv, osdn_dtype qkv) {
     if (B < 0 || H < 0 || T < 0 || !dtype_ok(qkv) || !head_dim_ok(dk) || !head_dim_ok(dv))
         return -1;
@@ -382,7 +382,7 @@ int64_t bwd_ckpt_bytes(int64_t B, int64_t H, int64_t T, int32_t dk, int32_t dv, 
     if (!mul_ok(n, B, kMaxElems) || !mul_ok(n, H, kMaxElems) ||
         !mul_ok(n, (T + C - 1) / C, kMaxElems) || !mul_ok(n, int64_t(dk) * dv, kMaxElems))
         return -1;
-    return round256(n * 4);
+    return round256(n * (qkv == OSDN_BF16 ? 2 : 4));
 }
 
 // bytes of the chunk inverses of the backward (bf16 inputs: two bf16 64 x 64 planes per chunk;
@@ -479,8 +479,7 @@ osdn_status osdn_chunk_bwd(const void *q, const void *k, const void *v, const fl
     char *ws = static_cast<char *>(workspace);
     osdn::BwdArgs a{q, k, v, d, beta, alpha, S0, grad_o, grad_S_T, grad_q, grad_k, grad_v,
                     grad_beta, grad_alpha, grad_d, grad_S0,
-                    T > 0 ? reinterpret_cast<float *>(ws) : nullptr,
-                    T > 0 ? reinterpret_cast<float *>(ws + ck) : nullptr,
+                    T > 0 ? ws : nullptr, T > 0 ? ws + ck : nullptr,
                     T > 0 && tk > 0 ? reinterpret_cast<uint16_t *>(ws + 2 * ck) : nullptr, BH, T,
                     dk, dv, qkv, d_dtype};
     const hipError_t err = osdn::launch_chunk_bwd(a, static_cast<hipStream_t>(stream));

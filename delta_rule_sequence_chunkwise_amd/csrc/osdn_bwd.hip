@@ -649,8 +649,8 @@ __global__ void __launch_bounds__(2 * NT)
 bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                       const bf16_t *__restrict__ v, const TD *__restrict__ d,
                       const float *__restrict__ beta, const float *__restrict__ alpha,
-                      const bf16_t *__restrict__ dO, const float *__restrict__ Mck,
-                      const float *__restrict__ dMck, const uint16_t *__restrict__ Tck,
+                      const bf16_t *__restrict__ dO, const uint16_t *__restrict__ Mck,
+                      const uint16_t *__restrict__ dMck, const uint16_t *__restrict__ Tck,
                       bf16_t *__restrict__ gq, bf16_t *__restrict__ gk, bf16_t *__restrict__ gv,
                       float *__restrict__ gbeta, TD *__restrict__ gd,
                       float *__restrict__ galpha, int64_t T, int64_t nch) {
@@ -658,7 +658,7 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
     constexpr int PH = DK + 8, PCH = C + 8, PVH = BV + 8;  // bf16 pitches
     constexpr int NF = DK / 16, NFH = NF / 2;  // feature tiles; per half
     constexpr int MB = 2 * DK * PVH > C * PCH ? 2 * DK * PVH : C * PCH;
-    constexpr int MU = DK * BV / 4 / NTH;      // float4 units of an M0 (dMC) slice per thread
+    constexpr int MU = DK * BV / 4 / NTH;      // 4-value units of an M0 (dMC) slice per thread
     static_assert(MU == 1 || MU == 2, "one or two M units per thread");
     static_assert(C * BV / 4 == NTH, "one 4-value unit of v and dO per thread");
     __shared__ alignas(16) uint16_t sQ[C * PH], sK[C * PH], sKt[C * PH];
@@ -683,8 +683,8 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
     const int lr = lane & 15, lq = lane >> 4;
     const int R0 = 16 * rw;  // this wave's rows
     const int jt = 16 * hw;  // this wave's columns of the value slice
-    const float *M0 = Mck + (bh * nch + c) * DK * DV;
-    const float *dMC = dMck + (bh * nch + c) * DK * DV;
+    const uint16_t *M0 = Mck + (bh * nch + c) * DK * DV;  // bf16
+    const uint16_t *dMC = dMck + (bh * nch + c) * DK * DV;
     // the chunk's rows of every per-token array: uniform bases, 32-bit offsets
     const bf16_t *vc = v + row0 * DV, *oc = dO + row0 * DV;
     bf16_t *gvc = gv + row0 * DV, *gqc = gq + row0 * DK, *gkc = gk + row0 * DK;
@@ -777,22 +777,20 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
     float pew[4] = {0.f, 0.f, 0.f, 0.f}, pdb[4] = {0.f, 0.f, 0.f, 0.f};
     float frob = 0.f;
 
-    // the value slice's M0, dMC (fp32, four per 16-byte unit) and v, dO (bf16, four per 8-byte
-    // unit) pass through named registers one slice ahead (an array carried across the loop
-    // would live in scratch)
-    float4 m0a = make_float4(0.f, 0.f, 0.f, 0.f), m0b = m0a, dma = m0a, dmb = m0a;
-    uint2 vu = make_uint2(0, 0), ou = make_uint2(0, 0);
+    // the value slice's M0, dMC, v and dO (bf16, four per 8-byte unit) pass through named
+    // registers one slice ahead (an array carried across the loop would live in scratch)
+    uint2 m0a = make_uint2(0, 0), m0b = m0a, dma = m0a, dmb = m0a, vu = m0a, ou = m0a;
 #define OSDN_BWD_LOAD_SLICE(S0)                                                               \
     do {                                                                                      \
         {                                                                                     \
             const int f = tid / (BV / 4), j = 4 * (tid % (BV / 4));                          \
-            m0a = *reinterpret_cast<const float4 *>(M0 + f * DV + (S0) + j);                  \
-            dma = *reinterpret_cast<const float4 *>(dMC + f * DV + (S0) + j);                 \
+            m0a = *reinterpret_cast<const uint2 *>(M0 + f * DV + (S0) + j);                   \
+            dma = *reinterpret_cast<const uint2 *>(dMC + f * DV + (S0) + j);                  \
         }                                                                                     \
         if constexpr (MU == 2) {                                                              \
             const int u = tid + NTH, f = u / (BV / 4), j = 4 * (u % (BV / 4));               \
-            m0b = *reinterpret_cast<const float4 *>(M0 + f * DV + (S0) + j);                  \
-            dmb = *reinterpret_cast<const float4 *>(dMC + f * DV + (S0) + j);                 \
+            m0b = *reinterpret_cast<const uint2 *>(M0 + f * DV + (S0) + j);                   \
+            dmb = *reinterpret_cast<const uint2 *>(dMC + f * DV + (S0) + j);                  \
         }                                                                                     \
         {                                                                                     \
             const int r = tid / (BV / 4), j = 4 * (tid % (BV / 4));                          \
@@ -809,12 +807,11 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
 #pragma unroll
         for (int i = 0; i < MU; ++i) {
             const int u = tid + i * NTH, f = u / (BV / 4), j = 4 * (u % (BV / 4));
-            const float4 mm4 = i == 0 ? m0a : m0b, dd4 = i == 0 ? dma : dmb;
-            *reinterpret_cast<uint2 *>(&sM0b[f * PVH + j]) =
-                make_uint2(pack2(mm4.x, mm4.y), pack2(mm4.z, mm4.w));
-            *reinterpret_cast<uint2 *>(&sdMb[f * PVH + j]) =
-                make_uint2(pack2(dd4.x, dd4.y), pack2(dd4.z, dd4.w));
-            frob += mm4.x * dd4.x + mm4.y * dd4.y + mm4.z * dd4.z + mm4.w * dd4.w;
+            const uint2 mm = i == 0 ? m0a : m0b, dd = i == 0 ? dma : dmb;
+            *reinterpret_cast<uint2 *>(&sM0b[f * PVH + j]) = mm;
+            *reinterpret_cast<uint2 *>(&sdMb[f * PVH + j]) = dd;
+            frob += bf_lo(mm.x) * bf_lo(dd.x) + bf_hi(mm.x) * bf_hi(dd.x) +
+                    bf_lo(mm.y) * bf_lo(dd.y) + bf_hi(mm.y) * bf_hi(dd.y);
         }
         {  // v into sRh (R replaces it in place), dO and gam dO; rows past the end are zero
             const int r = tid / (BV / 4), j = 4 * (tid % (BV / 4));
@@ -1161,8 +1158,8 @@ bwd_tinv_kernel(const bf16_t *__restrict__ k, const TD *__restrict__ d,
 // ---- reverse pass over chunks on bf16 matrix cores (bf16 inputs, C = 64) --------------------
 // Same data flow as bwd_state_kernel, on eight waves (two per SIMD).  One workgroup per
 // (sequence, 32-column value slice) walks the chunks backwards.  dM (fp32, dk x 32) lives in
-// registers: wave w owns its 16x16 tiles in the MFMA C layout and stores them straight to the
-// checkpoint; LDS holds its bf16 copy, the operand of K~ dM.  Per chunk, with a barrier after
+// registers: wave w owns its 16x16 tiles in the MFMA C layout and stores them, rounded to bf16,
+// straight to the checkpoint; LDS holds the same bf16 copy, the operand of K~ dM.  Per chunk, with a barrier after
 // each phase:
 //   stores   the chunk's q, k, K~ = d (.) k, T planes and dO (prefetched into registers one
 //            chunk ahead) into LDS, and the next chunk's loads issued;
@@ -1177,7 +1174,7 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
                       const TD *__restrict__ d, const float *__restrict__ beta,
                       const float *__restrict__ alpha, const bf16_t *__restrict__ dO,
                       const float *__restrict__ dS_T, const uint16_t *__restrict__ Tck,
-                      float *__restrict__ dMck, float *__restrict__ dS0, int64_t T, int dv) {
+                      uint16_t *__restrict__ dMck, float *__restrict__ dS0, int64_t T, int dv) {
     constexpr int C = 64, NW = 8, NTH = NW * 64;
     constexpr int PH = DK + 8, PCH = C + 8, PVH = BV + 8;  // bf16 pitches
     constexpr int G = DK / 8, NU = C * G / NTH;  // 16-byte units of a Q/K row; units per thread
@@ -1288,7 +1285,7 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             const int f = f0 + 4 * lq + e, j = c0 + lr;
             dM[m][e] = dS_T ? dS_T[(bh * DK + f) * dv + j0 + j] : 0.f;
             sdMb[f * PVH + j] = bf16_bits(dM[m][e]);
-            if (nch > 0) dMck[((bh * nch + nch - 1) * DK + f) * dv + j0 + j] = dM[m][e];
+            if (nch > 0) dMck[((bh * nch + nch - 1) * DK + f) * dv + j0 + j] = bf16_bits(dM[m][e]);
         }
     }
     for (int i = tid; i < C * PCH; i += NTH) sPb[i] = 0;  // tiles above the diagonal stay zero
@@ -1435,9 +1432,10 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
                     dM[m][e] = gl * dM[m][e] + acc[e];
                     sdMb[f * PVH + j] = bf16_bits(dM[m][e]);
                 }
-                if (c > 0) {  // row f0 + 4 lq + lr % 4, columns c0 + 4 (lr / 4) .. +3
-                    const v4f x = quad_transpose(dM[m], lane);
-                    store4(dMck + ((bh * nch + c - 1) * DK + f0 + 4 * lq + (lr & 3)) * dv + j0 + c0 + 4 * (lr >> 2), x);
+                if (c > 0) {  // bf16, row f0 + 4 lq + lr % 4, columns c0 + 4 (lr / 4) .. +3
+                    const uint2 x = pack4u(quad_transpose(dM[m], lane));
+                    *reinterpret_cast<uint2 *>(dMck + ((bh * nch + c - 1) * DK + f0 + 4 * lq + (lr & 3)) * dv +
+                                               j0 + c0 + 4 * (lr >> 2)) = x;
                 }
             }
         }
@@ -1478,14 +1476,15 @@ hipError_t bwd_typed(const BwdArgs &a, hipStream_t stream) {
                            dim3(static_cast<unsigned>(a.BH * (DV / BVA))), dim3(2 * NT), 0, stream,
                            static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.k),
                            static_cast<const TD *>(a.d), a.beta, a.alpha,
-                           static_cast<const bf16_t *>(a.dO), a.dS_T, a.Tck, a.dMck, a.dS0,
-                           a.T, DV);
+                           static_cast<const bf16_t *>(a.dO), a.dS_T, a.Tck,
+                           static_cast<uint16_t *>(a.dMck), a.dS0, a.T, DV);
     } else
     hipLaunchKernelGGL((bwd_state_kernel<C, DK, BVA, TQ, TD>),
                        dim3(static_cast<unsigned>(a.BH * (DV / BVA))), dim3(NT), 0, stream,
                        static_cast<const TQ *>(a.q), static_cast<const TQ *>(a.k),
                        static_cast<const TD *>(a.d), a.beta, a.alpha,
-                       static_cast<const TQ *>(a.dO), a.dS_T, a.dMck, a.dS0, a.T, DV);
+                       static_cast<const TQ *>(a.dO), a.dS_T, static_cast<float *>(a.dMck), a.dS0,
+                       a.T, DV);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || nch == 0) return e;
     if constexpr (sizeof(TQ) == 2) {
@@ -1493,7 +1492,8 @@ hipError_t bwd_typed(const BwdArgs &a, hipStream_t stream) {
                            dim3(static_cast<unsigned>(a.BH * nch)), dim3(2 * NT), 0, stream,
                            static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.k),
                            static_cast<const bf16_t *>(a.v), static_cast<const TD *>(a.d),
-                           a.beta, a.alpha, static_cast<const bf16_t *>(a.dO), a.Mck, a.dMck,
+                           a.beta, a.alpha, static_cast<const bf16_t *>(a.dO),
+                           static_cast<const uint16_t *>(a.Mck), static_cast<const uint16_t *>(a.dMck),
                            a.Tck, static_cast<bf16_t *>(a.gq), static_cast<bf16_t *>(a.gk),
                            static_cast<bf16_t *>(a.gv), a.gbeta, static_cast<TD *>(a.gd),
                            a.galpha, a.T, nch);
@@ -1503,7 +1503,8 @@ hipError_t bwd_typed(const BwdArgs &a, hipStream_t stream) {
                            dim3(static_cast<unsigned>(a.BH * nch)), dim3(NT), 0, stream,
                            static_cast<const TQ *>(a.q), static_cast<const TQ *>(a.k),
                            static_cast<const TQ *>(a.v), static_cast<const TD *>(a.d), a.beta,
-                           a.alpha, static_cast<const TQ *>(a.dO), a.Mck, a.dMck,
+                           a.alpha, static_cast<const TQ *>(a.dO), static_cast<const float *>(a.Mck),
+                           static_cast<const float *>(a.dMck),
                            static_cast<TQ *>(a.gq), static_cast<TQ *>(a.gk),
                            static_cast<TQ *>(a.gv), a.gbeta, static_cast<TD *>(a.gd), a.galpha,
                            a.T, nch);

@@ -263,7 +263,7 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                   const uint16_t *__restrict__ v, const TD *__restrict__ d,
                   const float *__restrict__ beta, const float *__restrict__ alpha,
                   const float *S0, uint16_t *__restrict__ o, float *S_T, int64_t BH,
-                  int64_t T, int dv, const float *__restrict__ gcs, float *__restrict__ ckpt) {
+                  int64_t T, int dv, const float *__restrict__ gcs, uint16_t *__restrict__ ckpt) {
     using L = Lds<DK, GATE>;
     constexpr int NS = DK / 32;   // 32-wide k-steps over the key features
     constexpr int NFT = DK / 16;  // 16-row feature tiles of the state
@@ -357,12 +357,14 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
         for (int64_t c = -2; c < nchunks; ++c) {
             if (c >= 0) {
                 // ---- chunk c: R, U, read-out, carry --------------------------------------------
-                if constexpr (CKPT) {  // the state at this chunk's start, for the backward
-                    float *dst = ckpt + (bh * nchunks + c) * DK * dv + j0 + VW * ct + lr;
+                if constexpr (CKPT) {  // the state at this chunk's start in bf16, for the backward:
+                                       // row 16 ft + 4 lq + lr % 4, columns 4 (lr / 4) .. +3 of
+                                       // the wave's 16 after a quad transpose
+                    uint16_t *dst = ckpt + (bh * nchunks + c) * DK * dv + (4 * lq + (lr & 3)) * dv +
+                                    j0 + VW * ct + 4 * (lr >> 2);
 #pragma unroll
                     for (int ft = 0; ft < NFT; ++ft)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) dst[(16 * ft + 4 * lq + i) * dv] = M[ft][i];
+                        *reinterpret_cast<uint2 *>(dst + 16 * ft * dv) = pack4u(quad_transpose(M[ft], lane));
                 }
                 const int b = static_cast<int>(c & 1);
                 const int n = rows_of(c);
@@ -711,7 +713,8 @@ hipError_t launch_typed(const ChunkArgs &a, hipStream_t stream) {
                        stream, static_cast<const uint16_t *>(a.q),                             \
                        static_cast<const uint16_t *>(a.k), static_cast<const uint16_t *>(a.v), \
                        static_cast<const TD *>(a.d), a.beta, a.alpha, a.S0,                    \
-                       static_cast<uint16_t *>(a.o), a.S_T, a.BH, a.T, a.dv, a.gcs, a.ckpt)
+                       static_cast<uint16_t *>(a.o), a.S_T, a.BH, a.T, a.dv, a.gcs,            \
+                       static_cast<uint16_t *>(a.ckpt))
     if (a.gcs) OSDN_CHUNK_LAUNCH(true, false);
     else if (a.ckpt) OSDN_CHUNK_LAUNCH(false, true);
     else OSDN_CHUNK_LAUNCH(false, false);

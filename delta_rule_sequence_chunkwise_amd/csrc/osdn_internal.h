@@ -42,7 +42,8 @@ struct ChunkArgs {
     osdn_dtype qkv, d_dtype;
     const float *gcs = nullptr;  // [BH, nchunks, dk]: per-feature factor applied to the
                                  // state's rows after each chunk's carry (channel-wise gate)
-    float *ckpt = nullptr;       // [BH, nchunks, dk, dv]: the state at every chunk start
+    void *ckpt = nullptr;        // [BH, nchunks, dk, dv]: the state at every chunk start, fp32
+                                 // from the fp32 forward, bf16 from the matrix-core forward
                                  // (then o is not written and may be NULL; no channel gate)
 };
 
@@ -55,7 +56,8 @@ struct BwdArgs {
     float *gbeta, *galpha;
     void *gd;             // d dtype
     float *dS0;
-    float *Mck, *dMck;    // workspace: [BH, nchunks, dk, dv] each
+    void *Mck, *dMck;     // workspace: [BH, nchunks, dk, dv] each, bf16 for bf16 inputs (the
+                          // precision the matrix products take them in), else fp32
     uint16_t *Tck;        // workspace (bf16 inputs): (I + A)^{-1} of every chunk, [BH, nchunks,
                           // 2, 64, 64] bf16, planes hi = bf16(T) and lo = bf16(T - hi)
     int64_t BH, T;
