@@ -233,3 +233,44 @@ def test_step_kda_rejects(L):
     bad = list(args)
     bad[8] = 0
     assert L.osdn_step_kda(*bad) == 0
+
+
+def call_bwd(L, **over):
+    a = dict(q=addr(1), k=addr(2), v=addr(3), beta=addr(4), d=addr(5), alpha=addr(6),
+             S0=addr(7), go=addr(8), gST=addr(9), gq=addr(10), gk=addr(11), gv=addr(12),
+             gb=addr(13), gd=addr(14), ga=addr(15), gS0=addr(16), ws=addr(17), wsb=1 << 31,
+             B=2, H=3, T=100, dk=128, dv=64, qkv=osdn.OSDN_BF16, d_dtype=osdn.OSDN_F32,
+             stream=None)
+    a.update(over)
+    return L.osdn_chunk_bwd(a["q"], a["k"], a["v"], a["beta"], a["d"], a["alpha"], a["S0"],
+                            a["go"], a["gST"], a["gq"], a["gk"], a["gv"], a["gb"], a["gd"],
+                            a["ga"], a["gS0"], a["ws"], a["wsb"], a["B"], a["H"], a["T"],
+                            a["dk"], a["dv"], a["qkv"], a["d_dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), -1), (dict(go=None), -1), (dict(gd=None), -1), (dict(ws=None), -1),
+    (dict(T=-1), -2), (dict(wsb=1000), -2), (dict(dk=96), -3), (dict(qkv=7), -3),
+    (dict(q=addr(1) + 8), -4), (dict(ws=addr(17) + 128), -4), (dict(gb=addr(13) + 2), -4),
+    (dict(gq=addr(1)), -5), (dict(ws=addr(8)), -5), (dict(gk=addr(10) + 256), -5),
+    (dict(gS0=addr(17) + 4096), -5),
+])
+def test_chunk_bwd_rejects(L, over, status):
+    assert call_bwd(L, **over) == status
+
+
+def test_bwd_workspace_size(L):
+    # bf16 inputs: two bf16 checkpoints [B,H,nchunks,dk,dv] (64-row chunks) and the chunk
+    # inverses (two bf16 64 x 64 planes per chunk), each rounded up to 256 bytes
+    nch = (100 + 63) // 64
+    ck = 2 * 3 * nch * 128 * 64 * 2
+    ti = 2 * 3 * nch * 2 * 64 * 64 * 2
+    assert L.osdn_chunk_bwd_workspace(2, 3, 100, 128, 64, osdn.OSDN_BF16) == 2 * ck + ti
+    # fp32 inputs: two fp32 checkpoints (32-row chunks), no inverses
+    nch = (100 + 31) // 32
+    assert L.osdn_chunk_bwd_workspace(2, 3, 100, 128, 64, osdn.OSDN_F32) == 2 * (2 * 3 * nch * 128 * 64 * 4)
+    assert L.osdn_chunk_bwd_workspace(2, 3, 100, 96, 64, osdn.OSDN_BF16) == -1
+    assert L.osdn_chunk_bwd_workspace(2, 3, -1, 128, 64, osdn.OSDN_BF16) == -1
+    need = L.osdn_chunk_bwd_workspace(2, 3, 100, 128, 64, osdn.OSDN_BF16)
+    assert call_bwd(L, wsb=need - 1) == -2
+    assert call_bwd(L, B=0) == 0
