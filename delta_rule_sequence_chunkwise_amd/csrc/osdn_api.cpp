@@ -385,14 +385,15 @@ int64_t bwd_ckpt_bytes(int64_t B, int64_t H, int64_t T, int32_t dk, int32_t dv, 
     return round256(n * (qkv == OSDN_BF16 ? 2 : 4));
 }
 
-// bytes of the chunk inverses of the backward (bf16 inputs: two bf16 64 x 64 planes per chunk;
-// fp32 inputs: none); called after bwd_ckpt_bytes has accepted the sizes
+// bytes of the per-chunk planes of the backward (bf16 inputs: three bf16 64 x 64 planes per
+// chunk, the inverse's hi and lo and the scores; fp32 inputs: none); called after
+// bwd_ckpt_bytes has accepted the sizes
 int64_t bwd_tinv_bytes(int64_t B, int64_t H, int64_t T, osdn_dtype qkv) {
     if (qkv != OSDN_BF16) return 0;
     const int64_t C = osdn::bwd_chunk_size(qkv);
     int64_t n = 1;
     if (!mul_ok(n, B, kMaxElems) || !mul_ok(n, H, kMaxElems) ||
-        !mul_ok(n, (T + C - 1) / C, kMaxElems) || !mul_ok(n, 2 * C * C, kMaxElems))
+        !mul_ok(n, (T + C - 1) / C, kMaxElems) || !mul_ok(n, 3 * C * C, kMaxElems))
         return -1;
     return round256(n * 2);
 }

@@ -694,8 +694,8 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
     {  // Q, K, K~ = d (.) k as bf16 (8 features per 16-byte unit) and the T planes, all loads
        // issued first
         constexpr int G = DK / 8, NU = C * G / NTH;  // units per row, units per thread
-        constexpr int TU = 2 * C * C / 8 / NTH;      // 16-byte units of the T planes per thread
-        static_assert(NU * NTH == C * G && TU == 2, "whole units");
+        constexpr int TU = 3 * C * C / 8 / NTH;      // 16-byte units of the T, P planes per thread
+        static_assert(NU * NTH == C * G && TU == 3, "whole units");
         uint4 qu[NU], ku[NU], tu[TU];
         float dd[NU][8];
 #pragma unroll
@@ -706,13 +706,13 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             ku[i] = *reinterpret_cast<const uint4 *>(k + e);
             load8(d + e, dd[i]);
         }
-        const uint4 *tp = reinterpret_cast<const uint4 *>(Tck + (bh * nch + c) * (2 * C * C));
+        const uint4 *tp = reinterpret_cast<const uint4 *>(Tck + (bh * nch + c) * (3 * C * C));
 #pragma unroll
         for (int i = 0; i < TU; ++i) tu[i] = tp[tid + i * NTH];
 #pragma unroll
         for (int i = 0; i < TU; ++i) {  // unit u: plane u / 512, row (u / 8) % 64, columns 8 (u % 8) ..
             const int u = tid + i * NTH, r = (u >> 3) & 63, g = u & 7;
-            *reinterpret_cast<uint4 *>(&(i == 0 ? sTh : sTl)[r * PCH + 8 * g]) = tu[i];
+            *reinterpret_cast<uint4 *>(&(i == 0 ? sTh : i == 1 ? sTl : sPb)[r * PCH + 8 * g]) = tu[i];
         }
 #pragma unroll
         for (int i = 0; i < NU; ++i) {
@@ -751,21 +751,6 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             aq[e] = aq[e] * G;
         }
     };
-    // P of this wave's score tiles into LDS (bf16) for the slices; AS is formed again at the end
-    static_for<0, 2>([&](auto I) __attribute__((always_inline)) {
-        const int t = 2 * I + hw;
-        v4f aq = zero4();
-        if (t <= rw) {
-#pragma unroll
-            for (int k0 = 0; k0 < DK; k0 += 32)
-                aq = mfma32(frag_rows(sQ, PH, R0, k0, lr, lq), frag_rows(sKt, PH, 16 * t, k0, lr, lq), aq);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = R0 + 4 * lq + e, j = 16 * t + lr;
-            sPb[i * PCH + j] = bf16_bits(j <= i ? aq[e] * __expf(sg[i] - sg[j]) : 0.f);
-        }
-    });
 
     v4f aQ[NFH], aK[NFH], aKt[NFH], adP[2], adA[2];
 #pragma unroll
@@ -1067,25 +1052,28 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
     }
 }
 
-// ---- (I + A)^{-1} of every chunk (bf16 inputs, C = 64) ---------------------------------------
-// One workgroup per (sequence, chunk).  AS = strictly lower (K K~^T) o G on matrix cores (the
-// same tiles the per-chunk pass forms), then T = (I + diag(b) AS)^{-1} in fp32 by blocks, stored
-// as two bf16 planes, hi = bf16(T) and lo = bf16(T - hi), row-major 64 x 64 each.  The reverse
-// pass and the per-chunk pass take their products with T and T^T from the planes at fp32
-// accuracy (hi.hi + hi.lo + lo.hi).  T of a chunk does not depend on the state, so all chunks
-// are inverted in parallel instead of inside the sequential reverse pass.
+// ---- (I + A)^{-1} and P of every chunk (bf16 inputs, C = 64) ---------------------------------
+// One workgroup per (sequence, chunk).  AS = strictly lower (K K~^T) o G and P =
+// lower-inclusive (Q K~^T) o G on matrix cores (the same tiles the per-chunk pass forms), then
+// T = (I + diag(b) AS)^{-1} in fp32 by blocks.  Three bf16 planes per chunk, row-major 64 x 64
+// each: hi = bf16(T), lo = bf16(T - hi), and P (zero above the diagonal).  The reverse pass and
+// the per-chunk pass take their products with T and T^T from the first two at fp32 accuracy
+// (hi.hi + hi.lo + lo.hi) and P^T dO from the third.  Neither depends on the state, so all
+// chunks are done in parallel instead of inside the sequential reverse pass.
 template <int DK, typename TD>
 __global__ void __launch_bounds__(NT)
-bwd_tinv_kernel(const bf16_t *__restrict__ k, const TD *__restrict__ d,
-                const float *__restrict__ beta, const float *__restrict__ alpha,
-                uint16_t *__restrict__ Tck, int64_t T, int64_t nch) {
+bwd_tinv_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
+                const TD *__restrict__ d, const float *__restrict__ beta,
+                const float *__restrict__ alpha, uint16_t *__restrict__ Tck, int64_t T,
+                int64_t nch) {
     constexpr int C = 64, PH = DK + 8, PC = C + 1;
-    // K, K~ (bf16) until AS is in registers; then AS, T and the block products' scratch (fp32)
-    // in the same bytes, so four workgroups fit a CU
-    constexpr int KB = 2 * C * PH * 2, FB = (2 * C * PC + 3 * 16 * 17) * 4;
+    // K~ (bf16) until AS and P are in registers; then AS, T and the block products' scratch
+    // (fp32) in the same bytes, so four workgroups fit a CU.  The A operands (this wave's rows
+    // of Q and K) come from memory straight into registers in the fragment layout.
+    constexpr int KB = C * PH * 2, FB = (2 * C * PC + 3 * 16 * 17) * 4;
     __shared__ alignas(16) unsigned char smem[KB > FB ? KB : FB];
     __shared__ float sb[C], sg[C], sgam[C], sw[C];
-    uint16_t *const sK = reinterpret_cast<uint16_t *>(smem), *const sKt = sK + C * PH;
+    uint16_t *const sKt = reinterpret_cast<uint16_t *>(smem);
     float *const sAS = reinterpret_cast<float *>(smem), *const sT = sAS + C * PC;
     float *const sTmp = sT + C * PC;
 
@@ -1095,7 +1083,23 @@ bwd_tinv_kernel(const bf16_t *__restrict__ k, const TD *__restrict__ d,
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lq = lane >> 4;
     const int R0 = 16 * wave;
-    {  // K and K~ = d (.) k as bf16, rows past the end zero
+    // this wave's rows of Q and K as A-operand fragments: lane (q, n) holds row R0 + n,
+    // features k0 + 8q .. +7 of each 32-wide k-step (zero past the end)
+    constexpr int NS = DK / 32;
+    v8s qf[NS], kf[NS];
+    {
+        const int r = R0 + lr;
+        const uint32_t m = r < n ? 0xffffffffu : 0u;
+        const int64_t e = (row0 + (r < n ? r : n - 1)) * DK + 8 * lq;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const uint4 a = *reinterpret_cast<const uint4 *>(q + e + 32 * s);
+            const uint4 b = *reinterpret_cast<const uint4 *>(k + e + 32 * s);
+            qf[s] = __builtin_bit_cast(v8s, make_uint4(a.x & m, a.y & m, a.z & m, a.w & m));
+            kf[s] = __builtin_bit_cast(v8s, make_uint4(b.x & m, b.y & m, b.z & m, b.w & m));
+        }
+    }
+    {  // K~ = d (.) k as bf16, rows past the end zero
         constexpr int G = DK / 8, NU = C * G / NT;
         static_assert(NU * NT == C * G, "whole units");
         uint4 ku[NU];
@@ -1115,23 +1119,36 @@ bwd_tinv_kernel(const bf16_t *__restrict__ k, const TD *__restrict__ d,
 #pragma unroll
             for (int e = 0; e < 4; ++e) kt[e] = pack2(dd[i][2 * e] * bf_lo(kw[e]), dd[i][2 * e + 1] * bf_hi(kw[e]));
             const uint32_t m = r < n ? 0xffffffffu : 0u;
-            *reinterpret_cast<uint4 *>(&sK[r * PH + 8 * g]) = make_uint4(kw[0] & m, kw[1] & m, kw[2] & m, kw[3] & m);
             *reinterpret_cast<uint4 *>(&sKt[r * PH + 8 * g]) = make_uint4(kt[0] & m, kt[1] & m, kt[2] & m, kt[3] & m);
         }
     }
     if (tid < 64) decay_scan<C>(beta, alpha, row0, n, sb, sg, sgam, sw, lane);
     __syncthreads();
-    v4f ak[C / 16];  // this wave's rows of AS
+    uint16_t *dst = Tck + (bh * nch + c) * (3 * C * C);
+    v4f ak[C / 16];  // this wave's rows of AS; P's go straight to its plane
 #pragma unroll
     for (int t = 0; t < C / 16; ++t) {
+        v4f aq = zero4();
         ak[t] = zero4();
         if (t <= wave) {
 #pragma unroll
-            for (int k0 = 0; k0 < DK; k0 += 32)
-                ak[t] = mfma32(frag_rows(sK, PH, R0, k0, lr, lq), frag_rows(sKt, PH, 16 * t, k0, lr, lq), ak[t]);
+            for (int s = 0; s < NS; ++s) {
+                const v8s kt = frag_rows(sKt, PH, 16 * t, 32 * s, lr, lq);
+                ak[t] = mfma32(kf[s], kt, ak[t]);
+                aq = mfma32(qf[s], kt, aq);
+            }
         }
+        v4f pt;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = R0 + 4 * lq + e, j = 16 * t + lr;
+            pt[e] = j <= i ? aq[e] * __expf(sg[i] - sg[j]) : 0.f;
+        }
+        // row R0 + 4 lq + lr % 4, columns 16 t + 4 (lr / 4) .. +3 after a quad transpose
+        *reinterpret_cast<uint2 *>(dst + 2 * C * C + (R0 + 4 * lq + (lr & 3)) * C + 16 * t + 4 * (lr >> 2)) =
+            pack4u(quad_transpose(pt, lane));
     }
-    __syncthreads();  // K and K~ are dead: AS takes their bytes
+    __syncthreads();  // K~ is dead: AS takes its bytes
 #pragma unroll
     for (int t = 0; t < C / 16; ++t)
 #pragma unroll
@@ -1140,7 +1157,6 @@ bwd_tinv_kernel(const bf16_t *__restrict__ k, const TD *__restrict__ d,
             sAS[i * PC + j] = j < i ? ak[t][e] * __expf(sg[i] - sg[j]) : 0.f;
         }
     block_inverse64<PC>(sT, sAS, sb, sTmp, tid);  // its first barrier orders the AS writes
-    uint16_t *dst = Tck + (bh * nch + c) * (2 * C * C);
     for (int u = tid; u < C * C / 4; u += NT) {  // four elements per thread and pass
         const int r = u / (C / 4), j = 4 * (u % (C / 4));
         uint32_t hw[2], lw[2];
@@ -1161,10 +1177,10 @@ bwd_tinv_kernel(const bf16_t *__restrict__ k, const TD *__restrict__ d,
 // registers: wave w owns its 16x16 tiles in the MFMA C layout and stores them, rounded to bf16,
 // straight to the checkpoint; LDS holds the same bf16 copy, the operand of K~ dM.  Per chunk, with a barrier after
 // each phase:
-//   stores   the chunk's q, k, K~ = d (.) k, T planes and dO (prefetched into registers one
-//            chunk ahead) into LDS, and the next chunk's loads issued;
-//   scores   gam dO; the ten lower tiles of P spread over the waves; one 16x16 tile of K~ dM
-//            per wave; one wave runs the decay scan of the next chunk (double-buffered);
+//   stores   the chunk's q, k, K~ = d (.) k, T and P planes and dO (prefetched into registers
+//            one chunk ahead) into LDS, and the next chunk's loads issued;
+//   scores   gam dO; one 16x16 tile of K~ dM per wave; one wave runs the decay scan of the
+//            next chunk (double-buffered);
 //   dU       dU = P^T dO + diag(w) K~ dM, one tile per wave, as hi/lo bf16;
 //   dR       dR = T^T dU from the T planes (hi.hi + hi.lo + lo.hi), one tile per wave;
 //   update   dM <- gam_L dM + Q^T diag(gam) dO - K^T diag(gam b) dR on the wave's own tiles.
@@ -1179,16 +1195,16 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
     constexpr int PH = DK + 8, PCH = C + 8, PVH = BV + 8;  // bf16 pitches
     constexpr int G = DK / 8, NU = C * G / NTH;  // 16-byte units of a Q/K row; units per thread
     constexpr int DU = sizeof(TD) == 4 ? 2 : 1;  // 16-byte units of d per unit of k
-    constexpr int TU = 2 * C * C / 8 / NTH;      // 16-byte units of the T planes per thread
+    constexpr int TU = 3 * C * C / 8 / NTH;      // 16-byte units of the T, P planes per thread
     constexpr int MT = DK / 64;                  // 16x16 tiles of dM per wave
-    static_assert(BV == 32 && NU * NTH == C * G && NU <= 2 && TU == 2 && C * BV / 4 == NTH,
+    static_assert(BV == 32 && NU * NTH == C * G && NU <= 2 && TU == 3 && C * BV / 4 == NTH,
                   "unit layout");
     __shared__ alignas(16) uint16_t sQ[C * PH], sK[C * PH], sKt[C * PH];
     __shared__ alignas(16) uint16_t sPb[C * PCH], sTh[C * PCH], sTl[C * PCH];
     __shared__ alignas(16) uint16_t sDOb[C * PVH], sGDOb[C * PVH], sGDRb[C * PVH];
     __shared__ alignas(16) uint16_t sdUh[C * PVH], sdUl[C * PVH];
     __shared__ alignas(16) uint16_t sdMb[DK * PVH];  // bf16 copy of dM (operand of K~ dM)
-    __shared__ float sb[2][C], sg[2][C], sgam[2][C], sw[2][C];  // decay scan, by chunk parity
+    __shared__ float sb[2][C], sgam[2][C], sw[2][C];  // decay scan, by chunk parity
 
     // workgroup -> (sequence, value slice); the slices of one sequence share an XCD (and its
     // L2) when the sequence count allows it, so their re-reads of q, k, d and T hit L2
@@ -1214,11 +1230,11 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
     const int64_t seq0 = bh * T;
     auto rows_of = [&](int64_t cc) { return static_cast<int>(T - cc * C < C ? T - cc * C : C); };
 
-    // the next chunk's q, k, d, T planes and dO in named registers, loaded one chunk ahead (an
-    // array carried across the loop would live in scratch); unit i of this thread is
-    // u = tid + i NTH: row u / G, features 8 (u % G) .. +7; T unit u holds elements 8u .. 8u+7
-    // of the two planes (plane u / 512, row (u / 8) % 64, columns 8 (u % 8) ..)
-    uint4 q0, q1, k0r, k1r, dl0, dl1, dh0, dh1, t0, t1;
+    // the next chunk's q, k, d, T and P planes and dO in named registers, loaded one chunk
+    // ahead (an array carried across the loop would live in scratch); unit i of this thread
+    // is u = tid + i NTH: row u / G, features 8 (u % G) .. +7; plane unit u holds elements
+    // 8u .. 8u+7 of the three planes (plane u / 512, row (u / 8) % 64, columns 8 (u % 8) ..)
+    uint4 q0, q1, k0r, k1r, dl0, dl1, dh0, dh1, t0, t1, t2;
     uint2 ou;
     auto qreg = [&](auto I) -> uint4 & { if constexpr (decltype(I)::value == 0) return q0; else return q1; };
     auto kreg = [&](auto I) -> uint4 & { if constexpr (decltype(I)::value == 0) return k0r; else return k1r; };
@@ -1249,9 +1265,10 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
         });
     };
     auto load_t = [&](int64_t cc) __attribute__((always_inline)) {
-        const uint4 *tp = reinterpret_cast<const uint4 *>(Tck + (bh * nch + cc) * (2 * C * C));
+        const uint4 *tp = reinterpret_cast<const uint4 *>(Tck + (bh * nch + cc) * (3 * C * C));
         t0 = tp[tid];
         t1 = tp[tid + NTH];
+        t2 = tp[tid + 2 * NTH];
     };
     // decay scan of chunk cc into buffer cc & 1 (one wave; beta, alpha of the chunk in bv, av)
     float bv = 0.f, av = 1.f;
@@ -1270,7 +1287,6 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
         }
         const float gl = __shfl(x, C - 1);
         sb[pb][lane] = lane < nn ? bv : 0.f;
-        sg[pb][lane] = x;
         sgam[pb][lane] = __expf(x);
         sw[pb][lane] = __expf(gl - x);
     };
@@ -1288,7 +1304,6 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             if (nch > 0) dMck[((bh * nch + nch - 1) * DK + f) * dv + j0 + j] = bf16_bits(dM[m][e]);
         }
     }
-    for (int i = tid; i < C * PCH; i += NTH) sPb[i] = 0;  // tiles above the diagonal stay zero
     if (nch > 0) {
         load_qk(nch - 1);
         load_d(nch - 1);
@@ -1299,10 +1314,6 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             if (nch > 1) load_ba(nch - 2);
         }
     }
-    // this wave's lower tiles of P: (row block, column tile) codes 4 rb + t, -1 for none
-    const int pt0 = wave == 0 ? 15 : wave == 1 ? 14 : wave == 2 ? 13 : wave == 3 ? 12
-                  : wave == 4 ? 10 : wave == 5 ? 9 : wave == 6 ? 8 : -1;
-    const int pt1 = wave == 0 ? 0 : wave == 1 ? 5 : wave == 6 ? 4 : -1;
 
     for (int64_t c = nch - 1; c >= 0; --c) {
         const int n = rows_of(c), pb = static_cast<int>(c & 1);
@@ -1339,6 +1350,7 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             const int r = (tid >> 3) & 63, g = tid & 7;  // unit tid of each plane
             *reinterpret_cast<uint4 *>(&sTh[r * PCH + 8 * g]) = t0;
             *reinterpret_cast<uint4 *>(&sTl[r * PCH + 8 * g]) = t1;
+            *reinterpret_cast<uint4 *>(&sPb[r * PCH + 8 * g]) = t2;
         }
         {
             const int r = tid / (BV / 4), j = 4 * (tid % (BV / 4));
@@ -1354,21 +1366,6 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             *reinterpret_cast<uint2 *>(&sGDOb[r * PVH + j]) =
                 make_uint2(pack2(gm * bf_lo(o.x), gm * bf_hi(o.x)), pack2(gm * bf_lo(o.y), gm * bf_hi(o.y)));
         }
-        // this wave's lower tiles of P (bf16; zero above the diagonal inside a diagonal tile)
-        auto p_tile = [&](int code) __attribute__((always_inline)) {
-            const int pr = 16 * (code >> 2), t = code & 3;
-            v4f aq = zero4();
-#pragma unroll
-            for (int k0 = 0; k0 < DK; k0 += 32)
-                aq = mfma32(frag_rows(sQ, PH, pr, k0, lr, lq), frag_rows(sKt, PH, 16 * t, k0, lr, lq), aq);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = pr + 4 * lq + e, j = 16 * t + lr;
-                sPb[i * PCH + j] = bf16_bits(j <= i ? aq[e] * __expf(sg[pb][i] - sg[pb][j]) : 0.f);
-            }
-        };
-        if (pt0 >= 0) p_tile(pt0);
-        if (pt1 >= 0) p_tile(pt1);
         // this wave's tile of K~ dM
         v4f kdm = zero4();
 #pragma unroll
@@ -1467,8 +1464,9 @@ hipError_t bwd_typed(const BwdArgs &a, hipStream_t stream) {
     if constexpr (sizeof(TQ) == 2) {
         if (nch > 0) {
             hipLaunchKernelGGL((bwd_tinv_kernel<DK, TD>), dim3(static_cast<unsigned>(a.BH * nch)),
-                               dim3(NT), 0, stream, static_cast<const bf16_t *>(a.k),
-                               static_cast<const TD *>(a.d), a.beta, a.alpha, a.Tck, a.T, nch);
+                               dim3(NT), 0, stream, static_cast<const bf16_t *>(a.q),
+                               static_cast<const bf16_t *>(a.k), static_cast<const TD *>(a.d),
+                               a.beta, a.alpha, a.Tck, a.T, nch);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
