@@ -665,12 +665,11 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
     __shared__ alignas(16) uint16_t sPb[C * PCH];  // P, later dP o G (bf16)
     __shared__ alignas(16) uint16_t sTh[C * PCH], sTl[C * PCH];  // T = (I + A)^{-1}: hi, lo
     __shared__ alignas(16) uint16_t sMb[MB];       // M0 and dMC slices, later Gb (bf16)
-    __shared__ alignas(16) uint16_t sDOb[C * PVH], sGDOb[C * PVH], sUb[C * PVH], sWUb[C * PVH];
-    __shared__ alignas(16) uint16_t sDRb[C * PVH], sGDRb[C * PVH];
+    __shared__ alignas(16) uint16_t sDOb[C * PVH], sUb[C * PVH], sDRb[C * PVH];
     __shared__ alignas(16) uint16_t sRh[C * PVH], sRl[C * PVH];  // V, then R (hi, lo)
     __shared__ alignas(16) uint16_t sdUh[C * PVH], sdUl[C * PVH];
     __shared__ float sb[C], sg[C], sgam[C], sw[C];
-    __shared__ float srow[2][6][C];  // per-half row sums: go, gr, ew, db, rowp, rowb
+    __shared__ float srow[2][6][C];  // per-half row sums of the dg and dbeta terms
     __shared__ float scol[4][C];     // column sums of the decay term, by row block
     __shared__ float sred[NW];
     uint16_t *const sM0b = sMb, *const sdMb = sMb + DK * PVH;
@@ -756,10 +755,10 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
 #pragma unroll
     for (int t = 0; t < NFH; ++t) aQ[t] = aK[t] = aKt[t] = zero4();
     adP[0] = adP[1] = adA[0] = adA[1] = zero4();
-    // per-lane partial row sums over the value columns: <dO_r, (Q M0)_r>, <dR_r, (K M0)_r>,
-    // <(K~ dMC)_r, U_r>, <dR_r, Y_r> for rows R0 + 4 lq + e
-    float pgo[4] = {0.f, 0.f, 0.f, 0.f}, pgr[4] = {0.f, 0.f, 0.f, 0.f};
-    float pew[4] = {0.f, 0.f, 0.f, 0.f}, pdb[4] = {0.f, 0.f, 0.f, 0.f};
+    // per-lane partial row sums over the value columns (rows R0 + 4 lq + e), fp32:
+    // <dR_r, (K M0)_r>, <(K~ dMC)_r, U_r>, <dR_r, Y_r>; <dO_r, (Q M0)_r> comes from the dQ
+    // partial at the end
+    float pgr[4] = {0.f, 0.f, 0.f, 0.f}, pew[4] = {0.f, 0.f, 0.f, 0.f}, pdb[4] = {0.f, 0.f, 0.f, 0.f};
     float frob = 0.f;
 
     // the value slice's M0, dMC, v and dO (bf16, four per 8-byte unit) pass through named
@@ -798,32 +797,26 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             frob += bf_lo(mm.x) * bf_lo(dd.x) + bf_hi(mm.x) * bf_hi(dd.x) +
                     bf_lo(mm.y) * bf_lo(dd.y) + bf_hi(mm.y) * bf_hi(dd.y);
         }
-        {  // v into sRh (R replaces it in place), dO and gam dO; rows past the end are zero
+        {  // v into sRh (R replaces it in place) and dO; rows past the end are zero
             const int r = tid / (BV / 4), j = 4 * (tid % (BV / 4));
             const uint32_t m = r < n ? 0xffffffffu : 0u;
             *reinterpret_cast<uint2 *>(&sRh[r * PVH + j]) = make_uint2(vu.x & m, vu.y & m);
             *reinterpret_cast<uint2 *>(&sDOb[r * PVH + j]) = make_uint2(ou.x & m, ou.y & m);
-            const float gm = sgam[r];
-            *reinterpret_cast<uint2 *>(&sGDOb[r * PVH + j]) =
-                make_uint2(pack2(gm * bf_lo(ou.x), gm * bf_hi(ou.x)) & m,
-                           pack2(gm * bf_lo(ou.y), gm * bf_hi(ou.y)) & m);
         }
         if (s0 + BV < DV) OSDN_BWD_LOAD_SLICE(s0 + BV);  // in flight through this slice's work
         __syncthreads();
-        // K M0, Q M0, K~ dMC on this wave's tile; Y = V - gam K M0 (registers), R = b Y into
-        // LDS as hi/lo bf16 over V
-        v4f km = zero4(), qm = zero4(), kdm = zero4(), y;
+        // K M0, K~ dMC on this wave's tile; Y = V - gam K M0 (registers), R = b Y into LDS as
+        // hi/lo bf16 over V
+        v4f km = zero4(), kdm = zero4(), y;
 #pragma unroll 2
         for (int k0 = 0; k0 < DK; k0 += 32) {
             const v8s m0f = frag_cols(sM0b, PVH, k0, jt, lr, lq);
             km = mfma32(frag_rows(sK, PH, R0, k0, lr, lq), m0f, km);
-            qm = mfma32(frag_rows(sQ, PH, R0, k0, lr, lq), m0f, qm);
             kdm = mfma32(frag_rows(sKt, PH, R0, k0, lr, lq), frag_cols(sdMb, PVH, k0, jt, lr, lq), kdm);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = R0 + 4 * lq + e, j = jt + lr;
-            pgo[e] += __uint_as_float(uint32_t(sDOb[r * PVH + j]) << 16) * qm[e];
             y[e] = __uint_as_float(uint32_t(sRh[r * PVH + j]) << 16) - sgam[r] * km[e];
             const float x = sb[r] * y[e];
             const uint16_t h = bf16_bits(x);
@@ -849,7 +842,6 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
         for (int e = 0; e < 4; ++e) {
             const int r = R0 + 4 * lq + e, j = jt + lr;
             sUb[r * PVH + j] = bf16_bits(u[e]);
-            sWUb[r * PVH + j] = bf16_bits(sw[r] * u[e]);
             pew[e] += kdm[e] * u[e];
             const float x = du[e] + sw[r] * kdm[e];
             const uint16_t h = bf16_bits(x);
@@ -873,7 +865,6 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
         for (int e = 0; e < 4; ++e) {
             const int r = R0 + 4 * lq + e, j = jt + lr;
             sDRb[r * PVH + j] = bf16_bits(dr[e]);
-            sGDRb[r * PVH + j] = bf16_bits(-sgam[r] * sb[r] * dr[e]);
             pgr[e] += dr[e] * km[e];
             pdb[e] += dr[e] * y[e];
             gvt[e] = sb[r] * dr[e];
@@ -885,7 +876,8 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
         }
         __syncthreads();
         // dP += dO U^T, dA += dR U^T (negated later) on this wave's score tiles, and the
-        // slice's part of dQ, dK, dK~ on this wave's feature tiles (K = the slice's 32 columns)
+        // slice's part of dO M0^T, dR M0^T, U dMC^T on this wave's feature tiles (K = the
+        // slice's 32 columns; the row factors gam, -gam b, w of dQ, dK, dK~ come at the end)
         static_for<0, 2>([&](auto I) __attribute__((always_inline)) {
             const int t = 2 * I + hw;
             if (t <= rw) {
@@ -894,15 +886,15 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
                 adA[I] = mfma32(frag_rows(sDRb, PVH, R0, 0, lr, lq), ub, adA[I]);
             }
         });
-        const v8s gdo = frag_rows(sGDOb, PVH, R0, 0, lr, lq), gdr = frag_rows(sGDRb, PVH, R0, 0, lr, lq);
-        const v8s wub = frag_rows(sWUb, PVH, R0, 0, lr, lq);
+        const v8s dob = frag_rows(sDOb, PVH, R0, 0, lr, lq), drb = frag_rows(sDRb, PVH, R0, 0, lr, lq);
+        const v8s urb = frag_rows(sUb, PVH, R0, 0, lr, lq);
 #pragma unroll 2
         for (int t = 0; t < NFH; ++t) {
             const int f0 = 16 * (NFH * hw + t);
             const v8s m0r = frag_rows(sM0b, PVH, f0, 0, lr, lq);
-            aQ[t] = mfma32(gdo, m0r, aQ[t]);
-            aK[t] = mfma32(gdr, m0r, aK[t]);
-            aKt[t] = mfma32(wub, frag_rows(sdMb, PVH, f0, 0, lr, lq), aKt[t]);
+            aQ[t] = mfma32(dob, m0r, aQ[t]);
+            aK[t] = mfma32(drb, m0r, aK[t]);
+            aKt[t] = mfma32(urb, frag_rows(sdMb, PVH, f0, 0, lr, lq), aKt[t]);
         }
     }
 #undef OSDN_BWD_LOAD_SLICE
@@ -940,6 +932,25 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
         colp = sum_rows(colp);
         if (lq == 0) scol[rw][16 * t + lr] = colp;
     });
+    // the slices' parts of dQ, dK, dK~ take their row factors: gam dO M0^T, -gam b dR M0^T,
+    // diag(w) U dMC^T; the first gives <Q_r, (gam dO M0^T)_r> = gam_r <dO_r, (Q M0)_r> (this
+    // wave's feature tiles; the other half's come through LDS)
+    float pgo[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int r = R0 + 4 * lq + e;
+        const float fq = sgam[r], fk = -sgam[r] * sb[r], fw = sw[r];
+        pgr[e] *= fk;
+        pew[e] *= fw;
+#pragma unroll
+        for (int t = 0; t < NFH; ++t) {
+            const int f = 16 * (NFH * hw + t) + lr;
+            aQ[t][e] *= fq;
+            aK[t][e] *= fk;
+            aKt[t][e] *= fw;
+            pgo[e] += __uint_as_float(uint32_t(sQ[r * PH + f]) << 16) * aQ[t][e];
+        }
+    }
     // row sums: across the 16 lanes of a row (total in its last lane), then (below) across the
     // two halves
 #pragma unroll
@@ -998,9 +1009,9 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
     if (tid < 64) {  // dbeta; dg of every row, then its reverse running sum d ln(alpha) (wave 0)
         const int r = lane;
         const float go = srow[0][0][r] + srow[1][0][r], gr = srow[0][1][r] + srow[1][1][r];
-        const float ew = sw[r] * (srow[0][2][r] + srow[1][2][r]);
+        const float ew = srow[0][2][r] + srow[1][2][r];
         const float db = srow[0][3][r] + srow[1][3][r] + srow[0][5][r] + srow[1][5][r];
-        float g = sgam[r] * go - sb[r] * sgam[r] * gr + srow[0][4][r] + srow[1][4][r] -
+        float g = go + gr + srow[0][4][r] + srow[1][4][r] -
                   (scol[0][r] + scol[1][r] + scol[2][r] + scol[3][r]);
         // the last row's terms: gam_L <dMC, M0> + sum_s w_s <(K~ dMC)_s, U_s>
         float ews = r < n ? ew : 0.f;
