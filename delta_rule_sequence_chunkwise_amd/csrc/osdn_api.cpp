@@ -385,15 +385,15 @@ int64_t bwd_ckpt_bytes(int64_t B, int64_t H, int64_t T, int32_t dk, int32_t dv, 
     return round256(n * (qkv == OSDN_BF16 ? 2 : 4));
 }
 
-// bytes of the per-chunk planes of the backward (bf16 inputs: three bf16 64 x 64 planes per
-// chunk, the inverse's hi and lo and the scores; fp32 inputs: none); called after
-// bwd_ckpt_bytes has accepted the sizes
-int64_t bwd_tinv_bytes(int64_t B, int64_t H, int64_t T, osdn_dtype qkv) {
+// bytes of the per-chunk planes of the backward (bf16 inputs, per chunk: three bf16 64 x 64
+// planes, the inverse's hi and lo and the scores, and K~ as 64 x dk bf16; fp32 inputs: none);
+// called after bwd_ckpt_bytes has accepted the sizes
+int64_t bwd_tinv_bytes(int64_t B, int64_t H, int64_t T, int32_t dk, osdn_dtype qkv) {
     if (qkv != OSDN_BF16) return 0;
     const int64_t C = osdn::bwd_chunk_size(qkv);
     int64_t n = 1;
     if (!mul_ok(n, B, kMaxElems) || !mul_ok(n, H, kMaxElems) ||
-        !mul_ok(n, (T + C - 1) / C, kMaxElems) || !mul_ok(n, 3 * C * C, kMaxElems))
+        !mul_ok(n, (T + C - 1) / C, kMaxElems) || !mul_ok(n, 3 * C * C + C * dk, kMaxElems))
         return -1;
     return round256(n * 2);
 }
@@ -406,7 +406,7 @@ int64_t osdn_chunk_bwd_workspace(int64_t B, int64_t H, int64_t T, int32_t dk, in
                                  osdn_dtype qkv) {
     const int64_t b = bwd_ckpt_bytes(B, H, T, dk, dv, qkv);
     if (b < 0) return -1;
-    const int64_t t = bwd_tinv_bytes(B, H, T, qkv);
+    const int64_t t = bwd_tinv_bytes(B, H, T, dk, qkv);
     return t < 0 ? -1 : 2 * b + t;
 }
 
@@ -422,7 +422,7 @@ osdn_status osdn_chunk_bwd(const void *q, const void *k, const void *v, const fl
     if (!head_dim_ok(dk) || !head_dim_ok(dv)) return OSDN_ERR_UNSUPPORTED;
     const int64_t ck = bwd_ckpt_bytes(B, H, T, dk, dv, qkv);
     if (ck < 0) return OSDN_ERR_SHAPE;
-    const int64_t tk = bwd_tinv_bytes(B, H, T, qkv);
+    const int64_t tk = bwd_tinv_bytes(B, H, T, dk, qkv);
     if (tk < 0) return OSDN_ERR_SHAPE;
     const int64_t wsb = 2 * ck + tk;
     int64_t BH = 1;

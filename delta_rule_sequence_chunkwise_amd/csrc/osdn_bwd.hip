@@ -690,22 +690,22 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
     TD *gdc = gd + row0 * DK;
     const TD *dc = d + row0 * DK;
 
-    {  // Q, K, K~ = d (.) k as bf16 (8 features per 16-byte unit) and the T planes, all loads
-       // issued first
+    {  // Q, K (bf16, 8 features per 16-byte unit), K~ and the T, P planes, all loads issued
+       // first
         constexpr int G = DK / 8, NU = C * G / NTH;  // units per row, units per thread
         constexpr int TU = 3 * C * C / 8 / NTH;      // 16-byte units of the T, P planes per thread
         static_assert(NU * NTH == C * G && TU == 3, "whole units");
-        uint4 qu[NU], ku[NU], tu[TU];
-        float dd[NU][8];
+        uint4 qu[NU], ku[NU], kt[NU], tu[TU];
+        const uint16_t *pc = Tck + (bh * nch + c) * (3 * C * C + C * DK);
 #pragma unroll
         for (int i = 0; i < NU; ++i) {
             const int u = tid + i * NTH, r = u / G, g = u % G;
             const int64_t e = (row0 + (r < n ? r : n - 1)) * DK + 8 * g;
             qu[i] = *reinterpret_cast<const uint4 *>(q + e);
             ku[i] = *reinterpret_cast<const uint4 *>(k + e);
-            load8(d + e, dd[i]);
+            kt[i] = *reinterpret_cast<const uint4 *>(pc + 3 * C * C + r * DK + 8 * g);
         }
-        const uint4 *tp = reinterpret_cast<const uint4 *>(Tck + (bh * nch + c) * (3 * C * C));
+        const uint4 *tp = reinterpret_cast<const uint4 *>(pc);
 #pragma unroll
         for (int i = 0; i < TU; ++i) tu[i] = tp[tid + i * NTH];
 #pragma unroll
@@ -716,15 +716,12 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
 #pragma unroll
         for (int i = 0; i < NU; ++i) {
             const int u = tid + i * NTH, r = u / G, g = u % G;
-            const uint32_t kw[4] = {ku[i].x, ku[i].y, ku[i].z, ku[i].w};
-            uint32_t kt[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) kt[e] = pack2(dd[i][2 * e] * bf_lo(kw[e]), dd[i][2 * e + 1] * bf_hi(kw[e]));
             const uint32_t m = r < n ? 0xffffffffu : 0u;  // rows past the end are zero
             *reinterpret_cast<uint4 *>(&sQ[r * PH + 8 * g]) =
                 make_uint4(qu[i].x & m, qu[i].y & m, qu[i].z & m, qu[i].w & m);
-            *reinterpret_cast<uint4 *>(&sK[r * PH + 8 * g]) = make_uint4(kw[0] & m, kw[1] & m, kw[2] & m, kw[3] & m);
-            *reinterpret_cast<uint4 *>(&sKt[r * PH + 8 * g]) = make_uint4(kt[0] & m, kt[1] & m, kt[2] & m, kt[3] & m);
+            *reinterpret_cast<uint4 *>(&sK[r * PH + 8 * g]) =
+                make_uint4(ku[i].x & m, ku[i].y & m, ku[i].z & m, ku[i].w & m);
+            *reinterpret_cast<uint4 *>(&sKt[r * PH + 8 * g]) = kt[i];
         }
     }
     if (tid < 64) decay_scan<C>(beta, alpha, row0, n, sb, sg, sgam, sw, lane);
@@ -1066,11 +1063,12 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
 // ---- (I + A)^{-1} and P of every chunk (bf16 inputs, C = 64) ---------------------------------
 // One workgroup per (sequence, chunk).  AS = strictly lower (K K~^T) o G and P =
 // lower-inclusive (Q K~^T) o G on matrix cores (the same tiles the per-chunk pass forms), then
-// T = (I + diag(b) AS)^{-1} in fp32 by blocks.  Three bf16 planes per chunk, row-major 64 x 64
-// each: hi = bf16(T), lo = bf16(T - hi), and P (zero above the diagonal).  The reverse pass and
-// the per-chunk pass take their products with T and T^T from the first two at fp32 accuracy
-// (hi.hi + hi.lo + lo.hi) and P^T dO from the third.  Neither depends on the state, so all
-// chunks are done in parallel instead of inside the sequential reverse pass.
+// T = (I + diag(b) AS)^{-1} in fp32 by blocks.  Per chunk, bf16 and row-major: hi = bf16(T),
+// lo = bf16(T - hi), P (zero above the diagonal), 64 x 64 each, then K~ = d (.) k (64 x dk).
+// The reverse pass and the per-chunk pass take their products with T and T^T from the first
+// two at fp32 accuracy (hi.hi + hi.lo + lo.hi), P^T dO from the third, and K~ as it is.  None
+// depends on the state, so all chunks are done in parallel instead of inside the sequential
+// reverse pass.
 template <int DK, typename TD>
 __global__ void __launch_bounds__(NT)
 bwd_tinv_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
@@ -1110,7 +1108,8 @@ bwd_tinv_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
             kf[s] = __builtin_bit_cast(v8s, make_uint4(b.x & m, b.y & m, b.z & m, b.w & m));
         }
     }
-    {  // K~ = d (.) k as bf16, rows past the end zero
+    uint16_t *dst = Tck + (bh * nch + c) * (3 * C * C + C * DK);
+    {  // K~ = d (.) k as bf16, rows past the end zero, into LDS and its plane
         constexpr int G = DK / 8, NU = C * G / NT;
         static_assert(NU * NT == C * G, "whole units");
         uint4 ku[NU];
@@ -1130,12 +1129,13 @@ bwd_tinv_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 #pragma unroll
             for (int e = 0; e < 4; ++e) kt[e] = pack2(dd[i][2 * e] * bf_lo(kw[e]), dd[i][2 * e + 1] * bf_hi(kw[e]));
             const uint32_t m = r < n ? 0xffffffffu : 0u;
-            *reinterpret_cast<uint4 *>(&sKt[r * PH + 8 * g]) = make_uint4(kt[0] & m, kt[1] & m, kt[2] & m, kt[3] & m);
+            const uint4 x = make_uint4(kt[0] & m, kt[1] & m, kt[2] & m, kt[3] & m);
+            *reinterpret_cast<uint4 *>(&sKt[r * PH + 8 * g]) = x;
+            *reinterpret_cast<uint4 *>(dst + 3 * C * C + r * DK + 8 * g) = x;
         }
     }
     if (tid < 64) decay_scan<C>(beta, alpha, row0, n, sb, sg, sgam, sw, lane);
     __syncthreads();
-    uint16_t *dst = Tck + (bh * nch + c) * (3 * C * C);
     v4f ak[C / 16];  // this wave's rows of AS; P's go straight to its plane
 #pragma unroll
     for (int t = 0; t < C / 16; ++t) {
@@ -1188,25 +1188,25 @@ bwd_tinv_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 // registers: wave w owns its 16x16 tiles in the MFMA C layout and stores them, rounded to bf16,
 // straight to the checkpoint; LDS holds the same bf16 copy, the operand of K~ dM.  Per chunk, with a barrier after
 // each phase:
-//   stores   the chunk's q, k, K~ = d (.) k, T and P planes and dO (prefetched into registers
-//            one chunk ahead) into LDS, and the next chunk's loads issued;
+//   stores   the chunk's q, k, K~, T and P planes and dO (prefetched into registers one
+//            chunk ahead) into LDS, and the next chunk's loads issued;
 //   scores   gam dO; one 16x16 tile of K~ dM per wave; one wave runs the decay scan of the
 //            next chunk (double-buffered);
 //   dU       dU = P^T dO + diag(w) K~ dM, one tile per wave, as hi/lo bf16;
 //   dR       dR = T^T dU from the T planes (hi.hi + hi.lo + lo.hi), one tile per wave;
 //   update   dM <- gam_L dM + Q^T diag(gam) dO - K^T diag(gam b) dR on the wave's own tiles.
-template <int DK, int BV, typename TD>
+template <int DK, int BV>
 __global__ void __launch_bounds__(2 * NT)
 bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
-                      const TD *__restrict__ d, const float *__restrict__ beta,
+                      const float *__restrict__ beta,
                       const float *__restrict__ alpha, const bf16_t *__restrict__ dO,
                       const float *__restrict__ dS_T, const uint16_t *__restrict__ Tck,
                       uint16_t *__restrict__ dMck, float *__restrict__ dS0, int64_t T, int dv) {
     constexpr int C = 64, NW = 8, NTH = NW * 64;
     constexpr int PH = DK + 8, PCH = C + 8, PVH = BV + 8;  // bf16 pitches
     constexpr int G = DK / 8, NU = C * G / NTH;  // 16-byte units of a Q/K row; units per thread
-    constexpr int DU = sizeof(TD) == 4 ? 2 : 1;  // 16-byte units of d per unit of k
     constexpr int TU = 3 * C * C / 8 / NTH;      // 16-byte units of the T, P planes per thread
+    constexpr int CHS = 3 * C * C + C * DK;      // per-chunk planes: T hi, T lo, P, K~
     constexpr int MT = DK / 64;                  // 16x16 tiles of dM per wave
     static_assert(BV == 32 && NU * NTH == C * G && NU <= 2 && TU == 3 && C * BV / 4 == NTH,
                   "unit layout");
@@ -1241,16 +1241,16 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
     const int64_t seq0 = bh * T;
     auto rows_of = [&](int64_t cc) { return static_cast<int>(T - cc * C < C ? T - cc * C : C); };
 
-    // the next chunk's q, k, d, T and P planes and dO in named registers, loaded one chunk
+    // the next chunk's q, k, K~, T and P planes and dO in named registers, loaded one chunk
     // ahead (an array carried across the loop would live in scratch); unit i of this thread
     // is u = tid + i NTH: row u / G, features 8 (u % G) .. +7; plane unit u holds elements
-    // 8u .. 8u+7 of the three planes (plane u / 512, row (u / 8) % 64, columns 8 (u % 8) ..)
-    uint4 q0, q1, k0r, k1r, dl0, dl1, dh0, dh1, t0, t1, t2;
+    // 8u .. 8u+7 of the three 64 x 64 planes (plane u / 512, row (u / 8) % 64, columns
+    // 8 (u % 8) ..)
+    uint4 q0, q1, k0r, k1r, w0, w1, t0, t1, t2;
     uint2 ou;
     auto qreg = [&](auto I) -> uint4 & { if constexpr (decltype(I)::value == 0) return q0; else return q1; };
     auto kreg = [&](auto I) -> uint4 & { if constexpr (decltype(I)::value == 0) return k0r; else return k1r; };
-    auto dlreg = [&](auto I) -> uint4 & { if constexpr (decltype(I)::value == 0) return dl0; else return dl1; };
-    auto dhreg = [&](auto I) -> uint4 & { if constexpr (decltype(I)::value == 0) return dh0; else return dh1; };
+    auto wreg = [&](auto I) -> uint4 & { if constexpr (decltype(I)::value == 0) return w0; else return w1; };
     // issued in three parts spread over the phases of the chunk before (a wave stalls while
     // the CU's load queue is full, so one burst would hold up the barrier that follows it)
     auto load_qk = [&](int64_t cc) __attribute__((always_inline)) {
@@ -1265,18 +1265,12 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
         const int r = tid / (BV / 4), j = 4 * (tid % (BV / 4));
         ou = *reinterpret_cast<const uint2 *>(dO + (seq0 + cc * C + (r < nn ? r : nn - 1)) * dv + j0 + j);
     };
-    auto load_d = [&](int64_t cc) __attribute__((always_inline)) {
-        const TD *dc = d + (seq0 + cc * C) * DK;
-        const int nn = rows_of(cc);
-        static_for<0, NU>([&](auto I) __attribute__((always_inline)) {
-            const int u = tid + I * NTH, r = u / G, g = u % G;
-            const uint4 *dp = reinterpret_cast<const uint4 *>(dc + (r < nn ? r : nn - 1) * DK + 8 * g);
-            dlreg(I) = dp[0];
-            if constexpr (DU == 2) dhreg(I) = dp[1];
-        });
+    auto load_kt = [&](int64_t cc) __attribute__((always_inline)) {  // K~, zero past the end
+        const uint4 *wp = reinterpret_cast<const uint4 *>(Tck + (bh * nch + cc) * CHS + 3 * C * C);
+        static_for<0, NU>([&](auto I) __attribute__((always_inline)) { wreg(I) = wp[tid + I * NTH]; });
     };
     auto load_t = [&](int64_t cc) __attribute__((always_inline)) {
-        const uint4 *tp = reinterpret_cast<const uint4 *>(Tck + (bh * nch + cc) * (3 * C * C));
+        const uint4 *tp = reinterpret_cast<const uint4 *>(Tck + (bh * nch + cc) * CHS);
         t0 = tp[tid];
         t1 = tp[tid + NTH];
         t2 = tp[tid + 2 * NTH];
@@ -1317,7 +1311,7 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
     }
     if (nch > 0) {
         load_qk(nch - 1);
-        load_d(nch - 1);
+        load_kt(nch - 1);
         load_t(nch - 1);
         if (wave == NW - 1) {
             load_ba(nch - 1);
@@ -1329,33 +1323,14 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
     for (int64_t c = nch - 1; c >= 0; --c) {
         const int n = rows_of(c), pb = static_cast<int>(c & 1);
         __syncthreads();  // the previous chunk is done with every buffer
-        // this chunk's registers into LDS: Q, K, K~ = d (.) k (bf16), the T planes, dO
+        // this chunk's registers into LDS: Q, K, K~ (bf16), the T and P planes, dO
         static_for<0, NU>([&](auto I) __attribute__((always_inline)) {
             const int u = tid + I * NTH, r = u / G, g = u % G;
             const uint32_t m = r < n ? 0xffffffffu : 0u;  // rows past the end are zero
             const uint4 kq = kreg(I), qq = qreg(I);
-            const uint32_t kw[4] = {kq.x, kq.y, kq.z, kq.w};
-            float dd[8];
-            if constexpr (DU == 2) {
-                const uint4 lo = dlreg(I), hi = dhreg(I);
-                const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-#pragma unroll
-                for (int e = 0; e < 8; ++e) dd[e] = __uint_as_float(w[e]);
-            } else {
-                const uint4 lo = dlreg(I);
-                const uint32_t w[4] = {lo.x, lo.y, lo.z, lo.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    dd[2 * e] = bf_lo(w[e]);
-                    dd[2 * e + 1] = bf_hi(w[e]);
-                }
-            }
-            uint32_t kt[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) kt[e] = pack2(dd[2 * e] * bf_lo(kw[e]), dd[2 * e + 1] * bf_hi(kw[e]));
             *reinterpret_cast<uint4 *>(&sQ[r * PH + 8 * g]) = make_uint4(qq.x & m, qq.y & m, qq.z & m, qq.w & m);
-            *reinterpret_cast<uint4 *>(&sK[r * PH + 8 * g]) = make_uint4(kw[0] & m, kw[1] & m, kw[2] & m, kw[3] & m);
-            *reinterpret_cast<uint4 *>(&sKt[r * PH + 8 * g]) = make_uint4(kt[0] & m, kt[1] & m, kt[2] & m, kt[3] & m);
+            *reinterpret_cast<uint4 *>(&sK[r * PH + 8 * g]) = make_uint4(kq.x & m, kq.y & m, kq.z & m, kq.w & m);
+            *reinterpret_cast<uint4 *>(&sKt[r * PH + 8 * g]) = wreg(I);
         });
         {
             const int r = (tid >> 3) & 63, g = tid & 7;  // unit tid of each plane
@@ -1386,7 +1361,7 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             scan(c - 1);
             if (c > 1) load_ba(c - 2);
         }
-        if (c > 0) load_d(c - 1);
+        if (c > 0) load_kt(c - 1);
         __syncthreads();
         {  // dU = P^T dO + diag(w) K~ dM on this wave's tile, as hi/lo bf16
             v4f du = zero4();
@@ -1481,10 +1456,10 @@ hipError_t bwd_typed(const BwdArgs &a, hipStream_t stream) {
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
-        hipLaunchKernelGGL((bwd_state_mfma_kernel<DK, BVA, TD>),
+        hipLaunchKernelGGL((bwd_state_mfma_kernel<DK, BVA>),
                            dim3(static_cast<unsigned>(a.BH * (DV / BVA))), dim3(2 * NT), 0, stream,
                            static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.k),
-                           static_cast<const TD *>(a.d), a.beta, a.alpha,
+                           a.beta, a.alpha,
                            static_cast<const bf16_t *>(a.dO), a.dS_T, a.Tck,
                            static_cast<uint16_t *>(a.dMck), a.dS0, a.T, DV);
     } else

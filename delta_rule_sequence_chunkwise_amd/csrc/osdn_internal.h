@@ -58,9 +58,10 @@ struct BwdArgs {
     float *dS0;
     void *Mck, *dMck;     // workspace: [BH, nchunks, dk, dv] each, bf16 for bf16 inputs (the
                           // precision the matrix products take them in), else fp32
-    uint16_t *Tck;        // workspace (bf16 inputs), [BH, nchunks, 3, 64, 64] bf16 per chunk:
-                          // planes hi = bf16(T) and lo = bf16(T - hi) of T = (I + A)^{-1},
-                          // then the intra-chunk scores P (zero above the diagonal)
+    uint16_t *Tck;        // workspace (bf16 inputs), per chunk (bf16, row-major): the planes
+                          // hi = bf16(T) and lo = bf16(T - hi) of T = (I + A)^{-1} and the
+                          // scores P (64 x 64 each; P zero above the diagonal), then
+                          // K~ = d (.) k (64 x dk; zero past the end)
     int64_t BH, T;
     int32_t dk, dv;
     osdn_dtype qkv, d_dtype;

@@ -260,12 +260,12 @@ def test_chunk_bwd_rejects(L, over, status):
 
 
 def test_bwd_workspace_size(L):
-    # bf16 inputs: two bf16 checkpoints [B,H,nchunks,dk,dv] (64-row chunks) and three bf16
-    # 64 x 64 planes per chunk (the inverse's hi and lo, the scores), each rounded up to 256
-    # bytes
+    # bf16 inputs: two bf16 checkpoints [B,H,nchunks,dk,dv] (64-row chunks) and per chunk three
+    # bf16 64 x 64 planes (the inverse's hi and lo, the scores) and K~ (64 x dk bf16), each
+    # rounded up to 256 bytes
     nch = (100 + 63) // 64
     ck = 2 * 3 * nch * 128 * 64 * 2
-    ti = 2 * 3 * nch * 3 * 64 * 64 * 2
+    ti = 2 * 3 * nch * (3 * 64 * 64 + 64 * 128) * 2
     assert L.osdn_chunk_bwd_workspace(2, 3, 100, 128, 64, osdn.OSDN_BF16) == 2 * ck + ti
     # fp32 inputs: two fp32 checkpoints (32-row chunks), no inverses
     nch = (100 + 31) // 32
