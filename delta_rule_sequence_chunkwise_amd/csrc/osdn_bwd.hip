@@ -1186,15 +1186,18 @@ bwd_tinv_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 // Same data flow as bwd_state_kernel, on eight waves (two per SIMD).  One workgroup per
 // (sequence, 32-column value slice) walks the chunks backwards.  dM (fp32, dk x 32) lives in
 // registers: wave w owns its 16x16 tiles in the MFMA C layout and stores them, rounded to bf16,
-// straight to the checkpoint; LDS holds the same bf16 copy, the operand of K~ dM.  Per chunk, with a barrier after
-// each phase:
-//   stores   the chunk's q, k, K~, T and P planes and dO (prefetched into registers one
-//            chunk ahead) into LDS, and the next chunk's loads issued;
-//   scores   gam dO; one 16x16 tile of K~ dM per wave; one wave runs the decay scan of the
-//            next chunk (double-buffered);
-//   dU       dU = P^T dO + diag(w) K~ dM, one tile per wave, as hi/lo bf16;
-//   dR       dR = T^T dU from the T planes (hi.hi + hi.lo + lo.hi), one tile per wave;
-//   update   dM <- gam_L dM + Q^T diag(gam) dO - K^T diag(gam b) dR on the wave's own tiles.
+// straight to the checkpoint; LDS holds the same bf16 copy, the operand of K~ dM.  Per chunk c,
+// with a barrier after each phase:
+//   scores   q, k of chunk c into LDS; gam dO; one 16x16 tile of K~ dM per wave; one wave runs
+//            the decay scan of chunk c-1 (double-buffered);
+//   dU       dU = P^T dO + diag(w) K~ dM, one tile per wave, as hi/lo bf16; K~ of chunk c-1
+//            into LDS;
+//   dR       dR = T^T dU from the T planes (hi.hi + hi.lo + lo.hi), one tile per wave; P and
+//            dO of chunk c-1 into LDS;
+//   update   dM <- gam_L dM + Q^T diag(gam) dO - K^T diag(gam b) dR on the wave's own tiles;
+//            the T planes of chunk c-1 into LDS.
+// So each tile of the next chunk is written in a phase after the last read of its buffer,
+// with no phase of its own; its loads go to registers two to four phases before.
 template <int DK, int BV>
 __global__ void __launch_bounds__(2 * NT)
 bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
@@ -1241,18 +1244,17 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
     const int64_t seq0 = bh * T;
     auto rows_of = [&](int64_t cc) { return static_cast<int>(T - cc * C < C ? T - cc * C : C); };
 
-    // the next chunk's q, k, K~, T and P planes and dO in named registers, loaded one chunk
-    // ahead (an array carried across the loop would live in scratch); unit i of this thread
-    // is u = tid + i NTH: row u / G, features 8 (u % G) .. +7; plane unit u holds elements
-    // 8u .. 8u+7 of the three 64 x 64 planes (plane u / 512, row (u / 8) % 64, columns
-    // 8 (u % 8) ..)
+    // q, k, K~, the T and P planes and dO of a coming chunk in named registers (an array
+    // carried across the loop would live in scratch); unit i of this thread is u = tid + i NTH:
+    // row u / G, features 8 (u % G) .. +7; plane unit u holds elements 8u .. 8u+7 of the three
+    // 64 x 64 planes (plane u / 512, row (u / 8) % 64, columns 8 (u % 8) ..)
     uint4 q0, q1, k0r, k1r, w0, w1, t0, t1, t2;
     uint2 ou;
     auto qreg = [&](auto I) -> uint4 & { if constexpr (decltype(I)::value == 0) return q0; else return q1; };
     auto kreg = [&](auto I) -> uint4 & { if constexpr (decltype(I)::value == 0) return k0r; else return k1r; };
     auto wreg = [&](auto I) -> uint4 & { if constexpr (decltype(I)::value == 0) return w0; else return w1; };
-    // issued in three parts spread over the phases of the chunk before (a wave stalls while
-    // the CU's load queue is full, so one burst would hold up the barrier that follows it)
+    // loads and stores by part; the loads are spread over the phases (a wave stalls while the
+    // CU's load queue is full, so one burst would hold up the barrier that follows it)
     auto load_qk = [&](int64_t cc) __attribute__((always_inline)) {
         const bf16_t *qc = q + (seq0 + cc * C) * DK, *kc = k + (seq0 + cc * C) * DK;
         const int nn = rows_of(cc);
@@ -1262,18 +1264,46 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             qreg(I) = *reinterpret_cast<const uint4 *>(qc + e);
             kreg(I) = *reinterpret_cast<const uint4 *>(kc + e);
         });
-        const int r = tid / (BV / 4), j = 4 * (tid % (BV / 4));
-        ou = *reinterpret_cast<const uint2 *>(dO + (seq0 + cc * C + (r < nn ? r : nn - 1)) * dv + j0 + j);
+    };
+    auto store_qk = [&](int nn) __attribute__((always_inline)) {
+        static_for<0, NU>([&](auto I) __attribute__((always_inline)) {
+            const int u = tid + I * NTH, r = u / G, g = u % G;
+            const uint32_t m = r < nn ? 0xffffffffu : 0u;  // rows past the end are zero
+            const uint4 kq = kreg(I), qq = qreg(I);
+            *reinterpret_cast<uint4 *>(&sQ[r * PH + 8 * g]) = make_uint4(qq.x & m, qq.y & m, qq.z & m, qq.w & m);
+            *reinterpret_cast<uint4 *>(&sK[r * PH + 8 * g]) = make_uint4(kq.x & m, kq.y & m, kq.z & m, kq.w & m);
+        });
     };
     auto load_kt = [&](int64_t cc) __attribute__((always_inline)) {  // K~, zero past the end
         const uint4 *wp = reinterpret_cast<const uint4 *>(Tck + (bh * nch + cc) * CHS + 3 * C * C);
         static_for<0, NU>([&](auto I) __attribute__((always_inline)) { wreg(I) = wp[tid + I * NTH]; });
     };
-    auto load_t = [&](int64_t cc) __attribute__((always_inline)) {
+    auto store_kt = [&]() __attribute__((always_inline)) {
+        static_for<0, NU>([&](auto I) __attribute__((always_inline)) {
+            const int u = tid + I * NTH, r = u / G, g = u % G;
+            *reinterpret_cast<uint4 *>(&sKt[r * PH + 8 * g]) = wreg(I);
+        });
+    };
+    auto load_pdo = [&](int64_t cc) __attribute__((always_inline)) {  // P plane, dO slice
+        t2 = reinterpret_cast<const uint4 *>(Tck + (bh * nch + cc) * CHS)[tid + 2 * NTH];
+        const int nn = rows_of(cc), r = tid / (BV / 4), j = 4 * (tid % (BV / 4));
+        ou = *reinterpret_cast<const uint2 *>(dO + (seq0 + cc * C + (r < nn ? r : nn - 1)) * dv + j0 + j);
+    };
+    auto store_pdo = [&](int nn) __attribute__((always_inline)) {
+        *reinterpret_cast<uint4 *>(&sPb[((tid >> 3) & 63) * PCH + 8 * (tid & 7)]) = t2;
+        const int r = tid / (BV / 4), j = 4 * (tid % (BV / 4));
+        const uint32_t m = r < nn ? 0xffffffffu : 0u;
+        *reinterpret_cast<uint2 *>(&sDOb[r * PVH + j]) = make_uint2(ou.x & m, ou.y & m);
+    };
+    auto load_t = [&](int64_t cc) __attribute__((always_inline)) {  // T hi, lo planes
         const uint4 *tp = reinterpret_cast<const uint4 *>(Tck + (bh * nch + cc) * CHS);
         t0 = tp[tid];
         t1 = tp[tid + NTH];
-        t2 = tp[tid + 2 * NTH];
+    };
+    auto store_t = [&]() __attribute__((always_inline)) {
+        const int r = (tid >> 3) & 63, g = tid & 7;  // unit tid of each plane
+        *reinterpret_cast<uint4 *>(&sTh[r * PCH + 8 * g]) = t0;
+        *reinterpret_cast<uint4 *>(&sTl[r * PCH + 8 * g]) = t1;
     };
     // decay scan of chunk cc into buffer cc & 1 (one wave; beta, alpha of the chunk in bv, av)
     float bv = 0.f, av = 1.f;
@@ -1309,10 +1339,18 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             if (nch > 0) dMck[((bh * nch + nch - 1) * DK + f) * dv + j0 + j] = bf16_bits(dM[m][e]);
         }
     }
-    if (nch > 0) {
+    if (nch > 0) {  // the last chunk's tiles (q, k stay in registers for its first phase)
         load_qk(nch - 1);
         load_kt(nch - 1);
+        load_pdo(nch - 1);
         load_t(nch - 1);
+        store_kt();
+        store_pdo(rows_of(nch - 1));
+        store_t();
+        if (nch > 1) {
+            load_kt(nch - 2);
+            load_pdo(nch - 2);
+        }
         if (wave == NW - 1) {
             load_ba(nch - 1);
             scan(nch - 1);
@@ -1322,29 +1360,8 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
 
     for (int64_t c = nch - 1; c >= 0; --c) {
         const int n = rows_of(c), pb = static_cast<int>(c & 1);
-        __syncthreads();  // the previous chunk is done with every buffer
-        // this chunk's registers into LDS: Q, K, K~ (bf16), the T and P planes, dO
-        static_for<0, NU>([&](auto I) __attribute__((always_inline)) {
-            const int u = tid + I * NTH, r = u / G, g = u % G;
-            const uint32_t m = r < n ? 0xffffffffu : 0u;  // rows past the end are zero
-            const uint4 kq = kreg(I), qq = qreg(I);
-            *reinterpret_cast<uint4 *>(&sQ[r * PH + 8 * g]) = make_uint4(qq.x & m, qq.y & m, qq.z & m, qq.w & m);
-            *reinterpret_cast<uint4 *>(&sK[r * PH + 8 * g]) = make_uint4(kq.x & m, kq.y & m, kq.z & m, kq.w & m);
-            *reinterpret_cast<uint4 *>(&sKt[r * PH + 8 * g]) = wreg(I);
-        });
-        {
-            const int r = (tid >> 3) & 63, g = tid & 7;  // unit tid of each plane
-            *reinterpret_cast<uint4 *>(&sTh[r * PCH + 8 * g]) = t0;
-            *reinterpret_cast<uint4 *>(&sTl[r * PCH + 8 * g]) = t1;
-            *reinterpret_cast<uint4 *>(&sPb[r * PCH + 8 * g]) = t2;
-        }
-        {
-            const int r = tid / (BV / 4), j = 4 * (tid % (BV / 4));
-            const uint32_t m = r < n ? 0xffffffffu : 0u;
-            *reinterpret_cast<uint2 *>(&sDOb[r * PVH + j]) = make_uint2(ou.x & m, ou.y & m);
-        }
-        if (c > 0) load_qk(c - 1);  // in flight through this chunk's work
-        __syncthreads();
+        __syncthreads();  // the previous chunk is done with sQ, sK, sGDOb, sGDRb, sdMb
+        store_qk(n);
         {  // gam-scaled dO for the dM update
             const int r = tid / (BV / 4), j = 4 * (tid % (BV / 4));
             const uint2 o = *reinterpret_cast<const uint2 *>(&sDOb[r * PVH + j]);
@@ -1361,7 +1378,7 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             scan(c - 1);
             if (c > 1) load_ba(c - 2);
         }
-        if (c > 0) load_kt(c - 1);
+        if (c > 0) load_t(c - 1);
         __syncthreads();
         {  // dU = P^T dO + diag(w) K~ dM on this wave's tile, as hi/lo bf16
             v4f du = zero4();
@@ -1377,7 +1394,10 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
                 sdUl[r * PVH + j] = bf16_bits(x - __uint_as_float(uint32_t(h) << 16));
             }
         }
-        if (c > 0) load_t(c - 1);
+        if (c > 0) {  // K~ of the next chunk (sKt was last read by this chunk's K~ dM)
+            store_kt();
+            load_qk(c - 1);
+        }
         __syncthreads();
         {  // dR = T^T dU (T^T upper triangular: k-steps from the tile's first row on); -gam b dR
             v4f dr = zero4();
@@ -1394,6 +1414,13 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             for (int e = 0; e < 4; ++e) {
                 const int r = R0 + 4 * lq + e, j = jt + lr;
                 sGDRb[r * PVH + j] = bf16_bits(-sgam[pb][r] * sb[pb][r] * dr[e]);
+            }
+        }
+        if (c > 0) {  // P and dO of the next chunk (last read by this chunk's dU)
+            store_pdo(rows_of(c - 1));
+            if (c > 1) {
+                load_kt(c - 2);
+                load_pdo(c - 2);
             }
         }
         __syncthreads();
@@ -1422,6 +1449,7 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
                 }
             }
         }
+        if (c > 0) store_t();  // T of the next chunk (last read by this chunk's dR)
     }
     if (dS0) {
 #pragma unroll
