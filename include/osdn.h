@@ -205,13 +205,13 @@ osdn_status osdn_step_kda(const void *q, const void *k, const void *v, const flo
  * Every other argument as for osdn_chunk_fwd; the chunk size is the library's (64 rows for
  * bf16 inputs, 32 for fp32).  Outputs must not overlap each other, an input or the workspace.
  * Kernels run on `stream`: the forward recording the state at every chunk start (the same
- * forward osdn_chunk_fwd runs for this input type), for bf16 inputs the inverse (I + A)^{-1}
- * and the scores of every chunk, a reverse pass over chunks for the state gradient, and the
+ * forward osdn_chunk_fwd runs for this input type), for bf16 inputs the inverse (I + A)^{-1},
+ * the scores and k~ of every chunk, a reverse pass over chunks for the state gradient, and the
  * per-chunk gradients.
  * The workspace holds the state and state-gradient checkpoints ([B,H,nchunks,dk,dv] each;
  * bf16 for bf16 inputs, the precision the matrix products take them in; fp32 for fp32 inputs)
- * and, for bf16 inputs, three bf16 64 x 64 planes per chunk: the inverse (I + A)^{-1} as hi and
- * lo parts, and the intra-chunk scores.
+ * and, for bf16 inputs, per chunk three bf16 64 x 64 planes (the inverse (I + A)^{-1} as hi and
+ * lo parts, and the intra-chunk scores) and k~ = d (.) k as 64 x dk bf16.
  */
 int64_t osdn_chunk_bwd_workspace(int64_t B, int64_t H, int64_t T, int32_t dk, int32_t dv,
                                  osdn_dtype qkv); /* -1 if invalid */
