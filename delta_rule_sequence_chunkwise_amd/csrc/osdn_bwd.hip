@@ -803,8 +803,9 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
         if (s0 + BV < DV) OSDN_BWD_LOAD_SLICE(s0 + BV);  // in flight through this slice's work
         __syncthreads();
         // K M0, K~ dMC on this wave's tile; Y = V - gam K M0 (registers), R = b Y into LDS as
-        // hi/lo bf16 over V
-        v4f km = zero4(), kdm = zero4(), y;
+        // hi/lo bf16 over V; dU = P^T dO + diag(w) K~ dMC (the same tile: no other wave's part
+        // is needed) as hi/lo bf16
+        v4f km = zero4(), kdm = zero4(), y, du = zero4();
 #pragma unroll 2
         for (int k0 = 0; k0 < DK; k0 += 32) {
             const v8s m0f = frag_cols(sM0b, PVH, k0, jt, lr, lq);
@@ -820,9 +821,21 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             sRh[r * PVH + j] = h;
             sRl[r * PVH + j] = bf16_bits(x - __uint_as_float(uint32_t(h) << 16));
         }
+#pragma unroll
+        for (int k0 = 0; k0 < C; k0 += 32)
+            du = mfma32(frag_cols(sPb, PCH, k0, R0, lr, lq), frag_cols(sDOb, PVH, k0, jt, lr, lq), du);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = R0 + 4 * lq + e, j = jt + lr;
+            const float x = du[e] + sw[r] * kdm[e];
+            const uint16_t h = bf16_bits(x);
+            sdUh[r * PVH + j] = h;
+            sdUl[r * PVH + j] = bf16_bits(x - __uint_as_float(uint32_t(h) << 16));
+        }
         __syncthreads();
-        // U = T R (T lower triangular) and dU = P^T dO + diag(w) K~ dMC
-        v4f u = zero4(), du = zero4();
+        // U = T R (T lower triangular) and dR = T^T dU (T^T upper triangular), two independent
+        // chains; dV = diag(b) dR
+        v4f u = zero4(), dr = zero4();
 #pragma unroll
         for (int k0 = 0; k0 < C; k0 += 32) {
             if (k0 > R0 + 15) continue;
@@ -832,22 +845,6 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             u = mfma32(th, rl, u);
             u = mfma32(tl, rh, u);
         }
-#pragma unroll
-        for (int k0 = 0; k0 < C; k0 += 32)
-            du = mfma32(frag_cols(sPb, PCH, k0, R0, lr, lq), frag_cols(sDOb, PVH, k0, jt, lr, lq), du);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = R0 + 4 * lq + e, j = jt + lr;
-            sUb[r * PVH + j] = bf16_bits(u[e]);
-            pew[e] += kdm[e] * u[e];
-            const float x = du[e] + sw[r] * kdm[e];
-            const uint16_t h = bf16_bits(x);
-            sdUh[r * PVH + j] = h;
-            sdUl[r * PVH + j] = bf16_bits(x - __uint_as_float(uint32_t(h) << 16));
-        }
-        __syncthreads();
-        // dR = T^T dU (T^T upper triangular); dV = diag(b) dR
-        v4f dr = zero4();
 #pragma unroll
         for (int k0 = 0; k0 < C; k0 += 32) {
             if (k0 + 32 <= R0) continue;
@@ -861,6 +858,8 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = R0 + 4 * lq + e, j = jt + lr;
+            sUb[r * PVH + j] = bf16_bits(u[e]);
+            pew[e] += kdm[e] * u[e];
             sDRb[r * PVH + j] = bf16_bits(dr[e]);
             pgr[e] += dr[e] * km[e];
             pdb[e] += dr[e] * y[e];
