@@ -98,9 +98,9 @@ def main():
                          "reference for scaling HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the (b,h) "
-              "sequences shard across GPUs with no communication; see the design notes). "
-              "Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: libosdn has no multi-GPU path (the (b,h) "
+              "sequences would shard across GPUs with no communication). Run with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
