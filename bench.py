@@ -262,6 +262,24 @@ def bench_bwd(n_steps, torch, dev, synth, w, x, fwd, cpu):
     e1.record(stream)
     torch.cuda.synchronize()
     per = e0.elapsed_time(e1) / 1e3 / n_steps
+    # the training pair: the forward that keeps the chunk-start states, and the backward that
+    # takes them (no forward recompute inside)
+    o_buf, st_buf, states = osdn.osdn_chunk_fwd_states(q, k, v, beta, d, alpha, S0)
+    osdn.osdn_chunk_bwd(q, k, v, beta, d, alpha, S0, do, dS_T, grads=grads, workspace=ws,
+                        states=states)
+    torch.cuda.synchronize()
+    e2 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n_steps):
+        osdn.osdn_chunk_fwd_states(q, k, v, beta, d, alpha, S0, o=o_buf, S_T=st_buf, states=states)
+    e1.record(stream)
+    for _ in range(n_steps):
+        osdn.osdn_chunk_bwd(q, k, v, beta, d, alpha, S0, do, dS_T, grads=grads, workspace=ws,
+                            states=states)
+    e2.record(stream)
+    torch.cuda.synchronize()
+    fwd_states_ms = e0.elapsed_time(e1) / n_steps
+    bwd_states_ms = e1.elapsed_time(e2) / n_steps
     head_tokens = B * H * T
     eq = 2 if w.qkv == "bf16" else 4
     # in: q, k, v, do (qkv type), d (fp32), beta, alpha; out: grad q, k, v (qkv type), grad d
@@ -274,6 +292,11 @@ def bench_bwd(n_steps, torch, dev, synth, w, x, fwd, cpu):
                        "fp32 S0, dS_T and grad S0",
            "ms_per_step": round(per * 1e3, 4),
            "tokens_per_s": round(B * T / per, 1),
+           "training_pair": {"fwd_states_ms": round(fwd_states_ms, 4),
+                             "bwd_from_states_ms": round(bwd_states_ms, 4),
+                             "step_ms": round(fwd_states_ms + bwd_states_ms, 4),
+                             "note": "osdn_chunk_fwd_states (o, S_T and the chunk-start states) "
+                                     "then osdn_chunk_bwd_states (no forward recompute)"},
            "roofline": {"bound": "hbm", "achieved": round(alg / per / 1e9, 2),
                         "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                         "frac": round(alg / per / PEAK_HBM, 5), "alg_bytes_per_step": alg,

@@ -63,11 +63,18 @@ const char *osdn_status_string(osdn_status s) {
 
 int32_t osdn_abi_version(void) { return OSDN_ABI_VERSION; }
 
-osdn_status osdn_chunk_fwd(const void *q, const void *k, const void *v, const float *beta,
+}  // extern "C"
+
+namespace {
+
+// The chunkwise forward: validation, then the launch.  With want_states, `states` receives the
+// state at every chunk start ([B,H,nchunks,dk,dv]; bf16 for bf16 inputs, else fp32; the
+// chunk size is then the backward's).
+osdn_status chunk_fwd_impl(const void *q, const void *k, const void *v, const float *beta,
                            const void *d, const float *alpha, const float *S0, void *o,
-                           float *S_T, int64_t B, int64_t H, int64_t T, int32_t dk,
-                           int32_t dv, int32_t chunk, osdn_dtype qkv, osdn_dtype d_dtype,
-                           void *stream) {
+                           float *S_T, void *states, bool want_states, int64_t B, int64_t H,
+                           int64_t T, int32_t dk, int32_t dv, int32_t chunk, osdn_dtype qkv,
+                           osdn_dtype d_dtype, void *stream) {
     if (B < 0 || H < 0 || T < 0) return OSDN_ERR_SHAPE;
     if (!dtype_ok(qkv) || !dtype_ok(d_dtype)) return OSDN_ERR_UNSUPPORTED;
     if (!head_dim_ok(dk) || !head_dim_ok(dv)) return OSDN_ERR_UNSUPPORTED;
@@ -84,14 +91,19 @@ osdn_status osdn_chunk_fwd(const void *q, const void *k, const void *v, const fl
     if (!mul_ok(st, int64_t(dk) * dv, kMaxElems)) return OSDN_ERR_SHAPE;
     if (BH > int64_t(0x7fffffff) / 4) return OSDN_ERR_SHAPE;  // grid: BH x (dv / 32) groups
 
+    int64_t nst = st;  // elements of the states at every chunk start
+    if (want_states && !mul_ok(nst, (T + chunk - 1) / chunk, kMaxElems)) return OSDN_ERR_SHAPE;
+
     if (BH == 0) return OSDN_OK;
-    if (T > 0 && (!q || !k || !v || !beta || !d || !o)) return OSDN_ERR_NULL;
+    if (T > 0 && (!q || !k || !v || !beta || !d || !o || (want_states && !states)))
+        return OSDN_ERR_NULL;
     if (T == 0 && !S_T) return OSDN_OK;
 
     const int64_t eq = elem_size(qkv), ed = elem_size(d_dtype);
     if (T > 0) {
         if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(d, 16) ||
-            !aligned(o, 16) || !aligned(beta, 4) || (alpha && !aligned(alpha, 4)))
+            !aligned(o, 16) || !aligned(beta, 4) || (alpha && !aligned(alpha, 4)) ||
+            (want_states && !aligned(states, 16)))
             return OSDN_ERR_ALIGN;
     }
     if ((S0 && !aligned(S0, 16)) || (S_T && !aligned(S_T, 16))) return OSDN_ERR_ALIGN;
@@ -107,12 +119,29 @@ osdn_status osdn_chunk_fwd(const void *q, const void *k, const void *v, const fl
     for (const Range *in : {&rq, &rk, &rv, &rd, &rb, &ra})
         if (overlap(rst, *in)) return OSDN_ERR_ALIAS;
     if (overlap(rst, rs0) && (rst.lo != rs0.lo)) return OSDN_ERR_ALIAS;
+    const Range rsts = range_of(want_states ? states : nullptr, n_tok ? nst * eq : 0);
+    for (const Range *x : {&rq, &rk, &rv, &rd, &rb, &ra, &rs0, &rst, &ro})
+        if (overlap(rsts, *x)) return OSDN_ERR_ALIAS;
 
     osdn::ChunkArgs a{q, k, v, d, beta, alpha, S0, o, S_T, BH, T, dk, dv, chunk, qkv, d_dtype};
+    if (want_states && T > 0) a.ckpt = states;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const hipError_t err = qkv == OSDN_BF16 ? osdn::launch_chunk_fwd_mfma(a, s)
                                             : osdn::launch_chunk_fwd_f32math(a, s);
     return err == hipSuccess ? OSDN_OK : OSDN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+osdn_status osdn_chunk_fwd(const void *q, const void *k, const void *v, const float *beta,
+                           const void *d, const float *alpha, const float *S0, void *o,
+                           float *S_T, int64_t B, int64_t H, int64_t T, int32_t dk,
+                           int32_t dv, int32_t chunk, osdn_dtype qkv, osdn_dtype d_dtype,
+                           void *stream) {
+    return chunk_fwd_impl(q, k, v, beta, d, alpha, S0, o, S_T, nullptr, false, B, H, T, dk, dv,
+                          chunk, qkv, d_dtype, stream);
 }
 
 osdn_status osdn_step(const void *q, const void *k, const void *v, const float *beta,
@@ -410,13 +439,20 @@ int64_t osdn_chunk_bwd_workspace(int64_t B, int64_t H, int64_t T, int32_t dk, in
     return t < 0 ? -1 : 2 * b + t;
 }
 
-osdn_status osdn_chunk_bwd(const void *q, const void *k, const void *v, const float *beta,
+}  // extern "C"
+
+namespace {
+
+// The backward: validation, then the launches.  With states_given, `states` holds the state at
+// every chunk start from the forward (osdn_chunk_fwd_states) and is not recomputed.
+osdn_status chunk_bwd_impl(const void *q, const void *k, const void *v, const float *beta,
                            const void *d, const float *alpha, const float *S0,
-                           const void *grad_o, const float *grad_S_T, void *grad_q,
-                           void *grad_k, void *grad_v, float *grad_beta, void *grad_d,
-                           float *grad_alpha, float *grad_S0, void *workspace,
-                           int64_t workspace_bytes, int64_t B, int64_t H, int64_t T, int32_t dk,
-                           int32_t dv, osdn_dtype qkv, osdn_dtype d_dtype, void *stream) {
+                           const void *grad_o, const float *grad_S_T, const void *states,
+                           bool states_given, void *grad_q, void *grad_k, void *grad_v,
+                           float *grad_beta, void *grad_d, float *grad_alpha, float *grad_S0,
+                           void *workspace, int64_t workspace_bytes, int64_t B, int64_t H,
+                           int64_t T, int32_t dk, int32_t dv, osdn_dtype qkv,
+                           osdn_dtype d_dtype, void *stream) {
     if (B < 0 || H < 0 || T < 0) return OSDN_ERR_SHAPE;
     if (!dtype_ok(qkv) || !dtype_ok(d_dtype)) return OSDN_ERR_UNSUPPORTED;
     if (!head_dim_ok(dk) || !head_dim_ok(dv)) return OSDN_ERR_UNSUPPORTED;
@@ -438,7 +474,7 @@ osdn_status osdn_chunk_bwd(const void *q, const void *k, const void *v, const fl
 
     if (BH == 0) return OSDN_OK;
     if (T > 0 && (!q || !k || !v || !beta || !d || !grad_o || !grad_q || !grad_k || !grad_v ||
-                  !grad_beta || !grad_d || !workspace))
+                  !grad_beta || !grad_d || !workspace || (states_given && !states)))
         return OSDN_ERR_NULL;
     if (T == 0 && !grad_S0) return OSDN_OK;
     if (T > 0 && workspace_bytes < wsb) return OSDN_ERR_SHAPE;
@@ -450,7 +486,8 @@ osdn_status osdn_chunk_bwd(const void *q, const void *k, const void *v, const fl
             !aligned(grad_o, 16) || !aligned(grad_q, 16) || !aligned(grad_k, 16) ||
             !aligned(grad_v, 16) || !aligned(grad_d, 16) || !aligned(beta, 4) ||
             !aligned(grad_beta, 4) || (alpha && !aligned(alpha, 4)) ||
-            (grad_alpha && !aligned(grad_alpha, 4)) || !aligned(workspace, 256))
+            (grad_alpha && !aligned(grad_alpha, 4)) || !aligned(workspace, 256) ||
+            (states_given && !aligned(states, 16)))
             return OSDN_ERR_ALIGN;
     }
     if ((S0 && !aligned(S0, 16)) || (grad_S_T && !aligned(grad_S_T, 16)) ||
@@ -463,13 +500,16 @@ osdn_status osdn_chunk_bwd(const void *q, const void *k, const void *v, const fl
     const Range rb = range_of(beta, nt * 4), ra = range_of(alpha, alpha ? nt * 4 : 0);
     const Range rs0 = range_of(S0, st * 4), rgo = range_of(grad_o, nt ? nv * eq : 0);
     const Range rgst = range_of(grad_S_T, st * 4);
+    int64_t nst = st;  // elements of the states at every chunk start
+    if (!mul_ok(nst, nch, kMaxElems)) return OSDN_ERR_SHAPE;
+    const Range rsts = range_of(states_given ? states : nullptr, nt ? nst * eq : 0);
     const Range gq = range_of(grad_q, nt ? nqk * eq : 0), gk = range_of(grad_k, nt ? nqk * eq : 0);
     const Range gv = range_of(grad_v, nt ? nv * eq : 0), gd = range_of(grad_d, nt ? nqk * ed : 0);
     const Range gb = range_of(grad_beta, nt * 4), ga = range_of(grad_alpha, grad_alpha ? nt * 4 : 0);
     const Range gs0 = range_of(grad_S0, st * 4);
     const Range rw = range_of(workspace, T > 0 ? wsb : 0);
     const Range *outs[] = {&gq, &gk, &gv, &gd, &gb, &ga, &gs0, &rw};
-    const Range *ins[] = {&rq, &rk, &rv, &rd, &rb, &ra, &rs0, &rgo, &rgst};
+    const Range *ins[] = {&rq, &rk, &rv, &rd, &rb, &ra, &rs0, &rgo, &rgst, &rsts};
     for (int i = 0; i < 8; ++i) {
         for (const Range *in : ins)
             if (overlap(*outs[i], *in)) return OSDN_ERR_ALIAS;
@@ -480,11 +520,64 @@ osdn_status osdn_chunk_bwd(const void *q, const void *k, const void *v, const fl
     char *ws = static_cast<char *>(workspace);
     osdn::BwdArgs a{q, k, v, d, beta, alpha, S0, grad_o, grad_S_T, grad_q, grad_k, grad_v,
                     grad_beta, grad_alpha, grad_d, grad_S0,
-                    T > 0 ? ws : nullptr, T > 0 ? ws + ck : nullptr,
+                    T > 0 ? (states_given ? const_cast<void *>(states) : ws) : nullptr,
+                    T > 0 ? ws + ck : nullptr, states_given,
                     T > 0 && tk > 0 ? reinterpret_cast<uint16_t *>(ws + 2 * ck) : nullptr, BH, T,
                     dk, dv, qkv, d_dtype};
     const hipError_t err = osdn::launch_chunk_bwd(a, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? OSDN_OK : OSDN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+osdn_status osdn_chunk_bwd(const void *q, const void *k, const void *v, const float *beta,
+                           const void *d, const float *alpha, const float *S0,
+                           const void *grad_o, const float *grad_S_T, void *grad_q,
+                           void *grad_k, void *grad_v, float *grad_beta, void *grad_d,
+                           float *grad_alpha, float *grad_S0, void *workspace,
+                           int64_t workspace_bytes, int64_t B, int64_t H, int64_t T, int32_t dk,
+                           int32_t dv, osdn_dtype qkv, osdn_dtype d_dtype, void *stream) {
+    return chunk_bwd_impl(q, k, v, beta, d, alpha, S0, grad_o, grad_S_T, nullptr, false, grad_q,
+                          grad_k, grad_v, grad_beta, grad_d, grad_alpha, grad_S0, workspace,
+                          workspace_bytes, B, H, T, dk, dv, qkv, d_dtype, stream);
+}
+
+int64_t osdn_chunk_states_bytes(int64_t B, int64_t H, int64_t T, int32_t dk, int32_t dv,
+                                osdn_dtype qkv) {
+    if (B < 0 || H < 0 || T < 0 || !dtype_ok(qkv) || !head_dim_ok(dk) || !head_dim_ok(dv))
+        return -1;
+    const int64_t C = osdn::bwd_chunk_size(qkv);
+    int64_t n = elem_size(qkv);
+    if (!mul_ok(n, B, kMaxElems) || !mul_ok(n, H, kMaxElems) ||
+        !mul_ok(n, (T + C - 1) / C, kMaxElems) || !mul_ok(n, int64_t(dk) * dv, kMaxElems))
+        return -1;
+    return n;
+}
+
+osdn_status osdn_chunk_fwd_states(const void *q, const void *k, const void *v,
+                                  const float *beta, const void *d, const float *alpha,
+                                  const float *S0, void *o, float *S_T, void *states, int64_t B,
+                                  int64_t H, int64_t T, int32_t dk, int32_t dv, osdn_dtype qkv,
+                                  osdn_dtype d_dtype, void *stream) {
+    if (!dtype_ok(qkv)) return OSDN_ERR_UNSUPPORTED;
+    return chunk_fwd_impl(q, k, v, beta, d, alpha, S0, o, S_T, states, true, B, H, T, dk, dv,
+                          osdn::bwd_chunk_size(qkv), qkv, d_dtype, stream);
+}
+
+osdn_status osdn_chunk_bwd_states(const void *q, const void *k, const void *v,
+                                  const float *beta, const void *d, const float *alpha,
+                                  const float *S0, const void *states, const void *grad_o,
+                                  const float *grad_S_T, void *grad_q, void *grad_k,
+                                  void *grad_v, float *grad_beta, void *grad_d,
+                                  float *grad_alpha, float *grad_S0, void *workspace,
+                                  int64_t workspace_bytes, int64_t B, int64_t H, int64_t T,
+                                  int32_t dk, int32_t dv, osdn_dtype qkv, osdn_dtype d_dtype,
+                                  void *stream) {
+    return chunk_bwd_impl(q, k, v, beta, d, alpha, S0, grad_o, grad_S_T, states, true, grad_q,
+                          grad_k, grad_v, grad_beta, grad_d, grad_alpha, grad_S0, workspace,
+                          workspace_bytes, B, H, T, dk, dv, qkv, d_dtype, stream);
 }
 
 }  // extern "C"

@@ -1464,8 +1464,8 @@ template <int C, int DK, int DV, typename TQ, typename TD>
 hipError_t bwd_typed(const BwdArgs &a, hipStream_t stream) {
     const int64_t nch = (a.T + C - 1) / C;
     // forward states at every chunk start (the matrix-core forward for bf16 inputs, the fp32
-    // one for fp32 inputs)
-    if (nch > 0) {
+    // one for fp32 inputs), unless the caller passes those of its forward
+    if (nch > 0 && !a.states_given) {
         ChunkArgs f{a.q, a.k, a.v, a.d, a.beta, a.alpha, a.S0, nullptr, nullptr, a.BH, a.T, DK,
                     DV, C, a.qkv, a.d_dtype};
         f.ckpt = a.Mck;

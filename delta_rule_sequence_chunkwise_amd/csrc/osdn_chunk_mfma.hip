@@ -36,7 +36,7 @@
 // With the channel-wise gate (the caller passes pre-scaled q, k, d and per-chunk factors G_C)
 // the state waves also multiply the state's rows by G_C after each carry; the loader brings
 // G_C into LDS with the other loads of its chunk.  For the backward a variant records the state
-// at every chunk start instead of writing o.
+// at every chunk start (CKPT), with or without writing o (OUT).
 // Loads stall the issuing wave while HBM drains them, and too many in flight at once thrash
 // the CU's load queues; so they are issued in groups of at most 16 by waves whose other work
 // is light, and each state wave shares its SIMD with a stager.
@@ -257,7 +257,7 @@ __device__ __forceinline__ void diag_inverse2(Lds<DK, G> &sm, int b, int kb0, in
             pack4u(Y[j]);
 }
 
-template <int DK, typename TD, bool GATE, bool CKPT>
+template <int DK, typename TD, bool GATE, bool CKPT, bool OUT>
 __global__ void __launch_bounds__(NW * 64)
 chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                   const uint16_t *__restrict__ v, const TD *__restrict__ d,
@@ -438,7 +438,7 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                 const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
                     o + row0 * dv, 0, n * dv * 2, 0x00020000);
 #pragma unroll
-                for (int rt = 0; rt < NBLK && !CKPT; ++rt) {
+                for (int rt = 0; rt < NBLK && OUT; ++rt) {
                     v4f a = oacc[rt];
                     if (rt >= 2) a = mfma32(ub1, pf[rt][1], a);
                     const uint2 pk = pack4u(a);
@@ -708,16 +708,17 @@ template <int DK, typename TD>
 hipError_t launch_typed(const ChunkArgs &a, hipStream_t stream) {
     const int nvt = a.dv / BV;
     const dim3 grid(static_cast<unsigned>(a.BH * nvt));
-#define OSDN_CHUNK_LAUNCH(GATE, CKPT)                                                         \
-    hipLaunchKernelGGL((chunk_mfma_kernel<DK, TD, GATE, CKPT>), grid, dim3(NW * 64), 0,       \
+#define OSDN_CHUNK_LAUNCH(GATE, CKPT, OUT)                                                    \
+    hipLaunchKernelGGL((chunk_mfma_kernel<DK, TD, GATE, CKPT, OUT>), grid, dim3(NW * 64), 0,  \
                        stream, static_cast<const uint16_t *>(a.q),                             \
                        static_cast<const uint16_t *>(a.k), static_cast<const uint16_t *>(a.v), \
                        static_cast<const TD *>(a.d), a.beta, a.alpha, a.S0,                    \
                        static_cast<uint16_t *>(a.o), a.S_T, a.BH, a.T, a.dv, a.gcs,            \
                        static_cast<uint16_t *>(a.ckpt))
-    if (a.gcs) OSDN_CHUNK_LAUNCH(true, false);
-    else if (a.ckpt) OSDN_CHUNK_LAUNCH(false, true);
-    else OSDN_CHUNK_LAUNCH(false, false);
+    if (a.gcs) OSDN_CHUNK_LAUNCH(true, false, true);
+    else if (a.ckpt && a.o) OSDN_CHUNK_LAUNCH(false, true, true);
+    else if (a.ckpt) OSDN_CHUNK_LAUNCH(false, true, false);
+    else OSDN_CHUNK_LAUNCH(false, false, true);
 #undef OSDN_CHUNK_LAUNCH
     return hipGetLastError();
 }

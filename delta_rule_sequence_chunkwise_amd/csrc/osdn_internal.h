@@ -44,7 +44,7 @@ struct ChunkArgs {
                                  // state's rows after each chunk's carry (channel-wise gate)
     void *ckpt = nullptr;        // [BH, nchunks, dk, dv]: the state at every chunk start, fp32
                                  // from the fp32 forward, bf16 from the matrix-core forward
-                                 // (then o is not written and may be NULL; no channel gate)
+                                 // (o may then be NULL: not written; no channel gate)
 };
 
 struct BwdArgs {
@@ -56,8 +56,10 @@ struct BwdArgs {
     float *gbeta, *galpha;
     void *gd;             // d dtype
     float *dS0;
-    void *Mck, *dMck;     // workspace: [BH, nchunks, dk, dv] each, bf16 for bf16 inputs (the
-                          // precision the matrix products take them in), else fp32
+    void *Mck, *dMck;     // [BH, nchunks, dk, dv] each, bf16 for bf16 inputs (the precision
+                          // the matrix products take them in), else fp32: the workspace's, or
+                          // for Mck the caller's states from the forward (states_given)
+    bool states_given;    // Mck holds the forward's states: no recompute
     uint16_t *Tck;        // workspace (bf16 inputs), per chunk (bf16, row-major): the planes
                           // hi = bf16(T) and lo = bf16(T - hi) of T = (I + A)^{-1} and the
                           // scores P (64 x 64 each; P zero above the diagonal), then

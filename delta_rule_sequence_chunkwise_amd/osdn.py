@@ -22,7 +22,8 @@ STATUS = {0: "OSDN_OK", -1: "OSDN_ERR_NULL", -2: "OSDN_ERR_SHAPE", -3: "OSDN_ERR
           -4: "OSDN_ERR_ALIGN", -5: "OSDN_ERR_ALIAS", -6: "OSDN_ERR_LAUNCH"}
 EXPORTS = ("osdn_chunk_fwd", "osdn_step", "osdn_precond_scan", "osdn_precond_step",
            "osdn_chunk_fwd_kda", "osdn_chunk_fwd_kda_workspace", "osdn_step_kda",
-           "osdn_chunk_bwd", "osdn_chunk_bwd_workspace", "osdn_status_string",
+           "osdn_chunk_bwd", "osdn_chunk_bwd_workspace", "osdn_chunk_states_bytes",
+           "osdn_chunk_fwd_states", "osdn_chunk_bwd_states", "osdn_status_string",
            "osdn_abi_version")
 
 
@@ -68,6 +69,14 @@ def lib() -> ctypes.CDLL:
     L.osdn_chunk_bwd.restype = ctypes.c_int
     L.osdn_chunk_bwd.argtypes = [vp] * 17 + [i64, i64, i64, i64, i32, i32, ctypes.c_int,
                                              ctypes.c_int, vp]
+    L.osdn_chunk_states_bytes.restype = i64
+    L.osdn_chunk_states_bytes.argtypes = [i64, i64, i64, i32, i32, ctypes.c_int]
+    L.osdn_chunk_fwd_states.restype = ctypes.c_int
+    L.osdn_chunk_fwd_states.argtypes = [vp] * 10 + [i64, i64, i64, i32, i32, ctypes.c_int,
+                                                    ctypes.c_int, vp]
+    L.osdn_chunk_bwd_states.restype = ctypes.c_int
+    L.osdn_chunk_bwd_states.argtypes = [vp] * 18 + [i64, i64, i64, i64, i32, i32, ctypes.c_int,
+                                                    ctypes.c_int, vp]
     L.osdn_status_string.restype = ctypes.c_char_p
     L.osdn_status_string.argtypes = [ctypes.c_int]
     L.osdn_abi_version.restype = ctypes.c_int32
@@ -150,6 +159,53 @@ def osdn_chunk_fwd(q, k, v, beta, d, alpha=None, S0=None, *, chunk: int = 64, o=
     if st != 0:
         raise OSDNError(st, "osdn_chunk_fwd")
     return o, S_T
+
+
+def states_bytes(B: int, H: int, T: int, dk: int, dv: int, dtype_code: int) -> int:
+    n = lib().osdn_chunk_states_bytes(B, H, T, dk, dv, dtype_code)
+    if n < 0:
+        raise ValueError("invalid sizes for osdn_chunk_fwd_states")
+    return n
+
+
+def osdn_chunk_fwd_states(q, k, v, beta, d, alpha=None, S0=None, *, o=None, S_T=None,
+                          states=None, want_state: bool = True, stream=None):
+    """osdn_chunk_fwd with the backward's chunk size (64 rows for bf16, 32 for fp32) that also
+    keeps the state at every chunk start for osdn_chunk_bwd(..., states=...).  Returns
+    (o, S_T, states): states [B,H,nchunks,dk,dv], bf16 for bf16 inputs, fp32 for fp32."""
+    torch = _torch()
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    chunk = 64 if q.dtype == torch.bfloat16 else 32
+    nch = (T + chunk - 1) // chunk
+    sdt = torch.bfloat16 if q.dtype == torch.bfloat16 else torch.float32
+    if states is None:
+        states = torch.empty((B, H, nch, dk, dv), dtype=sdt, device=q.device)
+    if tuple(states.shape) != (B, H, nch, dk, dv) or states.dtype != sdt:
+        raise ValueError(f"states must be {sdt} [B,H,{nch},dk,dv]")
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    if S_T is None and want_state:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    for name, t, shape in (("k", k, (B, H, T, dk)), ("v", v, (B, H, T, dv)),
+                           ("beta", beta, (B, H, T)), ("d", d, (B, H, T, dk)),
+                           ("o", o, (B, H, T, dv))):
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+    if alpha is not None and (tuple(alpha.shape) != (B, H, T) or alpha.dtype != torch.float32):
+        raise ValueError("alpha must be float32 [B,H,T]")
+    for name, t in (("S0", S0), ("S_T", S_T)):
+        if t is not None and (tuple(t.shape) != (B, H, dk, dv) or t.dtype != torch.float32):
+            raise ValueError(f"{name} must be float32 [B,H,dk,dv]")
+    if k.dtype != q.dtype or v.dtype != q.dtype or o.dtype != q.dtype:
+        raise TypeError("q, k, v and o must share one dtype")
+    st = lib().osdn_chunk_fwd_states(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(d),
+                                     _ptr(alpha), _ptr(S0), _ptr(o), _ptr(S_T), _ptr(states),
+                                     B, H, T, dk, dv, _dtype_code(q), _dtype_code(d),
+                                     _stream(stream, q.device))
+    if st != 0:
+        raise OSDNError(st, "osdn_chunk_fwd_states")
+    return o, S_T, states
 
 
 def osdn_step(q, k, v, beta, d, alpha, S, *, o=None, stream=None):
@@ -296,12 +352,13 @@ def bwd_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, dtype_code: in
 
 
 def osdn_chunk_bwd(q, k, v, beta, d, alpha, S0, grad_o, grad_S_T=None, *, grads=None,
-                   want_grad_S0: bool = True, workspace=None, stream=None):
+                   want_grad_S0: bool = True, workspace=None, states=None, stream=None):
     """Gradients of osdn_chunk_fwd(q, k, v, beta, d, alpha, S0) for output gradients grad_o
     [B,H,T,dv] (dtype of q) and grad_S_T [B,H,dk,dv] fp32 (None: zero).  Returns a dict with
     grad_q, grad_k, grad_v (dtype of q), grad_beta (fp32), grad_d (dtype of d), grad_alpha
     (fp32, None without alpha) and grad_S0 (fp32, None unless want_grad_S0).  ``grads`` may
-    supply some of those output tensors; the rest and the workspace are allocated with torch."""
+    supply some of those output tensors; the rest and the workspace are allocated with torch.
+    ``states`` (from osdn_chunk_fwd_states on the same inputs) spares the forward recompute."""
     torch = _torch()
     B, H, T, dk = q.shape
     dv = v.shape[-1]
@@ -335,13 +392,21 @@ def osdn_chunk_bwd(q, k, v, beta, d, alpha, S0, grad_o, grad_S_T=None, *, grads=
     need = bwd_workspace_bytes(B, H, T, dk, dv, _dtype_code(q))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    st = lib().osdn_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(d), _ptr(alpha),
-                              _ptr(S0), _ptr(grad_o), _ptr(grad_S_T), _ptr(g["grad_q"]),
-                              _ptr(g["grad_k"]), _ptr(g["grad_v"]), _ptr(g["grad_beta"]),
-                              _ptr(g["grad_d"]), _ptr(g["grad_alpha"]), _ptr(g["grad_S0"]),
-                              _ptr(workspace), workspace.numel() * workspace.element_size(),
-                              B, H, T, dk, dv, _dtype_code(q), _dtype_code(d),
-                              _stream(stream, q.device))
+    wsb = workspace.numel() * workspace.element_size()
+    tail = (B, H, T, dk, dv, _dtype_code(q), _dtype_code(d), _stream(stream, q.device))
+    grad_ptrs = (_ptr(g["grad_q"]), _ptr(g["grad_k"]), _ptr(g["grad_v"]), _ptr(g["grad_beta"]),
+                 _ptr(g["grad_d"]), _ptr(g["grad_alpha"]), _ptr(g["grad_S0"]))
+    ins = (_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(d), _ptr(alpha), _ptr(S0))
+    if states is None:
+        st = lib().osdn_chunk_bwd(*ins, _ptr(grad_o), _ptr(grad_S_T), *grad_ptrs,
+                                  _ptr(workspace), wsb, *tail)
+        name = "osdn_chunk_bwd"
+    else:
+        if states.numel() * states.element_size() < states_bytes(B, H, T, dk, dv, _dtype_code(q)):
+            raise ValueError("states is smaller than osdn_chunk_states_bytes")
+        st = lib().osdn_chunk_bwd_states(*ins, _ptr(states), _ptr(grad_o), _ptr(grad_S_T),
+                                         *grad_ptrs, _ptr(workspace), wsb, *tail)
+        name = "osdn_chunk_bwd_states"
     if st != 0:
-        raise OSDNError(st, "osdn_chunk_bwd")
+        raise OSDNError(st, name)
     return g

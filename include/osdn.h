@@ -224,6 +224,41 @@ osdn_status osdn_chunk_bwd(const void *q, const void *k, const void *v, const fl
                            int64_t workspace_bytes, int64_t B, int64_t H, int64_t T, int32_t dk,
                            int32_t dv, osdn_dtype qkv, osdn_dtype d_dtype, void *stream);
 
+/*
+ * The training pair: the forward that also keeps the state at every chunk start, and the
+ * backward that takes those states instead of recomputing them (the first of its launches).
+ *
+ * osdn_chunk_fwd_states: as osdn_chunk_fwd with the backward's chunk size (64 rows for bf16
+ * inputs, 32 for fp32), and in addition
+ *   states   [B,H,nchunks,dk,dv] out, bf16 for bf16 inputs (the precision the backward's
+ *            products take them in), fp32 for fp32 inputs; the state before chunk c's first
+ *            row in slot c; osdn_chunk_states_bytes(B, H, T, dk, dv, qkv) bytes, 16-byte
+ *            aligned, overlapping no other argument
+ * o and S_T are bitwise those of osdn_chunk_fwd with that chunk size.
+ *
+ * osdn_chunk_bwd_states: as osdn_chunk_bwd, with `states` (input) from osdn_chunk_fwd_states on
+ * the same inputs; it may not overlap an output or the workspace.  The gradients are bitwise
+ * those of osdn_chunk_bwd.  The workspace is osdn_chunk_bwd_workspace bytes as there.
+ */
+int64_t osdn_chunk_states_bytes(int64_t B, int64_t H, int64_t T, int32_t dk, int32_t dv,
+                                osdn_dtype qkv); /* -1 if invalid */
+
+osdn_status osdn_chunk_fwd_states(const void *q, const void *k, const void *v,
+                                  const float *beta, const void *d, const float *alpha,
+                                  const float *S0, void *o, float *S_T, void *states, int64_t B,
+                                  int64_t H, int64_t T, int32_t dk, int32_t dv, osdn_dtype qkv,
+                                  osdn_dtype d_dtype, void *stream);
+
+osdn_status osdn_chunk_bwd_states(const void *q, const void *k, const void *v,
+                                  const float *beta, const void *d, const float *alpha,
+                                  const float *S0, const void *states, const void *grad_o,
+                                  const float *grad_S_T, void *grad_q, void *grad_k,
+                                  void *grad_v, float *grad_beta, void *grad_d,
+                                  float *grad_alpha, float *grad_S0, void *workspace,
+                                  int64_t workspace_bytes, int64_t B, int64_t H, int64_t T,
+                                  int32_t dk, int32_t dv, osdn_dtype qkv, osdn_dtype d_dtype,
+                                  void *stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char *osdn_status_string(osdn_status s);
 

@@ -275,3 +275,60 @@ def test_bwd_workspace_size(L):
     need = L.osdn_chunk_bwd_workspace(2, 3, 100, 128, 64, osdn.OSDN_BF16)
     assert call_bwd(L, wsb=need - 1) == -2
     assert call_bwd(L, B=0) == 0
+
+
+def call_fwd_states(L, **over):
+    a = dict(q=addr(1), k=addr(2), v=addr(3), beta=addr(4), d=addr(5), alpha=addr(6),
+             S0=addr(7), o=addr(8), S_T=addr(9), states=addr(10), B=2, H=3, T=100, dk=128,
+             dv=64, qkv=osdn.OSDN_BF16, d_dtype=osdn.OSDN_F32, stream=None)
+    a.update(over)
+    return L.osdn_chunk_fwd_states(a["q"], a["k"], a["v"], a["beta"], a["d"], a["alpha"],
+                                   a["S0"], a["o"], a["S_T"], a["states"], a["B"], a["H"],
+                                   a["T"], a["dk"], a["dv"], a["qkv"], a["d_dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(states=None), -1), (dict(q=None), -1), (dict(T=-1), -2), (dict(dk=96), -3),
+    (dict(qkv=7), -3), (dict(states=addr(10) + 8), -4), (dict(states=addr(8) + 256), -5),
+    (dict(states=addr(1)), -5), (dict(o=addr(10) + 4096), -5),
+])
+def test_chunk_fwd_states_rejects(L, over, status):
+    assert call_fwd_states(L, **over) == status
+
+
+def test_states_size_and_empty_work(L):
+    # the state at every chunk start, [B,H,nchunks,dk,dv]: bf16 with 64-row chunks for bf16
+    # inputs, fp32 with 32-row chunks for fp32 inputs
+    assert L.osdn_chunk_states_bytes(2, 3, 100, 128, 64, osdn.OSDN_BF16) == 2 * 3 * 2 * 128 * 64 * 2
+    assert L.osdn_chunk_states_bytes(2, 3, 100, 128, 64, osdn.OSDN_F32) == 2 * 3 * 4 * 128 * 64 * 4
+    assert L.osdn_chunk_states_bytes(2, 3, 0, 128, 64, osdn.OSDN_BF16) == 0
+    assert L.osdn_chunk_states_bytes(2, 3, 100, 96, 64, osdn.OSDN_BF16) == -1
+    assert call_fwd_states(L, B=0) == 0
+    assert call_fwd_states(L, T=0, q=None, states=None, S_T=None) == 0
+
+
+def call_bwd_states(L, **over):
+    a = dict(q=addr(1), k=addr(2), v=addr(3), beta=addr(4), d=addr(5), alpha=addr(6),
+             S0=addr(7), states=addr(18), go=addr(8), gST=addr(9), gq=addr(10), gk=addr(11),
+             gv=addr(12), gb=addr(13), gd=addr(14), ga=addr(15), gS0=addr(16), ws=addr(17),
+             wsb=1 << 31, B=2, H=3, T=100, dk=128, dv=64, qkv=osdn.OSDN_BF16,
+             d_dtype=osdn.OSDN_F32, stream=None)
+    a.update(over)
+    return L.osdn_chunk_bwd_states(a["q"], a["k"], a["v"], a["beta"], a["d"], a["alpha"],
+                                   a["S0"], a["states"], a["go"], a["gST"], a["gq"], a["gk"],
+                                   a["gv"], a["gb"], a["gd"], a["ga"], a["gS0"], a["ws"],
+                                   a["wsb"], a["B"], a["H"], a["T"], a["dk"], a["dv"], a["qkv"],
+                                   a["d_dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(states=None), -1), (dict(gq=None), -1), (dict(wsb=1000), -2),
+    (dict(states=addr(18) + 8), -4), (dict(states=addr(10) + 512), -5),
+    (dict(states=addr(17)), -5), (dict(gS0=addr(18) + 4096), -5),
+])
+def test_chunk_bwd_states_rejects(L, over, status):
+    assert call_bwd_states(L, **over) == status
+
+
+def test_chunk_bwd_states_empty_work_is_ok(L):
+    assert call_bwd_states(L, B=0) == 0

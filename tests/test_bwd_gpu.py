@@ -149,3 +149,43 @@ def test_bwd_full_1p3b_sampled():
         errs = {n: rel_err(got[n][b:b + 1, h:h + 1], ref[n]) for n in NAMES}
         say(f"  seq ({b},{h}): " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
         assert all(e <= TOL["bf16"] for e in errs.values()), errs
+
+
+def _workspace_states(ws, B, H, T, dk, dv, qkv):
+    """The backward's own recomputed states: the first region of its workspace."""
+    torch, _ = torch_dev()
+    C = 64 if qkv == "bf16" else 32
+    nch = (T + C - 1) // C
+    n = B * H * nch * dk * dv
+    dt = torch.bfloat16 if qkv == "bf16" else torch.float32
+    return ws[: n * (2 if qkv == "bf16" else 4)].view(dt).view(B, H, nch, dk, dv)
+
+
+@pytest.mark.parametrize("case", [(1, 2, 130, 128, 128, "bf16"), (2, 1, 64, 64, 128, "bf16"),
+                                  (1, 1, 67, 64, 64, "f32"), (1, 2, 33, 128, 64, "f32")],
+                         ids=lambda c: "x".join(map(str, c)))
+def test_training_pair_matches_recompute_bitwise(case):
+    """osdn_chunk_fwd_states gives osdn_chunk_fwd's o and S_T (at the backward's chunk size)
+    and the backward's own checkpoints; osdn_chunk_bwd with those states gives the gradients
+    of the recomputing backward, bitwise."""
+    torch, dev = torch_dev()
+    B, H, T, dk, dv, qkv = case
+    say("training pair", case)
+    x, g = bwd_inputs(B, H, T, dk, dv, qkv, seed=T + dk)
+    args = (to_dev(x["q"], qkv), to_dev(x["k"], qkv), to_dev(x["v"], qkv), to_dev(x["beta"], "f32"),
+            to_dev(x["d"], "f32"), to_dev(x["alpha"], "f32"), to_dev(x["S0"], "f32"))
+    C = 64 if qkv == "bf16" else 32
+    o_ref, s_ref = osdn.osdn_chunk_fwd(*args, chunk=C)
+    o, s_t, states = osdn.osdn_chunk_fwd_states(*args)
+    go, gst = to_dev(g["do"], qkv), to_dev(g["dS_T"], "f32")
+    ws = torch.empty(osdn.bwd_workspace_bytes(B, H, T, dk, dv, osdn._dtype_code(args[0])),
+                     dtype=torch.uint8, device=dev)
+    ref = osdn.osdn_chunk_bwd(*args, go, gst, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(s_t, s_ref)
+    assert torch.equal(states, _workspace_states(ws, B, H, T, dk, dv, qkv))
+    got = osdn.osdn_chunk_bwd(*args, go, gst, states=states)
+    torch.cuda.synchronize()
+    for name, t in ref.items():
+        if t is not None:
+            assert torch.equal(got[name], t), name
