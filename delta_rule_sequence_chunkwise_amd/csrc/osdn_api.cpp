@@ -67,9 +67,13 @@ int32_t osdn_abi_version(void) { return OSDN_ABI_VERSION; }
 
 namespace {
 
+int64_t states_bytes(int64_t B, int64_t H, int64_t T, int32_t dk, int32_t dv, osdn_dtype qkv,
+                     int64_t *u_offset);
+
 // The chunkwise forward: validation, then the launch.  With want_states, `states` receives the
 // state at every chunk start ([B,H,nchunks,dk,dv]; bf16 for bf16 inputs, else fp32; the
-// chunk size is then the backward's).
+// chunk size is then the backward's) and, for bf16 inputs, the pseudo-values U of every row
+// after them.
 osdn_status chunk_fwd_impl(const void *q, const void *k, const void *v, const float *beta,
                            const void *d, const float *alpha, const float *S0, void *o,
                            float *S_T, void *states, bool want_states, int64_t B, int64_t H,
@@ -91,8 +95,11 @@ osdn_status chunk_fwd_impl(const void *q, const void *k, const void *v, const fl
     if (!mul_ok(st, int64_t(dk) * dv, kMaxElems)) return OSDN_ERR_SHAPE;
     if (BH > int64_t(0x7fffffff) / 4) return OSDN_ERR_SHAPE;  // grid: BH x (dv / 32) groups
 
-    int64_t nst = st;  // elements of the states at every chunk start
-    if (want_states && !mul_ok(nst, (T + chunk - 1) / chunk, kMaxElems)) return OSDN_ERR_SHAPE;
+    int64_t nsb = 0, uoff = 0;  // bytes of the states buffer; where U starts in it
+    if (want_states) {
+        nsb = states_bytes(B, H, T, dk, dv, qkv, &uoff);
+        if (nsb < 0) return OSDN_ERR_SHAPE;
+    }
 
     if (BH == 0) return OSDN_OK;
     if (T > 0 && (!q || !k || !v || !beta || !d || !o || (want_states && !states)))
@@ -119,12 +126,15 @@ osdn_status chunk_fwd_impl(const void *q, const void *k, const void *v, const fl
     for (const Range *in : {&rq, &rk, &rv, &rd, &rb, &ra})
         if (overlap(rst, *in)) return OSDN_ERR_ALIAS;
     if (overlap(rst, rs0) && (rst.lo != rs0.lo)) return OSDN_ERR_ALIAS;
-    const Range rsts = range_of(want_states ? states : nullptr, n_tok ? nst * eq : 0);
+    const Range rsts = range_of(want_states ? states : nullptr, n_tok ? nsb : 0);
     for (const Range *x : {&rq, &rk, &rv, &rd, &rb, &ra, &rs0, &rst, &ro})
         if (overlap(rsts, *x)) return OSDN_ERR_ALIAS;
 
     osdn::ChunkArgs a{q, k, v, d, beta, alpha, S0, o, S_T, BH, T, dk, dv, chunk, qkv, d_dtype};
-    if (want_states && T > 0) a.ckpt = states;
+    if (want_states && T > 0) {
+        a.ckpt = states;
+        if (qkv == OSDN_BF16) a.uout = static_cast<char *>(states) + uoff;
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     const hipError_t err = qkv == OSDN_BF16 ? osdn::launch_chunk_fwd_mfma(a, s)
                                             : osdn::launch_chunk_fwd_f32math(a, s);
@@ -414,6 +424,17 @@ int64_t bwd_ckpt_bytes(int64_t B, int64_t H, int64_t T, int32_t dk, int32_t dv, 
     return round256(n * (qkv == OSDN_BF16 ? 2 : 4));
 }
 
+// bytes of each per-row buffer of the backward (bf16 inputs: U and dR, [BH, T, dv] bf16; fp32
+// inputs: none); called after bwd_ckpt_bytes has accepted the sizes
+int64_t bwd_rows_bytes(int64_t B, int64_t H, int64_t T, int32_t dv, osdn_dtype qkv) {
+    if (qkv != OSDN_BF16) return 0;
+    int64_t n = 2;
+    if (!mul_ok(n, B, kMaxElems) || !mul_ok(n, H, kMaxElems) || !mul_ok(n, T, kMaxElems) ||
+        !mul_ok(n, dv, kMaxElems))
+        return -1;
+    return round256(n);
+}
+
 // bytes of the per-chunk planes of the backward (bf16 inputs, per chunk: three bf16 64 x 64
 // planes, the inverse's hi and lo and the scores, and K~ as 64 x dk bf16; fp32 inputs: none);
 // called after bwd_ckpt_bytes has accepted the sizes
@@ -427,6 +448,18 @@ int64_t bwd_tinv_bytes(int64_t B, int64_t H, int64_t T, int32_t dk, osdn_dtype q
     return round256(n * 2);
 }
 
+// bytes of the training pair's states buffer: the checkpoints, then (bf16 inputs) U of every
+// row from 256 bytes-aligned *u_offset on; -1 if the sizes are invalid
+int64_t states_bytes(int64_t B, int64_t H, int64_t T, int32_t dk, int32_t dv, osdn_dtype qkv,
+                     int64_t *u_offset) {
+    const int64_t ck = bwd_ckpt_bytes(B, H, T, dk, dv, qkv);
+    if (ck < 0) return -1;
+    const int64_t ub = bwd_rows_bytes(B, H, T, dv, qkv);
+    if (ub < 0) return -1;
+    *u_offset = ck;
+    return ck + ub;
+}
+
 }  // namespace
 
 extern "C" {
@@ -436,7 +469,9 @@ int64_t osdn_chunk_bwd_workspace(int64_t B, int64_t H, int64_t T, int32_t dk, in
     const int64_t b = bwd_ckpt_bytes(B, H, T, dk, dv, qkv);
     if (b < 0) return -1;
     const int64_t t = bwd_tinv_bytes(B, H, T, dk, qkv);
-    return t < 0 ? -1 : 2 * b + t;
+    if (t < 0) return -1;
+    const int64_t u = bwd_rows_bytes(B, H, T, dv, qkv);
+    return u < 0 ? -1 : 2 * b + t + 2 * u;
 }
 
 }  // extern "C"
@@ -460,7 +495,9 @@ osdn_status chunk_bwd_impl(const void *q, const void *k, const void *v, const fl
     if (ck < 0) return OSDN_ERR_SHAPE;
     const int64_t tk = bwd_tinv_bytes(B, H, T, dk, qkv);
     if (tk < 0) return OSDN_ERR_SHAPE;
-    const int64_t wsb = 2 * ck + tk;
+    const int64_t ub = bwd_rows_bytes(B, H, T, dv, qkv);
+    if (ub < 0) return OSDN_ERR_SHAPE;
+    const int64_t wsb = 2 * ck + tk + 2 * ub;
     int64_t BH = 1;
     if (!mul_ok(BH, B, kMaxElems) || !mul_ok(BH, H, kMaxElems)) return OSDN_ERR_SHAPE;
     int64_t tok = BH, st = BH;
@@ -500,9 +537,12 @@ osdn_status chunk_bwd_impl(const void *q, const void *k, const void *v, const fl
     const Range rb = range_of(beta, nt * 4), ra = range_of(alpha, alpha ? nt * 4 : 0);
     const Range rs0 = range_of(S0, st * 4), rgo = range_of(grad_o, nt ? nv * eq : 0);
     const Range rgst = range_of(grad_S_T, st * 4);
-    int64_t nst = st;  // elements of the states at every chunk start
-    if (!mul_ok(nst, nch, kMaxElems)) return OSDN_ERR_SHAPE;
-    const Range rsts = range_of(states_given ? states : nullptr, nt ? nst * eq : 0);
+    int64_t nsb = 0, uoff = 0;  // bytes of the forward's states buffer; where U starts in it
+    if (states_given) {
+        nsb = states_bytes(B, H, T, dk, dv, qkv, &uoff);
+        if (nsb < 0) return OSDN_ERR_SHAPE;
+    }
+    const Range rsts = range_of(states_given ? states : nullptr, nt ? nsb : 0);
     const Range gq = range_of(grad_q, nt ? nqk * eq : 0), gk = range_of(grad_k, nt ? nqk * eq : 0);
     const Range gv = range_of(grad_v, nt ? nv * eq : 0), gd = range_of(grad_d, nt ? nqk * ed : 0);
     const Range gb = range_of(grad_beta, nt * 4), ga = range_of(grad_alpha, grad_alpha ? nt * 4 : 0);
@@ -522,8 +562,14 @@ osdn_status chunk_bwd_impl(const void *q, const void *k, const void *v, const fl
                     grad_beta, grad_alpha, grad_d, grad_S0,
                     T > 0 ? (states_given ? const_cast<void *>(states) : ws) : nullptr,
                     T > 0 ? ws + ck : nullptr, states_given,
-                    T > 0 && tk > 0 ? reinterpret_cast<uint16_t *>(ws + 2 * ck) : nullptr, BH, T,
-                    dk, dv, qkv, d_dtype};
+                    T > 0 && tk > 0 ? reinterpret_cast<uint16_t *>(ws + 2 * ck) : nullptr,
+                    T > 0 && ub > 0
+                        ? reinterpret_cast<uint16_t *>(
+                              states_given ? static_cast<char *>(const_cast<void *>(states)) + uoff
+                                           : ws + 2 * ck + tk)
+                        : nullptr,
+                    T > 0 && ub > 0 ? reinterpret_cast<uint16_t *>(ws + 2 * ck + tk + ub) : nullptr,
+                    BH, T, dk, dv, qkv, d_dtype};
     const hipError_t err = osdn::launch_chunk_bwd(a, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? OSDN_OK : OSDN_ERR_LAUNCH;
 }
@@ -546,14 +592,8 @@ osdn_status osdn_chunk_bwd(const void *q, const void *k, const void *v, const fl
 
 int64_t osdn_chunk_states_bytes(int64_t B, int64_t H, int64_t T, int32_t dk, int32_t dv,
                                 osdn_dtype qkv) {
-    if (B < 0 || H < 0 || T < 0 || !dtype_ok(qkv) || !head_dim_ok(dk) || !head_dim_ok(dv))
-        return -1;
-    const int64_t C = osdn::bwd_chunk_size(qkv);
-    int64_t n = elem_size(qkv);
-    if (!mul_ok(n, B, kMaxElems) || !mul_ok(n, H, kMaxElems) ||
-        !mul_ok(n, (T + C - 1) / C, kMaxElems) || !mul_ok(n, int64_t(dk) * dv, kMaxElems))
-        return -1;
-    return n;
+    int64_t uoff = 0;
+    return states_bytes(B, H, T, dk, dv, qkv, &uoff);
 }
 
 osdn_status osdn_chunk_fwd_states(const void *q, const void *k, const void *v,

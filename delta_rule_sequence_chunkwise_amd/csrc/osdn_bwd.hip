@@ -141,10 +141,9 @@ __device__ __forceinline__ void solve_upper(float *X, const float *AS, const flo
 // g = running sum of ln(alpha) over the chunk's rows (0 past the end), gam = e^g,
 // w = e^{g_last - g}; beta (0 past the end).  Wave 0 only.
 template <int C>
-__device__ __forceinline__ void decay_scan(const float *beta, const float *alpha, int64_t row0,
-                                           int n, float *sb, float *sg, float *sgam, float *sw,
-                                           int lane) {
-    float x = (lane < n && alpha) ? logf(alpha[row0 + lane]) : 0.f;
+__device__ __forceinline__ void decay_scan_of(float bv, float av, bool has_alpha, int n, float *sb,
+                                              float *sg, float *sgam, float *sw, int lane) {
+    float x = (lane < n && has_alpha) ? logf(av) : 0.f;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
         const float y = __shfl_up(x, off);
@@ -152,11 +151,20 @@ __device__ __forceinline__ void decay_scan(const float *beta, const float *alpha
     }
     const float gl = __shfl(x, C - 1);
     if (lane < C) {
-        sb[lane] = lane < n ? beta[row0 + lane] : 0.f;
+        sb[lane] = lane < n ? bv : 0.f;
         sg[lane] = x;
         sgam[lane] = __expf(x);
         sw[lane] = __expf(gl - x);
     }
+}
+// the same with the chunk's beta, alpha loaded here (rows past the end repeat the last one)
+template <int C>
+__device__ __forceinline__ void decay_scan(const float *beta, const float *alpha, int64_t row0,
+                                           int n, float *sb, float *sg, float *sgam, float *sw,
+                                           int lane) {
+    const int r = lane < n ? lane : n - 1;
+    decay_scan_of<C>(beta[row0 + r], alpha ? alpha[row0 + r] : 1.f, alpha != nullptr, n, sb, sg,
+                     sgam, sw, lane);
 }
 
 // eight consecutive values of d as fp32 (32 bytes of fp32 or 16 bytes of bf16)
@@ -651,7 +659,8 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
                       const float *__restrict__ beta, const float *__restrict__ alpha,
                       const bf16_t *__restrict__ dO, const uint16_t *__restrict__ Mck,
                       const uint16_t *__restrict__ dMck, const uint16_t *__restrict__ Tck,
-                      bf16_t *__restrict__ gq, bf16_t *__restrict__ gk, bf16_t *__restrict__ gv,
+                      const uint16_t *__restrict__ Uck, const uint16_t *__restrict__ dRck,
+                      bf16_t *__restrict__ gq, bf16_t *__restrict__ gk,
                       float *__restrict__ gbeta, TD *__restrict__ gd,
                       float *__restrict__ galpha, int64_t T, int64_t nch) {
     constexpr int C = 64, BV = 32, NW = 8, NTH = NW * 64;
@@ -660,14 +669,11 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
     constexpr int MB = 2 * DK * PVH > C * PCH ? 2 * DK * PVH : C * PCH;
     constexpr int MU = DK * BV / 4 / NTH;      // 4-value units of an M0 (dMC) slice per thread
     static_assert(MU == 1 || MU == 2, "one or two M units per thread");
-    static_assert(C * BV / 4 == NTH, "one 4-value unit of v and dO per thread");
+    static_assert(C * BV / 4 == NTH, "one 4-value unit of v, dO, U, dR per thread");
     __shared__ alignas(16) uint16_t sQ[C * PH], sK[C * PH], sKt[C * PH];
-    __shared__ alignas(16) uint16_t sPb[C * PCH];  // P, later dP o G (bf16)
-    __shared__ alignas(16) uint16_t sTh[C * PCH], sTl[C * PCH];  // T = (I + A)^{-1}: hi, lo
+    __shared__ alignas(16) uint16_t sPb[C * PCH];  // dP o G (bf16) for the closing products
     __shared__ alignas(16) uint16_t sMb[MB];       // M0 and dMC slices, later Gb (bf16)
-    __shared__ alignas(16) uint16_t sDOb[C * PVH], sUb[C * PVH], sDRb[C * PVH];
-    __shared__ alignas(16) uint16_t sRh[C * PVH], sRl[C * PVH];  // V, then R (hi, lo)
-    __shared__ alignas(16) uint16_t sdUh[C * PVH], sdUl[C * PVH];
+    __shared__ alignas(16) uint16_t sDOb[C * PVH], sUb[C * PVH], sDRb[C * PVH], sVb[C * PVH];
     __shared__ float sb[C], sg[C], sgam[C], sw[C];
     __shared__ float srow[2][6][C];  // per-half row sums of the dg and dbeta terms
     __shared__ float scol[4][C];     // column sums of the decay term, by row block
@@ -686,46 +692,35 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
     const uint16_t *dMC = dMck + (bh * nch + c) * DK * DV;
     // the chunk's rows of every per-token array: uniform bases, 32-bit offsets
     const bf16_t *vc = v + row0 * DV, *oc = dO + row0 * DV;
-    bf16_t *gvc = gv + row0 * DV, *gqc = gq + row0 * DK, *gkc = gk + row0 * DK;
+    const uint16_t *uc = Uck + row0 * DV, *rc = dRck + row0 * DV;
+    bf16_t *gqc = gq + row0 * DK, *gkc = gk + row0 * DK;
     TD *gdc = gd + row0 * DK;
     const TD *dc = d + row0 * DK;
 
-    {  // Q, K (bf16, 8 features per 16-byte unit), K~ and the T, P planes, all loads issued
-       // first
-        constexpr int G = DK / 8, NU = C * G / NTH;  // units per row, units per thread
-        constexpr int TU = 3 * C * C / 8 / NTH;      // 16-byte units of the T, P planes per thread
-        static_assert(NU * NTH == C * G && TU == 3, "whole units");
-        uint4 qu[NU], ku[NU], kt[NU], tu[TU];
+    // every load of the prologue is issued before the first wait: beta, alpha (every wave, for
+    // the scan of wave 0), Q, K, K~ (bf16, 8 features per 16-byte unit; K~ from its plane), the
+    // first two value slices (below)
+    const float pbv = beta[row0 + (lane < n ? lane : n - 1)];
+    const float pav = (alpha ? alpha : beta)[row0 + (lane < n ? lane : n - 1)];  // unused without alpha
+    __builtin_amdgcn_sched_barrier(0);  // the loads leave in this order (waits count them so)
+    constexpr int G = DK / 8, NU = C * G / NTH;  // units per row, units per thread
+    static_assert(NU * NTH == C * G, "whole units");
+    uint4 qu[NU], ku[NU], kt[NU];
+    {
         const uint16_t *pc = Tck + (bh * nch + c) * (3 * C * C + C * DK);
+#pragma unroll
+        for (int i = 0; i < NU; ++i) {
+            const int u = tid + i * NTH, r = u / G, g = u % G;
+            kt[i] = *reinterpret_cast<const uint4 *>(pc + 3 * C * C + r * DK + 8 * g);
+        }
 #pragma unroll
         for (int i = 0; i < NU; ++i) {
             const int u = tid + i * NTH, r = u / G, g = u % G;
             const int64_t e = (row0 + (r < n ? r : n - 1)) * DK + 8 * g;
             qu[i] = *reinterpret_cast<const uint4 *>(q + e);
             ku[i] = *reinterpret_cast<const uint4 *>(k + e);
-            kt[i] = *reinterpret_cast<const uint4 *>(pc + 3 * C * C + r * DK + 8 * g);
-        }
-        const uint4 *tp = reinterpret_cast<const uint4 *>(pc);
-#pragma unroll
-        for (int i = 0; i < TU; ++i) tu[i] = tp[tid + i * NTH];
-#pragma unroll
-        for (int i = 0; i < TU; ++i) {  // unit u: plane u / 512, row (u / 8) % 64, columns 8 (u % 8) ..
-            const int u = tid + i * NTH, r = (u >> 3) & 63, g = u & 7;
-            *reinterpret_cast<uint4 *>(&(i == 0 ? sTh : i == 1 ? sTl : sPb)[r * PCH + 8 * g]) = tu[i];
-        }
-#pragma unroll
-        for (int i = 0; i < NU; ++i) {
-            const int u = tid + i * NTH, r = u / G, g = u % G;
-            const uint32_t m = r < n ? 0xffffffffu : 0u;  // rows past the end are zero
-            *reinterpret_cast<uint4 *>(&sQ[r * PH + 8 * g]) =
-                make_uint4(qu[i].x & m, qu[i].y & m, qu[i].z & m, qu[i].w & m);
-            *reinterpret_cast<uint4 *>(&sK[r * PH + 8 * g]) =
-                make_uint4(ku[i].x & m, ku[i].y & m, ku[i].z & m, ku[i].w & m);
-            *reinterpret_cast<uint4 *>(&sKt[r * PH + 8 * g]) = kt[i];
         }
     }
-    if (tid < 64) decay_scan<C>(beta, alpha, row0, n, sb, sg, sgam, sw, lane);
-    __syncthreads();
     // score tile t of this wave's rows: AS = strictly lower (K K~^T) o G and P =
     // lower-inclusive (Q K~^T) o G in the C layout (zero for tiles above the diagonal)
     auto score_tiles = [&](int t, v4f &ak, v4f &aq) __attribute__((always_inline)) {
@@ -752,128 +747,109 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
 #pragma unroll
     for (int t = 0; t < NFH; ++t) aQ[t] = aK[t] = aKt[t] = zero4();
     adP[0] = adP[1] = adA[0] = adA[1] = zero4();
-    // per-lane partial row sums over the value columns (rows R0 + 4 lq + e), fp32:
-    // <dR_r, (K M0)_r>, <(K~ dMC)_r, U_r>, <dR_r, Y_r>; <dO_r, (Q M0)_r> comes from the dQ
-    // partial at the end
-    float pgr[4] = {0.f, 0.f, 0.f, 0.f}, pew[4] = {0.f, 0.f, 0.f, 0.f}, pdb[4] = {0.f, 0.f, 0.f, 0.f};
+    float pdb[4] = {0.f, 0.f, 0.f, 0.f};  // <dR_r, V_r> over the value columns, per lane
     float frob = 0.f;
 
-    // the value slice's M0, dMC, v and dO (bf16, four per 8-byte unit) pass through named
-    // registers one slice ahead (an array carried across the loop would live in scratch)
-    uint2 m0a = make_uint2(0, 0), m0b = m0a, dma = m0a, dmb = m0a, vu = m0a, ou = m0a;
-#define OSDN_BWD_LOAD_SLICE(S0)                                                               \
-    do {                                                                                      \
-        {                                                                                     \
-            const int f = tid / (BV / 4), j = 4 * (tid % (BV / 4));                          \
-            m0a = *reinterpret_cast<const uint2 *>(M0 + f * DV + (S0) + j);                   \
-            dma = *reinterpret_cast<const uint2 *>(dMC + f * DV + (S0) + j);                  \
-        }                                                                                     \
-        if constexpr (MU == 2) {                                                              \
-            const int u = tid + NTH, f = u / (BV / 4), j = 4 * (u % (BV / 4));               \
-            m0b = *reinterpret_cast<const uint2 *>(M0 + f * DV + (S0) + j);                   \
-            dmb = *reinterpret_cast<const uint2 *>(dMC + f * DV + (S0) + j);                  \
-        }                                                                                     \
-        {                                                                                     \
-            const int r = tid / (BV / 4), j = 4 * (tid % (BV / 4));                          \
-            const int e = (r < n ? r : n - 1) * DV + (S0) + j;                                \
-            vu = *reinterpret_cast<const uint2 *>(vc + e);                                    \
-            ou = *reinterpret_cast<const uint2 *>(oc + e);                                    \
-        }                                                                                     \
-    } while (0)
-    OSDN_BWD_LOAD_SLICE(0);
+    // the value slices' M0, dMC, v, dO, U and dR (bf16, four per 8-byte unit) pass through
+    // named registers two slices ahead (two register sets; the slice loop is unrolled)
+    struct SliceRegs {
+        uint2 m0a, m0b, dma, dmb, vu, ou, uu, ru;
+    };
+    SliceRegs ra{}, rb{};
+    auto load_slice = [&](SliceRegs &x, int S0) __attribute__((always_inline)) {
+        {
+            const int f = tid / (BV / 4), j = 4 * (tid % (BV / 4));
+            x.m0a = *reinterpret_cast<const uint2 *>(M0 + f * DV + S0 + j);
+            x.dma = *reinterpret_cast<const uint2 *>(dMC + f * DV + S0 + j);
+        }
+        if constexpr (MU == 2) {
+            const int u = tid + NTH, f = u / (BV / 4), j = 4 * (u % (BV / 4));
+            x.m0b = *reinterpret_cast<const uint2 *>(M0 + f * DV + S0 + j);
+            x.dmb = *reinterpret_cast<const uint2 *>(dMC + f * DV + S0 + j);
+        }
+        const int r = tid / (BV / 4), j = 4 * (tid % (BV / 4));
+        const int e = (r < n ? r : n - 1) * DV + S0 + j;
+        x.vu = *reinterpret_cast<const uint2 *>(vc + e);
+        x.ou = *reinterpret_cast<const uint2 *>(oc + e);
+        x.uu = *reinterpret_cast<const uint2 *>(uc + e);
+        x.ru = *reinterpret_cast<const uint2 *>(rc + e);
+    };
+    constexpr int NS = DV / BV;  // value slices
+    __builtin_amdgcn_sched_barrier(0);
+    load_slice(ra, 0);
+    if constexpr (NS > 1) load_slice(rb, BV);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+        const int u = tid + i * NTH, r = u / G, g = u % G;
+        const uint32_t m = r < n ? 0xffffffffu : 0u;  // rows past the end are zero
+        *reinterpret_cast<uint4 *>(&sQ[r * PH + 8 * g]) =
+            make_uint4(qu[i].x & m, qu[i].y & m, qu[i].z & m, qu[i].w & m);
+        *reinterpret_cast<uint4 *>(&sK[r * PH + 8 * g]) =
+            make_uint4(ku[i].x & m, ku[i].y & m, ku[i].z & m, ku[i].w & m);
+        *reinterpret_cast<uint4 *>(&sKt[r * PH + 8 * g]) = kt[i];
+    }
+    {  // the decay scan: every wave computes it and writes the same values (no branch for
+       // its loads to sink into: they stay first)
+        float x = (lane < n && alpha) ? logf(pav) : 0.f;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_up(x, off);
+            if (lane >= off) x += y;
+        }
+        const float gl = __shfl(x, C - 1);
+        sb[lane] = lane < n ? pbv : 0.f;
+        sg[lane] = x;
+        sgam[lane] = __expf(x);
+        sw[lane] = __expf(gl - x);
+    }
+    // d of this thread's output elements, loaded during the last slice (see below)
+    const int ro = R0 + 4 * lq + (lr & 3), fo = 4 * (lr >> 2);
+    float dfin[NFH][4];
 
-#pragma unroll 1
-    for (int s0 = 0; s0 < DV; s0 += BV) {
-        __syncthreads();  // the previous slice (and the scores) are done
+    static_for<0, NS>([&](auto S) __attribute__((always_inline)) {
+        constexpr int s0 = S * BV;
+        SliceRegs &x = (S & 1) ? rb : ra;
+        __syncthreads();  // the previous slice (and the prologue) are done
 #pragma unroll
         for (int i = 0; i < MU; ++i) {
             const int u = tid + i * NTH, f = u / (BV / 4), j = 4 * (u % (BV / 4));
-            const uint2 mm = i == 0 ? m0a : m0b, dd = i == 0 ? dma : dmb;
+            const uint2 mm = i == 0 ? x.m0a : x.m0b, dd = i == 0 ? x.dma : x.dmb;
             *reinterpret_cast<uint2 *>(&sM0b[f * PVH + j]) = mm;
             *reinterpret_cast<uint2 *>(&sdMb[f * PVH + j]) = dd;
             frob += bf_lo(mm.x) * bf_lo(dd.x) + bf_hi(mm.x) * bf_hi(dd.x) +
                     bf_lo(mm.y) * bf_lo(dd.y) + bf_hi(mm.y) * bf_hi(dd.y);
         }
-        {  // v into sRh (R replaces it in place) and dO; rows past the end are zero
+        {  // v, dO, U, dR; rows past the end are zero
             const int r = tid / (BV / 4), j = 4 * (tid % (BV / 4));
             const uint32_t m = r < n ? 0xffffffffu : 0u;
-            *reinterpret_cast<uint2 *>(&sRh[r * PVH + j]) = make_uint2(vu.x & m, vu.y & m);
-            *reinterpret_cast<uint2 *>(&sDOb[r * PVH + j]) = make_uint2(ou.x & m, ou.y & m);
+            *reinterpret_cast<uint2 *>(&sVb[r * PVH + j]) = make_uint2(x.vu.x & m, x.vu.y & m);
+            *reinterpret_cast<uint2 *>(&sDOb[r * PVH + j]) = make_uint2(x.ou.x & m, x.ou.y & m);
+            *reinterpret_cast<uint2 *>(&sUb[r * PVH + j]) = make_uint2(x.uu.x & m, x.uu.y & m);
+            *reinterpret_cast<uint2 *>(&sDRb[r * PVH + j]) = make_uint2(x.ru.x & m, x.ru.y & m);
         }
-        if (s0 + BV < DV) OSDN_BWD_LOAD_SLICE(s0 + BV);  // in flight through this slice's work
-        __syncthreads();
-        // K M0, K~ dMC on this wave's tile; Y = V - gam K M0 (registers), R = b Y into LDS as
-        // hi/lo bf16 over V; dU = P^T dO + diag(w) K~ dMC (the same tile: no other wave's part
-        // is needed) as hi/lo bf16
-        v4f km = zero4(), kdm = zero4(), y, du = zero4();
-#pragma unroll 2
-        for (int k0 = 0; k0 < DK; k0 += 32) {
-            const v8s m0f = frag_cols(sM0b, PVH, k0, jt, lr, lq);
-            km = mfma32(frag_rows(sK, PH, R0, k0, lr, lq), m0f, km);
-            kdm = mfma32(frag_rows(sKt, PH, R0, k0, lr, lq), frag_cols(sdMb, PVH, k0, jt, lr, lq), kdm);
-        }
+        if constexpr (S + 2 < NS) load_slice(x, s0 + 2 * BV);  // in flight through two slices
+        if constexpr (S + 1 == NS) {
+            // d where this thread's outputs go (after a quad transpose lane (lq, lr) holds row
+            // R0 + 4 lq + lr % 4, features 16 tile + 4 (lr / 4) .. +3), ahead of the products
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = R0 + 4 * lq + e, j = jt + lr;
-            y[e] = __uint_as_float(uint32_t(sRh[r * PVH + j]) << 16) - sgam[r] * km[e];
-            const float x = sb[r] * y[e];
-            const uint16_t h = bf16_bits(x);
-            sRh[r * PVH + j] = h;
-            sRl[r * PVH + j] = bf16_bits(x - __uint_as_float(uint32_t(h) << 16));
-        }
-#pragma unroll
-        for (int k0 = 0; k0 < C; k0 += 32)
-            du = mfma32(frag_cols(sPb, PCH, k0, R0, lr, lq), frag_cols(sDOb, PVH, k0, jt, lr, lq), du);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = R0 + 4 * lq + e, j = jt + lr;
-            const float x = du[e] + sw[r] * kdm[e];
-            const uint16_t h = bf16_bits(x);
-            sdUh[r * PVH + j] = h;
-            sdUl[r * PVH + j] = bf16_bits(x - __uint_as_float(uint32_t(h) << 16));
+            for (int t = 0; t < NFH; ++t) {
+                const int off = (ro < n ? ro : n - 1) * DK + 16 * (NFH * hw + t) + fo;
+                if constexpr (sizeof(TD) == 4) {
+                    const float4 y = *reinterpret_cast<const float4 *>(dc + off);
+                    dfin[t][0] = y.x; dfin[t][1] = y.y; dfin[t][2] = y.z; dfin[t][3] = y.w;
+                } else {
+                    const uint2 y = *reinterpret_cast<const uint2 *>(dc + off);
+                    dfin[t][0] = bf_lo(y.x); dfin[t][1] = bf_hi(y.x);
+                    dfin[t][2] = bf_lo(y.y); dfin[t][3] = bf_hi(y.y);
+                }
+            }
         }
         __syncthreads();
-        // U = T R (T lower triangular) and dR = T^T dU (T^T upper triangular), two independent
-        // chains; dV = diag(b) dR
-        v4f u = zero4(), dr = zero4();
-#pragma unroll
-        for (int k0 = 0; k0 < C; k0 += 32) {
-            if (k0 > R0 + 15) continue;
-            const v8s th = frag_rows(sTh, PCH, R0, k0, lr, lq), tl = frag_rows(sTl, PCH, R0, k0, lr, lq);
-            const v8s rh = frag_cols(sRh, PVH, k0, jt, lr, lq), rl = frag_cols(sRl, PVH, k0, jt, lr, lq);
-            u = mfma32(th, rh, u);
-            u = mfma32(th, rl, u);
-            u = mfma32(tl, rh, u);
-        }
-#pragma unroll
-        for (int k0 = 0; k0 < C; k0 += 32) {
-            if (k0 + 32 <= R0) continue;
-            const v8s th = frag_cols(sTh, PCH, k0, R0, lr, lq), tl = frag_cols(sTl, PCH, k0, R0, lr, lq);
-            const v8s uh = frag_cols(sdUh, PVH, k0, jt, lr, lq), ul = frag_cols(sdUl, PVH, k0, jt, lr, lq);
-            dr = mfma32(th, uh, dr);
-            dr = mfma32(th, ul, dr);
-            dr = mfma32(tl, uh, dr);
-        }
-        v4f gvt;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = R0 + 4 * lq + e, j = jt + lr;
-            sUb[r * PVH + j] = bf16_bits(u[e]);
-            pew[e] += kdm[e] * u[e];
-            sDRb[r * PVH + j] = bf16_bits(dr[e]);
-            pgr[e] += dr[e] * km[e];
-            pdb[e] += dr[e] * y[e];
-            gvt[e] = sb[r] * dr[e];
-        }
-        gvt = quad_transpose(gvt, lane);  // row R0 + 4 lq + lr % 4, columns jt + 4 (lr / 4) ..
-        {
-            const int r = R0 + 4 * lq + (lr & 3);
-            if (r < n) store4(gvc + r * DV + s0 + jt + 4 * (lr >> 2), gvt);
-        }
-        __syncthreads();
-        // dP += dO U^T, dA += dR U^T (negated later) on this wave's score tiles, and the
-        // slice's part of dO M0^T, dR M0^T, U dMC^T on this wave's feature tiles (K = the
-        // slice's 32 columns; the row factors gam, -gam b, w of dQ, dK, dK~ come at the end)
+        // dP += dO U^T, dA += dR U^T (negated later) on this wave's score tiles; the slice's
+        // part of dO M0^T, dR M0^T, U dMC^T on this wave's feature tiles (K = the slice's 32
+        // columns; the row factors gam, -gam b, w of dQ, dK, dK~ come at the end); <dR, V> on
+        // this wave's tile
         static_for<0, 2>([&](auto I) __attribute__((always_inline)) {
             const int t = 2 * I + hw;
             if (t <= rw) {
@@ -892,8 +868,13 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             aK[t] = mfma32(drb, m0r, aK[t]);
             aKt[t] = mfma32(urb, frag_rows(sdMb, PVH, f0, 0, lr, lq), aKt[t]);
         }
-    }
-#undef OSDN_BWD_LOAD_SLICE
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = R0 + 4 * lq + e, j = jt + lr;
+            pdb[e] += __uint_as_float(uint32_t(sDRb[r * PVH + j]) << 16) *
+                      __uint_as_float(uint32_t(sVb[r * PVH + j]) << 16);
+        }
+    });
     {  // <dMC, M0> over the workgroup (fixed order); ends with a barrier: the slices are done
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) frob += __shfl_xor(frob, m);
@@ -928,24 +909,31 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
         colp = sum_rows(colp);
         if (lq == 0) scol[rw][16 * t + lr] = colp;
     });
-    // the slices' parts of dQ, dK, dK~ take their row factors: gam dO M0^T, -gam b dR M0^T,
-    // diag(w) U dMC^T; the first gives <Q_r, (gam dO M0^T)_r> = gam_r <dO_r, (Q M0)_r> (this
-    // wave's feature tiles; the other half's come through LDS)
-    float pgo[4] = {0.f, 0.f, 0.f, 0.f};
+    // The slices' parts of dQ, dK, dK~ (dO M0^T, dR M0^T, U dMC^T) give the other row sums:
+    //   <Q_r, (dO M0^T)_r> = <dO_r, (Q M0)_r>,  <K_r, (dR M0^T)_r> = <dR_r, (K M0)_r>,
+    //   <K~_r, (U dMC^T)_r> = <U_r, (K~ dMC)_r>
+    // (this wave's feature tiles; the other half's come through LDS); then they take their row
+    // factors gam, -gam b, w for the closing products
+    float pgo[4] = {0.f, 0.f, 0.f, 0.f}, pgr[4] = {0.f, 0.f, 0.f, 0.f}, pew[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int r = R0 + 4 * lq + e;
         const float fq = sgam[r], fk = -sgam[r] * sb[r], fw = sw[r];
-        pgr[e] *= fk;
-        pew[e] *= fw;
 #pragma unroll
         for (int t = 0; t < NFH; ++t) {
             const int f = 16 * (NFH * hw + t) + lr;
+            pgo[e] += __uint_as_float(uint32_t(sQ[r * PH + f]) << 16) * aQ[t][e];
+            pgr[e] += __uint_as_float(uint32_t(sK[r * PH + f]) << 16) * aK[t][e];
+            pew[e] += __uint_as_float(uint32_t(sKt[r * PH + f]) << 16) * aKt[t][e];
             aQ[t][e] *= fq;
             aK[t][e] *= fk;
             aKt[t][e] *= fw;
-            pgo[e] += __uint_as_float(uint32_t(sQ[r * PH + f]) << 16) * aQ[t][e];
         }
+        // dbeta: <dR_r, Y_r> with Y = V - gam K M0;  dg: gam go - gam b gr - w ew
+        pdb[e] -= sgam[r] * pgr[e];
+        pgo[e] *= fq;
+        pgr[e] *= fk;
+        pew[e] *= fw;
     }
     // row sums: across the 16 lanes of a row (total in its last lane), then (below) across the
     // two halves
@@ -982,25 +970,6 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             sGb[i * PCH + j] = bf16_bits(adA[I][e] * G * sb[i]);
         }
     });
-    // the outputs leave as 4-vectors: after a quad transpose lane (lq, lr) holds row
-    // R0 + 4 lq + lr % 4, features 16 tile + 4 (lr / 4) .. +3; d there, loaded ahead of the
-    // products
-    const int ro = R0 + 4 * lq + (lr & 3), fo = 4 * (lr >> 2);
-    float dfin[NFH][4];
-#pragma unroll
-    for (int t = 0; t < NFH; ++t) {
-        float d8[8];
-        const int off = (ro < n ? ro : n - 1) * DK + 16 * (NFH * hw + t) + fo;
-        if constexpr (sizeof(TD) == 4) {
-            const float4 x = *reinterpret_cast<const float4 *>(dc + off);
-            d8[0] = x.x; d8[1] = x.y; d8[2] = x.z; d8[3] = x.w;
-        } else {
-            const uint2 x = *reinterpret_cast<const uint2 *>(dc + off);
-            d8[0] = bf_lo(x.x); d8[1] = bf_hi(x.x); d8[2] = bf_lo(x.y); d8[3] = bf_hi(x.y);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dfin[t][e] = d8[e];
-    }
     __syncthreads();
     if (tid < 64) {  // dbeta; dg of every row, then its reverse running sum d ln(alpha) (wave 0)
         const int r = lane;
@@ -1191,8 +1160,9 @@ bwd_tinv_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 //            the decay scan of chunk c-1 (double-buffered);
 //   dU       dU = P^T dO + diag(w) K~ dM, one tile per wave, as hi/lo bf16; K~ of chunk c-1
 //            into LDS;
-//   dR       dR = T^T dU from the T planes (hi.hi + hi.lo + lo.hi), one tile per wave; P and
-//            dO of chunk c-1 into LDS;
+//   dR       dR = T^T dU from the T planes (hi.hi + hi.lo + lo.hi), one tile per wave, stored
+//            in bf16 for the per-chunk pass, with dV = diag(b) dR; P and dO of chunk c-1 into
+//            LDS;
 //   update   dM <- gam_L dM + Q^T diag(gam) dO - K^T diag(gam b) dR on the wave's own tiles;
 //            the T planes of chunk c-1 into LDS.
 // So each tile of the next chunk is written in a phase after the last read of its buffer,
@@ -1203,7 +1173,8 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
                       const float *__restrict__ beta,
                       const float *__restrict__ alpha, const bf16_t *__restrict__ dO,
                       const float *__restrict__ dS_T, const uint16_t *__restrict__ Tck,
-                      uint16_t *__restrict__ dMck, float *__restrict__ dS0, int64_t T, int dv) {
+                      uint16_t *__restrict__ dMck, uint16_t *__restrict__ dRck,
+                      bf16_t *__restrict__ gv, float *__restrict__ dS0, int64_t T, int dv) {
     constexpr int C = 64, NW = 8, NTH = NW * 64;
     constexpr int PH = DK + 8, PCH = C + 8, PVH = BV + 8;  // bf16 pitches
     constexpr int G = DK / 8, NU = C * G / NTH;  // 16-byte units of a Q/K row; units per thread
@@ -1309,7 +1280,7 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
     auto load_ba = [&](int64_t cc) __attribute__((always_inline)) {
         const int r = min(lane, rows_of(cc) - 1);
         bv = beta[seq0 + cc * C + r];
-        av = alpha ? alpha[seq0 + cc * C + r] : 1.f;
+        av = (alpha ? alpha : beta)[seq0 + cc * C + r];  // unused without alpha
     };
     auto scan = [&](int64_t cc) __attribute__((always_inline)) {
         const int nn = rows_of(cc), pb = static_cast<int>(cc & 1);
@@ -1346,15 +1317,14 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
         store_kt();
         store_pdo(rows_of(nch - 1));
         store_t();
-        if (nch > 1) {
-            load_kt(nch - 2);
-            load_pdo(nch - 2);
-        }
-        if (wave == NW - 1) {
-            load_ba(nch - 1);
-            scan(nch - 1);
-            if (nch > 1) load_ba(nch - 2);
-        }
+        // every global access of the loop below is issued unconditionally (past the first chunk
+        // the loads repeat chunk 0, the stores fall outside their buffer's range), so that the
+        // compiler's wait counts stay exact and a wait for one load does not also wait for the
+        // stores and loads issued after it
+        load_kt(nch > 1 ? nch - 2 : 0);
+        load_pdo(nch > 1 ? nch - 2 : 0);
+        load_ba(nch - 1);
+        if (wave == NW - 1) scan(nch - 1);
     }
 
     for (int64_t c = nch - 1; c >= 0; --c) {
@@ -1373,11 +1343,8 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
 #pragma unroll
         for (int k0 = 0; k0 < DK; k0 += 32)
             kdm = mfma32(frag_rows(sKt, PH, R0, k0, lr, lq), frag_cols(sdMb, PVH, k0, jt, lr, lq), kdm);
-        if (wave == NW - 1 && c > 0) {  // the next chunk's decay scan, into the other buffer
-            scan(c - 1);
-            if (c > 1) load_ba(c - 2);
-        }
-        if (c > 0) load_t(c - 1);
+        load_ba(c > 0 ? c - 1 : 0);  // the next chunk's beta, alpha (scanned in the dR phase)
+        load_t(c > 0 ? c - 1 : 0);
         __syncthreads();
         {  // dU = P^T dO + diag(w) K~ dM on this wave's tile, as hi/lo bf16
             v4f du = zero4();
@@ -1393,10 +1360,8 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
                 sdUl[r * PVH + j] = bf16_bits(x - __uint_as_float(uint32_t(h) << 16));
             }
         }
-        if (c > 0) {  // K~ of the next chunk (sKt was last read by this chunk's K~ dM)
-            store_kt();
-            load_qk(c - 1);
-        }
+        if (c > 0) store_kt();  // K~ of the next chunk (sKt was last read by this chunk's K~ dM)
+        load_qk(c > 0 ? c - 1 : 0);
         __syncthreads();
         {  // dR = T^T dU (T^T upper triangular: k-steps from the tile's first row on); -gam b dR
             v4f dr = zero4();
@@ -1409,23 +1374,39 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
                 dr = mfma32(th, ul, dr);
                 dr = mfma32(tl, uh, dr);
             }
+            v4f gvt;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = R0 + 4 * lq + e, j = jt + lr;
                 sGDRb[r * PVH + j] = bf16_bits(-sgam[pb][r] * sb[pb][r] * dr[e]);
+                gvt[e] = sb[pb][r] * dr[e];
             }
+            // dR and dV in bf16: row R0 + 4 lq + lr % 4, columns jt + 4 (lr / 4) .. +3; rows
+            // past the end fall outside the range
+            const uint2 drp = pack4u(quad_transpose(dr, lane));
+            const uint2 gvp = pack4u(quad_transpose(gvt, lane));
+            const int64_t rowc = (seq0 + c * C) * dv;
+            const int boff = ((R0 + 4 * lq + (lr & 3)) * dv + j0 + jt + 4 * (lr >> 2)) * 2;
+            __builtin_amdgcn_raw_buffer_store_b64(
+                u32x2{drp.x, drp.y}, __builtin_amdgcn_make_buffer_rsrc(dRck + rowc, 0, n * dv * 2, 0x00020000),
+                boff, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(
+                u32x2{gvp.x, gvp.y}, __builtin_amdgcn_make_buffer_rsrc(gv + rowc, 0, n * dv * 2, 0x00020000),
+                boff, 0, 0);
+            // the next chunk's decay scan, into the other buffer (this chunk reads only its own)
+            if (wave == NW - 1 && c > 0) scan(c - 1);
         }
-        if (c > 0) {  // P and dO of the next chunk (last read by this chunk's dU)
-            store_pdo(rows_of(c - 1));
-            if (c > 1) {
-                load_kt(c - 2);
-                load_pdo(c - 2);
-            }
-        }
+        if (c > 0) store_pdo(rows_of(c - 1));  // P and dO of the next chunk (last read by dU)
+        load_kt(c > 1 ? c - 2 : 0);
+        load_pdo(c > 1 ? c - 2 : 0);
         __syncthreads();
         {  // dM <- gam_L dM + Q^T diag(gam) dO - K^T diag(gam b) dR on this wave's tiles; the
            // result is the gradient at the previous chunk's end
             const float gl = sgam[pb][C - 1];
+            // slot c - 1 of the checkpoints: none (an empty range) for the first chunk
+            const __amdgpu_buffer_rsrc_t mrsrc = __builtin_amdgcn_make_buffer_rsrc(
+                dMck + ((bh * nch + (c > 0 ? c - 1 : 0)) * DK) * dv, 0, c > 0 ? DK * dv * 2 : 0,
+                0x00020000);
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
                 const int ti = MT * wave + m, f0 = 16 * (ti >> 1), c0 = 16 * (ti & 1);
@@ -1441,11 +1422,10 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
                     dM[m][e] = gl * dM[m][e] + acc[e];
                     sdMb[f * PVH + j] = bf16_bits(dM[m][e]);
                 }
-                if (c > 0) {  // bf16, row f0 + 4 lq + lr % 4, columns c0 + 4 (lr / 4) .. +3
-                    const uint2 x = pack4u(quad_transpose(dM[m], lane));
-                    *reinterpret_cast<uint2 *>(dMck + ((bh * nch + c - 1) * DK + f0 + 4 * lq + (lr & 3)) * dv +
-                                               j0 + c0 + 4 * (lr >> 2)) = x;
-                }
+                // bf16, row f0 + 4 lq + lr % 4, columns c0 + 4 (lr / 4) .. +3
+                const uint2 x = pack4u(quad_transpose(dM[m], lane));
+                __builtin_amdgcn_raw_buffer_store_b64(
+                    u32x2{x.x, x.y}, mrsrc, ((f0 + 4 * lq + (lr & 3)) * dv + j0 + c0 + 4 * (lr >> 2)) * 2, 0, 0);
             }
         }
         if (c > 0) store_t();  // T of the next chunk (last read by this chunk's dR)
@@ -1469,6 +1449,7 @@ hipError_t bwd_typed(const BwdArgs &a, hipStream_t stream) {
         ChunkArgs f{a.q, a.k, a.v, a.d, a.beta, a.alpha, a.S0, nullptr, nullptr, a.BH, a.T, DK,
                     DV, C, a.qkv, a.d_dtype};
         f.ckpt = a.Mck;
+        f.uout = a.Uck;
         const hipError_t e = sizeof(TQ) == 2 ? launch_chunk_fwd_mfma(f, stream)
                                              : launch_chunk_fwd_f32math(f, stream);
         if (e != hipSuccess) return e;
@@ -1488,7 +1469,8 @@ hipError_t bwd_typed(const BwdArgs &a, hipStream_t stream) {
                            static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.k),
                            a.beta, a.alpha,
                            static_cast<const bf16_t *>(a.dO), a.dS_T, a.Tck,
-                           static_cast<uint16_t *>(a.dMck), a.dS0, a.T, DV);
+                           static_cast<uint16_t *>(a.dMck), a.dRck, static_cast<bf16_t *>(a.gv),
+                           a.dS0, a.T, DV);
     } else
     hipLaunchKernelGGL((bwd_state_kernel<C, DK, BVA, TQ, TD>),
                        dim3(static_cast<unsigned>(a.BH * (DV / BVA))), dim3(NT), 0, stream,
@@ -1505,8 +1487,8 @@ hipError_t bwd_typed(const BwdArgs &a, hipStream_t stream) {
                            static_cast<const bf16_t *>(a.v), static_cast<const TD *>(a.d),
                            a.beta, a.alpha, static_cast<const bf16_t *>(a.dO),
                            static_cast<const uint16_t *>(a.Mck), static_cast<const uint16_t *>(a.dMck),
-                           a.Tck, static_cast<bf16_t *>(a.gq), static_cast<bf16_t *>(a.gk),
-                           static_cast<bf16_t *>(a.gv), a.gbeta, static_cast<TD *>(a.gd),
+                           a.Tck, a.Uck, a.dRck, static_cast<bf16_t *>(a.gq),
+                           static_cast<bf16_t *>(a.gk), a.gbeta, static_cast<TD *>(a.gd),
                            a.galpha, a.T, nch);
     } else {
         constexpr int BVB = 32;  // value slice of the fp32 per-chunk pass

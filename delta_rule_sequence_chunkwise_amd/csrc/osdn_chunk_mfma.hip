@@ -263,7 +263,8 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                   const uint16_t *__restrict__ v, const TD *__restrict__ d,
                   const float *__restrict__ beta, const float *__restrict__ alpha,
                   const float *S0, uint16_t *__restrict__ o, float *S_T, int64_t BH,
-                  int64_t T, int dv, const float *__restrict__ gcs, uint16_t *__restrict__ ckpt) {
+                  int64_t T, int dv, const float *__restrict__ gcs, uint16_t *__restrict__ ckpt,
+                  uint16_t *__restrict__ uout) {
     using L = Lds<DK, GATE>;
     constexpr int NS = DK / 32;   // 32-wide k-steps over the key features
     constexpr int NFT = DK / 16;  // 16-row feature tiles of the state
@@ -426,6 +427,21 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                 solve(3);
                 const v8s ub1 = c_to_frag(U[2], U[3]);
                 const v8s uwb1 = c_to_frag(w4[2] * U[2], w4[3] * U[3]);
+                if constexpr (CKPT) {  // U for the backward, bf16: row 16 i + 4 lq + lr % 4,
+                                       // columns 4 (lr / 4) .. +3 of the wave's 16 after a quad
+                                       // transpose; rows past the end fall outside the range
+                    if (uout) {
+                        const __amdgpu_buffer_rsrc_t ursrc = __builtin_amdgcn_make_buffer_rsrc(
+                            uout + row0 * dv, 0, n * dv * 2, 0x00020000);
+#pragma unroll
+                        for (int i = 0; i < NBLK; ++i) {
+                            const uint2 pk = pack4u(quad_transpose(U[i], lane));
+                            __builtin_amdgcn_raw_buffer_store_b64(
+                                u32x2{pk.x, pk.y}, ursrc,
+                                ((16 * i + 4 * lq + (lr & 3)) * dv + j0 + VW * ct + 4 * (lr >> 2)) * 2, 0, 0);
+                        }
+                    }
+                }
 #pragma unroll
                 for (int ft = 0; ft < NFT; ++ft) M[ft] = mfma32(kt_frag(ft, 1), uwb1, acc[ft]);
                 if constexpr (GATE) {  // channel-wise gate: the state's rows times the chunk's G_C
@@ -714,7 +730,7 @@ hipError_t launch_typed(const ChunkArgs &a, hipStream_t stream) {
                        static_cast<const uint16_t *>(a.k), static_cast<const uint16_t *>(a.v), \
                        static_cast<const TD *>(a.d), a.beta, a.alpha, a.S0,                    \
                        static_cast<uint16_t *>(a.o), a.S_T, a.BH, a.T, a.dv, a.gcs,            \
-                       static_cast<uint16_t *>(a.ckpt))
+                       static_cast<uint16_t *>(a.ckpt), static_cast<uint16_t *>(a.uout))
     if (a.gcs) OSDN_CHUNK_LAUNCH(true, false, true);
     else if (a.ckpt && a.o) OSDN_CHUNK_LAUNCH(false, true, true);
     else if (a.ckpt) OSDN_CHUNK_LAUNCH(false, true, false);

@@ -45,6 +45,8 @@ struct ChunkArgs {
     void *ckpt = nullptr;        // [BH, nchunks, dk, dv]: the state at every chunk start, fp32
                                  // from the fp32 forward, bf16 from the matrix-core forward
                                  // (o may then be NULL: not written; no channel gate)
+    void *uout = nullptr;        // with ckpt, matrix-core forward: [BH, T, dv] bf16, the
+                                 // pseudo-values U of every row (NULL: not written)
 };
 
 struct BwdArgs {
@@ -64,6 +66,8 @@ struct BwdArgs {
                           // hi = bf16(T) and lo = bf16(T - hi) of T = (I + A)^{-1} and the
                           // scores P (64 x 64 each; P zero above the diagonal), then
                           // K~ = d (.) k (64 x dk; zero past the end)
+    uint16_t *Uck, *dRck; // workspace (bf16 inputs): U from the forward and dR from the reverse
+                          // pass, [BH, T, dv] bf16 each
     int64_t BH, T;
     int32_t dk, dv;
     osdn_dtype qkv, d_dtype;

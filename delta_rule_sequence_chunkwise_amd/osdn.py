@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "lib", "libosdn.so")
 
 OSDN_F32 = 0
 OSDN_BF16 = 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 STATUS = {0: "OSDN_OK", -1: "OSDN_ERR_NULL", -2: "OSDN_ERR_SHAPE", -3: "OSDN_ERR_UNSUPPORTED",
           -4: "OSDN_ERR_ALIGN", -5: "OSDN_ERR_ALIAS", -6: "OSDN_ERR_LAUNCH"}
@@ -168,21 +168,37 @@ def states_bytes(B: int, H: int, T: int, dk: int, dv: int, dtype_code: int) -> i
     return n
 
 
+def states_parts(states, B: int, H: int, T: int, dk: int, dv: int, dtype):
+    """Views of the training pair's states buffer: (checkpoints [B,H,nchunks,dk,dv], U
+    [B,H,T,dv] or None); dtype is the inputs' (torch.bfloat16 or torch.float32)."""
+    torch = _torch()
+    bf = dtype == torch.bfloat16
+    chunk = 64 if bf else 32
+    nch = (T + chunk - 1) // chunk
+    n = B * H * nch * dk * dv * (2 if bf else 4)
+    ck = states[:n].view(torch.bfloat16 if bf else torch.float32).view(B, H, nch, dk, dv)
+    if not bf:
+        return ck, None
+    uoff = (n + 255) // 256 * 256
+    u = states[uoff:uoff + B * H * T * dv * 2].view(torch.bfloat16).view(B, H, T, dv)
+    return ck, u
+
+
 def osdn_chunk_fwd_states(q, k, v, beta, d, alpha=None, S0=None, *, o=None, S_T=None,
                           states=None, want_state: bool = True, stream=None):
     """osdn_chunk_fwd with the backward's chunk size (64 rows for bf16, 32 for fp32) that also
-    keeps the state at every chunk start for osdn_chunk_bwd(..., states=...).  Returns
-    (o, S_T, states): states [B,H,nchunks,dk,dv], bf16 for bf16 inputs, fp32 for fp32."""
+    keeps what the backward would recompute, for osdn_chunk_bwd(..., states=...).  Returns
+    (o, S_T, states): states is a uint8 buffer of osdn_chunk_states_bytes bytes holding the
+    state at every chunk start ([B,H,nchunks,dk,dv], bf16 for bf16 inputs, fp32 for fp32) and,
+    for bf16 inputs, the pseudo-values U of every row after them (states_parts splits it)."""
     torch = _torch()
     B, H, T, dk = q.shape
     dv = v.shape[-1]
-    chunk = 64 if q.dtype == torch.bfloat16 else 32
-    nch = (T + chunk - 1) // chunk
-    sdt = torch.bfloat16 if q.dtype == torch.bfloat16 else torch.float32
+    nbytes = states_bytes(B, H, T, dk, dv, _dtype_code(q))
     if states is None:
-        states = torch.empty((B, H, nch, dk, dv), dtype=sdt, device=q.device)
-    if tuple(states.shape) != (B, H, nch, dk, dv) or states.dtype != sdt:
-        raise ValueError(f"states must be {sdt} [B,H,{nch},dk,dv]")
+        states = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    if states.dtype != torch.uint8 or not states.is_contiguous() or states.numel() < nbytes:
+        raise ValueError(f"states must be a contiguous uint8 buffer of at least {nbytes} bytes")
     if o is None:
         o = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
     if S_T is None and want_state:

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define OSDN_ABI_VERSION 1
+#define OSDN_ABI_VERSION 2
 
 typedef enum osdn_status {
     OSDN_OK = 0,
@@ -211,7 +211,9 @@ osdn_status osdn_step_kda(const void *q, const void *k, const void *v, const flo
  * The workspace holds the state and state-gradient checkpoints ([B,H,nchunks,dk,dv] each;
  * bf16 for bf16 inputs, the precision the matrix products take them in; fp32 for fp32 inputs)
  * and, for bf16 inputs, per chunk three bf16 64 x 64 planes (the inverse (I + A)^{-1} as hi and
- * lo parts, and the intra-chunk scores) and k~ = d (.) k as 64 x dk bf16.
+ * lo parts, and the intra-chunk scores) and k~ = d (.) k as 64 x dk bf16, then the per-row
+ * pseudo-values U (from the forward) and their gradient dR (from the reverse pass), [B,H,T,dv]
+ * bf16 each.
  */
 int64_t osdn_chunk_bwd_workspace(int64_t B, int64_t H, int64_t T, int32_t dk, int32_t dv,
                                  osdn_dtype qkv); /* -1 if invalid */
@@ -230,10 +232,11 @@ osdn_status osdn_chunk_bwd(const void *q, const void *k, const void *v, const fl
  *
  * osdn_chunk_fwd_states: as osdn_chunk_fwd with the backward's chunk size (64 rows for bf16
  * inputs, 32 for fp32), and in addition
- *   states   [B,H,nchunks,dk,dv] out, bf16 for bf16 inputs (the precision the backward's
- *            products take them in), fp32 for fp32 inputs; the state before chunk c's first
- *            row in slot c; osdn_chunk_states_bytes(B, H, T, dk, dv, qkv) bytes, 16-byte
- *            aligned, overlapping no other argument
+ *   states   out, osdn_chunk_states_bytes(B, H, T, dk, dv, qkv) bytes, 16-byte aligned,
+ *            overlapping no other argument: [B,H,nchunks,dk,dv], bf16 for bf16 inputs (the
+ *            precision the backward's products take them in), fp32 for fp32 inputs, the state
+ *            before chunk c's first row in slot c; for bf16 inputs then, from the next 256-byte
+ *            boundary, the pseudo-values U of every row, [B,H,T,dv] bf16
  * o and S_T are bitwise those of osdn_chunk_fwd with that chunk size.
  *
  * osdn_chunk_bwd_states: as osdn_chunk_bwd, with `states` (input) from osdn_chunk_fwd_states on

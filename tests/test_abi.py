@@ -260,13 +260,14 @@ def test_chunk_bwd_rejects(L, over, status):
 
 
 def test_bwd_workspace_size(L):
-    # bf16 inputs: two bf16 checkpoints [B,H,nchunks,dk,dv] (64-row chunks) and per chunk three
-    # bf16 64 x 64 planes (the inverse's hi and lo, the scores) and K~ (64 x dk bf16), each
-    # rounded up to 256 bytes
+    # bf16 inputs: two bf16 checkpoints [B,H,nchunks,dk,dv] (64-row chunks), per chunk three
+    # bf16 64 x 64 planes (the inverse's hi and lo, the scores) and K~ (64 x dk bf16), and two
+    # bf16 per-row buffers U and dR [B,H,T,dv], each rounded up to 256 bytes
     nch = (100 + 63) // 64
     ck = 2 * 3 * nch * 128 * 64 * 2
     ti = 2 * 3 * nch * (3 * 64 * 64 + 64 * 128) * 2
-    assert L.osdn_chunk_bwd_workspace(2, 3, 100, 128, 64, osdn.OSDN_BF16) == 2 * ck + ti
+    ub = (2 * 3 * 100 * 64 * 2 + 255) // 256 * 256
+    assert L.osdn_chunk_bwd_workspace(2, 3, 100, 128, 64, osdn.OSDN_BF16) == 2 * ck + ti + 2 * ub
     # fp32 inputs: two fp32 checkpoints (32-row chunks), no inverses
     nch = (100 + 31) // 32
     assert L.osdn_chunk_bwd_workspace(2, 3, 100, 128, 64, osdn.OSDN_F32) == 2 * (2 * 3 * nch * 128 * 64 * 4)
@@ -298,8 +299,10 @@ def test_chunk_fwd_states_rejects(L, over, status):
 
 def test_states_size_and_empty_work(L):
     # the state at every chunk start, [B,H,nchunks,dk,dv]: bf16 with 64-row chunks for bf16
-    # inputs, fp32 with 32-row chunks for fp32 inputs
-    assert L.osdn_chunk_states_bytes(2, 3, 100, 128, 64, osdn.OSDN_BF16) == 2 * 3 * 2 * 128 * 64 * 2
+    # inputs, then U [B,H,T,dv] bf16 from a 256-byte boundary on; fp32 with 32-row chunks for
+    # fp32 inputs
+    ub = (2 * 3 * 100 * 64 * 2 + 255) // 256 * 256
+    assert L.osdn_chunk_states_bytes(2, 3, 100, 128, 64, osdn.OSDN_BF16) == 2 * 3 * 2 * 128 * 64 * 2 + ub
     assert L.osdn_chunk_states_bytes(2, 3, 100, 128, 64, osdn.OSDN_F32) == 2 * 3 * 4 * 128 * 64 * 4
     assert L.osdn_chunk_states_bytes(2, 3, 0, 128, 64, osdn.OSDN_BF16) == 0
     assert L.osdn_chunk_states_bytes(2, 3, 100, 96, 64, osdn.OSDN_BF16) == -1

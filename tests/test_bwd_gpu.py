@@ -152,13 +152,19 @@ def test_bwd_full_1p3b_sampled():
 
 
 def _workspace_states(ws, B, H, T, dk, dv, qkv):
-    """The backward's own recomputed states: the first region of its workspace."""
+    """The backward's own recomputed states and (bf16) U: the workspace's first region, and its
+    region after the two checkpoints and the per-chunk planes."""
     torch, _ = torch_dev()
     C = 64 if qkv == "bf16" else 32
     nch = (T + C - 1) // C
     n = B * H * nch * dk * dv
+    r256 = lambda x: (x + 255) // 256 * 256
     dt = torch.bfloat16 if qkv == "bf16" else torch.float32
-    return ws[: n * (2 if qkv == "bf16" else 4)].view(dt).view(B, H, nch, dk, dv)
+    ck = ws[: n * (2 if qkv == "bf16" else 4)].view(dt).view(B, H, nch, dk, dv)
+    if qkv != "bf16":
+        return ck, None
+    off = 2 * r256(n * 2) + r256(B * H * nch * (3 * C * C + C * dk) * 2)
+    return ck, ws[off:off + B * H * T * dv * 2].view(dt).view(B, H, T, dv)
 
 
 @pytest.mark.parametrize("case", [(1, 2, 130, 128, 128, "bf16"), (2, 1, 64, 64, 128, "bf16"),
@@ -166,8 +172,8 @@ def _workspace_states(ws, B, H, T, dk, dv, qkv):
                          ids=lambda c: "x".join(map(str, c)))
 def test_training_pair_matches_recompute_bitwise(case):
     """osdn_chunk_fwd_states gives osdn_chunk_fwd's o and S_T (at the backward's chunk size)
-    and the backward's own checkpoints; osdn_chunk_bwd with those states gives the gradients
-    of the recomputing backward, bitwise."""
+    and the backward's own checkpoints (and, for bf16, U); osdn_chunk_bwd with those states
+    gives the gradients of the recomputing backward, bitwise."""
     torch, dev = torch_dev()
     B, H, T, dk, dv, qkv = case
     say("training pair", case)
@@ -183,7 +189,10 @@ def test_training_pair_matches_recompute_bitwise(case):
     ref = osdn.osdn_chunk_bwd(*args, go, gst, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(o, o_ref) and torch.equal(s_t, s_ref)
-    assert torch.equal(states, _workspace_states(ws, B, H, T, dk, dv, qkv))
+    ck, u = osdn.states_parts(states, B, H, T, dk, dv, args[0].dtype)
+    ck_ref, u_ref = _workspace_states(ws, B, H, T, dk, dv, qkv)
+    assert torch.equal(ck, ck_ref)
+    assert (u is None) == (u_ref is None) and (u is None or torch.equal(u, u_ref))
     got = osdn.osdn_chunk_bwd(*args, go, gst, states=states)
     torch.cuda.synchronize()
     for name, t in ref.items():
