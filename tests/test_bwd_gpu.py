@@ -81,6 +81,9 @@ BF16_CASES = [
     (1, 2, 200, 128, 64, "f32", False, True, False),
     (1, 1, 1, 128, 128, "f32", True, True, True),
     (2, 2, 257, 64, 64, "bf16", True, True, True),
+    # sequence counts that are multiples of 8 take the reverse pass's XCD-grouped mapping
+    (2, 4, 130, 128, 128, "f32", True, True, True),
+    (1, 8, 100, 64, 128, "bf16", True, False, True),
 ]
 
 
@@ -168,6 +171,7 @@ def _workspace_states(ws, B, H, T, dk, dv, qkv):
 
 
 @pytest.mark.parametrize("case", [(1, 2, 130, 128, 128, "bf16"), (2, 1, 64, 64, 128, "bf16"),
+                                  (2, 4, 100, 128, 64, "bf16"),
                                   (1, 1, 67, 64, 64, "f32"), (1, 2, 33, 128, 64, "f32")],
                          ids=lambda c: "x".join(map(str, c)))
 def test_training_pair_matches_recompute_bitwise(case):
