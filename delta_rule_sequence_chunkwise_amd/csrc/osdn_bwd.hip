@@ -139,7 +139,7 @@ __device__ __forceinline__ void solve_upper(float *X, const float *AS, const flo
 }
 
 // g = running sum of ln(alpha) over the chunk's rows (0 past the end), gam = e^g,
-// w = e^{g_last - g}; beta (0 past the end).  Wave 0 only.
+// w = e^{g_last - g}; beta (0 past the end).  One wave's work (several may write the same values).
 template <int C>
 __device__ __forceinline__ void decay_scan_of(float bv, float av, bool has_alpha, int n, float *sb,
                                               float *sg, float *sgam, float *sw, int lane) {
@@ -789,20 +789,9 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             make_uint4(ku[i].x & m, ku[i].y & m, ku[i].z & m, ku[i].w & m);
         *reinterpret_cast<uint4 *>(&sKt[r * PH + 8 * g]) = kt[i];
     }
-    {  // the decay scan: every wave computes it and writes the same values (no branch for
-       // its loads to sink into: they stay first)
-        float x = (lane < n && alpha) ? logf(pav) : 0.f;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_up(x, off);
-            if (lane >= off) x += y;
-        }
-        const float gl = __shfl(x, C - 1);
-        sb[lane] = lane < n ? pbv : 0.f;
-        sg[lane] = x;
-        sgam[lane] = __expf(x);
-        sw[lane] = __expf(gl - x);
-    }
+    // the decay scan: every wave computes it and writes the same values (no branch for its
+    // loads to sink into: they stay first)
+    decay_scan_of<C>(pbv, pav, alpha != nullptr, n, sb, sg, sgam, sw, lane);
     // d of this thread's output elements, loaded during the last slice (see below)
     const int ro = R0 + 4 * lq + (lr & 3), fo = 4 * (lr >> 2);
     float dfin[NFH][4];
