@@ -310,6 +310,28 @@ def test_states_size_and_empty_work(L):
     assert call_fwd_states(L, T=0, q=None, states=None, S_T=None) == 0
 
 
+@pytest.mark.parametrize("B,H,T,dk,dv,bf", [(2, 3, 100, 128, 64, True), (1, 1, 1, 64, 64, True),
+                                             (2, 1, 67, 64, 128, False)])
+def test_states_parts_layout(L, B, H, T, dk, dv, bf):
+    """The training pair's states buffer: checkpoints first, then (bf16 inputs) U from the next
+    256-byte boundary, ending inside osdn_chunk_states_bytes."""
+    import torch
+    dt = torch.bfloat16 if bf else torch.float32
+    nbytes = osdn.states_bytes(B, H, T, dk, dv, osdn.OSDN_BF16 if bf else osdn.OSDN_F32)
+    buf = torch.zeros(nbytes, dtype=torch.uint8)
+    ck, u = osdn.states_parts(buf, B, H, T, dk, dv, dt)
+    nch = (T + (64 if bf else 32) - 1) // (64 if bf else 32)
+    assert ck.shape == (B, H, nch, dk, dv) and ck.dtype == dt
+    assert ck.data_ptr() == buf.data_ptr()
+    if not bf:
+        assert u is None
+        return
+    off = u.data_ptr() - buf.data_ptr()
+    assert u.shape == (B, H, T, dv) and u.dtype == torch.bfloat16
+    assert off % 256 == 0 and off >= ck.numel() * 2
+    assert off + u.numel() * 2 <= nbytes
+
+
 def call_bwd_states(L, **over):
     a = dict(q=addr(1), k=addr(2), v=addr(3), beta=addr(4), d=addr(5), alpha=addr(6),
              S0=addr(7), states=addr(18), go=addr(8), gST=addr(9), gq=addr(10), gk=addr(11),
