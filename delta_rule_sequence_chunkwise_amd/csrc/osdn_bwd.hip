@@ -662,7 +662,7 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
                       const uint16_t *__restrict__ Uck, const uint16_t *__restrict__ dRck,
                       bf16_t *__restrict__ gq, bf16_t *__restrict__ gk,
                       float *__restrict__ gbeta, TD *__restrict__ gd,
-                      float *__restrict__ galpha, int64_t T, int64_t nch) {
+                      float *__restrict__ galpha, int64_t T, int64_t nch, int64_t total) {
     constexpr int C = 64, BV = 32, NW = 8, NTH = NW * 64;
     constexpr int PH = DK + 8, PCH = C + 8, PVH = BV + 8;  // bf16 pitches
     constexpr int NF = DK / 16, NFH = NF / 2;  // feature tiles; per half
@@ -680,47 +680,89 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
     __shared__ float sred[NW];
     uint16_t *const sM0b = sMb, *const sdMb = sMb + DK * PVH;
 
-    const int64_t bh = blockIdx.x / nch, c = blockIdx.x % nch;
-    const int64_t c0 = c * C, row0 = bh * T + c0;
-    const int n = static_cast<int>(T - c0 < C ? T - c0 : C);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int rw = wave & 3, hw = wave >> 2;
-    const int lr = lane & 15, lq = lane >> 4;
-    const int R0 = 16 * rw;  // this wave's rows
-    const int jt = 16 * hw;  // this wave's columns of the value slice
-    const uint16_t *M0 = Mck + (bh * nch + c) * DK * DV;  // bf16
-    const uint16_t *dMC = dMck + (bh * nch + c) * DK * DV;
-    // the chunk's rows of every per-token array: uniform bases, 32-bit offsets
-    const bf16_t *vc = v + row0 * DV, *oc = dO + row0 * DV;
-    const uint16_t *uc = Uck + row0 * DV, *rc = dRck + row0 * DV;
-    bf16_t *gqc = gq + row0 * DK, *gkc = gk + row0 * DK;
-    TD *gdc = gd + row0 * DK;
-    const TD *dc = d + row0 * DK;
-
-    // every load of the prologue is issued before the first wait: beta, alpha (every wave, for
-    // the scan of wave 0), Q, K, K~ (bf16, 8 features per 16-byte unit; K~ from its plane), the
-    // first two value slices (below)
-    const float pbv = beta[row0 + (lane < n ? lane : n - 1)];
-    const float pav = (alpha ? alpha : beta)[row0 + (lane < n ? lane : n - 1)];  // unused without alpha
-    __builtin_amdgcn_sched_barrier(0);  // the loads leave in this order (waits count them so)
+    // thread indices; re-derived at the top of every chunk from an opaque copy of the thread id,
+    // so that the compiler does not hoist the many LDS addresses built from them out of the
+    // chunk loop (held across it they would not fit in the registers)
+    int tid, lane, wave, rw, hw, lr, lq, R0, jt, ro, fo;
+    auto derive = [&]() __attribute__((always_inline)) {
+        tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        lane = tid & 63;
+        wave = tid >> 6;
+        rw = wave & 3;   // this wave's rows: R0 = 16 rw ..
+        hw = wave >> 2;  // this wave's half of the features and columns jt = 16 hw .. of a slice
+        lr = lane & 15;
+        lq = lane >> 4;
+        R0 = 16 * rw;
+        jt = 16 * hw;
+        ro = R0 + 4 * lq + (lr & 3);  // an output 4-vector's row and first feature in its tile
+        fo = 4 * (lr >> 2);
+    };
+    derive();
+    // Persistent: the workgroup takes chunks ci = blockIdx.x, + gridDim.x, ... (ci = sequence *
+    // nch + chunk), and issues the next chunk's prologue loads while it finishes the current one.
+    // A chunk's rows are row0 .. row0 + n - 1 of the [B*H*T] token rows.
+    auto rows_of_chunk = [&](int64_t cc, int64_t &r0, int &nn) __attribute__((always_inline)) {
+        const int64_t cb = cc / nch, c0 = (cc % nch) * C;
+        r0 = cb * T + c0;
+        nn = static_cast<int>(T - c0 < C ? T - c0 : C);
+    };
     constexpr int G = DK / 8, NU = C * G / NTH;  // units per row, units per thread
     static_assert(NU * NTH == C * G, "whole units");
-    uint4 qu[NU], ku[NU], kt[NU];
-    {
-        const uint16_t *pc = Tck + (bh * nch + c) * (3 * C * C + C * DK);
-#pragma unroll
-        for (int i = 0; i < NU; ++i) {
-            const int u = tid + i * NTH, r = u / G, g = u % G;
-            kt[i] = *reinterpret_cast<const uint4 *>(pc + 3 * C * C + r * DK + 8 * g);
+    // the value slices' M0, dMC, v, dO, U and dR (bf16, four per 8-byte unit) pass through
+    // named registers two slices ahead (two register sets; the slice loop is unrolled)
+    struct SliceRegs {
+        uint2 m0a, m0b, dma, dmb, vu, ou, uu, ru;
+    };
+    SliceRegs ra{}, rb{};
+    auto load_slice = [&](SliceRegs &x, int S0, int64_t cc, int64_t r0, int nn)
+        __attribute__((always_inline)) {
+        const uint16_t *M0 = Mck + cc * DK * DV, *dMC = dMck + cc * DK * DV;  // bf16
+        {
+            const int f = tid / (BV / 4), j = 4 * (tid % (BV / 4));
+            x.m0a = *reinterpret_cast<const uint2 *>(M0 + f * DV + S0 + j);
+            x.dma = *reinterpret_cast<const uint2 *>(dMC + f * DV + S0 + j);
         }
-#pragma unroll
-        for (int i = 0; i < NU; ++i) {
-            const int u = tid + i * NTH, r = u / G, g = u % G;
-            const int64_t e = (row0 + (r < n ? r : n - 1)) * DK + 8 * g;
-            qu[i] = *reinterpret_cast<const uint4 *>(q + e);
-            ku[i] = *reinterpret_cast<const uint4 *>(k + e);
+        if constexpr (MU == 2) {
+            const int u = tid + NTH, f = u / (BV / 4), j = 4 * (u % (BV / 4));
+            x.m0b = *reinterpret_cast<const uint2 *>(M0 + f * DV + S0 + j);
+            x.dmb = *reinterpret_cast<const uint2 *>(dMC + f * DV + S0 + j);
         }
-    }
+        // the chunk's rows of every per-token array: uniform bases, 32-bit offsets
+        const int r = tid / (BV / 4), j = 4 * (tid % (BV / 4));
+        const int e = (r < nn ? r : nn - 1) * DV + S0 + j;
+        x.vu = *reinterpret_cast<const uint2 *>(v + r0 * DV + e);
+        x.ou = *reinterpret_cast<const uint2 *>(dO + r0 * DV + e);
+        x.uu = *reinterpret_cast<const uint2 *>(Uck + r0 * DV + e);
+        x.ru = *reinterpret_cast<const uint2 *>(dRck + r0 * DV + e);
+    };
+    constexpr int NS = DV / BV;  // value slices
+    // a chunk's prologue loads, issued while the previous chunk finishes: beta, alpha (every
+    // wave, for the scan), Q, K, K~ (bf16, 8 features per 16-byte unit; K~ from its plane) in
+    // named registers (an array carried across the chunk loop would live in scratch or LDS)
+    static_assert(NU == 1 || NU == 2, "one or two units per thread");
+    float pbv, pav;
+    uint4 q0r, q1r, k0r, k1r, w0r, w1r;
+    auto qreg = [&](auto I) -> uint4 & { if constexpr (decltype(I)::value == 0) return q0r; else return q1r; };
+    auto kreg = [&](auto I) -> uint4 & { if constexpr (decltype(I)::value == 0) return k0r; else return k1r; };
+    auto wreg = [&](auto I) -> uint4 & { if constexpr (decltype(I)::value == 0) return w0r; else return w1r; };
+    auto issue_prologue = [&](int64_t cc, int64_t r0, int nn) __attribute__((always_inline)) {
+        pbv = beta[r0 + (lane < nn ? lane : nn - 1)];
+        pav = (alpha ? alpha : beta)[r0 + (lane < nn ? lane : nn - 1)];  // unused without alpha
+        __builtin_amdgcn_sched_barrier(0);  // the loads leave in this order (waits count them so)
+        const uint16_t *pc = Tck + cc * (3 * C * C + C * DK);
+        static_for<0, NU>([&](auto I) __attribute__((always_inline)) {
+            const int u = tid + I * NTH, r = u / G, g = u % G;
+            wreg(I) = *reinterpret_cast<const uint4 *>(pc + 3 * C * C + r * DK + 8 * g);
+        });
+        static_for<0, NU>([&](auto I) __attribute__((always_inline)) {
+            const int u = tid + I * NTH, r = u / G, g = u % G;
+            const int64_t e = (r0 + (r < nn ? r : nn - 1)) * DK + 8 * g;
+            qreg(I) = *reinterpret_cast<const uint4 *>(q + e);
+            kreg(I) = *reinterpret_cast<const uint4 *>(k + e);
+        });
+        __builtin_amdgcn_sched_barrier(0);
+    };
     // score tile t of this wave's rows: AS = strictly lower (K K~^T) o G and P =
     // lower-inclusive (Q K~^T) o G in the C layout (zero for tiles above the diagonal)
     auto score_tiles = [&](int t, v4f &ak, v4f &aq) __attribute__((always_inline)) {
@@ -743,57 +785,41 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
         }
     };
 
+    int64_t ci = blockIdx.x, row0;
+    int n;
+    if (ci >= total) return;
+    rows_of_chunk(ci, row0, n);
+    issue_prologue(ci, row0, n);
+
+#pragma unroll 1
+    for (;;) {
+    derive();
     v4f aQ[NFH], aK[NFH], aKt[NFH], adP[2], adA[2];
 #pragma unroll
     for (int t = 0; t < NFH; ++t) aQ[t] = aK[t] = aKt[t] = zero4();
     adP[0] = adP[1] = adA[0] = adA[1] = zero4();
     float pdb[4] = {0.f, 0.f, 0.f, 0.f};  // <dR_r, V_r> over the value columns, per lane
     float frob = 0.f;
+    const TD *dc = d + row0 * DK;
 
-    // the value slices' M0, dMC, v, dO, U and dR (bf16, four per 8-byte unit) pass through
-    // named registers two slices ahead (two register sets; the slice loop is unrolled)
-    struct SliceRegs {
-        uint2 m0a, m0b, dma, dmb, vu, ou, uu, ru;
-    };
-    SliceRegs ra{}, rb{};
-    auto load_slice = [&](SliceRegs &x, int S0) __attribute__((always_inline)) {
-        {
-            const int f = tid / (BV / 4), j = 4 * (tid % (BV / 4));
-            x.m0a = *reinterpret_cast<const uint2 *>(M0 + f * DV + S0 + j);
-            x.dma = *reinterpret_cast<const uint2 *>(dMC + f * DV + S0 + j);
-        }
-        if constexpr (MU == 2) {
-            const int u = tid + NTH, f = u / (BV / 4), j = 4 * (u % (BV / 4));
-            x.m0b = *reinterpret_cast<const uint2 *>(M0 + f * DV + S0 + j);
-            x.dmb = *reinterpret_cast<const uint2 *>(dMC + f * DV + S0 + j);
-        }
-        const int r = tid / (BV / 4), j = 4 * (tid % (BV / 4));
-        const int e = (r < n ? r : n - 1) * DV + S0 + j;
-        x.vu = *reinterpret_cast<const uint2 *>(vc + e);
-        x.ou = *reinterpret_cast<const uint2 *>(oc + e);
-        x.uu = *reinterpret_cast<const uint2 *>(uc + e);
-        x.ru = *reinterpret_cast<const uint2 *>(rc + e);
-    };
-    constexpr int NS = DV / BV;  // value slices
+    // the first two value slices of this chunk, then its prologue tiles into LDS
     __builtin_amdgcn_sched_barrier(0);
-    load_slice(ra, 0);
-    if constexpr (NS > 1) load_slice(rb, BV);
+    load_slice(ra, 0, ci, row0, n);
+    if constexpr (NS > 1) load_slice(rb, BV, ci, row0, n);
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < NU; ++i) {
-        const int u = tid + i * NTH, r = u / G, g = u % G;
+    static_for<0, NU>([&](auto I) __attribute__((always_inline)) {
+        const int u = tid + I * NTH, r = u / G, g = u % G;
         const uint32_t m = r < n ? 0xffffffffu : 0u;  // rows past the end are zero
-        *reinterpret_cast<uint4 *>(&sQ[r * PH + 8 * g]) =
-            make_uint4(qu[i].x & m, qu[i].y & m, qu[i].z & m, qu[i].w & m);
-        *reinterpret_cast<uint4 *>(&sK[r * PH + 8 * g]) =
-            make_uint4(ku[i].x & m, ku[i].y & m, ku[i].z & m, ku[i].w & m);
-        *reinterpret_cast<uint4 *>(&sKt[r * PH + 8 * g]) = kt[i];
-    }
+        const uint4 qq = qreg(I), kk = kreg(I);
+        *reinterpret_cast<uint4 *>(&sQ[r * PH + 8 * g]) = make_uint4(qq.x & m, qq.y & m, qq.z & m, qq.w & m);
+        *reinterpret_cast<uint4 *>(&sK[r * PH + 8 * g]) = make_uint4(kk.x & m, kk.y & m, kk.z & m, kk.w & m);
+        *reinterpret_cast<uint4 *>(&sKt[r * PH + 8 * g]) = wreg(I);
+    });
     // the decay scan: every wave computes it and writes the same values (no branch for its
     // loads to sink into: they stay first)
     decay_scan_of<C>(pbv, pav, alpha != nullptr, n, sb, sg, sgam, sw, lane);
+    const float acur = pav;  // alpha of row lane of this chunk (wave 0's galpha)
     // d of this thread's output elements, loaded during the last slice (see below)
-    const int ro = R0 + 4 * lq + (lr & 3), fo = 4 * (lr >> 2);
     float dfin[NFH][4];
 
     static_for<0, NS>([&](auto S) __attribute__((always_inline)) {
@@ -817,7 +843,7 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             *reinterpret_cast<uint2 *>(&sUb[r * PVH + j]) = make_uint2(x.uu.x & m, x.uu.y & m);
             *reinterpret_cast<uint2 *>(&sDRb[r * PVH + j]) = make_uint2(x.ru.x & m, x.ru.y & m);
         }
-        if constexpr (S + 2 < NS) load_slice(x, s0 + 2 * BV);  // in flight through two slices
+        if constexpr (S + 2 < NS) load_slice(x, s0 + 2 * BV, ci, row0, n);  // two slices ahead
         if constexpr (S + 1 == NS) {
             // d where this thread's outputs go (after a quad transpose lane (lq, lr) holds row
             // R0 + 4 lq + lr % 4, features 16 tile + 4 (lr / 4) .. +3), ahead of the products
@@ -849,7 +875,7 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
         });
         const v8s dob = frag_rows(sDOb, PVH, R0, 0, lr, lq), drb = frag_rows(sDRb, PVH, R0, 0, lr, lq);
         const v8s urb = frag_rows(sUb, PVH, R0, 0, lr, lq);
-#pragma unroll 2
+#pragma unroll
         for (int t = 0; t < NFH; ++t) {
             const int f0 = 16 * (NFH * hw + t);
             const v8s m0r = frag_rows(sM0b, PVH, f0, 0, lr, lq);
@@ -864,6 +890,13 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
                       __uint_as_float(uint32_t(sVb[r * PVH + j]) << 16);
         }
     });
+    // the next chunk's prologue, in flight through this chunk's closing phase (past the last
+    // chunk the loads repeat this one: every load is issued, so the wait counts stay exact)
+    const int64_t cn = ci + gridDim.x;
+    int64_t rn0 = row0;
+    int nn = n;
+    if (cn < total) rows_of_chunk(cn, rn0, nn);
+    issue_prologue(cn < total ? cn : ci, rn0, nn);
     {  // <dMC, M0> over the workgroup (fixed order); ends with a barrier: the slices are done
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) frob += __shfl_xor(frob, m);
@@ -980,7 +1013,7 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
         }
         if (r < n) {
             gbeta[row0 + r] = db;
-            if (alpha && galpha) galpha[row0 + r] = g / alpha[row0 + r];
+            if (alpha && galpha) galpha[row0 + r] = g / acur;
         }
     }
     // dQ += (dP o G) K~, dK += Gb K~, dK~ += (dP o G)^T Q + Gb^T K on this wave's feature tiles
@@ -996,6 +1029,10 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             aKt[t] = mfma32(frag_cols(sGb, PCH, k0, R0, lr, lq), frag_cols(sK, PH, k0, f0, lr, lq), aKt[t]);
         }
     }
+    const __amdgpu_buffer_rsrc_t grs_q = __builtin_amdgcn_make_buffer_rsrc(gq + row0 * DK, 0, n * DK * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t grs_k = __builtin_amdgcn_make_buffer_rsrc(gk + row0 * DK, 0, n * DK * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t grs_d = __builtin_amdgcn_make_buffer_rsrc(
+        gd + row0 * DK, 0, n * DK * static_cast<int>(sizeof(TD)), 0x00020000);
 #pragma unroll
     for (int t = 0; t < NFH; ++t) {
         const v4f gqt = quad_transpose(aQ[t], lane), gkt = quad_transpose(aK[t], lane);
@@ -1009,11 +1046,26 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             gk4[e] = gkt[e] + gkw[e] * dfin[t][e];
             gd4[e] = gkw[e] * kv[e];
         }
-        if (ro < n) {
-            store4(gqc + ro * DK + f, gqt);
-            store4(gkc + ro * DK + f, gk4);
-            store4(gdc + ro * DK + f, gd4);
+        // rows past the end fall outside the buffers' ranges
+        const int eo = ro * DK + f;
+        const uint2 pq = pack4u(gqt), pk = pack4u(gk4);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{pq.x, pq.y}, grs_q, eo * 2, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{pk.x, pk.y}, grs_k, eo * 2, 0, 0);
+        if constexpr (sizeof(TD) == 4) {
+            __builtin_amdgcn_raw_buffer_store_b128(
+                u32x4{__float_as_uint(gd4[0]), __float_as_uint(gd4[1]), __float_as_uint(gd4[2]),
+                      __float_as_uint(gd4[3])},
+                grs_d, eo * 4, 0, 0);
+        } else {
+            const uint2 pd = pack4u(gd4);
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{pd.x, pd.y}, grs_d, eo * 2, 0, 0);
         }
+    }
+    if (cn >= total) break;
+    ci = cn;
+    row0 = rn0;
+    n = nn;
+    __syncthreads();  // the closing phase is done with the LDS tiles the next chunk overwrites
     }
 }
 
@@ -1429,6 +1481,20 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
     }
 }
 
+// compute units of the current device (cached per device; 256 if the query fails)
+int64_t num_cus() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        cus = 256;
+    if (dev >= 0 && dev < 64) cache[dev] = cus;
+    return cus;
+}
+
 template <int C, int DK, int DV, typename TQ, typename TD>
 hipError_t bwd_typed(const BwdArgs &a, hipStream_t stream) {
     const int64_t nch = (a.T + C - 1) / C;
@@ -1470,15 +1536,19 @@ hipError_t bwd_typed(const BwdArgs &a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || nch == 0) return e;
     if constexpr (sizeof(TQ) == 2) {
+        // persistent: one workgroup per CU (its LDS allows no more), each taking every
+        // grid-th chunk
+        const int64_t total = a.BH * nch;
+        const int64_t grid = total < num_cus() ? total : num_cus();
         hipLaunchKernelGGL((bwd_chunk_mfma_kernel<DK, DV, TD>),
-                           dim3(static_cast<unsigned>(a.BH * nch)), dim3(2 * NT), 0, stream,
+                           dim3(static_cast<unsigned>(grid)), dim3(2 * NT), 0, stream,
                            static_cast<const bf16_t *>(a.q), static_cast<const bf16_t *>(a.k),
                            static_cast<const bf16_t *>(a.v), static_cast<const TD *>(a.d),
                            a.beta, a.alpha, static_cast<const bf16_t *>(a.dO),
                            static_cast<const uint16_t *>(a.Mck), static_cast<const uint16_t *>(a.dMck),
                            a.Tck, a.Uck, a.dRck, static_cast<bf16_t *>(a.gq),
                            static_cast<bf16_t *>(a.gk), a.gbeta, static_cast<TD *>(a.gd),
-                           a.galpha, a.T, nch);
+                           a.galpha, a.T, nch, total);
     } else {
         constexpr int BVB = 32;  // value slice of the fp32 per-chunk pass
         hipLaunchKernelGGL((bwd_chunk_kernel<C, DK, DV, BVB, TQ, TD>),

@@ -17,6 +17,7 @@ typedef short v4s __attribute__((__vector_size__(4 * sizeof(short))));
 typedef float v4f __attribute__((__vector_size__(4 * sizeof(float))));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
