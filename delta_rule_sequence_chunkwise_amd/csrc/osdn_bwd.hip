@@ -24,13 +24,15 @@
 //   dd  = dK~ o K,   dK += dK~ o D
 //
 // Launches on the caller's stream: (1) the forward (the bf16 matrix-core kernel for bf16
-// inputs, the fp32 one for fp32 inputs) records M0 of every chunk into the workspace; (2) for
-// bf16 inputs, bwd_tinv_kernel inverts every chunk's I + A in parallel into the workspace (T
-// does not depend on the state); (3) the reverse pass walks the chunks backwards per
-// (sequence, value slice) carrying dM, records dMC of every chunk and writes the initial-state
-// gradient; (4) the per-chunk pass, one workgroup per (sequence, chunk), computes every
-// gradient of the chunk's rows from M0, dMC (and T).  For fp32 inputs (2) is skipped and
-// (3), (4) are fp32 on the vector ALUs (bwd_state_kernel, bwd_chunk_kernel): tile products
+// inputs, the fp32 one for fp32 inputs) records M0 of every chunk into the workspace, and for
+// bf16 inputs U of every row; (2) for bf16 inputs, bwd_tinv_kernel inverts every chunk's I + A
+// in parallel into the workspace (T does not depend on the state), with P and K~; (3) the
+// reverse pass walks the chunks backwards per (sequence, value slice) carrying dM, records dMC
+// of every chunk (and for bf16 inputs dR and dV of every row) and writes the initial-state
+// gradient; (4) the per-chunk pass computes every other gradient of a chunk's rows from M0,
+// dMC and, for bf16 inputs, U and dR (for fp32 inputs it forms U and dR itself by triangular
+// solves; one workgroup per chunk, or for bf16 inputs persistent workgroups taking every
+// grid-th chunk).  For fp32 inputs (2) is skipped and (3), (4) are fp32 on the vector ALUs (bwd_state_kernel, bwd_chunk_kernel): tile products
 // are register-blocked (each of the 256 threads owns one (M/16) x (N/16) block of every M x N
 // product), the triangular solves run column-parallel with the partial sums of one column
 // reduced across adjacent lanes.  For bf16 inputs they run on matrix cores
