@@ -94,6 +94,16 @@ def test_bwd_bf16(case):
     check(x, g, "bf16", dd, label=str(case))
 
 
+@pytest.mark.parametrize("case", [(1, 8, 2100, 64, 64, "bf16"), (1, 4, 4200, 128, 64, "f32")],
+                         ids=lambda c: "x".join(map(str, c)))
+def test_bwd_bf16_several_chunks_per_workgroup(case):
+    """More chunks than compute units (264 > 256), so the persistent per-chunk pass takes
+    several chunks in one workgroup, one of them ragged."""
+    B, H, T, dk, dv, dd = case
+    x, g = bwd_inputs(B, H, T, dk, dv, "bf16", seed=T + dk)
+    check(x, g, "bf16", dd, label=str(case))
+
+
 def test_bwd_empty_sequence_passes_state_gradient():
     torch, dev = torch_dev()
     say("chunk_bwd T=0")
