@@ -1388,8 +1388,8 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             kdm = mfma32(frag_rows(sKt, PH, R0, k0, lr, lq), frag_cols(sdMb, PVH, k0, jt, lr, lq), kdm);
         load_ba(c > 0 ? c - 1 : 0);  // the next chunk's beta, alpha (scanned in the dR phase)
         load_t(c > 0 ? c - 1 : 0);
-        __syncthreads();
-        {  // dU = P^T dO + diag(w) K~ dM on this wave's tile, as hi/lo bf16
+        {  // dU = P^T dO + diag(w) K~ dM on this wave's tile (its own K~ dM: no barrier), as
+           // hi/lo bf16
             v4f du = zero4();
 #pragma unroll
             for (int k0 = 0; k0 < C; k0 += 32)
@@ -1403,7 +1403,6 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
                 sdUl[r * PVH + j] = bf16_bits(x - __uint_as_float(uint32_t(h) << 16));
             }
         }
-        if (c > 0) store_kt();  // K~ of the next chunk (sKt was last read by this chunk's K~ dM)
         load_qk(c > 0 ? c - 1 : 0);
         __syncthreads();
         {  // dR = T^T dU (T^T upper triangular: k-steps from the tile's first row on); -gam b dR
@@ -1439,6 +1438,7 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             // the next chunk's decay scan, into the other buffer (this chunk reads only its own)
             if (wave == NW - 1 && c > 0) scan(c - 1);
         }
+        if (c > 0) store_kt();  // K~ of the next chunk (sKt was last read by this chunk's K~ dM)
         if (c > 0) store_pdo(rows_of(c - 1));  // P and dO of the next chunk (last read by dU)
         load_kt(c > 1 ? c - 2 : 0);
         load_pdo(c > 1 ? c - 2 : 0);
