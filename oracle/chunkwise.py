@@ -110,19 +110,77 @@ def precond_scan(k, beta, eta: float, r=None, d1=None, chunk: int = 64
     return out, d_next
 
 
+def _segment_products(a):
+    """Per-feature products of the gates a [n, dk] (n a multiple of 16) inside aligned row
+    segments of 1, 2, 4, 8 and 16 rows, built level by level from the sibling segment's total:
+    pre[h][r] = prod of a over r's h-segment up to r (inclusive),
+    suf[h][r] = prod of a over r's h-segment after r (exclusive),
+    tot[h][r] = prod of a over r's whole h-segment."""
+    n = a.shape[0]
+    pre, suf, tot = {1: a.copy()}, {1: np.ones_like(a)}, {1: a.copy()}
+    h = 1
+    while h < 16:
+        sib = tot[h][np.arange(n) ^ h]  # the sibling h-segment's total
+        lower = ((np.arange(n) & h) == 0)[:, None]
+        pre[2 * h] = np.where(lower, pre[h], sib * pre[h])
+        suf[2 * h] = np.where(lower, suf[h] * sib, suf[h])
+        tot[2 * h] = tot[h] * sib
+        h *= 2
+    return pre, suf, tot
+
+
+def _anchored_scores(X, Y, a):
+    """E[r, s] = sum_f X[r, f] Y[s, f] prod_{s < t <= r} a[t, f] for s <= r (0 above the
+    diagonal), as sums of plain matrix products whose operand factors are all products of
+    gates, hence at most 1 (no reciprocal of a running product):
+
+    * r and s in different 16-row blocks i > j: anchor at the last row e of block j,
+      x_r = prod_{e < t <= r} a_t (the blocks between, then r's block up to r),
+      y_s = prod_{s < t <= e} a_t;
+    * r and s in one block: at the level h where they first fall into different h-row
+      halves of one 2h-row segment, x_r = product over r's half up to r, y_s = product over
+      s's half after s; one product per level, its entries outside such pairs dropped;
+    * r = s: factor 1."""
+    n, dk = X.shape
+    pre, suf, tot = _segment_products(a)
+    r = np.arange(n)[:, None]
+    s = np.arange(n)[None, :]
+    E = np.where(r == s, X @ Y.T, 0.0)
+    h = 8
+    while h >= 1:  # inside 16-row blocks
+        up = ((np.arange(n) & h) != 0)[:, None]
+        Xh = np.where(up, X * pre[h], 0.0)
+        Yh = np.where(~up, Y * suf[h], 0.0)
+        keep = ((r ^ s) >> (2 * h).bit_length() - 1 == 0) & ((r & h) != 0) & ((s & h) == 0)
+        E += np.where(keep, Xh @ Yh.T, 0.0)
+        h //= 2
+    nb = n // 16
+    blk_tot = tot[16][::16]  # [nb, dk]
+    for j in range(nb):  # blocks after j, anchored at the end of block j
+        cols = slice(16 * j, 16 * j + 16)
+        Yj = Y[cols] * suf[16][cols]
+        for i in range(j + 1, nb):
+            rows = slice(16 * i, 16 * i + 16)
+            cross = np.prod(blk_tot[j + 1:i], axis=0) if i > j + 1 else np.ones(dk)
+            E[rows, cols] = (X[rows] * pre[16][rows] * cross) @ Yj.T
+    return E
+
+
 def chunk_fwd_channel(q, k, v, beta, d, alpha_ch, S0=None, chunk: int = 64
                       ) -> Tuple[np.ndarray, np.ndarray]:
     """Chunk form of the recurrence with a channel-wise gate a_t in R^dk (Erase-then-Delta
     Attention, section 2.2, eq. 5) and the OSDN write key k~ = d (.) k; derived here.
 
-    Inside a chunk let G_r = prod_{s<=r} a_s (per feature, inclusive).  Unrolling
-    M_r = Diag(a_r) M_{r-1} + k~_r u_r^T gives M_r = Diag(G_r) M0 + sum_{s<=r} Diag(G_r / G_s) k~_s u_s^T,
-    so with the operands scaled per feature,  q' = q G,  k' = k G,  k~' = k~ / G,
-    every decay factor folds into them:
-        (I + A) U = diag(b) (V - K' M0),  A[r,s] = b_r <k'_r, k~'_s>  (s < r),
-        O = Q' M0 + lower_incl(Q' K~'^T) U,
-        M_C = Diag(G_C) (M0 + K~'^T U).
-    """
+    Inside a chunk, unrolling M_r = Diag(a_r) M_{r-1} + k~_r u_r^T gives
+        M_r = Diag(G_r) M0 + sum_{s<=r} Diag(rho(s->r)) k~_s u_s^T,
+    G_r = prod_{t<=r} a_t (from the chunk start), rho(s->r) = prod_{s<t<=r} a_t, so
+        (I + A) U = diag(b) (V - (K o G) M0),   A[r,s] = b_r sum_f k_rf k~_sf rho_f(s->r) (s<r),
+        O   = (Q o G) M0 + P U,                 P[r,s] = sum_f q_rf k~_sf rho_f(s->r)   (s<=r),
+        M_C = Diag(G_C) M0 + (K~ o rho(.->C))^T U.
+    Every factor here is a product of gates, so at most 1.  A and P are formed by
+    ``_anchored_scores`` (plain products of gate-scaled operands, no reciprocals), which is
+    how the matrix-core path forms them; the chunk is padded to a multiple of 16 rows with
+    gates 1 and zero rows, which changes nothing."""
     q, k, v, beta, d, alpha_ch = (np.asarray(x, dtype=np.float64)
                                   for x in (q, k, v, beta, d, alpha_ch))
     B, H, T, dk = q.shape
@@ -134,17 +192,23 @@ def chunk_fwd_channel(q, k, v, beta, d, alpha_ch, S0=None, chunk: int = 64
             M = np.zeros((dk, dv)) if S0 is None else np.array(S0[b, h], dtype=np.float64)
             for c0 in range(0, T, chunk):
                 c1 = min(c0 + chunk, T)
-                G = np.cumprod(alpha_ch[b, h, c0:c1], axis=0)
-                Qp = q[b, h, c0:c1] * G
-                Kp = k[b, h, c0:c1] * G
-                Ktp = d[b, h, c0:c1] * k[b, h, c0:c1] / G
-                bet = beta[b, h, c0:c1]
                 n = c1 - c0
-                A = np.tril(bet[:, None] * (Kp @ Ktp.T), -1)
-                rhs = bet[:, None] * (v[b, h, c0:c1] - Kp @ M)
-                U = solve_triangular(np.eye(n) + A, rhs, lower=True, unit_diagonal=True)
-                o[b, h, c0:c1] = Qp @ M + np.tril(Qp @ Ktp.T) @ U
-                M = G[-1][:, None] * (M + Ktp.T @ U)
+                npad = -(-n // 16) * 16
+                pad = lambda x, fill=0.0: np.concatenate(
+                    [x, np.full((npad - n,) + x.shape[1:], fill)]) if npad > n else x
+                a = pad(alpha_ch[b, h, c0:c1], 1.0)
+                Q, K = pad(q[b, h, c0:c1]), pad(k[b, h, c0:c1])
+                Kt = pad(d[b, h, c0:c1] * k[b, h, c0:c1])
+                V = pad(v[b, h, c0:c1])
+                bet = pad(beta[b, h, c0:c1])
+                G = np.cumprod(a, axis=0)
+                rest = np.concatenate([np.cumprod(a[::-1], axis=0)[::-1][1:], np.ones((1, dk))])
+                A = np.tril(bet[:, None] * _anchored_scores(K, Kt, a), -1)
+                P = _anchored_scores(Q, Kt, a)
+                rhs = bet[:, None] * (V - (K * G) @ M)
+                U = solve_triangular(np.eye(npad) + A, rhs, lower=True, unit_diagonal=True)
+                o[b, h, c0:c1] = ((Q * G) @ M + P @ U)[:n]
+                M = G[-1][:, None] * M + (Kt * rest).T @ U
             S_T[b, h] = M
     return o, S_T
 

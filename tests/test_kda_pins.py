@@ -60,15 +60,23 @@ def test_pins_reject_mutant(kind):
     assert failed, f"mutant {kind} passed every pin"
 
 
-def test_chunk_model_equals_recurrence():
-    """The chunk algebra with operands pre-scaled per feature (q' = q G, k' = k G,
-    d' = d / G^2, G the running product of the gate inside the chunk) and the state's rows
-    scaled by the chunk's total decay after each carry, against the recurrence."""
+@pytest.mark.parametrize("gates", ["generator", "strong", "tiny", "mixed"])
+def test_chunk_model_equals_recurrence(gates):
+    """The chunk algebra with the gate folded into the operands by anchored products (every
+    factor a product of gates, no reciprocal; the form the matrix-core path uses) against the
+    recurrence, for gates from mild to 1e-30 (eq. 5 sets no lower bound on a_t)."""
     from oracle import chunkwise
     rng = np.random.default_rng(46)
     q, k, v, beta, d, a, S0 = pins.rand_kda(rng, 1, 2, 150, 8, 5)
+    if gates == "strong":
+        a = rng.uniform(0.05, 0.6, a.shape)
+    elif gates == "tiny":
+        a = rng.uniform(1e-30, 1e-20, a.shape)
+    elif gates == "mixed":
+        a = rng.uniform(0.5, 1.0, a.shape)
+        a[rng.random(a.shape) < 0.1] = 1e-35
     o_ref, S_ref = oracle.chunk_fwd(q, k, v, beta, d, None, S0, alpha_ch=a)
-    for chunk in (1, 16, 64):
+    for chunk in (1, 16, 64, 150):
         o, S = chunkwise.chunk_fwd_channel(q, k, v, beta, d, a, S0, chunk=chunk)
         assert np.max(np.abs(o - o_ref)) <= 1e-10 * np.max(np.abs(o_ref))
         assert np.max(np.abs(S - S_ref)) <= 1e-10 * np.max(np.abs(S_ref))
