@@ -268,9 +268,11 @@ namespace {
 
 int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
 
-// byte offsets of the channel-wise gate's workspace: q', k', d', G_C
+// byte offsets of the channel-wise gate's workspace (bf16 inputs): the gate-scaled q, k, k~
+// ([BH, T, dk] bf16 each), the chunk planes ([BH, nchunks, kda_planes::kElems] bf16) and G_C
+// ([BH, nchunks, dk] fp32).  fp32 inputs need none (the fp32 kernel forms the ratios itself).
 struct KdaLayout {
-    int64_t q, k, d, g, total;
+    int64_t q, k, kt, planes, g, total;
 };
 
 bool kda_layout(int64_t B, int64_t H, int64_t T, int32_t dk, int32_t chunk, osdn_dtype qkv,
@@ -282,15 +284,19 @@ bool kda_layout(int64_t B, int64_t H, int64_t T, int32_t dk, int32_t chunk, osdn
     if (!mul_ok(n, B, kMaxElems) || !mul_ok(n, H, kMaxElems) || !mul_ok(n, T, kMaxElems) ||
         !mul_ok(n, dk, kMaxElems))
         return false;
-    int64_t ng = 1;
+    int64_t ng = 1, np = 1;
     if (!mul_ok(ng, B, kMaxElems) || !mul_ok(ng, H, kMaxElems) ||
-        !mul_ok(ng, (T + chunk - 1) / chunk, kMaxElems) || !mul_ok(ng, dk, kMaxElems))
+        !mul_ok(ng, (T + chunk - 1) / chunk, kMaxElems))
         return false;
-    const int64_t eq = elem_size(qkv), ed = qkv == OSDN_BF16 ? 2 : 4;
-    L.q = 0;
-    L.k = round256(n * eq);
-    L.d = L.k + round256(n * eq);
-    L.g = L.d + round256(n * ed);
+    np = ng;
+    if (!mul_ok(ng, dk, kMaxElems) || !mul_ok(np, osdn::kda_planes::kElems, kMaxElems))
+        return false;
+    L = KdaLayout{};
+    if (qkv != OSDN_BF16) return true;
+    L.k = round256(n * 2);
+    L.kt = L.k + round256(n * 2);
+    L.planes = L.kt + round256(n * 2);
+    L.g = L.planes + round256(np * 2);
     L.total = L.g + round256(ng * 4);
     return true;
 }
@@ -326,10 +332,10 @@ osdn_status osdn_chunk_fwd_kda(const void *q, const void *k, const void *v, cons
     if (!mul_ok(st, int64_t(dk) * dv, kMaxElems)) return OSDN_ERR_SHAPE;
     if (BH > int64_t(0x7fffffff) / 4) return OSDN_ERR_SHAPE;
     const int64_t nchunks = (T + chunk - 1) / chunk;
-    if (BH * nchunks * (dk / 4) > int64_t(0x7fffffff) * 64) return OSDN_ERR_SHAPE;  // prep grid
+    if (BH * nchunks > int64_t(0x7fffffff)) return OSDN_ERR_SHAPE;  // planes grid
 
     if (BH == 0) return OSDN_OK;
-    if (T > 0 && (!q || !k || !v || !beta || !d || !alpha_ch || !o || !workspace))
+    if (T > 0 && (!q || !k || !v || !beta || !d || !alpha_ch || !o || (W.total > 0 && !workspace)))
         return OSDN_ERR_NULL;
     if (T == 0 && !S_T) return OSDN_OK;
     if (T > 0 && workspace_bytes < W.total) return OSDN_ERR_SHAPE;
@@ -338,7 +344,7 @@ osdn_status osdn_chunk_fwd_kda(const void *q, const void *k, const void *v, cons
     if (T > 0) {
         if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(d, 16) ||
             !aligned(o, 16) || !aligned(beta, 4) || !aligned(alpha_ch, 16) ||
-            !aligned(workspace, 256))
+            (W.total > 0 && !aligned(workspace, 256)))
             return OSDN_ERR_ALIGN;
     }
     if ((S0 && !aligned(S0, 16)) || (S_T && !aligned(S_T, 16))) return OSDN_ERR_ALIGN;
@@ -359,18 +365,29 @@ osdn_status osdn_chunk_fwd_kda(const void *q, const void *k, const void *v, cons
         if (overlap(rw, *in)) return OSDN_ERR_ALIAS;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    char *ws = static_cast<char *>(workspace);
-    float *gcs = T > 0 ? reinterpret_cast<float *>(ws + W.g) : nullptr;
-    const osdn_dtype dp_dtype = qkv == OSDN_BF16 ? OSDN_BF16 : OSDN_F32;
-    if (T > 0) {
-        osdn::KdaPrepArgs p{q, k, d, alpha_ch, ws + W.q, ws + W.k, ws + W.d, gcs, BH, T,
-                            nchunks, dk, chunk, qkv, d_dtype};
-        if (osdn::launch_kda_prep(p, s) != hipSuccess) return OSDN_ERR_LAUNCH;
+    if (qkv != OSDN_BF16) {  // fp32: the kernel forms the exact per-feature ratios itself
+        osdn::ChunkArgs a{q, k, v, d, beta, nullptr, S0, o, S_T, BH, T, dk, dv, chunk, qkv,
+                          d_dtype};
+        a.alpha_ch = alpha_ch;
+        const hipError_t err = osdn::launch_chunk_fwd_f32math(a, s);
+        return err == hipSuccess ? OSDN_OK : OSDN_ERR_LAUNCH;
     }
-    osdn::ChunkArgs a{T > 0 ? ws + W.q : q, T > 0 ? ws + W.k : k, v, T > 0 ? ws + W.d : d,
-                      beta, nullptr, S0, o, S_T, BH, T, dk, dv, chunk, qkv, dp_dtype, gcs};
-    const hipError_t err = qkv == OSDN_BF16 ? osdn::launch_chunk_fwd_mfma(a, s)
-                                            : osdn::launch_chunk_fwd_f32math(a, s);
+    if (T == 0) {  // S_T = S0 (or 0)
+        osdn::ChunkArgs a{q, k, v, d, beta, nullptr, S0, o, S_T, BH, T, dk, dv, chunk, qkv,
+                          d_dtype};
+        const hipError_t err = osdn::launch_chunk_fwd_mfma(a, s);
+        return err == hipSuccess ? OSDN_OK : OSDN_ERR_LAUNCH;
+    }
+    char *ws = static_cast<char *>(workspace);
+    float *gcs = reinterpret_cast<float *>(ws + W.g);
+    uint16_t *planes = reinterpret_cast<uint16_t *>(ws + W.planes);
+    osdn::KdaPrepArgs p{q, k, d, alpha_ch, beta, ws + W.q, ws + W.k, ws + W.kt, planes, gcs,
+                        BH, T, nchunks, dk, d_dtype};
+    if (osdn::launch_kda_planes(p, s) != hipSuccess) return OSDN_ERR_LAUNCH;
+    osdn::ChunkArgs a{ws + W.q, ws + W.k, v, ws + W.kt, beta, nullptr, S0, o, S_T, BH, T, dk,
+                      dv, chunk, qkv, OSDN_BF16, gcs};
+    a.planes = planes;
+    const hipError_t err = osdn::launch_chunk_fwd_mfma(a, s);
     return err == hipSuccess ? OSDN_OK : OSDN_ERR_LAUNCH;
 }
 

@@ -16,8 +16,13 @@
 //
 // Rows past the end of the sequence are zero (beta = 0, alpha = 1), so they add nothing.
 // For the backward the kernel can also record the state at every chunk start (and skip o).
-// With the channel-wise gate the caller passes pre-scaled q, k, d and per-chunk factors G_C,
-// and the state's rows are multiplied by G_C after each carry.
+// With the channel-wise gate a_t in R^dk (GATE; Erase-then-Delta Attention, section 2.2,
+// eq. 5) the decay is per key feature: Lg_r = sum_{t<=r} ln a_t per feature, kept in double
+// precision, and every ratio the chunk needs is formed exactly as e^{Lg_r - Lg_s} <= 1:
+//   A[r][s] = beta_r sum_i k_ri k~_si e^{Lg_ri - Lg_si},  P[r][s] = sum_i q_ri k~_si e^{...},
+//   R = diag(beta) (V - (K o e^{Lg}) M),  O = (Q o e^{Lg}) M + P U,
+//   M <- Diag(e^{Lg_C}) M + (K~ o e^{Lg_C - Lg})^T U.
+// A gate of 0 is taken as e^{-690}, which rounds every ratio across it to 0 in fp32.
 #include "osdn_internal.h"
 
 namespace osdn {
@@ -25,13 +30,13 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <int DK, int BV, int CH, typename TQ, typename TD>
+template <int DK, int BV, int CH, typename TQ, typename TD, bool GATE>
 __global__ void __launch_bounds__(kThreads)
 chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
                      const TQ *__restrict__ v, const TD *__restrict__ d,
                      const float *__restrict__ beta, const float *__restrict__ alpha,
                      const float *S0, TQ *__restrict__ o, float *S_T, int64_t T, int dv,
-                     const float *__restrict__ gcs, float *__restrict__ ckpt) {
+                     float *__restrict__ ckpt) {
     constexpr int PX = DK + 1;  // padded row pitches (bank-conflict relief)
     constexpr int PC = CH + 1;
     constexpr int PV = BV + 1;
@@ -47,6 +52,14 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
     __shared__ float sb[CH];        // beta
     __shared__ float sgam[CH];      // e^{g_r}
     __shared__ float sdec[CH];      // e^{g_C - g_r}
+    __shared__ double sLg[GATE ? CH * PX : 1];  // channel-wise gate: Lg per row and feature
+    // e^{Lg_r - Lg_s} of key feature i (channel-wise gate)
+    auto ratio = [&](int r, int s_, int i) __attribute__((always_inline)) {
+        return expf(static_cast<float>(sLg[r * PX + i] - sLg[s_ * PX + i]));
+    };
+    auto decay = [&](int r, int i) __attribute__((always_inline)) {  // e^{Lg_r}
+        return expf(static_cast<float>(sLg[r * PX + i]));
+    };
 
     const int ntiles = dv / BV;
     const int64_t bh = blockIdx.x / ntiles;
@@ -87,7 +100,22 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
         }
         if (tid < CH) {
             sb[tid] = tid < n ? beta[row0 + tid] : 0.f;
-            sg[tid] = (tid < n && alpha) ? logf(alpha[row0 + tid]) : 0.f;
+            sg[tid] = (tid < n && alpha && !GATE) ? logf(alpha[row0 + tid]) : 0.f;
+        }
+        if constexpr (GATE) {
+            for (int idx = tid; idx < CH * DK; idx += kThreads) {
+                const int r = idx / DK, i = idx % DK;
+                sLg[r * PX + i] =
+                    r < n ? log(fmax(static_cast<double>(alpha[(row0 + r) * DK + i]), 1e-300)) : 0.0;
+            }
+            __syncthreads();
+            if (tid < DK) {  // running sums down each feature column
+                double acc = 0.0;
+                for (int r = 0; r < CH; ++r) {
+                    acc += sLg[r * PX + tid];
+                    sLg[r * PX + tid] = acc;
+                }
+            }
         }
         __syncthreads();
         if (tid == 0) {
@@ -110,8 +138,13 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
             float val = 0.f;
             if (s < r) {
                 float dot = 0.f;
-                for (int i = 0; i < DK; ++i) dot += sX[r * PX + i] * sKt[s * PX + i];
-                val = sb[r] * __expf(sg[r] - sg[s]) * dot;
+                if constexpr (GATE) {
+                    for (int i = 0; i < DK; ++i) dot += sX[r * PX + i] * sKt[s * PX + i] * ratio(r, s, i);
+                    val = sb[r] * dot;
+                } else {
+                    for (int i = 0; i < DK; ++i) dot += sX[r * PX + i] * sKt[s * PX + i];
+                    val = sb[r] * __expf(sg[r] - sg[s]) * dot;
+                }
             }
             sA[r * PC + s] = val;
         }
@@ -138,7 +171,11 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
             for (int idx = tid - CH; idx < CH * BV; idx += kThreads - CH) {
                 const int r = idx / BV, j = idx % BV;
                 float km = 0.f;
-                for (int i = 0; i < DK; ++i) km += sX[r * PX + i] * sM[i * PV + j];
+                if constexpr (GATE) {
+                    for (int i = 0; i < DK; ++i) km += sX[r * PX + i] * decay(r, i) * sM[i * PV + j];
+                } else {
+                    for (int i = 0; i < DK; ++i) km += sX[r * PX + i] * sM[i * PV + j];
+                }
                 sR[r * PV + j] = sb[r] * (sR[r * PV + j] - sgam[r] * km);
             }
         }
@@ -163,15 +200,24 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
             float val = 0.f;
             if (s <= r) {
                 float dot = 0.f;
-                for (int i = 0; i < DK; ++i) dot += sX[r * PX + i] * sKt[s * PX + i];
-                val = __expf(sg[r] - sg[s]) * dot;
+                if constexpr (GATE) {
+                    for (int i = 0; i < DK; ++i) dot += sX[r * PX + i] * sKt[s * PX + i] * ratio(r, s, i);
+                    val = dot;
+                } else {
+                    for (int i = 0; i < DK; ++i) dot += sX[r * PX + i] * sKt[s * PX + i];
+                    val = __expf(sg[r] - sg[s]) * dot;
+                }
             }
             sA[r * PC + s] = val;
         }
         for (int idx = tid; idx < CH * BV; idx += kThreads) {
             const int r = idx / BV, j = idx % BV;
             float qm = 0.f;
-            for (int i = 0; i < DK; ++i) qm += sX[r * PX + i] * sM[i * PV + j];
+            if constexpr (GATE) {
+                for (int i = 0; i < DK; ++i) qm += sX[r * PX + i] * decay(r, i) * sM[i * PV + j];
+            } else {
+                for (int i = 0; i < DK; ++i) qm += sX[r * PX + i] * sM[i * PV + j];
+            }
             sQM[r * PV + j] = qm;
         }
         __syncthreads();
@@ -189,11 +235,15 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
         for (int idx = tid; idx < DK * BV; idx += kThreads) {
             const int i = idx / BV, j = idx % BV;
             float acc = 0.f;
-            for (int s = 0; s < CH; ++s)
-                acc += sdec[s] * sKt[s * PX + i] * sU[s * PV + j];
-            const float mv = gam_last * sM[i * PV + j] + acc;
-            // channel-wise gate: the state's rows times the chunk's G_C
-            sM[i * PV + j] = gcs ? gcs[(bh * ((T + CH - 1) / CH) + c0 / CH) * DK + i] * mv : mv;
+            if constexpr (GATE) {
+                for (int s = 0; s < CH; ++s)
+                    acc += ratio(CH - 1, s, i) * sKt[s * PX + i] * sU[s * PV + j];
+                sM[i * PV + j] = decay(CH - 1, i) * sM[i * PV + j] + acc;
+            } else {
+                for (int s = 0; s < CH; ++s)
+                    acc += sdec[s] * sKt[s * PX + i] * sU[s * PV + j];
+                sM[i * PV + j] = gam_last * sM[i * PV + j] + acc;
+            }
         }
     }
     __syncthreads();
@@ -210,11 +260,19 @@ hipError_t launch_typed(const ChunkArgs &a, hipStream_t stream) {
     constexpr int BV = 32;
     const int ntiles = a.dv / BV;
     const dim3 grid(static_cast<unsigned>(a.BH * ntiles));
-    hipLaunchKernelGGL((chunk_f32math_kernel<DK, BV, CH, TQ, TD>), grid, dim3(kThreads), 0,
-                       stream, static_cast<const TQ *>(a.q), static_cast<const TQ *>(a.k),
-                       static_cast<const TQ *>(a.v), static_cast<const TD *>(a.d), a.beta,
-                       a.alpha, a.S0, static_cast<TQ *>(a.o), a.S_T, a.T, a.dv, a.gcs,
-                       static_cast<float *>(a.ckpt));
+    if (a.alpha_ch) {  // the per-feature log sums need LDS: at most 32 rows per chunk
+        constexpr int CG = CH < 32 ? CH : 32;
+        hipLaunchKernelGGL((chunk_f32math_kernel<DK, BV, CG, TQ, TD, true>), grid, dim3(kThreads),
+                           0, stream, static_cast<const TQ *>(a.q), static_cast<const TQ *>(a.k),
+                           static_cast<const TQ *>(a.v), static_cast<const TD *>(a.d), a.beta,
+                           a.alpha_ch, a.S0, static_cast<TQ *>(a.o), a.S_T, a.T, a.dv, nullptr);
+    } else {
+        hipLaunchKernelGGL((chunk_f32math_kernel<DK, BV, CH, TQ, TD, false>), grid,
+                           dim3(kThreads), 0, stream, static_cast<const TQ *>(a.q),
+                           static_cast<const TQ *>(a.k), static_cast<const TQ *>(a.v),
+                           static_cast<const TD *>(a.d), a.beta, a.alpha, a.S0,
+                           static_cast<TQ *>(a.o), a.S_T, a.T, a.dv, static_cast<float *>(a.ckpt));
+    }
     return hipGetLastError();
 }
 

@@ -33,9 +33,11 @@
 //   k~ = d (.) k of those rows; d reaches their registers one step ahead.
 // * The loader wave (6) brings q and v of chunk c+2 into LDS.  Prep wave 2 runs chunk c+2's
 //   decay scan after its tiles: its LDS writes then never queue behind an LDS DMA of its own.
-// With the channel-wise gate (the caller passes pre-scaled q, k, d and per-chunk factors G_C)
-// the state waves also multiply the state's rows by G_C after each carry; the loader brings
-// G_C into LDS with the other loads of its chunk.  For the backward a variant records the state
+// With the channel-wise gate (GATE) the caller passes the gate-scaled q o G, k o G and
+// k~ o (G_C / G), each chunk's product of gates G_C and its planes (P, the diagonal-block
+// inverses, -A_ik) from the planes kernel: the stagers copy k~ in instead of forming it, prep
+// wave 3 copies the planes in instead of forming them, and the carry scales the state's rows
+// by G_C; the loader brings G_C into LDS with the other loads of its chunk.  For the backward a variant records the state
 // at every chunk start (CKPT), with or without writing o (OUT).
 // Loads stall the issuing wave while HBM drains them, and too many in flight at once thrash
 // the CU's load queues; so they are issued in groups of at most 16 by waves whose other work
@@ -103,6 +105,14 @@ struct alignas(16) Lds {
     alignas(16) uint16_t ntile[NBLK][16 * 16];  // N of diagonal block kb, rows by blk (prep)
 };
 
+static_assert(Lds<128>::CP == kda_planes::kPPitch && Lds<64>::CP == kda_planes::kPPitch,
+              "P pitch shared with the channel-gate planes");
+static_assert(sizeof(Lds<128>::dinv[0]) == 2 * kda_planes::kDinv &&
+              sizeof(Lds<128>::aneg[0]) == 2 * kda_planes::kAneg &&
+              sizeof(Lds<128>::p[0]) == 2 * kda_planes::kP, "plane sizes");
+static_assert(Lds<128>::blk(9, 1) == kda_planes::blk(9, 1) && Lds<64>::blk(3, 2) == kda_planes::blk(3, 2),
+              "block layout shared with the channel-gate planes");
+
 // Prep wave pw owns the Gram/score column blocks kblk(pw, 0), kblk(pw, 1)
 __host__ __device__ constexpr int kblk(int pw, int j) { return pw == 0 ? (j == 0 ? 0 : 3) : (j == 0 ? 1 : 2); }
 
@@ -134,6 +144,35 @@ __device__ __forceinline__ void load_rows(uint16_t *dst, const uint16_t *src, in
         const int base = R0 * L::KU + i * 64;  // physical unit of lane 0
         const int pu = base + lane, r = pu / L::KU, lu = (pu % L::KU) ^ L::fqk(r);
         load_to_lds16(src + (row0 + min(r, n - 1)) * DK + 8 * lu, dst + 8 * base);
+        if (i % 8 == 7 && i + 1 < NLOAD) wait_global8();
+    }
+}
+
+// rows [R0, R0 + NR) of a row-major bf16 k~ tile into the k~ buffer (16-byte units swizzled by
+// pk(r), the layout the stagers otherwise write): channel-wise gate, where k~ arrives pre-scaled
+template <int DK, int R0, int NR>
+__device__ __forceinline__ void load_kt_rows(uint16_t *dst, const uint16_t *src, int64_t row0, int n,
+                                             int lane) {
+    using L = Lds<DK>;
+    constexpr int NLOAD = NR * L::KU / 64;
+    static_assert(NR * L::KU % 64 == 0, "whole wave-loads");
+#pragma unroll
+    for (int i = 0; i < NLOAD; ++i) {
+        const int base = R0 * L::KU + i * 64;
+        const int pu = base + lane, r = pu / L::KU, lu = (pu % L::KU) ^ L::pk(r);
+        load_to_lds16(src + (row0 + min(r, n - 1)) * DK + 8 * lu, dst + 8 * base);
+        if (i % 8 == 7 && i + 1 < NLOAD) wait_global8();
+    }
+}
+
+// n16 16-byte units of a contiguous image into LDS (one wave, at most 16 loads in flight)
+template <int N16>
+__device__ __forceinline__ void copy_image(uint16_t *dst, const uint16_t *src, int lane) {
+    constexpr int NLOAD = (N16 + 63) / 64;
+#pragma unroll
+    for (int i = 0; i < NLOAD; ++i) {
+        if (N16 % 64 == 0 || i + 1 < NLOAD || lane < N16 % 64)
+            load_to_lds16(src + 8 * (64 * i + lane), dst + 8 * 64 * i);
         if (i % 8 == 7 && i + 1 < NLOAD) wait_global8();
     }
 }
@@ -264,7 +303,7 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                   const float *__restrict__ beta, const float *__restrict__ alpha,
                   const float *S0, uint16_t *__restrict__ o, float *S_T, int64_t BH,
                   int64_t T, int dv, const float *__restrict__ gcs, uint16_t *__restrict__ ckpt,
-                  uint16_t *__restrict__ uout) {
+                  uint16_t *__restrict__ uout, const uint16_t *__restrict__ planes) {
     using L = Lds<DK, GATE>;
     constexpr int NS = DK / 32;   // 32-wide k-steps over the key features
     constexpr int NFT = DK / 16;  // 16-row feature tiles of the state
@@ -420,7 +459,11 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                 const v8s uwb0 = c_to_frag(w4[0] * U[0], w4[1] * U[1]);
                 v4f acc[NFT], oacc[NBLK];
 #pragma unroll
-                for (int ft = 0; ft < NFT; ++ft) acc[ft] = mfma32(kt_frag(ft, 0), uwb0, gC * M[ft]);
+                for (int ft = 0; ft < NFT; ++ft) {
+                    // channel-wise gate: the state's rows times the chunk's G_C (gam = 1 there)
+                    const v4f m0 = GATE ? ld4(&sm.gc[sl][16 * ft + 4 * lq]) * M[ft] : gC * M[ft];
+                    acc[ft] = mfma32(kt_frag(ft, 0), uwb0, m0);
+                }
 #pragma unroll
                 for (int rt = 0; rt < NBLK; ++rt) oacc[rt] = mfma32(ub0, pf[rt][0], gtok[rt] * Z[rt]);
                 solve(2);
@@ -444,10 +487,6 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                 }
 #pragma unroll
                 for (int ft = 0; ft < NFT; ++ft) M[ft] = mfma32(kt_frag(ft, 1), uwb1, acc[ft]);
-                if constexpr (GATE) {  // channel-wise gate: the state's rows times the chunk's G_C
-#pragma unroll
-                    for (int ft = 0; ft < NFT; ++ft) M[ft] *= ld4(&sm.gc[sl][16 * ft + 4 * lq]);
-                }
                 // read-out O^T = (M^T Q^T) diag(gam) + U^T P^T: lane holds O[16rt+lr][4 columns];
                 // rows past the chunk's last valid row fall outside the buffer range and are
                 // dropped by the store
@@ -518,6 +557,38 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
             }
         }
         return;
+    }
+
+    if constexpr (GATE) {
+        if (wave == 4 || wave == 5) {
+            // ---- stager waves (channel-wise gate): the gate-scaled k rows of chunk c+2 into the
+            // k buffer and its gate-scaled k~ rows (passed in d) into the k~ buffer ------------
+            const uint16_t *ktg = reinterpret_cast<const uint16_t *>(d);
+            auto gstager = [&](auto h_c) __attribute__((always_inline)) {
+                constexpr int H = decltype(h_c)::value;
+                auto stage_step = [&](auto par_c, int64_t cc, int slot) __attribute__((always_inline)) {
+                    constexpr int PAR = decltype(par_c)::value;  // cc mod 2
+                    if (cc < nchunks) {
+                        load_rows<DK, 32 * H, 32>(k_buf[PAR], k, seq0 + cc * CH, rows_of(cc), lane);
+                        load_kt_rows<DK, 32 * H, 32>(sm.kt[slot], ktg, seq0 + cc * CH, rows_of(cc), lane);
+                        wait_global();
+                    }
+                    block_sync();
+                };
+                int sl2 = 0;  // (c+2) mod 3
+                for (int64_t c = -2; c < nchunks; c += 2) {
+                    stage_step(I0{}, c + 2, sl2);
+                    sl2 = sl2 == 2 ? 0 : sl2 + 1;
+                    if (c + 1 < nchunks) {
+                        stage_step(I1{}, c + 3, sl2);
+                        sl2 = sl2 == 2 ? 0 : sl2 + 1;
+                    }
+                }
+            };
+            if (wave == 4) gstager(I0{});
+            else gstager(I1{});
+            return;
+        }
     }
 
     if (wave == 4 || wave == 5) {
@@ -703,7 +774,22 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
         if (PW == 0 && nchunks > 0) load_ba(0);
         int sl1 = 2;  // (c+1) mod 3; (c+2) mod 3 is the slot after it
         for (int64_t c = -2; c < nchunks; ++c) {
-            prep_step(pw_c, c, sl1);
+            if constexpr (!GATE) {
+                prep_step(pw_c, c, sl1);
+            } else if constexpr (PW == 1) {
+                // channel-wise gate: chunk c+1's planes (P, the block inverses, -A_ik) are
+                // copied in as formed by the planes kernel
+                namespace KP = kda_planes;
+                const int64_t c1 = c + 1;
+                if (c1 >= 0 && c1 < nchunks) {
+                    const int b1 = static_cast<int>(c1 & 1);
+                    const uint16_t *img = planes + (bh * nchunks + c1) * KP::kElems;
+                    copy_image<KP::kP / 8>(sm.p[b1], img, lane);
+                    copy_image<KP::kDinv / 8>(sm.dinv[b1], img + KP::kP, lane);
+                    copy_image<KP::kAneg / 8>(sm.aneg[b1], img + KP::kP + KP::kDinv, lane);
+                    wait_global();
+                }
+            }
             if constexpr (PW == 0) {
                 const int64_t cc = c + 2;
                 if (cc < nchunks) {
@@ -730,7 +816,8 @@ hipError_t launch_typed(const ChunkArgs &a, hipStream_t stream) {
                        static_cast<const uint16_t *>(a.k), static_cast<const uint16_t *>(a.v), \
                        static_cast<const TD *>(a.d), a.beta, a.alpha, a.S0,                    \
                        static_cast<uint16_t *>(a.o), a.S_T, a.BH, a.T, a.dv, a.gcs,            \
-                       static_cast<uint16_t *>(a.ckpt), static_cast<uint16_t *>(a.uout))
+                       static_cast<uint16_t *>(a.ckpt), static_cast<uint16_t *>(a.uout),       \
+                       a.planes)
     if (a.gcs) OSDN_CHUNK_LAUNCH(true, false, true);
     else if (a.ckpt && a.o) OSDN_CHUNK_LAUNCH(false, true, true);
     else if (a.ckpt) OSDN_CHUNK_LAUNCH(false, true, false);
@@ -742,6 +829,8 @@ hipError_t launch_typed(const ChunkArgs &a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_chunk_fwd_mfma(const ChunkArgs &a, hipStream_t stream) {
+    if (a.gcs)  // channel-wise gate: d carries the gate-scaled k~ (bf16)
+        return a.dk == 64 ? launch_typed<64, bf16_t>(a, stream) : launch_typed<128, bf16_t>(a, stream);
     if (a.dk == 64)
         return a.d_dtype == OSDN_F32 ? launch_typed<64, float>(a, stream)
                                      : launch_typed<64, bf16_t>(a, stream);

@@ -40,8 +40,12 @@ struct ChunkArgs {
     int64_t BH, T;
     int32_t dk, dv, chunk;
     osdn_dtype qkv, d_dtype;
-    const float *gcs = nullptr;  // [BH, nchunks, dk]: per-feature factor applied to the
-                                 // state's rows after each chunk's carry (channel-wise gate)
+    const float *gcs = nullptr;  // channel-wise gate, [BH, nchunks, dk]: G_C, the product of
+                                 // the chunk's gates, applied to the state's rows in the carry.
+                                 // The matrix-core forward then takes q, k, d as the gate-scaled
+                                 // q o G, k o G, k~ o (G_C / G) (bf16) and the chunk planes
+    const uint16_t *planes = nullptr;  // [BH, nchunks, kda_planes::kElems] (matrix-core, gate)
+    const float *alpha_ch = nullptr;   // fp32 forward: the channel-wise gate [BH, T, dk]
     void *ckpt = nullptr;        // [BH, nchunks, dk, dv]: the state at every chunk start, fp32
                                  // from the fp32 forward, bf16 from the matrix-core forward
                                  // (o may then be NULL: not written; no channel gate)
@@ -73,14 +77,30 @@ struct BwdArgs {
     osdn_dtype qkv, d_dtype;
 };
 
+// The channel-wise gate's planes of one 64-row chunk (bf16 inputs): the chunk's score matrix P
+// and the pieces of its UT transform, bf16, laid out exactly as the matrix-core forward keeps
+// them in LDS, so that it copies them in unchanged.
+namespace kda_planes {
+constexpr int kRows = 64;
+constexpr int kPPitch = kRows + 8;           // row pitch (bf16) of P
+constexpr int kP = kRows * kPPitch;          // P: row-major, zero above the diagonal
+constexpr int kDinv = 4 * 256;               // (I + A_ii)^{-1}, i = 0..3: 16 x 16 blocks
+constexpr int kAneg = 6 * 256;               // -A_ik, (i, k) = (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+constexpr int kElems = kP + kDinv + kAneg;   // bf16 per chunk
+// element (r, 4 g + e) of a 16 x 16 block: 8-byte granule g of row r sits at granule
+// g ^ 2 ((r >> 3) & 1), so 16-lane reads of four-element granules touch distinct banks
+__host__ __device__ constexpr int blk(int r, int g) { return r * 16 + 4 * (g ^ (((r >> 3) & 1) << 1)); }
+}  // namespace kda_planes
+
 struct KdaPrepArgs {
     const void *q, *k, *d;
-    const float *alpha_ch;
-    void *qp, *kp, *dp;  // workspace: q', k' (qkv dtype), d' (bf16 for OSDN_BF16, else fp32)
-    float *gcs;          // workspace: [BH, nchunks, dk]
+    const float *alpha_ch, *beta;
+    void *qp, *kp, *ktp;  // workspace [BH, T, dk] bf16: q o G, k o G, k~ o (G_C / G)
+    uint16_t *planes;     // workspace [BH, nchunks, kda_planes::kElems] bf16
+    float *gcs;           // workspace [BH, nchunks, dk]: G_C
     int64_t BH, T, nchunks;
-    int32_t dk, chunk;
-    osdn_dtype qkv, d_dtype;
+    int32_t dk;
+    osdn_dtype d_dtype;
 };
 
 struct StepArgs {
@@ -110,7 +130,7 @@ hipError_t launch_chunk_fwd_f32math(const ChunkArgs &a, hipStream_t stream);
 hipError_t launch_chunk_fwd_mfma(const ChunkArgs &a, hipStream_t stream);
 hipError_t launch_step(const StepArgs &a, hipStream_t stream);
 hipError_t launch_precond(const PrecondArgs &a, hipStream_t stream);
-hipError_t launch_kda_prep(const KdaPrepArgs &a, hipStream_t stream);
+hipError_t launch_kda_planes(const KdaPrepArgs &a, hipStream_t stream);
 hipError_t launch_step_kda(const StepArgs &a, hipStream_t stream);  // alpha: [BH, dk]
 hipError_t launch_chunk_bwd(const BwdArgs &a, hipStream_t stream);
 int32_t bwd_chunk_size(osdn_dtype qkv);  // rows per chunk of the backward

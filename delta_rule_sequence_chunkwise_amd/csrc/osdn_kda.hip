@@ -4,16 +4,30 @@
 //
 //   M_t = Diag(a_t) M_{t-1} + b_t k~_t (v_t - (Diag(a_t) M_{t-1})^T k_t)^T ,   o_t = M_t^T q_t
 //
-// Chunkwise, the decay folds into the operands.  Inside a chunk let G_r = prod_{s<=r} a_s (per
-// key feature, inclusive).  Unrolling the step gives M_r = Diag(G_r) M0 + sum_{s<=r}
-// Diag(G_r / G_s) k~_s u_s^T, so with  q' = q G,  k' = k G,  d' = d / G^2  (hence
-// k~' = d' k' = k~ / G) the chunk is the undecayed chunk algebra on (q', k', d'), except that
-// the carried state becomes  Diag(G_C) (M0 + K~'^T U)  -- the forward kernels take G_C per
-// chunk and scale the state's rows after each carry.  kda_prep_kernel writes q', k', d' and
-// G_C into a workspace (one thread per four consecutive features of a chunk, 8- and 16-byte
-// accesses); it is bound by HBM bandwidth.  G is clamped at 2^-60 inside 1/G^2,
-// so a chunk whose product of gates on a feature falls below that is computed as if it were
-// 2^-60 there.
+// Chunkwise (derived here; the pages give no chunk form), with G_r = prod_{t<=r} a_t from the
+// chunk start and rho(s->r) = prod_{s<t<=r} a_t, per key feature:
+//
+//   (I + A) U = diag(b) (V - (K o G) M0),   A[r,s] = b_r sum_f k_rf k~_sf rho_f(s->r)  (s < r)
+//   O = (Q o G) M0 + P U,                   P[r,s] = sum_f q_rf k~_sf rho_f(s->r)      (s <= r)
+//   M_C = Diag(G_C) M0 + (K~ o rho(.->C))^T U
+//
+// The ratio rho sits inside the dk-long inner products, so it is folded into the operands of the
+// matrix products -- as products of gates only, each at most 1, never as G_r / G_s (a running
+// product from the chunk start underflows after a few strong gates, and its reciprocal then
+// overflows).  Pairs (r, s) in different 16-row blocks i > j are anchored at the last row e of
+// block j: x_r = prod_{e<t<=r} a_t, y_s = prod_{s<t<=e} a_t.  Inside a block, the pair falls
+// into different halves of one 2h-row segment for exactly one h in {8, 4, 2, 1}, and is anchored
+// at the boundary of those halves; one product per h covers all such pairs, and its other
+// entries are dropped.  The diagonal takes factor 1.  The segment products come level by level
+// from the sibling segment's total (a lane swap), so no factor is ever divided.
+//
+// kda_planes_kernel does this for every chunk in parallel (one workgroup of four waves per
+// chunk, wave i on rows 16i..16i+15, lane (row, quarter) holding 8 features of each 32-wide
+// k-step in registers, which is both the A and the B layout of the 16x16x32 products), and
+// writes for the forward: q o G, k o G, k~ o rho(.->C) (bf16), G_C, and the chunk planes -- P,
+// the diagonal-block inverses (I + A_ii)^{-1} (by substitution in fp32, rounded once) and -A_ik
+// (bf16, in the forward's LDS layout).  The matrix-core forward's GATE variant copies these in
+// instead of forming them.  (The fp32 path forms the exact ratios itself; see the fp32 kernel.)
 //
 // The decode step applies Diag(a) to the state's rows in place of the scalar gate.
 #include "osdn_internal.h"
@@ -22,54 +36,269 @@
 namespace osdn {
 namespace {
 
-constexpr float kMinGate = 0x1p-60f;
+constexpr int kPlanesThreads = 256;
 
-// four consecutive elements as fp32 (16 bytes of fp32, 8 bytes of bf16)
-__device__ __forceinline__ float4 load4f(const float *p) { return *reinterpret_cast<const float4 *>(p); }
-__device__ __forceinline__ float4 load4f(const bf16_t *p) {
-    const uint2 u = *reinterpret_cast<const uint2 *>(p);
-    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+// 8 consecutive inputs as fp32
+__device__ __forceinline__ void load8(const float *p, float *o) {
+    const float4 a = *reinterpret_cast<const float4 *>(p), b = *reinterpret_cast<const float4 *>(p + 4);
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
 }
-__device__ __forceinline__ void store4f(float *p, float4 x) { *reinterpret_cast<float4 *>(p) = x; }
-__device__ __forceinline__ void store4f(bf16_t *p, float4 x) {
-    *reinterpret_cast<uint2 *>(p) = make_uint2(
-        uint32_t(f32_to_bf16_bits(x.x)) | (uint32_t(f32_to_bf16_bits(x.y)) << 16),
-        uint32_t(f32_to_bf16_bits(x.z)) | (uint32_t(f32_to_bf16_bits(x.w)) << 16));
-}
-
-constexpr int kPrepThreads = 256;
-
-// thread -> (sequence, chunk, four consecutive features); it walks the chunk's rows
-template <int DK, typename TQ, typename TDI, typename TDO>
-__global__ void __launch_bounds__(kPrepThreads)
-kda_prep_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k, const TDI *__restrict__ d,
-                const float *__restrict__ a, TQ *__restrict__ qp, TQ *__restrict__ kp,
-                TDO *__restrict__ dp, float *__restrict__ gcs, int64_t T, int chunk,
-                int64_t nchunks, int64_t total) {
-    constexpr int QPR = DK / 4;  // feature quads per row
-    const int64_t g = int64_t(blockIdx.x) * kPrepThreads + threadIdx.x;
-    if (g >= total) return;
-    const int64_t seg = g / QPR;  // (sequence, chunk)
-    const int f = static_cast<int>(g % QPR) * 4;
-    const int64_t bh = seg / nchunks, c = seg % nchunks;
-    const int64_t t0 = c * chunk;
-    const int n = static_cast<int>(T - t0 < chunk ? T - t0 : chunk);
-    const int64_t base = (bh * T + t0) * DK + f;
-    float4 G = make_float4(1.f, 1.f, 1.f, 1.f);
-#pragma unroll 4
-    for (int r = 0; r < n; ++r) {
-        const int64_t i = base + int64_t(r) * DK;
-        const float4 av = load4f(a + i), qv = load4f(q + i), kv = load4f(k + i), dv = load4f(d + i);
-        G.x *= av.x; G.y *= av.y; G.z *= av.z; G.w *= av.w;
-        store4f(qp + i, make_float4(qv.x * G.x, qv.y * G.y, qv.z * G.z, qv.w * G.w));
-        store4f(kp + i, make_float4(kv.x * G.x, kv.y * G.y, kv.z * G.z, kv.w * G.w));
-        const float gx = fmaxf(G.x, kMinGate), gy = fmaxf(G.y, kMinGate);
-        const float gz = fmaxf(G.z, kMinGate), gw = fmaxf(G.w, kMinGate);
-        store4f(dp + i, make_float4(dv.x / (gx * gx), dv.y / (gy * gy), dv.z / (gz * gz),
-                                    dv.w / (gw * gw)));
+__device__ __forceinline__ void load8(const bf16_t *p, float *o) {
+    const uint4 u = *reinterpret_cast<const uint4 *>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        o[2 * e] = bf_lo(w[e]);
+        o[2 * e + 1] = bf_hi(w[e]);
     }
-    store4f(gcs + seg * DK + f, G);
+}
+__device__ __forceinline__ void load8(const uint16_t *p, float *o) {
+    load8(reinterpret_cast<const bf16_t *>(p), o);
+}
+// 8 fp32 products x * f rounded to one bf16 fragment
+__device__ __forceinline__ v8s frag8(const float *x, const float *f) {
+    return __builtin_bit_cast(v8s, make_uint4(pack2(x[0] * f[0], x[1] * f[1]), pack2(x[2] * f[2], x[3] * f[3]),
+                                              pack2(x[4] * f[4], x[5] * f[5]), pack2(x[6] * f[6], x[7] * f[7])));
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+template <int DK, typename TD>
+__global__ void __launch_bounds__(kPlanesThreads)
+kda_planes_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                  const TD *__restrict__ d, const float *__restrict__ a,
+                  const float *__restrict__ beta, uint16_t *__restrict__ qp,
+                  uint16_t *__restrict__ kp, uint16_t *__restrict__ ktp,
+                  uint16_t *__restrict__ planes, float *__restrict__ gcs, int64_t T,
+                  int64_t nchunks) {
+    namespace KP = kda_planes;
+    constexpr int NS = DK / 32;  // 32-wide k-steps
+    constexpr int NV = NS * 8;   // feature values per lane: k-step s, element e -> 32 s + 8 lq + e
+    __shared__ float btot[4][DK];                            // product of a block's 16 gates
+    __shared__ alignas(16) uint16_t ycol[3][NS][64 * 8];     // k~ o (suffix product), B fragments
+    __shared__ alignas(16) float sbeta[KP::kRows];
+    __shared__ float sN[4][16 * 17];                         // A_ii, fp32
+    __shared__ alignas(16) uint16_t sdinv[4][256];
+
+    const int64_t seg = blockIdx.x;  // (sequence, chunk)
+    const int64_t bh = seg / nchunks, c = seg % nchunks;
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // row block
+    const int lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+    const int r = 16 * w + lr;               // row in the chunk
+    const int64_t t = c * KP::kRows + r;     // row in the sequence
+    const bool valid = t < T;
+    const int64_t rowoff = (bh * T + (valid ? t : 0)) * DK;
+
+    // the lane's row: gates, q, k, k~ (rows past the end: gate 1, zero operands, beta 0)
+    float av[NV], qv[NV], kv[NV], ktv[NV];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const int f0 = 32 * s + 8 * lq;
+        if (valid) {
+            float dd[8];
+            load8(a + rowoff + f0, av + 8 * s);
+            load8(q + rowoff + f0, qv + 8 * s);
+            load8(k + rowoff + f0, kv + 8 * s);
+            load8(d + rowoff + f0, dd);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ktv[8 * s + e] = dd[e] * kv[8 * s + e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                av[8 * s + e] = 1.f;
+                qv[8 * s + e] = kv[8 * s + e] = ktv[8 * s + e] = 0.f;
+            }
+        }
+    }
+    if (lq == 0) sbeta[r] = valid ? beta[bh * T + t] : 0.f;
+
+    // segment products of the gates: pre = inclusive prefix, suf = exclusive suffix, tot = whole
+    // segment, per feature, over the lane's aligned h-row segment (h = 1, 2, 4, 8, 16)
+    float pre[NV], suf[NV], tot[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        pre[i] = av[i];
+        suf[i] = 1.f;
+        tot[i] = av[i];
+    }
+    v4f accA = zero4(), accP = zero4();  // diagonal block, C layout: row 4 lq + e, column lr
+    // pairs with row r in the upper h-half and column s in the lower h-half of one 2h-segment
+    auto level = [&](auto h_c) __attribute__((always_inline)) {
+        constexpr int H = decltype(h_c)::value;
+        constexpr int SH = H == 1 ? 1 : H == 2 ? 2 : H == 4 ? 3 : 4;  // log2(2H)
+        const bool up = (lr & H) != 0;
+        v4f ca = zero4(), cp = zero4();
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            float fx[8], fy[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                fx[e] = up ? pre[8 * s + e] : 0.f;
+                fy[e] = up ? 0.f : suf[8 * s + e];
+            }
+            const v8s y = frag8(ktv + 8 * s, fy);
+            ca = mfma32(frag8(kv + 8 * s, fx), y, ca);
+            cp = mfma32(frag8(qv + 8 * s, fx), y, cp);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = 4 * lq + e;
+            if (((row ^ lr) >> SH) == 0) {
+                accA[e] += ca[e];
+                accP[e] += cp[e];
+            }
+        }
+    };
+    // h -> 2h: the sibling h-segment's total arrives by a lane swap that stays inside the
+    // 2h-segment (any lane of the sibling holds the same total)
+    auto grow = [&](auto h_c, auto ctrl_c) __attribute__((always_inline)) {
+        constexpr int H = decltype(h_c)::value;
+        constexpr int CTRL = decltype(ctrl_c)::value;
+        const bool lower = (lr & H) == 0;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const float sib = dpp_mov<CTRL>(tot[i]);
+            pre[i] = lower ? pre[i] : sib * pre[i];
+            suf[i] = lower ? suf[i] * sib : suf[i];
+            tot[i] = tot[i] * sib;
+        }
+    };
+    using std::integral_constant;
+    level(integral_constant<int, 1>{});
+    grow(integral_constant<int, 1>{}, integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
+    level(integral_constant<int, 2>{});
+    grow(integral_constant<int, 2>{}, integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]
+    level(integral_constant<int, 4>{});
+    grow(integral_constant<int, 4>{}, integral_constant<int, 0x141>{});  // row_half_mirror
+    level(integral_constant<int, 8>{});
+    grow(integral_constant<int, 8>{}, integral_constant<int, 0x140>{});  // row_mirror
+    {  // the diagonal of P: factor 1
+        v4f cp = zero4();
+        float one[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+        for (int s = 0; s < NS; ++s) cp = mfma32(frag8(qv + 8 * s, one), frag8(ktv + 8 * s, one), cp);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (4 * lq + e == lr) accP[e] += cp[e];
+    }
+    // pre, suf, tot now span the lane's 16-row block
+    if (lr == 0) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) btot[w][32 * s + 8 * lq + e] = tot[8 * s + e];
+    }
+    if (w < 3) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            *reinterpret_cast<v8s *>(&ycol[w][s][8 * lane]) = frag8(ktv + 8 * s, suf + 8 * s);
+    }
+    __syncthreads();
+
+    // products of the other blocks' totals: before this block (G at the block start) and after
+    float below[NV], above[NV];
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int f = 32 * s + 8 * lq + e;
+            float bl = 1.f, ab = 1.f;
+            for (int m = 0; m < w; ++m) bl *= btot[m][f];
+            for (int m = w + 1; m < 4; ++m) ab *= btot[m][f];
+            below[8 * s + e] = bl;
+            above[8 * s + e] = ab;
+        }
+
+    // the forward's operands: q o G, k o G with G_r = below o pre; k~ o rho(.->C) = k~ o suf o above
+    if (valid) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            float g[8], h[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                g[e] = below[8 * s + e] * pre[8 * s + e];
+                h[e] = suf[8 * s + e] * above[8 * s + e];
+            }
+            const int64_t o = rowoff + 32 * s + 8 * lq;
+            *reinterpret_cast<v8s *>(qp + o) = frag8(qv + 8 * s, g);
+            *reinterpret_cast<v8s *>(kp + o) = frag8(kv + 8 * s, g);
+            *reinterpret_cast<v8s *>(ktp + o) = frag8(ktv + 8 * s, h);
+        }
+    }
+    if (w == 0 && lr == 0) {  // G_C = the product of the four block totals
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            float gc[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) gc[e] = tot[8 * s + e] * above[8 * s + e];
+            float *dst = gcs + seg * DK + 32 * s + 8 * lq;
+            *reinterpret_cast<float4 *>(dst) = make_float4(gc[0], gc[1], gc[2], gc[3]);
+            *reinterpret_cast<float4 *>(dst + 4) = make_float4(gc[4], gc[5], gc[6], gc[7]);
+        }
+    }
+
+    uint16_t *img = planes + seg * KP::kElems;
+    uint16_t *pimg = img, *dimg = img + KP::kP, *aimg = img + KP::kP + KP::kDinv;
+    const v4f b4 = ld4(&sbeta[16 * w + 4 * lq]);  // beta of the rows 4 lq + e of this block
+    // after a quad transpose the lane holds row 4 lq + (lr & 3), columns 4 (lr >> 2) .. +3
+    const int trow = 4 * lq + (lr & 3), tg = lr >> 2;
+    auto store_p = [&](int j, v4f x) __attribute__((always_inline)) {
+        *reinterpret_cast<uint2 *>(pimg + (16 * w + trow) * KP::kPPitch + 16 * j + 4 * tg) =
+            pack4u(quad_transpose(x, lane));
+    };
+
+    // tiles (w, j), j < w: rows anchored at the last row of block j
+    float cross[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) cross[i] = 1.f;
+    for (int j = w - 1; j >= 0; --j) {
+        v4f ca = zero4(), cp = zero4();
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            float fx[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) fx[e] = pre[8 * s + e] * cross[8 * s + e];
+            const v8s y = *reinterpret_cast<const v8s *>(&ycol[j][s][8 * lane]);
+            ca = mfma32(frag8(kv + 8 * s, fx), y, ca);
+            cp = mfma32(frag8(qv + 8 * s, fx), y, cp);
+        }
+        const int tile = (w * (w - 1)) / 2 + j;
+        *reinterpret_cast<uint2 *>(aimg + tile * 256 + KP::blk(trow, tg)) =
+            pack4u(quad_transpose(-b4 * ca, lane));
+        store_p(j, cp);
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) cross[8 * s + e] *= btot[j][32 * s + 8 * lq + e];
+    }
+    store_p(w, accP);
+    for (int j = w + 1; j < 4; ++j) store_p(j, zero4());
+
+    // (I + A_ii)^{-1} by forward substitution in fp32, one column per lane of the first 16
+    const v4f nA = b4 * accA;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sN[w][(4 * lq + e) * 17 + lr] = nA[e];
+    __syncthreads();
+    if (lane < 16) {
+        float dc[16];
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            float acc = rr == lane ? 1.f : 0.f;
+#pragma unroll
+            for (int ss = 0; ss < rr; ++ss) acc -= sN[w][rr * 17 + ss] * dc[ss];
+            dc[rr] = acc;
+        }
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr)
+            sdinv[w][KP::blk(rr, lane >> 2) + (lane & 3)] = f32_to_bf16_bits(dc[rr]);
+    }
+    __syncthreads();
+    if (lane < 32)
+        *reinterpret_cast<uint4 *>(dimg + w * 256 + 8 * lane) =
+            *reinterpret_cast<const uint4 *>(&sdinv[w][8 * lane]);
 }
 
 // one decode token with the channel-wise gate (same layout as step_kernel)
@@ -160,26 +389,21 @@ step_kda_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k, const TQ *__
     }
 }
 
-template <int DK, typename TQ, typename TDI, typename TDO>
-hipError_t prep_typed(const KdaPrepArgs &a, hipStream_t stream) {
-    const int64_t total = a.BH * a.nchunks * (DK / 4);
-    const dim3 grid(static_cast<unsigned>((total + kPrepThreads - 1) / kPrepThreads));
-    hipLaunchKernelGGL((kda_prep_kernel<DK, TQ, TDI, TDO>), grid, dim3(kPrepThreads), 0, stream,
-                       static_cast<const TQ *>(a.q), static_cast<const TQ *>(a.k),
-                       static_cast<const TDI *>(a.d), a.alpha_ch, static_cast<TQ *>(a.qp),
-                       static_cast<TQ *>(a.kp), static_cast<TDO *>(a.dp), a.gcs, a.T, a.chunk,
-                       a.nchunks, total);
+template <int DK, typename TD>
+hipError_t planes_typed(const KdaPrepArgs &a, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(a.BH * a.nchunks));
+    hipLaunchKernelGGL((kda_planes_kernel<DK, TD>), grid, dim3(kPlanesThreads), 0, stream,
+                       static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
+                       static_cast<const TD *>(a.d), a.alpha_ch, a.beta,
+                       static_cast<uint16_t *>(a.qp), static_cast<uint16_t *>(a.kp),
+                       static_cast<uint16_t *>(a.ktp), a.planes, a.gcs, a.T, a.nchunks);
     return hipGetLastError();
 }
 
 template <int DK>
-hipError_t prep_dk(const KdaPrepArgs &a, hipStream_t stream) {
-    // bf16 operands: d' in bf16 (the forward rounds k~ to bf16 anyway); fp32: d' in fp32
-    if (a.qkv == OSDN_BF16)
-        return a.d_dtype == OSDN_F32 ? prep_typed<DK, bf16_t, float, bf16_t>(a, stream)
-                                     : prep_typed<DK, bf16_t, bf16_t, bf16_t>(a, stream);
-    return a.d_dtype == OSDN_F32 ? prep_typed<DK, float, float, float>(a, stream)
-                                 : prep_typed<DK, float, bf16_t, float>(a, stream);
+hipError_t planes_dk(const KdaPrepArgs &a, hipStream_t stream) {
+    return a.d_dtype == OSDN_F32 ? planes_typed<DK, float>(a, stream)
+                                 : planes_typed<DK, bf16_t>(a, stream);
 }
 
 template <int DK, int DV>
@@ -203,8 +427,8 @@ hipError_t step_dims(const StepArgs &a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_kda_prep(const KdaPrepArgs &a, hipStream_t stream) {
-    return a.dk == 64 ? prep_dk<64>(a, stream) : prep_dk<128>(a, stream);
+hipError_t launch_kda_planes(const KdaPrepArgs &a, hipStream_t stream) {
+    return a.dk == 64 ? planes_dk<64>(a, stream) : planes_dk<128>(a, stream);
 }
 
 hipError_t launch_step_kda(const StepArgs &a, hipStream_t stream) {

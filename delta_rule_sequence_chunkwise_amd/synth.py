@@ -198,6 +198,14 @@ def make_channel_gate(B: int, H: int, T: int, dk: int, seed: int) -> np.ndarray:
     return round_f32(np.exp(-0.05 * np.logaddexp(0.0, rng.standard_normal((B, H, T, dk)))))
 
 
+def make_channel_gate_uniform(B: int, H: int, T: int, dk: int, lo: float, hi: float,
+                              seed: int) -> np.ndarray:
+    """Channel-wise gate a [B,H,T,dk] ~ U(lo, hi), rounded to float32: the strong-decay and
+    tiny-gate regimes (stream seed + 104723, apart from the other draws)."""
+    rng = np.random.Generator(np.random.PCG64(seed + 104723))
+    return round_f32(rng.uniform(lo, hi, (B, H, T, dk)))
+
+
 def make_output_grads(B: int, H: int, T: int, dk: int, dv: int, *, qkv: str, seed: int,
                       state: bool = True) -> Dict[str, Optional[np.ndarray]]:
     """Output gradients for the backward: do [B,H,T,dv] ~ N(0,1) (rounded to the qkv type) and,

@@ -155,18 +155,22 @@ osdn_status osdn_precond_step(const void *k, const float *beta, const float *r, 
  *
  * i.e. each key feature (row of M) has its own retention factor a_t[i].
  *
- *   alpha_ch  [B,H,T,dk] f32   per-token, per-key-feature retention, in (0, 1]; within one
- *                              chunk the running product of a feature's factors must stay
- *                              above 2^-60 (below that it is taken as 2^-60); 16-byte
- *                              aligned (OSDN_ERR_ALIGN otherwise)
- *   workspace                  caller-owned device memory of at least
+ *   alpha_ch  [B,H,T,dk] f32   per-token, per-key-feature retention in [0, 1], any size
+ *                              (Erase-then-Delta Attention sets no lower bound): the decay
+ *                              enters only as products of these factors, never divided;
+ *                              16-byte aligned (OSDN_ERR_ALIGN otherwise)
+ *   workspace                  bf16 inputs: caller-owned device memory of at least
  *                              osdn_chunk_fwd_kda_workspace(B, H, T, dk, chunk, qkv) bytes,
  *                              256-byte aligned; its contents on entry are ignored and on
- *                              return unspecified; it must not overlap any other argument
+ *                              return unspecified; it must not overlap any other argument.
+ *                              fp32 inputs need none (the size is 0; may be NULL)
  *   workspace_bytes            its size
  *   every other argument       as for osdn_chunk_fwd (there is no scalar alpha here)
- * Two kernels run on `stream`: one writes the gate-scaled q, k, d and the per-chunk decay
- * into the workspace, the chunkwise forward then reads them.
+ * bf16 inputs: two kernels run on `stream`.  The first forms, for every chunk in parallel, the
+ * gate-scaled q o G, k o G, k~ o (G_C / G) (G the running product of the gates from the chunk
+ * start, G_C its value at the chunk's end, each formed as a product), G_C, the score matrix and
+ * the pieces of the chunk's UT transform, into the workspace; the chunkwise forward then reads
+ * them.  fp32 inputs: one kernel, at chunk min(chunk, 32).
  */
 int64_t osdn_chunk_fwd_kda_workspace(int64_t B, int64_t H, int64_t T, int32_t dk,
                                      int32_t chunk, osdn_dtype qkv); /* -1 if invalid */

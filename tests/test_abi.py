@@ -213,10 +213,14 @@ def test_chunk_fwd_kda_rejects(L, over, status):
 
 def test_kda_workspace_size(L):
     n = L.osdn_chunk_fwd_kda_workspace(2, 3, 100, 128, 64, osdn.OSDN_BF16)
-    # q', k' (bf16), d' (bf16), G_C (fp32, two chunks), each rounded up to 256 bytes
-    assert n == 3 * (2 * 3 * 100 * 128 * 2) + 2 * 3 * 2 * 128 * 4
+    # gate-scaled q, k, k~ (bf16), the chunk planes (P 64 x 72, four 16 x 16 inverses, six
+    # 16 x 16 off-diagonal blocks, bf16, two chunks), G_C (fp32, two chunks), each rounded up
+    # to 256 bytes
+    planes = 2 * 3 * 2 * (64 * 72 + 4 * 256 + 6 * 256) * 2
+    assert n == 3 * (2 * 3 * 100 * 128 * 2) + planes + 2 * 3 * 2 * 128 * 4
     assert L.osdn_chunk_fwd_kda_workspace(2, 3, 100, 96, 64, osdn.OSDN_BF16) == -1
-    assert L.osdn_chunk_fwd_kda_workspace(1, 1, 10, 64, 16, osdn.OSDN_F32) == 3 * 2560 + 256
+    # fp32 inputs need no workspace
+    assert L.osdn_chunk_fwd_kda_workspace(1, 1, 10, 64, 16, osdn.OSDN_F32) == 0
     assert call_kda(L, B=0) == 0 and call_kda(L, T=0, q=None, S_T=None, ws=None) == 0
 
 

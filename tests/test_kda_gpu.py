@@ -2,9 +2,11 @@
 float64 oracle on the same seeded inputs.
 
 Error measure and bounds as for the scalar gate: max |x - x_ref| / max |x_ref| for o and the
-final state, 1e-4 for fp32 inputs and 2e-2 for bf16 inputs (fp32 accumulation).  The gate-scaled
-operands q G, k G (rounded to the input precision) and d / G^2 (bf16 on the bf16 path) add one
-rounding each to what the forward rounds anyway."""
+final state, 1e-4 for fp32 inputs and 2e-2 for bf16 inputs (fp32 accumulation).  On the bf16
+path the gate-scaled operands (products of gates, each at most 1, times q, k or k~) are rounded
+to bf16 once, as the forward rounds its operands anyway.  Gates from the generator's mild
+recipe, strong decay U(0.05, 0.6), tiny gates down to 1e-30, and gates of exactly 0 are
+covered (Erase-then-Delta Attention, section 2.2, eq. 5 bounds a_t only by (0, 1))."""
 import numpy as np
 import pytest
 
@@ -15,9 +17,18 @@ from tests.gpu_util import TOL, oracle_inputs, rel_err, say, to_dev, to_np, torc
 pytestmark = pytest.mark.gpu
 
 
-def kda_inputs(B, H, T, dk, dv, qkv, seed, s0=True):
+def kda_inputs(B, H, T, dk, dv, qkv, seed, s0=True, gates=None):
     x = synth.make_shape(B, H, T, dk, dv, qkv=qkv, alpha=False, s0=s0, seed=seed)
-    x["alpha_ch"] = synth.make_channel_gate(B, H, T, dk, seed=seed)
+    if gates is None:
+        x["alpha_ch"] = synth.make_channel_gate(B, H, T, dk, seed=seed)
+    elif gates == "zeros":  # mild gates with about 2% exact zeros
+        a = synth.make_channel_gate_uniform(B, H, T, dk, 0.5, 1.0, seed=seed)
+        z = synth.make_channel_gate_uniform(B, H, T, dk, 0.0, 1.0, seed=seed + 1)
+        a[z < 0.02] = 0.0
+        x["alpha_ch"] = a
+    else:
+        lo, hi = gates
+        x["alpha_ch"] = synth.make_channel_gate_uniform(B, H, T, dk, lo, hi, seed=seed)
     return x
 
 
@@ -70,6 +81,28 @@ F32_CASES = [
 def test_kda_f32(case):
     B, H, T, dk, dv, chunk = case
     check(kda_inputs(B, H, T, dk, dv, "f32", seed=T + 7), "f32", chunk=chunk, label=str(case))
+
+
+STRONG = [
+    # qkv, B, H, T, dk, dv, gates, chunk (fp32)
+    ("bf16", 1, 2, 256, 128, 128, (0.05, 0.6), 64),
+    ("bf16", 2, 1, 200, 64, 128, (0.05, 0.6), 64),
+    ("bf16", 1, 2, 192, 128, 64, (0.2, 0.6), 64),
+    ("bf16", 1, 1, 130, 128, 128, (1e-30, 1e-20), 64),
+    ("bf16", 2, 1, 150, 64, 64, (1e-6, 1.0), 64),
+    ("bf16", 1, 2, 160, 128, 128, "zeros", 64),
+    ("f32", 1, 2, 192, 128, 128, (0.05, 0.6), 64),
+    ("f32", 1, 1, 100, 64, 64, (0.05, 0.6), 16),
+    ("f32", 1, 1, 96, 128, 64, (1e-30, 1e-20), 32),
+    ("f32", 1, 2, 130, 64, 128, "zeros", 64),
+]
+
+
+@pytest.mark.parametrize("case", STRONG, ids=lambda c: "x".join(map(str, c)))
+def test_kda_strong_decay(case):
+    qkv, B, H, T, dk, dv, gates, chunk = case
+    x = kda_inputs(B, H, T, dk, dv, qkv, seed=T + dk + 5, gates=gates)
+    check(x, qkv, chunk=chunk, label=str(case))
 
 
 def test_uniform_channels_match_scalar_gate():
