@@ -7,16 +7,24 @@ pass of the whole chunkwise hot path over one batch of synthetic input already r
 HBM.  Prints ONE JSON line.  Besides the contract fields it carries:
 
   roofline      the chunk kernel against HBM: algorithmic bytes per launch / average
-                launch time from HIP events on the launch stream (peak 8 TB/s);
+                launch time from HIP events on the launch stream (peak 8 TB/s); `traffic` is
+                the rocprofv3 FETCH_SIZE/WRITE_SIZE figure stored under profiles/ for the same
+                kernel source (null once the source has changed);
   mfma          algorithmic FLOPs per launch / launch time against the bf16 dense peak;
   cpu_baseline  the float64 oracle on the host cores, same workload, with the parity error
-                of the GPU output against it;
+                of the GPU output against it (whole tensor and worst single sequence), and
+                the oracle's single-core rate on one sequence;
+  configs       the same figures (time per step, tokens/s, TFLOP/s, both roofline
+                fractions, parity, oracle timing) for the other forward workloads: tiny
+                (fp32), 340m and long;
   decode        osdn_step over the decode workload (B=128, H=16, dk=dv=128), timed over
-                `--decode-steps` consecutive calls (state updated in place);
+                `--decode-steps` consecutive calls (state updated in place), and a control
+                that rotates the calls over four distinct 128 MiB states (512 MiB, more
+                than the 256 MB Infinity Cache holds);
   precond_scan  the Phase-1 preconditioner scan (osdn_precond_scan, chunkwise form) over the
                 same workload's keys and gates, with its own HBM roofline, its oracle timed on
                 the host, and the forward with the scan in front (scan + chunkwise forward);
-  kda           the forward with the channel-wise gate (osdn_chunk_fwd_kda: the gate-scaling
+  kda           the forward with the channel-wise gate (osdn_chunk_fwd_kda: the chunk planes
                 kernel, then the chunkwise forward) on the same workload with a per-feature
                 gate, with its HBM roofline and the parity of its output;
   bwd           the backward (osdn_chunk_bwd: forward state checkpoints, the chunk inverses, the
@@ -93,6 +101,8 @@ def main():
     ap.add_argument("--bwd-steps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="1.3b")
+    ap.add_argument("--configs", default="tiny,340m,long",
+                    help="other forward workloads measured beside the main one ('' for none)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 times): the "
                          "reference for scaling HBM byte counters")
@@ -123,90 +133,46 @@ def main():
         __graft_entry__.build()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    w = synth.WORKLOADS[args.workload]
-    x = synth.make_inputs(w)
-    qdt = torch.bfloat16 if w.qkv == "bf16" else torch.float32
-    to = lambda a, dt: None if a is None else torch.from_numpy(a).to(dev).to(dt)
-    q, k, v = (to(x[n], qdt) for n in ("q", "k", "v"))
-    beta, d, alpha, S0 = (to(x[n], torch.float32) for n in ("beta", "d", "alpha", "S0"))
-    B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
-    o = torch.empty((B, H, T, dv), dtype=qdt, device=dev)
-    S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
-
-    def step():
-        osdn.osdn_chunk_fwd(q, k, v, beta, d, alpha, S0, chunk=w.chunk, o=o, S_T=S_T)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    wall_s = (t1 - t0) / args.steps
-    launch_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
-
-    head_tokens = B * H * T
-    eq = 2 if w.qkv == "bf16" else 4
-    alg_bytes = head_tokens * bytes_per_head_token(dk, dv, eq, 4, alpha is not None) \
-        + B * H * dk * dv * 4 * (2 if S0 is not None else 1)
-    alg_flops = head_tokens * flops_per_head_token(dk, dv, w.chunk)
-    achieved = alg_bytes / launch_s
-    traffic = load_traffic("chunk_fwd_1.3b_traffic", CHUNK_KERNEL_SRC)
+    cpu = not args.no_cpu_baseline
+    main_rec, ctx = bench_forward(synth.WORKLOADS[args.workload], args.steps, args.warmup,
+                                  torch, dev, cpu, keep=True)
+    w, x = ctx["w"], ctx["x"]
+    q, k, v, beta, d, alpha, S0, o, S_T = ctx["dev"]
+    B, H, T = w.B, w.H, w.T
 
     line = {
         "metric": METRIC,
-        "value": round(B * T / wall_s, 1),
+        "value": main_rec["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall_s * 1e3, 4),
+        "ms_per_step": main_rec["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.qkv,
         "data": "synthetic (seeded generator; q,k unit-norm, v normal, beta sigmoid, "
                 "d log-normal, alpha in (0.86, 0.995))",
-        "config": {"workload": f"{w.name}-shape OSDN chunkwise forward: B={B} H={H} T={T} "
-                               f"dk={dk} dv={dv} chunk={w.chunk}, {w.qkv} q/k/v/o, fp32 "
-                               "beta/d/alpha, fp32 final state",
-                   "B": B, "H": H, "T": T, "dk": dk, "dv": dv, "chunk": w.chunk},
-        "head_tokens_per_s": round(head_tokens / wall_s, 1),
-        "tflops": round(alg_flops / launch_s / 1e12, 3),
-        "mfma": {"achieved": round(alg_flops / launch_s / 1e12, 3), "peak": PEAK_BF16 / 1e12,
-                 "unit": "TFLOP/s", "frac": round(alg_flops / launch_s / PEAK_BF16, 5),
-                 "flops_per_launch": alg_flops},
-        "roofline": {"bound": "hbm", "achieved": round(achieved / 1e9, 2),
-                     "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM, 5),
-                     "traffic": traffic, "alg_bytes_per_launch": alg_bytes,
-                     "launch_ms": round(launch_s * 1e3, 4)},
+        "config": main_rec["config"],
     }
+    for key in ("head_tokens_per_s", "tflops", "mfma", "roofline", "cpu_baseline", "parity"):
+        if key in main_rec:
+            line[key] = main_rec[key]
+    line["roofline"]["traffic"] = load_traffic("chunk_fwd_1.3b_traffic", CHUNK_KERNEL_SRC) \
+        if w.name == "1.3b" else None
+    line["roofline"]["traffic_source"] = (
+        "profiles/chunk_fwd_1.3b_traffic.json: rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 "
+        "per launch (factors from a plain copy), taken on the same kernel source; null when "
+        "the source has changed since")
 
-    if not args.no_cpu_baseline:
-        import oracle
-        nt = oracle.default_threads()
-        c0 = time.perf_counter()
-        o_ref, S_ref = oracle.chunk_fwd(x["q"], x["k"], x["v"], x["beta"], x["d"],
-                                        x["alpha"], x["S0"], nthreads=nt)
-        cpu_s = time.perf_counter() - c0
-        o_gpu = o.float().cpu().numpy()
-        S_gpu = S_T.cpu().numpy()
-        rel = lambda a, b: float(np.max(np.abs(a - b)) / np.max(np.abs(b)))
-        line["cpu_baseline"] = {"value": round(B * T / cpu_s, 1), "unit": "tokens/s",
-                                "cores": nt, "kind": "oracle",
-                                "sample": f"the whole {w.name} workload ({B * H} sequences x "
-                                          f"{T} tokens), float64 C recurrence, "
-                                          f"{cpu_s:.2f} s wall"}
-        line["parity"] = {"e_o": rel(o_gpu, o_ref), "e_S": rel(S_gpu, S_ref),
-                          "tol": 2e-2 if w.qkv == "bf16" else 1e-4}
-        del o_ref, S_ref
+    if args.configs:
+        line["configs"] = {}
+        for name in args.configs.split(","):
+            if name and name != w.name:
+                steps = max(3, args.steps // 4) if name == "long" else args.steps
+                rec, _ = bench_forward(synth.WORKLOADS[name], steps, args.warmup, torch, dev, cpu)
+                line["configs"][name] = rec
 
     if args.decode_steps > 0:
         line["decode"] = bench_decode(args.decode_steps, torch, dev, synth)
@@ -225,6 +191,101 @@ def main():
                                 (q, k, v, beta, d, alpha, S0), not args.no_cpu_baseline)
 
     print(json.dumps(line), flush=True)
+
+
+def bench_forward(w, n_steps, warmup, torch, dev, cpu, keep=False):
+    """Times osdn_chunk_fwd on workload `w`: `warmup` untimed calls, then `n_steps` calls
+    bracketed by HIP events on the launch stream (and the host clock).  With `cpu`, the float64
+    oracle runs on the same inputs on all host cores (parity of the GPU output, whole tensor and
+    worst single sequence) and on one core over one sequence."""
+    import numpy as np
+    import oracle
+    from delta_rule_sequence_chunkwise_amd import osdn, synth
+
+    x = synth.make_inputs(w)
+    qdt = torch.bfloat16 if w.qkv == "bf16" else torch.float32
+    to = lambda a, dt: None if a is None else torch.from_numpy(a).to(dev).to(dt)
+    q, k, v = (to(x[n], qdt) for n in ("q", "k", "v"))
+    beta, d, alpha, S0 = (to(x[n], torch.float32) for n in ("beta", "d", "alpha", "S0"))
+    B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
+    o = torch.empty((B, H, T, dv), dtype=qdt, device=dev)
+    S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+
+    def step():
+        osdn.osdn_chunk_fwd(q, k, v, beta, d, alpha, S0, chunk=w.chunk, o=o, S_T=S_T)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(n_steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall_s = (t1 - t0) / n_steps
+    launch_s = ev0.elapsed_time(ev1) / 1e3 / n_steps
+
+    head_tokens = B * H * T
+    eq = 2 if w.qkv == "bf16" else 4
+    alg_bytes = head_tokens * bytes_per_head_token(dk, dv, eq, 4, alpha is not None) \
+        + B * H * dk * dv * 4 * (2 if S0 is not None else 1)
+    alg_flops = head_tokens * flops_per_head_token(dk, dv, w.chunk)
+    t_floor = max(alg_bytes / PEAK_HBM, alg_flops / PEAK_BF16)
+    rec = {
+        "config": {"workload": f"{w.name}-shape OSDN chunkwise forward: B={B} H={H} T={T} "
+                               f"dk={dk} dv={dv} chunk={w.chunk}, {w.qkv} q/k/v/o, fp32 "
+                               f"beta/d{'/alpha' if alpha is not None else ''}, fp32 final "
+                               "state",
+                   "B": B, "H": H, "T": T, "dk": dk, "dv": dv, "chunk": w.chunk},
+        "ms_per_step": round(wall_s * 1e3, 4),
+        "launch_ms": round(launch_s * 1e3, 4),
+        "tokens_per_s": round(B * T / wall_s, 1),
+        "head_tokens_per_s": round(head_tokens / wall_s, 1),
+        "tflops": round(alg_flops / launch_s / 1e12, 3),
+        "mfma": {"achieved": round(alg_flops / launch_s / 1e12, 3), "peak": PEAK_BF16 / 1e12,
+                 "unit": "TFLOP/s", "frac": round(alg_flops / launch_s / PEAK_BF16, 5),
+                 "flops_per_launch": alg_flops},
+        "roofline": {"bound": "hbm", "achieved": round(alg_bytes / launch_s / 1e9, 2),
+                     "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                     "frac": round(alg_bytes / launch_s / PEAK_HBM, 5),
+                     "alg_bytes_per_launch": alg_bytes, "launch_ms": round(launch_s * 1e3, 4),
+                     "frac_of_binding_floor": round(t_floor / launch_s, 5)},
+    }
+    if cpu:
+        nt = oracle.default_threads()
+        c0 = time.perf_counter()
+        o_ref, S_ref = oracle.chunk_fwd(x["q"], x["k"], x["v"], x["beta"], x["d"],
+                                        x["alpha"], x["S0"], nthreads=nt)
+        cpu_s = time.perf_counter() - c0
+        one = lambda a: None if a is None else np.ascontiguousarray(a[:1, :1])
+        c1 = time.perf_counter()
+        oracle.chunk_fwd(one(x["q"]), one(x["k"]), one(x["v"]), one(x["beta"]), one(x["d"]),
+                         one(x["alpha"]), one(x["S0"]), nthreads=1)
+        one_s = time.perf_counter() - c1
+        o_gpu = o.float().cpu().numpy()
+        S_gpu = S_T.cpu().numpy()
+        rel = lambda a, b: float(np.max(np.abs(a - b)) / np.max(np.abs(b)))
+        worst = lambda a, b: max(rel(a[i, j], b[i, j]) for i in range(B) for j in range(H))
+        rec["cpu_baseline"] = {"value": round(B * T / cpu_s, 1), "unit": "tokens/s",
+                               "cores": nt, "kind": "oracle",
+                               "sample": f"the whole {w.name} workload ({B * H} sequences x "
+                                         f"{T} tokens), float64 C recurrence, {cpu_s:.2f} s "
+                                         "wall",
+                               "single_core": {"value": round(T / one_s, 1),
+                                               "unit": "head-tokens/s", "cores": 1,
+                                               "sample": f"one sequence ({T} tokens), "
+                                                         f"{one_s:.2f} s wall"}}
+        rec["parity"] = {"e_o": rel(o_gpu, o_ref), "e_S": rel(S_gpu, S_ref),
+                         "worst_sequence_e_o": worst(o_gpu, o_ref),
+                         "worst_sequence_e_S": worst(S_gpu, S_ref),
+                         "tol": 2e-2 if w.qkv == "bf16" else 1e-4}
+        del o_ref, S_ref
+    ctx = {"w": w, "x": x, "dev": (q, k, v, beta, d, alpha, S0, o, S_T)} if keep else None
+    return rec, ctx
 
 
 def bwd_flops_per_head_token(dk, dv, C):
@@ -370,8 +431,9 @@ def bench_kda(n_steps, torch, dev, synth, w, x, fwd, cpu):
            "roofline": {"bound": "hbm", "achieved": round(alg / per / 1e9, 2),
                         "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                         "frac": round(alg / per / PEAK_HBM, 5), "alg_bytes_per_step": alg,
-                        "note": "two launches: the gate-scaling kernel writes and the forward "
-                                "reads gate-scaled q, k, d (workspace traffic beyond alg)"}}
+                        "note": "two launches: the planes kernel writes and the forward "
+                                "reads the gate-scaled q, k, k~ and the chunk planes "
+                                "(workspace traffic beyond alg)"}}
     if cpu:
         import oracle
         o_ref, S_ref = oracle.chunk_fwd(x["q"], x["k"], x["v"], x["beta"], x["d"], None,
@@ -410,6 +472,21 @@ def bench_decode(n_steps, torch, dev, synth, distinct=64):
     ev1.record(stream)
     torch.cuda.synchronize()
     per = ev0.elapsed_time(ev1) / 1e3 / n_steps
+    # control: the calls rotate over `nrot` distinct states, so each state is touched again
+    # only after nrot - 1 others (nrot x 128 MiB, more than the 256 MB Infinity Cache holds)
+    nrot = 4
+    states = [S.clone() for _ in range(nrot)]
+    for t in range(nrot):
+        osdn.osdn_step(q[t], k[t], v[t], beta[t], d[t], alpha[t], states[t], o=o[t])
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for t in range(n_steps):
+        i = t % n_in
+        osdn.osdn_step(q[i], k[i], v[i], beta[i], d[i], alpha[i], states[t % nrot], o=o[i])
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    per_rot = ev0.elapsed_time(ev1) / 1e3 / n_steps
+    del states
     state_bytes = 2 * BH * w.dk * w.dv * 4
     io_bytes = BH * ((2 * w.dk + 2 * w.dv) * 2 + w.dk * 4 + 8)
     alg = state_bytes + io_bytes
@@ -420,8 +497,18 @@ def bench_decode(n_steps, torch, dev, synth, distinct=64):
             "achieved_GBps": round(alg / per / 1e9, 1),
             "frac_of_hbm_peak": round(alg / per / PEAK_HBM, 4),
             "traffic": load_traffic("step_decode_traffic", STEP_KERNEL_SRC),
-            "note": "the 128 MiB state fits in the 256 MB Infinity Cache; achieved is "
-                    "algorithmic bytes / time, see profiles for DRAM counters"}
+            "traffic_source": "profiles/step_decode_traffic.json: rocprofv3 FETCH_SIZE x 2.0 + "
+                              "WRITE_SIZE x 1.0 per launch (L2-to-fabric requests; Infinity "
+                              "Cache hits are behind the fabric and count too)",
+            "state_rotation": {"states": nrot, "footprint_MiB": nrot * state_bytes // 2 // (1 << 20),
+                               "us_per_step": round(per_rot * 1e6, 3),
+                               "achieved_GBps": round(alg / per_rot / 1e9, 1),
+                               "frac_of_hbm_peak": round(alg / per_rot / PEAK_HBM, 4),
+                               "note": "each call updates a different state, so a state is "
+                                       "read again only after three others (384 MiB) were "
+                                       "streamed: it cannot be served from the Infinity Cache"},
+            "note": "in place, the 128 MiB state fits in the 256 MB Infinity Cache; the "
+                    "state_rotation figure is the one free of it"}
 
 
 def bench_precond(n_steps, torch, dev, synth, w, x, fwd, cpu):
