@@ -57,6 +57,7 @@ const char *osdn_status_string(osdn_status s) {
         case OSDN_ERR_ALIGN: return "misaligned pointer";
         case OSDN_ERR_ALIAS: return "output overlaps memory it must not overlap";
         case OSDN_ERR_LAUNCH: return "HIP launch failed";
+        case OSDN_ERR_SCRATCH: return "problem needs more scratch than the no-allocation entry point holds";
     }
     return "unknown status";
 }

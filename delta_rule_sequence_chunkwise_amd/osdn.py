@@ -16,12 +16,14 @@ LIB_PATH = os.path.join(_HERE, "lib", "libosdn.so")
 
 OSDN_F32 = 0
 OSDN_BF16 = 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 STATUS = {0: "OSDN_OK", -1: "OSDN_ERR_NULL", -2: "OSDN_ERR_SHAPE", -3: "OSDN_ERR_UNSUPPORTED",
-          -4: "OSDN_ERR_ALIGN", -5: "OSDN_ERR_ALIAS", -6: "OSDN_ERR_LAUNCH"}
+          -4: "OSDN_ERR_ALIGN", -5: "OSDN_ERR_ALIAS", -6: "OSDN_ERR_LAUNCH",
+          -7: "OSDN_ERR_SCRATCH"}
 EXPORTS = ("osdn_chunk_fwd", "osdn_step", "osdn_precond_scan", "osdn_precond_step",
-           "osdn_chunk_fwd_kda", "osdn_chunk_fwd_kda_workspace", "osdn_step_kda",
+           "osdn_chunk_fwd_kda", "osdn_chunk_fwd_kda_workspace", "osdn_chunk_fwd_kda_noalloc",
+           "osdn_step_kda",
            "osdn_chunk_bwd", "osdn_chunk_bwd_workspace", "osdn_chunk_states_bytes",
            "osdn_chunk_fwd_states", "osdn_chunk_bwd_states", "osdn_status_string",
            "osdn_abi_version")
@@ -62,6 +64,9 @@ def lib() -> ctypes.CDLL:
     L.osdn_chunk_fwd_kda.restype = ctypes.c_int
     L.osdn_chunk_fwd_kda.argtypes = [vp] * 10 + [i64, i64, i64, i64, i32, i32, i32, ctypes.c_int,
                                                  ctypes.c_int, vp]
+    L.osdn_chunk_fwd_kda_noalloc.restype = ctypes.c_int
+    L.osdn_chunk_fwd_kda_noalloc.argtypes = [vp] * 9 + [i64, i64, i64, i32, i32, i32,
+                                                          ctypes.c_int, ctypes.c_int, vp]
     L.osdn_step_kda.restype = ctypes.c_int
     L.osdn_step_kda.argtypes = [vp] * 8 + [i64, i64, i32, i32, ctypes.c_int, ctypes.c_int, vp]
     L.osdn_chunk_bwd_workspace.restype = i64
@@ -335,6 +340,25 @@ def osdn_chunk_fwd_kda(q, k, v, beta, d, alpha_ch, S0=None, *, chunk: int = 64, 
                                   _stream(stream, q.device))
     if st != 0:
         raise OSDNError(st, "osdn_chunk_fwd_kda")
+    return o, S_T
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def osdn_chunk_fwd_kda_noalloc(q, k, v, beta, d, alpha_ch, S0, o, S_T, *, chunk: int = 64,
+                               stream=None):
+    """osdn_chunk_fwd_kda through the entry point that allocates nothing: the caller passes the
+    outputs o [B,H,T,dv] and S_T [B,H,dk,dv] (or None); the library's own scratch array holds the
+    workspace.  Raises OSDNError (status -7) when the problem needs more scratch than it has."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    st = lib().osdn_chunk_fwd_kda_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(d),
+                                          _ptr(alpha_ch), _ptr(S0), _ptr(o), _ptr(S_T),
+                                          B, H, T, dk, dv, chunk, _dtype_code(q),
+                                          _dtype_code(d), _stream(stream, q.device))
+    if st != 0:
+        raise OSDNError(st, "osdn_chunk_fwd_kda_noalloc")
     return o, S_T
 
 

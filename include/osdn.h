@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define OSDN_ABI_VERSION 2
+#define OSDN_ABI_VERSION 3
 
 typedef enum osdn_status {
     OSDN_OK = 0,
@@ -51,6 +51,8 @@ typedef enum osdn_status {
     OSDN_ERR_ALIGN = -4,       /* a pointer violates the alignment rule above                */
     OSDN_ERR_ALIAS = -5,       /* an output overlaps memory it must not overlap              */
     OSDN_ERR_LAUNCH = -6,      /* the HIP runtime rejected the launch (e.g. no gfx950 device) */
+    OSDN_ERR_SCRATCH = -7,     /* the no-allocation entry point: the problem needs more scratch
+                                  than OSDN_NOALLOC_SCRATCH_BYTES                             */
 } osdn_status;
 
 typedef enum osdn_dtype { OSDN_F32 = 0, OSDN_BF16 = 1 } osdn_dtype;
@@ -265,6 +267,31 @@ osdn_status osdn_chunk_bwd_states(const void *q, const void *k, const void *v,
                                   int64_t workspace_bytes, int64_t B, int64_t H, int64_t T,
                                   int32_t dk, int32_t dv, osdn_dtype qkv, osdn_dtype d_dtype,
                                   void *stream);
+
+/*
+ * osdn_chunk_fwd_kda with no workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * The caller passes inputs and outputs as for osdn_chunk_fwd_kda; the bf16 path's gate-scaled
+ * operands and chunk planes go into a library-owned device array of
+ * OSDN_NOALLOC_SCRATCH_BYTES (64 MiB) on each GPU the library runs on, held until the process
+ * ends.  No call allocates or frees memory.
+ *   - A problem whose workspace (osdn_chunk_fwd_kda_workspace) exceeds the array returns
+ *     OSDN_ERR_SCRATCH before anything is enqueued (at dk = 128: about 67 k head-tokens,
+ *     B * H * T, per call).  fp32 inputs need no scratch.
+ *   - Every call on one GPU shares that GPU's array; it keeps the last call's contents, which
+ *     no call reads before writing them.  Calls that overlap in time on one GPU (other
+ *     streams, other host threads) race on it: serialise them.
+ *   - The first call on a device looks up the array's address on that device (current device);
+ *     a failure there returns OSDN_ERR_LAUNCH.
+ * Outputs are bitwise those of osdn_chunk_fwd_kda (the same kernels).
+ */
+#define OSDN_NOALLOC_SCRATCH_BYTES (64ll << 20)
+osdn_status osdn_chunk_fwd_kda_noalloc(const void *q, const void *k, const void *v,
+                                       const float *beta, const void *d, const float *alpha_ch,
+                                       const float *S0, void *o, float *S_T, int64_t B,
+                                       int64_t H, int64_t T, int32_t dk, int32_t dv,
+                                       int32_t chunk, osdn_dtype qkv, osdn_dtype d_dtype,
+                                       void *stream);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char *osdn_status_string(osdn_status s);

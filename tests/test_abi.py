@@ -224,6 +224,22 @@ def test_kda_workspace_size(L):
     assert call_kda(L, B=0) == 0 and call_kda(L, T=0, q=None, S_T=None, ws=None) == 0
 
 
+def test_kda_noalloc_rejects_before_touching_the_gpu(L):
+    """The no-allocation entry point checks the problem against its scratch array (64 MiB)
+    before any HIP call: too large a problem returns OSDN_ERR_SCRATCH, an unsupported one the
+    usual status.  (Fake addresses: nothing is dereferenced.)"""
+    ptrs = [addr(i) for i in range(1, 10)]
+    call = lambda B, H, T, dk, dv, chunk, qkv: L.osdn_chunk_fwd_kda_noalloc(
+        *ptrs, B, H, T, dk, dv, chunk, qkv, osdn.OSDN_F32, None)
+    need = L.osdn_chunk_fwd_kda_workspace(4, 16, 4096, 128, 64, osdn.OSDN_BF16)
+    assert need > osdn.NOALLOC_SCRATCH_BYTES
+    assert call(4, 16, 4096, 128, 128, 64, osdn.OSDN_BF16) == -7
+    assert call(4, 16, 4096, 96, 128, 64, osdn.OSDN_BF16) == -3
+    assert call(1, 1, 10, 128, 128, 32, osdn.OSDN_BF16) == -3
+    assert call(0, 16, 4096, 128, 128, 64, osdn.OSDN_BF16) == 0
+    assert L.osdn_status_string(-7).decode().startswith("problem needs more scratch")
+
+
 def test_step_kda_rejects(L):
     args = [addr(1), addr(2), addr(3), addr(4), addr(5), addr(6), addr(7), addr(8), 4, 2, 128,
             128, osdn.OSDN_BF16, osdn.OSDN_F32, None]
