@@ -31,8 +31,9 @@
 //   tiles are split by column block: wave 2 takes blocks {0,3}, wave 3 blocks {1,2}.
 // * Stager waves (4, 5) bring the k rows of chunk c+2 into LDS (two row blocks each) and write
 //   k~ = d (.) k of those rows; d reaches their registers one step ahead.
-// * The loader wave (6) brings q and v of chunk c+2 into LDS.  Prep wave 2 runs chunk c+2's
-//   decay scan after its tiles: its LDS writes then never queue behind an LDS DMA of its own.
+// * The loader wave (6) brings q and v of chunk c+2, and beta and alpha of chunk c+3, into
+//   LDS.  Prep wave 2 runs chunk c+2's decay scan after its tiles from those LDS copies: a
+//   global load of its own would return only after the step's bulk loads ahead of it.
 // With the channel-wise gate (GATE) the caller passes the gate-scaled q o G, k o G and
 // k~ o (G_C / G), each chunk's product of gates G_C and its planes (P, the diagonal-block
 // inverses, -A_ik) from the planes kernel: the stagers copy k~ in instead of forming it, prep
@@ -102,6 +103,8 @@ struct alignas(16) Lds {
     alignas(16) float eb[3][CH];
     alignas(16) float gc[GATE ? 3 : 1][GATE ? DK : 4];  // channel-wise gate: G_C of the chunk
     alignas(16) float cik[3][8];
+    alignas(16) float rawb[2][CH];  // [chunk parity] beta and alpha as loaded, for the scan
+    alignas(16) float rawa[2][CH];
     alignas(16) uint16_t ntile[NBLK][16 * 16];  // N of diagonal block kb, rows by blk (prep)
 };
 
@@ -342,6 +345,17 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
 
+    // beta and alpha of chunk c reach LDS by DMA (loader wave, step c-3), so the scanning wave
+    // issues no global load: behind the bulk loads of the step it would wait a memory round trip
+    auto load_ba = [&](int64_t cc, int par) __attribute__((always_inline)) {
+        const int64_t r = seq0 + cc * CH + min(lane, rows_of(cc) - 1);
+        load_to_lds4(beta + r, &sm.rawb[par][0]);
+        if (has_alpha) load_to_lds4(alpha + r, &sm.rawa[par][0]);
+    };
+    if (wave == 6 && nchunks > 0) {
+        load_ba(0, 0);
+        wait_global();
+    }
     // score tiles above the diagonal are read as zeros by the read-out and never written
     for (int i = tid; i < 2 * CH * L::CP; i += NW * 64) (&sm.p[0][0])[i] = 0;
     block_sync();
@@ -541,6 +555,7 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                 load_rows<DK, 0, CH>(q_buf[PAR], q, r0, n, lane);
                 load_v(v_buf[PAR], v, r0, n, dv, j0, lane);
             }
+            if (cc + 1 >= 0 && cc + 1 < nchunks) load_ba(cc + 1, PAR ^ 1);
             wait_global();
             if constexpr (GATE) {
                 if (has_gc) *reinterpret_cast<float4 *>(&sm.gc[slot][4 * lane]) = gcv;
@@ -760,18 +775,11 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
         }
     };
     // one loop per prep wave, so its registers need no merging between the two variants.
-    // Prep wave 0 also runs the decay scan of chunk c+2 after its tiles (it issues no LDS DMA,
-    // so its LDS writes never wait for loads); beta and alpha come one step ahead in registers.
+    // Prep wave 0 also runs the decay scan of chunk c+2 after its tiles (it issues no memory
+    // instruction, so neither its LDS writes nor its scan wait for loads); the loader brought
+    // that chunk's beta and alpha into LDS a step earlier.
     auto prep_loop = [&](auto pw_c) __attribute__((always_inline)) {
         constexpr int PW = decltype(pw_c)::value;
-        float nbeta = 0.f, nalpha = 1.f;
-        auto load_ba = [&](int64_t cc) __attribute__((always_inline)) {
-            const int64_t cl = cc < nchunks ? cc : nchunks - 1;
-            const int r = min(lane, rows_of(cl) - 1);
-            nbeta = beta[seq0 + cl * CH + r];
-            nalpha = has_alpha ? alpha[seq0 + cl * CH + r] : 1.f;
-        };
-        if (PW == 0 && nchunks > 0) load_ba(0);
         int sl1 = 2;  // (c+1) mod 3; (c+2) mod 3 is the slot after it
         for (int64_t c = -2; c < nchunks; ++c) {
             if constexpr (!GATE) {
@@ -794,8 +802,9 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                 const int64_t cc = c + 2;
                 if (cc < nchunks) {
                     const int sl2 = sl1 == 2 ? 0 : sl1 + 1;
-                    scan_chunk<DK>(sm, sl2, nbeta, nalpha, rows_of(cc), has_alpha, lane);
-                    load_ba(cc + 1);
+                    const int par = static_cast<int>(cc & 1);
+                    scan_chunk<DK>(sm, sl2, sm.rawb[par][lane], has_alpha ? sm.rawa[par][lane] : 1.f,
+                                   rows_of(cc), has_alpha, lane);
                 }
             }
             block_sync();

@@ -25,8 +25,8 @@
 // chunk, wave i on rows 16i..16i+15, lane (row, quarter) holding 8 features of each 32-wide
 // k-step in registers, which is both the A and the B layout of the 16x16x32 products), and
 // writes for the forward: q o G, k o G, k~ o rho(.->C) (bf16), G_C, and the chunk planes -- P,
-// the diagonal-block inverses (I + A_ii)^{-1} (by substitution in fp32, rounded once) and -A_ik
-// (bf16, in the forward's LDS layout).  The matrix-core forward's GATE variant copies these in
+// the diagonal-block inverses (I + A_ii)^{-1} (the forward's own series on bf16 matrix cores)
+// and -A_ik (bf16, in the forward's LDS layout).  The matrix-core forward's GATE variant copies these in
 // instead of forming them.  (The fp32 path forms the exact ratios itself; see the fp32 kernel.)
 //
 // The decode step applies Diag(a) to the state's rows in place of the scalar gate.
@@ -36,7 +36,7 @@
 namespace osdn {
 namespace {
 
-constexpr int kPlanesThreads = 256;
+constexpr int kPlanesThreads = 512;  // 8 waves: (16-row block, half of the key features)
 
 // 8 consecutive inputs as fp32
 __device__ __forceinline__ void load8(const float *p, float *o) {
@@ -60,6 +60,13 @@ __device__ __forceinline__ v8s frag8(const float *x, const float *f) {
     return __builtin_bit_cast(v8s, make_uint4(pack2(x[0] * f[0], x[1] * f[1]), pack2(x[2] * f[2], x[3] * f[3]),
                                               pack2(x[4] * f[4], x[5] * f[5]), pack2(x[6] * f[6], x[7] * f[7])));
 }
+// 8 bf16 values (4 packed words) times 8 fp32 factors, rounded to one bf16 fragment
+__device__ __forceinline__ v8s frag8p(const uint32_t *x, const float *f) {
+    return __builtin_bit_cast(v8s, make_uint4(pack2(bf_lo(x[0]) * f[0], bf_hi(x[0]) * f[1]),
+                                              pack2(bf_lo(x[1]) * f[2], bf_hi(x[1]) * f[3]),
+                                              pack2(bf_lo(x[2]) * f[4], bf_hi(x[2]) * f[5]),
+                                              pack2(bf_lo(x[3]) * f[6], bf_hi(x[3]) * f[7])));
+}
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
@@ -72,48 +79,77 @@ kda_planes_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                   const float *__restrict__ beta, uint16_t *__restrict__ qp,
                   uint16_t *__restrict__ kp, uint16_t *__restrict__ ktp,
                   uint16_t *__restrict__ planes, float *__restrict__ gcs, int64_t T,
-                  int64_t nchunks) {
+                  int64_t nchunks, int64_t total) {
     namespace KP = kda_planes;
-    constexpr int NS = DK / 32;  // 32-wide k-steps
-    constexpr int NV = NS * 8;   // feature values per lane: k-step s, element e -> 32 s + 8 lq + e
-    __shared__ float btot[4][DK];                            // product of a block's 16 gates
-    __shared__ alignas(16) uint16_t ycol[3][NS][64 * 8];     // k~ o (suffix product), B fragments
+    constexpr int NS = DK / 32;   // 32-wide k-steps
+    constexpr int NSH = NS / 2;   // k-steps of one feature half
+    constexpr int NV = NSH * 8;   // feature values per lane: k-step s0 + s, element e -> 32 (s0 + s) + 8 lq + e
+    __shared__ alignas(16) float btot[4][DK];                        // product of a block's 16 gates
+    __shared__ alignas(16) uint16_t ycol[3][NS][64 * 8];             // k~ o (suffix product), B fragments
     __shared__ alignas(16) float sbeta[KP::kRows];
-    __shared__ float sN[4][16 * 17];                         // A_ii, fp32
-    __shared__ alignas(16) uint16_t sdinv[4][256];
+    __shared__ alignas(16) float part[2][10][2][64 * 4];             // partial tiles per feature half
+    __shared__ alignas(16) uint16_t sN[4][256];                      // N of each block, for its A layout
 
-    const int64_t seg = blockIdx.x;  // (sequence, chunk)
-    const int64_t bh = seg / nchunks, c = seg % nchunks;
     const int tid = threadIdx.x;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // row block
+    const int w8 = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int w = w8 & 3, fh = w8 >> 2;  // row block, feature half
+    const int s0 = fh * NSH;
     const int lane = tid & 63, lr = lane & 15, lq = lane >> 4;
     const int r = 16 * w + lr;               // row in the chunk
+    auto feat = [&](int i) __attribute__((always_inline)) { return 32 * (s0 + i / 8) + 8 * lq + i % 8; };
+
+    // The workgroups are persistent: each takes every gridDim.x-th (sequence, chunk) and loads
+    // the lane's row of the next one (gates, q and k packed as bf16 pairs, d, beta) while it
+    // works on the current one.  Rows past the end: gate 1, zero operands, beta 0.
+    float pa[NV], pd[NV], pb;
+    uint32_t pq[NV / 2], pk[NV / 2];
+    auto fetch = [&](int64_t sg) __attribute__((always_inline)) {
+        const int64_t bh_ = sg / nchunks, t_ = (sg % nchunks) * KP::kRows + r;
+        if (sg < total && t_ < T) {
+            const int64_t off = (bh_ * T + t_) * DK;
+#pragma unroll
+            for (int s = 0; s < NSH; ++s) {
+                const int f0 = feat(8 * s);
+                load8(a + off + f0, pa + 8 * s);
+                const uint4 uq = *reinterpret_cast<const uint4 *>(q + off + f0);
+                const uint4 uk = *reinterpret_cast<const uint4 *>(k + off + f0);
+                pq[4 * s] = uq.x; pq[4 * s + 1] = uq.y; pq[4 * s + 2] = uq.z; pq[4 * s + 3] = uq.w;
+                pk[4 * s] = uk.x; pk[4 * s + 1] = uk.y; pk[4 * s + 2] = uk.z; pk[4 * s + 3] = uk.w;
+                load8(d + off + f0, pd + 8 * s);
+            }
+            pb = beta[bh_ * T + t_];
+        } else {
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                pa[i] = 1.f;
+                pd[i] = 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < NV / 2; ++i) pq[i] = pk[i] = 0u;
+            pb = 0.f;
+        }
+    };
+    fetch(blockIdx.x);
+    for (int64_t seg = blockIdx.x; seg < total; seg += gridDim.x) {
+    const int64_t bh = seg / nchunks, c = seg % nchunks;
     const int64_t t = c * KP::kRows + r;     // row in the sequence
     const bool valid = t < T;
     const int64_t rowoff = (bh * T + (valid ? t : 0)) * DK;
-
-    // the lane's row: gates, q, k, k~ (rows past the end: gate 1, zero operands, beta 0)
-    float av[NV], qv[NV], kv[NV], ktv[NV];
+    // the lane's row: gates, q, k (packed: qv[4 s + e] holds elements 2 e, 2 e + 1 of k-step
+    // s), k~ = d o k
+    float av[NV], ktv[NV];
+    uint32_t qv[NV / 2], kv[NV / 2];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        const int f0 = 32 * s + 8 * lq;
-        if (valid) {
-            float dd[8];
-            load8(a + rowoff + f0, av + 8 * s);
-            load8(q + rowoff + f0, qv + 8 * s);
-            load8(k + rowoff + f0, kv + 8 * s);
-            load8(d + rowoff + f0, dd);
+    for (int i = 0; i < NV; ++i) av[i] = pa[i];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) ktv[8 * s + e] = dd[e] * kv[8 * s + e];
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                av[8 * s + e] = 1.f;
-                qv[8 * s + e] = kv[8 * s + e] = ktv[8 * s + e] = 0.f;
-            }
-        }
+    for (int i = 0; i < NV / 2; ++i) {
+        qv[i] = pq[i];
+        kv[i] = pk[i];
+        ktv[2 * i] = pd[2 * i] * bf_lo(pk[i]);
+        ktv[2 * i + 1] = pd[2 * i + 1] * bf_hi(pk[i]);
     }
-    if (lq == 0) sbeta[r] = valid ? beta[bh * T + t] : 0.f;
+    if (fh == 0 && lq == 0) sbeta[r] = pb;
+    fetch(seg + gridDim.x);
 
     // segment products of the gates: pre = inclusive prefix, suf = exclusive suffix, tot = whole
     // segment, per feature, over the lane's aligned h-row segment (h = 1, 2, 4, 8, 16)
@@ -132,7 +168,7 @@ kda_planes_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
         const bool up = (lr & H) != 0;
         v4f ca = zero4(), cp = zero4();
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
+        for (int s = 0; s < NSH; ++s) {
             float fx[8], fy[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -140,8 +176,8 @@ kda_planes_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                 fy[e] = up ? 0.f : suf[8 * s + e];
             }
             const v8s y = frag8(ktv + 8 * s, fy);
-            ca = mfma32(frag8(kv + 8 * s, fx), y, ca);
-            cp = mfma32(frag8(qv + 8 * s, fx), y, cp);
+            ca = mfma32(frag8p(kv + 4 * s, fx), y, ca);
+            cp = mfma32(frag8p(qv + 4 * s, fx), y, cp);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -177,9 +213,14 @@ kda_planes_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
     grow(integral_constant<int, 8>{}, integral_constant<int, 0x140>{});  // row_mirror
     {  // the diagonal of P: factor 1
         v4f cp = zero4();
-        float one[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
 #pragma unroll
-        for (int s = 0; s < NS; ++s) cp = mfma32(frag8(qv + 8 * s, one), frag8(ktv + 8 * s, one), cp);
+        for (int s = 0; s < NSH; ++s) {
+            const float *ts = ktv + 8 * s;
+            const v8s xq = __builtin_bit_cast(v8s, make_uint4(qv[4 * s], qv[4 * s + 1], qv[4 * s + 2], qv[4 * s + 3]));
+            const v8s xt = __builtin_bit_cast(v8s, make_uint4(pack2(ts[0], ts[1]), pack2(ts[2], ts[3]),
+                                                              pack2(ts[4], ts[5]), pack2(ts[6], ts[7])));
+            cp = mfma32(xq, xt, cp);
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             if (4 * lq + e == lr) accP[e] += cp[e];
@@ -187,118 +228,146 @@ kda_planes_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
     // pre, suf, tot now span the lane's 16-row block
     if (lr == 0) {
 #pragma unroll
-        for (int s = 0; s < NS; ++s)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) btot[w][32 * s + 8 * lq + e] = tot[8 * s + e];
+        for (int s = 0; s < NSH; ++s) {
+            float *dst = &btot[w][feat(8 * s)];
+            *reinterpret_cast<float4 *>(dst) = make_float4(tot[8 * s], tot[8 * s + 1], tot[8 * s + 2], tot[8 * s + 3]);
+            *reinterpret_cast<float4 *>(dst + 4) = make_float4(tot[8 * s + 4], tot[8 * s + 5], tot[8 * s + 6], tot[8 * s + 7]);
+        }
     }
     if (w < 3) {
 #pragma unroll
-        for (int s = 0; s < NS; ++s)
-            *reinterpret_cast<v8s *>(&ycol[w][s][8 * lane]) = frag8(ktv + 8 * s, suf + 8 * s);
+        for (int s = 0; s < NSH; ++s)
+            *reinterpret_cast<v8s *>(&ycol[w][s0 + s][8 * lane]) = frag8(ktv + 8 * s, suf + 8 * s);
     }
     __syncthreads();
 
-    // products of the other blocks' totals: before this block (G at the block start) and after
-    float below[NV], above[NV];
+    // products over other blocks' totals, 8 features at a time from LDS
+    auto mul_btot = [&](float *x, int m) __attribute__((always_inline)) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
+        for (int s = 0; s < NSH; ++s) {
+            const float *src = &btot[m][feat(8 * s)];
+            const v4f b0 = ld4(src), b1 = ld4(src + 4);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int f = 32 * s + 8 * lq + e;
-            float bl = 1.f, ab = 1.f;
-            for (int m = 0; m < w; ++m) bl *= btot[m][f];
-            for (int m = w + 1; m < 4; ++m) ab *= btot[m][f];
-            below[8 * s + e] = bl;
-            above[8 * s + e] = ab;
-        }
-
-    // the forward's operands: q o G, k o G with G_r = below o pre; k~ o rho(.->C) = k~ o suf o above
-    if (valid) {
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            float g[8], h[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                g[e] = below[8 * s + e] * pre[8 * s + e];
-                h[e] = suf[8 * s + e] * above[8 * s + e];
+            for (int e = 0; e < 4; ++e) {
+                x[8 * s + e] *= b0[e];
+                x[8 * s + 4 + e] *= b1[e];
             }
-            const int64_t o = rowoff + 32 * s + 8 * lq;
-            *reinterpret_cast<v8s *>(qp + o) = frag8(qv + 8 * s, g);
-            *reinterpret_cast<v8s *>(kp + o) = frag8(kv + 8 * s, g);
-            *reinterpret_cast<v8s *>(ktp + o) = frag8(ktv + 8 * s, h);
         }
-    }
-    if (w == 0 && lr == 0) {  // G_C = the product of the four block totals
+    };
+    // the forward's operands: q o G, k o G with G = (blocks before) o pre; k~ o rho(.->C) =
+    // k~ o suf o (blocks after); G_C = the product of all four block totals
+    {
+        float g[NV], h[NV];
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            float gc[8];
+        for (int i = 0; i < NV; ++i) {
+            g[i] = pre[i];
+            h[i] = suf[i];
+        }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) gc[e] = tot[8 * s + e] * above[8 * s + e];
-            float *dst = gcs + seg * DK + 32 * s + 8 * lq;
-            *reinterpret_cast<float4 *>(dst) = make_float4(gc[0], gc[1], gc[2], gc[3]);
-            *reinterpret_cast<float4 *>(dst + 4) = make_float4(gc[4], gc[5], gc[6], gc[7]);
+        for (int m = 0; m < 4; ++m) {
+            if (m < w) mul_btot(g, m);
+            if (m > w) mul_btot(h, m);
+        }
+        if (valid) {
+#pragma unroll
+            for (int s = 0; s < NSH; ++s) {
+                const int64_t o = rowoff + feat(8 * s);
+                *reinterpret_cast<v8s *>(qp + o) = frag8p(qv + 4 * s, g + 8 * s);
+                *reinterpret_cast<v8s *>(kp + o) = frag8p(kv + 4 * s, g + 8 * s);
+                *reinterpret_cast<v8s *>(ktp + o) = frag8(ktv + 8 * s, h + 8 * s);
+            }
+        }
+        if (w == 3 && lr == 15) {  // G at the chunk's last row: (blocks 0..2) o the block's total
+#pragma unroll
+            for (int s = 0; s < NSH; ++s) {
+                float *dst = gcs + seg * DK + feat(8 * s);
+                *reinterpret_cast<float4 *>(dst) = make_float4(g[8 * s], g[8 * s + 1], g[8 * s + 2], g[8 * s + 3]);
+                *reinterpret_cast<float4 *>(dst + 4) = make_float4(g[8 * s + 4], g[8 * s + 5], g[8 * s + 6], g[8 * s + 7]);
+            }
         }
     }
 
+    // tiles (w, j), j < w: rows anchored at the last row of block j.  Each half's partial
+    // products go to LDS (slot w: the diagonal tile; 4 + w (w - 1) / 2 + j: tile (w, j))
+    float cross[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) cross[i] = 1.f;
+    *reinterpret_cast<v4f *>(&part[fh][w][0][4 * lane]) = accA;
+    *reinterpret_cast<v4f *>(&part[fh][w][1][4 * lane]) = accP;
+#pragma unroll
+    for (int j = 2; j >= 0; --j) {
+        if (j < w) {
+            v4f ca = zero4(), cp = zero4();
+#pragma unroll
+            for (int s = 0; s < NSH; ++s) {
+                float fx[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) fx[e] = pre[8 * s + e] * cross[8 * s + e];
+                const v8s y = *reinterpret_cast<const v8s *>(&ycol[j][s0 + s][8 * lane]);
+                ca = mfma32(frag8p(kv + 4 * s, fx), y, ca);
+                cp = mfma32(frag8p(qv + 4 * s, fx), y, cp);
+            }
+            const int slot = 4 + (w * (w - 1)) / 2 + j;
+            *reinterpret_cast<v4f *>(&part[fh][slot][0][4 * lane]) = ca;
+            *reinterpret_cast<v4f *>(&part[fh][slot][1][4 * lane]) = cp;
+            mul_btot(cross, j);
+        }
+    }
+    __syncthreads();
+
+    // the two halves summed: half 0 finishes the diagonal block (P, and the inverse of
+    // I + A_ii), half 1 the off-diagonal tiles (P and -A_ij)
     uint16_t *img = planes + seg * KP::kElems;
     uint16_t *pimg = img, *dimg = img + KP::kP, *aimg = img + KP::kP + KP::kDinv;
     const v4f b4 = ld4(&sbeta[16 * w + 4 * lq]);  // beta of the rows 4 lq + e of this block
     // after a quad transpose the lane holds row 4 lq + (lr & 3), columns 4 (lr >> 2) .. +3
     const int trow = 4 * lq + (lr & 3), tg = lr >> 2;
+    auto tile_sum = [&](int slot, int m) __attribute__((always_inline)) {
+        return ld4(&part[0][slot][m][4 * lane]) + ld4(&part[1][slot][m][4 * lane]);
+    };
     auto store_p = [&](int j, v4f x) __attribute__((always_inline)) {
         *reinterpret_cast<uint2 *>(pimg + (16 * w + trow) * KP::kPPitch + 16 * j + 4 * tg) =
             pack4u(quad_transpose(x, lane));
     };
-
-    // tiles (w, j), j < w: rows anchored at the last row of block j
-    float cross[NV];
+    if (fh == 1) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) cross[i] = 1.f;
-    for (int j = w - 1; j >= 0; --j) {
-        v4f ca = zero4(), cp = zero4();
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            float fx[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) fx[e] = pre[8 * s + e] * cross[8 * s + e];
-            const v8s y = *reinterpret_cast<const v8s *>(&ycol[j][s][8 * lane]);
-            ca = mfma32(frag8(kv + 8 * s, fx), y, ca);
-            cp = mfma32(frag8(qv + 8 * s, fx), y, cp);
+        for (int j = 0; j < 3; ++j) {
+            if (j < w) {
+                const int slot = 4 + (w * (w - 1)) / 2 + j;
+                *reinterpret_cast<uint2 *>(aimg + (slot - 4) * 256 + KP::blk(trow, tg)) =
+                    pack4u(quad_transpose(-b4 * tile_sum(slot, 0), lane));
+                store_p(j, tile_sum(slot, 1));
+            }
         }
-        const int tile = (w * (w - 1)) / 2 + j;
-        *reinterpret_cast<uint2 *>(aimg + tile * 256 + KP::blk(trow, tg)) =
-            pack4u(quad_transpose(-b4 * ca, lane));
-        store_p(j, cp);
-#pragma unroll
-        for (int s = 0; s < NS; ++s)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) cross[8 * s + e] *= btot[j][32 * s + 8 * lq + e];
-    }
-    store_p(w, accP);
+    } else {
+    store_p(w, tile_sum(w, 1));
     for (int j = w + 1; j < 4; ++j) store_p(j, zero4());
-
-    // (I + A_ii)^{-1} by forward substitution in fp32, one column per lane of the first 16
-    const v4f nA = b4 * accA;
+    // D = (I + N)^{-1}, N = diag(beta) A_ii strictly lower (so N^16 = 0), as
+    // (I - N)(I + N^2)(I + N^4)(I + N^8) on bf16 matrix cores.  N's C layout is its B layout; its
+    // A layout comes back through LDS.  The result, in the C layout of D^T = the A layout of D
+    // (lane holds row lr, columns 4 lq .. +3), is stored as the forward keeps it.
+    const v4f nC = b4 * tile_sum(w, 0);
+    uint16_t *scr = &sN[w][0];
+    *reinterpret_cast<uint2 *>(scr + KP::blk(trow, tg)) = pack4u(quad_transpose(nC, lane));
+    asm volatile("" ::: "memory");
+    const v4s Na = ld4s(scr + KP::blk(lr, lq)), Nb = pack4(nC);
+    v4f X = mfma16(Na, Nb, zero4()), Xt = mfma16(Nb, Na, zero4());  // N^2 (B layout), its transpose
+    const v4s N2a = pack4(Xt), N2b = pack4(X);
+    X = mfma16(N2a, N2b, zero4());
+    Xt = mfma16(N2b, N2a, zero4());
+    const v4s N4a = pack4(Xt), N4b = pack4(X);
+    v4f Y = mfma16(N4b, N4a, zero4());  // (N^8)^T
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sN[w][(4 * lq + e) * 17 + lr] = nA[e];
-    __syncthreads();
-    if (lane < 16) {
-        float dc[16];
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-            float acc = rr == lane ? 1.f : 0.f;
-#pragma unroll
-            for (int ss = 0; ss < rr; ++ss) acc -= sN[w][rr * 17 + ss] * dc[ss];
-            dc[rr] = acc;
-        }
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr)
-            sdinv[w][KP::blk(rr, lane >> 2) + (lane & 3)] = f32_to_bf16_bits(dc[rr]);
+    for (int e = 0; e < 4; ++e)
+        if (4 * lq + e == lr) Y[e] += 1.f;
+    Y = mfma16(N4b, pack4(Y), Y);
+    Y = mfma16(N2b, pack4(Y), Y);
+    const uint2 nb = __builtin_bit_cast(uint2, Nb);
+    Y = mfma16(__builtin_bit_cast(v4s, make_uint2(nb.x ^ 0x80008000u, nb.y ^ 0x80008000u)), pack4(Y), Y);
+    *reinterpret_cast<uint2 *>(dimg + w * 256 + KP::blk(lr, lq)) = pack4u(Y);
     }
-    __syncthreads();
-    if (lane < 32)
-        *reinterpret_cast<uint4 *>(dimg + w * 256 + 8 * lane) =
-            *reinterpret_cast<const uint4 *>(&sdinv[w][8 * lane]);
+    __syncthreads();  // the next chunk reuses the LDS
+    }
 }
 
 // one decode token with the channel-wise gate (same layout as step_kernel)
@@ -389,14 +458,29 @@ step_kda_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k, const TQ *__
     }
 }
 
+// one persistent workgroup per compute unit (its registers allow no second)
+int compute_units() {
+    static int n = 0;
+    if (n == 0) {
+        int dev = 0, cu = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cu > 0)
+            n = cu;
+        else
+            n = 256;
+    }
+    return n;
+}
+
 template <int DK, typename TD>
 hipError_t planes_typed(const KdaPrepArgs &a, hipStream_t stream) {
-    const dim3 grid(static_cast<unsigned>(a.BH * a.nchunks));
+    const int64_t total = a.BH * a.nchunks;
+    const dim3 grid(static_cast<unsigned>(total < compute_units() ? total : compute_units()));
     hipLaunchKernelGGL((kda_planes_kernel<DK, TD>), grid, dim3(kPlanesThreads), 0, stream,
                        static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
                        static_cast<const TD *>(a.d), a.alpha_ch, a.beta,
                        static_cast<uint16_t *>(a.qp), static_cast<uint16_t *>(a.kp),
-                       static_cast<uint16_t *>(a.ktp), a.planes, a.gcs, a.T, a.nchunks);
+                       static_cast<uint16_t *>(a.ktp), a.planes, a.gcs, a.T, a.nchunks, total);
     return hipGetLastError();
 }
 

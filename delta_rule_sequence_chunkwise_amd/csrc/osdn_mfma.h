@@ -78,6 +78,10 @@ __device__ __forceinline__ v8s c_to_frag(v4f x0, v4f x1) {
 __device__ __forceinline__ void load_to_lds16(const void *g, void *lds_base) {
     __builtin_amdgcn_global_load_lds((glb_void_t *)(g), (lds_void_t *)(lds_base), 16, 0, 0);
 }
+// 4 bytes from global memory straight into LDS: lane l's bytes land at lds_base + 4 l
+__device__ __forceinline__ void load_to_lds4(const void *g, void *lds_base) {
+    __builtin_amdgcn_global_load_lds((glb_void_t *)(g), (lds_void_t *)(lds_base), 4, 0, 0);
+}
 // Workgroup barrier for LDS hand-offs: wait for this wave's LDS operations, then s_barrier.
 // The waits are the s_waitcnt builtin (not inline asm) so the compiler's own wait insertion
 // knows the counters they drain; the empty asm statements keep memory accesses on their side.

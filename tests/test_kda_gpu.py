@@ -105,6 +105,13 @@ def test_kda_strong_decay(case):
     check(x, qkv, chunk=chunk, label=str(case))
 
 
+def test_kda_more_chunks_than_compute_units():
+    """2 x 8 sequences of 1100 tokens: 288 chunks (the last of each ragged), more than the
+    planes kernel's persistent workgroups, so each takes several in turn."""
+    x = kda_inputs(2, 8, 1100, 128, 128, "bf16", seed=31, gates=(0.3, 1.0))
+    check(x, "bf16", label="288 chunks")
+
+
 def test_uniform_channels_match_scalar_gate():
     """Equal channel factors on the GPU's KDA path against the scalar-gate path on the GPU."""
     torch, _ = torch_dev()
