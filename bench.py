@@ -93,8 +93,8 @@ def load_traffic(name, paths):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--precond-steps", type=int, default=20)
     ap.add_argument("--kda-steps", type=int, default=10)
@@ -507,8 +507,9 @@ def bench_decode(n_steps, torch, dev, synth, distinct=64):
                                "note": "each call updates a different state, so a state is "
                                        "read again only after three others (384 MiB) were "
                                        "streamed: it cannot be served from the Infinity Cache"},
-            "note": "in place, the 128 MiB state fits in the 256 MB Infinity Cache; the "
-                    "state_rotation figure is the one free of it"}
+            "note": "in place, the 128 MiB state could stay in the 256 MB Infinity Cache, but the "
+                    "kernel's state accesses are non-temporal; the state_rotation figure (four "
+                    "states, 512 MiB) is free of the cache by construction"}
 
 
 def bench_precond(n_steps, torch, dev, synth, w, x, fwd, cpu):

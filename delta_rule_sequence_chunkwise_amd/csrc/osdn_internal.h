@@ -31,6 +31,19 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
     return bf16_t{f32_to_bf16_bits(x)};
 }
 
+// A decode step streams the whole state through once per token (in a model, every layer's state
+// in turn), so its state accesses are non-temporal: they do not displace what the caches hold.
+__device__ __forceinline__ float4 load_stream(const float4 *p) {
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    const f4 x = __builtin_nontemporal_load(reinterpret_cast<const f4 *>(p));
+    return make_float4(x.x, x.y, x.z, x.w);
+}
+__device__ __forceinline__ void store_stream(float4 *p, float4 v) {
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    const f4 x = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(x, reinterpret_cast<f4 *>(p));
+}
+
 // ---- launch arguments -----------------------------------------------------------------------
 struct ChunkArgs {
     const void *q, *k, *v, *d;

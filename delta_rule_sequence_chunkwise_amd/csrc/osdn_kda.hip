@@ -394,7 +394,7 @@ step_kda_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k, const TQ *__
     float4 *Mrow = reinterpret_cast<float4 *>(S + bh * DK * DV);
     float4 m[RPT];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) m[i] = Mrow[(rg + i * RG) * TPR + cg];
+    for (int i = 0; i < RPT; ++i) m[i] = load_stream(&Mrow[(rg + i * RG) * TPR + cg]);
 
     if (tid < DK) {
         const float kv = to_f32(k[bh * DK + tid]), qv = to_f32(q[bh * DK + tid]);
@@ -454,7 +454,7 @@ step_kda_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k, const TQ *__
         mn.y = ar * m[i].y + w * u.y;
         mn.z = ar * m[i].z + w * u.z;
         mn.w = ar * m[i].w + w * u.w;
-        Mrow[row * TPR + cg] = mn;
+        store_stream(&Mrow[row * TPR + cg], mn);
     }
 }
 

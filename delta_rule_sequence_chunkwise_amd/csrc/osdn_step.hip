@@ -10,7 +10,10 @@
 // The step is bound by HBM bandwidth: M is dk*dv*4 bytes in and out per (b,h), everything
 // else is a few hundred bytes.  One workgroup of 256 threads owns one (b,h); thread t holds
 // four consecutive value columns (one 16-byte vector) of every (256/(dv/4))-th key row, so
-// each wavefront moves whole contiguous rows per load.
+// each wavefront moves whole contiguous rows per load.  The state is read and written with
+// non-temporal accesses: in a model every layer's state streams through once per token, so
+// none of it is worth keeping in the caches (measured at the decode shape with the state
+// rotated over four buffers: 48.5 us per step against 56.7 us with ordinary accesses).
 #include "osdn_internal.h"
 
 namespace osdn {
@@ -40,7 +43,7 @@ step_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k, const TQ *__rest
     float4 *Mrow = reinterpret_cast<float4 *>(S + bh * DK * DV);
     float4 m[RPT];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) m[i] = Mrow[(rg + i * RG) * TPR + cg];
+    for (int i = 0; i < RPT; ++i) m[i] = load_stream(&Mrow[(rg + i * RG) * TPR + cg]);
 
     if (tid < DK) {
         const float kv = to_f32(k[bh * DK + tid]);
@@ -102,7 +105,7 @@ step_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k, const TQ *__rest
         mn.y = al * m[i].y + w * u.y;
         mn.z = al * m[i].z + w * u.z;
         mn.w = al * m[i].w + w * u.w;
-        Mrow[(rg + i * RG) * TPR + cg] = mn;
+        store_stream(&Mrow[(rg + i * RG) * TPR + cg], mn);
     }
 }
 
