@@ -492,6 +492,16 @@ int64_t osdn_chunk_bwd_workspace(int64_t B, int64_t H, int64_t T, int32_t dk, in
     return u < 0 ? -1 : 2 * b + t + 2 * u;
 }
 
+int64_t osdn_chunk_bwd_states_workspace(int64_t B, int64_t H, int64_t T, int32_t dk, int32_t dv,
+                                        osdn_dtype qkv) {
+    const int64_t b = bwd_ckpt_bytes(B, H, T, dk, dv, qkv);
+    if (b < 0) return -1;
+    const int64_t t = bwd_tinv_bytes(B, H, T, dk, qkv);
+    if (t < 0) return -1;
+    const int64_t u = bwd_rows_bytes(B, H, T, dv, qkv);
+    return u < 0 ? -1 : b + t + u;
+}
+
 }  // extern "C"
 
 namespace {
@@ -515,7 +525,10 @@ osdn_status chunk_bwd_impl(const void *q, const void *k, const void *v, const fl
     if (tk < 0) return OSDN_ERR_SHAPE;
     const int64_t ub = bwd_rows_bytes(B, H, T, dv, qkv);
     if (ub < 0) return OSDN_ERR_SHAPE;
-    const int64_t wsb = 2 * ck + tk + 2 * ub;
+    // workspace: [M0 checkpoints] dMC checkpoints, chunk planes, [U] dR; the bracketed parts
+    // only when the states are not given (they are then the caller's)
+    const int64_t m0b = states_given ? 0 : ck, u0b = states_given ? 0 : ub;
+    const int64_t wsb = m0b + ck + tk + u0b + ub;
     int64_t BH = 1;
     if (!mul_ok(BH, B, kMaxElems) || !mul_ok(BH, H, kMaxElems)) return OSDN_ERR_SHAPE;
     int64_t tok = BH, st = BH;
@@ -576,17 +589,18 @@ osdn_status chunk_bwd_impl(const void *q, const void *k, const void *v, const fl
     }
 
     char *ws = static_cast<char *>(workspace);
+    char *sts = static_cast<char *>(const_cast<void *>(states));
     osdn::BwdArgs a{q, k, v, d, beta, alpha, S0, grad_o, grad_S_T, grad_q, grad_k, grad_v,
                     grad_beta, grad_alpha, grad_d, grad_S0,
-                    T > 0 ? (states_given ? const_cast<void *>(states) : ws) : nullptr,
-                    T > 0 ? ws + ck : nullptr, states_given,
-                    T > 0 && tk > 0 ? reinterpret_cast<uint16_t *>(ws + 2 * ck) : nullptr,
+                    T > 0 ? (states_given ? static_cast<void *>(sts) : ws) : nullptr,
+                    T > 0 ? ws + m0b : nullptr, states_given,
+                    T > 0 && tk > 0 ? reinterpret_cast<uint16_t *>(ws + m0b + ck) : nullptr,
                     T > 0 && ub > 0
-                        ? reinterpret_cast<uint16_t *>(
-                              states_given ? static_cast<char *>(const_cast<void *>(states)) + uoff
-                                           : ws + 2 * ck + tk)
+                        ? reinterpret_cast<uint16_t *>(states_given ? sts + uoff
+                                                                    : ws + m0b + ck + tk)
                         : nullptr,
-                    T > 0 && ub > 0 ? reinterpret_cast<uint16_t *>(ws + 2 * ck + tk + ub) : nullptr,
+                    T > 0 && ub > 0 ? reinterpret_cast<uint16_t *>(ws + m0b + ck + tk + u0b)
+                                    : nullptr,
                     BH, T, dk, dv, qkv, d_dtype};
     const hipError_t err = osdn::launch_chunk_bwd(a, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? OSDN_OK : OSDN_ERR_LAUNCH;

@@ -24,7 +24,8 @@ STATUS = {0: "OSDN_OK", -1: "OSDN_ERR_NULL", -2: "OSDN_ERR_SHAPE", -3: "OSDN_ERR
 EXPORTS = ("osdn_chunk_fwd", "osdn_step", "osdn_precond_scan", "osdn_precond_step",
            "osdn_chunk_fwd_kda", "osdn_chunk_fwd_kda_workspace", "osdn_chunk_fwd_kda_noalloc",
            "osdn_step_kda",
-           "osdn_chunk_bwd", "osdn_chunk_bwd_workspace", "osdn_chunk_states_bytes",
+           "osdn_chunk_bwd", "osdn_chunk_bwd_workspace", "osdn_chunk_bwd_states_workspace",
+           "osdn_chunk_states_bytes",
            "osdn_chunk_fwd_states", "osdn_chunk_bwd_states", "osdn_status_string",
            "osdn_abi_version")
 
@@ -71,6 +72,8 @@ def lib() -> ctypes.CDLL:
     L.osdn_step_kda.argtypes = [vp] * 8 + [i64, i64, i32, i32, ctypes.c_int, ctypes.c_int, vp]
     L.osdn_chunk_bwd_workspace.restype = i64
     L.osdn_chunk_bwd_workspace.argtypes = [i64, i64, i64, i32, i32, ctypes.c_int]
+    L.osdn_chunk_bwd_states_workspace.restype = i64
+    L.osdn_chunk_bwd_states_workspace.argtypes = [i64, i64, i64, i32, i32, ctypes.c_int]
     L.osdn_chunk_bwd.restype = ctypes.c_int
     L.osdn_chunk_bwd.argtypes = [vp] * 17 + [i64, i64, i64, i64, i32, i32, ctypes.c_int,
                                              ctypes.c_int, vp]
@@ -391,6 +394,13 @@ def bwd_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, dtype_code: in
     return n
 
 
+def bwd_states_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, dtype_code: int) -> int:
+    n = lib().osdn_chunk_bwd_states_workspace(B, H, T, dk, dv, dtype_code)
+    if n < 0:
+        raise ValueError("invalid shape for the backward's workspace")
+    return n
+
+
 def osdn_chunk_bwd(q, k, v, beta, d, alpha, S0, grad_o, grad_S_T=None, *, grads=None,
                    want_grad_S0: bool = True, workspace=None, states=None, stream=None):
     """Gradients of osdn_chunk_fwd(q, k, v, beta, d, alpha, S0) for output gradients grad_o
@@ -429,7 +439,8 @@ def osdn_chunk_bwd(q, k, v, beta, d, alpha, S0, grad_o, grad_S_T=None, *, grads=
         g.setdefault("grad_S0", new((B, H, dk, dv), torch.float32))
     else:
         g["grad_S0"] = None
-    need = bwd_workspace_bytes(B, H, T, dk, dv, _dtype_code(q))
+    need = (bwd_workspace_bytes if states is None else bwd_states_workspace_bytes)(
+        B, H, T, dk, dv, _dtype_code(q))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     wsb = workspace.numel() * workspace.element_size()

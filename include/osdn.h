@@ -247,10 +247,14 @@ osdn_status osdn_chunk_bwd(const void *q, const void *k, const void *v, const fl
  *
  * osdn_chunk_bwd_states: as osdn_chunk_bwd, with `states` (input) from osdn_chunk_fwd_states on
  * the same inputs; it may not overlap an output or the workspace.  The gradients are bitwise
- * those of osdn_chunk_bwd.  The workspace is osdn_chunk_bwd_workspace bytes as there.
+ * those of osdn_chunk_bwd.  The workspace holds only what the states do not (the state gradient
+ * at every chunk end, the chunk planes and, for bf16 inputs, dR):
+ * osdn_chunk_bwd_states_workspace(B, H, T, dk, dv, qkv) bytes, 256-byte aligned.
  */
 int64_t osdn_chunk_states_bytes(int64_t B, int64_t H, int64_t T, int32_t dk, int32_t dv,
                                 osdn_dtype qkv); /* -1 if invalid */
+int64_t osdn_chunk_bwd_states_workspace(int64_t B, int64_t H, int64_t T, int32_t dk, int32_t dv,
+                                        osdn_dtype qkv); /* -1 if invalid */
 
 osdn_status osdn_chunk_fwd_states(const void *q, const void *k, const void *v,
                                   const float *beta, const void *d, const float *alpha,

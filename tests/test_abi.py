@@ -375,5 +375,21 @@ def test_chunk_bwd_states_rejects(L, over, status):
     assert call_bwd_states(L, **over) == status
 
 
+def test_bwd_states_workspace_is_smaller(L):
+    """With the forward's states given, the backward's workspace drops the M0 checkpoints and U
+    (the caller's states hold them): exactly that size is accepted, one byte less rejected."""
+    full = L.osdn_chunk_bwd_workspace(2, 3, 100, 128, 64, osdn.OSDN_BF16)
+    sw = L.osdn_chunk_bwd_states_workspace(2, 3, 100, 128, 64, osdn.OSDN_BF16)
+    states = L.osdn_chunk_states_bytes(2, 3, 100, 128, 64, osdn.OSDN_BF16)
+    assert sw + states == full
+    # sizes are checked before any launch (fake addresses: only the rejection can be observed
+    # without a device)
+    assert call_bwd_states(L, wsb=sw - 1) == -2
+    f32 = L.osdn_chunk_bwd_states_workspace(2, 3, 100, 128, 64, osdn.OSDN_F32)
+    assert f32 + L.osdn_chunk_states_bytes(2, 3, 100, 128, 64, osdn.OSDN_F32) == \
+        L.osdn_chunk_bwd_workspace(2, 3, 100, 128, 64, osdn.OSDN_F32)
+    assert L.osdn_chunk_bwd_states_workspace(2, 3, 100, 96, 64, osdn.OSDN_BF16) == -1
+
+
 def test_chunk_bwd_states_empty_work_is_ok(L):
     assert call_bwd_states(L, B=0) == 0
