@@ -48,13 +48,12 @@ if ROOT not in sys.path:
 METRIC = "tokens/s + TFLOP/s (fraction of bf16 MFMA peak), OSDN chunkwise fwd"
 PEAK_HBM = 8.0e12      # bytes/s, MI355X HBM3E
 PEAK_BF16 = 2.5e15     # FLOP/s, MI355X dense bf16 matrix peak
-CHUNK_KERNEL_SRC = ["delta_rule_sequence_chunkwise_amd/csrc/osdn_chunk_mfma.hip",
-                    "delta_rule_sequence_chunkwise_amd/csrc/osdn_mfma.h"]
-STEP_KERNEL_SRC = ["delta_rule_sequence_chunkwise_amd/csrc/osdn_step.hip"]
-KDA_PREP_SRC = ["delta_rule_sequence_chunkwise_amd/csrc/osdn_kda.hip",
-                "delta_rule_sequence_chunkwise_amd/csrc/osdn_mfma.h"]
-PRECOND_KERNEL_SRC = ["delta_rule_sequence_chunkwise_amd/csrc/osdn_precond.hip",
-                      "delta_rule_sequence_chunkwise_amd/csrc/osdn_mfma.h"]
+_CSRC = "delta_rule_sequence_chunkwise_amd/csrc/"
+CHUNK_KERNEL_SRC = [_CSRC + f for f in ("osdn_chunk_mfma.hip", "osdn_mfma.h", "osdn_internal.h")]
+STEP_KERNEL_SRC = [_CSRC + f for f in ("osdn_step.hip", "osdn_internal.h")]
+KDA_KERNEL_SRC = [_CSRC + f for f in ("osdn_kda.hip", "osdn_chunk_mfma.hip", "osdn_mfma.h",
+                                      "osdn_internal.h")]
+PRECOND_KERNEL_SRC = [_CSRC + f for f in ("osdn_precond.hip", "osdn_mfma.h", "osdn_internal.h")]
 
 
 def flops_per_head_token(dk, dv, C):
@@ -431,9 +430,12 @@ def bench_kda(n_steps, torch, dev, synth, w, x, fwd, cpu):
            "roofline": {"bound": "hbm", "achieved": round(alg / per / 1e9, 2),
                         "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                         "frac": round(alg / per / PEAK_HBM, 5), "alg_bytes_per_step": alg,
+                        "traffic": load_traffic("kda_1.3b_traffic", KDA_KERNEL_SRC),
                         "note": "two launches: the planes kernel writes and the forward "
                                 "reads the gate-scaled q, k, k~ and the chunk planes "
-                                "(workspace traffic beyond alg)"}}
+                                "(workspace traffic beyond alg); traffic is both launches' "
+                                "rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 from "
+                                "profiles/kda_1.3b_traffic.json"}}
     if cpu:
         import oracle
         o_ref, S_ref = oracle.chunk_fwd(x["q"], x["k"], x["v"], x["beta"], x["d"], None,
