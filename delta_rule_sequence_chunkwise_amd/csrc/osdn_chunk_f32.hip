@@ -9,8 +9,8 @@
 //
 //   a1  k~ = d (.) k;  g = running sum of ln(alpha) inside the chunk
 //   a2  A[r][s] = beta_r e^{g_r - g_s} <k_r, k~_s>  for s < r          (chunk Gram matrix)
-//   a3  T = (I + A)^{-1}, unit lower triangular                          (UT transform)
-//   a4  R = diag(beta) (V - diag(e^g) K M);  U = T R                     (pseudo-values)
+//   a3  R = diag(beta) (V - diag(e^g) K M)
+//   a4  U = (I + A)^{-1} R, by forward substitution down the rows       (UT transform)
 //   a5  P[r][s] = e^{g_r - g_s} <q_r, k~_s>  for s <= r                 (intra-chunk scores)
 //   a6  O = diag(e^g) Q M + P U;  M <- e^{g_C} M + (diag(e^{g_C - g}) K~)^T U
 //
@@ -28,7 +28,38 @@
 namespace osdn {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;  // eight waves: two per SIMD, so one hides the other's LDS waits
+
+// X <- (I + A)^{-1} X in place for a strictly lower C x C A (C rows, NC columns): row r of the
+// result is X_r - sum_{s<r} A[r][s] (result)_s, taken row by row.  Column j is owned by TPC
+// adjacent lanes; lane sub keeps rows s = i TPC + sub of the column in registers, so each row
+// costs one short dot product and a reduction over the TPC lanes.
+template <int C, int NC, int PX, int PA>
+__device__ __forceinline__ void solve_unit_lower(float *X, const float *A, int tid) {
+    constexpr int TPC = kThreads / NC, RPT = C / TPC;
+    static_assert(TPC * NC == kThreads && RPT * TPC == C && 64 % TPC == 0, "solve layout");
+    const int j = tid / TPC, sub = tid % TPC;
+    float mine[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) mine[i] = 0.f;
+#pragma unroll
+    for (int r = 0; r < C; ++r) {
+        float part = 0.f;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            if (i * TPC < r) {
+                const int s = i * TPC + sub;
+                if (s < r) part += A[r * PA + s] * mine[i];
+            }
+        }
+#pragma unroll
+        for (int m = 1; m < TPC; m <<= 1) part += __shfl_xor(part, m);
+        const float val = X[r * PX + j] - part;
+        if (r % TPC == sub) mine[r / TPC] = val;
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) X[(i * TPC + sub) * PX + j] = mine[i];
+}
 
 template <int DK, int BV, int CH, typename TQ, typename TD, bool GATE>
 __global__ void __launch_bounds__(kThreads)
@@ -43,10 +74,8 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
     __shared__ float sX[CH * PX];   // K, later Q
     __shared__ float sKt[CH * PX];  // K~ = d (.) K
     __shared__ float sA[CH * PC];   // A, later P
-    __shared__ float sT[CH * PC];   // T = (I + A)^{-1}
     __shared__ float sM[DK * PV];   // state slice M[:, j0:j0+BV]
-    __shared__ float sR[CH * PV];   // V, then R
-    __shared__ float sU[CH * PV];   // U
+    __shared__ float sR[CH * PV];   // V, then R, then U
     __shared__ float sQM[CH * PV];  // Q M
     __shared__ float sg[CH];        // g (running log-decay)
     __shared__ float sb[CH];        // beta
@@ -118,17 +147,19 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
             }
         }
         __syncthreads();
-        if (tid == 0) {
-            float acc = 0.f;
-            for (int r = 0; r < CH; ++r) {
-                acc += sg[r];
-                sg[r] = acc;
+        if (tid < 64) {  // running sum of ln(alpha) by a scan over wave 0's lanes
+            float acc = tid < CH ? sg[tid] : 0.f;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float up = __shfl_up(acc, off);
+                if (tid >= off) acc += up;
             }
-        }
-        __syncthreads();
-        if (tid < CH) {
-            sgam[tid] = __expf(sg[tid]);
-            sdec[tid] = __expf(sg[CH - 1] - sg[tid]);
+            const float last = __shfl(acc, CH - 1);
+            if (tid < CH) {
+                sg[tid] = acc;
+                sgam[tid] = __expf(acc);
+                sdec[tid] = __expf(last - acc);
+            }
         }
         __syncthreads();
 
@@ -148,46 +179,21 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
             }
             sA[r * PC + s] = val;
         }
-        __syncthreads();
-
-        if (tid < CH) {
-            // a3: column j of T by forward substitution, T[r][j] = delta_rj - sum A[r][s] T[s][j]
-            const int j = tid;
-            for (int r = 0; r < CH; ++r) {
-                float val;
-                if (r < j) {
-                    val = 0.f;
-                } else if (r == j) {
-                    val = 1.f;
-                } else {
-                    float acc = 0.f;
-                    for (int s = j; s < r; ++s) acc += sA[r * PC + s] * sT[s * PC + j];
-                    val = -acc;
-                }
-                sT[r * PC + j] = val;
-            }
-        } else {
-            // a4 (first half): R = diag(beta) (V - diag(e^g) K M)
-            for (int idx = tid - CH; idx < CH * BV; idx += kThreads - CH) {
-                const int r = idx / BV, j = idx % BV;
-                float km = 0.f;
-                if constexpr (GATE) {
-                    for (int i = 0; i < DK; ++i) km += sX[r * PX + i] * decay(r, i) * sM[i * PV + j];
-                } else {
-                    for (int i = 0; i < DK; ++i) km += sX[r * PX + i] * sM[i * PV + j];
-                }
-                sR[r * PV + j] = sb[r] * (sR[r * PV + j] - sgam[r] * km);
-            }
-        }
-        __syncthreads();
-
-        // a4 (second half): U = T R; meanwhile stage Q over K (K is no longer read)
+        // a3: R = diag(beta) (V - diag(e^g) K M)
         for (int idx = tid; idx < CH * BV; idx += kThreads) {
             const int r = idx / BV, j = idx % BV;
-            float acc = 0.f;
-            for (int s = 0; s <= r; ++s) acc += sT[r * PC + s] * sR[s * PV + j];
-            sU[r * PV + j] = acc;
+            float km = 0.f;
+            if constexpr (GATE) {
+                for (int i = 0; i < DK; ++i) km += sX[r * PX + i] * decay(r, i) * sM[i * PV + j];
+            } else {
+                for (int i = 0; i < DK; ++i) km += sX[r * PX + i] * sM[i * PV + j];
+            }
+            sR[r * PV + j] = sb[r] * (sR[r * PV + j] - sgam[r] * km);
         }
+        __syncthreads();
+
+        // a4: U = (I + A)^{-1} R in place; then stage Q over K (K is no longer read)
+        solve_unit_lower<CH, BV, PV, PC>(sR, sA, tid);
         for (int idx = tid; idx < CH * DK; idx += kThreads) {
             const int r = idx / DK, i = idx % DK;
             sX[r * PX + i] = r < n ? to_f32(q[(row0 + r) * DK + i]) : 0.f;
@@ -227,7 +233,7 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
             const int r = idx / BV, j = idx % BV;
             if (o && r < n) {
                 float acc = sgam[r] * sQM[r * PV + j];
-                for (int s = 0; s <= r; ++s) acc += sA[r * PC + s] * sU[s * PV + j];
+                for (int s = 0; s <= r; ++s) acc += sA[r * PC + s] * sR[s * PV + j];
                 o[(row0 + r) * dv + j0 + j] = from_f32<TQ>(acc);
             }
         }
@@ -237,11 +243,11 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
             float acc = 0.f;
             if constexpr (GATE) {
                 for (int s = 0; s < CH; ++s)
-                    acc += ratio(CH - 1, s, i) * sKt[s * PX + i] * sU[s * PV + j];
+                    acc += ratio(CH - 1, s, i) * sKt[s * PX + i] * sR[s * PV + j];
                 sM[i * PV + j] = decay(CH - 1, i) * sM[i * PV + j] + acc;
             } else {
                 for (int s = 0; s < CH; ++s)
-                    acc += sdec[s] * sKt[s * PX + i] * sU[s * PV + j];
+                    acc += sdec[s] * sKt[s * PX + i] * sR[s * PV + j];
                 sM[i * PV + j] = gam_last * sM[i * PV + j] + acc;
             }
         }
