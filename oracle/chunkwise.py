@@ -294,3 +294,99 @@ def chunk_bwd(q, k, v, beta, d, alpha=None, S0=None, do=None, dS_T=None, chunk: 
                 dM = gam[-1] * dM + Q.T @ (gam[:, None] * dO) - K.T @ ((gam * bt)[:, None] * dR)
             out["dS0"][b, h] = dM
     return out
+
+
+def _pair_decays(a):
+    """rho[r, s, f] = prod_{s < t <= r} a[t, f] for s <= r (1 on the diagonal, 0 above), by
+    running products down each column: exact for gates of any size, zero included."""
+    n, dk = a.shape
+    rho = np.zeros((n, n, dk))
+    for s in range(n):
+        run = np.ones(dk)
+        rho[s, s] = run
+        for r in range(s + 1, n):
+            run = run * a[r]
+            rho[r, s] = run
+    return rho
+
+
+def chunk_bwd_channel(q, k, v, beta, d, alpha_ch, S0=None, do=None, dS_T=None,
+                      chunk: int = 32):
+    """Chunk form of the reverse pass with the channel-wise gate (same contract and outputs as
+    ``oracle.backward.chunk_bwd`` with ``alpha_ch`` and no scalar decay), derived here by
+    differentiating the chunk algebra of ``chunk_fwd_channel``.  Per chunk, with M0 the state at
+    its start, dMC the gradient with respect to the state at its end, L its last row,
+    G_r = prod_{t<=r} a_t, rho(s->r) = prod_{s<t<=r} a_t, W_s = rho(s->L) (all per feature f),
+    K^ = K o G, Q^ = Q o G, K~w = K~ o W, and A, P as in ``chunk_fwd_channel``:
+
+        dU  = P^T dO + K~w dMC                 dR = (I + A)^{-T} dU
+        dM0 = Diag(G_L) dMC + Q^T dO - K^T diag(b) dR      (with Q^, K^)
+        dP  = lower-inclusive(dO U^T)          dA = -strictly-lower(dR U^T)
+        dQ[r,f]  = G_rf (dO M0^T)[r,f] + sum_s dP[r,s] k~_sf rho_f(s->r)
+        dK'[r,f] = -b_r G_rf (dR M0^T)[r,f] + b_r sum_s dA[r,s] k~_sf rho_f(s->r)
+        dK~[s,f] = W_sf (U dMC^T)[s,f] + sum_r (dP[r,s] q_rf + b_r dA[r,s] k_rf) rho_f(s->r)
+        dV  = diag(b) dR
+        db_r = <dR_r, v_r - (K^ M0)_r> + sum_s dA[r,s] (A[r,s] / b_r)
+        dLg[r,f] = q_rf dQ[r,f] + k_rf dK'[r,f] - k~_rf dK~[r,f]
+                   + [r = L] (G_Lf <dMC[f,:], M0[f,:]> + sum_s k~_sf W_sf (U dMC^T)[s,f])
+        d ln a_t = sum_{t <= r <= L} dLg[r] ;  da = d ln a / a
+        dd  = dK~ o K ;  dK = dK' + dK~ o D
+
+    dLg is the gradient with respect to the running log-gate sums Lg_r = ln G_r, each row's
+    taken as its own variable: it collects every place Lg_r enters (the G factors of Q^ and K^,
+    both ends of rho, W, and G_L on the carried state).  The gate gradient divides by a, so it is
+    defined for gates in (0, 1]."""
+    q, k, v, beta, d, alpha_ch = (np.asarray(x, dtype=np.float64)
+                                  for x in (q, k, v, beta, d, alpha_ch))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    out = dict(dq=np.zeros_like(q), dk=np.zeros_like(k), dv=np.zeros_like(v),
+               dbeta=np.zeros_like(beta), dd=np.zeros_like(d), dalpha=None,
+               dalpha_ch=np.zeros_like(alpha_ch), dS0=np.zeros((B, H, dk, dv)))
+    for b in range(B):
+        for h in range(H):
+            M = np.zeros((dk, dv)) if S0 is None else np.array(S0[b, h], dtype=np.float64)
+            starts, parts = [], []
+            for c0 in range(0, T, chunk):  # forward: the state at every chunk start
+                c1 = min(c0 + chunk, T)
+                Q, K, V, bt = q[b, h, c0:c1], k[b, h, c0:c1], v[b, h, c0:c1], beta[b, h, c0:c1]
+                a = alpha_ch[b, h, c0:c1]
+                Kt = d[b, h, c0:c1] * K
+                rho = _pair_decays(a)
+                G = np.cumprod(a, axis=0)
+                W = rho[-1]  # W[s] = rho(s -> L)
+                AS = np.tril(np.einsum("rf,sf,rsf->rs", K, Kt, rho), -1)
+                A = bt[:, None] * AS
+                P = np.tril(np.einsum("rf,sf,rsf->rs", Q, Kt, rho))
+                R = bt[:, None] * (V - (K * G) @ M)
+                U = solve_triangular(np.eye(c1 - c0) + A, R, lower=True, unit_diagonal=True)
+                starts.append(M)
+                parts.append((c0, c1, Q, K, V, bt, a, Kt, rho, G, W, AS, A, U, P))
+                M = G[-1][:, None] * M + (Kt * W).T @ U
+            dM = np.zeros((dk, dv)) if dS_T is None else np.array(dS_T[b, h], dtype=np.float64)
+            for (c0, c1, Q, K, V, bt, a, Kt, rho, G, W, AS, A, U, P), M0 in zip(parts[::-1],
+                                                                                 starts[::-1]):
+                n = c1 - c0
+                dO = np.zeros((n, dv)) if do is None else np.asarray(do[b, h, c0:c1], np.float64)
+                UdM = U @ dM.T  # [n, dk]
+                dU = P.T @ dO + (Kt * W) @ dM
+                dR = solve_triangular(np.eye(n) + A, dU, lower=True, unit_diagonal=True, trans=1)
+                dP = np.tril(dO @ U.T)
+                dA = -np.tril(dR @ U.T, -1)
+                dQ = G * (dO @ M0.T) + np.einsum("rs,sf,rsf->rf", dP, Kt, rho)
+                dKp = bt[:, None] * (-G * (dR @ M0.T) + np.einsum("rs,sf,rsf->rf", dA, Kt, rho))
+                dKt = (W * UdM + np.einsum("rs,rf,rsf->sf", dP, Q, rho)
+                       + np.einsum("rs,rf,rsf->sf", bt[:, None] * dA, K, rho))
+                out["dv"][b, h, c0:c1] = bt[:, None] * dR
+                out["dbeta"][b, h, c0:c1] = (np.sum(dR * (V - (K * G) @ M0), axis=1)
+                                             + np.sum(dA * AS, axis=1))
+                dLg = Q * dQ + K * dKp - Kt * dKt
+                dLg[-1] += G[-1] * np.sum(dM * M0, axis=1) + np.sum(Kt * W * UdM, axis=0)
+                dla = np.cumsum(dLg[::-1], axis=0)[::-1]
+                out["dalpha_ch"][b, h, c0:c1] = dla / a
+                out["dq"][b, h, c0:c1] = dQ
+                out["dd"][b, h, c0:c1] = dKt * K
+                out["dk"][b, h, c0:c1] = dKp + dKt * d[b, h, c0:c1]
+                dM = G[-1][:, None] * dM + (Q * G).T @ dO - (K * G).T @ (bt[:, None] * dR)
+            out["dS0"][b, h] = dM
+    return out

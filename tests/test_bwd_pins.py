@@ -101,3 +101,92 @@ def test_chunk_model_equals_reverse_pass(chunk):
         got = chunkwise.chunk_bwd(q, k, v, beta, d, aa, ss, do, dst, chunk=chunk)
         for n in ("dq", "dk", "dv", "dbeta", "dd", "dS0") + (("dalpha",) if aa is not None else ()):
             assert pins._rel(got[n], ref[n]) < 1e-12, (n, chunk)
+
+
+# ---- the channel-wise gate ---------------------------------------------------------------------
+
+def oracle_impl_kda(q, k, v, beta, d, a, S0, do, dS_T):
+    return backward.chunk_bwd(q, k, v, beta, d, None, S0, do, dS_T, alpha_ch=a)
+
+
+@pytest.mark.parametrize("name", sorted(pins.KDA_BWD_PINS))
+def test_oracle_meets_kda_pin(name):
+    fn, tol = pins.KDA_BWD_PINS[name]
+    err = fn(oracle_impl_kda)
+    assert err <= tol, f"{name}: {err:.3e} > {tol:.1e}"
+
+
+def test_kda_forward_states_match_c_oracle():
+    rng = np.random.default_rng(65)
+    q, k, v, beta, d, a, S0, do, dS_T = pins.rand_bwd_kda(rng, 2, 2, 33, 7, 5)
+    g = backward.chunk_bwd(q, k, v, beta, d, None, S0, do, dS_T, alpha_ch=a)
+    o, S_T = oracle.chunk_fwd(q, k, v, beta, d, None, S0, nthreads=2, alpha_ch=a)
+    assert pins._rel(g["o"], o) < 1e-13 and pins._rel(g["S_T"], S_T) < 1e-13
+
+
+def _kda_mutant(kind):
+    """The reverse pass with the channel-wise gate and one planted mistake in its decay line."""
+    def impl(q, k, v, beta, d, a, S0, do, dS_T):
+        f = backward.forward_states(q, k, v, beta, d, None, S0, alpha_ch=a)
+        B, H, T, dk = k.shape
+        dM = np.array(dS_T, dtype=np.float64)
+        g = {n: np.zeros_like(x) for n, x in (("dq", q), ("dk", k), ("dv", v), ("dbeta", beta),
+                                              ("dd", d), ("dalpha_ch", a))}
+        for t in range(T - 1, -1, -1):
+            kt, qt, dot = k[:, :, t], q[:, :, t], do[:, :, t]
+            kw = d[:, :, t] * kt
+            u, y = f["u"][:, :, t], f["y"][:, :, t]
+            Mp = f["Mprev"][:, :, t]
+            Mh = a[:, :, t, :, None] * Mp
+            Mt = Mh + kw[..., :, None] * u[..., None, :]
+            dM = dM + qt[..., :, None] * dot[..., None, :]
+            g["dq"][:, :, t] = np.einsum("bhkv,bhv->bhk", Mt, dot)
+            dkw = np.einsum("bhkv,bhv->bhk", dM, u)
+            du = np.einsum("bhkv,bhk->bhv", dM, kw)
+            g["dbeta"][:, :, t] = np.sum(du * (v[:, :, t] - y), axis=-1)
+            g["dv"][:, :, t] = beta[:, :, t, None] * du
+            dy = -beta[:, :, t, None] * du
+            dMh = dM + kt[..., :, None] * dy[..., None, :]
+            g["dd"][:, :, t] = dkw * kt
+            g["dk"][:, :, t] = np.einsum("bhkv,bhv->bhk", Mh, dy) + dkw * d[:, :, t]
+            src = Mh if kind == "da_from_decayed" else Mp
+            g["dalpha_ch"][:, :, t] = np.einsum("bhkv,bhkv->bhk", dMh, src)
+            if kind == "da_before_recall":
+                g["dalpha_ch"][:, :, t] = np.einsum("bhkv,bhkv->bhk", dM, Mp)
+            dM = dMh if kind == "carry_undecayed" else a[:, :, t, :, None] * dMh
+        g["dS0"] = dM
+        g["o"], g["S_T"] = f["o"], f["S_T"]
+        return g
+    return impl
+
+
+KDA_MUTANTS = ["da_from_decayed", "da_before_recall", "carry_undecayed"]
+
+
+def test_kda_mutant_harness_is_faithful():
+    impl = _kda_mutant("none")
+    for name in ("kda_autograd", "kda_identities"):
+        fn, tol = pins.KDA_BWD_PINS[name]
+        assert fn(impl) <= tol, name
+
+
+@pytest.mark.parametrize("kind", KDA_MUTANTS)
+def test_kda_pins_catch_mutant(kind):
+    impl = _kda_mutant(kind)
+    failed = [n for n in ("kda_autograd", "kda_identities", "kda_uniform")
+              if pins.KDA_BWD_PINS[n][0](impl) > pins.KDA_BWD_PINS[n][1]]
+    assert failed, f"mutant {kind} passes every pin"
+
+
+@pytest.mark.parametrize("lo", [None, 0.05, 1e-3])
+@pytest.mark.parametrize("chunk", [1, 3, 16, 32, 75])
+def test_kda_chunk_form_equals_token_reverse_pass(lo, chunk):
+    """The chunk algebra the GPU backward implements (oracle.chunkwise.chunk_bwd_channel)
+    against the token reverse pass, at chunk sizes from 1 to T and gates down to 1e-3."""
+    from oracle import chunkwise
+    rng = np.random.default_rng(66)
+    q, k, v, beta, d, a, S0, do, dS_T = pins.rand_bwd_kda(rng, 2, 2, 75, 6, 5, lo=lo)
+    ref = backward.chunk_bwd(q, k, v, beta, d, None, S0, do, dS_T, alpha_ch=a)
+    g = chunkwise.chunk_bwd_channel(q, k, v, beta, d, a, S0, do, dS_T, chunk=chunk)
+    for n in ("dq", "dk", "dv", "dbeta", "dd", "dalpha_ch", "dS0"):
+        assert pins._rel(g[n], ref[n]) < 1e-12, n
