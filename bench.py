@@ -30,7 +30,11 @@ HBM.  Prints ONE JSON line.  Besides the contract fields it carries:
   bwd           the backward (osdn_chunk_bwd: forward state checkpoints, the chunk inverses, the
                 reverse pass over chunks, the per-chunk gradients) on the same workload with
                 seeded output gradients, with its HBM roofline, its matrix-core FLOP count, and
-                the float64 reverse pass on one sampled sequence (parity and CPU baseline).
+                the float64 reverse pass on one sampled sequence (parity and CPU baseline);
+  kda_bwd       the backward with the channel-wise gate (osdn_chunk_bwd_kda: the fp32 forward
+                recording chunk-start states, the reverse pass, the per-chunk gradients) on the
+                same workload with the channel gate of `kda`, its HBM roofline, and the float64
+                reverse pass on one sampled sequence (parity and CPU baseline).
 """
 from __future__ import annotations
 
@@ -98,6 +102,7 @@ def main():
     ap.add_argument("--precond-steps", type=int, default=20)
     ap.add_argument("--kda-steps", type=int, default=10)
     ap.add_argument("--bwd-steps", type=int, default=5)
+    ap.add_argument("--kda-bwd-steps", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="1.3b")
     ap.add_argument("--configs", default="tiny,340m,long",
@@ -188,6 +193,10 @@ def main():
     if args.bwd_steps > 0:
         line["bwd"] = bench_bwd(args.bwd_steps, torch, dev, synth, w, x,
                                 (q, k, v, beta, d, alpha, S0), not args.no_cpu_baseline)
+
+    if args.kda_bwd_steps > 0:
+        line["kda_bwd"] = bench_kda_bwd(args.kda_bwd_steps, torch, dev, synth, w, x,
+                                        (q, k, v, beta, d, S0), not args.no_cpu_baseline)
 
     print(json.dumps(line), flush=True)
 
@@ -361,7 +370,8 @@ def bench_bwd(n_steps, torch, dev, synth, w, x, fwd, cpu):
                         "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                         "frac": round(alg / per / PEAK_HBM, 5), "alg_bytes_per_step": alg,
                         "note": "four launches; the state checkpoints (bf16, 2 x 134 MB written "
-                                "and read) and the chunk inverses (67 MB) are beyond alg"},
+                                "and read), the chunk planes (168 MB) and U and dR (67 MB "
+                                "each) are beyond alg"},
            "mfma": {"achieved": round(flops / per / 1e12, 3), "peak": PEAK_BF16 / 1e12,
                     "unit": "TFLOP/s", "frac": round(flops / per / PEAK_BF16, 5),
                     "flops_per_step": flops,
@@ -378,6 +388,72 @@ def bench_bwd(n_steps, torch, dev, synth, w, x, fwd, cpu):
         par = {}
         for n, gn in (("dq", "grad_q"), ("dk", "grad_k"), ("dv", "grad_v"), ("dbeta", "grad_beta"),
                       ("dd", "grad_d"), ("dalpha", "grad_alpha"), ("dS0", "grad_S0")):
+            par[n] = rel(grads[gn][b:b + 1, h:h + 1].float().cpu().numpy(), ref[n])
+        par["tol"] = 2e-2
+        rec["parity"] = par
+        rec["cpu_baseline"] = {"value": round(T / cpu_s, 1), "unit": "head-tokens/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"one (b,h) sequence of the workload ({T} tokens), "
+                                         f"float64 numpy reverse pass, {cpu_s:.2f} s wall"}
+    return rec
+
+
+def bench_kda_bwd(n_steps, torch, dev, synth, w, x, fwd, cpu):
+    """Times `n_steps` osdn_chunk_bwd_kda calls on the workload with the channel-wise gate of
+    bench_kda (output gradients seeded as in bench_bwd)."""
+    import numpy as np
+    from delta_rule_sequence_chunkwise_amd import osdn
+
+    B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
+    q, k, v, beta, d, S0 = fwd
+    a_np = synth.make_channel_gate(B, H, T, dk, seed=w.seed)
+    a = torch.from_numpy(a_np).to(dev)
+    gr = synth.make_output_grads(B, H, T, dk, dv, qkv=w.qkv, seed=w.seed, state=True)
+    do = torch.from_numpy(gr["do"]).to(dev).to(q.dtype)
+    dS_T = torch.from_numpy(gr["dS_T"]).to(dev)
+    ws = torch.empty(osdn.bwd_kda_workspace_bytes(B, H, T, dk, dv, osdn.OSDN_BF16),
+                     dtype=torch.uint8, device=dev)
+    grads = osdn.osdn_chunk_bwd_kda(q, k, v, beta, d, a, S0, do, dS_T, workspace=ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n_steps):
+        osdn.osdn_chunk_bwd_kda(q, k, v, beta, d, a, S0, do, dS_T, grads=grads, workspace=ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    per = e0.elapsed_time(e1) / 1e3 / n_steps
+    head_tokens = B * H * T
+    eq = 2 if w.qkv == "bf16" else 4
+    # in: q, k, v, do (qkv type), d and the gate (fp32), beta; out: grads of q, k, v (qkv type),
+    # of d and the gate (fp32), of beta; per sequence: S0 and dS_T in, grad S0 out (fp32)
+    alg = head_tokens * ((2 * dk + 2 * dv) * eq + 2 * dk * 4 + 4 + (2 * dk + dv) * eq
+                         + 2 * dk * 4 + 4) + B * H * dk * dv * 4 * 3
+    rec = {"workload": f"{w.name}-shape backward with a channel-wise gate a[B,H,T,dk]: B={B} "
+                       f"H={H} T={T} dk={dk} dv={dv}, bf16 q/k/v/do and gradients of q/k/v, "
+                       "fp32 beta/d/gate and their gradients, fp32 S0, dS_T and grad S0",
+           "ms_per_step": round(per * 1e3, 4),
+           "tokens_per_s": round(B * T / per, 1),
+           "roofline": {"bound": "hbm", "achieved": round(alg / per / 1e9, 2),
+                        "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                        "frac": round(alg / per / PEAK_HBM, 5), "alg_bytes_per_step": alg,
+                        "note": "three launches on the vector ALUs in fp32 (32-row chunks, the "
+                                "per-feature decay of every score term formed in the product); "
+                                "the fp32 state checkpoints (2 x 268 MB written and read) are "
+                                "beyond alg"}}
+    if cpu:
+        from oracle import backward
+        b, h = 0, 0
+        sl = lambda t: None if t is None else np.ascontiguousarray(t[b:b + 1, h:h + 1])
+        c0 = time.perf_counter()
+        ref = backward.chunk_bwd(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["beta"]), sl(x["d"]),
+                                 None, sl(x["S0"]), sl(gr["do"]), sl(gr["dS_T"]),
+                                 alpha_ch=sl(a_np))
+        cpu_s = time.perf_counter() - c0
+        rel = lambda p, r: float(np.max(np.abs(p - r)) / np.max(np.abs(r)))
+        par = {}
+        for n, gn in (("dq", "grad_q"), ("dk", "grad_k"), ("dv", "grad_v"), ("dbeta", "grad_beta"),
+                      ("dd", "grad_d"), ("dalpha_ch", "grad_alpha_ch"), ("dS0", "grad_S0")):
             par[n] = rel(grads[gn][b:b + 1, h:h + 1].float().cpu().numpy(), ref[n])
         par["tol"] = 2e-2
         rec["parity"] = par

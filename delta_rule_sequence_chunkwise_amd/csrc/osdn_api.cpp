@@ -653,3 +653,110 @@ osdn_status osdn_chunk_bwd_states(const void *q, const void *k, const void *v,
 }
 
 }  // extern "C"
+
+namespace {
+
+constexpr int64_t kGateBwdChunk = 32;  // rows per chunk of the channel-wise gate's backward
+
+// bytes of each of the two fp32 checkpoints of the channel-wise gate's backward,
+// [BH, nchunks, dk, dv]; -1 if the sizes are invalid
+int64_t bwd_gate_ckpt_bytes(int64_t B, int64_t H, int64_t T, int32_t dk, int32_t dv,
+                            osdn_dtype qkv) {
+    if (B < 0 || H < 0 || T < 0 || !dtype_ok(qkv) || !head_dim_ok(dk) || !head_dim_ok(dv))
+        return -1;
+    int64_t n = 4;
+    if (!mul_ok(n, B, kMaxElems) || !mul_ok(n, H, kMaxElems) ||
+        !mul_ok(n, (T + kGateBwdChunk - 1) / kGateBwdChunk, kMaxElems) ||
+        !mul_ok(n, int64_t(dk) * dv, kMaxElems))
+        return -1;
+    return round256(n);
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t osdn_chunk_bwd_kda_workspace(int64_t B, int64_t H, int64_t T, int32_t dk, int32_t dv,
+                                     osdn_dtype qkv) {
+    const int64_t b = bwd_gate_ckpt_bytes(B, H, T, dk, dv, qkv);
+    return b < 0 ? -1 : 2 * b;
+}
+
+osdn_status osdn_chunk_bwd_kda(const void *q, const void *k, const void *v, const float *beta,
+                               const void *d, const float *alpha_ch, const float *S0,
+                               const void *grad_o, const float *grad_S_T, void *grad_q,
+                               void *grad_k, void *grad_v, float *grad_beta, void *grad_d,
+                               float *grad_alpha_ch, float *grad_S0, void *workspace,
+                               int64_t workspace_bytes, int64_t B, int64_t H, int64_t T,
+                               int32_t dk, int32_t dv, osdn_dtype qkv, osdn_dtype d_dtype,
+                               void *stream) {
+    if (B < 0 || H < 0 || T < 0) return OSDN_ERR_SHAPE;
+    if (!dtype_ok(qkv) || !dtype_ok(d_dtype)) return OSDN_ERR_UNSUPPORTED;
+    if (!head_dim_ok(dk) || !head_dim_ok(dv)) return OSDN_ERR_UNSUPPORTED;
+    const int64_t ck = bwd_gate_ckpt_bytes(B, H, T, dk, dv, qkv);
+    if (ck < 0) return OSDN_ERR_SHAPE;
+    const int64_t wsb = 2 * ck;
+    int64_t BH = 1;
+    if (!mul_ok(BH, B, kMaxElems) || !mul_ok(BH, H, kMaxElems)) return OSDN_ERR_SHAPE;
+    int64_t tok = BH, st = BH;
+    if (!mul_ok(tok, T, kMaxElems) || !mul_ok(st, int64_t(dk) * dv, kMaxElems))
+        return OSDN_ERR_SHAPE;
+    int64_t nqk = tok, nv = tok;
+    if (!mul_ok(nqk, dk, kMaxElems) || !mul_ok(nv, dv, kMaxElems)) return OSDN_ERR_SHAPE;
+    const int64_t nch = (T + kGateBwdChunk - 1) / kGateBwdChunk;
+    if (BH * nch > int64_t(0x7fffffff) || BH * (dv / 32) > int64_t(0x7fffffff))
+        return OSDN_ERR_SHAPE;  // grid sizes
+
+    if (BH == 0) return OSDN_OK;
+    if (T > 0 && (!q || !k || !v || !beta || !d || !alpha_ch || !grad_o || !grad_q || !grad_k ||
+                  !grad_v || !grad_beta || !grad_d || !workspace))
+        return OSDN_ERR_NULL;
+    if (T == 0 && !grad_S0) return OSDN_OK;
+    if (T > 0 && workspace_bytes < wsb) return OSDN_ERR_SHAPE;
+
+    const int64_t eq = elem_size(qkv), ed = elem_size(d_dtype);
+    if (T > 0) {
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(d, 16) ||
+            !aligned(grad_o, 16) || !aligned(grad_q, 16) || !aligned(grad_k, 16) ||
+            !aligned(grad_v, 16) || !aligned(grad_d, 16) || !aligned(beta, 4) ||
+            !aligned(alpha_ch, 16) || !aligned(grad_beta, 4) ||
+            (grad_alpha_ch && !aligned(grad_alpha_ch, 4)) || !aligned(workspace, 256))
+            return OSDN_ERR_ALIGN;
+    }
+    if ((S0 && !aligned(S0, 16)) || (grad_S_T && !aligned(grad_S_T, 16)) ||
+        (grad_S0 && !aligned(grad_S0, 16)))
+        return OSDN_ERR_ALIGN;
+
+    const int64_t nt = T > 0 ? tok : 0;
+    const Range rq = range_of(q, nt ? nqk * eq : 0), rk = range_of(k, nt ? nqk * eq : 0);
+    const Range rv = range_of(v, nt ? nv * eq : 0), rd = range_of(d, nt ? nqk * ed : 0);
+    const Range rb = range_of(beta, nt * 4), ra = range_of(alpha_ch, nt ? nqk * 4 : 0);
+    const Range rs0 = range_of(S0, st * 4), rgo = range_of(grad_o, nt ? nv * eq : 0);
+    const Range rgst = range_of(grad_S_T, st * 4);
+    const Range gq = range_of(grad_q, nt ? nqk * eq : 0), gk = range_of(grad_k, nt ? nqk * eq : 0);
+    const Range gv = range_of(grad_v, nt ? nv * eq : 0), gd = range_of(grad_d, nt ? nqk * ed : 0);
+    const Range gb = range_of(grad_beta, nt * 4);
+    const Range ga = range_of(grad_alpha_ch, grad_alpha_ch && nt ? nqk * 4 : 0);
+    const Range gs0 = range_of(grad_S0, st * 4);
+    const Range rw = range_of(workspace, T > 0 ? wsb : 0);
+    const Range *outs[] = {&gq, &gk, &gv, &gd, &gb, &ga, &gs0, &rw};
+    const Range *ins[] = {&rq, &rk, &rv, &rd, &rb, &ra, &rs0, &rgo, &rgst};
+    for (int i = 0; i < 8; ++i) {
+        for (const Range *in : ins)
+            if (overlap(*outs[i], *in)) return OSDN_ERR_ALIAS;
+        for (int j = i + 1; j < 8; ++j)
+            if (overlap(*outs[i], *outs[j])) return OSDN_ERR_ALIAS;
+    }
+
+    char *ws = static_cast<char *>(workspace);
+    osdn::BwdArgs a{q, k, v, d, beta, nullptr, S0, grad_o, grad_S_T, grad_q, grad_k, grad_v,
+                    grad_beta, nullptr, grad_d, grad_S0,
+                    T > 0 ? static_cast<void *>(ws) : nullptr, T > 0 ? ws + ck : nullptr, false,
+                    nullptr, nullptr, nullptr, BH, T, dk, dv, qkv, d_dtype};
+    a.alpha_ch = alpha_ch;
+    a.galpha_ch = grad_alpha_ch;
+    const hipError_t err = osdn::launch_chunk_bwd_gate(a, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? OSDN_OK : OSDN_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1581,12 +1581,552 @@ hipError_t bwd_dims(const BwdArgs &a, hipStream_t stream) {
     return a.dv == 64 ? bwd_dtypes<TQ, 128, 64>(a, stream) : bwd_dtypes<TQ, 128, 128>(a, stream);
 }
 
+
+// ---- the channel-wise gate: fp32 arithmetic for either input type, 32-row chunks ----------
+// With a_t in [0,1]^dk scaling the key features of the state (Erase-then-Delta Attention,
+// section 2.2, eq. 5), the forward's chunk algebra has per-feature decays: with Lg_r the
+// running sum of ln a over the chunk's rows up to r (per feature, in double precision),
+// G_r = e^{Lg_r}, rho_f(s -> r) = e^{Lg_rf - Lg_sf} and W_s = rho(s -> L) for the last row L,
+//   AS[r,s] = sum_f k_rf k~_sf rho_f(s->r) (s < r),  P[r,s] = sum_f q_rf k~_sf rho_f(s->r) (s <= r),
+//   U = (I + A)^{-1} diag(b) (V - (K o G) M0),  O = (Q o G) M0 + P U,
+//   M_C = Diag(G_L) M0 + (K~ o W)^T U.
+// Differentiating it gives, per chunk (dMC the gradient at its end):
+//   dU = P^T dO + (K~ o W) dMC,   dR = (I + A)^{-T} dU,
+//   dM0 = Diag(G_L) dMC + (Q o G)^T dO - (K o G)^T diag(b) dR,
+//   dP = lower-inclusive(dO U^T),   dA = -strictly-lower(dR U^T),
+//   dQ[r,f]  = G_rf (dO M0^T)[r,f] + sum_s dP[r,s] k~_sf rho_f(s->r),
+//   dK'[r,f] = b_r (-G_rf (dR M0^T)[r,f] + sum_s dA[r,s] k~_sf rho_f(s->r)),
+//   dK~[s,f] = W_sf (U dMC^T)[s,f] + sum_r (dP[r,s] q_rf + b_r dA[r,s] k_rf) rho_f(s->r),
+//   db_r = <dR_r, v_r - ((K o G) M0)_r> + sum_s dA[r,s] AS[r,s],   dV = diag(b) dR,
+//   dLg[r,f] = q_rf dQ + k_rf dK' - k~_rf dK~  (+ at r = L: G_Lf <dMC[f,:], M0[f,:]>
+//              + sum_s k~_sf W_sf (U dMC^T)[s,f]),
+//   d ln a_t = sum_{t <= r <= L} dLg[r],  da = d ln a / a,  dd = dK~ o K,  dK = dK' + dK~ o D.
+// Every decay factor is e to a difference of running sums with the later row first, so at
+// most 1.  Rows past the end are zero with gate 1 (ln a = 0) and beta = 0.
+
+// Q, K, K~ = d (.) k in fp32 and ln a in double (zero rows, and ln a = 0, past the end)
+template <int C, int DK, int PX, typename TQ, typename TD>
+__device__ __forceinline__ void load_qk_gate(const TQ *q, const TQ *k, const TD *d,
+                                             const float *a, int64_t row0, int n, float *sQ,
+                                             float *sK, float *sKt, double *sLg, int tid) {
+    for (int idx = tid; idx < C * DK; idx += NT) {
+        const int r = idx / DK, f = idx % DK;
+        float qv = 0.f, kv = 0.f, dv = 0.f;
+        double lg = 0.0;
+        if (r < n) {
+            const int64_t e = (row0 + r) * DK + f;
+            qv = to_f32(q[e]);
+            kv = to_f32(k[e]);
+            dv = to_f32(d[e]);
+            lg = log(fmax(static_cast<double>(a[e]), 1e-300));
+        }
+        sQ[r * PX + f] = qv;
+        sK[r * PX + f] = kv;
+        sKt[r * PX + f] = dv * kv;
+        sLg[r * PX + f] = lg;
+    }
+}
+
+// ln a -> its running sum down each feature column (the threads of the first DK lanes)
+template <int C, int DK, int PX>
+__device__ __forceinline__ void gate_scan(double *sLg, int tid) {
+    if (tid < DK) {
+        double acc = 0.0;
+        for (int r = 0; r < C; ++r) {
+            acc += sLg[r * PX + tid];
+            sLg[r * PX + tid] = acc;
+        }
+    }
+}
+
+// AS (strictly lower) and P (lower-inclusive) with the per-feature decay inside the sum
+template <int C, int DK, int PX, int PC>
+__device__ __forceinline__ void scores_gate(const float *sQ, const float *sK, const float *sKt,
+                                            const double *sLg, float *sAS, float *sP, int tid) {
+    constexpr int TM = C / 16;
+    const int i0 = (tid / 16) * TM, j0 = (tid % 16) * TM;
+    float ak[TM][TM], aq[TM][TM];
+    zero(ak);
+    zero(aq);
+    if (j0 <= i0 + TM - 1) {  // tiles wholly above the diagonal stay zero
+        for (int f = 0; f < DK; ++f) {
+            float qv[TM], kv[TM], tv[TM];
+            double lr[TM], ls[TM];
+#pragma unroll
+            for (int m = 0; m < TM; ++m) {
+                qv[m] = sQ[(i0 + m) * PX + f];
+                kv[m] = sK[(i0 + m) * PX + f];
+                lr[m] = sLg[(i0 + m) * PX + f];
+                tv[m] = sKt[(j0 + m) * PX + f];
+                ls[m] = sLg[(j0 + m) * PX + f];
+            }
+#pragma unroll
+            for (int m = 0; m < TM; ++m)
+#pragma unroll
+                for (int nn = 0; nn < TM; ++nn) {
+                    if (j0 + nn <= i0 + m) {
+                        const float e = __expf(static_cast<float>(lr[m] - ls[nn])) * tv[nn];
+                        ak[m][nn] += kv[m] * e;
+                        aq[m][nn] += qv[m] * e;
+                    }
+                }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < TM; ++m)
+#pragma unroll
+        for (int nn = 0; nn < TM; ++nn) {
+            const int i = i0 + m, j = j0 + nn;
+            sAS[i * PC + j] = j < i ? ak[m][nn] : 0.f;
+            sP[i * PC + j] = j <= i ? aq[m][nn] : 0.f;
+        }
+}
+
+// Reverse pass over chunks with the channel-wise gate: one workgroup per (sequence, BV-wide
+// value slice), dM[:, slice] in LDS; dMck[c] gets the gradient at the end of chunk c.
+template <int C, int DK, int BV, typename TQ, typename TD>
+__global__ void __launch_bounds__(NT)
+bwd_state_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
+                      const TD *__restrict__ d, const float *__restrict__ beta,
+                      const float *__restrict__ alpha_ch, const TQ *__restrict__ dO,
+                      const float *__restrict__ dS_T, float *__restrict__ dMck,
+                      float *__restrict__ dS0, int64_t T, int dv) {
+    constexpr int PX = DK + 1, PC = C + 1, PS = BV + 1;
+    __shared__ float sQ[C * PX], sK[C * PX], sKt[C * PX];
+    __shared__ double sLg[C * PX];
+    __shared__ float sAS[C * PC], sP[C * PC];
+    __shared__ float sdO[C * PS], sX[C * PS], sdM[DK * PS];
+    __shared__ float sb[C], sGL[DK];
+
+    const int nvt = dv / BV;
+    const int64_t bh = blockIdx.x / nvt;
+    const int j0 = static_cast<int>(blockIdx.x % nvt) * BV;
+    const int tid = threadIdx.x;
+    const int64_t nch = (T + C - 1) / C;
+
+    for (int idx = tid; idx < DK * BV; idx += NT) {
+        const int f = idx / BV, j = idx % BV;
+        sdM[f * PS + j] = dS_T ? dS_T[(bh * DK + f) * dv + j0 + j] : 0.f;
+    }
+    for (int64_t c = nch - 1; c >= 0; --c) {
+        const int64_t c0 = c * C, row0 = bh * T + c0;
+        const int n = static_cast<int>(T - c0 < C ? T - c0 : C);
+        __syncthreads();  // the previous chunk is done with every buffer
+        load_qk_gate<C, DK, PX>(q, k, d, alpha_ch, row0, n, sQ, sK, sKt, sLg, tid);
+        for (int idx = tid; idx < C * BV; idx += NT) {
+            const int r = idx / BV, j = idx % BV;
+            sdO[r * PS + j] = r < n ? to_f32(dO[(row0 + r) * dv + j0 + j]) : 0.f;
+        }
+        if (tid < C) sb[tid] = tid < n ? beta[row0 + tid] : 0.f;
+        for (int idx = tid; idx < DK * BV; idx += NT) {  // the gradient at this chunk's end
+            const int f = idx / BV, j = idx % BV;
+            dMck[((bh * nch + c) * DK + f) * dv + j0 + j] = sdM[f * PS + j];
+        }
+        __syncthreads();
+        gate_scan<C, DK, PX>(sLg, tid);
+        __syncthreads();
+        scores_gate<C, DK, PX, PC>(sQ, sK, sKt, sLg, sAS, sP, tid);
+        __syncthreads();
+        // in place: Q o G, K o G, K~ o W; and G_L
+        for (int idx = tid; idx < C * DK; idx += NT) {
+            const int r = idx / DK, f = idx % DK;
+            const double lg = sLg[r * PX + f], lgL = sLg[(C - 1) * PX + f];
+            const float g = __expf(static_cast<float>(lg));
+            sQ[r * PX + f] *= g;
+            sK[r * PX + f] *= g;
+            sKt[r * PX + f] *= __expf(static_cast<float>(lgL - lg));
+        }
+        if (tid < DK) sGL[tid] = __expf(static_cast<float>(sLg[(C - 1) * PX + tid]));
+        __syncthreads();
+        {  // dU = P^T dO + (K~ o W) dM
+            constexpr int TM = C / 16, TN = BV / 16;
+            const int i0 = (tid / 16) * TM, j0l = (tid % 16) * TN;
+            float acc[TM][TN];
+            zero(acc);
+            mm<TM, TN, DK>(acc, i0, j0l, [&](int i, int kk) { return sKt[i * PX + kk]; },
+                           [&](int kk, int j) { return sdM[kk * PS + j]; });
+            mm<TM, TN, C>(acc, i0, j0l, [&](int i, int kk) { return sP[kk * PC + i]; },
+                          [&](int kk, int j) { return sdO[kk * PS + j]; });
+#pragma unroll
+            for (int m = 0; m < TM; ++m)
+#pragma unroll
+                for (int nn = 0; nn < TN; ++nn) sX[(i0 + m) * PS + j0l + nn] = acc[m][nn];
+        }
+        __syncthreads();
+        solve_upper<C, BV, PS, PC>(sX, sAS, sb, tid);  // dR
+        __syncthreads();
+        {  // dM <- Diag(G_L) dM + (Q o G)^T dO - (K o G)^T diag(b) dR
+            constexpr int TM = DK / 16, TN = BV / 16;
+            const int i0 = (tid / 16) * TM, j0l = (tid % 16) * TN;
+            float acc[TM][TN];
+            zero(acc);
+            mm<TM, TN, C>(acc, i0, j0l, [&](int f, int r) { return sQ[r * PX + f]; },
+                          [&](int r, int j) { return sdO[r * PS + j]; });
+            mm<TM, TN, C>(acc, i0, j0l, [&](int f, int r) { return sK[r * PX + f]; },
+                          [&](int r, int j) { return -sb[r] * sX[r * PS + j]; });
+#pragma unroll
+            for (int m = 0; m < TM; ++m)
+#pragma unroll
+                for (int nn = 0; nn < TN; ++nn) {
+                    float &x = sdM[(i0 + m) * PS + j0l + nn];
+                    x = sGL[i0 + m] * x + acc[m][nn];
+                }
+        }
+    }
+    __syncthreads();
+    if (dS0) {
+        for (int idx = tid; idx < DK * BV; idx += NT) {
+            const int f = idx / BV, j = idx % BV;
+            dS0[(bh * DK + f) * dv + j0 + j] = sdM[f * PS + j];
+        }
+    }
+}
+
+// Per-chunk gradients with the channel-wise gate: one workgroup per (sequence, chunk), the
+// value columns taken BV at a time.
+template <int C, int DK, int DV, int BV, typename TQ, typename TD>
+__global__ void __launch_bounds__(NT)
+bwd_chunk_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
+                      const TQ *__restrict__ v, const TD *__restrict__ d,
+                      const float *__restrict__ beta, const float *__restrict__ alpha_ch,
+                      const TQ *__restrict__ dO, const float *__restrict__ Mck,
+                      const float *__restrict__ dMck, TQ *__restrict__ gq, TQ *__restrict__ gk,
+                      TQ *__restrict__ gv, float *__restrict__ gbeta, TD *__restrict__ gd,
+                      float *__restrict__ galpha_ch, int64_t T, int64_t nch) {
+    constexpr int PX = DK + 1, PC = C + 1, PS = BV + 1;
+    constexpr int TC = C / 16, TK = DK / 16, TV = BV / 16;  // register blocks
+    constexpr int FPT = DK * BV / NT;                        // (f, j) pairs per thread
+    static_assert(FPT * NT == DK * BV && NT % BV == 0, "slice layout");
+    // raw Q, K, K~; K o G and K~ o W for the slice products (K o G is reused for dLg)
+    __shared__ float sQ[C * PX], sK[C * PX], sKt[C * PX], sKg[C * PX], sKw[C * PX];
+    __shared__ double sLg[C * PX];
+    __shared__ float sAS[C * PC], sP[C * PC];  // AS, P; after the slices b dA and dP
+    __shared__ float sM0[DK * PS], sdM[DK * PS];
+    __shared__ float sY[C * PS], sdO[C * PS], sU[C * PS], sdR[C * PS];
+    __shared__ float sb[C], sdb[C], sLast[DK];
+
+    const int64_t bh = blockIdx.x / nch, c = blockIdx.x % nch;
+    const int64_t c0 = c * C, row0 = bh * T + c0;
+    const int n = static_cast<int>(T - c0 < C ? T - c0 : C);
+    const int tid = threadIdx.x;
+    const int ti = tid / 16, tj = tid % 16;
+    const float *M0 = Mck + (bh * nch + c) * DK * DV;
+    const float *dMC = dMck + (bh * nch + c) * DK * DV;
+
+    load_qk_gate<C, DK, PX>(q, k, d, alpha_ch, row0, n, sQ, sK, sKt, sLg, tid);
+    if (tid < C) {
+        sb[tid] = tid < n ? beta[row0 + tid] : 0.f;
+        sdb[tid] = 0.f;
+    }
+    __syncthreads();
+    gate_scan<C, DK, PX>(sLg, tid);
+    __syncthreads();
+    scores_gate<C, DK, PX, PC>(sQ, sK, sKt, sLg, sAS, sP, tid);
+    for (int idx = tid; idx < C * DK; idx += NT) {
+        const int r = idx / DK, f = idx % DK;
+        const double lg = sLg[r * PX + f], lgL = sLg[(C - 1) * PX + f];
+        sKg[r * PX + f] = sK[r * PX + f] * __expf(static_cast<float>(lg));
+        sKw[r * PX + f] = sKt[r * PX + f] * __expf(static_cast<float>(lgL - lg));
+    }
+
+    float aQ[TC][TK], aK[TC][TK], aKt[TC][TK], adP[TC][TC], adA[TC][TC];
+    zero(aQ);
+    zero(aK);
+    zero(aKt);
+    zero(adP);
+    zero(adA);
+    float frob[FPT];  // this thread's parts of <dMC[f,:], M0[f,:]>, f = tid / BV + i NT / BV
+#pragma unroll
+    for (int i = 0; i < FPT; ++i) frob[i] = 0.f;
+    const int ic = ti * TC, jc = tj * TC;  // C x C block
+    const int ik = ti * TC, jk = tj * TK;  // C x DK block
+    const int is = ti * TC, js = tj * TV;  // C x BV block
+
+    for (int s0 = 0; s0 < DV; s0 += BV) {
+        __syncthreads();  // the previous slice (and the scaled copies) are done
+#pragma unroll
+        for (int i = 0; i < FPT; ++i) {
+            const int idx = tid + i * NT, f = idx / BV, j = idx % BV;
+            const float m0 = M0[f * DV + s0 + j], dm = dMC[f * DV + s0 + j];
+            sM0[f * PS + j] = m0;
+            sdM[f * PS + j] = dm;
+            frob[i] += m0 * dm;
+        }
+        for (int idx = tid; idx < C * BV; idx += NT) {
+            const int r = idx / BV, j = idx % BV;
+            sY[r * PS + j] = r < n ? to_f32(v[(row0 + r) * DV + s0 + j]) : 0.f;
+            sdO[r * PS + j] = r < n ? to_f32(dO[(row0 + r) * DV + s0 + j]) : 0.f;
+        }
+        __syncthreads();
+        {  // Y = V - (K o G) M0, R = b Y into U;  (K~ o W) dMC into dR (added to below)
+            float a1[TC][TV], a3[TC][TV];
+            zero(a1);
+            zero(a3);
+            mm<TC, TV, DK>(a1, is, js, [&](int i, int kk) { return sKg[i * PX + kk]; },
+                           [&](int kk, int j) { return sM0[kk * PS + j]; });
+            mm<TC, TV, DK>(a3, is, js, [&](int i, int kk) { return sKw[i * PX + kk]; },
+                           [&](int kk, int j) { return sdM[kk * PS + j]; });
+#pragma unroll
+            for (int m = 0; m < TC; ++m)
+#pragma unroll
+                for (int nn = 0; nn < TV; ++nn) {
+                    const int r = is + m, j = js + nn;
+                    const float y = sY[r * PS + j] - a1[m][nn];
+                    sY[r * PS + j] = y;
+                    sU[r * PS + j] = sb[r] * y;
+                    sdR[r * PS + j] = a3[m][nn];
+                }
+        }
+        __syncthreads();
+        solve_lower<C, BV, PS, PC>(sU, sAS, sb, tid);  // U = (I + A)^{-1} R
+        __syncthreads();
+        {  // dU = P^T dO + (K~ o W) dMC (the same thread wrote that part of sdR above)
+            float acc[TC][TV];
+            zero(acc);
+            mm<TC, TV, C>(acc, is, js, [&](int i, int kk) { return sP[kk * PC + i]; },
+                          [&](int kk, int j) { return sdO[kk * PS + j]; });
+#pragma unroll
+            for (int m = 0; m < TC; ++m)
+#pragma unroll
+                for (int nn = 0; nn < TV; ++nn) sdR[(is + m) * PS + js + nn] += acc[m][nn];
+        }
+        __syncthreads();
+        solve_upper<C, BV, PS, PC>(sdR, sAS, sb, tid);  // dR = (I + A)^{-T} dU
+        __syncthreads();
+        for (int idx = tid; idx < C * BV; idx += NT) {
+            const int r = idx / BV, j = idx % BV;
+            if (r < n) gv[(row0 + r) * DV + s0 + j] = from_f32<TQ>(sb[r] * sdR[r * PS + j]);
+        }
+        if (tid < C) {  // <dR_r, y_r> of this slice
+            float db = 0.f;
+            for (int j = 0; j < BV; ++j) db += sdR[tid * PS + j] * sY[tid * PS + j];
+            sdb[tid] += db;
+        }
+        auto bu = [&](int kk, int j) { return sU[j * PS + kk]; };
+        mm<TC, TC, BV>(adP, ic, jc, [&](int i, int kk) { return sdO[i * PS + kk]; }, bu);
+        mm<TC, TC, BV>(adA, ic, jc, [&](int i, int kk) { return sdR[i * PS + kk]; }, bu);
+        auto bm0t = [&](int kk, int f) { return sM0[f * PS + kk]; };
+        mm<TC, TK, BV>(aQ, ik, jk, [&](int i, int kk) { return sdO[i * PS + kk]; }, bm0t);
+        mm<TC, TK, BV>(aK, ik, jk, [&](int i, int kk) { return -sdR[i * PS + kk]; }, bm0t);
+        mm<TC, TK, BV>(aKt, ik, jk, [&](int i, int kk) { return sU[i * PS + kk]; },
+                       [&](int kk, int f) { return sdM[f * PS + kk]; });
+    }
+    // G_L <dMC[f,:], M0[f,:]> per feature: the BV threads of one f are adjacent lanes
+#pragma unroll
+    for (int i = 0; i < FPT; ++i) {
+#pragma unroll
+        for (int m = 1; m < BV; m <<= 1) frob[i] += __shfl_xor(frob[i], m);
+        const int f = tid / BV + i * (NT / BV);
+        if (tid % BV == 0)
+            sLast[f] = __expf(static_cast<float>(sLg[(C - 1) * PX + f])) * frob[i];
+    }
+    // dP (lower-inclusive), dA (strictly lower, negated); db_r += sum_s dA[r,s] AS[r,s]
+    {
+        float rowb[TC];
+#pragma unroll
+        for (int m = 0; m < TC; ++m) {
+            rowb[m] = 0.f;
+#pragma unroll
+            for (int nn = 0; nn < TC; ++nn) {
+                const int i = ic + m, j = jc + nn;
+                adP[m][nn] = j <= i ? adP[m][nn] : 0.f;
+                adA[m][nn] = j < i ? -adA[m][nn] : 0.f;
+                rowb[m] += adA[m][nn] * sAS[i * PC + j];
+            }
+#pragma unroll
+            for (int w = 1; w < 16; w <<= 1) rowb[m] += __shfl_xor(rowb[m], w);
+        }
+        __syncthreads();  // every slice product and every read of AS is done
+        if (tj == 0) {
+#pragma unroll
+            for (int m = 0; m < TC; ++m) sdb[ic + m] += rowb[m];
+        }
+#pragma unroll
+        for (int m = 0; m < TC; ++m)
+#pragma unroll
+            for (int nn = 0; nn < TC; ++nn) {
+                const int i = ic + m, j = jc + nn;
+                sP[i * PC + j] = adP[m][nn];
+                sAS[i * PC + j] = adA[m][nn] * sb[i];
+            }
+    }
+    // the slice terms' decay factors: dQ G, dK' b G, dK~ W; then the column sums
+    // sum_s k~_sf (W o U dMC^T)[s,f] of the last row's term, through LDS (sM0 as [16][DK])
+    float *colpart = sM0;
+    {
+        float colk[TK];
+#pragma unroll
+        for (int nn = 0; nn < TK; ++nn) colk[nn] = 0.f;
+#pragma unroll
+        for (int m = 0; m < TC; ++m)
+#pragma unroll
+            for (int nn = 0; nn < TK; ++nn) {
+                const int r = ik + m, f = jk + nn;
+                const double lg = sLg[r * PX + f], lgL = sLg[(C - 1) * PX + f];
+                const float g = __expf(static_cast<float>(lg));
+                aQ[m][nn] *= g;
+                aK[m][nn] *= sb[r] * g;
+                aKt[m][nn] *= __expf(static_cast<float>(lgL - lg));
+                colk[nn] += sKt[r * PX + f] * aKt[m][nn];
+            }
+#pragma unroll
+        for (int nn = 0; nn < TK; ++nn) colpart[ti * DK + jk + nn] = colk[nn];
+    }
+    __syncthreads();
+    if (tid < DK) {
+        float s = 0.f;
+        for (int t = 0; t < 16; ++t) s += colpart[t * DK + tid];
+        sLast[tid] += s;
+    }
+    // the score terms, with the decay of every (row, column, feature) inside:
+    // dQ[r,f] += sum_s dP[r,s] k~_sf rho,  dK'[r,f] += sum_s b_r dA[r,s] k~_sf rho
+    {
+        double lr[TC][TK];
+#pragma unroll
+        for (int m = 0; m < TC; ++m)
+#pragma unroll
+            for (int nn = 0; nn < TK; ++nn) lr[m][nn] = sLg[(ik + m) * PX + jk + nn];
+        for (int s = 0; s <= ik + TC - 1; ++s) {
+            float kt[TK];
+            double ls[TK];
+#pragma unroll
+            for (int nn = 0; nn < TK; ++nn) {
+                kt[nn] = sKt[s * PX + jk + nn];
+                ls[nn] = sLg[s * PX + jk + nn];
+            }
+#pragma unroll
+            for (int m = 0; m < TC; ++m) {
+                const int r = ik + m;
+                if (s <= r) {
+                    const float dp = sP[r * PC + s], da = sAS[r * PC + s];
+#pragma unroll
+                    for (int nn = 0; nn < TK; ++nn) {
+                        const float e = __expf(static_cast<float>(lr[m][nn] - ls[nn])) * kt[nn];
+                        aQ[m][nn] += dp * e;
+                        aK[m][nn] += da * e;
+                    }
+                }
+            }
+        }
+    }
+    // dK~[s,f] += sum_{r >= s} (dP[r,s] q_rf + b_r dA[r,s] k_rf) rho_f(s -> r)
+    {
+        double ls[TC][TK];
+#pragma unroll
+        for (int m = 0; m < TC; ++m)
+#pragma unroll
+            for (int nn = 0; nn < TK; ++nn) ls[m][nn] = sLg[(ik + m) * PX + jk + nn];
+        for (int r = ik; r < C; ++r) {
+            float qv[TK], kv[TK];
+            double lr[TK];
+#pragma unroll
+            for (int nn = 0; nn < TK; ++nn) {
+                qv[nn] = sQ[r * PX + jk + nn];
+                kv[nn] = sK[r * PX + jk + nn];
+                lr[nn] = sLg[r * PX + jk + nn];
+            }
+#pragma unroll
+            for (int m = 0; m < TC; ++m) {
+                const int s = ik + m;
+                if (s <= r) {
+                    const float dp = sP[r * PC + s], da = sAS[r * PC + s];
+#pragma unroll
+                    for (int nn = 0; nn < TK; ++nn) {
+                        const float e = __expf(static_cast<float>(lr[nn] - ls[m][nn]));
+                        aKt[m][nn] += (dp * qv[nn] + da * kv[nn]) * e;
+                    }
+                }
+            }
+        }
+    }
+    // outputs, and dLg into sKg (K o G is no longer read)
+#pragma unroll
+    for (int m = 0; m < TC; ++m) {
+        const int r = ik + m;
+#pragma unroll
+        for (int nn = 0; nn < TK; ++nn) {
+            const int f = jk + nn;
+            const float qv = sQ[r * PX + f], kv = sK[r * PX + f], tv = sKt[r * PX + f];
+            sKg[r * PX + f] = qv * aQ[m][nn] + kv * aK[m][nn] - tv * aKt[m][nn];
+            if (r < n) {
+                const int64_t e = (row0 + r) * DK + f;
+                gq[e] = from_f32<TQ>(aQ[m][nn]);
+                gk[e] = from_f32<TQ>(aK[m][nn] + aKt[m][nn] * to_f32(d[e]));
+                gd[e] = from_f32<TD>(aKt[m][nn] * kv);
+            }
+        }
+    }
+    __syncthreads();
+    if (tid < DK && galpha_ch) {  // d ln a_t = sum_{r >= t} dLg[r]; the last row's term at n-1
+        float acc = sLast[tid];
+        for (int r = n - 1; r >= 0; --r) {
+            acc += sKg[r * PX + tid];
+            const int64_t e = (row0 + r) * DK + tid;
+            galpha_ch[e] = acc / alpha_ch[e];
+        }
+    }
+    if (tid < n) gbeta[row0 + tid] = sdb[tid];
+}
+
+// The backward with the channel-wise gate: the fp32 forward (its GATE variant, 32-row chunks)
+// records the state at every chunk start, then the reverse pass and the per-chunk gradients.
+template <int DK, int DV, typename TQ, typename TD>
+hipError_t bwd_gate_typed(const BwdArgs &a, hipStream_t stream) {
+    constexpr int C = 32;
+    const int64_t nch = (a.T + C - 1) / C;
+    if (nch > 0) {
+        ChunkArgs f{a.q, a.k, a.v, a.d, a.beta, nullptr, a.S0, nullptr, nullptr, a.BH, a.T, DK,
+                    DV, C, a.qkv, a.d_dtype};
+        f.alpha_ch = a.alpha_ch;
+        f.ckpt = a.Mck;
+        const hipError_t e = launch_chunk_fwd_f32math(f, stream);
+        if (e != hipSuccess) return e;
+    }
+    constexpr int BVA = 32, BVB = 16;
+    hipLaunchKernelGGL((bwd_state_gate_kernel<C, DK, BVA, TQ, TD>),
+                       dim3(static_cast<unsigned>(a.BH * (DV / BVA))), dim3(NT), 0, stream,
+                       static_cast<const TQ *>(a.q), static_cast<const TQ *>(a.k),
+                       static_cast<const TD *>(a.d), a.beta, a.alpha_ch,
+                       static_cast<const TQ *>(a.dO), a.dS_T, static_cast<float *>(a.dMck), a.dS0,
+                       a.T, DV);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || nch == 0) return e;
+    hipLaunchKernelGGL((bwd_chunk_gate_kernel<C, DK, DV, BVB, TQ, TD>),
+                       dim3(static_cast<unsigned>(a.BH * nch)), dim3(NT), 0, stream,
+                       static_cast<const TQ *>(a.q), static_cast<const TQ *>(a.k),
+                       static_cast<const TQ *>(a.v), static_cast<const TD *>(a.d), a.beta,
+                       a.alpha_ch, static_cast<const TQ *>(a.dO),
+                       static_cast<const float *>(a.Mck), static_cast<const float *>(a.dMck),
+                       static_cast<TQ *>(a.gq), static_cast<TQ *>(a.gk), static_cast<TQ *>(a.gv),
+                       a.gbeta, static_cast<TD *>(a.gd), a.galpha_ch, a.T, nch);
+    return hipGetLastError();
+}
+
+template <typename TQ, int DK, int DV>
+hipError_t bwd_gate_dtypes(const BwdArgs &a, hipStream_t stream) {
+    return a.d_dtype == OSDN_F32 ? bwd_gate_typed<DK, DV, TQ, float>(a, stream)
+                                 : bwd_gate_typed<DK, DV, TQ, bf16_t>(a, stream);
+}
+
+template <typename TQ>
+hipError_t bwd_gate_dims(const BwdArgs &a, hipStream_t stream) {
+    if (a.dk == 64)
+        return a.dv == 64 ? bwd_gate_dtypes<TQ, 64, 64>(a, stream)
+                          : bwd_gate_dtypes<TQ, 64, 128>(a, stream);
+    return a.dv == 64 ? bwd_gate_dtypes<TQ, 128, 64>(a, stream)
+                      : bwd_gate_dtypes<TQ, 128, 128>(a, stream);
+}
+
 }  // namespace
 
 int32_t bwd_chunk_size(osdn_dtype qkv) { return qkv == OSDN_BF16 ? 64 : 32; }
 
 hipError_t launch_chunk_bwd(const BwdArgs &a, hipStream_t stream) {
     return a.qkv == OSDN_BF16 ? bwd_dims<bf16_t>(a, stream) : bwd_dims<float>(a, stream);
+}
+
+hipError_t launch_chunk_bwd_gate(const BwdArgs &a, hipStream_t stream) {
+    return a.qkv == OSDN_BF16 ? bwd_gate_dims<bf16_t>(a, stream) : bwd_gate_dims<float>(a, stream);
 }
 
 }  // namespace osdn

@@ -271,7 +271,8 @@ hipError_t launch_typed(const ChunkArgs &a, hipStream_t stream) {
         hipLaunchKernelGGL((chunk_f32math_kernel<DK, BV, CG, TQ, TD, true>), grid, dim3(kThreads),
                            0, stream, static_cast<const TQ *>(a.q), static_cast<const TQ *>(a.k),
                            static_cast<const TQ *>(a.v), static_cast<const TD *>(a.d), a.beta,
-                           a.alpha_ch, a.S0, static_cast<TQ *>(a.o), a.S_T, a.T, a.dv, nullptr);
+                           a.alpha_ch, a.S0, static_cast<TQ *>(a.o), a.S_T, a.T, a.dv,
+                           static_cast<float *>(a.ckpt));
     } else {
         hipLaunchKernelGGL((chunk_f32math_kernel<DK, BV, CH, TQ, TD, false>), grid,
                            dim3(kThreads), 0, stream, static_cast<const TQ *>(a.q),

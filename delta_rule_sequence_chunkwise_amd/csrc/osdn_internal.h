@@ -60,8 +60,8 @@ struct ChunkArgs {
     const uint16_t *planes = nullptr;  // [BH, nchunks, kda_planes::kElems] (matrix-core, gate)
     const float *alpha_ch = nullptr;   // fp32 forward: the channel-wise gate [BH, T, dk]
     void *ckpt = nullptr;        // [BH, nchunks, dk, dv]: the state at every chunk start, fp32
-                                 // from the fp32 forward, bf16 from the matrix-core forward
-                                 // (o may then be NULL: not written; no channel gate)
+                                 // from the fp32 forward (either gate), bf16 from the
+                                 // matrix-core forward (o may then be NULL: not written)
     void *uout = nullptr;        // with ckpt, matrix-core forward: [BH, T, dv] bf16, the
                                  // pseudo-values U of every row (NULL: not written)
 };
@@ -88,6 +88,8 @@ struct BwdArgs {
     int64_t BH, T;
     int32_t dk, dv;
     osdn_dtype qkv, d_dtype;
+    const float *alpha_ch = nullptr;  // the channel-wise gate [BH, T, dk] (its own backward)
+    float *galpha_ch = nullptr;       // its gradient, [BH, T, dk] fp32 (NULL: not written)
 };
 
 // The channel-wise gate's planes of one 64-row chunk (bf16 inputs): the chunk's score matrix P
@@ -146,6 +148,9 @@ hipError_t launch_precond(const PrecondArgs &a, hipStream_t stream);
 hipError_t launch_kda_planes(const KdaPrepArgs &a, hipStream_t stream);
 hipError_t launch_step_kda(const StepArgs &a, hipStream_t stream);  // alpha: [BH, dk]
 hipError_t launch_chunk_bwd(const BwdArgs &a, hipStream_t stream);
+// the backward with the channel-wise gate (alpha_ch set, alpha NULL): fp32 arithmetic, 32-row
+// chunks, Mck and dMck fp32 [BH, nchunks, dk, dv] each, Tck/Uck/dRck unused
+hipError_t launch_chunk_bwd_gate(const BwdArgs &a, hipStream_t stream);
 int32_t bwd_chunk_size(osdn_dtype qkv);  // rows per chunk of the backward
 
 }  // namespace osdn

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "lib", "libosdn.so")
 
 OSDN_F32 = 0
 OSDN_BF16 = 1
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 STATUS = {0: "OSDN_OK", -1: "OSDN_ERR_NULL", -2: "OSDN_ERR_SHAPE", -3: "OSDN_ERR_UNSUPPORTED",
           -4: "OSDN_ERR_ALIGN", -5: "OSDN_ERR_ALIAS", -6: "OSDN_ERR_LAUNCH",
@@ -26,7 +26,8 @@ EXPORTS = ("osdn_chunk_fwd", "osdn_step", "osdn_precond_scan", "osdn_precond_ste
            "osdn_step_kda",
            "osdn_chunk_bwd", "osdn_chunk_bwd_workspace", "osdn_chunk_bwd_states_workspace",
            "osdn_chunk_states_bytes",
-           "osdn_chunk_fwd_states", "osdn_chunk_bwd_states", "osdn_status_string",
+           "osdn_chunk_fwd_states", "osdn_chunk_bwd_states",
+           "osdn_chunk_bwd_kda", "osdn_chunk_bwd_kda_workspace", "osdn_status_string",
            "osdn_abi_version")
 
 
@@ -85,6 +86,11 @@ def lib() -> ctypes.CDLL:
     L.osdn_chunk_bwd_states.restype = ctypes.c_int
     L.osdn_chunk_bwd_states.argtypes = [vp] * 18 + [i64, i64, i64, i64, i32, i32, ctypes.c_int,
                                                     ctypes.c_int, vp]
+    L.osdn_chunk_bwd_kda_workspace.restype = i64
+    L.osdn_chunk_bwd_kda_workspace.argtypes = [i64, i64, i64, i32, i32, ctypes.c_int]
+    L.osdn_chunk_bwd_kda.restype = ctypes.c_int
+    L.osdn_chunk_bwd_kda.argtypes = [vp] * 17 + [i64, i64, i64, i64, i32, i32, ctypes.c_int,
+                                                 ctypes.c_int, vp]
     L.osdn_status_string.restype = ctypes.c_char_p
     L.osdn_status_string.argtypes = [ctypes.c_int]
     L.osdn_abi_version.restype = ctypes.c_int32
@@ -460,4 +466,61 @@ def osdn_chunk_bwd(q, k, v, beta, d, alpha, S0, grad_o, grad_S_T=None, *, grads=
         name = "osdn_chunk_bwd_states"
     if st != 0:
         raise OSDNError(st, name)
+    return g
+
+
+def bwd_kda_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, dtype_code: int) -> int:
+    n = lib().osdn_chunk_bwd_kda_workspace(B, H, T, dk, dv, dtype_code)
+    if n < 0:
+        raise ValueError("invalid sizes for osdn_chunk_bwd_kda")
+    return n
+
+
+def osdn_chunk_bwd_kda(q, k, v, beta, d, alpha_ch, S0, grad_o, grad_S_T=None, *, grads=None,
+                       want_grad_S0: bool = True, workspace=None, stream=None):
+    """Gradients of osdn_chunk_fwd_kda(q, k, v, beta, d, alpha_ch, S0) for output gradients
+    grad_o [B,H,T,dv] (dtype of q) and grad_S_T [B,H,dk,dv] fp32 (None: zero).  Returns a dict
+    with grad_q, grad_k, grad_v (dtype of q), grad_beta (fp32), grad_d (dtype of d),
+    grad_alpha_ch (fp32 [B,H,T,dk]) and grad_S0 (fp32, None unless want_grad_S0).  ``grads``
+    may supply some of those output tensors; the rest and the workspace are allocated with
+    torch."""
+    torch = _torch()
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    for name, t, shape in (("k", k, (B, H, T, dk)), ("v", v, (B, H, T, dv)),
+                           ("beta", beta, (B, H, T)), ("d", d, (B, H, T, dk)),
+                           ("grad_o", grad_o, (B, H, T, dv))):
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+    for name, t in (("S0", S0), ("grad_S_T", grad_S_T)):
+        if t is not None and (tuple(t.shape) != (B, H, dk, dv) or t.dtype != torch.float32):
+            raise ValueError(f"{name} must be float32 [B,H,dk,dv]")
+    if tuple(alpha_ch.shape) != (B, H, T, dk) or alpha_ch.dtype != torch.float32:
+        raise ValueError("alpha_ch must be float32 [B,H,T,dk]")
+    if k.dtype != q.dtype or v.dtype != q.dtype or grad_o.dtype != q.dtype:
+        raise TypeError("q, k, v and grad_o must share one dtype")
+    g = dict(grads or {})
+    new = lambda shape, dt: torch.empty(shape, dtype=dt, device=q.device)
+    g.setdefault("grad_q", new((B, H, T, dk), q.dtype))
+    g.setdefault("grad_k", new((B, H, T, dk), q.dtype))
+    g.setdefault("grad_v", new((B, H, T, dv), q.dtype))
+    g.setdefault("grad_beta", new((B, H, T), torch.float32))
+    g.setdefault("grad_d", new((B, H, T, dk), d.dtype))
+    g.setdefault("grad_alpha_ch", new((B, H, T, dk), torch.float32))
+    if want_grad_S0:
+        g.setdefault("grad_S0", new((B, H, dk, dv), torch.float32))
+    else:
+        g["grad_S0"] = None
+    need = bwd_kda_workspace_bytes(B, H, T, dk, dv, _dtype_code(q))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    wsb = workspace.numel() * workspace.element_size()
+    st = lib().osdn_chunk_bwd_kda(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(d), _ptr(alpha_ch), _ptr(S0), _ptr(grad_o),
+        _ptr(grad_S_T), _ptr(g["grad_q"]), _ptr(g["grad_k"]), _ptr(g["grad_v"]),
+        _ptr(g["grad_beta"]), _ptr(g["grad_d"]), _ptr(g["grad_alpha_ch"]), _ptr(g["grad_S0"]),
+        _ptr(workspace), wsb, B, H, T, dk, dv, _dtype_code(q), _dtype_code(d),
+        _stream(stream, q.device))
+    if st != 0:
+        raise OSDNError(st, "osdn_chunk_bwd_kda")
     return g

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define OSDN_ABI_VERSION 3
+#define OSDN_ABI_VERSION 4
 
 typedef enum osdn_status {
     OSDN_OK = 0,
@@ -271,6 +271,41 @@ osdn_status osdn_chunk_bwd_states(const void *q, const void *k, const void *v,
                                   int64_t workspace_bytes, int64_t B, int64_t H, int64_t T,
                                   int32_t dk, int32_t dv, osdn_dtype qkv, osdn_dtype d_dtype,
                                   void *stream);
+
+/*
+ * Gradients of the forward with the channel-wise gate (osdn_chunk_fwd_kda with the same
+ * inputs) for a scalar loss whose gradients with respect to the outputs are grad_o and
+ * grad_S_T, as for osdn_chunk_bwd.  The pages give no backward pass; these are the gradients of
+ * the token step M_t = Diag(a_t) M_{t-1} + beta_t k~_t (v_t - (Diag(a_t) M_{t-1})^T k_t)^T
+ * (Erase-then-Delta Attention, section 2.2, eq. 5, with the OSDN write key of section 2.1 of
+ * the OSDN technical summary), computed in a chunk form derived from the gated chunk algebra.
+ *
+ *   alpha_ch        [B,H,T,dk] f32   the gate, in (0, 1]: the gate's own gradient is formed as
+ *                                    d(ln a)/a, so a gate of exactly 0 gives a non-finite
+ *                                    grad_alpha_ch there (the other gradients stay finite);
+ *                                    16-byte aligned
+ *   grad_alpha_ch   [B,H,T,dk] f32   out; NULL: not written
+ *   workspace       caller-owned device memory of at least osdn_chunk_bwd_kda_workspace(B, H,
+ *                   T, dk, dv, qkv) bytes, 256-byte aligned: the state at every chunk start and
+ *                   the state gradient at every chunk end, [B,H,nchunks,dk,dv] fp32 each
+ *   every other argument   as for osdn_chunk_bwd (there is no scalar alpha here)
+ * Every product is fp32 on the vector ALUs, for either input type, with 32-row chunks; the
+ * per-feature decays inside the chunk's score products are e to differences of running sums of
+ * ln a kept in double precision, so every factor is at most 1.  Three kernels run on `stream`:
+ * the fp32 forward with the gate recording the state at every chunk start, a reverse pass over
+ * chunks for the state gradient, and the per-chunk gradients.
+ */
+int64_t osdn_chunk_bwd_kda_workspace(int64_t B, int64_t H, int64_t T, int32_t dk, int32_t dv,
+                                     osdn_dtype qkv); /* -1 if invalid */
+
+osdn_status osdn_chunk_bwd_kda(const void *q, const void *k, const void *v, const float *beta,
+                               const void *d, const float *alpha_ch, const float *S0,
+                               const void *grad_o, const float *grad_S_T, void *grad_q,
+                               void *grad_k, void *grad_v, float *grad_beta, void *grad_d,
+                               float *grad_alpha_ch, float *grad_S0, void *workspace,
+                               int64_t workspace_bytes, int64_t B, int64_t H, int64_t T,
+                               int32_t dk, int32_t dv, osdn_dtype qkv, osdn_dtype d_dtype,
+                               void *stream);
 
 /*
  * osdn_chunk_fwd_kda with no workspace argument, for callers that cannot allocate device

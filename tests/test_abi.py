@@ -393,3 +393,39 @@ def test_bwd_states_workspace_is_smaller(L):
 
 def test_chunk_bwd_states_empty_work_is_ok(L):
     assert call_bwd_states(L, B=0) == 0
+
+
+def call_bwd_kda(L, **over):
+    a = dict(q=addr(1), k=addr(2), v=addr(3), beta=addr(4), d=addr(5), a=addr(6),
+             S0=addr(7), go=addr(8), gST=addr(9), gq=addr(10), gk=addr(11), gv=addr(12),
+             gb=addr(13), gd=addr(14), ga=addr(15), gS0=addr(16), ws=addr(17), wsb=1 << 31,
+             B=2, H=3, T=100, dk=128, dv=64, qkv=osdn.OSDN_BF16, d_dtype=osdn.OSDN_F32,
+             stream=None)
+    a.update(over)
+    return L.osdn_chunk_bwd_kda(a["q"], a["k"], a["v"], a["beta"], a["d"], a["a"], a["S0"],
+                                a["go"], a["gST"], a["gq"], a["gk"], a["gv"], a["gb"], a["gd"],
+                                a["ga"], a["gS0"], a["ws"], a["wsb"], a["B"], a["H"], a["T"],
+                                a["dk"], a["dv"], a["qkv"], a["d_dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(a=None), -1), (dict(q=None), -1), (dict(gd=None), -1), (dict(ws=None), -1),
+    (dict(T=-1), -2), (dict(wsb=1000), -2), (dict(dk=96), -3), (dict(d_dtype=7), -3),
+    (dict(a=addr(6) + 4), -4), (dict(ws=addr(17) + 128), -4), (dict(ga=addr(15) + 2), -4),
+    (dict(ga=addr(6)), -5), (dict(gq=addr(15)), -5), (dict(ws=addr(6)), -5),
+])
+def test_chunk_bwd_kda_rejects(L, over, status):
+    assert call_bwd_kda(L, **over) == status
+
+
+def test_bwd_kda_workspace_size(L):
+    # two fp32 checkpoints [B,H,nchunks,dk,dv] with 32-row chunks, for either input type
+    nch = (100 + 31) // 32
+    for qkv in (osdn.OSDN_BF16, osdn.OSDN_F32):
+        assert L.osdn_chunk_bwd_kda_workspace(2, 3, 100, 128, 64, qkv) == 2 * (2 * 3 * nch * 128 * 64 * 4)
+    assert L.osdn_chunk_bwd_kda_workspace(2, 3, 100, 96, 64, osdn.OSDN_BF16) == -1
+    assert L.osdn_chunk_bwd_kda_workspace(2, 3, -1, 128, 64, osdn.OSDN_BF16) == -1
+    need = L.osdn_chunk_bwd_kda_workspace(2, 3, 100, 128, 64, osdn.OSDN_BF16)
+    assert call_bwd_kda(L, wsb=need - 1) == -2
+    assert call_bwd_kda(L, B=0) == 0
+    assert call_bwd_kda(L, T=0, gS0=None) == 0  # nothing to write
