@@ -1604,26 +1604,32 @@ hipError_t bwd_dims(const BwdArgs &a, hipStream_t stream) {
 // Every decay factor is e to a difference of running sums with the later row first, so at
 // most 1.  Rows past the end are zero with gate 1 (ln a = 0) and beta = 0.
 
-// Q, K, K~ = d (.) k in fp32 and ln a in double (zero rows, and ln a = 0, past the end)
+// Q, K, K~ = d (.) k in fp32 and ln a in double (zero rows, and ln a = 0, past the end); every
+// load is issued before the first is used
 template <int C, int DK, int PX, typename TQ, typename TD>
 __device__ __forceinline__ void load_qk_gate(const TQ *q, const TQ *k, const TD *d,
                                              const float *a, int64_t row0, int n, float *sQ,
                                              float *sK, float *sKt, double *sLg, int tid) {
-    for (int idx = tid; idx < C * DK; idx += NT) {
-        const int r = idx / DK, f = idx % DK;
-        float qv = 0.f, kv = 0.f, dv = 0.f;
-        double lg = 0.0;
-        if (r < n) {
-            const int64_t e = (row0 + r) * DK + f;
-            qv = to_f32(q[e]);
-            kv = to_f32(k[e]);
-            dv = to_f32(d[e]);
-            lg = log(fmax(static_cast<double>(a[e]), 1e-300));
-        }
-        sQ[r * PX + f] = qv;
-        sK[r * PX + f] = kv;
-        sKt[r * PX + f] = dv * kv;
-        sLg[r * PX + f] = lg;
+    constexpr int IT = C * DK / NT;
+    static_assert(IT * NT == C * DK, "tile layout");
+    float qv[IT], kv[IT], dv[IT], av[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int idx = tid + it * NT, r = idx / DK, f = idx % DK;
+        const int64_t e = (row0 + (r < n ? r : 0)) * DK + f;
+        qv[it] = to_f32(q[e]);
+        kv[it] = to_f32(k[e]);
+        dv[it] = to_f32(d[e]);
+        av[it] = a[e];
+    }
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int idx = tid + it * NT, r = idx / DK, f = idx % DK;
+        const bool in = r < n;
+        sQ[r * PX + f] = in ? qv[it] : 0.f;
+        sK[r * PX + f] = in ? kv[it] : 0.f;
+        sKt[r * PX + f] = in ? dv[it] * kv[it] : 0.f;
+        sLg[r * PX + f] = in ? log(fmax(static_cast<double>(av[it]), 1e-300)) : 0.0;
     }
 }
 

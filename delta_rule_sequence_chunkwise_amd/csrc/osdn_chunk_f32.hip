@@ -18,7 +18,8 @@
 // For the backward the kernel can also record the state at every chunk start (and skip o).
 // With the channel-wise gate a_t in R^dk (GATE; Erase-then-Delta Attention, section 2.2,
 // eq. 5) the decay is per key feature: Lg_r = sum_{t<=r} ln a_t per feature, kept in double
-// precision, and every ratio the chunk needs is formed exactly as e^{Lg_r - Lg_s} <= 1:
+// precision, and every ratio the chunk needs is formed as e^{Lg_r - Lg_s} <= 1 (for A and P
+// in one pass, each once):
 //   A[r][s] = beta_r sum_i k_ri k~_si e^{Lg_ri - Lg_si},  P[r][s] = sum_i q_ri k~_si e^{...},
 //   R = diag(beta) (V - (K o e^{Lg}) M),  O = (Q o e^{Lg}) M + P U,
 //   M <- Diag(e^{Lg_C}) M + (K~ o e^{Lg_C - Lg})^T U.
@@ -82,10 +83,8 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
     __shared__ float sgam[CH];      // e^{g_r}
     __shared__ float sdec[CH];      // e^{g_C - g_r}
     __shared__ double sLg[GATE ? CH * PX : 1];  // channel-wise gate: Lg per row and feature
-    // e^{Lg_r - Lg_s} of key feature i (channel-wise gate)
-    auto ratio = [&](int r, int s_, int i) __attribute__((always_inline)) {
-        return expf(static_cast<float>(sLg[r * PX + i] - sLg[s_ * PX + i]));
-    };
+    __shared__ float sQ[GATE ? CH * PX : 1];    // channel-wise gate: Q (A and P in one pass)
+    __shared__ float sP[GATE ? CH * PC : 1];    // channel-wise gate: P (A stays in sA)
     auto decay = [&](int r, int i) __attribute__((always_inline)) {  // e^{Lg_r}
         return expf(static_cast<float>(sLg[r * PX + i]));
     };
@@ -122,6 +121,7 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
             }
             sX[r * PX + i] = kv;
             sKt[r * PX + i] = dd * kv;
+            if constexpr (GATE) sQ[r * PX + i] = r < n ? to_f32(q[(row0 + r) * DK + i]) : 0.f;
         }
         for (int idx = tid; idx < CH * BV; idx += kThreads) {
             const int r = idx / BV, j = idx % BV;
@@ -163,77 +163,120 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
         }
         __syncthreads();
 
-        // a2: strictly lower Gram matrix of (K, K~), gated and decayed
-        for (int idx = tid; idx < CH * CH; idx += kThreads) {
-            const int r = idx / CH, s = idx % CH;
-            float val = 0.f;
-            if (s < r) {
-                float dot = 0.f;
-                if constexpr (GATE) {
-                    for (int i = 0; i < DK; ++i) dot += sX[r * PX + i] * sKt[s * PX + i] * ratio(r, s, i);
-                    val = sb[r] * dot;
-                } else {
+        if constexpr (GATE) {
+            // a2, a5 in one pass, the decay of each (row, column, feature) formed once and used
+            // for both: thread (r, s0) owns columns s0, s0 + 1 of row r
+            static_assert(CH * CH / 2 <= kThreads, "gate scores layout");
+            if (tid < CH * CH / 2) {
+                const int r = tid / (CH / 2), s0 = (tid % (CH / 2)) * 2;
+                float ak0 = 0.f, ak1 = 0.f, aq0 = 0.f, aq1 = 0.f;
+                if (s0 <= r) {
+                    const bool two = s0 + 1 <= r;
+                    for (int i = 0; i < DK; ++i) {
+                        const double lr = sLg[r * PX + i];
+                        const float e0 = __expf(static_cast<float>(lr - sLg[s0 * PX + i])) *
+                                         sKt[s0 * PX + i];
+                        const float e1 =
+                            two ? __expf(static_cast<float>(lr - sLg[(s0 + 1) * PX + i])) *
+                                      sKt[(s0 + 1) * PX + i]
+                                : 0.f;
+                        const float kx = sX[r * PX + i], qx = sQ[r * PX + i];
+                        ak0 += kx * e0;
+                        ak1 += kx * e1;
+                        aq0 += qx * e0;
+                        aq1 += qx * e1;
+                    }
+                }
+                sA[r * PC + s0] = s0 < r ? sb[r] * ak0 : 0.f;
+                sA[r * PC + s0 + 1] = s0 + 1 < r ? sb[r] * ak1 : 0.f;
+                sP[r * PC + s0] = s0 <= r ? aq0 : 0.f;
+                sP[r * PC + s0 + 1] = s0 + 1 <= r ? aq1 : 0.f;
+            }
+            __syncthreads();
+            // in place, once per element: K o G, Q o G, K~ o e^{Lg_C - Lg}
+            for (int idx = tid; idx < CH * DK; idx += kThreads) {
+                const int r = idx / DK, i = idx % DK;
+                const double lg = sLg[r * PX + i];
+                const float g = __expf(static_cast<float>(lg));
+                sX[r * PX + i] *= g;
+                sQ[r * PX + i] *= g;
+                sKt[r * PX + i] *= __expf(static_cast<float>(sLg[(CH - 1) * PX + i] - lg));
+            }
+            __syncthreads();
+            // a3: R = diag(beta) (V - (K o G) M)
+            for (int idx = tid; idx < CH * BV; idx += kThreads) {
+                const int r = idx / BV, j = idx % BV;
+                float km = 0.f;
+                for (int i = 0; i < DK; ++i) km += sX[r * PX + i] * sM[i * PV + j];
+                sR[r * PV + j] = sb[r] * (sR[r * PV + j] - km);
+            }
+            __syncthreads();
+            // a4: U = (I + A)^{-1} R in place
+            solve_unit_lower<CH, BV, PV, PC>(sR, sA, tid);
+            __syncthreads();
+            // (Q o G) M for the inter-chunk read-out
+            for (int idx = tid; idx < CH * BV; idx += kThreads) {
+                const int r = idx / BV, j = idx % BV;
+                float qm = 0.f;
+                for (int i = 0; i < DK; ++i) qm += sQ[r * PX + i] * sM[i * PV + j];
+                sQM[r * PV + j] = qm;
+            }
+            __syncthreads();
+        } else {
+            // a2: strictly lower Gram matrix of (K, K~), decayed
+            for (int idx = tid; idx < CH * CH; idx += kThreads) {
+                const int r = idx / CH, s = idx % CH;
+                float val = 0.f;
+                if (s < r) {
+                    float dot = 0.f;
                     for (int i = 0; i < DK; ++i) dot += sX[r * PX + i] * sKt[s * PX + i];
                     val = sb[r] * __expf(sg[r] - sg[s]) * dot;
                 }
+                sA[r * PC + s] = val;
             }
-            sA[r * PC + s] = val;
-        }
-        // a3: R = diag(beta) (V - diag(e^g) K M)
-        for (int idx = tid; idx < CH * BV; idx += kThreads) {
-            const int r = idx / BV, j = idx % BV;
-            float km = 0.f;
-            if constexpr (GATE) {
-                for (int i = 0; i < DK; ++i) km += sX[r * PX + i] * decay(r, i) * sM[i * PV + j];
-            } else {
+            // a3: R = diag(beta) (V - diag(e^g) K M)
+            for (int idx = tid; idx < CH * BV; idx += kThreads) {
+                const int r = idx / BV, j = idx % BV;
+                float km = 0.f;
                 for (int i = 0; i < DK; ++i) km += sX[r * PX + i] * sM[i * PV + j];
+                sR[r * PV + j] = sb[r] * (sR[r * PV + j] - sgam[r] * km);
             }
-            sR[r * PV + j] = sb[r] * (sR[r * PV + j] - sgam[r] * km);
-        }
-        __syncthreads();
+            __syncthreads();
 
-        // a4: U = (I + A)^{-1} R in place; then stage Q over K (K is no longer read)
-        solve_unit_lower<CH, BV, PV, PC>(sR, sA, tid);
-        for (int idx = tid; idx < CH * DK; idx += kThreads) {
-            const int r = idx / DK, i = idx % DK;
-            sX[r * PX + i] = r < n ? to_f32(q[(row0 + r) * DK + i]) : 0.f;
-        }
-        __syncthreads();
+            // a4: U = (I + A)^{-1} R in place; then stage Q over K (K is no longer read)
+            solve_unit_lower<CH, BV, PV, PC>(sR, sA, tid);
+            for (int idx = tid; idx < CH * DK; idx += kThreads) {
+                const int r = idx / DK, i = idx % DK;
+                sX[r * PX + i] = r < n ? to_f32(q[(row0 + r) * DK + i]) : 0.f;
+            }
+            __syncthreads();
 
-        // a5: P = lower-inclusive (Q K~^T) with decay;  Q M for the inter-chunk read-out
-        for (int idx = tid; idx < CH * CH; idx += kThreads) {
-            const int r = idx / CH, s = idx % CH;
-            float val = 0.f;
-            if (s <= r) {
-                float dot = 0.f;
-                if constexpr (GATE) {
-                    for (int i = 0; i < DK; ++i) dot += sX[r * PX + i] * sKt[s * PX + i] * ratio(r, s, i);
-                    val = dot;
-                } else {
+            // a5: P = lower-inclusive (Q K~^T) with decay;  Q M for the inter-chunk read-out
+            for (int idx = tid; idx < CH * CH; idx += kThreads) {
+                const int r = idx / CH, s = idx % CH;
+                float val = 0.f;
+                if (s <= r) {
+                    float dot = 0.f;
                     for (int i = 0; i < DK; ++i) dot += sX[r * PX + i] * sKt[s * PX + i];
                     val = __expf(sg[r] - sg[s]) * dot;
                 }
+                sA[r * PC + s] = val;
             }
-            sA[r * PC + s] = val;
-        }
-        for (int idx = tid; idx < CH * BV; idx += kThreads) {
-            const int r = idx / BV, j = idx % BV;
-            float qm = 0.f;
-            if constexpr (GATE) {
-                for (int i = 0; i < DK; ++i) qm += sX[r * PX + i] * decay(r, i) * sM[i * PV + j];
-            } else {
+            for (int idx = tid; idx < CH * BV; idx += kThreads) {
+                const int r = idx / BV, j = idx % BV;
+                float qm = 0.f;
                 for (int i = 0; i < DK; ++i) qm += sX[r * PX + i] * sM[i * PV + j];
+                sQM[r * PV + j] = qm;
             }
-            sQM[r * PV + j] = qm;
+            __syncthreads();
         }
-        __syncthreads();
-
         // a6: outputs of this chunk and the state carried to the next one
         for (int idx = tid; idx < CH * BV; idx += kThreads) {
             const int r = idx / BV, j = idx % BV;
             if (o && r < n) {
+                const float *Pm = GATE ? sP : sA;  // the scores
                 float acc = sgam[r] * sQM[r * PV + j];
-                for (int s = 0; s <= r; ++s) acc += sA[r * PC + s] * sR[s * PV + j];
+                for (int s = 0; s <= r; ++s) acc += Pm[r * PC + s] * sR[s * PV + j];
                 o[(row0 + r) * dv + j0 + j] = from_f32<TQ>(acc);
             }
         }
@@ -241,9 +284,8 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
         for (int idx = tid; idx < DK * BV; idx += kThreads) {
             const int i = idx / BV, j = idx % BV;
             float acc = 0.f;
-            if constexpr (GATE) {
-                for (int s = 0; s < CH; ++s)
-                    acc += ratio(CH - 1, s, i) * sKt[s * PX + i] * sR[s * PV + j];
+            if constexpr (GATE) {  // sKt holds K~ o e^{Lg_C - Lg} here
+                for (int s = 0; s < CH; ++s) acc += sKt[s * PX + i] * sR[s * PV + j];
                 sM[i * PV + j] = decay(CH - 1, i) * sM[i * PV + j] + acc;
             } else {
                 for (int s = 0; s < CH; ++s)
