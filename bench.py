@@ -96,8 +96,11 @@ def load_traffic(name, paths):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=100)
+    # Long enough for the board's clocks to settle: timed launch by launch at the 1.3B shape,
+    # the forward takes ~150 us for its first ~10 launches, ~190 us around launch 20, and
+    # settles at ~152 us after ~60 launches; the timed steps follow that transient.
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--precond-steps", type=int, default=20)
     ap.add_argument("--kda-steps", type=int, default=10)

@@ -778,10 +778,54 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
     // Prep wave 0 also runs the decay scan of chunk c+2 after its tiles (it issues no memory
     // instruction, so neither its LDS writes nor its scan wait for loads); the loader brought
     // that chunk's beta and alpha into LDS a step earlier.
+    // L2 warm-up (the second prep wave, plain variant): two steps before the loader and the
+    // stagers load chunk cc, this workgroup touches its share (1/nvt) of the chunk's 128-byte
+    // lines of q, k, d and v with one dword load each, so that their loads hit L2 instead of
+    // waiting on HBM.  The values are only waited for two steps later (an empty asm use).
+    constexpr int QL = DK * 2 / 128;                 // 128-byte lines per row of q (and k)
+    constexpr int DL = DK * int(sizeof(TD)) / 128;   // ... of d
+    constexpr int PFN = (2 * QL + DL + 2 + 1) / 2;   // loads per lane (at most 2 lines of v a
+                                                     // row, at least 2 workgroups a sequence)
+    constexpr int PFD = 2;                           // prefetch distance in chunks
+    const int VL = dv * 2 / 128;                     // ... of v
+    const int RL = 2 * QL + DL + VL;                 // lines per row, all four tensors
+    auto prefetch = [&](int64_t cc, uint32_t (&pf)[PFN]) __attribute__((always_inline)) {
+        const int n = cc < nchunks ? rows_of(cc) : 0;
+        const int total = n * RL, per = (total + nvt - 1) / nvt, first = vt * per;
+#pragma unroll
+        for (int i = 0; i < PFN; ++i) {
+            const int li = 64 * i + lane, l = first + li;
+            uint32_t x = 0;
+            if (li < per && l < total) {
+                const int row = l / RL, w = l % RL;
+                const int64_t tr = seq0 + cc * CH + row;
+                const char *p;
+                if (w < QL) p = reinterpret_cast<const char *>(q + tr * DK) + 128 * w;
+                else if (w < 2 * QL) p = reinterpret_cast<const char *>(k + tr * DK) + 128 * (w - QL);
+                else if (w < 2 * QL + DL) p = reinterpret_cast<const char *>(d + tr * DK) + 128 * (w - 2 * QL);
+                else p = reinterpret_cast<const char *>(v + tr * dv) + 128 * (w - 2 * QL - DL);
+                x = *reinterpret_cast<const uint32_t *>(p);
+            }
+            pf[i] = x;
+        }
+    };
+    // one loop per prep wave, so its registers need no merging between the two variants.
+    // Prep wave 0 also runs the decay scan of chunk c+2 after its tiles (it issues no memory
+    // instruction, so neither its LDS writes nor its scan wait for loads); the loader brought
+    // that chunk's beta and alpha into LDS a step earlier.
     auto prep_loop = [&](auto pw_c) __attribute__((always_inline)) {
         constexpr int PW = decltype(pw_c)::value;
+        constexpr bool PF = !GATE && PW == 1;
+        uint32_t pfa[PFN], pfb[PFN];
+#pragma unroll
+        for (int i = 0; i < PFN; ++i) pfa[i] = pfb[i] = 0;
         int sl1 = 2;  // (c+1) mod 3; (c+2) mod 3 is the slot after it
-        for (int64_t c = -2; c < nchunks; ++c) {
+        auto body = [&](int64_t c, uint32_t (&pf)[PFN]) __attribute__((always_inline)) {
+            if constexpr (PF) {
+#pragma unroll
+                for (int i = 0; i < PFN; ++i) asm volatile("" ::"v"(pf[i]));  // from step c-2
+                prefetch(c + 2 + PFD, pf);
+            }
             if constexpr (!GATE) {
                 prep_step(pw_c, c, sl1);
             } else if constexpr (PW == 1) {
@@ -809,6 +853,14 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
             }
             block_sync();
             sl1 = sl1 == 2 ? 0 : sl1 + 1;
+        };
+        for (int64_t c = -2; c < nchunks; c += 2) {
+            body(c, pfa);
+            if (c + 1 < nchunks) body(c + 1, pfb);
+        }
+        if constexpr (PF) {
+#pragma unroll
+            for (int i = 0; i < PFN; ++i) asm volatile("" ::"v"(pfa[i]), "v"(pfb[i]));
         }
     };
     if (wave == 2) prep_loop(I0{});
