@@ -778,7 +778,7 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
     // Prep wave 0 also runs the decay scan of chunk c+2 after its tiles (it issues no memory
     // instruction, so neither its LDS writes nor its scan wait for loads); the loader brought
     // that chunk's beta and alpha into LDS a step earlier.
-    // L2 warm-up (the second prep wave, plain variant): two steps before the loader and the
+    // L2 warm-up (the second prep wave, plain forward): two steps before the loader and the
     // stagers load chunk cc, this workgroup touches its share (1/nvt) of the chunk's 128-byte
     // lines of q, k, d and v with one dword load each, so that their loads hit L2 instead of
     // waiting on HBM.  The values are only waited for two steps later (an empty asm use).
@@ -815,7 +815,9 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
     // that chunk's beta and alpha into LDS a step earlier.
     auto prep_loop = [&](auto pw_c) __attribute__((always_inline)) {
         constexpr int PW = decltype(pw_c)::value;
-        constexpr bool PF = !GATE && PW == 1;
+        constexpr bool PF = !GATE && !CKPT && PW == 1;  // (with the checkpoint stores in the
+                                                         // way, the warmed lines were evicted
+                                                         // before use: +38 MB fetched)
         uint32_t pfa[PFN], pfb[PFN];
 #pragma unroll
         for (int i = 0; i < PFN; ++i) pfa[i] = pfb[i] = 0;
