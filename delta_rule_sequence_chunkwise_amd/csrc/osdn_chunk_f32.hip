@@ -62,6 +62,24 @@ __device__ __forceinline__ void solve_unit_lower(float *X, const float *A, int t
     for (int i = 0; i < RPT; ++i) X[(i * TPC + sub) * PX + j] = mine[i];
 }
 
+// acc[m][n] += sum_{kk < K} a(i0 + m, kk) * b(kk, j0 + n): a register-blocked product tile,
+// each operand value read from LDS once per TN (or TM) products
+template <int TM, int TN, int K, typename FA, typename FB>
+__device__ __forceinline__ void tile_mm(float (&acc)[TM][TN], int i0, int j0, FA &&a, FB &&b) {
+#pragma unroll 4
+    for (int kk = 0; kk < K; ++kk) {
+        float av[TM], bv[TN];
+#pragma unroll
+        for (int m = 0; m < TM; ++m) av[m] = a(i0 + m, kk);
+#pragma unroll
+        for (int nn = 0; nn < TN; ++nn) bv[nn] = b(kk, j0 + nn);
+#pragma unroll
+        for (int m = 0; m < TM; ++m)
+#pragma unroll
+            for (int nn = 0; nn < TN; ++nn) acc[m][nn] += av[m] * bv[nn];
+    }
+}
+
 template <int DK, int BV, int CH, typename TQ, typename TD, bool GATE>
 __global__ void __launch_bounds__(kThreads)
 chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
@@ -93,6 +111,18 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
     const int64_t bh = blockIdx.x / ntiles;
     const int j0 = (blockIdx.x % ntiles) * BV;
     const int tid = threadIdx.x;
+    // product tiles: thread (ty, tx) of a 32 x 16 grid owns rows ty TM.., columns tx TN..
+    static_assert(kThreads == 512 && BV == 32, "tile layout");
+    constexpr int TR = CH < 32 ? 1 : CH / 32;  // rows per thread of a CH-row product
+    constexpr int TS = CH / 16;                // columns per thread of a CH x CH product
+    constexpr int TD_ = DK / 32;               // rows per thread of the DK-row state update
+    const int ty = tid >> 4, tx = tid & 15;
+    const int ir = ty * TR;                    // first row of a CH-row tile (< CH: active)
+    const bool rows_ok = ir < CH;
+    auto zero_tile = [](auto &acc) __attribute__((always_inline)) {
+        for (auto &row : acc)
+            for (auto &x : row) x = 0.f;
+    };
 
     for (int idx = tid; idx < DK * BV; idx += kThreads) {
         const int i = idx / BV, j = idx % BV;
@@ -204,42 +234,63 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
             }
             __syncthreads();
             // a3: R = diag(beta) (V - (K o G) M)
-            for (int idx = tid; idx < CH * BV; idx += kThreads) {
-                const int r = idx / BV, j = idx % BV;
-                float km = 0.f;
-                for (int i = 0; i < DK; ++i) km += sX[r * PX + i] * sM[i * PV + j];
-                sR[r * PV + j] = sb[r] * (sR[r * PV + j] - km);
+            if (rows_ok) {
+                float km[TR][2];
+                zero_tile(km);
+                tile_mm<TR, 2, DK>(km, ir, 2 * tx, [&](int r, int i) { return sX[r * PX + i]; },
+                                   [&](int i, int j) { return sM[i * PV + j]; });
+#pragma unroll
+                for (int m = 0; m < TR; ++m)
+#pragma unroll
+                    for (int nn = 0; nn < 2; ++nn) {
+                        const int r = ir + m, j = 2 * tx + nn;
+                        sR[r * PV + j] = sb[r] * (sR[r * PV + j] - km[m][nn]);
+                    }
             }
             __syncthreads();
             // a4: U = (I + A)^{-1} R in place
             solve_unit_lower<CH, BV, PV, PC>(sR, sA, tid);
             __syncthreads();
             // (Q o G) M for the inter-chunk read-out
-            for (int idx = tid; idx < CH * BV; idx += kThreads) {
-                const int r = idx / BV, j = idx % BV;
-                float qm = 0.f;
-                for (int i = 0; i < DK; ++i) qm += sQ[r * PX + i] * sM[i * PV + j];
-                sQM[r * PV + j] = qm;
+            if (rows_ok) {
+                float qm[TR][2];
+                zero_tile(qm);
+                tile_mm<TR, 2, DK>(qm, ir, 2 * tx, [&](int r, int i) { return sQ[r * PX + i]; },
+                                   [&](int i, int j) { return sM[i * PV + j]; });
+#pragma unroll
+                for (int m = 0; m < TR; ++m)
+#pragma unroll
+                    for (int nn = 0; nn < 2; ++nn) sQM[(ir + m) * PV + 2 * tx + nn] = qm[m][nn];
             }
             __syncthreads();
         } else {
-            // a2: strictly lower Gram matrix of (K, K~), decayed
-            for (int idx = tid; idx < CH * CH; idx += kThreads) {
-                const int r = idx / CH, s = idx % CH;
-                float val = 0.f;
-                if (s < r) {
-                    float dot = 0.f;
-                    for (int i = 0; i < DK; ++i) dot += sX[r * PX + i] * sKt[s * PX + i];
-                    val = sb[r] * __expf(sg[r] - sg[s]) * dot;
-                }
-                sA[r * PC + s] = val;
-            }
-            // a3: R = diag(beta) (V - diag(e^g) K M)
-            for (int idx = tid; idx < CH * BV; idx += kThreads) {
-                const int r = idx / BV, j = idx % BV;
-                float km = 0.f;
-                for (int i = 0; i < DK; ++i) km += sX[r * PX + i] * sM[i * PV + j];
-                sR[r * PV + j] = sb[r] * (sR[r * PV + j] - sgam[r] * km);
+            // a2: strictly lower Gram matrix of (K, K~), decayed (tiles above the diagonal
+            // stay zero); a3: R = diag(beta) (V - diag(e^g) K M)
+            if (rows_ok) {
+                const int is = tx * TS;
+                float ak[TR][TS];
+                zero_tile(ak);
+                if (is <= ir + TR - 1)
+                    tile_mm<TR, TS, DK>(ak, ir, is, [&](int r, int i) { return sX[r * PX + i]; },
+                                        [&](int i, int s_) { return sKt[s_ * PX + i]; });
+#pragma unroll
+                for (int m = 0; m < TR; ++m)
+#pragma unroll
+                    for (int nn = 0; nn < TS; ++nn) {
+                        const int r = ir + m, s_ = is + nn;
+                        sA[r * PC + s_] = s_ < r ? sb[r] * __expf(sg[r] - sg[s_]) * ak[m][nn] : 0.f;
+                    }
+                float km[TR][2];
+                zero_tile(km);
+                tile_mm<TR, 2, DK>(km, ir, 2 * tx, [&](int r, int i) { return sX[r * PX + i]; },
+                                   [&](int i, int j) { return sM[i * PV + j]; });
+#pragma unroll
+                for (int m = 0; m < TR; ++m)
+#pragma unroll
+                    for (int nn = 0; nn < 2; ++nn) {
+                        const int r = ir + m, j = 2 * tx + nn;
+                        sR[r * PV + j] = sb[r] * (sR[r * PV + j] - sgam[r] * km[m][nn]);
+                    }
             }
             __syncthreads();
 
@@ -252,46 +303,72 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
             __syncthreads();
 
             // a5: P = lower-inclusive (Q K~^T) with decay;  Q M for the inter-chunk read-out
-            for (int idx = tid; idx < CH * CH; idx += kThreads) {
-                const int r = idx / CH, s = idx % CH;
-                float val = 0.f;
-                if (s <= r) {
-                    float dot = 0.f;
-                    for (int i = 0; i < DK; ++i) dot += sX[r * PX + i] * sKt[s * PX + i];
-                    val = __expf(sg[r] - sg[s]) * dot;
-                }
-                sA[r * PC + s] = val;
-            }
-            for (int idx = tid; idx < CH * BV; idx += kThreads) {
-                const int r = idx / BV, j = idx % BV;
-                float qm = 0.f;
-                for (int i = 0; i < DK; ++i) qm += sX[r * PX + i] * sM[i * PV + j];
-                sQM[r * PV + j] = qm;
+            if (rows_ok) {
+                const int is = tx * TS;
+                float aq[TR][TS];
+                zero_tile(aq);
+                if (is <= ir + TR - 1)
+                    tile_mm<TR, TS, DK>(aq, ir, is, [&](int r, int i) { return sX[r * PX + i]; },
+                                        [&](int i, int s_) { return sKt[s_ * PX + i]; });
+#pragma unroll
+                for (int m = 0; m < TR; ++m)
+#pragma unroll
+                    for (int nn = 0; nn < TS; ++nn) {
+                        const int r = ir + m, s_ = is + nn;
+                        sA[r * PC + s_] = s_ <= r ? __expf(sg[r] - sg[s_]) * aq[m][nn] : 0.f;
+                    }
+                float qm[TR][2];
+                zero_tile(qm);
+                tile_mm<TR, 2, DK>(qm, ir, 2 * tx, [&](int r, int i) { return sX[r * PX + i]; },
+                                   [&](int i, int j) { return sM[i * PV + j]; });
+#pragma unroll
+                for (int m = 0; m < TR; ++m)
+#pragma unroll
+                    for (int nn = 0; nn < 2; ++nn) sQM[(ir + m) * PV + 2 * tx + nn] = qm[m][nn];
             }
             __syncthreads();
         }
-        // a6: outputs of this chunk and the state carried to the next one
-        for (int idx = tid; idx < CH * BV; idx += kThreads) {
-            const int r = idx / BV, j = idx % BV;
-            if (o && r < n) {
-                const float *Pm = GATE ? sP : sA;  // the scores
-                float acc = sgam[r] * sQM[r * PV + j];
-                for (int s = 0; s <= r; ++s) acc += Pm[r * PC + s] * sR[s * PV + j];
-                o[(row0 + r) * dv + j0 + j] = from_f32<TQ>(acc);
+        // a6: outputs of this chunk (P is zero above the diagonal) and the state carried to
+        // the next one
+        if (o && rows_ok) {
+            const float *Pm = GATE ? sP : sA;  // the scores
+            float pu[TR][2];
+            zero_tile(pu);
+            tile_mm<TR, 2, CH>(pu, ir, 2 * tx, [&](int r, int s_) { return Pm[r * PC + s_]; },
+                               [&](int s_, int j) { return sR[s_ * PV + j]; });
+#pragma unroll
+            for (int m = 0; m < TR; ++m) {
+                const int r = ir + m;
+                if (r < n) {
+#pragma unroll
+                    for (int nn = 0; nn < 2; ++nn) {
+                        const int j = 2 * tx + nn;
+                        o[(row0 + r) * dv + j0 + j] =
+                            from_f32<TQ>(sgam[r] * sQM[r * PV + j] + pu[m][nn]);
+                    }
+                }
             }
         }
-        const float gam_last = sgam[CH - 1];
-        for (int idx = tid; idx < DK * BV; idx += kThreads) {
-            const int i = idx / BV, j = idx % BV;
-            float acc = 0.f;
-            if constexpr (GATE) {  // sKt holds K~ o e^{Lg_C - Lg} here
-                for (int s = 0; s < CH; ++s) acc += sKt[s * PX + i] * sR[s * PV + j];
-                sM[i * PV + j] = decay(CH - 1, i) * sM[i * PV + j] + acc;
-            } else {
-                for (int s = 0; s < CH; ++s)
-                    acc += sdec[s] * sKt[s * PX + i] * sR[s * PV + j];
-                sM[i * PV + j] = gam_last * sM[i * PV + j] + acc;
-            }
+        {
+            const int id = ty * TD_;
+            float mu[TD_][2];
+            zero_tile(mu);
+            if constexpr (GATE)  // sKt holds K~ o e^{Lg_C - Lg} here
+                tile_mm<TD_, 2, CH>(mu, id, 2 * tx, [&](int i, int s_) { return sKt[s_ * PX + i]; },
+                                    [&](int s_, int j) { return sR[s_ * PV + j]; });
+            else
+                tile_mm<TD_, 2, CH>(mu, id, 2 * tx,
+                                    [&](int i, int s_) { return sdec[s_] * sKt[s_ * PX + i]; },
+                                    [&](int s_, int j) { return sR[s_ * PV + j]; });
+            const float gam_last = sgam[CH - 1];
+#pragma unroll
+            for (int m = 0; m < TD_; ++m)
+#pragma unroll
+                for (int nn = 0; nn < 2; ++nn) {
+                    const int i = id + m, j = 2 * tx + nn;
+                    const float keep = GATE ? decay(CH - 1, i) : gam_last;
+                    sM[i * PV + j] = keep * sM[i * PV + j] + mu[m][nn];
+                }
         }
     }
     __syncthreads();
