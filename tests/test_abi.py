@@ -429,3 +429,23 @@ def test_bwd_kda_workspace_size(L):
     assert call_bwd_kda(L, wsb=need - 1) == -2
     assert call_bwd_kda(L, B=0) == 0
     assert call_bwd_kda(L, T=0, gS0=None) == 0  # nothing to write
+
+
+def test_header_compiles_as_c_and_links(L, tmp_path):
+    """include/osdn.h is plain C (C99, no C++ types in the signatures): a C program that
+    includes it compiles warning-free, links against the library and sees the same ABI
+    version as the library."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "abi.c"
+    src.write_text('#include "osdn.h"\n'
+                   "int main(void) { return osdn_abi_version() == OSDN_ABI_VERSION ? 0 : 1; }\n")
+    exe = tmp_path / "abi"
+    lib_dir = os.path.dirname(osdn.LIB_PATH)
+    subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                    "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe),
+                    "-L", lib_dir, "-losdn", f"-Wl,-rpath,{lib_dir}"], check=True)
+    subprocess.run([str(exe)], check=True)
