@@ -10,9 +10,12 @@
 //   a5  P = lower-inclusive( (Q K~^T) (.) e^{g_r - g_s} )                    intra-chunk scores
 //   a6  O = diag(gam) Q M + P U;   M <- gam_C M + K~^T diag(w) U            read-out, carry
 //
-// One workgroup of seven waves owns one (b,h) sequence and a 32-wide slice of the value
-// columns (value columns are independent given the chunk's A and P) and walks the chunks in
-// order, one barrier per step.  Each role runs its own loop over steps c = -2 .. nchunks-1:
+// One workgroup owns one (b,h) sequence and a slice of the value columns (value columns are
+// independent given the chunk's A and P) and walks the chunks in order, one barrier per step.
+// The slice is 32 columns wide (seven waves, numbered as below), or 16 (six waves: one state
+// wave, the other roles numbered one lower) when the grid of 16-column slices still fits the
+// device with one workgroup per compute unit (long sequences, few heads).  Each role runs its
+// own loop over steps c = -2 .. nchunks-1:
 //
 // * State waves (0, 1), one per 16 value columns, process chunk c.  A state wave holds its
 //   dk x 16 slice of M in VGPRs (fp32, the C layout of 16x16 MFMA tiles) for the whole
@@ -61,9 +64,10 @@ namespace {
 constexpr int CH = 64;                       // rows per chunk
 constexpr int NBLK = CH / 16;                // 16-row blocks per chunk
 constexpr int NOFF = NBLK * (NBLK - 1) / 2;  // off-diagonal 16x16 blocks of the Gram matrix
-constexpr int BV = 32;                       // value columns per workgroup
-constexpr int NW = 7;  // waves per workgroup: 2 state, 2 prep, 2 stagers, 1 loader
 constexpr int VW = 16;                       // value columns per state wave
+// A workgroup runs NSW state waves (one per 16 value columns of its slice), then 2 prep waves,
+// 2 stagers and 1 loader: NSW + 5 waves, a slice of 16 NSW value columns.
+__host__ __device__ constexpr int n_waves(int nsw) { return nsw + 5; }
 
 template <int DK, bool GATE = false>
 struct alignas(16) Lds {
@@ -77,12 +81,20 @@ struct alignas(16) Lds {
     //   unit from each of 16 consecutive rows.
     __device__ static constexpr int fqk(int r) { return DK == 128 ? (r & 15) : ((r >> 1) & 7); }
     __device__ static constexpr int qk_at(int r, int u) { return (r * KU + (u ^ fqk(r))) * 8; }
-    // * k~: 8-byte granule g of row r sits at granule g ^ 2 pk(r), pk a bit permutation of the
-    //   row index, so that both 16-byte reads of 16 consecutive rows and the transposing reads
-    //   (four granules of rows k0..k0+3 and k0+8..k0+11) are spread over all banks.
+    // * k~: 8-byte granule g of row r sits at granule g ^ 2 pk(r).  The tile is read three
+    //   ways: 16-byte units of 16 consecutive rows (prep waves), written the same way
+    //   (stagers), and read by transposing reads of four granules of rows k0..k0+3 and
+    //   k0+8..k0+11 (state waves).  Measured on gfx950: a 16-byte read is served 16 lanes at a
+    //   time from the 64 banks, lanes grouped by half-wave and by the parity of lane bits 2..4;
+    //   a 16-byte write 8 lanes at a time from 32 banks; a transposing read 32 lanes at a time
+    //   from 64.  pk (a linear map of the row's low four bits) keeps the writes and the
+    //   transposing reads conflict-free.  With dk = 64 the prep reads are conflict-free too;
+    //   with dk = 128 the map that also achieves that measured slower, so each of those reads
+    //   takes two extra cycles.
     __device__ static constexpr int pk(int r) {
-        return DK == 128 ? (((r & 3) << 2) | (((r >> 3) & 1) << 1) | ((r >> 2) & 1))
-                         : ((((r >> 1) & 1) << 2) | (((r >> 3) & 1) << 1) | ((r >> 2) & 1));
+        const int b0 = r & 1, b1 = (r >> 1) & 1, b2 = (r >> 2) & 1, b3 = (r >> 3) & 1;
+        return DK == 128 ? (b2 | (b0 << 1) | (b1 << 2) | (b3 << 3))
+                         : (b2 | ((b0 ^ b2 ^ b3) << 1) | (b1 << 2));
     }
     __device__ static constexpr int kt_gr(int r, int g) { return r * KP + 4 * (g ^ (2 * pk(r))); }
     __device__ static constexpr int kt_at(int r, int u) { return kt_gr(r, 2 * u); }
@@ -180,11 +192,12 @@ __device__ __forceinline__ void copy_image(uint16_t *dst, const uint16_t *src, i
     }
 }
 
-// the workgroup's 64 x 32 slice of v into LDS as [value tile][row][16] (loader wave)
+// the workgroup's 64 x 16 NSW slice of v into LDS as [value tile][row][16] (loader wave)
+template <int NSW>
 __device__ __forceinline__ void load_v(uint16_t *vb, const uint16_t *v, int64_t row0, int n,
                                        int dv, int j0, int lane) {
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
+    for (int ii = 0; ii < 2 * NSW; ++ii) {
         const int vt = ii >> 1, h = ii & 1;
         const int r = 32 * h + (lane >> 1);
         load_to_lds16(v + (row0 + min(r, n - 1)) * dv + j0 + VW * vt + 8 * (lane & 1),
@@ -299,8 +312,8 @@ __device__ __forceinline__ void diag_inverse2(Lds<DK, G> &sm, int b, int kb0, in
             pack4u(Y[j]);
 }
 
-template <int DK, typename TD, bool GATE, bool CKPT, bool OUT>
-__global__ void __launch_bounds__(NW * 64)
+template <int DK, typename TD, bool GATE, bool CKPT, bool OUT, int NSW>
+__global__ void __launch_bounds__(n_waves(NSW) * 64)
 chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                   const uint16_t *__restrict__ v, const TD *__restrict__ d,
                   const float *__restrict__ beta, const float *__restrict__ alpha,
@@ -310,6 +323,10 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
     using L = Lds<DK, GATE>;
     constexpr int NS = DK / 32;   // 32-wide k-steps over the key features
     constexpr int NFT = DK / 16;  // 16-row feature tiles of the state
+    constexpr int NW = n_waves(NSW);
+    constexpr int BV = VW * NSW;  // value columns of the workgroup's slice
+    // roles by wave: state waves first, then the prep waves, the stagers and the loader
+    constexpr int W_PREP = NSW, W_STAGE = NSW + 2, W_LOAD = NSW + 4;
 
     __shared__ L sm;
     // q, k and v tiles by chunk parity: one __shared__ variable each, indexed by the parity,
@@ -352,7 +369,7 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
         load_to_lds4(beta + r, &sm.rawb[par][0]);
         if (has_alpha) load_to_lds4(alpha + r, &sm.rawa[par][0]);
     };
-    if (wave == 6 && nchunks > 0) {
+    if (wave == W_LOAD && nchunks > 0) {
         load_ba(0, 0);
         wait_global();
     }
@@ -365,7 +382,7 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
     // Gram/score tiles and block inverses of chunk c+1; the loader brings q, k, v of chunk
     // c+2 into LDS and scans it; the stager writes k~ of chunk c+2.
 
-    if (wave < 2) {
+    if (wave < NSW) {
         // ---- state waves -----------------------------------------------------------------------
         const int ct = wave;  // value tile
         v4f M[NFT], KM[NBLK], Z[NBLK];
@@ -537,7 +554,7 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
         return;
     }
 
-    if (wave == 6) {
+    if (wave == W_LOAD) {
         // ---- loader wave: q and v of chunk c+2 into LDS, and the decay scan of chunk c+2 ------
         // Issuing the loads stalls while HBM drains them, so a wave with little other work
         // issues them; the parity of the target buffers is a compile-time constant.
@@ -553,7 +570,7 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                 const int64_t r0 = seq0 + cc * CH;
                 const int n = rows_of(cc);
                 load_rows<DK, 0, CH>(q_buf[PAR], q, r0, n, lane);
-                load_v(v_buf[PAR], v, r0, n, dv, j0, lane);
+                load_v<NSW>(v_buf[PAR], v, r0, n, dv, j0, lane);
             }
             if (cc + 1 >= 0 && cc + 1 < nchunks) load_ba(cc + 1, PAR ^ 1);
             wait_global();
@@ -575,7 +592,7 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
     }
 
     if constexpr (GATE) {
-        if (wave == 4 || wave == 5) {
+        if (wave == W_STAGE || wave == W_STAGE + 1) {
             // ---- stager waves (channel-wise gate): the gate-scaled k rows of chunk c+2 into the
             // k buffer and its gate-scaled k~ rows (passed in d) into the k~ buffer ------------
             const uint16_t *ktg = reinterpret_cast<const uint16_t *>(d);
@@ -600,13 +617,13 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                     }
                 }
             };
-            if (wave == 4) gstager(I0{});
+            if (wave == W_STAGE) gstager(I0{});
             else gstager(I1{});
             return;
         }
     }
 
-    if (wave == 4 || wave == 5) {
+    if (wave == W_STAGE || wave == W_STAGE + 1) {
         // ---- stager waves: k rows of chunk c+2 into LDS, then k~ = d (.) k of chunk c+2 -------
         // Stager h owns row blocks 2h, 2h+1.  d is loaded into registers one step before it is
         // used, block by block as soon as the block's registers are free (lane (q, n) holds
@@ -669,7 +686,7 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                 }
             }
         };
-        if (wave == 4) stager(I0{});
+        if (wave == W_STAGE) stager(I0{});
         else stager(I1{});
         return;
     }
@@ -865,16 +882,43 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
             for (int i = 0; i < PFN; ++i) asm volatile("" ::"v"(pfa[i]), "v"(pfb[i]));
         }
     };
-    if (wave == 2) prep_loop(I0{});
+    if (wave == W_PREP) prep_loop(I0{});
     else prep_loop(I1{});
+}
+
+// compute units of the current device (cached per device)
+int device_cus() {
+    static int cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cus[dev] = n;
+    }
+    return cus[dev];
 }
 
 template <int DK, typename TD>
 hipError_t launch_typed(const ChunkArgs &a, hipStream_t stream) {
-    const int nvt = a.dv / BV;
+    // Plain forward: where even 16-column slices (one state wave a workgroup) leave the grid
+    // within one workgroup per compute unit, take them: the per-chunk chain of a workgroup is
+    // no longer, and twice as many compute units walk the sequences (long sequences, few heads).
+    const bool narrow = !a.gcs && !a.ckpt && a.BH * (a.dv / VW) <= device_cus();
+    const int nvt = a.dv / (narrow ? VW : 2 * VW);
     const dim3 grid(static_cast<unsigned>(a.BH * nvt));
+    if (narrow) {
+        hipLaunchKernelGGL((chunk_mfma_kernel<DK, TD, false, false, true, 1>), grid,
+                           dim3(n_waves(1) * 64), 0, stream, static_cast<const uint16_t *>(a.q),
+                           static_cast<const uint16_t *>(a.k), static_cast<const uint16_t *>(a.v),
+                           static_cast<const TD *>(a.d), a.beta, a.alpha, a.S0,
+                           static_cast<uint16_t *>(a.o), a.S_T, a.BH, a.T, a.dv, a.gcs,
+                           static_cast<uint16_t *>(a.ckpt), static_cast<uint16_t *>(a.uout), a.planes);
+        return hipGetLastError();
+    }
 #define OSDN_CHUNK_LAUNCH(GATE, CKPT, OUT)                                                    \
-    hipLaunchKernelGGL((chunk_mfma_kernel<DK, TD, GATE, CKPT, OUT>), grid, dim3(NW * 64), 0,  \
+    hipLaunchKernelGGL((chunk_mfma_kernel<DK, TD, GATE, CKPT, OUT, 2>), grid,                 \
+                       dim3(n_waves(2) * 64), 0,                                              \
                        stream, static_cast<const uint16_t *>(a.q),                             \
                        static_cast<const uint16_t *>(a.k), static_cast<const uint16_t *>(a.v), \
                        static_cast<const TD *>(a.d), a.beta, a.alpha, a.S0,                    \

@@ -219,3 +219,37 @@ def test_outputs_stay_in_bounds(qkv):
     assert bool(torch.all(buf[n:] == 7.0)), "write past the end of o"
     o_ref, _ = oracle.chunk_fwd(*oracle_inputs(x))
     assert rel_err(to_np(o), o_ref) <= TOL[qkv]
+
+
+def _device_cus():
+    import torch
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+SLICE_CASES = [
+    # dk, dv, T, d dtype
+    (128, 128, 130, "f32"),
+    (64, 64, 70, "bf16"),
+    (128, 64, 64, "f32"),
+    (64, 128, 1, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", SLICE_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_value_slice_widths(case):
+    """The bf16 forward gives each workgroup a 16-column value slice (one state wave) when the
+    grid of such slices fits the device at one workgroup per compute unit, else a 32-column
+    slice (two state waves).  A batch with enough heads to need the 32-column form is checked
+    against the oracle; three of its heads run alone take the 16-column form and must give
+    the same bits (each 16-column tile does the same arithmetic in both)."""
+    dk, dv, T, dd = case
+    H = _device_cus() * 16 // dv + 1
+    x = synth.make_shape(1, H, T, dk, dv, qkv="bf16", alpha=True, s0=True, seed=T + 3 * dk)
+    check(x, "bf16", d_dtype=dd, label=f"{case} H={H} (32-column slices)")
+    o_all, S_all = gpu_chunk(x, qkv="bf16", d_dtype=dd)
+    idx = [0, 1, H - 1]
+    sub = {n: (a[:, idx] if a is not None and a.ndim >= 2 else a) for n, a in x.items()}
+    say("chunk_fwd", "heads", idx, "alone (16-column slices)")
+    o_sub, S_sub = gpu_chunk(sub, qkv="bf16", d_dtype=dd)
+    assert np.array_equal(o_sub, o_all[:, idx])
+    assert np.array_equal(S_sub, S_all[:, idx])
