@@ -1845,7 +1845,10 @@ bwd_chunk_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
 #pragma unroll
     for (int i = 0; i < FPT; ++i) frob[i] = 0.f;
     const int ic = ti * TC, jc = tj * TC;  // C x C block
-    const int ik = ti * TC, jk = tj * TK;  // C x DK block
+    // C x DK block: rows ik.., features tj + 16 nn (the 16 lanes of a row pair read 16
+    // consecutive features, so their LDS reads of a row are free of bank conflicts)
+    const int ik = ti * TC;
+    auto fk = [&](int nn) __attribute__((always_inline)) { return tj + 16 * nn; };
     const int is = ti * TC, js = tj * TV;  // C x BV block
 
     for (int s0 = 0; s0 < DV; s0 += BV) {
@@ -1911,11 +1914,11 @@ bwd_chunk_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
         auto bu = [&](int kk, int j) { return sU[j * PS + kk]; };
         mm<TC, TC, BV>(adP, ic, jc, [&](int i, int kk) { return sdO[i * PS + kk]; }, bu);
         mm<TC, TC, BV>(adA, ic, jc, [&](int i, int kk) { return sdR[i * PS + kk]; }, bu);
-        auto bm0t = [&](int kk, int f) { return sM0[f * PS + kk]; };
-        mm<TC, TK, BV>(aQ, ik, jk, [&](int i, int kk) { return sdO[i * PS + kk]; }, bm0t);
-        mm<TC, TK, BV>(aK, ik, jk, [&](int i, int kk) { return -sdR[i * PS + kk]; }, bm0t);
-        mm<TC, TK, BV>(aKt, ik, jk, [&](int i, int kk) { return sU[i * PS + kk]; },
-                       [&](int kk, int f) { return sdM[f * PS + kk]; });
+        auto bm0t = [&](int kk, int nn) { return sM0[fk(nn) * PS + kk]; };
+        mm<TC, TK, BV>(aQ, ik, 0, [&](int i, int kk) { return sdO[i * PS + kk]; }, bm0t);
+        mm<TC, TK, BV>(aK, ik, 0, [&](int i, int kk) { return -sdR[i * PS + kk]; }, bm0t);
+        mm<TC, TK, BV>(aKt, ik, 0, [&](int i, int kk) { return sU[i * PS + kk]; },
+                       [&](int kk, int nn) { return sdM[fk(nn) * PS + kk]; });
     }
     // G_L <dMC[f,:], M0[f,:]> per feature: the BV threads of one f are adjacent lanes
 #pragma unroll
@@ -1967,7 +1970,7 @@ bwd_chunk_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
         for (int m = 0; m < TC; ++m)
 #pragma unroll
             for (int nn = 0; nn < TK; ++nn) {
-                const int r = ik + m, f = jk + nn;
+                const int r = ik + m, f = fk(nn);
                 const double lg = sLg[r * PX + f], lgL = sLg[(C - 1) * PX + f];
                 const float g = __expf(static_cast<float>(lg));
                 aQ[m][nn] *= g;
@@ -1976,7 +1979,7 @@ bwd_chunk_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
                 colk[nn] += sKt[r * PX + f] * aKt[m][nn];
             }
 #pragma unroll
-        for (int nn = 0; nn < TK; ++nn) colpart[ti * DK + jk + nn] = colk[nn];
+        for (int nn = 0; nn < TK; ++nn) colpart[ti * DK + fk(nn)] = colk[nn];
     }
     __syncthreads();
     if (tid < DK) {
@@ -1991,14 +1994,14 @@ bwd_chunk_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
 #pragma unroll
         for (int m = 0; m < TC; ++m)
 #pragma unroll
-            for (int nn = 0; nn < TK; ++nn) lr[m][nn] = sLg[(ik + m) * PX + jk + nn];
+            for (int nn = 0; nn < TK; ++nn) lr[m][nn] = sLg[(ik + m) * PX + fk(nn)];
         for (int s = 0; s <= ik + TC - 1; ++s) {
             float kt[TK];
             double ls[TK];
 #pragma unroll
             for (int nn = 0; nn < TK; ++nn) {
-                kt[nn] = sKt[s * PX + jk + nn];
-                ls[nn] = sLg[s * PX + jk + nn];
+                kt[nn] = sKt[s * PX + fk(nn)];
+                ls[nn] = sLg[s * PX + fk(nn)];
             }
 #pragma unroll
             for (int m = 0; m < TC; ++m) {
@@ -2021,15 +2024,15 @@ bwd_chunk_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
 #pragma unroll
         for (int m = 0; m < TC; ++m)
 #pragma unroll
-            for (int nn = 0; nn < TK; ++nn) ls[m][nn] = sLg[(ik + m) * PX + jk + nn];
+            for (int nn = 0; nn < TK; ++nn) ls[m][nn] = sLg[(ik + m) * PX + fk(nn)];
         for (int r = ik; r < C; ++r) {
             float qv[TK], kv[TK];
             double lr[TK];
 #pragma unroll
             for (int nn = 0; nn < TK; ++nn) {
-                qv[nn] = sQ[r * PX + jk + nn];
-                kv[nn] = sK[r * PX + jk + nn];
-                lr[nn] = sLg[r * PX + jk + nn];
+                qv[nn] = sQ[r * PX + fk(nn)];
+                kv[nn] = sK[r * PX + fk(nn)];
+                lr[nn] = sLg[r * PX + fk(nn)];
             }
 #pragma unroll
             for (int m = 0; m < TC; ++m) {
@@ -2051,7 +2054,7 @@ bwd_chunk_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
         const int r = ik + m;
 #pragma unroll
         for (int nn = 0; nn < TK; ++nn) {
-            const int f = jk + nn;
+            const int f = fk(nn);
             const float qv = sQ[r * PX + f], kv = sK[r * PX + f], tv = sKt[r * PX + f];
             sKg[r * PX + f] = qv * aQ[m][nn] + kv * aK[m][nn] - tv * aKt[m][nn];
             if (r < n) {
