@@ -81,15 +81,30 @@ __device__ __forceinline__ void zero(float (&acc)[TM][TN]) {
         for (int n = 0; n < TN; ++n) acc[m][n] = 0.f;
 }
 
+// x summed over each aligned group of G lanes (G = 1, 2, 4, 8 or 16), every lane receiving its
+// group's sum, on DPP: the two quad swaps, then the half-row and row mirrors
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16, "lane group");
+    if constexpr (G >= 2) x = dpp_add<0xb1, 0xf>(x);   // quad_perm [1,0,3,2]
+    if constexpr (G >= 4) x = dpp_add<0x4e, 0xf>(x);   // quad_perm [2,3,0,1]
+    if constexpr (G >= 8) x = dpp_add<0x141, 0xf>(x);  // row_half_mirror
+    if constexpr (G >= 16) x = dpp_add<0x140, 0xf>(x); // row_mirror
+    return x;
+}
+
 // X[r][j] -= b_r sum_{s<r} AS[r][s] X[s][j] for every row r in order, columns j < NC, in place
 // (X = (I + A)^{-1} X with A = diag(b) AS).  Column j is owned by TPC adjacent lanes; lane sub
-// keeps rows s = i TPC + sub of it in registers.
+// keeps rows s = i TPC + sub of it in registers, and each row's sum is reduced across the TPC
+// lanes on DPP (a shuffle through LDS per reduction step measured several times slower).
 template <int C, int NC, int PX, int PA>
 __device__ __forceinline__ void solve_lower(float *X, const float *AS, const float *b, int tid) {
     constexpr int TPC = NT / NC, RPT = C / TPC;
-    static_assert(TPC * NC == NT && RPT * TPC == C && 64 % TPC == 0, "solve layout");
+    static_assert(TPC * NC == NT && RPT * TPC == C && TPC <= 16, "solve layout");
     const int j = tid / TPC, sub = tid % TPC;
-    float mine[RPT];
+    float rhs[C], mine[RPT];
+#pragma unroll
+    for (int r = 0; r < C; ++r) rhs[r] = X[r * PX + j];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) mine[i] = 0.f;
 #pragma unroll
@@ -102,9 +117,8 @@ __device__ __forceinline__ void solve_lower(float *X, const float *AS, const flo
                 if (s < r) part += AS[r * PA + s] * mine[i];
             }
         }
-#pragma unroll
-        for (int m = 1; m < TPC; m <<= 1) part += __shfl_xor(part, m);
-        const float val = X[r * PX + j] - b[r] * part;
+        part = group_sum<TPC>(part);
+        const float val = rhs[r] - b[r] * part;
         if (r % TPC == sub) mine[r / TPC] = val;
     }
 #pragma unroll
@@ -112,13 +126,15 @@ __device__ __forceinline__ void solve_lower(float *X, const float *AS, const flo
 }
 
 // X[r][j] -= sum_{s>r} b_s AS[s][r] X[s][j] for rows r = C-1 .. 0, in place
-// (X = (I + A)^{-T} X)
+// (X = (I + A)^{-T} X); the same layout
 template <int C, int NC, int PX, int PA>
 __device__ __forceinline__ void solve_upper(float *X, const float *AS, const float *b, int tid) {
     constexpr int TPC = NT / NC, RPT = C / TPC;
-    static_assert(TPC * NC == NT && RPT * TPC == C && 64 % TPC == 0, "solve layout");
+    static_assert(TPC * NC == NT && RPT * TPC == C && TPC <= 16, "solve layout");
     const int j = tid / TPC, sub = tid % TPC;
-    float mine[RPT];
+    float rhs[C], mine[RPT];
+#pragma unroll
+    for (int r = 0; r < C; ++r) rhs[r] = X[r * PX + j];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) mine[i] = 0.f;
 #pragma unroll
@@ -131,9 +147,8 @@ __device__ __forceinline__ void solve_upper(float *X, const float *AS, const flo
                 if (s > r) part += b[s] * AS[s * PA + r] * mine[i];
             }
         }
-#pragma unroll
-        for (int m = 1; m < TPC; m <<= 1) part += __shfl_xor(part, m);
-        const float val = X[r * PX + j] - part;
+        part = group_sum<TPC>(part);
+        const float val = rhs[r] - part;
         if (r % TPC == sub) mine[r / TPC] = val;
     }
 #pragma unroll
