@@ -81,18 +81,6 @@ __device__ __forceinline__ void zero(float (&acc)[TM][TN]) {
         for (int n = 0; n < TN; ++n) acc[m][n] = 0.f;
 }
 
-// x summed over each aligned group of G lanes (G = 1, 2, 4, 8 or 16), every lane receiving its
-// group's sum, on DPP: the two quad swaps, then the half-row and row mirrors
-template <int G>
-__device__ __forceinline__ float group_sum(float x) {
-    static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16, "lane group");
-    if constexpr (G >= 2) x = dpp_add<0xb1, 0xf>(x);   // quad_perm [1,0,3,2]
-    if constexpr (G >= 4) x = dpp_add<0x4e, 0xf>(x);   // quad_perm [2,3,0,1]
-    if constexpr (G >= 8) x = dpp_add<0x141, 0xf>(x);  // row_half_mirror
-    if constexpr (G >= 16) x = dpp_add<0x140, 0xf>(x); // row_mirror
-    return x;
-}
-
 // X[r][j] -= b_r sum_{s<r} AS[r][s] X[s][j] for every row r in order, columns j < NC, in place
 // (X = (I + A)^{-1} X with A = diag(b) AS).  Column j is owned by TPC adjacent lanes; lane sub
 // keeps rows s = i TPC + sub of it in registers, and each row's sum is reduced across the TPC

@@ -25,6 +25,7 @@
 //   M <- Diag(e^{Lg_C}) M + (K~ o e^{Lg_C - Lg})^T U.
 // A gate of 0 is taken as e^{-690}, which rounds every ratio across it to 0 in fp32.
 #include "osdn_internal.h"
+#include "osdn_mfma.h"
 
 namespace osdn {
 namespace {
@@ -38,7 +39,7 @@ constexpr int kThreads = 512;  // eight waves: two per SIMD, so one hides the ot
 template <int C, int NC, int PX, int PA>
 __device__ __forceinline__ void solve_unit_lower(float *X, const float *A, int tid) {
     constexpr int TPC = kThreads / NC, RPT = C / TPC;
-    static_assert(TPC * NC == kThreads && RPT * TPC == C && 64 % TPC == 0, "solve layout");
+    static_assert(TPC * NC == kThreads && RPT * TPC == C && TPC <= 16, "solve layout");
     const int j = tid / TPC, sub = tid % TPC;
     float mine[RPT];
 #pragma unroll
@@ -53,8 +54,7 @@ __device__ __forceinline__ void solve_unit_lower(float *X, const float *A, int t
                 if (s < r) part += A[r * PA + s] * mine[i];
             }
         }
-#pragma unroll
-        for (int m = 1; m < TPC; m <<= 1) part += __shfl_xor(part, m);
+        part = group_sum<TPC>(part);  // on DPP (an LDS shuffle per step measured far slower)
         const float val = X[r * PX + j] - part;
         if (r % TPC == sub) mine[r / TPC] = val;
     }

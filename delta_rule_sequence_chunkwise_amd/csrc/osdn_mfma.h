@@ -118,6 +118,18 @@ __device__ __forceinline__ float dpp_add(float x) {
     const int y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, false);
     return x + __int_as_float(y);
 }
+// x summed over each aligned group of G lanes (G = 1, 2, 4, 8 or 16), every lane receiving its
+// group's sum, on DPP: the two quad swaps, then the half-row and row mirrors
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16, "lane group");
+    if constexpr (G >= 2) x = dpp_add<0xb1, 0xf>(x);   // quad_perm [1,0,3,2]
+    if constexpr (G >= 4) x = dpp_add<0x4e, 0xf>(x);   // quad_perm [2,3,0,1]
+    if constexpr (G >= 8) x = dpp_add<0x141, 0xf>(x);  // row_half_mirror
+    if constexpr (G >= 16) x = dpp_add<0x140, 0xf>(x); // row_mirror
+    return x;
+}
+
 __device__ __forceinline__ float lane_value(float x, int l) {  // x of lane l (wave-uniform)
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
 }
