@@ -59,7 +59,7 @@ __device__ __forceinline__ void static_for(F &&f) {
 // acc[m][n] += sum_{kk < K} a(i0 + m, kk) * b(kk, j0 + n)
 template <int TM, int TN, int K, typename FA, typename FB>
 __device__ __forceinline__ void mm(float (&acc)[TM][TN], int i0, int j0, FA &&a, FB &&b) {
-#pragma unroll 2
+#pragma unroll 4
     for (int kk = 0; kk < K; ++kk) {
         float av[TM], bv[TN];
 #pragma unroll
@@ -1607,33 +1607,49 @@ hipError_t bwd_dims(const BwdArgs &a, hipStream_t stream) {
 // Every decay factor is e to a difference of running sums with the later row first, so at
 // most 1.  Rows past the end are zero with gate 1 (ln a = 0) and beta = 0.
 
-// Q, K, K~ = d (.) k in fp32 and ln a in double (zero rows, and ln a = 0, past the end); every
-// load is issued before the first is used
+// Q, K, K~ = d (.) k in fp32 and ln a in double (zero rows, and ln a = 0, past the end), in two
+// halves: the loads into registers (every one issued before any is used), then the LDS stores,
+// so that a caller can keep the loads in flight across other work
+template <int C, int DK>
+struct QkGateRegs {
+    static constexpr int IT = C * DK / NT;
+    static_assert(IT * NT == C * DK, "tile layout");
+    float q[IT], k[IT], d[IT], a[IT];
+};
+template <int C, int DK, typename TQ, typename TD>
+__device__ __forceinline__ void load_qk_regs(QkGateRegs<C, DK> &x, const TQ *q, const TQ *k,
+                                             const TD *d, const float *a, int64_t row0, int n,
+                                             int tid) {
+#pragma unroll
+    for (int it = 0; it < QkGateRegs<C, DK>::IT; ++it) {
+        const int idx = tid + it * NT, r = idx / DK, f = idx % DK;
+        const int64_t e = (row0 + (r < n ? r : 0)) * DK + f;
+        x.q[it] = to_f32(q[e]);
+        x.k[it] = to_f32(k[e]);
+        x.d[it] = to_f32(d[e]);
+        x.a[it] = a[e];
+    }
+}
+template <int C, int DK, int PX>
+__device__ __forceinline__ void store_qk_lds(const QkGateRegs<C, DK> &x, int n, float *sQ,
+                                             float *sK, float *sKt, double *sLg, int tid) {
+#pragma unroll
+    for (int it = 0; it < QkGateRegs<C, DK>::IT; ++it) {
+        const int idx = tid + it * NT, r = idx / DK, f = idx % DK;
+        const bool in = r < n;
+        sQ[r * PX + f] = in ? x.q[it] : 0.f;
+        sK[r * PX + f] = in ? x.k[it] : 0.f;
+        sKt[r * PX + f] = in ? x.d[it] * x.k[it] : 0.f;
+        sLg[r * PX + f] = in ? log(fmax(static_cast<double>(x.a[it]), 1e-300)) : 0.0;
+    }
+}
 template <int C, int DK, int PX, typename TQ, typename TD>
 __device__ __forceinline__ void load_qk_gate(const TQ *q, const TQ *k, const TD *d,
                                              const float *a, int64_t row0, int n, float *sQ,
                                              float *sK, float *sKt, double *sLg, int tid) {
-    constexpr int IT = C * DK / NT;
-    static_assert(IT * NT == C * DK, "tile layout");
-    float qv[IT], kv[IT], dv[IT], av[IT];
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        const int idx = tid + it * NT, r = idx / DK, f = idx % DK;
-        const int64_t e = (row0 + (r < n ? r : 0)) * DK + f;
-        qv[it] = to_f32(q[e]);
-        kv[it] = to_f32(k[e]);
-        dv[it] = to_f32(d[e]);
-        av[it] = a[e];
-    }
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        const int idx = tid + it * NT, r = idx / DK, f = idx % DK;
-        const bool in = r < n;
-        sQ[r * PX + f] = in ? qv[it] : 0.f;
-        sK[r * PX + f] = in ? kv[it] : 0.f;
-        sKt[r * PX + f] = in ? dv[it] * kv[it] : 0.f;
-        sLg[r * PX + f] = in ? log(fmax(static_cast<double>(av[it]), 1e-300)) : 0.0;
-    }
+    QkGateRegs<C, DK> x;
+    load_qk_regs<C, DK>(x, q, k, d, a, row0, n, tid);
+    store_qk_lds<C, DK, PX>(x, n, sQ, sK, sKt, sLg, tid);
 }
 
 // ln a -> its running sum down each feature column (the threads of the first DK lanes)
@@ -1658,6 +1674,7 @@ __device__ __forceinline__ void scores_gate(const float *sQ, const float *sK, co
     zero(ak);
     zero(aq);
     if (j0 <= i0 + TM - 1) {  // tiles wholly above the diagonal stay zero
+#pragma unroll 4
         for (int f = 0; f < DK; ++f) {
             float qv[TM], kv[TM], tv[TM];
             double lr[TM], ls[TM];
@@ -1717,25 +1734,45 @@ bwd_state_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
         const int f = idx / BV, j = idx % BV;
         sdM[f * PS + j] = dS_T ? dS_T[(bh * DK + f) * dv + j0 + j] : 0.f;
     }
+    // the next chunk's (c - 1's) inputs are loaded into registers while chunk c is processed; the
+    // barriers wait for LDS only (the kernel reads back none of its global writes), so those
+    // loads stay in flight across them
+    constexpr int OIT = C * BV / NT;
+    static_assert(OIT * NT == C * BV, "dO tile layout");
+    QkGateRegs<C, DK> nx;
+    float ndo[OIT];
+    auto issue = [&](int64_t cc) __attribute__((always_inline)) {
+        const int64_t r0 = bh * T + cc * C;
+        const int nn = static_cast<int>(T - cc * C < C ? T - cc * C : C);
+        load_qk_regs<C, DK>(nx, q, k, d, alpha_ch, r0, nn, tid);
+#pragma unroll
+        for (int it = 0; it < OIT; ++it) {
+            const int idx = tid + it * NT, r = idx / BV, j = idx % BV;
+            ndo[it] = to_f32(dO[(r0 + (r < nn ? r : 0)) * dv + j0 + j]);
+        }
+    };
+    if (nch > 0) issue(nch - 1);
     for (int64_t c = nch - 1; c >= 0; --c) {
         const int64_t c0 = c * C, row0 = bh * T + c0;
         const int n = static_cast<int>(T - c0 < C ? T - c0 : C);
-        __syncthreads();  // the previous chunk is done with every buffer
-        load_qk_gate<C, DK, PX>(q, k, d, alpha_ch, row0, n, sQ, sK, sKt, sLg, tid);
-        for (int idx = tid; idx < C * BV; idx += NT) {
-            const int r = idx / BV, j = idx % BV;
-            sdO[r * PS + j] = r < n ? to_f32(dO[(row0 + r) * dv + j0 + j]) : 0.f;
+        block_sync();  // the previous chunk is done with every buffer
+        store_qk_lds<C, DK, PX>(nx, n, sQ, sK, sKt, sLg, tid);
+#pragma unroll
+        for (int it = 0; it < OIT; ++it) {
+            const int idx = tid + it * NT, r = idx / BV, j = idx % BV;
+            sdO[r * PS + j] = r < n ? ndo[it] : 0.f;
         }
+        if (c > 0) issue(c - 1);
         if (tid < C) sb[tid] = tid < n ? beta[row0 + tid] : 0.f;
         for (int idx = tid; idx < DK * BV; idx += NT) {  // the gradient at this chunk's end
             const int f = idx / BV, j = idx % BV;
             dMck[((bh * nch + c) * DK + f) * dv + j0 + j] = sdM[f * PS + j];
         }
-        __syncthreads();
+        block_sync();
         gate_scan<C, DK, PX>(sLg, tid);
-        __syncthreads();
+        block_sync();
         scores_gate<C, DK, PX, PC>(sQ, sK, sKt, sLg, sAS, sP, tid);
-        __syncthreads();
+        block_sync();
         // in place: Q o G, K o G, K~ o W; and G_L
         for (int idx = tid; idx < C * DK; idx += NT) {
             const int r = idx / DK, f = idx % DK;
@@ -1746,7 +1783,7 @@ bwd_state_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
             sKt[r * PX + f] *= __expf(static_cast<float>(lgL - lg));
         }
         if (tid < DK) sGL[tid] = __expf(static_cast<float>(sLg[(C - 1) * PX + tid]));
-        __syncthreads();
+        block_sync();
         {  // dU = P^T dO + (K~ o W) dM
             constexpr int TM = C / 16, TN = BV / 16;
             const int i0 = (tid / 16) * TM, j0l = (tid % 16) * TN;
@@ -1761,9 +1798,9 @@ bwd_state_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
 #pragma unroll
                 for (int nn = 0; nn < TN; ++nn) sX[(i0 + m) * PS + j0l + nn] = acc[m][nn];
         }
-        __syncthreads();
+        block_sync();
         solve_upper<C, BV, PS, PC>(sX, sAS, sb, tid);  // dR
-        __syncthreads();
+        block_sync();
         {  // dM <- Diag(G_L) dM + (Q o G)^T dO - (K o G)^T diag(b) dR
             constexpr int TM = DK / 16, TN = BV / 16;
             const int i0 = (tid / 16) * TM, j0l = (tid % 16) * TN;
@@ -1782,7 +1819,7 @@ bwd_state_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
                 }
         }
     }
-    __syncthreads();
+    block_sync();
     if (dS0) {
         for (int idx = tid; idx < DK * BV; idx += NT) {
             const int f = idx / BV, j = idx % BV;
