@@ -672,6 +672,13 @@ int64_t bwd_gate_ckpt_bytes(int64_t B, int64_t H, int64_t T, int32_t dk, int32_t
     return round256(n);
 }
 
+// bytes of the channel-wise gate backward's score tiles AS and P of every chunk,
+// [BH, nchunks, 2, C, C] fp32 (valid sizes assumed: checked by bwd_gate_ckpt_bytes)
+int64_t bwd_gate_score_bytes(int64_t B, int64_t H, int64_t T) {
+    return round256(B * H * ((T + kGateBwdChunk - 1) / kGateBwdChunk) * 2 * kGateBwdChunk *
+                    kGateBwdChunk * 4);
+}
+
 }  // namespace
 
 extern "C" {
@@ -679,7 +686,7 @@ extern "C" {
 int64_t osdn_chunk_bwd_kda_workspace(int64_t B, int64_t H, int64_t T, int32_t dk, int32_t dv,
                                      osdn_dtype qkv) {
     const int64_t b = bwd_gate_ckpt_bytes(B, H, T, dk, dv, qkv);
-    return b < 0 ? -1 : 2 * b;
+    return b < 0 ? -1 : 2 * b + bwd_gate_score_bytes(B, H, T);
 }
 
 osdn_status osdn_chunk_bwd_kda(const void *q, const void *k, const void *v, const float *beta,
@@ -695,7 +702,7 @@ osdn_status osdn_chunk_bwd_kda(const void *q, const void *k, const void *v, cons
     if (!head_dim_ok(dk) || !head_dim_ok(dv)) return OSDN_ERR_UNSUPPORTED;
     const int64_t ck = bwd_gate_ckpt_bytes(B, H, T, dk, dv, qkv);
     if (ck < 0) return OSDN_ERR_SHAPE;
-    const int64_t wsb = 2 * ck;
+    const int64_t wsb = 2 * ck + bwd_gate_score_bytes(B, H, T);
     int64_t BH = 1;
     if (!mul_ok(BH, B, kMaxElems) || !mul_ok(BH, H, kMaxElems)) return OSDN_ERR_SHAPE;
     int64_t tok = BH, st = BH;
@@ -755,6 +762,7 @@ osdn_status osdn_chunk_bwd_kda(const void *q, const void *k, const void *v, cons
                     nullptr, nullptr, nullptr, BH, T, dk, dv, qkv, d_dtype};
     a.alpha_ch = alpha_ch;
     a.galpha_ch = grad_alpha_ch;
+    a.scores = T > 0 ? reinterpret_cast<float *>(ws + 2 * ck) : nullptr;
     const hipError_t err = osdn::launch_chunk_bwd_gate(a, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? OSDN_OK : OSDN_ERR_LAUNCH;
 }

@@ -1708,6 +1708,36 @@ __device__ __forceinline__ void scores_gate(const float *sQ, const float *sK, co
         }
 }
 
+// The score tiles AS and P of every 32-row chunk with the channel-wise gate, one workgroup per
+// (sequence, chunk), into [BH, nchunks, 2, C, C] fp32: they depend on q, k, d and the gate
+// only, so the reverse pass (in each of its value slices) and the per-chunk pass load them.
+template <int C, int DK, typename TQ, typename TD>
+__global__ void __launch_bounds__(NT)
+bwd_scores_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
+                       const TD *__restrict__ d, const float *__restrict__ alpha_ch,
+                       float *__restrict__ scores, int64_t T, int64_t nch) {
+    constexpr int PX = DK + 1, PC = C + 1;
+    __shared__ float sQ[C * PX], sK[C * PX], sKt[C * PX];
+    __shared__ double sLg[C * PX];
+    __shared__ float sAS[C * PC], sP[C * PC];
+    const int64_t bh = blockIdx.x / nch, c = blockIdx.x % nch;
+    const int64_t c0 = c * C, row0 = bh * T + c0;
+    const int n = static_cast<int>(T - c0 < C ? T - c0 : C);
+    const int tid = threadIdx.x;
+    load_qk_gate<C, DK, PX>(q, k, d, alpha_ch, row0, n, sQ, sK, sKt, sLg, tid);
+    __syncthreads();
+    gate_scan<C, DK, PX>(sLg, tid);
+    __syncthreads();
+    scores_gate<C, DK, PX, PC>(sQ, sK, sKt, sLg, sAS, sP, tid);
+    __syncthreads();
+    float *dst = scores + (bh * nch + c) * 2 * C * C;
+    for (int idx = tid; idx < C * C; idx += NT) {
+        const int i = idx / C, j = idx % C;
+        dst[idx] = sAS[i * PC + j];
+        dst[C * C + idx] = sP[i * PC + j];
+    }
+}
+
 // Reverse pass over chunks with the channel-wise gate: one workgroup per (sequence, BV-wide
 // value slice), dM[:, slice] in LDS; dMck[c] gets the gradient at the end of chunk c.
 template <int C, int DK, int BV, typename TQ, typename TD>
@@ -1715,8 +1745,8 @@ __global__ void __launch_bounds__(NT)
 bwd_state_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
                       const TD *__restrict__ d, const float *__restrict__ beta,
                       const float *__restrict__ alpha_ch, const TQ *__restrict__ dO,
-                      const float *__restrict__ dS_T, float *__restrict__ dMck,
-                      float *__restrict__ dS0, int64_t T, int dv) {
+                      const float *__restrict__ dS_T, const float *__restrict__ scores,
+                      float *__restrict__ dMck, float *__restrict__ dS0, int64_t T, int dv) {
     constexpr int PX = DK + 1, PC = C + 1, PS = BV + 1;
     __shared__ float sQ[C * PX], sK[C * PX], sKt[C * PX];
     __shared__ double sLg[C * PX];
@@ -1739,11 +1769,19 @@ bwd_state_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
     // loads stay in flight across them
     constexpr int OIT = C * BV / NT;
     static_assert(OIT * NT == C * BV, "dO tile layout");
+    constexpr int SIT = C * C / NT;  // score-tile elements per thread
+    static_assert(SIT * NT == C * C, "score tile layout");
     QkGateRegs<C, DK> nx;
-    float ndo[OIT];
+    float ndo[OIT], nas[SIT], np[SIT];
     auto issue = [&](int64_t cc) __attribute__((always_inline)) {
         const int64_t r0 = bh * T + cc * C;
         const int nn = static_cast<int>(T - cc * C < C ? T - cc * C : C);
+        const float *sc = scores + (bh * nch + cc) * 2 * C * C;
+#pragma unroll
+        for (int it = 0; it < SIT; ++it) {
+            nas[it] = sc[tid + it * NT];
+            np[it] = sc[C * C + tid + it * NT];
+        }
         load_qk_regs<C, DK>(nx, q, k, d, alpha_ch, r0, nn, tid);
 #pragma unroll
         for (int it = 0; it < OIT; ++it) {
@@ -1762,6 +1800,12 @@ bwd_state_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
             const int idx = tid + it * NT, r = idx / BV, j = idx % BV;
             sdO[r * PS + j] = r < n ? ndo[it] : 0.f;
         }
+#pragma unroll
+        for (int it = 0; it < SIT; ++it) {
+            const int idx = tid + it * NT, i = idx / C, j = idx % C;
+            sAS[i * PC + j] = nas[it];
+            sP[i * PC + j] = np[it];
+        }
         if (c > 0) issue(c - 1);
         if (tid < C) sb[tid] = tid < n ? beta[row0 + tid] : 0.f;
         for (int idx = tid; idx < DK * BV; idx += NT) {  // the gradient at this chunk's end
@@ -1770,8 +1814,6 @@ bwd_state_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
         }
         block_sync();
         gate_scan<C, DK, PX>(sLg, tid);
-        block_sync();
-        scores_gate<C, DK, PX, PC>(sQ, sK, sKt, sLg, sAS, sP, tid);
         block_sync();
         // in place: Q o G, K o G, K~ o W; and G_L
         for (int idx = tid; idx < C * DK; idx += NT) {
@@ -1836,7 +1878,8 @@ bwd_chunk_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
                       const TQ *__restrict__ v, const TD *__restrict__ d,
                       const float *__restrict__ beta, const float *__restrict__ alpha_ch,
                       const TQ *__restrict__ dO, const float *__restrict__ Mck,
-                      const float *__restrict__ dMck, TQ *__restrict__ gq, TQ *__restrict__ gk,
+                      const float *__restrict__ dMck, const float *__restrict__ scores,
+                      TQ *__restrict__ gq, TQ *__restrict__ gk,
                       TQ *__restrict__ gv, float *__restrict__ gbeta, TD *__restrict__ gd,
                       float *__restrict__ galpha_ch, int64_t T, int64_t nch) {
     constexpr int PX = DK + 1, PC = C + 1, PS = BV + 1;
@@ -1859,7 +1902,25 @@ bwd_chunk_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
     const float *M0 = Mck + (bh * nch + c) * DK * DV;
     const float *dMC = dMck + (bh * nch + c) * DK * DV;
 
+    // the chunk's score tiles (from the score-tile kernel), loads issued first
+    constexpr int SIT = C * C / NT;
+    static_assert(SIT * NT == C * C, "score tile layout");
+    float tas[SIT], tp[SIT];
+    {
+        const float *sc = scores + (bh * nch + c) * 2 * C * C;
+#pragma unroll
+        for (int it = 0; it < SIT; ++it) {
+            tas[it] = sc[tid + it * NT];
+            tp[it] = sc[C * C + tid + it * NT];
+        }
+    }
     load_qk_gate<C, DK, PX>(q, k, d, alpha_ch, row0, n, sQ, sK, sKt, sLg, tid);
+#pragma unroll
+    for (int it = 0; it < SIT; ++it) {
+        const int idx = tid + it * NT, i = idx / C, j = idx % C;
+        sAS[i * PC + j] = tas[it];
+        sP[i * PC + j] = tp[it];
+    }
     if (tid < C) {
         sb[tid] = tid < n ? beta[row0 + tid] : 0.f;
         sdb[tid] = 0.f;
@@ -1867,7 +1928,6 @@ bwd_chunk_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
     __syncthreads();
     gate_scan<C, DK, PX>(sLg, tid);
     __syncthreads();
-    scores_gate<C, DK, PX, PC>(sQ, sK, sKt, sLg, sAS, sP, tid);
     for (int idx = tid; idx < C * DK; idx += NT) {
         const int r = idx / DK, f = idx % DK;
         const double lg = sLg[r * PX + f], lgL = sLg[(C - 1) * PX + f];
@@ -2132,12 +2192,20 @@ hipError_t bwd_gate_typed(const BwdArgs &a, hipStream_t stream) {
         if (e != hipSuccess) return e;
     }
     constexpr int BVA = 32, BVB = 16;
+    if (nch > 0) {
+        hipLaunchKernelGGL((bwd_scores_gate_kernel<C, DK, TQ, TD>),
+                           dim3(static_cast<unsigned>(a.BH * nch)), dim3(NT), 0, stream,
+                           static_cast<const TQ *>(a.q), static_cast<const TQ *>(a.k),
+                           static_cast<const TD *>(a.d), a.alpha_ch, a.scores, a.T, nch);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL((bwd_state_gate_kernel<C, DK, BVA, TQ, TD>),
                        dim3(static_cast<unsigned>(a.BH * (DV / BVA))), dim3(NT), 0, stream,
                        static_cast<const TQ *>(a.q), static_cast<const TQ *>(a.k),
                        static_cast<const TD *>(a.d), a.beta, a.alpha_ch,
-                       static_cast<const TQ *>(a.dO), a.dS_T, static_cast<float *>(a.dMck), a.dS0,
-                       a.T, DV);
+                       static_cast<const TQ *>(a.dO), a.dS_T, a.scores,
+                       static_cast<float *>(a.dMck), a.dS0, a.T, DV);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || nch == 0) return e;
     hipLaunchKernelGGL((bwd_chunk_gate_kernel<C, DK, DV, BVB, TQ, TD>),
@@ -2146,8 +2214,9 @@ hipError_t bwd_gate_typed(const BwdArgs &a, hipStream_t stream) {
                        static_cast<const TQ *>(a.v), static_cast<const TD *>(a.d), a.beta,
                        a.alpha_ch, static_cast<const TQ *>(a.dO),
                        static_cast<const float *>(a.Mck), static_cast<const float *>(a.dMck),
-                       static_cast<TQ *>(a.gq), static_cast<TQ *>(a.gk), static_cast<TQ *>(a.gv),
-                       a.gbeta, static_cast<TD *>(a.gd), a.galpha_ch, a.T, nch);
+                       a.scores, static_cast<TQ *>(a.gq), static_cast<TQ *>(a.gk),
+                       static_cast<TQ *>(a.gv), a.gbeta, static_cast<TD *>(a.gd), a.galpha_ch,
+                       a.T, nch);
     return hipGetLastError();
 }
 

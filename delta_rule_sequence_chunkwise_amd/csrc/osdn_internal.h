@@ -90,6 +90,8 @@ struct BwdArgs {
     osdn_dtype qkv, d_dtype;
     const float *alpha_ch = nullptr;  // the channel-wise gate [BH, T, dk] (its own backward)
     float *galpha_ch = nullptr;       // its gradient, [BH, T, dk] fp32 (NULL: not written)
+    float *scores = nullptr;          // channel-wise gate: workspace for the score tiles AS and P
+                                      // of every chunk, [BH, nchunks, 2, C, C] fp32
 };
 
 // The channel-wise gate's planes of one 64-row chunk (bf16 inputs): the chunk's score matrix P
@@ -149,7 +151,7 @@ hipError_t launch_kda_planes(const KdaPrepArgs &a, hipStream_t stream);
 hipError_t launch_step_kda(const StepArgs &a, hipStream_t stream);  // alpha: [BH, dk]
 hipError_t launch_chunk_bwd(const BwdArgs &a, hipStream_t stream);
 // the backward with the channel-wise gate (alpha_ch set, alpha NULL): fp32 arithmetic, 32-row
-// chunks, Mck and dMck fp32 [BH, nchunks, dk, dv] each, Tck/Uck/dRck unused
+// chunks, Mck and dMck fp32 [BH, nchunks, dk, dv] each, scores as above, Tck/Uck/dRck unused
 hipError_t launch_chunk_bwd_gate(const BwdArgs &a, hipStream_t stream);
 int32_t bwd_chunk_size(osdn_dtype qkv);  // rows per chunk of the backward
 
