@@ -2183,23 +2183,22 @@ template <int DK, int DV, typename TQ, typename TD>
 hipError_t bwd_gate_typed(const BwdArgs &a, hipStream_t stream) {
     constexpr int C = 32;
     const int64_t nch = (a.T + C - 1) / C;
-    if (nch > 0) {
-        ChunkArgs f{a.q, a.k, a.v, a.d, a.beta, nullptr, a.S0, nullptr, nullptr, a.BH, a.T, DK,
-                    DV, C, a.qkv, a.d_dtype};
-        f.alpha_ch = a.alpha_ch;
-        f.ckpt = a.Mck;
-        const hipError_t e = launch_chunk_fwd_f32math(f, stream);
-        if (e != hipSuccess) return e;
-    }
-    constexpr int BVA = 32, BVB = 16;
-    if (nch > 0) {
+    if (nch > 0) {  // the score tiles of every chunk, then the forward, which takes them
         hipLaunchKernelGGL((bwd_scores_gate_kernel<C, DK, TQ, TD>),
                            dim3(static_cast<unsigned>(a.BH * nch)), dim3(NT), 0, stream,
                            static_cast<const TQ *>(a.q), static_cast<const TQ *>(a.k),
                            static_cast<const TD *>(a.d), a.alpha_ch, a.scores, a.T, nch);
-        const hipError_t e = hipGetLastError();
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        ChunkArgs f{a.q, a.k, a.v, a.d, a.beta, nullptr, a.S0, nullptr, nullptr, a.BH, a.T, DK,
+                    DV, C, a.qkv, a.d_dtype};
+        f.alpha_ch = a.alpha_ch;
+        f.ckpt = a.Mck;
+        f.gate_scores = a.scores;
+        e = launch_chunk_fwd_f32math(f, stream);
         if (e != hipSuccess) return e;
     }
+    constexpr int BVA = 32, BVB = 16;
     hipLaunchKernelGGL((bwd_state_gate_kernel<C, DK, BVA, TQ, TD>),
                        dim3(static_cast<unsigned>(a.BH * (DV / BVA))), dim3(NT), 0, stream,
                        static_cast<const TQ *>(a.q), static_cast<const TQ *>(a.k),

@@ -86,7 +86,7 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
                      const TQ *__restrict__ v, const TD *__restrict__ d,
                      const float *__restrict__ beta, const float *__restrict__ alpha,
                      const float *S0, TQ *__restrict__ o, float *S_T, int64_t T, int dv,
-                     float *__restrict__ ckpt) {
+                     float *__restrict__ ckpt, const float *__restrict__ gscores) {
     constexpr int PX = DK + 1;  // padded row pitches (bank-conflict relief)
     constexpr int PC = CH + 1;
     constexpr int PV = BV + 1;
@@ -197,7 +197,14 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
             // a2, a5 in one pass, the decay of each (row, column, feature) formed once and used
             // for both: thread (r, s0) owns columns s0, s0 + 1 of row r
             static_assert(CH * CH / 2 <= kThreads, "gate scores layout");
-            if (tid < CH * CH / 2) {
+            if (gscores) {  // formed already (the backward's score tiles): A = diag(beta) AS, P
+                const float *sc = gscores + (bh * ((T + CH - 1) / CH) + c0 / CH) * 2 * CH * CH;
+                for (int idx = tid; idx < CH * CH; idx += kThreads) {
+                    const int r = idx / CH, s = idx % CH;
+                    sA[r * PC + s] = sb[r] * sc[idx];
+                    sP[r * PC + s] = sc[CH * CH + idx];
+                }
+            } else if (tid < CH * CH / 2) {
                 const int r = tid / (CH / 2), s0 = (tid % (CH / 2)) * 2;
                 float ak0 = 0.f, ak1 = 0.f, aq0 = 0.f, aq1 = 0.f;
                 if (s0 <= r) {
@@ -387,17 +394,19 @@ hipError_t launch_typed(const ChunkArgs &a, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(a.BH * ntiles));
     if (a.alpha_ch) {  // the per-feature log sums need LDS: at most 32 rows per chunk
         constexpr int CG = CH < 32 ? CH : 32;
+        if (a.gate_scores && CG != 32) return hipErrorInvalidValue;  // tiles are 32 x 32
         hipLaunchKernelGGL((chunk_f32math_kernel<DK, BV, CG, TQ, TD, true>), grid, dim3(kThreads),
                            0, stream, static_cast<const TQ *>(a.q), static_cast<const TQ *>(a.k),
                            static_cast<const TQ *>(a.v), static_cast<const TD *>(a.d), a.beta,
                            a.alpha_ch, a.S0, static_cast<TQ *>(a.o), a.S_T, a.T, a.dv,
-                           static_cast<float *>(a.ckpt));
+                           static_cast<float *>(a.ckpt), a.gate_scores);
     } else {
         hipLaunchKernelGGL((chunk_f32math_kernel<DK, BV, CH, TQ, TD, false>), grid,
                            dim3(kThreads), 0, stream, static_cast<const TQ *>(a.q),
                            static_cast<const TQ *>(a.k), static_cast<const TQ *>(a.v),
                            static_cast<const TD *>(a.d), a.beta, a.alpha, a.S0,
-                           static_cast<TQ *>(a.o), a.S_T, a.T, a.dv, static_cast<float *>(a.ckpt));
+                           static_cast<TQ *>(a.o), a.S_T, a.T, a.dv, static_cast<float *>(a.ckpt),
+                           nullptr);
     }
     return hipGetLastError();
 }

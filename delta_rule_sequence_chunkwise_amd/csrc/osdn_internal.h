@@ -64,6 +64,10 @@ struct ChunkArgs {
                                  // matrix-core forward (o may then be NULL: not written)
     void *uout = nullptr;        // with ckpt, matrix-core forward: [BH, T, dv] bf16, the
                                  // pseudo-values U of every row (NULL: not written)
+    const float *gate_scores = nullptr;  // fp32 forward with the channel-wise gate, 32-row
+                                         // chunks: the score tiles AS, P of every chunk as the
+                                         // backward forms them, [BH, nchunks, 2, 32, 32]
+                                         // (NULL: formed in the kernel)
 };
 
 struct BwdArgs {
