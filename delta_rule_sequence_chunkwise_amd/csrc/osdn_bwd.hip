@@ -56,10 +56,11 @@ __device__ __forceinline__ void static_for(F &&f) {
     }
 }
 
-// acc[m][n] += sum_{kk < K} a(i0 + m, kk) * b(kk, j0 + n)
+// acc[m][n] += sum_{kk < K} a(i0 + m, kk) * b(kk, j0 + n), unrolled deep: these kernels run one
+// wave per SIMD, so only a wave's own independent reads hide the LDS latency
 template <int TM, int TN, int K, typename FA, typename FB>
 __device__ __forceinline__ void mm(float (&acc)[TM][TN], int i0, int j0, FA &&a, FB &&b) {
-#pragma unroll 4
+#pragma unroll 16
     for (int kk = 0; kk < K; ++kk) {
         float av[TM], bv[TN];
 #pragma unroll
