@@ -129,10 +129,60 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
         sM[i * PV + j] = S0 ? S0[(bh * DK + i) * dv + j0 + j] : 0.f;
     }
 
+    // The next chunk's k, d, v, beta (and q and the gate with GATE; the scalar decay without)
+    // are loaded into registers while the current chunk is processed.  The barriers wait for
+    // LDS only (the kernel reads back none of its global writes), so those loads stay in flight
+    // across them.  Rows past the end re-read the chunk's last row and are zeroed on the way in.
+    // Score tiles given (GATE): the next chunk's AS and P come with them.
+    constexpr int LIT = CH * DK / kThreads, VIT = CH * BV / kThreads;
+    constexpr int SIT = (CH * CH + kThreads - 1) / kThreads;
+    static_assert(LIT * kThreads == CH * DK && VIT * kThreads == CH * BV, "prefetch layout");
+    float nk[LIT], nd[LIT], nq[GATE ? LIT : 1], na[GATE ? LIT : 1], nv[VIT], nb = 0.f, nal = 0.f;
+    float nsa[GATE ? SIT : 1], nsp[GATE ? SIT : 1];
+    const int64_t nchunks = (T + CH - 1) / CH;
+    auto issue = [&](int64_t cn) __attribute__((always_inline)) {
+        const int nn = static_cast<int>(T - cn < CH ? T - cn : CH);
+        const int64_t r0 = bh * T + cn;
+        if constexpr (GATE) {
+            if (gscores) {
+                const float *sc = gscores + (bh * nchunks + cn / CH) * 2 * CH * CH;
+#pragma unroll
+                for (int it = 0; it < SIT; ++it) {
+                    const int idx = tid + it * kThreads;
+                    if (idx < CH * CH) {
+                        nsa[it] = sc[idx];
+                        nsp[it] = sc[CH * CH + idx];
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < LIT; ++it) {
+            const int idx = tid + it * kThreads, r = idx / DK, i = idx % DK;
+            const int64_t e = (r0 + (r < nn ? r : nn - 1)) * DK + i;
+            nk[it] = to_f32(k[e]);
+            nd[it] = to_f32(d[e]);
+            if constexpr (GATE) {
+                nq[it] = to_f32(q[e]);
+                na[it] = alpha[e];
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < VIT; ++it) {
+            const int idx = tid + it * kThreads, r = idx / BV, j = idx % BV;
+            nv[it] = to_f32(v[(r0 + (r < nn ? r : nn - 1)) * dv + j0 + j]);
+        }
+        if (tid < nn) {
+            nb = beta[r0 + tid];
+            if (!GATE && alpha) nal = alpha[r0 + tid];
+        }
+    };
+    if (T > 0) issue(0);
+
     for (int64_t c0 = 0; c0 < T; c0 += CH) {
         const int n = static_cast<int>(T - c0 < CH ? T - c0 : CH);
         const int64_t row0 = bh * T + c0;
-        __syncthreads();  // the previous chunk is done with every buffer
+        block_sync();  // the previous chunk is done with every buffer
         if (ckpt) {  // the state at this chunk's start, for the backward
             const int64_t cc = bh * ((T + CH - 1) / CH) + c0 / CH;
             for (int idx = tid; idx < DK * BV; idx += kThreads) {
@@ -141,33 +191,42 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
             }
         }
 
-        // a1: keys, scaled keys, values, gates
-        for (int idx = tid; idx < CH * DK; idx += kThreads) {
-            const int r = idx / DK, i = idx % DK;
-            float kv = 0.f, dd = 0.f;
-            if (r < n) {
-                kv = to_f32(k[(row0 + r) * DK + i]);
-                dd = to_f32(d[(row0 + r) * DK + i]);
+        // a1: keys, scaled keys, values, gates (from the registers loaded a step ago)
+#pragma unroll
+        for (int it = 0; it < LIT; ++it) {
+            const int idx = tid + it * kThreads, r = idx / DK, i = idx % DK;
+            const bool in = r < n;
+            sX[r * PX + i] = in ? nk[it] : 0.f;
+            sKt[r * PX + i] = in ? nd[it] * nk[it] : 0.f;
+            if constexpr (GATE) {
+                sQ[r * PX + i] = in ? nq[it] : 0.f;
+                sLg[r * PX + i] = in ? log(fmax(static_cast<double>(na[it]), 1e-300)) : 0.0;
             }
-            sX[r * PX + i] = kv;
-            sKt[r * PX + i] = dd * kv;
-            if constexpr (GATE) sQ[r * PX + i] = r < n ? to_f32(q[(row0 + r) * DK + i]) : 0.f;
         }
-        for (int idx = tid; idx < CH * BV; idx += kThreads) {
-            const int r = idx / BV, j = idx % BV;
-            sR[r * PV + j] = r < n ? to_f32(v[(row0 + r) * dv + j0 + j]) : 0.f;
+#pragma unroll
+        for (int it = 0; it < VIT; ++it) {
+            const int idx = tid + it * kThreads, r = idx / BV, j = idx % BV;
+            sR[r * PV + j] = r < n ? nv[it] : 0.f;
         }
         if (tid < CH) {
-            sb[tid] = tid < n ? beta[row0 + tid] : 0.f;
-            sg[tid] = (tid < n && alpha && !GATE) ? logf(alpha[row0 + tid]) : 0.f;
+            sb[tid] = tid < n ? nb : 0.f;
+            sg[tid] = (tid < n && alpha && !GATE) ? logf(nal) : 0.f;
         }
         if constexpr (GATE) {
-            for (int idx = tid; idx < CH * DK; idx += kThreads) {
-                const int r = idx / DK, i = idx % DK;
-                sLg[r * PX + i] =
-                    r < n ? log(fmax(static_cast<double>(alpha[(row0 + r) * DK + i]), 1e-300)) : 0.0;
+            if (gscores) {  // AS into sA (scaled by beta below), P into sP
+#pragma unroll
+                for (int it = 0; it < SIT; ++it) {
+                    const int idx = tid + it * kThreads, r = idx / CH, s_ = idx % CH;
+                    if (idx < CH * CH) {
+                        sA[r * PC + s_] = nsa[it];
+                        sP[r * PC + s_] = nsp[it];
+                    }
+                }
             }
-            __syncthreads();
+        }
+        if (c0 + CH < T) issue(c0 + CH);
+        if constexpr (GATE) {
+            block_sync();
             if (tid < DK) {  // running sums down each feature column
                 double acc = 0.0;
                 for (int r = 0; r < CH; ++r) {
@@ -176,7 +235,7 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
                 }
             }
         }
-        __syncthreads();
+        block_sync();
         if (tid < 64) {  // running sum of ln(alpha) by a scan over wave 0's lanes
             float acc = tid < CH ? sg[tid] : 0.f;
 #pragma unroll
@@ -191,18 +250,16 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
                 sdec[tid] = __expf(last - acc);
             }
         }
-        __syncthreads();
+        block_sync();
 
         if constexpr (GATE) {
             // a2, a5 in one pass, the decay of each (row, column, feature) formed once and used
             // for both: thread (r, s0) owns columns s0, s0 + 1 of row r
             static_assert(CH * CH / 2 <= kThreads, "gate scores layout");
-            if (gscores) {  // formed already (the backward's score tiles): A = diag(beta) AS, P
-                const float *sc = gscores + (bh * ((T + CH - 1) / CH) + c0 / CH) * 2 * CH * CH;
+            if (gscores) {  // formed already (the backward's score tiles): A = diag(beta) AS
                 for (int idx = tid; idx < CH * CH; idx += kThreads) {
-                    const int r = idx / CH, s = idx % CH;
-                    sA[r * PC + s] = sb[r] * sc[idx];
-                    sP[r * PC + s] = sc[CH * CH + idx];
+                    const int r = idx / CH, s_ = idx % CH;
+                    sA[r * PC + s_] *= sb[r];
                 }
             } else if (tid < CH * CH / 2) {
                 const int r = tid / (CH / 2), s0 = (tid % (CH / 2)) * 2;
@@ -229,7 +286,7 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
                 sP[r * PC + s0] = s0 <= r ? aq0 : 0.f;
                 sP[r * PC + s0 + 1] = s0 + 1 <= r ? aq1 : 0.f;
             }
-            __syncthreads();
+            block_sync();
             // in place, once per element: K o G, Q o G, K~ o e^{Lg_C - Lg}
             for (int idx = tid; idx < CH * DK; idx += kThreads) {
                 const int r = idx / DK, i = idx % DK;
@@ -239,7 +296,7 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
                 sQ[r * PX + i] *= g;
                 sKt[r * PX + i] *= __expf(static_cast<float>(sLg[(CH - 1) * PX + i] - lg));
             }
-            __syncthreads();
+            block_sync();
             // a3: R = diag(beta) (V - (K o G) M)
             if (rows_ok) {
                 float km[TR][2];
@@ -254,10 +311,10 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
                         sR[r * PV + j] = sb[r] * (sR[r * PV + j] - km[m][nn]);
                     }
             }
-            __syncthreads();
+            block_sync();
             // a4: U = (I + A)^{-1} R in place
             solve_unit_lower<CH, BV, PV, PC>(sR, sA, tid);
-            __syncthreads();
+            block_sync();
             // (Q o G) M for the inter-chunk read-out
             if (rows_ok) {
                 float qm[TR][2];
@@ -269,7 +326,7 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
 #pragma unroll
                     for (int nn = 0; nn < 2; ++nn) sQM[(ir + m) * PV + 2 * tx + nn] = qm[m][nn];
             }
-            __syncthreads();
+            block_sync();
         } else {
             // a2: strictly lower Gram matrix of (K, K~), decayed (tiles above the diagonal
             // stay zero); a3: R = diag(beta) (V - diag(e^g) K M)
@@ -299,7 +356,7 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
                         sR[r * PV + j] = sb[r] * (sR[r * PV + j] - sgam[r] * km[m][nn]);
                     }
             }
-            __syncthreads();
+            block_sync();
 
             // a4: U = (I + A)^{-1} R in place; then stage Q over K (K is no longer read)
             solve_unit_lower<CH, BV, PV, PC>(sR, sA, tid);
@@ -307,7 +364,7 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
                 const int r = idx / DK, i = idx % DK;
                 sX[r * PX + i] = r < n ? to_f32(q[(row0 + r) * DK + i]) : 0.f;
             }
-            __syncthreads();
+            block_sync();
 
             // a5: P = lower-inclusive (Q K~^T) with decay;  Q M for the inter-chunk read-out
             if (rows_ok) {
@@ -333,7 +390,7 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
 #pragma unroll
                     for (int nn = 0; nn < 2; ++nn) sQM[(ir + m) * PV + 2 * tx + nn] = qm[m][nn];
             }
-            __syncthreads();
+            block_sync();
         }
         // a6: outputs of this chunk (P is zero above the diagonal) and the state carried to
         // the next one
@@ -378,7 +435,7 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
                 }
         }
     }
-    __syncthreads();
+    block_sync();
     if (S_T) {
         for (int idx = tid; idx < DK * BV; idx += kThreads) {
             const int i = idx / BV, j = idx % BV;
