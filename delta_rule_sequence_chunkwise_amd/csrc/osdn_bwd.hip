@@ -254,8 +254,7 @@ __device__ __forceinline__ void block_inverse64(float *sT, const float *sAS, con
                     if (s2 < r) part += sAS[(rb + r) * PC + rb + s2] * mine[i];
                 }
             }
-            part += __shfl_xor(part, 1);
-            part += __shfl_xor(part, 2);
+            part = group_sum<4>(part);  // the four lanes of the column, on DPP
             const float val = (r == jj ? 1.f : 0.f) - sb[rb + r] * part;
             if (r % 4 == sub) mine[r / 4] = val;
         }
