@@ -722,16 +722,16 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
     SliceRegs ra{}, rb{};
     auto load_slice = [&](SliceRegs &x, int S0, int64_t cc, int64_t r0, int nn)
         __attribute__((always_inline)) {
-        const uint16_t *M0 = Mck + cc * DK * DV, *dMC = dMck + cc * DK * DV;  // bf16
+        const uint16_t *M0 = Mck + cc * DK * DV, *dMC = dMck + cc * DK * DV;  // bf16, by ckpt_at
         {
             const int f = tid / (BV / 4), j = 4 * (tid % (BV / 4));
-            x.m0a = *reinterpret_cast<const uint2 *>(M0 + f * DV + S0 + j);
-            x.dma = *reinterpret_cast<const uint2 *>(dMC + f * DV + S0 + j);
+            x.m0a = *reinterpret_cast<const uint2 *>(M0 + ckpt_at(f, S0 + j, DK));
+            x.dma = *reinterpret_cast<const uint2 *>(dMC + ckpt_at(f, S0 + j, DK));
         }
         if constexpr (MU == 2) {
             const int u = tid + NTH, f = u / (BV / 4), j = 4 * (u % (BV / 4));
-            x.m0b = *reinterpret_cast<const uint2 *>(M0 + f * DV + S0 + j);
-            x.dmb = *reinterpret_cast<const uint2 *>(dMC + f * DV + S0 + j);
+            x.m0b = *reinterpret_cast<const uint2 *>(M0 + ckpt_at(f, S0 + j, DK));
+            x.dmb = *reinterpret_cast<const uint2 *>(dMC + ckpt_at(f, S0 + j, DK));
         }
         // the chunk's rows of every per-token array: uniform bases, 32-bit offsets
         const int r = tid / (BV / 4), j = 4 * (tid % (BV / 4));
@@ -1352,7 +1352,7 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
             const int f = f0 + 4 * lq + e, j = c0 + lr;
             dM[m][e] = dS_T ? dS_T[(bh * DK + f) * dv + j0 + j] : 0.f;
             sdMb[f * PVH + j] = bf16_bits(dM[m][e]);
-            if (nch > 0) dMck[((bh * nch + nch - 1) * DK + f) * dv + j0 + j] = bf16_bits(dM[m][e]);
+            if (nch > 0) dMck[(bh * nch + nch - 1) * DK * dv + ckpt_at(f, j0 + j, DK)] = bf16_bits(dM[m][e]);
         }
     }
     if (nch > 0) {  // the last chunk's tiles (q, k stay in registers for its first phase)
@@ -1471,7 +1471,7 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
                 // bf16, row f0 + 4 lq + lr % 4, columns c0 + 4 (lr / 4) .. +3
                 const uint2 x = pack4u(quad_transpose(dM[m], lane));
                 __builtin_amdgcn_raw_buffer_store_b64(
-                    u32x2{x.x, x.y}, mrsrc, ((f0 + 4 * lq + (lr & 3)) * dv + j0 + c0 + 4 * (lr >> 2)) * 2, 0, 0);
+                    u32x2{x.x, x.y}, mrsrc, ckpt_at(f0 + 4 * lq + (lr & 3), j0 + c0 + 4 * (lr >> 2), DK) * 2, 0, 0);
             }
         }
         if (c > 0) store_t();  // T of the next chunk (last read by this chunk's dR)

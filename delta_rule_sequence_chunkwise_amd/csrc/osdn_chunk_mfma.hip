@@ -428,14 +428,14 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
         for (int64_t c = -2; c < nchunks; ++c) {
             if (c >= 0) {
                 // ---- chunk c: R, U, read-out, carry --------------------------------------------
-                if constexpr (CKPT) {  // the state at this chunk's start in bf16, for the backward:
-                                       // row 16 ft + 4 lq + lr % 4, columns 4 (lr / 4) .. +3 of
-                                       // the wave's 16 after a quad transpose
-                    uint16_t *dst = ckpt + (bh * nchunks + c) * DK * dv + (4 * lq + (lr & 3)) * dv +
-                                    j0 + VW * ct + 4 * (lr >> 2);
+                if constexpr (CKPT) {  // the state at this chunk's start in bf16, for the backward
+                                       // (tiled by ckpt_at): row 16 ft + 4 lq + lr % 4, columns
+                                       // 4 (lr / 4) .. +3 of the wave's 16 after a quad transpose
+                    uint16_t *dst = ckpt + (bh * nchunks + c) * DK * dv +
+                                    ckpt_at(4 * lq + (lr & 3), j0 + VW * ct + 4 * (lr >> 2), DK);
 #pragma unroll
-                    for (int ft = 0; ft < NFT; ++ft)
-                        *reinterpret_cast<uint2 *>(dst + 16 * ft * dv) = pack4u(quad_transpose(M[ft], lane));
+                    for (int ft = 0; ft < NFT; ++ft)  // rows 16 ft .. of the tile
+                        *reinterpret_cast<uint2 *>(dst + 16 * 16 * ft) = pack4u(quad_transpose(M[ft], lane));
                 }
                 const int b = static_cast<int>(c & 1);
                 const int n = rows_of(c);

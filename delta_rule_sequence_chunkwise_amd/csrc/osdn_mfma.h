@@ -112,6 +112,14 @@ __device__ __forceinline__ void wait_global_n() {
     asm volatile("" ::: "memory");
 }
 
+// Element (f, col) of a bf16 dk x dv state (or state-gradient) checkpoint of one chunk, stored as
+// dv / 16 tiles of dk x 16, each tile contiguous: a wave owns 16 value columns, so its 8-byte-
+// per-lane store of 16 rows covers 512 contiguous bytes (row-major, it would write sixteen
+// 32-byte pieces of separate rows)
+__host__ __device__ constexpr int64_t ckpt_at(int f, int col, int dk) {
+    return (static_cast<int64_t>(col >> 4) * dk + f) * 16 + (col & 15);
+}
+
 // x + (x of the lane selected by the DPP control), 0 where the control selects no lane
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ float dpp_add(float x) {

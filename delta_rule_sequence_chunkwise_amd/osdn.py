@@ -182,17 +182,28 @@ def states_bytes(B: int, H: int, T: int, dk: int, dv: int, dtype_code: int) -> i
     return n
 
 
+def checkpoint_matrix(ck):
+    """The [B,H,nchunks,dk,dv] values of a bf16 checkpoint view [B,H,nchunks,dv/16,dk,16]
+    (a copy; fp32 views pass through)."""
+    if ck.dim() == 5:
+        return ck
+    B, H, nch, nt, dk, w = ck.shape
+    return ck.permute(0, 1, 2, 4, 3, 5).reshape(B, H, nch, dk, nt * w)
+
+
 def states_parts(states, B: int, H: int, T: int, dk: int, dv: int, dtype):
-    """Views of the training pair's states buffer: (checkpoints [B,H,nchunks,dk,dv], U
-    [B,H,T,dv] or None); dtype is the inputs' (torch.bfloat16 or torch.float32)."""
+    """Views of the training pair's states buffer: (checkpoints, U [B,H,T,dv] or None); dtype is
+    the inputs' (torch.bfloat16 or torch.float32).  The checkpoints are [B,H,nchunks,dk,dv] for
+    fp32 inputs and, for bf16 inputs, dv/16 contiguous column tiles [B,H,nchunks,dv/16,dk,16]
+    (checkpoint_matrix gives the [..., dk, dv] view's values)."""
     torch = _torch()
     bf = dtype == torch.bfloat16
     chunk = 64 if bf else 32
     nch = (T + chunk - 1) // chunk
     n = B * H * nch * dk * dv * (2 if bf else 4)
-    ck = states[:n].view(torch.bfloat16 if bf else torch.float32).view(B, H, nch, dk, dv)
     if not bf:
-        return ck, None
+        return states[:n].view(torch.float32).view(B, H, nch, dk, dv), None
+    ck = states[:n].view(torch.bfloat16).view(B, H, nch, dv // 16, dk, 16)
     uoff = (n + 255) // 256 * 256
     u = states[uoff:uoff + B * H * T * dv * 2].view(torch.bfloat16).view(B, H, T, dv)
     return ck, u

@@ -214,8 +214,10 @@ osdn_status osdn_step_kda(const void *q, const void *k, const void *v, const flo
  * forward osdn_chunk_fwd runs for this input type), for bf16 inputs the inverse (I + A)^{-1},
  * the scores and k~ of every chunk, a reverse pass over chunks for the state gradient, and the
  * per-chunk gradients.
- * The workspace holds the state and state-gradient checkpoints ([B,H,nchunks,dk,dv] each;
- * bf16 for bf16 inputs, the precision the matrix products take them in; fp32 for fp32 inputs)
+ * The workspace holds the state and state-gradient checkpoints (per sequence and chunk a dk x dv
+ * matrix; bf16 for bf16 inputs, the precision the matrix products take them in, stored as dv/16
+ * contiguous dk x 16 column tiles, [B,H,nchunks,dv/16,dk,16]; fp32 [B,H,nchunks,dk,dv] for fp32
+ * inputs)
  * and, for bf16 inputs, per chunk three bf16 64 x 64 planes (the inverse (I + A)^{-1} as hi and
  * lo parts, and the intra-chunk scores) and k~ = d (.) k as 64 x dk bf16, then the per-row
  * pseudo-values U (from the forward) and their gradient dR (from the reverse pass), [B,H,T,dv]
@@ -239,10 +241,11 @@ osdn_status osdn_chunk_bwd(const void *q, const void *k, const void *v, const fl
  * osdn_chunk_fwd_states: as osdn_chunk_fwd with the backward's chunk size (64 rows for bf16
  * inputs, 32 for fp32), and in addition
  *   states   out, osdn_chunk_states_bytes(B, H, T, dk, dv, qkv) bytes, 16-byte aligned,
- *            overlapping no other argument: [B,H,nchunks,dk,dv], bf16 for bf16 inputs (the
- *            precision the backward's products take them in), fp32 for fp32 inputs, the state
- *            before chunk c's first row in slot c; for bf16 inputs then, from the next 256-byte
- *            boundary, the pseudo-values U of every row, [B,H,T,dv] bf16
+ *            overlapping no other argument: the state before chunk c's first row in slot c,
+ *            for bf16 inputs in bf16 (the precision the backward's products take them in) as
+ *            dv/16 contiguous dk x 16 column tiles, [B,H,nchunks,dv/16,dk,16], then, from the
+ *            next 256-byte boundary, the pseudo-values U of every row, [B,H,T,dv] bf16; for
+ *            fp32 inputs fp32 [B,H,nchunks,dk,dv]
  * o and S_T are bitwise those of osdn_chunk_fwd with that chunk size.
  *
  * osdn_chunk_bwd_states: as osdn_chunk_bwd, with `states` (input) from osdn_chunk_fwd_states on

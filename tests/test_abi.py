@@ -341,7 +341,10 @@ def test_states_parts_layout(L, B, H, T, dk, dv, bf):
     buf = torch.zeros(nbytes, dtype=torch.uint8)
     ck, u = osdn.states_parts(buf, B, H, T, dk, dv, dt)
     nch = (T + (64 if bf else 32) - 1) // (64 if bf else 32)
-    assert ck.shape == (B, H, nch, dk, dv) and ck.dtype == dt
+    # bf16 checkpoints are dv/16 contiguous dk x 16 column tiles
+    assert ck.shape == ((B, H, nch, dv // 16, dk, 16) if bf else (B, H, nch, dk, dv))
+    assert ck.dtype == dt
+    assert osdn.checkpoint_matrix(ck).shape == (B, H, nch, dk, dv)
     assert ck.data_ptr() == buf.data_ptr()
     if not bf:
         assert u is None

@@ -173,9 +173,9 @@ def _workspace_states(ws, B, H, T, dk, dv, qkv):
     n = B * H * nch * dk * dv
     r256 = lambda x: (x + 255) // 256 * 256
     dt = torch.bfloat16 if qkv == "bf16" else torch.float32
-    ck = ws[: n * (2 if qkv == "bf16" else 4)].view(dt).view(B, H, nch, dk, dv)
     if qkv != "bf16":
-        return ck, None
+        return ws[: n * 4].view(dt).view(B, H, nch, dk, dv), None
+    ck = ws[: n * 2].view(dt).view(B, H, nch, dv // 16, dk, 16)  # column tiles
     off = 2 * r256(n * 2) + r256(B * H * nch * (3 * C * C + C * dk) * 2)
     return ck, ws[off:off + B * H * T * dv * 2].view(dt).view(B, H, T, dv)
 
@@ -206,6 +206,18 @@ def test_training_pair_matches_recompute_bitwise(case):
     ck, u = osdn.states_parts(states, B, H, T, dk, dv, args[0].dtype)
     ck_ref, u_ref = _workspace_states(ws, B, H, T, dk, dv, qkv)
     assert torch.equal(ck, ck_ref)
+    # the documented layout: slot c holds the state after the first c chunks, per the oracle
+    import oracle
+    q_, k_, v_, b_, d_, a_, s0_ = oracle_inputs(x, "f32")
+    mats = to_np(osdn.checkpoint_matrix(ck))
+    for c in range(ck.shape[2]):
+        if c == 0:
+            ref_c = s0_
+        else:
+            t_ = c * C
+            _, ref_c = oracle.chunk_fwd(q_[:, :, :t_], k_[:, :, :t_], v_[:, :, :t_], b_[:, :, :t_],
+                                        d_[:, :, :t_], a_[:, :, :t_], s0_)
+        assert rel_err(mats[:, :, c], ref_c) <= TOL[qkv], f"checkpoint {c}"
     assert (u is None) == (u_ref is None) and (u is None or torch.equal(u, u_ref))
     got = osdn.osdn_chunk_bwd(*args, go, gst, states=states)
     torch.cuda.synchronize()
