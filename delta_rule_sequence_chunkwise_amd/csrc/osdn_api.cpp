@@ -442,13 +442,16 @@ int64_t bwd_ckpt_bytes(int64_t B, int64_t H, int64_t T, int32_t dk, int32_t dv, 
     return round256(n * (qkv == OSDN_BF16 ? 2 : 4));
 }
 
-// bytes of each per-row buffer of the backward (bf16 inputs: U and dR, [BH, T, dv] bf16; fp32
-// inputs: none); called after bwd_ckpt_bytes has accepted the sizes
+// bytes of each per-row buffer of the backward (bf16 inputs: U and dR, bf16, per sequence and
+// 64-row chunk dv/16 contiguous 64 x 16 column tiles, the last chunk padded:
+// [BH, nchunks, dv/16, 64, 16]; fp32 inputs: none); called after bwd_ckpt_bytes has accepted
+// the sizes
 int64_t bwd_rows_bytes(int64_t B, int64_t H, int64_t T, int32_t dv, osdn_dtype qkv) {
     if (qkv != OSDN_BF16) return 0;
-    int64_t n = 2;
-    if (!mul_ok(n, B, kMaxElems) || !mul_ok(n, H, kMaxElems) || !mul_ok(n, T, kMaxElems) ||
-        !mul_ok(n, dv, kMaxElems))
+    const int64_t C = osdn::bwd_chunk_size(qkv);
+    int64_t n = 2 * C;
+    if (!mul_ok(n, B, kMaxElems) || !mul_ok(n, H, kMaxElems) ||
+        !mul_ok(n, (T + C - 1) / C, kMaxElems) || !mul_ok(n, dv, kMaxElems))
         return -1;
     return round256(n);
 }

@@ -738,8 +738,9 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
         const int e = (r < nn ? r : nn - 1) * DV + S0 + j;
         x.vu = *reinterpret_cast<const uint2 *>(v + r0 * DV + e);
         x.ou = *reinterpret_cast<const uint2 *>(dO + r0 * DV + e);
-        x.uu = *reinterpret_cast<const uint2 *>(Uck + r0 * DV + e);
-        x.ru = *reinterpret_cast<const uint2 *>(dRck + r0 * DV + e);
+        const int ue = rows_at(r < nn ? r : nn - 1, S0 + j);  // the chunk's column-tile block
+        x.uu = *reinterpret_cast<const uint2 *>(Uck + cc * C * DV + ue);
+        x.ru = *reinterpret_cast<const uint2 *>(dRck + cc * C * DV + ue);
     };
     constexpr int NS = DV / BV;  // value slices
     // a chunk's prologue loads, issued while the previous chunk finishes: beta, alpha (every
@@ -1426,15 +1427,15 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
                 sGDRb[r * PVH + j] = bf16_bits(-sgam[pb][r] * sb[pb][r] * dr[e]);
                 gvt[e] = sb[pb][r] * dr[e];
             }
-            // dR and dV in bf16: row R0 + 4 lq + lr % 4, columns jt + 4 (lr / 4) .. +3; rows
-            // past the end fall outside the range
+            // dR and dV in bf16: row R0 + 4 lq + lr % 4, columns jt + 4 (lr / 4) .. +3; dR into
+            // the chunk's block of column tiles (rows_at; padded, every row written), dV with
+            // the rows past the end outside the buffer range
             const uint2 drp = pack4u(quad_transpose(dr, lane));
             const uint2 gvp = pack4u(quad_transpose(gvt, lane));
             const int64_t rowc = (seq0 + c * C) * dv;
             const int boff = ((R0 + 4 * lq + (lr & 3)) * dv + j0 + jt + 4 * (lr >> 2)) * 2;
-            __builtin_amdgcn_raw_buffer_store_b64(
-                u32x2{drp.x, drp.y}, __builtin_amdgcn_make_buffer_rsrc(dRck + rowc, 0, n * dv * 2, 0x00020000),
-                boff, 0, 0);
+            *reinterpret_cast<uint2 *>(dRck + (bh * nch + c) * C * dv +
+                                       rows_at(R0 + 4 * lq + (lr & 3), j0 + jt + 4 * (lr >> 2))) = drp;
             __builtin_amdgcn_raw_buffer_store_b64(
                 u32x2{gvp.x, gvp.y}, __builtin_amdgcn_make_buffer_rsrc(gv + rowc, 0, n * dv * 2, 0x00020000),
                 boff, 0, 0);

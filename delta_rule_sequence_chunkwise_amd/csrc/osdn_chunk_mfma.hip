@@ -501,18 +501,18 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                 solve(3);
                 const v8s ub1 = c_to_frag(U[2], U[3]);
                 const v8s uwb1 = c_to_frag(w4[2] * U[2], w4[3] * U[3]);
-                if constexpr (CKPT) {  // U for the backward, bf16: row 16 i + 4 lq + lr % 4,
-                                       // columns 4 (lr / 4) .. +3 of the wave's 16 after a quad
-                                       // transpose; rows past the end fall outside the range
+                if constexpr (CKPT) {  // U for the backward, bf16, in the chunk's block of
+                                       // column tiles (rows_at; the last chunk's block is padded
+                                       // and its rows past the end are written as computed):
+                                       // row 16 i + 4 lq + lr % 4, columns 4 (lr / 4) .. +3 of the
+                                       // wave's 16 after a quad transpose
                     if (uout) {
-                        const __amdgpu_buffer_rsrc_t ursrc = __builtin_amdgcn_make_buffer_rsrc(
-                            uout + row0 * dv, 0, n * dv * 2, 0x00020000);
+                        uint16_t *ub = uout + (bh * nchunks + c) * CH * dv;
 #pragma unroll
                         for (int i = 0; i < NBLK; ++i) {
                             const uint2 pk = pack4u(quad_transpose(U[i], lane));
-                            __builtin_amdgcn_raw_buffer_store_b64(
-                                u32x2{pk.x, pk.y}, ursrc,
-                                ((16 * i + 4 * lq + (lr & 3)) * dv + j0 + VW * ct + 4 * (lr >> 2)) * 2, 0, 0);
+                            *reinterpret_cast<uint2 *>(
+                                ub + rows_at(16 * i + 4 * lq + (lr & 3), j0 + VW * ct + 4 * (lr >> 2))) = pk;
                         }
                     }
                 }

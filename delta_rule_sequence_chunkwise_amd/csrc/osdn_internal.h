@@ -62,8 +62,8 @@ struct ChunkArgs {
     void *ckpt = nullptr;        // [BH, nchunks, dk, dv]: the state at every chunk start, fp32
                                  // from the fp32 forward (either gate), bf16 from the
                                  // matrix-core forward (o may then be NULL: not written)
-    void *uout = nullptr;        // with ckpt, matrix-core forward: [BH, T, dv] bf16, the
-                                 // pseudo-values U of every row (NULL: not written)
+    void *uout = nullptr;        // with ckpt, matrix-core forward: the pseudo-values U of every
+                                 // row, bf16 [BH, nchunks, dv/16, 64, 16] (NULL: not written)
     const float *gate_scores = nullptr;  // fp32 forward with the channel-wise gate, 32-row
                                          // chunks: the score tiles AS, P of every chunk as the
                                          // backward forms them, [BH, nchunks, 2, 32, 32]
@@ -88,7 +88,7 @@ struct BwdArgs {
                           // scores P (64 x 64 each; P zero above the diagonal), then
                           // K~ = d (.) k (64 x dk; zero past the end)
     uint16_t *Uck, *dRck; // workspace (bf16 inputs): U from the forward and dR from the reverse
-                          // pass, [BH, T, dv] bf16 each
+                          // pass, bf16, [BH, nchunks, dv/16, 64, 16] each (rows_at)
     int64_t BH, T;
     int32_t dk, dv;
     osdn_dtype qkv, d_dtype;

@@ -119,6 +119,9 @@ __device__ __forceinline__ void wait_global_n() {
 __host__ __device__ constexpr int64_t ckpt_at(int f, int col, int dk) {
     return (static_cast<int64_t>(col >> 4) * dk + f) * 16 + (col & 15);
 }
+// Element (row r, value column col) of a 64-row chunk's block of a bf16 per-row buffer of the
+// backward (U, dR): dv / 16 contiguous 64 x 16 column tiles, for the same reason
+__host__ __device__ constexpr int rows_at(int r, int col) { return ((col >> 4) * 64 + r) * 16 + (col & 15); }
 
 // x + (x of the lane selected by the DPP control), 0 where the control selects no lane
 template <int CTRL, int ROW_MASK>

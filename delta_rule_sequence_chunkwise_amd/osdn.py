@@ -191,11 +191,18 @@ def checkpoint_matrix(ck):
     return ck.permute(0, 1, 2, 4, 3, 5).reshape(B, H, nch, dk, nt * w)
 
 
+def rows_matrix(u, T: int):
+    """The [B,H,T,dv] values of a per-row buffer view [B,H,nchunks,dv/16,64,16] (a copy)."""
+    B, H, nch, nt, c, w = u.shape
+    return u.permute(0, 1, 2, 4, 3, 5).reshape(B, H, nch * c, nt * w)[:, :, :T]
+
+
 def states_parts(states, B: int, H: int, T: int, dk: int, dv: int, dtype):
-    """Views of the training pair's states buffer: (checkpoints, U [B,H,T,dv] or None); dtype is
-    the inputs' (torch.bfloat16 or torch.float32).  The checkpoints are [B,H,nchunks,dk,dv] for
-    fp32 inputs and, for bf16 inputs, dv/16 contiguous column tiles [B,H,nchunks,dv/16,dk,16]
-    (checkpoint_matrix gives the [..., dk, dv] view's values)."""
+    """Views of the training pair's states buffer: (checkpoints, U or None); dtype is the
+    inputs' (torch.bfloat16 or torch.float32).  The checkpoints are [B,H,nchunks,dk,dv] for fp32
+    inputs and, for bf16 inputs, dv/16 contiguous column tiles [B,H,nchunks,dv/16,dk,16]
+    (checkpoint_matrix gives the [..., dk, dv] values); U (bf16 inputs) is per 64-row chunk
+    dv/16 contiguous 64 x 16 tiles, [B,H,nchunks,dv/16,64,16] (rows_matrix gives [B,H,T,dv])."""
     torch = _torch()
     bf = dtype == torch.bfloat16
     chunk = 64 if bf else 32
@@ -205,8 +212,8 @@ def states_parts(states, B: int, H: int, T: int, dk: int, dv: int, dtype):
         return states[:n].view(torch.float32).view(B, H, nch, dk, dv), None
     ck = states[:n].view(torch.bfloat16).view(B, H, nch, dv // 16, dk, 16)
     uoff = (n + 255) // 256 * 256
-    u = states[uoff:uoff + B * H * T * dv * 2].view(torch.bfloat16).view(B, H, T, dv)
-    return ck, u
+    u = states[uoff:uoff + B * H * nch * chunk * dv * 2].view(torch.bfloat16)
+    return ck, u.view(B, H, nch, dv // 16, chunk, 16)
 
 
 def osdn_chunk_fwd_states(q, k, v, beta, d, alpha=None, S0=None, *, o=None, S_T=None,

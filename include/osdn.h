@@ -220,8 +220,9 @@ osdn_status osdn_step_kda(const void *q, const void *k, const void *v, const flo
  * inputs)
  * and, for bf16 inputs, per chunk three bf16 64 x 64 planes (the inverse (I + A)^{-1} as hi and
  * lo parts, and the intra-chunk scores) and k~ = d (.) k as 64 x dk bf16, then the per-row
- * pseudo-values U (from the forward) and their gradient dR (from the reverse pass), [B,H,T,dv]
- * bf16 each.
+ * pseudo-values U (from the forward) and their gradient dR (from the reverse pass), bf16, per
+ * 64-row chunk dv/16 contiguous 64 x 16 column tiles, [B,H,nchunks,dv/16,64,16] each (the last
+ * chunk padded).
  */
 int64_t osdn_chunk_bwd_workspace(int64_t B, int64_t H, int64_t T, int32_t dk, int32_t dv,
                                  osdn_dtype qkv); /* -1 if invalid */
@@ -244,7 +245,8 @@ osdn_status osdn_chunk_bwd(const void *q, const void *k, const void *v, const fl
  *            overlapping no other argument: the state before chunk c's first row in slot c,
  *            for bf16 inputs in bf16 (the precision the backward's products take them in) as
  *            dv/16 contiguous dk x 16 column tiles, [B,H,nchunks,dv/16,dk,16], then, from the
- *            next 256-byte boundary, the pseudo-values U of every row, [B,H,T,dv] bf16; for
+ *            next 256-byte boundary, the pseudo-values U of every row, bf16, per 64-row chunk
+ *            dv/16 contiguous 64 x 16 column tiles, [B,H,nchunks,dv/16,64,16]; for
  *            fp32 inputs fp32 [B,H,nchunks,dk,dv]
  * o and S_T are bitwise those of osdn_chunk_fwd with that chunk size.
  *

@@ -177,7 +177,7 @@ def _workspace_states(ws, B, H, T, dk, dv, qkv):
         return ws[: n * 4].view(dt).view(B, H, nch, dk, dv), None
     ck = ws[: n * 2].view(dt).view(B, H, nch, dv // 16, dk, 16)  # column tiles
     off = 2 * r256(n * 2) + r256(B * H * nch * (3 * C * C + C * dk) * 2)
-    return ck, ws[off:off + B * H * T * dv * 2].view(dt).view(B, H, T, dv)
+    return ck, ws[off:off + B * H * nch * C * dv * 2].view(dt).view(B, H, nch, dv // 16, C, 16)
 
 
 @pytest.mark.parametrize("case", [(1, 2, 130, 128, 128, "bf16"), (2, 1, 64, 64, 128, "bf16"),
