@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define OSDN_ABI_VERSION 4
+#define OSDN_ABI_VERSION 5
 
 typedef enum osdn_status {
     OSDN_OK = 0,
