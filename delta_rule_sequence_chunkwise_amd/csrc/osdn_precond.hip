@@ -160,7 +160,6 @@ struct alignas(16) PrecondLds {
     alignas(16) float ew[2][CH];          // [chunk parity] e^{lr_{32(i/32)} - lr_{i+1}} c_i e_i
     alignas(16) uint16_t dsp[2][2][DK];   // [chunk parity][hi, lo] bf16 split of d0
     alignas(16) uint16_t wsp[2][CH];      // [hi, lo] bf16 split of w = R[C,.] c e
-    alignas(16) float uu[CH];             // the chain wave's X d0
 };
 
 // inclusive prefix sum over the 64 lanes (shifts by 1, 2, 4, 8 inside each 16-lane row, then
@@ -338,13 +337,16 @@ precond_chunk_kernel(const uint16_t *__restrict__ k, const float *__restrict__ b
     // Gram tiles of chunk s+1, waves 5-6 square the keys of chunk s+2 and wave 4 scans its
     // gates.
     if (wave == 0) {
+        // d0 stays in registers: lane (q, n) owns features 16 q + n and, for dk = 128,
+        // 16 (q + 4) + n (the carry's column tiles q and q + 4)
+        float d0a = sm.d0[0][16 * q + n], d0b = NF > 4 ? sm.d0[0][16 * (q + 4) + n] : 0.f;
         for (int s = -1; s <= nc; ++s) {
             if (s >= 0 && s < nc) {
                 const int sl = s & 3;
                 const uint16_t *xh = sm.xh[sl], *xl = sm.xl[s % 3];
-                const float *d0 = sm.d0[s % 3];
-                // u = X d0: A = xh then xl (rows 16J..), B = [hi(d0) | lo(d0) | 0 ...], so the
-                // sum of output columns 0 and 1 is x . d0 to fp32 accuracy.  The fragments of
+                // u^T = d0^T X^T: A = [hi(d0) ; lo(d0) ; 0 ...] (rows 0, 1), B = xh then xl
+                // (token columns 16J..), so the sum of output rows 0 and 1 is x . d0 to fp32
+                // accuracy, in lane n of the first quarter for token 16J + n.  The fragments of
                 // a feature slice are read together, one slice ahead of the products.
                 v4f ua[4];
 #pragma unroll
@@ -366,8 +368,8 @@ precond_chunk_kernel(const uint16_t *__restrict__ k, const float *__restrict__ b
                     __builtin_amdgcn_sched_barrier(0);  // the next slice's reads stay ahead
 #pragma unroll
                     for (int J = 0; J < 4; ++J) {
-                        ua[J] = mfma32(fa[st & 1][2 * J], b, ua[J]);
-                        ua[J] = mfma32(fa[st & 1][2 * J + 1], b, ua[J]);
+                        ua[J] = mfma32(b, fa[st & 1][2 * J], ua[J]);
+                        ua[J] = mfma32(b, fa[st & 1][2 * J + 1], ua[J]);
                     }
                 }
                 float Lrow[CH];
@@ -380,27 +382,18 @@ precond_chunk_kernel(const uint16_t *__restrict__ k, const float *__restrict__ b
                     Lrow[4 * m + 2] = t4[2];
                     Lrow[4 * m + 3] = t4[3];
                 }
+                // row 0 + row 1 of tile J sits in lanes 0..15; the two row swaps bring tile J
+                // to lanes 16J.., so lane j holds u_j
+                uint32_t uj[4];
 #pragma unroll
-                for (int J = 0; J < 4; ++J) {
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        const float v = dpp_add<0xb1, 0xf>(ua[J][m]);  // column 0 + column 1
-                        if (n == 0) sm.uu[16 * J + 4 * q + m] = v;
-                    }
-                }
-                // (I + L) e = 1 - b rho u by forward substitution; lane = row
-                float e = 1.f - sm.beta[sl][lane] * sm.rho[sl][lane] * sm.uu[lane];
-#pragma unroll
-                for (int i = 0; i < CH - 1; ++i) e = fmaf(-Lrow[i], lane_value(e, i), e);
-                const float lr1 = sm.lr[sl][lane + 1], ce = sm.cc[sl][lane] * e;
-                split1(__expf(sm.lr[sl][CH] - lr1) * ce, sm.wsp[0][lane], sm.wsp[1][lane]);
-                sm.ew[s & 1][lane] = __expf(sm.lr[sl][lane & 32] - lr1) * ce;
-                // carry d0 <- rho_C d0 + X^T w: A = [hi(w) ; lo(w) ; 0 ...], B = xh then xl
-                v8s aw[2];
-#pragma unroll
-                for (int st = 0; st < 2; ++st) aw[st] = split_frag(sm.wsp[0], sm.wsp[1], 32 * st + 8 * q, n);
-                v4f ca[NF];
-                v8s fb[2][4];
+                for (int J = 0; J < 4; ++J) uj[J] = __float_as_uint(ua[J][0] + ua[J][1]);
+                const u32x2 s01 = __builtin_amdgcn_permlane16_swap(uj[0], uj[1], false, false);
+                const u32x2 s23 = __builtin_amdgcn_permlane16_swap(uj[2], uj[3], false, false);
+                const u32x2 s03 = __builtin_amdgcn_permlane32_swap(s01[0], s23[0], false, false);
+                const float u = __uint_as_float(s03[0]);
+                // the carry's B fragments of X^T do not depend on e: the first two tiles' reads
+                // are issued before the substitution, which uses no LDS
+                v8s fb[3][4];
                 auto read_c = [&](int F, v8s *f) __attribute__((always_inline)) {
 #pragma unroll
                     for (int st = 0; st < 2; ++st) {
@@ -412,27 +405,52 @@ precond_chunk_kernel(const uint16_t *__restrict__ k, const float *__restrict__ b
                     }
                 };
                 read_c(0, fb[0]);
+                read_c(1, fb[1]);
+                // (I + L) e = 1 - b rho u by forward substitution; lane = row
+                float e = 1.f - sm.beta[sl][lane] * sm.rho[sl][lane] * u;
+#pragma unroll
+                for (int i = 0; i < CH - 1; ++i) e = fmaf(-Lrow[i], lane_value(e, i), e);
+                const float lr1 = sm.lr[sl][lane + 1], ce = sm.cc[sl][lane] * e;
+                split1(__expf(sm.lr[sl][CH] - lr1) * ce, sm.wsp[0][lane], sm.wsp[1][lane]);
+                sm.ew[s & 1][lane] = __expf(sm.lr[sl][lane & 32] - lr1) * ce;
+                // carry d0 <- rho_C d0 + X^T w: A = [hi(w) ; lo(w) ; 0 ...], B = xh then xl
+                v8s aw[2];
+#pragma unroll
+                for (int st = 0; st < 2; ++st) aw[st] = split_frag(sm.wsp[0], sm.wsp[1], 32 * st + 8 * q, n);
+                v4f ca[NF];
 #pragma unroll
                 for (int F = 0; F < NF; ++F) {
-                    if (F + 1 < NF) read_c(F + 1, fb[(F + 1) & 1]);
-                    __builtin_amdgcn_sched_barrier(0);  // the next tile's reads stay ahead
+                    if (F + 2 < NF) read_c(F + 2, fb[(F + 2) % 3]);
+                    __builtin_amdgcn_sched_barrier(0);  // the reads stay two tiles ahead
                     ca[F] = zero4();
 #pragma unroll
                     for (int st = 0; st < 2; ++st) {
-                        ca[F] = mfma32(aw[st], fb[F & 1][2 * st], ca[F]);
-                        ca[F] = mfma32(aw[st], fb[F & 1][2 * st + 1], ca[F]);
+                        ca[F] = mfma32(aw[st], fb[F % 3][2 * st], ca[F]);
+                        ca[F] = mfma32(aw[st], fb[F % 3][2 * st + 1], ca[F]);
                     }
                 }
-                if (q == 0) {  // rows 0 (hi(w) . x) and 1 (lo(w) . x) of column n
-                    const float rc = __expf(sm.lr[sl][CH]);
-                    float *dn = sm.d0[(s + 1) % 3];
+                // rows 0 (hi(w) . x) and 1 (lo(w) . x) of column tile F sit in lanes 0..15; the
+                // row swaps bring tiles q and q + 4 to quarter q, so every lane writes two
+                // features instead of lanes 0..15 writing all of them
+                auto gather4 = [&](int F0) __attribute__((always_inline)) {
+                    uint32_t x[4];
 #pragma unroll
-                    for (int F = 0; F < NF; ++F) {
-                        const int f = 16 * F + n;
-                        const float v = rc * d0[f] + ca[F][0] + ca[F][1];
-                        dn[f] = v;
-                        split1(v, sm.dsp[(s + 1) & 1][0][f], sm.dsp[(s + 1) & 1][1][f]);
-                    }
+                    for (int i = 0; i < 4; ++i)
+                        x[i] = F0 + i < NF ? __float_as_uint(ca[F0 + i][0] + ca[F0 + i][1]) : 0u;
+                    const u32x2 a = __builtin_amdgcn_permlane16_swap(x[0], x[1], false, false);
+                    const u32x2 b = __builtin_amdgcn_permlane16_swap(x[2], x[3], false, false);
+                    return __uint_as_float(__builtin_amdgcn_permlane32_swap(a[0], b[0], false, false)[0]);
+                };
+                const float rc = __expf(sm.lr[sl][CH]);
+                float *dn = sm.d0[(s + 1) % 3];
+                uint16_t *dh = sm.dsp[(s + 1) & 1][0], *dl = sm.dsp[(s + 1) & 1][1];
+                d0a = rc * d0a + gather4(0);
+                dn[16 * q + n] = d0a;
+                split1(d0a, dh[16 * q + n], dl[16 * q + n]);
+                if constexpr (NF > 4) {
+                    d0b = rc * d0b + gather4(4);
+                    dn[16 * (q + 4) + n] = d0b;
+                    split1(d0b, dh[16 * (q + 4) + n], dl[16 * (q + 4) + n]);
                 }
             }
             block_sync();
