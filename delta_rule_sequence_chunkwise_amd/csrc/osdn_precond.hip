@@ -207,36 +207,47 @@ precond_chunk_kernel(const uint16_t *__restrict__ k, const float *__restrict__ b
     const float *rq = r ? r + bh * T : nullptr;
     TD *oq = d_out + bh * T * DK;
 
-    // ---- key loading (waves 5 and 6, rows [R0, R0 + 32) of a chunk each): keys go to eight
-    // named registers (a register array carried across the step loop would live in scratch)
-    // and are squared there; rows past the end re-read the last row (their gate is zero)
+    // ---- key loading (waves 5 and 6, rows [R0, R0 + 32) of a chunk each): keys go to two sets
+    // of eight named registers (a register array carried across the step loop would live in
+    // scratch), so a chunk's loads are issued a whole step before it is squared; rows past the
+    // end re-read the last row (their gate is zero)
     const int R0 = 32 * (wave - 5);
-    uint4 kr0, kr1, kr2, kr3, kr4, kr5, kr6, kr7;
-    auto kreg = [&](auto I) __attribute__((always_inline)) -> uint4 & {
-        if constexpr (I == 0) return kr0;
-        else if constexpr (I == 1) return kr1;
-        else if constexpr (I == 2) return kr2;
-        else if constexpr (I == 3) return kr3;
-        else if constexpr (I == 4) return kr4;
-        else if constexpr (I == 5) return kr5;
-        else if constexpr (I == 6) return kr6;
-        else return kr7;
+    uint4 kr0, kr1, kr2, kr3, kr4, kr5, kr6, kr7, kr8, kr9, kr10, kr11, kr12, kr13, kr14, kr15;
+    auto kreg = [&](auto S, auto I) __attribute__((always_inline)) -> uint4 & {
+        constexpr int R = 8 * decltype(S)::value + decltype(I)::value;
+        if constexpr (R == 0) return kr0;
+        else if constexpr (R == 1) return kr1;
+        else if constexpr (R == 2) return kr2;
+        else if constexpr (R == 3) return kr3;
+        else if constexpr (R == 4) return kr4;
+        else if constexpr (R == 5) return kr5;
+        else if constexpr (R == 6) return kr6;
+        else if constexpr (R == 7) return kr7;
+        else if constexpr (R == 8) return kr8;
+        else if constexpr (R == 9) return kr9;
+        else if constexpr (R == 10) return kr10;
+        else if constexpr (R == 11) return kr11;
+        else if constexpr (R == 12) return kr12;
+        else if constexpr (R == 13) return kr13;
+        else if constexpr (R == 14) return kr14;
+        else return kr15;
     };
-    auto load_keys = [&](int cl) __attribute__((always_inline)) {
+    static_assert(NLD <= 8, "eight registers per key set");
+    auto load_keys = [&](int cl, auto S) __attribute__((always_inline)) {
         const int64_t row0 = int64_t(cl) * CH;
         static_for<0, NLD>([&](auto I) __attribute__((always_inline)) {
             const int pu = R0 * L::KU + I * 64 + lane, j = pu / L::KU, u = pu % L::KU;
             const int64_t row = row0 + j < T ? row0 + j : T - 1;
-            kreg(I) = *reinterpret_cast<const uint4 *>(kq + row * DK + 8 * u);
+            kreg(S, I) = *reinterpret_cast<const uint4 *>(kq + row * DK + 8 * u);
         });
     };
     // x = k^2 of the keys in registers -> xh, xl (xh + xl = x exactly for bf16 keys) and the
     // row norms (the KU units of a row sit in KU consecutive lanes)
-    auto square_keys = [&](int cl) __attribute__((always_inline)) {
+    auto square_keys = [&](int cl, auto S) __attribute__((always_inline)) {
         uint16_t *xh = sm.xh[cl & 3], *xl = sm.xl[cl % 3];
         static_for<0, NLD>([&](auto I) __attribute__((always_inline)) {
             const int pu = R0 * L::KU + I * 64 + lane, j = pu / L::KU, u = pu % L::KU;
-            const uint4 w = kreg(I);
+            const uint4 w = kreg(S, I);
             const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
             uint32_t hi[4], lo[4];
             float sn = 0.f;
@@ -322,8 +333,8 @@ precond_chunk_kernel(const uint16_t *__restrict__ k, const float *__restrict__ b
     }
     if (nc > 0) {
         if (wave == 5 || wave == 6) {
-            load_keys(0);
-            square_keys(0);
+            load_keys(0, std::integral_constant<int, 0>{});
+            square_keys(0, std::integral_constant<int, 0>{});
         } else if (wave == 4) {
             float b0, r0;
             gates(0, b0, r0);
@@ -511,13 +522,19 @@ precond_chunk_kernel(const uint16_t *__restrict__ k, const float *__restrict__ b
             block_sync();
         }
     } else if (wave != 4) {
-        // keys of chunk c (waves 5 and 6): loaded into registers in step c-3, squared into LDS
-        // in step c-2
-        if (nc > 1) load_keys(1);
-        for (int s = -1; s <= nc; ++s) {
-            if (s + 2 < nc) square_keys(s + 2);
-            if (s + 3 < nc) load_keys(s + 3);
+        // keys of chunk c (waves 5 and 6): loaded into registers at the start of step c-3,
+        // squared into LDS in step c-2; the two register sets alternate by step
+        using S0 = std::integral_constant<int, 0>;
+        using S1 = std::integral_constant<int, 1>;
+        if (nc > 1) load_keys(1, S0{});
+        auto key_step = [&](int s, auto ld, auto sq) __attribute__((always_inline)) {
+            if (s + 3 < nc) load_keys(s + 3, ld);
+            if (s + 2 < nc) square_keys(s + 2, sq);
             block_sync();
+        };
+        for (int s = -1; s <= nc; s += 2) {
+            key_step(s, S1{}, S0{});
+            if (s + 1 <= nc) key_step(s + 1, S0{}, S1{});
         }
     } else {
         // gates of chunk c (wave 4, which shares a SIMD with the chain wave, so its load is
