@@ -149,13 +149,8 @@ __device__ __forceinline__ void solve_upper(float *X, const float *AS, const flo
 template <int C>
 __device__ __forceinline__ void decay_scan_of(float bv, float av, bool has_alpha, int n, float *sb,
                                               float *sg, float *sgam, float *sw, int lane) {
-    float x = (lane < n && has_alpha) ? logf(av) : 0.f;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
-    const float gl = __shfl(x, C - 1);
+    const float x = wave_prefix((lane < n && has_alpha) ? logf(av) : 0.f);
+    const float gl = lane_value(x, C - 1);
     if (lane < C) {
         sb[lane] = lane < n ? bv : 0.f;
         sg[lane] = x;
@@ -1331,13 +1326,8 @@ bwd_state_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
     };
     auto scan = [&](int64_t cc) __attribute__((always_inline)) {
         const int nn = rows_of(cc), pb = static_cast<int>(cc & 1);
-        float x = (lane < nn && alpha) ? logf(av) : 0.f;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_up(x, off);
-            if (lane >= off) x += y;
-        }
-        const float gl = __shfl(x, C - 1);
+        const float x = wave_prefix((lane < nn && alpha) ? logf(av) : 0.f);
+        const float gl = lane_value(x, C - 1);
         sb[pb][lane] = lane < nn ? bv : 0.f;
         sgam[pb][lane] = __expf(x);
         sw[pb][lane] = __expf(gl - x);

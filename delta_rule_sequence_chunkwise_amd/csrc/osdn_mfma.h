@@ -163,6 +163,16 @@ __device__ __forceinline__ float row16_total(float x) {
     x = dpp_add<0x114, 0xf>(x);  // row_shr:4
     return dpp_add<0x118, 0xf>(x);  // row_shr:8
 }
+// inclusive prefix sum over the 64 lanes: shifts by 1, 2, 4, 8 inside each 16-lane row, then
+// the last lane of rows 0 and 2 into rows 1 and 3, then lane 31 into rows 2 and 3
+__device__ __forceinline__ float wave_prefix(float x) {
+    x = dpp_add<0x111, 0xf>(x);  // row_shr:1
+    x = dpp_add<0x112, 0xf>(x);  // row_shr:2
+    x = dpp_add<0x114, 0xf>(x);  // row_shr:4
+    x = dpp_add<0x118, 0xf>(x);  // row_shr:8
+    x = dpp_add<0x142, 0xa>(x);  // row_bcast:15 into rows 1, 3
+    return dpp_add<0x143, 0xc>(x);  // row_bcast:31 into rows 2, 3
+}
 // 4 x 4 transpose inside each quad of lanes by two DPP exchange stages: lane 4a + l holds
 // x[e] = X[l][e] on entry and X[e][l] on return.  On a 16x16 tile in the MFMA C layout (lane
 // (q, n) holds rows 4q..4q+3 of column n) lane (q, n) then holds row 4q + (n & 3), columns

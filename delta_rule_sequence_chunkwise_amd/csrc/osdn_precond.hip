@@ -162,18 +162,6 @@ struct alignas(16) PrecondLds {
     alignas(16) uint16_t wsp[2][CH];      // [hi, lo] bf16 split of w = R[C,.] c e
 };
 
-// inclusive prefix sum over the 64 lanes (shifts by 1, 2, 4, 8 inside each 16-lane row, then
-// the last lane of rows 0 and 2 into rows 1 and 3, then lane 31 into rows 2 and 3)
-__device__ __forceinline__ float wave_prefix(float x) {
-    x = dpp_add<0x111, 0xf>(x);
-    x = dpp_add<0x112, 0xf>(x);
-    x = dpp_add<0x114, 0xf>(x);
-    x = dpp_add<0x118, 0xf>(x);
-    x = dpp_add<0x142, 0xa>(x);
-    x = dpp_add<0x143, 0xc>(x);
-    return x;
-}
-
 // an fp32 value -> (bf16(v), bf16(v - bf16(v))) as raw bits
 __device__ __forceinline__ void split1(float v, uint16_t &hi, uint16_t &lo) {
     const uint32_t p = pack2(v, 0.f);
