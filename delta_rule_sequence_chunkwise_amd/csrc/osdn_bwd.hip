@@ -293,8 +293,7 @@ __device__ __forceinline__ void block_inverse64(float *sT, const float *sAS, con
 
 // Fixed-order sum over the workgroup (every thread passes its part; every thread gets the sum)
 __device__ __forceinline__ float block_sum(float x, float *scratch4, int tid) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+    x = sum_rows(group_sum<16>(x));  // over the wave, on DPP
     __syncthreads();
     if ((tid & 63) == 0) scratch4[tid >> 6] = x;
     __syncthreads();
@@ -899,8 +898,7 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
     if (cn < total) rows_of_chunk(cn, rn0, nn);
     issue_prologue(cn < total ? cn : ci, rn0, nn);
     {  // <dMC, M0> over the workgroup (fixed order); ends with a barrier: the slices are done
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) frob += __shfl_xor(frob, m);
+        frob = sum_rows(group_sum<16>(frob));
         __syncthreads();
         if (lane == 0) sred[wave] = frob;
         __syncthreads();
@@ -1002,16 +1000,10 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
         float g = go + gr + srow[0][4][r] + srow[1][4][r] -
                   (scol[0][r] + scol[1][r] + scol[2][r] + scol[3][r]);
         // the last row's terms: gam_L <dMC, M0> + sum_s w_s <(K~ dMC)_s, U_s>
-        float ews = r < n ? ew : 0.f;
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) ews += __shfl_xor(ews, m);
+        const float ews = sum_rows(group_sum<16>(r < n ? ew : 0.f));  // over the wave, on DPP
         g = r < n ? g - ew : 0.f;
         if (r == n - 1) g += sgam[C - 1] * frob + ews;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {  // suffix sum: x_r = sum_{r' >= r} g_r'
-            const float yv = __shfl_down(g, off);
-            if (lane + off < 64) g += yv;
-        }
+        g = wave_suffix(g, lane);  // x_r = sum_{r' >= r} g_r'
         if (r < n) {
             gbeta[row0 + r] = db;
             if (alpha && galpha) galpha[row0 + r] = g / acur;

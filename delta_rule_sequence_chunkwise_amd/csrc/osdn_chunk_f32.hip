@@ -237,13 +237,8 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
         }
         block_sync();
         if (tid < 64) {  // running sum of ln(alpha) by a scan over wave 0's lanes
-            float acc = tid < CH ? sg[tid] : 0.f;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float up = __shfl_up(acc, off);
-                if (tid >= off) acc += up;
-            }
-            const float last = __shfl(acc, CH - 1);
+            const float acc = wave_prefix(tid < CH ? sg[tid] : 0.f);  // on DPP
+            const float last = lane_value(acc, CH - 1);
             if (tid < CH) {
                 sg[tid] = acc;
                 sgam[tid] = __expf(acc);

@@ -173,6 +173,19 @@ __device__ __forceinline__ float wave_prefix(float x) {
     x = dpp_add<0x142, 0xa>(x);  // row_bcast:15 into rows 1, 3
     return dpp_add<0x143, 0xc>(x);  // row_bcast:31 into rows 2, 3
 }
+// inclusive suffix sum over the 64 lanes (lane r receives the sum of lanes r .. 63): shifts
+// by 1, 2, 4, 8 towards lower lanes inside each 16-lane row, then the totals of the later rows,
+// read from their first lanes
+__device__ __forceinline__ float wave_suffix(float x, int lane) {
+    x = dpp_add<0x101, 0xf>(x);  // row_shl:1
+    x = dpp_add<0x102, 0xf>(x);  // row_shl:2
+    x = dpp_add<0x104, 0xf>(x);  // row_shl:4
+    x = dpp_add<0x108, 0xf>(x);  // row_shl:8
+    const float t1 = lane_value(x, 16), t2 = lane_value(x, 32), t3 = lane_value(x, 48);
+    const int row = lane >> 4;
+    const float later = row == 0 ? (t3 + t2) + t1 : (row == 1 ? t3 + t2 : (row == 2 ? t3 : 0.f));
+    return x + later;
+}
 // 4 x 4 transpose inside each quad of lanes by two DPP exchange stages: lane 4a + l holds
 // x[e] = X[l][e] on entry and X[e][l] on return.  On a 16x16 tile in the MFMA C layout (lane
 // (q, n) holds rows 4q..4q+3 of column n) lane (q, n) then holds row 4q + (n & 3), columns
