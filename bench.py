@@ -104,7 +104,11 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--precond-steps", type=int, default=20)
     ap.add_argument("--kda-steps", type=int, default=10)
-    ap.add_argument("--bwd-steps", type=int, default=5)
+    ap.add_argument("--bwd-steps", type=int, default=20)
+    # untimed backward calls before each timed backward loop, past the clock transient that a
+    # few calls leave the board in (five calls timed right after the other legs read ~20 %
+    # slower than the settled figure)
+    ap.add_argument("--bwd-warmup", type=int, default=20)
     ap.add_argument("--kda-bwd-steps", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="1.3b")
@@ -194,7 +198,7 @@ def main():
                                 not args.no_cpu_baseline)
 
     if args.bwd_steps > 0:
-        line["bwd"] = bench_bwd(args.bwd_steps, torch, dev, synth, w, x,
+        line["bwd"] = bench_bwd(args.bwd_steps, args.bwd_warmup, torch, dev, synth, w, x,
                                 (q, k, v, beta, d, alpha, S0), not args.no_cpu_baseline)
 
     if args.kda_bwd_steps > 0:
@@ -312,8 +316,9 @@ def bwd_flops_per_head_token(dk, dv, C):
     return fwd + rev + per_chunk
 
 
-def bench_bwd(n_steps, torch, dev, synth, w, x, fwd, cpu):
-    """Times `n_steps` osdn_chunk_bwd calls on the workload (output gradients seeded)."""
+def bench_bwd(n_steps, n_warm, torch, dev, synth, w, x, fwd, cpu):
+    """Times `n_steps` osdn_chunk_bwd calls on the workload (output gradients seeded), after
+    `n_warm` untimed ones."""
     import numpy as np
     from delta_rule_sequence_chunkwise_amd import osdn
 
@@ -325,6 +330,8 @@ def bench_bwd(n_steps, torch, dev, synth, w, x, fwd, cpu):
     ws = torch.empty(osdn.bwd_workspace_bytes(B, H, T, dk, dv, osdn.OSDN_BF16),
                      dtype=torch.uint8, device=dev)
     grads = osdn.osdn_chunk_bwd(q, k, v, beta, d, alpha, S0, do, dS_T, workspace=ws)
+    for _ in range(n_warm):
+        osdn.osdn_chunk_bwd(q, k, v, beta, d, alpha, S0, do, dS_T, grads=grads, workspace=ws)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -337,8 +344,10 @@ def bench_bwd(n_steps, torch, dev, synth, w, x, fwd, cpu):
     # the training pair: the forward that keeps the chunk-start states, and the backward that
     # takes them (no forward recompute inside)
     o_buf, st_buf, states = osdn.osdn_chunk_fwd_states(q, k, v, beta, d, alpha, S0)
-    osdn.osdn_chunk_bwd(q, k, v, beta, d, alpha, S0, do, dS_T, grads=grads, workspace=ws,
-                        states=states)
+    for _ in range(max(1, n_warm)):
+        osdn.osdn_chunk_fwd_states(q, k, v, beta, d, alpha, S0, o=o_buf, S_T=st_buf, states=states)
+        osdn.osdn_chunk_bwd(q, k, v, beta, d, alpha, S0, do, dS_T, grads=grads, workspace=ws,
+                            states=states)
     torch.cuda.synchronize()
     e2 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
