@@ -285,6 +285,19 @@ precond_chunk_kernel(const uint16_t *__restrict__ k, const float *__restrict__ b
             I[h] = t - J[h] * (J[h] + 1) / 2;
             acc[h] = zero4();
         }
+        // the epilogue's operands, read before the products: per column i its norm, beta and
+        // running log-gate sum, per row j (four consecutive rows a lane) beta and the running sum
+        float ni[2], bi[2], lri[2];
+        v4f bj[2], lj[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int i = 16 * I[h] + n;
+            ni[h] = sm.nrm[sl][i];
+            bi[h] = sm.beta[sl][i];
+            lri[h] = sm.lr[sl][i + 1];
+            bj[h] = ld4(&sm.beta[sl][16 * J[h] + 4 * q]);
+            lj[h] = ld4(&sm.lr[sl][16 * J[h] + 4 * q]);
+        }
 #pragma unroll
         for (int st = 0; st < KS; ++st) {
 #pragma unroll
@@ -298,15 +311,12 @@ precond_chunk_kernel(const uint16_t *__restrict__ k, const float *__restrict__ b
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int i = 16 * I[h] + n;
-            const float ni = sm.nrm[sl][i];
-            const float ci = ni > 0.f ? eta * sm.beta[sl][i] / ni : 0.f;
+            const float ci = ni[h] > 0.f ? eta * bi[h] / ni[h] : 0.f;
             if (J[h] == I[h] && q == 0) sm.cc[sl][i] = ci;
-            const float lri = sm.lr[sl][i + 1];
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const int j = 16 * J[h] + 4 * q + m;
-                Lt[j * L::LP + i] =
-                    i < j ? sm.beta[sl][j] * __expf(sm.lr[sl][j] - lri) * ci * acc[h][m] : 0.f;
+                Lt[j * L::LP + i] = i < j ? bj[h][m] * __expf(lj[h][m] - lri[h]) * ci * acc[h][m] : 0.f;
             }
         }
     };
