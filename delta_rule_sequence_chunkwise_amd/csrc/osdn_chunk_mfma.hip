@@ -713,6 +713,29 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                 kr[j][s] = ld8(&kx[L::qk_at(row, 4 * s + lq)]);
                 qd[j][s] = ld8(&qx[L::qk_at(row, 4 * s + lq)]);
             }
+        // the decay factors and gates of every tile of the step, read before the first LDS
+        // write (the compiler cannot move them above it)
+        constexpr int IMIN = (kblk(PW, 0) < kblk(PW, 1) ? kblk(PW, 0) : kblk(PW, 1)) + 1;
+        float hgr[2], hbt[2], hear[NBLK], hnbr[NBLK], hcik[NOFF];
+        v4f hgs[2], heb[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int kb = kblk(PW, j);
+            hgr[j] = sm.g[s1][16 * kb + lr];
+            hbt[j] = sm.beta[s1][16 * kb + lr];
+            hgs[j] = ld4(&sm.g[s1][16 * kb + 4 * lq]);
+            heb[j] = ld4(&sm.eb[s1][16 * kb + 4 * lq]);
+        }
+#pragma unroll
+        for (int i = IMIN; i < NBLK; ++i) {
+            hear[i] = sm.ea[s1][16 * i + lr];
+            hnbr[i] = -sm.beta[s1][16 * i + lr];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int kb = kblk(PW, j);
+                if (kb < i) hcik[(i * (i - 1)) / 2 + kb] = sm.cik[s1][(i * (i - 1)) / 2 + kb];
+            }
+        }
         // diagonal blocks: tile (kb, kb) = K~_kb X_kb^T, the lane holds row r = 16kb+lr,
         // columns s = 16kb+4lq..+3; exact e^{g_r - g_s} shared by the score tile (s <= r)
         // and N (s < r); then both block inverses in lockstep
@@ -727,8 +750,8 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                 sc = mfma32(kt[j][s], qd[j][s], sc);
                 Gdt = mfma32(kt[j][s], kr[j][s], Gdt);  // G in the A layout: lane holds G[r][s]
             }
-            const float gr = sm.g[s1][r], bt = sm.beta[s1][r];
-            const v4f gs = ld4(&sm.g[s1][16 * kb + 4 * lq]);
+            const float gr = hgr[j], bt = hbt[j];
+            const v4f gs = hgs[j];
             v4f pv;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -742,7 +765,6 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
         // off-diagonal tiles (i, kb), i > kb, row block by row block; the fragments of the
         // next row block are read before the current one is processed.  The lane holds row
         // 16i+lr, columns 16kb+4lq..+3; e^{g_r - g_s} = ea[r] cik eb[s], each factor <= 1.
-        constexpr int IMIN = (kblk(PW, 0) < kblk(PW, 1) ? kblk(PW, 0) : kblk(PW, 1)) + 1;
         v8s kf[NS], qf[NS], kf_n[NS], qf_n[NS];
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
@@ -764,7 +786,7 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                 }
             }
             const int r = 16 * i + lr;
-            const float ear = sm.ea[s1][r], nbr = -sm.beta[s1][r];
+            const float ear = hear[i], nbr = hnbr[i];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int kb = kblk(PW, j);
@@ -776,9 +798,9 @@ chunk_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
                     gm = mfma32(kt[j][s], kf[s], gm);
                 }
                 const int t = (i * (i - 1)) / 2 + kb;
-                const float rowf = ear * sm.cik[s1][t];
+                const float rowf = ear * hcik[t];
                 const float growf = nbr * rowf;
-                const v4f eb4 = ld4(&sm.eb[s1][16 * kb + 4 * lq]);
+                const v4f eb4 = heb[j];
                 v4f pv, av;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
