@@ -936,16 +936,28 @@ bwd_chunk_mfma_kernel(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k
     // (this wave's feature tiles; the other half's come through LDS); then they take their row
     // factors gam, -gam b, w for the closing products
     float pgo[4] = {0.f, 0.f, 0.f, 0.f}, pgr[4] = {0.f, 0.f, 0.f, 0.f}, pew[4] = {0.f, 0.f, 0.f, 0.f};
+    // q, k, k~ at this lane's places of the feature tiles (rows R0 + 4 lq + e, column 16 T + lr),
+    // four rows per transposing read
+    v4s qt4[NFH], kt4[NFH], wt4[NFH];
+#pragma unroll
+    for (int t = 0; t < NFH; ++t) {
+        const int off = (R0 + 4 * lq + (lr >> 2)) * PH + 16 * (NFH * hw + t) + 4 * (lr & 3);
+        qt4[t] = ld_tr(&sQ[off]);
+        kt4[t] = ld_tr(&sK[off]);
+        wt4[t] = ld_tr(&sKt[off]);
+    }
+    auto bfe = [](short x) __attribute__((always_inline)) {
+        return __uint_as_float(uint32_t(static_cast<uint16_t>(x)) << 16);
+    };
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int r = R0 + 4 * lq + e;
         const float fq = sgam[r], fk = -sgam[r] * sb[r], fw = sw[r];
 #pragma unroll
         for (int t = 0; t < NFH; ++t) {
-            const int f = 16 * (NFH * hw + t) + lr;
-            pgo[e] += __uint_as_float(uint32_t(sQ[r * PH + f]) << 16) * aQ[t][e];
-            pgr[e] += __uint_as_float(uint32_t(sK[r * PH + f]) << 16) * aK[t][e];
-            pew[e] += __uint_as_float(uint32_t(sKt[r * PH + f]) << 16) * aKt[t][e];
+            pgo[e] += bfe(qt4[t][e]) * aQ[t][e];
+            pgr[e] += bfe(kt4[t][e]) * aK[t][e];
+            pew[e] += bfe(wt4[t][e]) * aKt[t][e];
             aQ[t][e] *= fq;
             aK[t][e] *= fk;
             aKt[t][e] *= fw;
