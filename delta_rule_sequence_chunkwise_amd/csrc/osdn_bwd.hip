@@ -1878,7 +1878,7 @@ bwd_chunk_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
                       TQ *__restrict__ gv, float *__restrict__ gbeta, TD *__restrict__ gd,
                       float *__restrict__ galpha_ch, int64_t T, int64_t nch) {
     constexpr int PX = DK + 1, PC = C + 1, PS = BV + 1;
-    constexpr int TC = C / 16, TK = DK / 16, TV = BV / 16;  // register blocks
+    constexpr int TC = C / 16, TK = DK / 16;  // register blocks
     constexpr int FPT = DK * BV / NT;                        // (f, j) pairs per thread
     static_assert(FPT * NT == DK * BV && NT % BV == 0, "slice layout");
     // raw Q, K, K~; K o G and K~ o W for the slice products (K o G is reused for dLg)
@@ -1930,21 +1930,29 @@ bwd_chunk_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
         sKw[r * PX + f] = sKt[r * PX + f] * __expf(static_cast<float>(lgL - lg));
     }
 
-    float aQ[TC][TK], aK[TC][TK], aKt[TC][TK], adP[TC][TC], adA[TC][TC];
-    zero(aQ);
-    zero(aK);
-    zero(aKt);
-    zero(adP);
-    zero(adA);
+    // The slice products run on the fp32 matrix cores (16x16x4): wave wv, lane (lg, l16).
+    static_assert(C == 32 && BV == 16 && DK % 64 == 0 && NT == 256, "matrix-core slice layout");
+    constexpr int FT = DK / 64;  // feature tiles of dQ, dK', dK~ per wave
+    const int lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // dQ, -dK' (before b), dK~ (before W): row tile x this wave's feature tiles 16 (FT wv + ft);
+    // mS: this wave's tiles of dP, dA (the tile above the diagonal is masked off below, so it is
+    // not formed: wave w takes slots 2w, 2w + 1 of dP(0,0), dP(1,0), dP(1,1), dA(0,0), dA(1,0),
+    // dA(1,1))
+    v4f mQ[2][FT], mK[2][FT], mKt[2][FT], mS[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        mS[rt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft) {
+            mQ[rt][ft] = v4f{0.f, 0.f, 0.f, 0.f};
+            mK[rt][ft] = v4f{0.f, 0.f, 0.f, 0.f};
+            mKt[rt][ft] = v4f{0.f, 0.f, 0.f, 0.f};
+        }
+    }
     float frob[FPT];  // this thread's parts of <dMC[f,:], M0[f,:]>, f = tid / BV + i NT / BV
 #pragma unroll
     for (int i = 0; i < FPT; ++i) frob[i] = 0.f;
-    const int ic = ti * TC, jc = tj * TC;  // C x C block
-    // C x DK block: rows ik.., features tj + 16 nn (the 16 lanes of a row pair read 16
-    // consecutive features, so their LDS reads of a row are free of bank conflicts)
-    const int ik = ti * TC;
-    auto fk = [&](int nn) __attribute__((always_inline)) { return tj + 16 * nn; };
-    const int is = ti * TC, js = tj * TV;  // C x BV block
 
     for (int s0 = 0; s0 < DV; s0 += BV) {
         __syncthreads();  // the previous slice (and the scaled copies) are done
@@ -1962,40 +1970,39 @@ bwd_chunk_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
             sdO[r * PS + j] = r < n ? to_f32(dO[(row0 + r) * DV + s0 + j]) : 0.f;
         }
         __syncthreads();
-        {  // Y = V - (K o G) M0, R = b Y into U;  (K~ o W) dMC into dR (added to below)
-            float a1[TC][TV], a3[TC][TV];
-            zero(a1);
-            zero(a3);
-            mm<TC, TV, DK>(a1, is, js, [&](int i, int kk) { return sKg[i * PX + kk]; },
-                           [&](int kk, int j) { return sM0[kk * PS + j]; });
-            mm<TC, TV, DK>(a3, is, js, [&](int i, int kk) { return sKw[i * PX + kk]; },
-                           [&](int kk, int j) { return sdM[kk * PS + j]; });
+        {  // waves 0, 1: Y = V - (K o G) M0 on row tile wv, R = b Y into U;
+           // waves 2, 3: dU = (K~ o W) dMC + P^T dO on row tile wv - 2, into dR
+            const int rt = wv & 1, ri = 16 * rt + l16;
+            v4f acc = {0.f, 0.f, 0.f, 0.f};
+            if (wv < 2) {
+#pragma unroll 8
+                for (int t = 0; t < DK / 4; ++t)
+                    acc = mfma4f(sKg[ri * PX + 4 * t + lg], sM0[(4 * t + lg) * PS + l16], acc);
+            } else {
+#pragma unroll 8
+                for (int t = 0; t < DK / 4; ++t)
+                    acc = mfma4f(sKw[ri * PX + 4 * t + lg], sdM[(4 * t + lg) * PS + l16], acc);
 #pragma unroll
-            for (int m = 0; m < TC; ++m)
+                for (int t = 0; t < C / 4; ++t)
+                    acc = mfma4f(sP[(4 * t + lg) * PC + ri], sdO[(4 * t + lg) * PS + l16], acc);
+            }
 #pragma unroll
-                for (int nn = 0; nn < TV; ++nn) {
-                    const int r = is + m, j = js + nn;
-                    const float y = sY[r * PS + j] - a1[m][nn];
-                    sY[r * PS + j] = y;
-                    sU[r * PS + j] = sb[r] * y;
-                    sdR[r * PS + j] = a3[m][nn];
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rt + 4 * lg + e;
+                if (wv < 2) {
+                    const float y = sY[r * PS + l16] - acc[e];
+                    sY[r * PS + l16] = y;
+                    sU[r * PS + l16] = sb[r] * y;
+                } else {
+                    sdR[r * PS + l16] = acc[e];
                 }
+            }
         }
         __syncthreads();
-        solve_lower<C, BV, PS, PC>(sU, sAS, sb, tid);  // U = (I + A)^{-1} R
-        __syncthreads();
-        {  // dU = P^T dO + (K~ o W) dMC (the same thread wrote that part of sdR above)
-            float acc[TC][TV];
-            zero(acc);
-            mm<TC, TV, C>(acc, is, js, [&](int i, int kk) { return sP[kk * PC + i]; },
-                          [&](int kk, int j) { return sdO[kk * PS + j]; });
-#pragma unroll
-            for (int m = 0; m < TC; ++m)
-#pragma unroll
-                for (int nn = 0; nn < TV; ++nn) sdR[(is + m) * PS + js + nn] += acc[m][nn];
-        }
-        __syncthreads();
-        solve_upper<C, BV, PS, PC>(sdR, sAS, sb, tid);  // dR = (I + A)^{-T} dU
+        // U = (I + A)^{-1} R and dR = (I + A)^{-T} dU: each reads its own array into registers
+        // first and shares nothing with the other, so one barrier serves both
+        solve_lower<C, BV, PS, PC>(sU, sAS, sb, tid);
+        solve_upper<C, BV, PS, PC>(sdR, sAS, sb, tid);
         __syncthreads();
         for (int idx = tid; idx < C * BV; idx += NT) {
             const int r = idx / BV, j = idx % BV;
@@ -2006,15 +2013,100 @@ bwd_chunk_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
             for (int j = 0; j < BV; ++j) db += sdR[tid * PS + j] * sY[tid * PS + j];
             sdb[tid] += db;
         }
-        auto bu = [&](int kk, int j) { return sU[j * PS + kk]; };
-        mm<TC, TC, BV>(adP, ic, jc, [&](int i, int kk) { return sdO[i * PS + kk]; }, bu);
-        mm<TC, TC, BV>(adA, ic, jc, [&](int i, int kk) { return sdR[i * PS + kk]; }, bu);
-        auto bm0t = [&](int kk, int nn) { return sM0[fk(nn) * PS + kk]; };
-        mm<TC, TK, BV>(aQ, ik, 0, [&](int i, int kk) { return sdO[i * PS + kk]; }, bm0t);
-        mm<TC, TK, BV>(aK, ik, 0, [&](int i, int kk) { return -sdR[i * PS + kk]; }, bm0t);
-        mm<TC, TK, BV>(aKt, ik, 0, [&](int i, int kk) { return sU[i * PS + kk]; },
-                       [&](int kk, int nn) { return sdM[fk(nn) * PS + kk]; });
+        {  // dP += dO U^T, dA += dR U^T, dQ += dO M0^T, dK' -= dR M0^T, dK~ += U dMC^T
+            float fO[2][4], fR[2][4], fU[2][4], fM[FT][4], fD[FT][4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) {
+                    const int o = (16 * rt + l16) * PS + 4 * t + lg;
+                    fO[rt][t] = sdO[o];
+                    fR[rt][t] = sdR[o];
+                    fU[rt][t] = sU[o];
+                }
+#pragma unroll
+                for (int ft = 0; ft < FT; ++ft) {
+                    const int o = (16 * (FT * wv + ft) + l16) * PS + 4 * t + lg;
+                    fM[ft][t] = sM0[o];
+                    fD[ft][t] = sdM[o];
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                    for (int ft = 0; ft < FT; ++ft) {
+                        mQ[rt][ft] = mfma4f(fO[rt][t], fM[ft][t], mQ[rt][ft]);
+                        mK[rt][ft] = mfma4f(fR[rt][t], fM[ft][t], mK[rt][ft]);
+                        mKt[rt][ft] = mfma4f(fU[rt][t], fD[ft][t], mKt[rt][ft]);
+                    }
+#pragma unroll
+            for (int slot = 0; slot < 2; ++slot) {
+                const int sel = 2 * wv + slot;  // wave-uniform
+                if (sel < 6) {
+                    const bool isA = sel >= 3, r1 = sel % 3 != 0, c1 = sel % 3 == 2;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const float a = isA ? (r1 ? fR[1][t] : fR[0][t])
+                                            : (r1 ? fO[1][t] : fO[0][t]);
+                        mS[slot] = mfma4f(a, c1 ? fU[1][t] : fU[0][t], mS[slot]);
+                    }
+                }
+            }
+        }
     }
+    // the matrix-core tiles into the register blocks below, one C x DK (or C x C) product at a
+    // time through the K~ o W rows, which are no longer read
+    const int ic = ti * TC, jc = tj * TC;  // C x C block
+    // C x DK block: rows ik.., features tj + 16 nn (the 16 lanes of a row pair read 16
+    // consecutive features, so their LDS reads of a row are free of bank conflicts)
+    const int ik = ti * TC;
+    auto fk = [&](int nn) __attribute__((always_inline)) { return tj + 16 * nn; };
+    float aQ[TC][TK], aK[TC][TK], aKt[TC][TK], adP[TC][TC], adA[TC][TC];
+    auto spill_ck = [&](const v4f (&m)[2][FT], float sign, float (&out)[TC][TK])
+        __attribute__((always_inline)) {
+        __syncthreads();
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    sKw[(16 * rt + 4 * lg + e) * PX + 16 * (FT * wv + ft) + l16] =
+                        sign * m[rt][ft][e];
+        __syncthreads();
+#pragma unroll
+        for (int m_ = 0; m_ < TC; ++m_)
+#pragma unroll
+            for (int nn = 0; nn < TK; ++nn) out[m_][nn] = sKw[(ik + m_) * PX + fk(nn)];
+    };
+    spill_ck(mQ, 1.f, aQ);
+    spill_ck(mK, -1.f, aK);
+    spill_ck(mKt, 1.f, aKt);
+    auto spill_cc = [&](bool isA, float (&out)[TC][TC]) __attribute__((always_inline)) {
+        __syncthreads();
+#pragma unroll
+        for (int slot = 0; slot < 2; ++slot) {
+            const int sel = 2 * wv + slot;
+            if (sel < 6 && (sel >= 3) == isA) {
+                const int r1 = sel % 3 != 0, c1 = sel % 3 == 2;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    sKw[(16 * r1 + 4 * lg + e) * PC + 16 * c1 + l16] = mS[slot][e];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m_ = 0; m_ < TC; ++m_)
+#pragma unroll
+            for (int nn = 0; nn < TC; ++nn) {
+                // the tile above the diagonal is never written; it is masked off below
+                out[m_][nn] = (ic + m_) / 16 >= (jc + nn) / 16 ? sKw[(ic + m_) * PC + jc + nn] : 0.f;
+            }
+    };
+    spill_cc(false, adP);
+    spill_cc(true, adA);
     // G_L <dMC[f,:], M0[f,:]> per feature: the BV threads of one f are adjacent lanes
 #pragma unroll
     for (int i = 0; i < FPT; ++i) {
