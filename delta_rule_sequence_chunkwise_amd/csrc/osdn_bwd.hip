@@ -144,6 +144,50 @@ __device__ __forceinline__ void solve_upper(float *X, const float *AS, const flo
     for (int i = 0; i < RPT; ++i) X[(i * TPC + sub) * PX + j] = mine[i];
 }
 
+// solve_lower on XL and solve_upper on XU in one pass (the same arithmetic as the two, row r of
+// the first beside row C-1-r of the second), so the two dependent chains overlap
+template <int C, int NC, int PX, int PA>
+__device__ __forceinline__ void solve_both(float *XL, float *XU, const float *AS, const float *b,
+                                           int tid) {
+    constexpr int TPC = NT / NC, RPT = C / TPC;
+    static_assert(TPC * NC == NT && RPT * TPC == C && TPC <= 16, "solve layout");
+    const int j = tid / TPC, sub = tid % TPC;
+    float rl[C], ru[C], ml[RPT], mu[RPT];
+#pragma unroll
+    for (int r = 0; r < C; ++r) {
+        rl[r] = XL[r * PX + j];
+        ru[r] = XU[r * PX + j];
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) ml[i] = mu[i] = 0.f;
+#pragma unroll
+    for (int st = 0; st < C; ++st) {
+        const int r = st, ru_ = C - 1 - st;
+        float pl = 0.f, pu = 0.f;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            if (i * TPC < r) {
+                const int s_ = i * TPC + sub;
+                if (s_ < r) pl += AS[r * PA + s_] * ml[i];
+            }
+            if (i * TPC + TPC - 1 > ru_) {
+                const int s_ = i * TPC + sub;
+                if (s_ > ru_) pu += b[s_] * AS[s_ * PA + ru_] * mu[i];
+            }
+        }
+        pl = group_sum<TPC>(pl);
+        pu = group_sum<TPC>(pu);
+        const float vl = rl[r] - b[r] * pl, vu = ru[ru_] - pu;
+        if (r % TPC == sub) ml[r / TPC] = vl;
+        if (ru_ % TPC == sub) mu[ru_ / TPC] = vu;
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        XL[(i * TPC + sub) * PX + j] = ml[i];
+        XU[(i * TPC + sub) * PX + j] = mu[i];
+    }
+}
+
 // g = running sum of ln(alpha) over the chunk's rows (0 past the end), gam = e^g,
 // w = e^{g_last - g}; beta (0 past the end).  One wave's work (several may write the same values).
 template <int C>
@@ -1604,37 +1648,42 @@ hipError_t bwd_dims(const BwdArgs &a, hipStream_t stream) {
 
 // Q, K, K~ = d (.) k in fp32 and ln a in double (zero rows, and ln a = 0, past the end), in two
 // halves: the loads into registers (every one issued before any is used), then the LDS stores,
-// so that a caller can keep the loads in flight across other work
-template <int C, int DK>
+// so that a caller can keep the loads in flight across other work.  The registers hold the
+// elements as loaded and are widened only when stored: a conversion at the load would make the
+// wave wait for it there.
+template <int C, int DK, typename TQ, typename TD>
 struct QkGateRegs {
     static constexpr int IT = C * DK / NT;
     static_assert(IT * NT == C * DK, "tile layout");
-    float q[IT], k[IT], d[IT], a[IT];
+    TQ q[IT], k[IT];
+    TD d[IT];
+    float a[IT];
 };
 template <int C, int DK, typename TQ, typename TD>
-__device__ __forceinline__ void load_qk_regs(QkGateRegs<C, DK> &x, const TQ *q, const TQ *k,
+__device__ __forceinline__ void load_qk_regs(QkGateRegs<C, DK, TQ, TD> &x, const TQ *q, const TQ *k,
                                              const TD *d, const float *a, int64_t row0, int n,
                                              int tid) {
 #pragma unroll
-    for (int it = 0; it < QkGateRegs<C, DK>::IT; ++it) {
+    for (int it = 0; it < QkGateRegs<C, DK, TQ, TD>::IT; ++it) {
         const int idx = tid + it * NT, r = idx / DK, f = idx % DK;
         const int64_t e = (row0 + (r < n ? r : 0)) * DK + f;
-        x.q[it] = to_f32(q[e]);
-        x.k[it] = to_f32(k[e]);
-        x.d[it] = to_f32(d[e]);
+        x.q[it] = q[e];
+        x.k[it] = k[e];
+        x.d[it] = d[e];
         x.a[it] = a[e];
     }
 }
-template <int C, int DK, int PX>
-__device__ __forceinline__ void store_qk_lds(const QkGateRegs<C, DK> &x, int n, float *sQ,
+template <int C, int DK, int PX, typename TQ, typename TD>
+__device__ __forceinline__ void store_qk_lds(const QkGateRegs<C, DK, TQ, TD> &x, int n, float *sQ,
                                              float *sK, float *sKt, double *sLg, int tid) {
 #pragma unroll
-    for (int it = 0; it < QkGateRegs<C, DK>::IT; ++it) {
+    for (int it = 0; it < QkGateRegs<C, DK, TQ, TD>::IT; ++it) {
         const int idx = tid + it * NT, r = idx / DK, f = idx % DK;
         const bool in = r < n;
-        sQ[r * PX + f] = in ? x.q[it] : 0.f;
-        sK[r * PX + f] = in ? x.k[it] : 0.f;
-        sKt[r * PX + f] = in ? x.d[it] * x.k[it] : 0.f;
+        const float qv = to_f32(x.q[it]), kv = to_f32(x.k[it]);
+        sQ[r * PX + f] = in ? qv : 0.f;
+        sK[r * PX + f] = in ? kv : 0.f;
+        sKt[r * PX + f] = in ? to_f32(x.d[it]) * kv : 0.f;
         sLg[r * PX + f] = in ? log(fmax(static_cast<double>(x.a[it]), 1e-300)) : 0.0;
     }
 }
@@ -1642,7 +1691,7 @@ template <int C, int DK, int PX, typename TQ, typename TD>
 __device__ __forceinline__ void load_qk_gate(const TQ *q, const TQ *k, const TD *d,
                                              const float *a, int64_t row0, int n, float *sQ,
                                              float *sK, float *sKt, double *sLg, int tid) {
-    QkGateRegs<C, DK> x;
+    QkGateRegs<C, DK, TQ, TD> x;
     load_qk_regs<C, DK>(x, q, k, d, a, row0, n, tid);
     store_qk_lds<C, DK, PX>(x, n, sQ, sK, sKt, sLg, tid);
 }
@@ -1754,6 +1803,10 @@ bwd_state_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
     const int j0 = static_cast<int>(blockIdx.x % nvt) * BV;
     const int tid = threadIdx.x;
     const int64_t nch = (T + C - 1) / C;
+    // the products run on the fp32 matrix cores (16x16x4): wave wv, lane (lg, l16)
+    static_assert(C == 32 && BV == 32 && DK % 64 == 0 && NT == 256, "matrix-core layout");
+    const int lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
 
     for (int idx = tid; idx < DK * BV; idx += NT) {
         const int f = idx / BV, j = idx % BV;
@@ -1766,8 +1819,9 @@ bwd_state_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
     static_assert(OIT * NT == C * BV, "dO tile layout");
     constexpr int SIT = C * C / NT;  // score-tile elements per thread
     static_assert(SIT * NT == C * C, "score tile layout");
-    QkGateRegs<C, DK> nx;
-    float ndo[OIT], nas[SIT], np[SIT];
+    QkGateRegs<C, DK, TQ, TD> nx;
+    TQ ndo[OIT];
+    float nas[SIT], np[SIT], nbt = 0.f;
     auto issue = [&](int64_t cc) __attribute__((always_inline)) {
         const int64_t r0 = bh * T + cc * C;
         const int nn = static_cast<int>(T - cc * C < C ? T - cc * C : C);
@@ -1781,8 +1835,9 @@ bwd_state_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
 #pragma unroll
         for (int it = 0; it < OIT; ++it) {
             const int idx = tid + it * NT, r = idx / BV, j = idx % BV;
-            ndo[it] = to_f32(dO[(r0 + (r < nn ? r : 0)) * dv + j0 + j]);
+            ndo[it] = dO[(r0 + (r < nn ? r : 0)) * dv + j0 + j];
         }
+        nbt = tid < nn ? beta[r0 + tid] : 0.f;  // (beta past the end is 0)
     };
     if (nch > 0) issue(nch - 1);
     for (int64_t c = nch - 1; c >= 0; --c) {
@@ -1793,7 +1848,7 @@ bwd_state_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
 #pragma unroll
         for (int it = 0; it < OIT; ++it) {
             const int idx = tid + it * NT, r = idx / BV, j = idx % BV;
-            sdO[r * PS + j] = r < n ? ndo[it] : 0.f;
+            sdO[r * PS + j] = r < n ? to_f32(ndo[it]) : 0.f;
         }
 #pragma unroll
         for (int it = 0; it < SIT; ++it) {
@@ -1801,8 +1856,8 @@ bwd_state_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
             sAS[i * PC + j] = nas[it];
             sP[i * PC + j] = np[it];
         }
+        if (tid < C) sb[tid] = nbt;
         if (c > 0) issue(c - 1);
-        if (tid < C) sb[tid] = tid < n ? beta[row0 + tid] : 0.f;
         for (int idx = tid; idx < DK * BV; idx += NT) {  // the gradient at this chunk's end
             const int f = idx / BV, j = idx % BV;
             dMck[((bh * nch + c) * DK + f) * dv + j0 + j] = sdM[f * PS + j];
@@ -1821,39 +1876,59 @@ bwd_state_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
         }
         if (tid < DK) sGL[tid] = __expf(static_cast<float>(sLg[(C - 1) * PX + tid]));
         block_sync();
-        {  // dU = P^T dO + (K~ o W) dM
-            constexpr int TM = C / 16, TN = BV / 16;
-            const int i0 = (tid / 16) * TM, j0l = (tid % 16) * TN;
-            float acc[TM][TN];
-            zero(acc);
-            mm<TM, TN, DK>(acc, i0, j0l, [&](int i, int kk) { return sKt[i * PX + kk]; },
-                           [&](int kk, int j) { return sdM[kk * PS + j]; });
-            mm<TM, TN, C>(acc, i0, j0l, [&](int i, int kk) { return sP[kk * PC + i]; },
-                          [&](int kk, int j) { return sdO[kk * PS + j]; });
+        {  // dU = (K~ o W) dM + P^T dO on the fp32 matrix cores: wave wv takes tile (wv / 2, wv % 2)
+            const int ri = 16 * (wv >> 1) + l16, cj = 16 * (wv & 1) + l16;
+            v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+            for (int t = 0; t < DK / 4; ++t)
+                acc = mfma4f(sKt[ri * PX + 4 * t + lg], sdM[(4 * t + lg) * PS + cj], acc);
 #pragma unroll
-            for (int m = 0; m < TM; ++m)
+            for (int t = 0; t < C / 4; ++t)
+                acc = mfma4f(sP[(4 * t + lg) * PC + ri], sdO[(4 * t + lg) * PS + cj], acc);
 #pragma unroll
-                for (int nn = 0; nn < TN; ++nn) sX[(i0 + m) * PS + j0l + nn] = acc[m][nn];
+            for (int e = 0; e < 4; ++e) sX[(16 * (wv >> 1) + 4 * lg + e) * PS + cj] = acc[e];
         }
         block_sync();
         solve_upper<C, BV, PS, PC>(sX, sAS, sb, tid);  // dR
         block_sync();
-        {  // dM <- Diag(G_L) dM + (Q o G)^T dO - (K o G)^T diag(b) dR
-            constexpr int TM = DK / 16, TN = BV / 16;
-            const int i0 = (tid / 16) * TM, j0l = (tid % 16) * TN;
-            float acc[TM][TN];
-            zero(acc);
-            mm<TM, TN, C>(acc, i0, j0l, [&](int f, int r) { return sQ[r * PX + f]; },
-                          [&](int r, int j) { return sdO[r * PS + j]; });
-            mm<TM, TN, C>(acc, i0, j0l, [&](int f, int r) { return sK[r * PX + f]; },
-                          [&](int r, int j) { return -sb[r] * sX[r * PS + j]; });
+        {  // dM <- Diag(G_L) dM + (Q o G)^T dO - (K o G)^T diag(b) dR on the fp32 matrix cores:
+           // wave wv takes feature tiles FW wv .. FW wv + FW - 1 and both column tiles
+            constexpr int FW = DK / 64;
+            v4f acc[FW][2];
 #pragma unroll
-            for (int m = 0; m < TM; ++m)
+            for (int ft = 0; ft < FW; ++ft) acc[ft][0] = acc[ft][1] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int nn = 0; nn < TN; ++nn) {
-                    float &x = sdM[(i0 + m) * PS + j0l + nn];
-                    x = sGL[i0 + m] * x + acc[m][nn];
+            for (int t = 0; t < C / 4; ++t) {
+                const int r = 4 * t + lg;
+                const float b0 = sdO[r * PS + l16], b1 = sdO[r * PS + 16 + l16];
+#pragma unroll
+                for (int ft = 0; ft < FW; ++ft) {
+                    const float a = sQ[r * PX + 16 * (FW * wv + ft) + l16];
+                    acc[ft][0] = mfma4f(a, b0, acc[ft][0]);
+                    acc[ft][1] = mfma4f(a, b1, acc[ft][1]);
                 }
+            }
+#pragma unroll
+            for (int t = 0; t < C / 4; ++t) {
+                const int r = 4 * t + lg;
+                const float b0 = -sb[r] * sX[r * PS + l16], b1 = -sb[r] * sX[r * PS + 16 + l16];
+#pragma unroll
+                for (int ft = 0; ft < FW; ++ft) {
+                    const float a = sK[r * PX + 16 * (FW * wv + ft) + l16];
+                    acc[ft][0] = mfma4f(a, b0, acc[ft][0]);
+                    acc[ft][1] = mfma4f(a, b1, acc[ft][1]);
+                }
+            }
+#pragma unroll
+            for (int ft = 0; ft < FW; ++ft)
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int f = 16 * (FW * wv + ft) + 4 * lg + e;
+                        float &x = sdM[f * PS + 16 * ct + l16];
+                        x = sGL[f] * x + acc[ft][ct][e];
+                    }
         }
     }
     block_sync();
@@ -1920,9 +1995,9 @@ bwd_chunk_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
         sb[tid] = tid < n ? beta[row0 + tid] : 0.f;
         sdb[tid] = 0.f;
     }
-    __syncthreads();
+    block_sync();
     gate_scan<C, DK, PX>(sLg, tid);
-    __syncthreads();
+    block_sync();
     for (int idx = tid; idx < C * DK; idx += NT) {
         const int r = idx / DK, f = idx % DK;
         const double lg = sLg[r * PX + f], lgL = sLg[(C - 1) * PX + f];
@@ -1953,23 +2028,47 @@ bwd_chunk_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
     float frob[FPT];  // this thread's parts of <dMC[f,:], M0[f,:]>, f = tid / BV + i NT / BV
 #pragma unroll
     for (int i = 0; i < FPT; ++i) frob[i] = 0.f;
-
-    for (int s0 = 0; s0 < DV; s0 += BV) {
-        __syncthreads();  // the previous slice (and the scaled copies) are done
+    // the next slice's inputs are loaded into registers while the current one is processed (as
+    // loaded: a conversion would wait for them); the barriers wait for LDS only, since the kernel
+    // reads back none of its global writes
+    constexpr int YIT = C * BV / NT;
+    static_assert(YIT * NT == C * BV, "slice tile layout");
+    float pm0[FPT], pdm[FPT];
+    TQ pv[YIT], pdo[YIT];
+    auto fetch = [&](int s0) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < FPT; ++i) {
             const int idx = tid + i * NT, f = idx / BV, j = idx % BV;
-            const float m0 = M0[f * DV + s0 + j], dm = dMC[f * DV + s0 + j];
-            sM0[f * PS + j] = m0;
-            sdM[f * PS + j] = dm;
-            frob[i] += m0 * dm;
+            pm0[i] = M0[f * DV + s0 + j];
+            pdm[i] = dMC[f * DV + s0 + j];
         }
-        for (int idx = tid; idx < C * BV; idx += NT) {
-            const int r = idx / BV, j = idx % BV;
-            sY[r * PS + j] = r < n ? to_f32(v[(row0 + r) * DV + s0 + j]) : 0.f;
-            sdO[r * PS + j] = r < n ? to_f32(dO[(row0 + r) * DV + s0 + j]) : 0.f;
+#pragma unroll
+        for (int i = 0; i < YIT; ++i) {
+            const int idx = tid + i * NT, r = idx / BV, j = idx % BV;
+            const int64_t e = (row0 + (r < n ? r : 0)) * DV + s0 + j;
+            pv[i] = v[e];
+            pdo[i] = dO[e];
         }
-        __syncthreads();
+    };
+    fetch(0);
+
+    for (int s0 = 0; s0 < DV; s0 += BV) {
+        block_sync();  // the previous slice (and the scaled copies) are done
+#pragma unroll
+        for (int i = 0; i < FPT; ++i) {
+            const int idx = tid + i * NT, f = idx / BV, j = idx % BV;
+            sM0[f * PS + j] = pm0[i];
+            sdM[f * PS + j] = pdm[i];
+            frob[i] += pm0[i] * pdm[i];
+        }
+#pragma unroll
+        for (int i = 0; i < YIT; ++i) {
+            const int idx = tid + i * NT, r = idx / BV, j = idx % BV;
+            sY[r * PS + j] = r < n ? to_f32(pv[i]) : 0.f;
+            sdO[r * PS + j] = r < n ? to_f32(pdo[i]) : 0.f;
+        }
+        if (s0 + BV < DV) fetch(s0 + BV);
+        block_sync();
         {  // waves 0, 1: Y = V - (K o G) M0 on row tile wv, R = b Y into U;
            // waves 2, 3: dU = (K~ o W) dMC + P^T dO on row tile wv - 2, into dR
             const int rt = wv & 1, ri = 16 * rt + l16;
@@ -1998,12 +2097,10 @@ bwd_chunk_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
                 }
             }
         }
-        __syncthreads();
-        // U = (I + A)^{-1} R and dR = (I + A)^{-T} dU: each reads its own array into registers
-        // first and shares nothing with the other, so one barrier serves both
-        solve_lower<C, BV, PS, PC>(sU, sAS, sb, tid);
-        solve_upper<C, BV, PS, PC>(sdR, sAS, sb, tid);
-        __syncthreads();
+        block_sync();
+        // U = (I + A)^{-1} R and dR = (I + A)^{-T} dU, side by side
+        solve_both<C, BV, PS, PC>(sU, sdR, sAS, sb, tid);
+        block_sync();
         for (int idx = tid; idx < C * BV; idx += NT) {
             const int r = idx / BV, j = idx % BV;
             if (r < n) gv[(row0 + r) * DV + s0 + j] = from_f32<TQ>(sb[r] * sdR[r * PS + j]);
@@ -2066,7 +2163,7 @@ bwd_chunk_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
     float aQ[TC][TK], aK[TC][TK], aKt[TC][TK], adP[TC][TC], adA[TC][TC];
     auto spill_ck = [&](const v4f (&m)[2][FT], float sign, float (&out)[TC][TK])
         __attribute__((always_inline)) {
-        __syncthreads();
+        block_sync();
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -2075,7 +2172,7 @@ bwd_chunk_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
                 for (int e = 0; e < 4; ++e)
                     sKw[(16 * rt + 4 * lg + e) * PX + 16 * (FT * wv + ft) + l16] =
                         sign * m[rt][ft][e];
-        __syncthreads();
+        block_sync();
 #pragma unroll
         for (int m_ = 0; m_ < TC; ++m_)
 #pragma unroll
@@ -2085,7 +2182,7 @@ bwd_chunk_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
     spill_ck(mK, -1.f, aK);
     spill_ck(mKt, 1.f, aKt);
     auto spill_cc = [&](bool isA, float (&out)[TC][TC]) __attribute__((always_inline)) {
-        __syncthreads();
+        block_sync();
 #pragma unroll
         for (int slot = 0; slot < 2; ++slot) {
             const int sel = 2 * wv + slot;
@@ -2096,7 +2193,7 @@ bwd_chunk_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
                     sKw[(16 * r1 + 4 * lg + e) * PC + 16 * c1 + l16] = mS[slot][e];
             }
         }
-        __syncthreads();
+        block_sync();
 #pragma unroll
         for (int m_ = 0; m_ < TC; ++m_)
 #pragma unroll
@@ -2107,6 +2204,12 @@ bwd_chunk_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
     };
     spill_cc(false, adP);
     spill_cc(true, adA);
+    // the gates for d ln a / a at the end, loaded now so that the loads are done by then
+    float ra[C];
+    if (tid < DK && galpha_ch) {
+#pragma unroll
+        for (int r = 0; r < C; ++r) ra[r] = alpha_ch[(row0 + (r < n ? r : 0)) * DK + tid];
+    }
     // G_L <dMC[f,:], M0[f,:]> per feature: the BV threads of one f are adjacent lanes
 #pragma unroll
     for (int i = 0; i < FPT; ++i) {
@@ -2132,7 +2235,7 @@ bwd_chunk_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
 #pragma unroll
             for (int w = 1; w < 16; w <<= 1) rowb[m] += __shfl_xor(rowb[m], w);
         }
-        __syncthreads();  // every slice product and every read of AS is done
+        block_sync();  // every slice product and every read of AS is done
         if (tj == 0) {
 #pragma unroll
             for (int m = 0; m < TC; ++m) sdb[ic + m] += rowb[m];
@@ -2168,7 +2271,7 @@ bwd_chunk_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
 #pragma unroll
         for (int nn = 0; nn < TK; ++nn) colpart[ti * DK + fk(nn)] = colk[nn];
     }
-    __syncthreads();
+    block_sync();
     if (tid < DK) {
         float s = 0.f;
         for (int t = 0; t < 16; ++t) s += colpart[t * DK + tid];
@@ -2252,13 +2355,15 @@ bwd_chunk_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
             }
         }
     }
-    __syncthreads();
+    block_sync();
     if (tid < DK && galpha_ch) {  // d ln a_t = sum_{r >= t} dLg[r]; the last row's term at n-1
         float acc = sLast[tid];
-        for (int r = n - 1; r >= 0; --r) {
-            acc += sKg[r * PX + tid];
-            const int64_t e = (row0 + r) * DK + tid;
-            galpha_ch[e] = acc / alpha_ch[e];
+#pragma unroll
+        for (int r = C - 1; r >= 0; --r) {
+            if (r < n) {
+                acc += sKg[r * PX + tid];
+                galpha_ch[(row0 + r) * DK + tid] = acc / ra[r];
+            }
         }
     }
     if (tid < n) gbeta[row0 + tid] = sdb[tid];
