@@ -133,11 +133,15 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
     // are loaded into registers while the current chunk is processed.  The barriers wait for
     // LDS only (the kernel reads back none of its global writes), so those loads stay in flight
     // across them.  Rows past the end re-read the chunk's last row and are zeroed on the way in.
-    // Score tiles given (GATE): the next chunk's AS and P come with them.
+    // Score tiles given (GATE): the next chunk's AS and P come with them.  The registers hold the
+    // elements as loaded and are widened only when stored: a conversion at the load would make
+    // the wave wait for it there.
     constexpr int LIT = CH * DK / kThreads, VIT = CH * BV / kThreads;
     constexpr int SIT = (CH * CH + kThreads - 1) / kThreads;
     static_assert(LIT * kThreads == CH * DK && VIT * kThreads == CH * BV, "prefetch layout");
-    float nk[LIT], nd[LIT], nq[GATE ? LIT : 1], na[GATE ? LIT : 1], nv[VIT], nb = 0.f, nal = 0.f;
+    TQ nk[LIT], nq[GATE ? LIT : 1], nv[VIT];
+    TD nd[LIT];
+    float na[GATE ? LIT : 1], nb = 0.f, nal = 0.f;
     float nsa[GATE ? SIT : 1], nsp[GATE ? SIT : 1];
     const int64_t nchunks = (T + CH - 1) / CH;
     auto issue = [&](int64_t cn) __attribute__((always_inline)) {
@@ -160,17 +164,17 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
         for (int it = 0; it < LIT; ++it) {
             const int idx = tid + it * kThreads, r = idx / DK, i = idx % DK;
             const int64_t e = (r0 + (r < nn ? r : nn - 1)) * DK + i;
-            nk[it] = to_f32(k[e]);
-            nd[it] = to_f32(d[e]);
+            nk[it] = k[e];
+            nd[it] = d[e];
             if constexpr (GATE) {
-                nq[it] = to_f32(q[e]);
+                nq[it] = q[e];
                 na[it] = alpha[e];
             }
         }
 #pragma unroll
         for (int it = 0; it < VIT; ++it) {
             const int idx = tid + it * kThreads, r = idx / BV, j = idx % BV;
-            nv[it] = to_f32(v[(r0 + (r < nn ? r : nn - 1)) * dv + j0 + j]);
+            nv[it] = v[(r0 + (r < nn ? r : nn - 1)) * dv + j0 + j];
         }
         if (tid < nn) {
             nb = beta[r0 + tid];
@@ -196,17 +200,18 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
         for (int it = 0; it < LIT; ++it) {
             const int idx = tid + it * kThreads, r = idx / DK, i = idx % DK;
             const bool in = r < n;
-            sX[r * PX + i] = in ? nk[it] : 0.f;
-            sKt[r * PX + i] = in ? nd[it] * nk[it] : 0.f;
+            const float kv = to_f32(nk[it]);
+            sX[r * PX + i] = in ? kv : 0.f;
+            sKt[r * PX + i] = in ? to_f32(nd[it]) * kv : 0.f;
             if constexpr (GATE) {
-                sQ[r * PX + i] = in ? nq[it] : 0.f;
+                sQ[r * PX + i] = in ? to_f32(nq[it]) : 0.f;
                 sLg[r * PX + i] = in ? log(fmax(static_cast<double>(na[it]), 1e-300)) : 0.0;
             }
         }
 #pragma unroll
         for (int it = 0; it < VIT; ++it) {
             const int idx = tid + it * kThreads, r = idx / BV, j = idx % BV;
-            sR[r * PV + j] = r < n ? nv[it] : 0.f;
+            sR[r * PV + j] = r < n ? to_f32(nv[it]) : 0.f;
         }
         if (tid < CH) {
             sb[tid] = tid < n ? nb : 0.f;
@@ -224,7 +229,20 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
                 }
             }
         }
-        if (c0 + CH < T) issue(c0 + CH);
+        // without GATE, this chunk's q (staged over K in a4), issued before the next chunk's
+        // loads so that the wait for it there covers these alone
+        TQ cq[GATE ? 1 : LIT];
+        if constexpr (!GATE) {
+#pragma unroll
+            for (int it = 0; it < LIT; ++it) {
+                const int idx = tid + it * kThreads, r = idx / DK, i = idx % DK;
+                cq[it] = q[(row0 + (r < n ? r : n - 1)) * DK + i];
+            }
+            asm volatile("" ::: "memory");  // keeps the next chunk's loads after these
+        }
+        // (on the last chunk it loads that chunk again, unused: with the issue unconditional, the
+        // waits for q above count these loads as issued after it on every path)
+        issue(c0 + CH < T ? c0 + CH : c0);
         if constexpr (GATE) {
             block_sync();
             if (tid < DK) {  // running sums down each feature column
@@ -355,9 +373,10 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
 
             // a4: U = (I + A)^{-1} R in place; then stage Q over K (K is no longer read)
             solve_unit_lower<CH, BV, PV, PC>(sR, sA, tid);
-            for (int idx = tid; idx < CH * DK; idx += kThreads) {
-                const int r = idx / DK, i = idx % DK;
-                sX[r * PX + i] = r < n ? to_f32(q[(row0 + r) * DK + i]) : 0.f;
+#pragma unroll
+            for (int it = 0; it < LIT; ++it) {
+                const int idx = tid + it * kThreads, r = idx / DK, i = idx % DK;
+                sX[r * PX + i] = r < n ? to_f32(cq[it]) : 0.f;
             }
             block_sync();
 
