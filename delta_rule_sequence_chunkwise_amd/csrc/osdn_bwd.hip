@@ -48,6 +48,14 @@ namespace {
 
 constexpr int NT = 256;  // threads per workgroup
 
+// fp32 16x16x4 on the matrix cores: lane (g, i) = (lane / 16, lane % 16) gives A[i][g] and
+// B[g][i]; the result's lane (g, j) holds rows 4g .. 4g + 3 of column j, as in the bf16 forms.
+// Its four products are added in k order, fused, so a product split 4 k at a time this way sums
+// in the same order as a plain multiply-add loop over k.
+__device__ __forceinline__ v4f mfma4f(float a, float b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F &&f) {
     if constexpr (B < E) {

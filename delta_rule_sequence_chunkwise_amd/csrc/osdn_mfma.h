@@ -29,11 +29,6 @@ __device__ __forceinline__ v4f mfma32(v8s a, v8s b, v4f c) {
 __device__ __forceinline__ v4f mfma16(v4s a, v4s b, v4f c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
-// fp32 16x16x4: lane (g, i) = (lane / 16, lane % 16) gives A[i][g] and B[g][i]; the result's
-// lane (g, j) holds rows 4g .. 4g + 3 of column j, as in the bf16 forms
-__device__ __forceinline__ v4f mfma4f(float a, float b, v4f c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
 __device__ __forceinline__ uint32_t pack2(float a, float b) {  // one v_cvt_pk_bf16_f32
     bf16x2_t r = {(__bf16)a, (__bf16)b};
     return __builtin_bit_cast(uint32_t, r);
