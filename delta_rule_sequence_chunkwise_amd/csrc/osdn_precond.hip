@@ -83,10 +83,11 @@ precond_serial_kernel(const TK *__restrict__ k, const float *__restrict__ beta,
     const float *rr = r ? r + bh * T : nullptr;
     TD *orow = d_out ? d_out + bh * T * DK + f0 : nullptr;
 
-    float kn[FPL], bn = 0.f, rn = 1.f;
+    TK kn[FPL];  // the next token's key as loaded (widened at its use, not at the load)
+    float bn = 0.f, rn = 1.f;
     if (T > 0) {
 #pragma unroll
-        for (int i = 0; i < FPL; ++i) kn[i] = to_f32(kr[i]);
+        for (int i = 0; i < FPL; ++i) kn[i] = kr[i];
         bn = br[0];
         rn = rr ? rr[0] : 1.f;
     }
@@ -94,10 +95,10 @@ precond_serial_kernel(const TK *__restrict__ k, const float *__restrict__ beta,
         float x[FPL];
         const float bc = bn, rc = rn;
 #pragma unroll
-        for (int i = 0; i < FPL; ++i) x[i] = kn[i] * kn[i];
+        for (int i = 0; i < FPL; ++i) x[i] = to_f32(kn[i]) * to_f32(kn[i]);
         if (t + 1 < T) {  // next token's loads are in flight while this one's reductions run
 #pragma unroll
-            for (int i = 0; i < FPL; ++i) kn[i] = to_f32(kr[(t + 1) * DK + i]);
+            for (int i = 0; i < FPL; ++i) kn[i] = kr[(t + 1) * DK + i];
             bn = br[t + 1];
             rn = rr ? rr[t + 1] : 1.f;
         }
