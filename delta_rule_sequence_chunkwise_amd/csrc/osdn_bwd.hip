@@ -152,50 +152,6 @@ __device__ __forceinline__ void solve_upper(float *X, const float *AS, const flo
     for (int i = 0; i < RPT; ++i) X[(i * TPC + sub) * PX + j] = mine[i];
 }
 
-// solve_lower on XL and solve_upper on XU in one pass (the same arithmetic as the two, row r of
-// the first beside row C-1-r of the second), so the two dependent chains overlap
-template <int C, int NC, int PX, int PA>
-__device__ __forceinline__ void solve_both(float *XL, float *XU, const float *AS, const float *b,
-                                           int tid) {
-    constexpr int TPC = NT / NC, RPT = C / TPC;
-    static_assert(TPC * NC == NT && RPT * TPC == C && TPC <= 16, "solve layout");
-    const int j = tid / TPC, sub = tid % TPC;
-    float rl[C], ru[C], ml[RPT], mu[RPT];
-#pragma unroll
-    for (int r = 0; r < C; ++r) {
-        rl[r] = XL[r * PX + j];
-        ru[r] = XU[r * PX + j];
-    }
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) ml[i] = mu[i] = 0.f;
-#pragma unroll
-    for (int st = 0; st < C; ++st) {
-        const int r = st, ru_ = C - 1 - st;
-        float pl = 0.f, pu = 0.f;
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            if (i * TPC < r) {
-                const int s_ = i * TPC + sub;
-                if (s_ < r) pl += AS[r * PA + s_] * ml[i];
-            }
-            if (i * TPC + TPC - 1 > ru_) {
-                const int s_ = i * TPC + sub;
-                if (s_ > ru_) pu += b[s_] * AS[s_ * PA + ru_] * mu[i];
-            }
-        }
-        pl = group_sum<TPC>(pl);
-        pu = group_sum<TPC>(pu);
-        const float vl = rl[r] - b[r] * pl, vu = ru[ru_] - pu;
-        if (r % TPC == sub) ml[r / TPC] = vl;
-        if (ru_ % TPC == sub) mu[ru_ / TPC] = vu;
-    }
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        XL[(i * TPC + sub) * PX + j] = ml[i];
-        XU[(i * TPC + sub) * PX + j] = mu[i];
-    }
-}
-
 // g = running sum of ln(alpha) over the chunk's rows (0 past the end), gam = e^g,
 // w = e^{g_last - g}; beta (0 past the end).  One wave's work (several may write the same values).
 template <int C>
@@ -1849,7 +1805,7 @@ bwd_state_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
     };
     if (nch > 0) issue(nch - 1);
     for (int64_t c = nch - 1; c >= 0; --c) {
-        const int64_t c0 = c * C, row0 = bh * T + c0;
+        const int64_t c0 = c * C;
         const int n = static_cast<int>(T - c0 < C ? T - c0 : C);
         block_sync();  // the previous chunk is done with every buffer
         store_qk_lds<C, DK, PX>(nx, n, sQ, sK, sKt, sLg, tid);
@@ -1971,6 +1927,7 @@ bwd_chunk_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
     __shared__ float sM0[DK * PS], sdM[DK * PS];
     __shared__ float sY[C * PS], sdO[C * PS], sU[C * PS], sdR[C * PS];
     __shared__ float sb[C], sdb[C], sLast[DK];
+    __shared__ float sT[C * PC];  // T = (I + A)^{-1}, formed once for every slice's two solves
 
     const int64_t bh = blockIdx.x / nch, c = blockIdx.x % nch;
     const int64_t c0 = c * C, row0 = bh * T + c0;
@@ -2003,8 +1960,11 @@ bwd_chunk_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
         sb[tid] = tid < n ? beta[row0 + tid] : 0.f;
         sdb[tid] = 0.f;
     }
+    for (int idx = tid; idx < C * C; idx += NT) sT[(idx / C) * PC + idx % C] = idx / C == idx % C;
     block_sync();
     gate_scan<C, DK, PX>(sLg, tid);
+    // T = (I + A)^{-1}: the forward substitution on the identity's columns (A = diag(b) AS)
+    solve_lower<C, C, PC, PC>(sT, sAS, sb, tid);
     block_sync();
     for (int idx = tid; idx < C * DK; idx += NT) {
         const int r = idx / DK, f = idx % DK;
@@ -2106,8 +2066,23 @@ bwd_chunk_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
             }
         }
         block_sync();
-        // U = (I + A)^{-1} R and dR = (I + A)^{-T} dU, side by side
-        solve_both<C, BV, PS, PC>(sU, sdR, sAS, sb, tid);
+        {  // waves 0, 1: U = T R on row tile wv; waves 2, 3: dR = T^T dU on row tile wv - 2
+            const int rt = wv & 1, ri = 16 * rt + l16;
+            v4f acc = {0.f, 0.f, 0.f, 0.f};
+            if (wv < 2) {
+#pragma unroll
+                for (int t = 0; t < C / 4; ++t)
+                    acc = mfma4f(sT[ri * PC + 4 * t + lg], sU[(4 * t + lg) * PS + l16], acc);
+            } else {
+#pragma unroll
+                for (int t = 0; t < C / 4; ++t)
+                    acc = mfma4f(sT[(4 * t + lg) * PC + ri], sdR[(4 * t + lg) * PS + l16], acc);
+            }
+            block_sync();  // every wave has read R and dU
+            float *dst = wv < 2 ? sU : sdR;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[(16 * rt + 4 * lg + e) * PS + l16] = acc[e];
+        }
         block_sync();
         for (int idx = tid; idx < C * BV; idx += NT) {
             const int r = idx / BV, j = idx % BV;
