@@ -1660,13 +1660,18 @@ __device__ __forceinline__ void load_qk_gate(const TQ *q, const TQ *k, const TD 
     store_qk_lds<C, DK, PX>(x, n, sQ, sK, sKt, sLg, tid);
 }
 
-// ln a -> its running sum down each feature column (the threads of the first DK lanes)
+// ln a -> its running sum down each feature column (the threads of the first DK lanes); the
+// column is read whole before the sums, so the reads do not wait on one another
 template <int C, int DK, int PX>
 __device__ __forceinline__ void gate_scan(double *sLg, int tid) {
     if (tid < DK) {
+        double x[C];
+#pragma unroll
+        for (int r = 0; r < C; ++r) x[r] = sLg[r * PX + tid];
         double acc = 0.0;
+#pragma unroll
         for (int r = 0; r < C; ++r) {
-            acc += sLg[r * PX + tid];
+            acc += x[r];
             sLg[r * PX + tid] = acc;
         }
     }
@@ -1822,16 +1827,18 @@ bwd_state_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
         }
         if (tid < C) sb[tid] = nbt;
         if (c > 0) issue(c - 1);
-        for (int idx = tid; idx < DK * BV; idx += NT) {  // the gradient at this chunk's end
-            const int f = idx / BV, j = idx % BV;
+#pragma unroll
+        for (int it = 0; it < DK * BV / NT; ++it) {  // the gradient at this chunk's end
+            const int idx = tid + it * NT, f = idx / BV, j = idx % BV;
             dMck[((bh * nch + c) * DK + f) * dv + j0 + j] = sdM[f * PS + j];
         }
         block_sync();
         gate_scan<C, DK, PX>(sLg, tid);
         block_sync();
         // in place: Q o G, K o G, K~ o W; and G_L
-        for (int idx = tid; idx < C * DK; idx += NT) {
-            const int r = idx / DK, f = idx % DK;
+#pragma unroll
+        for (int it = 0; it < C * DK / NT; ++it) {
+            const int idx = tid + it * NT, r = idx / DK, f = idx % DK;
             const double lg = sLg[r * PX + f], lgL = sLg[(C - 1) * PX + f];
             const float g = __expf(static_cast<float>(lg));
             sQ[r * PX + f] *= g;
@@ -1966,8 +1973,9 @@ bwd_chunk_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
     // T = (I + A)^{-1}: the forward substitution on the identity's columns (A = diag(b) AS)
     solve_lower<C, C, PC, PC>(sT, sAS, sb, tid);
     block_sync();
-    for (int idx = tid; idx < C * DK; idx += NT) {
-        const int r = idx / DK, f = idx % DK;
+#pragma unroll
+    for (int it = 0; it < C * DK / NT; ++it) {
+        const int idx = tid + it * NT, r = idx / DK, f = idx % DK;
         const double lg = sLg[r * PX + f], lgL = sLg[(C - 1) * PX + f];
         sKg[r * PX + f] = sK[r * PX + f] * __expf(static_cast<float>(lg));
         sKw[r * PX + f] = sKt[r * PX + f] * __expf(static_cast<float>(lgL - lg));

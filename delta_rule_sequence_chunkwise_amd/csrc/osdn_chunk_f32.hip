@@ -189,9 +189,10 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
         block_sync();  // the previous chunk is done with every buffer
         if (ckpt) {  // the state at this chunk's start, for the backward
             const int64_t cc = bh * ((T + CH - 1) / CH) + c0 / CH;
-            for (int idx = tid; idx < DK * BV; idx += kThreads) {
-                const int i = idx / BV, j = idx % BV;
-                ckpt[(cc * DK + i) * dv + j0 + j] = sM[i * PV + j];
+#pragma unroll
+            for (int it = 0; it < (DK * BV + kThreads - 1) / kThreads; ++it) {
+                const int idx = tid + it * kThreads, i = idx / BV, j = idx % BV;
+                if (idx < DK * BV) ckpt[(cc * DK + i) * dv + j0 + j] = sM[i * PV + j];
             }
         }
 
@@ -245,10 +246,14 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
         issue(c0 + CH < T ? c0 + CH : c0);
         if constexpr (GATE) {
             block_sync();
-            if (tid < DK) {  // running sums down each feature column
+            if (tid < DK) {  // running sums down each feature column (read whole first)
+                double x[CH];
+#pragma unroll
+                for (int r = 0; r < CH; ++r) x[r] = sLg[r * PX + tid];
                 double acc = 0.0;
+#pragma unroll
                 for (int r = 0; r < CH; ++r) {
-                    acc += sLg[r * PX + tid];
+                    acc += x[r];
                     sLg[r * PX + tid] = acc;
                 }
             }
@@ -301,8 +306,9 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
             }
             block_sync();
             // in place, once per element: K o G, Q o G, K~ o e^{Lg_C - Lg}
-            for (int idx = tid; idx < CH * DK; idx += kThreads) {
-                const int r = idx / DK, i = idx % DK;
+#pragma unroll
+            for (int it = 0; it < CH * DK / kThreads; ++it) {
+                const int idx = tid + it * kThreads, r = idx / DK, i = idx % DK;
                 const double lg = sLg[r * PX + i];
                 const float g = __expf(static_cast<float>(lg));
                 sX[r * PX + i] *= g;
