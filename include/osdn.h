@@ -295,12 +295,12 @@ osdn_status osdn_chunk_bwd_states(const void *q, const void *k, const void *v,
  *                   the state gradient at every chunk end, [B,H,nchunks,dk,dv] fp32 each, then
  *                   every chunk's gated score tiles, [B,H,nchunks,2,32,32] fp32
  *   every other argument   as for osdn_chunk_bwd (there is no scalar alpha here)
- * Every product is fp32 on the vector ALUs, for either input type, with 32-row chunks; the
- * per-feature decays inside the chunk's score products are e to differences of running sums of
- * ln a kept in double precision, so every factor is at most 1.  Four kernels run on `stream`:
- * the fp32 forward with the gate recording the state at every chunk start, the score tiles of
- * every chunk (in parallel), a reverse pass over chunks for the state gradient, and the
- * per-chunk gradients.
+ * All arithmetic is fp32 for either input type, with 32-row chunks (the products of the two
+ * gradient passes on the fp32 matrix cores, the rest on the vector ALUs); the per-feature decays
+ * inside the chunk's score products are e to differences of running sums of ln a kept in double
+ * precision, so every factor is at most 1.  Four kernels run on `stream`: the score tiles of
+ * every chunk (in parallel), the fp32 forward with the gate recording the state at every chunk
+ * start, a reverse pass over chunks for the state gradient, and the per-chunk gradients.
  */
 int64_t osdn_chunk_bwd_kda_workspace(int64_t B, int64_t H, int64_t T, int32_t dk, int32_t dv,
                                      osdn_dtype qkv); /* -1 if invalid */
