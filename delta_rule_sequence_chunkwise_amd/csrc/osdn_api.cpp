@@ -678,8 +678,8 @@ int64_t bwd_gate_ckpt_bytes(int64_t B, int64_t H, int64_t T, int32_t dk, int32_t
 // bytes of the channel-wise gate backward's score tiles AS and P of every chunk,
 // [BH, nchunks, 2, C, C] fp32 (valid sizes assumed: checked by bwd_gate_ckpt_bytes)
 int64_t bwd_gate_score_bytes(int64_t B, int64_t H, int64_t T) {
-    return round256(B * H * ((T + kGateBwdChunk - 1) / kGateBwdChunk) * 2 * kGateBwdChunk *
-                    kGateBwdChunk * 4);
+    return round256(B * H * ((T + kGateBwdChunk - 1) / kGateBwdChunk) * 3 * kGateBwdChunk *
+                    kGateBwdChunk * 4);  // AS, P and T of every chunk
 }
 
 }  // namespace

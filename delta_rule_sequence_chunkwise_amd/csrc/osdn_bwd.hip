@@ -47,6 +47,8 @@ namespace osdn {
 namespace {
 
 constexpr int NT = 256;  // threads per workgroup
+// tiles per chunk in the channel-gate score workspace: AS, P and T = (I + diag(beta) AS)^{-1}
+constexpr int kGateTiles = 3;
 
 // fp32 16x16x4 on the matrix cores: lane (g, i) = (lane / 16, lane % 16) gives A[i][g] and
 // B[g][i]; the result's lane (g, j) holds rows 4g .. 4g + 3 of column j, as in the bf16 forms.
@@ -1721,33 +1723,41 @@ __device__ __forceinline__ void scores_gate(const float *sQ, const float *sK, co
         }
 }
 
-// The score tiles AS and P of every 32-row chunk with the channel-wise gate, one workgroup per
-// (sequence, chunk), into [BH, nchunks, 2, C, C] fp32: they depend on q, k, d and the gate
-// only, so the reverse pass (in each of its value slices) and the per-chunk pass load them.
+// The score tiles AS and P of every 32-row chunk with the channel-wise gate, and
+// T = (I + diag(beta) AS)^{-1}, one workgroup per (sequence, chunk), into
+// [BH, nchunks, kGateTiles, C, C] fp32: they depend on q, k, d, beta and the gate only, so the
+// forward, the reverse pass (in each of its value slices) and the per-chunk pass load them.
 template <int C, int DK, typename TQ, typename TD>
 __global__ void __launch_bounds__(NT)
 bwd_scores_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
-                       const TD *__restrict__ d, const float *__restrict__ alpha_ch,
-                       float *__restrict__ scores, int64_t T, int64_t nch) {
+                       const TD *__restrict__ d, const float *__restrict__ beta,
+                       const float *__restrict__ alpha_ch, float *__restrict__ scores,
+                       int64_t T, int64_t nch) {
     constexpr int PX = DK + 1, PC = C + 1;
     __shared__ float sQ[C * PX], sK[C * PX], sKt[C * PX];
     __shared__ double sLg[C * PX];
-    __shared__ float sAS[C * PC], sP[C * PC];
+    __shared__ float sAS[C * PC], sP[C * PC], sT[C * PC], sb[C];
     const int64_t bh = blockIdx.x / nch, c = blockIdx.x % nch;
     const int64_t c0 = c * C, row0 = bh * T + c0;
     const int n = static_cast<int>(T - c0 < C ? T - c0 : C);
     const int tid = threadIdx.x;
     load_qk_gate<C, DK, PX>(q, k, d, alpha_ch, row0, n, sQ, sK, sKt, sLg, tid);
+    if (tid < C) sb[tid] = tid < n ? beta[row0 + tid] : 0.f;
+    for (int idx = tid; idx < C * C; idx += NT) sT[(idx / C) * PC + idx % C] = idx / C == idx % C;
     __syncthreads();
     gate_scan<C, DK, PX>(sLg, tid);
     __syncthreads();
     scores_gate<C, DK, PX, PC>(sQ, sK, sKt, sLg, sAS, sP, tid);
     __syncthreads();
-    float *dst = scores + (bh * nch + c) * 2 * C * C;
+    // T: the forward substitution on the identity's columns
+    solve_lower<C, C, PC, PC>(sT, sAS, sb, tid);
+    __syncthreads();
+    float *dst = scores + (bh * nch + c) * kGateTiles * C * C;
     for (int idx = tid; idx < C * C; idx += NT) {
         const int i = idx / C, j = idx % C;
         dst[idx] = sAS[i * PC + j];
         dst[C * C + idx] = sP[i * PC + j];
+        dst[2 * C * C + idx] = sT[i * PC + j];
     }
 }
 
@@ -1763,7 +1773,7 @@ bwd_state_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
     constexpr int PX = DK + 1, PC = C + 1, PS = BV + 1;
     __shared__ float sQ[C * PX], sK[C * PX], sKt[C * PX];
     __shared__ double sLg[C * PX];
-    __shared__ float sAS[C * PC], sP[C * PC];
+    __shared__ float sTi[C * PC], sP[C * PC];
     __shared__ float sdO[C * PS], sX[C * PS], sdM[DK * PS];
     __shared__ float sb[C], sGL[DK];
 
@@ -1790,14 +1800,14 @@ bwd_state_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
     static_assert(SIT * NT == C * C, "score tile layout");
     QkGateRegs<C, DK, TQ, TD> nx;
     TQ ndo[OIT];
-    float nas[SIT], np[SIT], nbt = 0.f;
+    float nti[SIT], np[SIT], nbt = 0.f;
     auto issue = [&](int64_t cc) __attribute__((always_inline)) {
         const int64_t r0 = bh * T + cc * C;
         const int nn = static_cast<int>(T - cc * C < C ? T - cc * C : C);
-        const float *sc = scores + (bh * nch + cc) * 2 * C * C;
+        const float *sc = scores + (bh * nch + cc) * kGateTiles * C * C;
 #pragma unroll
         for (int it = 0; it < SIT; ++it) {
-            nas[it] = sc[tid + it * NT];
+            nti[it] = sc[2 * C * C + tid + it * NT];  // T
             np[it] = sc[C * C + tid + it * NT];
         }
         load_qk_regs<C, DK>(nx, q, k, d, alpha_ch, r0, nn, tid);
@@ -1822,7 +1832,7 @@ bwd_state_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
 #pragma unroll
         for (int it = 0; it < SIT; ++it) {
             const int idx = tid + it * NT, i = idx / C, j = idx % C;
-            sAS[i * PC + j] = nas[it];
+            sTi[i * PC + j] = nti[it];
             sP[i * PC + j] = np[it];
         }
         if (tid < C) sb[tid] = nbt;
@@ -1860,7 +1870,16 @@ bwd_state_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
             for (int e = 0; e < 4; ++e) sX[(16 * (wv >> 1) + 4 * lg + e) * PS + cj] = acc[e];
         }
         block_sync();
-        solve_upper<C, BV, PS, PC>(sX, sAS, sb, tid);  // dR
+        {  // dR = T^T dU on the fp32 matrix cores: wave wv takes tile (wv / 2, wv % 2)
+            const int ri = 16 * (wv >> 1) + l16, cj = 16 * (wv & 1) + l16;
+            v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < C / 4; ++t)
+                acc = mfma4f(sTi[(4 * t + lg) * PC + ri], sX[(4 * t + lg) * PS + cj], acc);
+            block_sync();  // every wave has read dU
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sX[(16 * (wv >> 1) + 4 * lg + e) * PS + cj] = acc[e];
+        }
         block_sync();
         {  // dM <- Diag(G_L) dM + (Q o G)^T dO - (K o G)^T diag(b) dR on the fp32 matrix cores:
            // wave wv takes feature tiles FW wv .. FW wv + FW - 1 and both column tiles
@@ -1934,7 +1953,7 @@ bwd_chunk_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
     __shared__ float sM0[DK * PS], sdM[DK * PS];
     __shared__ float sY[C * PS], sdO[C * PS], sU[C * PS], sdR[C * PS];
     __shared__ float sb[C], sdb[C], sLast[DK];
-    __shared__ float sT[C * PC];  // T = (I + A)^{-1}, formed once for every slice's two solves
+    __shared__ float sT[C * PC];  // T = (I + A)^{-1} (from the score-tile kernel) for every slice
 
     const int64_t bh = blockIdx.x / nch, c = blockIdx.x % nch;
     const int64_t c0 = c * C, row0 = bh * T + c0;
@@ -1947,13 +1966,14 @@ bwd_chunk_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
     // the chunk's score tiles (from the score-tile kernel), loads issued first
     constexpr int SIT = C * C / NT;
     static_assert(SIT * NT == C * C, "score tile layout");
-    float tas[SIT], tp[SIT];
+    float tas[SIT], tp[SIT], tt[SIT];
     {
-        const float *sc = scores + (bh * nch + c) * 2 * C * C;
+        const float *sc = scores + (bh * nch + c) * kGateTiles * C * C;
 #pragma unroll
         for (int it = 0; it < SIT; ++it) {
             tas[it] = sc[tid + it * NT];
             tp[it] = sc[C * C + tid + it * NT];
+            tt[it] = sc[2 * C * C + tid + it * NT];
         }
     }
     load_qk_gate<C, DK, PX>(q, k, d, alpha_ch, row0, n, sQ, sK, sKt, sLg, tid);
@@ -1962,16 +1982,14 @@ bwd_chunk_gate_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
         const int idx = tid + it * NT, i = idx / C, j = idx % C;
         sAS[i * PC + j] = tas[it];
         sP[i * PC + j] = tp[it];
+        sT[i * PC + j] = tt[it];
     }
     if (tid < C) {
         sb[tid] = tid < n ? beta[row0 + tid] : 0.f;
         sdb[tid] = 0.f;
     }
-    for (int idx = tid; idx < C * C; idx += NT) sT[(idx / C) * PC + idx % C] = idx / C == idx % C;
     block_sync();
     gate_scan<C, DK, PX>(sLg, tid);
-    // T = (I + A)^{-1}: the forward substitution on the identity's columns (A = diag(b) AS)
-    solve_lower<C, C, PC, PC>(sT, sAS, sb, tid);
     block_sync();
 #pragma unroll
     for (int it = 0; it < C * DK / NT; ++it) {
@@ -2370,7 +2388,7 @@ hipError_t bwd_gate_typed(const BwdArgs &a, hipStream_t stream) {
         hipLaunchKernelGGL((bwd_scores_gate_kernel<C, DK, TQ, TD>),
                            dim3(static_cast<unsigned>(a.BH * nch)), dim3(NT), 0, stream,
                            static_cast<const TQ *>(a.q), static_cast<const TQ *>(a.k),
-                           static_cast<const TD *>(a.d), a.alpha_ch, a.scores, a.T, nch);
+                           static_cast<const TD *>(a.d), a.beta, a.alpha_ch, a.scores, a.T, nch);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         ChunkArgs f{a.q, a.k, a.v, a.d, a.beta, nullptr, a.S0, nullptr, nullptr, a.BH, a.T, DK,

@@ -149,7 +149,8 @@ chunk_f32math_kernel(const TQ *__restrict__ q, const TQ *__restrict__ k,
         const int64_t r0 = bh * T + cn;
         if constexpr (GATE) {
             if (gscores) {
-                const float *sc = gscores + (bh * nchunks + cn / CH) * 2 * CH * CH;
+                // AS and P, the first two of the chunk's three score tiles (the third is T)
+                const float *sc = gscores + (bh * nchunks + cn / CH) * 3 * CH * CH;
 #pragma unroll
                 for (int it = 0; it < SIT; ++it) {
                     const int idx = tid + it * kThreads;

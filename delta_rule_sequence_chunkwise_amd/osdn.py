@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "lib", "libosdn.so")
 
 OSDN_F32 = 0
 OSDN_BF16 = 1
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 STATUS = {0: "OSDN_OK", -1: "OSDN_ERR_NULL", -2: "OSDN_ERR_SHAPE", -3: "OSDN_ERR_UNSUPPORTED",
           -4: "OSDN_ERR_ALIGN", -5: "OSDN_ERR_ALIAS", -6: "OSDN_ERR_LAUNCH",

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define OSDN_ABI_VERSION 5
+#define OSDN_ABI_VERSION 6
 
 typedef enum osdn_status {
     OSDN_OK = 0,
@@ -293,7 +293,8 @@ osdn_status osdn_chunk_bwd_states(const void *q, const void *k, const void *v,
  *   workspace       caller-owned device memory of at least osdn_chunk_bwd_kda_workspace(B, H,
  *                   T, dk, dv, qkv) bytes, 256-byte aligned: the state at every chunk start and
  *                   the state gradient at every chunk end, [B,H,nchunks,dk,dv] fp32 each, then
- *                   every chunk's gated score tiles, [B,H,nchunks,2,32,32] fp32
+ *                   every chunk's gated score tiles and the inverse formed from them,
+ *                   [B,H,nchunks,3,32,32] fp32 (AS, P and (I + diag(beta) AS)^{-1})
  *   every other argument   as for osdn_chunk_bwd (there is no scalar alpha here)
  * All arithmetic is fp32 for either input type, with 32-row chunks (the products of the two
  * gradient passes on the fp32 matrix cores, the rest on the vector ALUs); the per-feature decays

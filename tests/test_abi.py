@@ -425,12 +425,13 @@ def test_chunk_bwd_kda_rejects(L, over, status):
 
 def test_bwd_kda_workspace_size(L):
     # two fp32 checkpoints [B,H,nchunks,dk,dv] with 32-row chunks, for either input type, then
-    # the score tiles [B,H,nchunks,2,32,32] fp32 (each region rounded up to 256 bytes)
+    # the score tiles and their inverse [B,H,nchunks,3,32,32] fp32 (each region rounded up to
+    # 256 bytes)
     nch = (100 + 31) // 32
     r256 = lambda n: (n + 255) // 256 * 256
     for qkv in (osdn.OSDN_BF16, osdn.OSDN_F32):
         assert L.osdn_chunk_bwd_kda_workspace(2, 3, 100, 128, 64, qkv) == \
-            2 * r256(2 * 3 * nch * 128 * 64 * 4) + r256(2 * 3 * nch * 2 * 32 * 32 * 4)
+            2 * r256(2 * 3 * nch * 128 * 64 * 4) + r256(2 * 3 * nch * 3 * 32 * 32 * 4)
     assert L.osdn_chunk_bwd_kda_workspace(2, 3, 100, 96, 64, osdn.OSDN_BF16) == -1
     assert L.osdn_chunk_bwd_kda_workspace(2, 3, -1, 128, 64, osdn.OSDN_BF16) == -1
     need = L.osdn_chunk_bwd_kda_workspace(2, 3, 100, 128, 64, osdn.OSDN_BF16)
