@@ -449,10 +449,11 @@ def bench_kda_bwd(n_steps, torch, dev, synth, w, x, fwd, cpu):
            "roofline": {"bound": "hbm", "achieved": round(alg / per / 1e9, 2),
                         "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                         "frac": round(alg / per / PEAK_HBM, 5), "alg_bytes_per_step": alg,
-                        "note": "four launches on the vector ALUs in fp32 (32-row chunks, the "
+                        "note": "four launches in fp32 (32-row chunks; the products of the "
+                                "reverse and per-chunk passes on the fp32 matrix cores, the "
                                 "per-feature decay of every score term formed in the product); "
                                 "the fp32 state checkpoints (2 x 268 MB written and read) and "
-                                "the chunk score tiles (67 MB) are beyond alg"}}
+                                "the chunk score tiles and inverse (101 MB) are beyond alg"}}
     if cpu:
         from oracle import backward
         b, h = 0, 0
