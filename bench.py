@@ -31,8 +31,9 @@ HBM.  Prints ONE JSON line.  Besides the contract fields it carries:
                 reverse pass over chunks, the per-chunk gradients) on the same workload with
                 seeded output gradients, with its HBM roofline, its matrix-core FLOP count, and
                 the float64 reverse pass on one sampled sequence (parity and CPU baseline);
-  kda_bwd       the backward with the channel-wise gate (osdn_chunk_bwd_kda: the fp32 forward
-                recording chunk-start states, the reverse pass, the per-chunk gradients) on the
+  kda_bwd       the backward with the channel-wise gate (osdn_chunk_bwd_kda: the score tiles and
+                their inverse, the fp32 forward recording chunk-start states, the reverse pass,
+                the per-chunk gradients) on the
                 same workload with the channel gate of `kda`, its HBM roofline, and the float64
                 reverse pass on one sampled sequence (parity and CPU baseline).
 """
